@@ -1,0 +1,228 @@
+"""CPU oracle for depthwise convolution -- TEST INFRASTRUCTURE ONLY.
+
+The oracle is the plain float64 direct-loop definition of DWC forward, data
+gradient and filter gradient (Flash-DWC, TACO: §2.1 for the per-channel inner
+product, §2.3 for the channel-last layouts, §5.1 for the two backward
+operators).  The arithmetic lives in ``dwc_oracle.c``; this module builds it
+with gcc and calls it through ctypes.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The GPU library never does, and the two share no code.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "dwc_oracle.c")
+LIB = os.path.join(HERE, "libdwc_oracle.so")
+
+_I64 = ctypes.c_int64
+_PD = ctypes.POINTER(ctypes.c_double)
+_PI = ctypes.POINTER(ctypes.c_int64)
+
+
+def compile_c(src: str, out: str) -> str:
+    """gcc -O2 with OpenMP and without fast-math: sums keep IEEE semantics."""
+    tmp = out + ".tmp"
+    subprocess.check_call(
+        ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+         "-Wall", "-Wextra", "-o", tmp, src, "-lm"])
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> str:
+    if force or not os.path.exists(LIB):
+        compile_c(SRC, LIB)
+    return LIB
+
+
+def _f64(a: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(_PD)
+
+
+def _pair(v) -> Tuple[int, int]:
+    if isinstance(v, (tuple, list)):
+        return int(v[0]), int(v[1])
+    return int(v), int(v)
+
+
+def _dims(n, h, w, c, fh, fw, stride, pad):
+    sh, sw = _pair(stride)
+    ph, pw = _pair(pad)
+    return [n, h, w, c, fh, fw, sh, sw, ph, pw]
+
+
+def _idx(idx: np.ndarray, width: int) -> np.ndarray:
+    idx = np.ascontiguousarray(idx, dtype=np.int64)
+    assert idx.ndim == 2 and idx.shape[1] == width
+    return idx
+
+
+class Oracle:
+    """One compiled copy of the oracle (the real one, or a planted-mistake
+    copy in the mutation tests)."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        dims = [_I64] * 10
+        for name in ("dwc_oracle_fwd", "dwc_oracle_bwd_data", "dwc_oracle_bwd_filter"):
+            f = getattr(lib, name)
+            f.argtypes = dims + [_PD, _PD, _PD]
+            f.restype = ctypes.c_int
+        for name in ("dwc_oracle_fwd_at", "dwc_oracle_bwd_data_at",
+                     "dwc_oracle_bwd_filter_at"):
+            f = getattr(lib, name)
+            f.argtypes = dims + [_PD, _PD, _PI, _I64, _PD]
+            f.restype = ctypes.c_int
+        lib.dwc_oracle_output_dims.argtypes = [_I64] * 8 + [_PI, _PI]
+        lib.dwc_oracle_output_dims.restype = ctypes.c_int
+        self.lib = lib
+        self.path = path
+
+    def output_dims(self, h, w, fh, fw, stride=1, pad=0) -> Tuple[int, int]:
+        sh, sw = _pair(stride)
+        ph, pw = _pair(pad)
+        oh, ow = _I64(), _I64()
+        rc = self.lib.dwc_oracle_output_dims(h, w, fh, fw, sh, sw, ph, pw,
+                                             ctypes.byref(oh), ctypes.byref(ow))
+        if rc:
+            raise ValueError("bad convolution geometry")
+        return oh.value, ow.value
+
+    def fwd(self, x: np.ndarray, w: np.ndarray, stride=1, pad=0) -> np.ndarray:
+        """Y = DWC(X, W): x is N x H x W x C, w is FH x FW x C."""
+        x, w = _f64(x), _f64(w)
+        n, h, wd, c = x.shape
+        fh, fw, c2 = w.shape
+        assert c == c2
+        oh, ow = self.output_dims(h, wd, fh, fw, stride, pad)
+        y = np.empty((n, oh, ow, c), dtype=np.float64)
+        rc = self.lib.dwc_oracle_fwd(*_dims(n, h, wd, c, fh, fw, stride, pad),
+                                     _p(x), _p(w), _p(y))
+        if rc:
+            raise ValueError("oracle fwd: bad arguments")
+        return y
+
+    def bwd_data(self, dy: np.ndarray, w: np.ndarray, in_hw: Sequence[int],
+                 stride=1, pad=0) -> np.ndarray:
+        """dX for input spatial size ``in_hw`` (several H can give one OH)."""
+        dy, w = _f64(dy), _f64(w)
+        n, oh, ow, c = dy.shape
+        fh, fw, c2 = w.shape
+        assert c == c2
+        h, wd = int(in_hw[0]), int(in_hw[1])
+        assert self.output_dims(h, wd, fh, fw, stride, pad) == (oh, ow)
+        dx = np.empty((n, h, wd, c), dtype=np.float64)
+        rc = self.lib.dwc_oracle_bwd_data(*_dims(n, h, wd, c, fh, fw, stride, pad),
+                                          _p(dy), _p(w), _p(dx))
+        if rc:
+            raise ValueError("oracle bwd_data: bad arguments")
+        return dx
+
+    def bwd_filter(self, x: np.ndarray, dy: np.ndarray, f_hw: Sequence[int],
+                   stride=1, pad=0) -> np.ndarray:
+        """dW (FH x FW x C) from X and dY."""
+        x, dy = _f64(x), _f64(dy)
+        n, h, wd, c = x.shape
+        fh, fw = int(f_hw[0]), int(f_hw[1])
+        assert self.output_dims(h, wd, fh, fw, stride, pad) == tuple(dy.shape[1:3])
+        dw = np.empty((fh, fw, c), dtype=np.float64)
+        rc = self.lib.dwc_oracle_bwd_filter(*_dims(n, h, wd, c, fh, fw, stride, pad),
+                                            _p(x), _p(dy), _p(dw))
+        if rc:
+            raise ValueError("oracle bwd_filter: bad arguments")
+        return dw
+
+    def fwd_at(self, x, w, idx, stride=1, pad=0) -> np.ndarray:
+        """Y at the (n, oh, ow, c) rows of ``idx``."""
+        x, w = _f64(x), _f64(w)
+        idx = _idx(idx, 4)
+        n, h, wd, c = x.shape
+        fh, fw, _ = w.shape
+        out = np.empty(len(idx), dtype=np.float64)
+        rc = self.lib.dwc_oracle_fwd_at(*_dims(n, h, wd, c, fh, fw, stride, pad), _p(x), _p(w),
+                                        idx.ctypes.data_as(_PI), len(idx), _p(out))
+        if rc:
+            raise ValueError("oracle fwd_at: bad arguments")
+        return out
+
+    def bwd_data_at(self, dy, w, in_hw, idx, stride=1, pad=0) -> np.ndarray:
+        """dX at the (n, ih, iw, c) rows of ``idx``."""
+        dy, w = _f64(dy), _f64(w)
+        idx = _idx(idx, 4)
+        n, _, _, c = dy.shape
+        fh, fw, _ = w.shape
+        h, wd = int(in_hw[0]), int(in_hw[1])
+        out = np.empty(len(idx), dtype=np.float64)
+        rc = self.lib.dwc_oracle_bwd_data_at(*_dims(n, h, wd, c, fh, fw, stride, pad),
+                                             _p(dy), _p(w), idx.ctypes.data_as(_PI),
+                                             len(idx), _p(out))
+        if rc:
+            raise ValueError("oracle bwd_data_at: bad arguments")
+        return out
+
+    def bwd_filter_at(self, x, dy, f_hw, idx, stride=1, pad=0) -> np.ndarray:
+        """dW at the (fh, fw, c) rows of ``idx``."""
+        x, dy = _f64(x), _f64(dy)
+        idx = _idx(idx, 3)
+        n, h, wd, c = x.shape
+        fh, fw = int(f_hw[0]), int(f_hw[1])
+        out = np.empty(len(idx), dtype=np.float64)
+        rc = self.lib.dwc_oracle_bwd_filter_at(*_dims(n, h, wd, c, fh, fw, stride, pad),
+                                               _p(x), _p(dy), idx.ctypes.data_as(_PI),
+                                               len(idx), _p(out))
+        if rc:
+            raise ValueError("oracle bwd_filter_at: bad arguments")
+        return out
+
+
+_default: Optional[Oracle] = None
+
+
+def get() -> Oracle:
+    global _default
+    if _default is None:
+        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+            build()
+        _default = Oracle(LIB)
+    return _default
+
+
+def output_dims(*a, **k):
+    return get().output_dims(*a, **k)
+
+
+def fwd(*a, **k):
+    return get().fwd(*a, **k)
+
+
+def bwd_data(*a, **k):
+    return get().bwd_data(*a, **k)
+
+
+def bwd_filter(*a, **k):
+    return get().bwd_filter(*a, **k)
+
+
+def fwd_at(*a, **k):
+    return get().fwd_at(*a, **k)
+
+
+def bwd_data_at(*a, **k):
+    return get().bwd_data_at(*a, **k)
+
+
+def bwd_filter_at(*a, **k):
+    return get().bwd_filter_at(*a, **k)
