@@ -1,0 +1,89 @@
+"""Build libdwc.so in-tree: hipcc for gfx950, one object per translation unit.
+
+Usage: ``python -m depthwise_convolution_dwc_amd.build`` (or ``build()``).
+Objects go to ``_build/`` at the repository root; the library lands next to
+this file as ``libdwc.so``.
+"""
+
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libdwc.so")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+# Every HIP translation unit is built without packed-fp32 instructions.
+HIP_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", CSRC, "-I", INCLUDE,
+]
+CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", CSRC, "-I", INCLUDE]
+
+
+def _units():
+    """(compiler, source, object, extra flags) per translation unit."""
+    u = []
+    for dt in (0, 1, 2):
+        u.append(("hip", "inst_direct.hip", f"inst_direct_dt{dt}.o", [f"-DDWC_INST_DT={dt}"]))
+    u.append(("hip", "inst_generic.hip", "inst_generic.o", []))
+    u.append(("hip", "dwc_api.cpp", "dwc_api.o", ["-x", "hip"]))
+    u.append(("cxx", "dwc_plan.cpp", "dwc_plan.o", []))
+    return u
+
+
+def _compile(unit, verbose):
+    kind, src, obj, extra = unit
+    src_p = os.path.join(CSRC, src)
+    obj_p = os.path.join(BUILD, obj)
+    if kind == "hip":
+        cmd = [HIPCC] + HIP_FLAGS + extra + ["-c", src_p, "-o", obj_p]
+    else:
+        cmd = ["g++"] + CXX_FLAGS + extra + ["-c", src_p, "-o", obj_p]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass warns that it does not know the packed-fp32 feature
+    msgs = [ln for ln in (r.stdout + r.stderr).splitlines()
+            if "is not a recognized feature" not in ln]
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {src}\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs), flush=True)
+    return obj_p
+
+
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    """Compile every translation unit and link libdwc.so; returns its path."""
+    if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
+        raise RuntimeError(f"hipcc not found at {HIPCC}")
+    os.makedirs(BUILD, exist_ok=True)
+    units = _units()
+    jobs = jobs or min(len(units), max(1, min(8, os.cpu_count() or 1)))
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda u: _compile(u, verbose), units))
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC",
+           f"-Wl,--version-script={os.path.join(CSRC, 'libdwc.map')}", "-o", tmp] + objs
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed\n" + r.stdout + r.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,109 @@
+// dwc_api.cpp -- the compute entry points of libdwc (extern "C").
+// Validation happens in dwc_plan.cpp before any HIP call; this file only
+// launches the planned kernels on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <string>
+
+#include "dwc_launch.h"
+#include "dwc_plan.h"
+
+using namespace dwc;
+
+namespace {
+
+int hip_fail(hipError_t e, const char* what) {
+  set_last_error(std::string(what) + ": " + hipGetErrorString(e));
+  return DWC_ERR_HIP;
+}
+
+hipError_t launch_fwd_type(const Plan& pl, const void* in, const void* filt, float* out,
+                           hipStream_t s) {
+  if (pl.kind == PLAN_DIRECT) {
+    FwdArgs a = pl.fa;
+    a.in = in;
+    a.filt = filt;
+    a.out = out;
+    switch (pl.dt) {
+      case DT_F32: return launch_fwd_direct_dt0(a.FW, a.SW, pl.tmw, pl.flip, a, pl.blocks, s);
+      case DT_BF16: return launch_fwd_direct_dt1(a.FW, a.SW, pl.tmw, pl.flip, a, pl.blocks, s);
+      case DT_F16: return launch_fwd_direct_dt2(a.FW, a.SW, pl.tmw, pl.flip, a, pl.blocks, s);
+    }
+    return hipErrorInvalidValue;
+  }
+  GenericArgs g = pl.ga;
+  g.a = in;
+  g.b = filt;
+  g.out = out;
+  return launch_generic(pl.gen_kind, pl.dt, g, s);
+}
+
+int prepare(const dwc_problem* p, int op, Plan* pl, const void* in0, const void* in1,
+            const void* out, const void* ws, size_t ws_bytes) {
+  std::string err;
+  int st = make_plan(p, op, pl, &err);
+  if (st == DWC_OK) st = check_pointers(p, *pl, in0, in1, out, ws, ws_bytes, &err);
+  if (st != DWC_OK) set_last_error(err);
+  return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dwc_fwd(const dwc_problem* p, const void* x, const void* w, void* y, void* stream) {
+  Plan pl;
+  const int st = prepare(p, DWC_OP_FWD, &pl, x, w, y, nullptr, 0);
+  if (st != DWC_OK || pl.empty) return st;
+  const hipError_t e = launch_fwd_type(pl, x, w, (float*)y, (hipStream_t)stream);
+  return e == hipSuccess ? DWC_OK : hip_fail(e, "dwc_fwd launch");
+}
+
+int dwc_bwd_data(const dwc_problem* p, const void* dy, const void* w, void* dx, void* stream) {
+  Plan pl;
+  const int st = prepare(p, DWC_OP_BWD_DATA, &pl, dy, w, dx, nullptr, 0);
+  if (st != DWC_OK || pl.empty) return st;
+  const hipError_t e = launch_fwd_type(pl, dy, w, (float*)dx, (hipStream_t)stream);
+  return e == hipSuccess ? DWC_OK : hip_fail(e, "dwc_bwd_data launch");
+}
+
+int dwc_bwd_filter(const dwc_problem* p, const void* x, const void* dy, void* dw,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  Plan pl;
+  const int st = prepare(p, DWC_OP_BWD_FILTER, &pl, x, dy, dw, workspace, workspace_bytes);
+  if (st != DWC_OK) return st;
+  const hipStream_t s = (hipStream_t)stream;
+  const int64_t m = (int64_t)p->fh * p->fw * p->c;
+  if (pl.empty) {  // empty batch: dW = 0 (a sum over no terms)
+    const hipError_t e = launch_reduce(ReduceArgs{nullptr, (float*)dw, m, 0}, s);
+    return e == hipSuccess ? DWC_OK : hip_fail(e, "dwc_bwd_filter zero fill");
+  }
+  // One slice writes dW directly; several write partials to the workspace.
+  float* part = pl.ws_bytes > 0 ? (float*)workspace : (float*)dw;
+  hipError_t e;
+  if (pl.kind == PLAN_DIRECT) {
+    WgradArgs a = pl.wa;
+    a.x = x;
+    a.dy = dy;
+    a.ws = part;
+    switch (pl.dt) {
+      case DT_F32: e = launch_wgrad_direct_dt0(a.FW, a.SW, pl.tj, a, pl.blocks, s); break;
+      case DT_BF16: e = launch_wgrad_direct_dt1(a.FW, a.SW, pl.tj, a, pl.blocks, s); break;
+      default: e = launch_wgrad_direct_dt2(a.FW, a.SW, pl.tj, a, pl.blocks, s); break;
+    }
+  } else {
+    GenericArgs g = pl.ga;
+    g.a = x;
+    g.b = dy;
+    g.out = part;
+    e = launch_generic(pl.gen_kind, pl.dt, g, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "dwc_bwd_filter launch");
+  if (pl.ws_bytes > 0) {
+    e = launch_reduce(ReduceArgs{(const float*)workspace, (float*)dw, m, pl.z}, s);
+    if (e != hipSuccess) return hip_fail(e, "dwc_bwd_filter reduce");
+  }
+  return DWC_OK;
+}
+
+}  // extern "C"

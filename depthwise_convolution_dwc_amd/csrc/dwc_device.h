@@ -1,0 +1,41 @@
+// dwc_device.h -- device-side helpers shared by the libdwc kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dwc_geom.h"
+
+namespace dwc {
+
+// Operand storage types.  bf16 is kept as its raw 16 bits.
+template <int DT> struct Elem;
+template <> struct Elem<DT_F32> { static constexpr int bytes = 4; };
+template <> struct Elem<DT_BF16> { static constexpr int bytes = 2; };
+template <> struct Elem<DT_F16> { static constexpr int bytes = 2; };
+
+// Buffer resource over [base, base + bytes).  A raw buffer load whose
+// per-lane offset is >= bytes returns 0, which is how every kernel reads the
+// implicit zero padding without branches.  The range check covers the
+// VGPR offset only, so every offset below goes in the VGPR operand.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// An offset that is always outside any resource built above.
+constexpr uint32_t kOOB = 0x80000000u;
+
+// The hardware hands workgroup b to XCD (b mod 8).  Give each XCD one
+// contiguous range of logical tile ids so that tiles which read the same
+// input rows share that XCD's L2.
+__device__ __forceinline__ int xcd_logical_block(int bid, int nblocks) {
+  constexpr int kXcd = 8;
+  const int x = bid % kXcd, k = bid / kXcd;
+  const int q = nblocks / kXcd, r = nblocks % kXcd;
+  return x * q + (x < r ? x : r) + k;
+}
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+}  // namespace dwc

@@ -1,0 +1,88 @@
+// dwc_geom.h -- kernel argument blocks and tile constants of libdwc.
+// Plain structs shared by the host planner (no HIP needed) and the kernels.
+#pragma once
+
+#include <stdint.h>
+
+namespace dwc {
+
+enum { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
+
+// Channels per wave: one channel per lane, 64 lanes.  In the channel-last
+// layout a wave's load of one pixel is 64 consecutive channels, i.e. one
+// 256-byte (fp32) or 128-byte (bf16/fp16) contiguous segment.
+constexpr int kWaveChannels = 64;
+constexpr int kWavesPerBlock = 4;
+constexpr int kBlockThreads = 64 * kWavesPerBlock;
+
+// Filter widths with register-window (direct) kernels; other widths run the
+// generic kernels.  X-macro: DWC_DIRECT_FW_LIST(M) expands M(F) per width.
+#define DWC_DIRECT_FW_LIST(M) M(3) M(5) M(7) M(9) M(13) M(17) M(21) M(27) M(31)
+
+// Output columns per lane (forward-type kernel) and per strip (filter-gradient
+// kernel) that have instantiations.
+#define DWC_FWD_TMW_LIST(M) M(7) M(14)
+#define DWC_WGRAD_TJ_LIST(M) M(7) M(14)
+
+// Output rows per lane in the forward-type direct kernel, and dY rows per
+// register block in the filter-gradient kernel.
+constexpr int kFwdRows = 4;
+constexpr int kWgradRows = 4;
+
+// Filter rows held in registers at once by both direct kernels for a filter
+// of width FW: the whole filter up to 9x9, else a chunk of about 64-81
+// registers chosen so that common square filters split with little waste
+// (13 -> 5+5+3, 17 -> 3 x 6, 21 -> 3 x 7, 27 -> 3 x 9, 31 -> 2 x 16).
+constexpr int filter_row_chunk(int fw) {
+  return fw <= 9 ? fw : fw == 13 ? 5 : fw <= 27 ? 3 : 2;
+}
+
+// Forward-type kernels: the forward map and the stride-1 data gradient (the
+// forward map of dY with the filter turned by 180 degrees).
+struct FwdArgs {
+  const void* in;    // N x IH x IW x C (X, or dY for the data gradient)
+  const void* filt;  // FH x FW x C
+  float* out;        // N x OH x OW x C
+  int N, IH, IW, C;
+  int OH, OW;
+  int FH, FW, SH, SW;
+  int PH, PW;        // zero padding; negative values crop
+  int tiles_w, tiles_h, cblocks;
+  int num_items;     // waves of work: N * cblocks * tiles_h * tiles_w
+};
+
+// Filter gradient: partial sums over slices of the N*OH axis.  One
+// workgroup (4 waves) per (slice, channel block, filter-row chunk); its waves
+// split the slice's (row group, column strip) units and add their sums in
+// LDS before one partial is written.
+struct WgradArgs {
+  const void* x;     // N x IH x IW x C
+  const void* dy;    // N x OH x OW x C
+  float* ws;         // Z x FH x FW x C partial sums
+  int N, IH, IW, C, OH, OW;
+  int FH, FW, SH, SW, PH, PW;
+  int cblocks, fh_tiles, Z;
+  int rows;          // N * OH
+  int num_items;     // workgroups: Z * cblocks * fh_tiles
+};
+
+// out[i] = sum_{z < Z} ws[z * M + i], summed in order of z.
+struct ReduceArgs {
+  const float* ws;
+  float* out;
+  int64_t M;
+  int Z;
+};
+
+// Generic kernels: one output element per lane.
+struct GenericArgs {
+  const void* a;     // forward / data gradient: X or dY; filter gradient: X
+  const void* b;     // forward / data gradient: W;       filter gradient: dY
+  float* out;        // Y, dX, or Z x FH x FW x C partial sums
+  int N, IH, IW, C, OH, OW;
+  int FH, FW, SH, SW, PH, PW;
+  int Z, rows;       // filter gradient split
+  int64_t total;     // elements (or work items) to produce
+};
+
+}  // namespace dwc

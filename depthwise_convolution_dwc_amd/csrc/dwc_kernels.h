@@ -1,0 +1,400 @@
+// dwc_kernels.h -- HIP kernels of libdwc for gfx950 (MI355X).
+//
+// Operations (Flash-DWC, TACO): forward DWC (§2.1), the stride-1 data
+// gradient as the forward map of dY with the filter turned by 180 degrees
+// (§5.1), and the filter gradient split along the N*OH accumulation axis
+// (§5.1).  Layouts are channel-last (§2.3).
+//
+// Mapping shared by the direct kernels: one channel per lane, 64 channels per
+// wave, so every load of one pixel is one contiguous 256-byte (fp32) or
+// 128-byte (bf16/fp16) segment, and every lane owns a strip of outputs in
+// registers.  Zero padding is read through buffer-resource range checks:
+// an out-of-range offset returns 0, so the FMA loops have no branches.
+#pragma once
+
+#include "dwc_device.h"
+
+namespace dwc {
+
+// Loads one operand element through a buffer resource.  `voff` is the
+// lane's byte offset (the channel), `soff` the wave-uniform byte offset of
+// the pixel.  Reads through a resource of zero bytes return 0.
+template <int DT>
+__device__ __forceinline__ float ld(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  if constexpr (DT == DT_F32) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0));
+  } else if constexpr (DT == DT_BF16) {
+    uint32_t b = __builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
+    return __uint_as_float(b << 16);
+  } else {
+    unsigned short h = __builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
+    return (float)__builtin_bit_cast(_Float16, h);
+  }
+}
+
+// Byte offsets, per lane, of the pixels col0 .. col0+SPAN-1 of an image row
+// relative to pixel col0, plus the lane's channel.  Columns outside
+// [0, cols) and channels >= C get an offset no resource covers, so they read
+// as zero (implicit zero padding).  Computed once per strip and shared by
+// every row the strip visits.
+template <int SPAN>
+__device__ __forceinline__ void column_offsets(uint32_t (&o)[SPAN], int col0, int cols,
+                                               uint32_t pix_bytes, int c, int C, int eb) {
+#pragma unroll
+  for (int j = 0; j < SPAN; ++j) {
+    const bool ok = (unsigned)(col0 + j) < (unsigned)cols && c < C;
+    o[j] = ok ? (uint32_t)j * pix_bytes + (uint32_t)c * eb : kOOB;
+  }
+}
+
+// The strip of SPAN pixels of image row `row` starting at column col0, one
+// channel per lane.  A row outside [0, rows) reads as zero.
+template <int DT, int SPAN>
+__device__ __forceinline__ void load_strip(float (&v)[SPAN], const char* img, int row, int rows,
+                                           int col0, int cols, uint32_t pix_bytes,
+                                           const uint32_t (&o)[SPAN]) {
+  const bool row_ok = (unsigned)row < (unsigned)rows;
+  const char* base = img + ((ptrdiff_t)row * cols + col0) * (ptrdiff_t)pix_bytes;
+  const auto r = make_rsrc(base, row_ok ? (uint32_t)SPAN * pix_bytes : 0u);
+#pragma unroll
+  for (int j = 0; j < SPAN; ++j) v[j] = ld<DT>(r, o[j], 0);
+}
+
+// ---------------------------------------------------------------------------
+// Forward-type direct kernel ("row streaming").
+//
+// A wave owns 64 channels x TR output rows x TMW output columns; each lane
+// keeps its TR x TMW outputs in registers.  The filter is processed in
+// chunks of FHC rows held in registers: filter reuse across all TR x TMW
+// outputs (§3.2).  For each chunk the wave streams the (TR-1)*S+FHC input
+// rows the chunk touches; each row's strip of (TMW-1)*S+FW pixels is loaded
+// once and feeds every (output row, filter row) pair that reads it, and
+// along the width consecutive taps share TMW-1 of their inputs (the
+// width-first reuse of §3.3, run as 1-D filters along the width accumulated
+// over filter rows).  All loop bounds are compile-time, so every accumulator
+// and tap is a register.  FLIP reads the filter turned by 180 degrees, which
+// makes this the stride-1 data gradient (§5.1).
+// ---------------------------------------------------------------------------
+template <int DT, int FW, int S, int TMW, bool FLIP>
+__global__ __launch_bounds__(kBlockThreads) void fwd_rows(FwdArgs a) {
+  constexpr int EB = Elem<DT>::bytes;
+  constexpr int TR = kFwdRows;
+  constexpr int FHC = filter_row_chunk(FW);
+  constexpr int SPAN = (TMW - 1) * S + FW;
+  constexpr int MSPAN = (TR - 1) * S + FHC;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int item = xcd_logical_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wave;
+  if (item >= a.num_items) return;
+  int t = item;
+  const int tw = t % a.tiles_w;
+  t /= a.tiles_w;
+  const int th = t % a.tiles_h;
+  t /= a.tiles_h;
+  const int cb = t % a.cblocks;
+  const int n = t / a.cblocks;
+  const int c = cb * kWaveChannels + lane;
+  const uint32_t voff = c < a.C ? (uint32_t)c * EB : kOOB;
+  const uint32_t Cb = (uint32_t)a.C * EB;
+  const char* img = (const char*)a.in + (size_t)n * a.IH * a.IW * Cb;
+  const auto zero = make_rsrc(a.in, 0);
+  const auto wrs = make_rsrc(a.filt, (uint32_t)(a.FH * FW) * Cb);
+  const int oh0 = th * TR, ow0 = tw * TMW;
+  const int ih_base = oh0 * S - a.PH;
+  const int iw0 = ow0 * S - a.PW;
+  uint32_t coff[SPAN];
+  column_offsets<SPAN>(coff, iw0, a.IW, Cb, c, a.C, EB);
+
+  float acc[TR][TMW];
+#pragma unroll
+  for (int r = 0; r < TR; ++r)
+#pragma unroll
+    for (int q = 0; q < TMW; ++q) acc[r][q] = 0.f;
+
+  for (int fh0 = 0; fh0 < a.FH; fh0 += FHC) {
+    float wv[FHC][FW];
+#pragma unroll
+    for (int k = 0; k < FHC; ++k) {
+      const int fh = fh0 + k;
+      const bool ok = fh < a.FH;
+      const int fhe = FLIP ? a.FH - 1 - fh : fh;
+#pragma unroll
+      for (int fw = 0; fw < FW; ++fw) {
+        const int fwe = FLIP ? FW - 1 - fw : fw;
+        wv[k][fw] = ld<DT>(ok ? wrs : zero, voff, ok ? (uint32_t)(fhe * FW + fwe) * Cb : 0u);
+      }
+    }
+    // Rows of this chunk: ih_base+fh0 .. +MSPAN-1.  Skip the chunk if all of
+    // them are padding; otherwise stream them branch-free (padding rows read
+    // as zeros), loading row m+1 while row m is multiplied.
+    const int row0 = ih_base + fh0;
+    if (row0 + MSPAN <= 0 || row0 >= a.IH) continue;
+    float xv[2][SPAN];
+    load_strip<DT, SPAN>(xv[0], img, row0, a.IH, iw0, a.IW, Cb, coff);
+#pragma unroll
+    for (int m = 0; m < MSPAN; ++m) {
+      if (m + 1 < MSPAN)
+        load_strip<DT, SPAN>(xv[(m + 1) & 1], img, row0 + m + 1, a.IH, iw0, a.IW, Cb, coff);
+#pragma unroll
+      for (int r = 0; r < TR; ++r) {
+        const int k = m - r * S;
+        if (k < 0 || k >= FHC) continue;
+#pragma unroll
+        for (int fw = 0; fw < FW; ++fw)
+#pragma unroll
+          for (int q = 0; q < TMW; ++q)
+            acc[r][q] = fmaf(xv[m & 1][q * S + fw], wv[k][fw], acc[r][q]);
+      }
+    }
+  }
+
+  if (c < a.C) {
+    float* out = a.out + (size_t)n * a.OH * a.OW * a.C + c;
+#pragma unroll
+    for (int r = 0; r < TR; ++r) {
+      const int oh = oh0 + r;
+      if (oh >= a.OH) break;
+#pragma unroll
+      for (int q = 0; q < TMW; ++q) {
+        const int ow = ow0 + q;
+        if (ow < a.OW) out[((size_t)oh * a.OW + ow) * a.C] = acc[r][q];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Filter-gradient direct kernel (§5.1 "accumulation-axis parallelism").
+//
+// A workgroup owns 64 channels x a chunk of TFH filter rows x all FW taps
+// and one slice [r0, r1) of the flattened N*OH axis; each lane keeps its
+// TFH x FW taps in registers.  The slice is cut into units of up to RY
+// consecutive output rows of one image x one strip of TJ columns, dealt
+// round-robin to the 4 waves.  For a unit, the RY x TJ dY values stay in
+// registers and each of the (RY-1)*S+TFH input rows it touches is loaded
+// once as a strip of (TJ-1)*S+FW pixels, which feeds every (dY row, filter
+// row) pair that reads it; along the width each input pixel meets every tap
+// whose window covers it (width-first reuse, §3.3).  The 4 waves add their
+// sums through LDS in a fixed order and one partial per slice is written;
+// reduce_partials adds the slices in slice order.  Deterministic.
+// ---------------------------------------------------------------------------
+template <int DT, int FW, int S, int TJ>
+__global__ __launch_bounds__(kBlockThreads) void wgrad_rows(WgradArgs a) {
+  constexpr int EB = Elem<DT>::bytes;
+  constexpr int TFH = filter_row_chunk(FW);
+  constexpr int RY = kWgradRows;
+  constexpr int SPAN = (TJ - 1) * S + FW;
+  constexpr int MSPAN = (RY - 1) * S + TFH;
+  __shared__ float red[2][TFH * FW][64];
+
+  const int wave = uniform(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
+  if (blk >= a.num_items) return;  // the whole workgroup leaves together
+  int t = blk;
+  const int ft = t % a.fh_tiles;
+  t /= a.fh_tiles;
+  const int cb = t % a.cblocks;
+  const int z = t / a.cblocks;
+  const int c = cb * kWaveChannels + lane;
+  const uint32_t Cb = (uint32_t)a.C * EB;
+  const int q0 = a.rows / a.Z, rem = a.rows % a.Z;
+  const int r0 = z * q0 + (z < rem ? z : rem);
+  const int r1 = r0 + q0 + (z < rem ? 1 : 0);
+  const int fh0 = ft * TFH;
+  const int strips = (a.OW + TJ - 1) / TJ;
+
+  float acc[TFH][FW];
+#pragma unroll
+  for (int k = 0; k < TFH; ++k)
+#pragma unroll
+    for (int fw = 0; fw < FW; ++fw) acc[k][fw] = 0.f;
+
+  int unit = 0;  // running index of (row group, strip) units in this slice
+  for (int row = r0; row < r1;) {
+    const int n = row / a.OH, oh0 = row - n * a.OH;
+    int cnt = r1 - row;
+    if (cnt > RY) cnt = RY;
+    if (cnt > a.OH - oh0) cnt = a.OH - oh0;
+    const char* ximg = (const char*)a.x + (size_t)n * a.IH * a.IW * Cb;
+    const char* dimg = (const char*)a.dy + (size_t)n * a.OH * a.OW * Cb;
+    for (int s = 0; s < strips; ++s, ++unit) {
+      if ((unit & 3) != wave) continue;
+      const int ow0 = s * TJ;
+      const int ih_base = oh0 * S - a.PH + fh0;
+      const int iw0 = ow0 * S - a.PW;
+      float dv[RY][TJ];
+      {
+        uint32_t doff[TJ];
+        column_offsets<TJ>(doff, ow0, a.OW, Cb, c, a.C, EB);
+#pragma unroll
+        for (int r = 0; r < RY; ++r)
+          load_strip<DT, TJ>(dv[r], dimg, r < cnt ? oh0 + r : -1, a.OH, ow0, a.OW, Cb, doff);
+      }
+      uint32_t xoff[SPAN];
+      column_offsets<SPAN>(xoff, iw0, a.IW, Cb, c, a.C, EB);
+      // Input rows ih_base .. +MSPAN-1, streamed branch-free (padding rows
+      // read as zeros), row m+1 loading while row m is multiplied.
+      if (ih_base + MSPAN <= 0 || ih_base >= a.IH) continue;
+      float xv[2][SPAN];
+      load_strip<DT, SPAN>(xv[0], ximg, ih_base, a.IH, iw0, a.IW, Cb, xoff);
+#pragma unroll
+      for (int m = 0; m < MSPAN; ++m) {
+        if (m + 1 < MSPAN)
+          load_strip<DT, SPAN>(xv[(m + 1) & 1], ximg, ih_base + m + 1, a.IH, iw0, a.IW, Cb, xoff);
+#pragma unroll
+        for (int r = 0; r < RY; ++r) {
+          const int k = m - r * S;
+          if (k < 0 || k >= TFH) continue;
+#pragma unroll
+          for (int q = 0; q < TJ; ++q)
+#pragma unroll
+            for (int fw = 0; fw < FW; ++fw)
+              acc[k][fw] = fmaf(xv[m & 1][q * S + fw], dv[r][q], acc[k][fw]);
+        }
+      }
+    }
+    row += cnt;
+  }
+
+  // (w0 + w2) + (w1 + w3), then one store of the slice partial.
+  if (wave >= 2) {
+#pragma unroll
+    for (int k = 0; k < TFH; ++k)
+#pragma unroll
+      for (int fw = 0; fw < FW; ++fw) red[wave - 2][k * FW + fw][lane] = acc[k][fw];
+  }
+  __syncthreads();
+  if (wave < 2) {
+#pragma unroll
+    for (int k = 0; k < TFH; ++k)
+#pragma unroll
+      for (int fw = 0; fw < FW; ++fw) acc[k][fw] += red[wave][k * FW + fw][lane];
+  }
+  __syncthreads();
+  if (wave == 1) {
+#pragma unroll
+    for (int k = 0; k < TFH; ++k)
+#pragma unroll
+      for (int fw = 0; fw < FW; ++fw) red[0][k * FW + fw][lane] = acc[k][fw];
+  }
+  __syncthreads();
+  if (wave == 0 && c < a.C) {
+    float* ws = a.ws + (size_t)z * a.FH * FW * a.C + c;
+#pragma unroll
+    for (int k = 0; k < TFH; ++k) {
+      const int fh = fh0 + k;
+      if (fh >= a.FH) break;
+#pragma unroll
+      for (int fw = 0; fw < FW; ++fw)
+        ws[((size_t)fh * FW + fw) * a.C] = acc[k][fw] + red[0][k * FW + fw][lane];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Generic kernels: one output element per lane, any filter size and stride.
+// Element index i runs channel-fastest, so a wave reads 64 consecutive
+// channels of one pixel.
+// ---------------------------------------------------------------------------
+template <int DT>
+__device__ __forceinline__ float load_at(const void* p, int64_t i) {
+  if constexpr (DT == DT_F32) {
+    return ((const float*)p)[i];
+  } else if constexpr (DT == DT_BF16) {
+    return __uint_as_float((uint32_t)((const unsigned short*)p)[i] << 16);
+  } else {
+    return (float)((const _Float16*)p)[i];
+  }
+}
+
+// Forward map, or (FLIP) the stride-1 data gradient as the forward map of dY
+// with the rotated filter and padding FH-1-ph.
+template <int DT, bool FLIP>
+__global__ __launch_bounds__(256) void fwd_generic(GenericArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= a.total) return;
+  const int c = (int)(i % a.C);
+  int64_t p = i / a.C;
+  const int ow = (int)(p % a.OW);
+  p /= a.OW;
+  const int oh = (int)(p % a.OH);
+  const int64_t n = p / a.OH;
+  float s = 0.f;
+  for (int fh = 0; fh < a.FH; ++fh) {
+    const int ih = oh * a.SH - a.PH + fh;
+    if (ih < 0 || ih >= a.IH) continue;
+    const int fhe = FLIP ? a.FH - 1 - fh : fh;
+    for (int fw = 0; fw < a.FW; ++fw) {
+      const int iw = ow * a.SW - a.PW + fw;
+      if (iw < 0 || iw >= a.IW) continue;
+      const int fwe = FLIP ? a.FW - 1 - fw : fw;
+      s = fmaf(load_at<DT>(a.a, ((n * a.IH + ih) * a.IW + iw) * a.C + c),
+               load_at<DT>(a.b, ((int64_t)fhe * a.FW + fwe) * a.C + c), s);
+    }
+  }
+  a.out[i] = s;
+}
+
+// Data gradient for any stride: every (tap, output) pair whose window reads
+// input pixel (ih, iw).  IH/IW are the input (dX) dims, OH/OW the dY dims.
+template <int DT>
+__global__ __launch_bounds__(256) void dgrad_generic(GenericArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= a.total) return;
+  const int c = (int)(i % a.C);
+  int64_t p = i / a.C;
+  const int iw = (int)(p % a.IW);
+  p /= a.IW;
+  const int ih = (int)(p % a.IH);
+  const int64_t n = p / a.IH;
+  float s = 0.f;
+  for (int fh = 0; fh < a.FH; ++fh) {
+    const int th = ih + a.PH - fh;
+    if (th < 0 || th % a.SH) continue;
+    const int oh = th / a.SH;
+    if (oh >= a.OH) continue;
+    for (int fw = 0; fw < a.FW; ++fw) {
+      const int tw = iw + a.PW - fw;
+      if (tw < 0 || tw % a.SW) continue;
+      const int ow = tw / a.SW;
+      if (ow >= a.OW) continue;
+      s = fmaf(load_at<DT>(a.a, ((n * a.OH + oh) * a.OW + ow) * a.C + c),
+               load_at<DT>(a.b, ((int64_t)fh * a.FW + fw) * a.C + c), s);
+    }
+  }
+  a.out[i] = s;
+}
+
+// Filter gradient partials: work item (z, fh, fw, c), channel fastest; the
+// item sums X * dY over the rows of slice z.
+template <int DT>
+__global__ __launch_bounds__(256) void wgrad_generic(GenericArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= a.total) return;
+  const int c = (int)(i % a.C);
+  int64_t p = i / a.C;
+  const int fw = (int)(p % a.FW);
+  p /= a.FW;
+  const int fh = (int)(p % a.FH);
+  const int z = (int)(p / a.FH);
+  const int q0 = a.rows / a.Z, rem = a.rows % a.Z;
+  const int r0 = z * q0 + (z < rem ? z : rem);
+  const int r1 = r0 + q0 + (z < rem ? 1 : 0);
+  float s = 0.f;
+  for (int row = r0; row < r1; ++row) {
+    const int64_t n = row / a.OH;
+    const int oh = row - (int)n * a.OH;
+    const int ih = oh * a.SH - a.PH + fh;
+    if (ih < 0 || ih >= a.IH) continue;
+    for (int ow = 0; ow < a.OW; ++ow) {
+      const int iw = ow * a.SW - a.PW + fw;
+      if (iw < 0 || iw >= a.IW) continue;
+      s = fmaf(load_at<DT>(a.a, ((n * a.IH + ih) * a.IW + iw) * a.C + c),
+               load_at<DT>(a.b, ((n * a.OH + oh) * a.OW + ow) * a.C + c), s);
+    }
+  }
+  a.out[i] = s;
+}
+
+}  // namespace dwc

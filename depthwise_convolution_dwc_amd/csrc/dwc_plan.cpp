@@ -1,0 +1,392 @@
+// dwc_plan.cpp -- validation, kernel choice and grid sizes of libdwc.
+// Host-only: nothing here touches the GPU, so every error path can be
+// exercised on a machine without one.
+#include "dwc_plan.h"
+
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <algorithm>
+#include <cmath>
+
+namespace dwc {
+
+namespace {
+
+thread_local std::string g_last_error;
+
+constexpr int64_t kI32Max = 0x7fffffff;
+// Fill target of the filter-gradient split: waves in flight on 256 CUs at
+// about four waves per SIMD.
+constexpr int64_t kWgradTargetWaves = 4096;
+
+int elem_bytes(int dt) { return dt == DT_F32 ? 4 : 2; }
+
+bool direct_fw(int fw) {
+#define DWC_IS(F) if (fw == F) return true;
+  DWC_DIRECT_FW_LIST(DWC_IS)
+#undef DWC_IS
+  return false;
+}
+
+const char* dt_name(int dt) { return dt == DT_F32 ? "f32" : dt == DT_BF16 ? "bf16" : "f16"; }
+
+int fail(std::string* err, int code, const std::string& msg) {
+  if (err) *err = msg;
+  return code;
+}
+
+// Strip width (output columns per lane) of a forward-type launch or of a
+// filter-gradient unit: the instantiated width with the fewest idle columns
+// in the last strip, ties to the wider strip.
+int pick_strip(int64_t ow) {
+  const int cand[] = {14, 7};
+  int best = cand[0];
+  int64_t best_waste = -1;
+  for (int c : cand) {
+    const int64_t waste = (ow + c - 1) / c * c - ow;
+    if (best_waste < 0 || waste < best_waste) {
+      best = c;
+      best_waste = waste;
+    }
+  }
+  return best;
+}
+
+// Strip-width override for A/B timing: DWC_FWD_STRIP / DWC_WGRAD_STRIP set
+// to an instantiated width (7 or 14) replace the automatic choice.
+int strip_override(const char* var, int fallback) {
+  const char* v = getenv(var);
+  if (!v) return fallback;
+  const int w = atoi(v);
+  return (w == 7 || w == 14) ? w : fallback;
+}
+
+// Number of slices of the N*OH axis for the filter gradient (§5.1 splits
+// the accumulation axis into Z sub-problems whose sums are merged).  Z is
+// the largest value that (a) does not overfill the GPU (~1024 workgroups),
+// (b) leaves every workgroup at least one unit per wave, and (c) keeps the
+// partial sums it writes and reads back under ~15% of the kernel's own
+// estimated time.
+int pick_split(int64_t rows, int64_t per_slice_blocks, int64_t strips, int64_t m, double flops,
+               double bytes) {
+  const int64_t fill = (1024 + per_slice_blocks - 1) / per_slice_blocks;
+  const int64_t groups_per_wave_set = (4 + strips - 1) / strips;  // row groups for 4 units
+  const int64_t by_units = std::max<int64_t>(1, rows / (kWgradRows * groups_per_wave_set));
+  const double t_est = std::max(flops / 100e12, bytes / 5e12);
+  const double cap = 0.15 * t_est * 5e12 / (8.0 * (double)m);
+  int64_t z = std::min<int64_t>({fill, by_units, (int64_t)std::max(1.0, std::floor(cap))});
+  z = std::max<int64_t>(1, std::min(z, rows));
+  return (int)std::min<int64_t>(z, 65535);
+}
+
+}  // namespace
+
+void set_last_error(const std::string& msg) { g_last_error = msg; }
+
+int make_plan(const dwc_problem* p, int op, Plan* pl, std::string* err) {
+  if (!p) return fail(err, DWC_ERR_BAD_PARAM, "problem pointer is NULL");
+  if (op < DWC_OP_FWD || op > DWC_OP_BWD_FILTER)
+    return fail(err, DWC_ERR_BAD_PARAM, "unknown operation code");
+  if (p->n < 0 || p->h < 1 || p->w < 1 || p->c < 1)
+    return fail(err, DWC_ERR_BAD_PARAM, "need n >= 0 and h, w, c >= 1");
+  if (p->fh < 1 || p->fw < 1) return fail(err, DWC_ERR_BAD_PARAM, "need fh, fw >= 1");
+  if (p->stride_h < 1 || p->stride_w < 1)
+    return fail(err, DWC_ERR_BAD_PARAM, "need stride_h, stride_w >= 1");
+  if (p->pad_h < 0 || p->pad_w < 0) return fail(err, DWC_ERR_BAD_PARAM, "need pad_h, pad_w >= 0");
+  if (p->in_dtype < DWC_F32 || p->in_dtype > DWC_F16)
+    return fail(err, DWC_ERR_BAD_PARAM, "in_dtype must be DWC_F32, DWC_BF16 or DWC_F16");
+  if (p->out_dtype != DWC_F32)
+    return fail(err, DWC_ERR_UNSUPPORTED, "outputs are fp32 only (out_dtype must be DWC_F32)");
+  if (p->algo < DWC_ALGO_AUTO || p->algo > DWC_ALGO_GENERIC)
+    return fail(err, DWC_ERR_BAD_PARAM, "unknown algo");
+  if (p->wgrad_split < 0) return fail(err, DWC_ERR_BAD_PARAM, "wgrad_split must be >= 0");
+  const int64_t a = p->h + 2 * (int64_t)p->pad_h - p->fh;
+  const int64_t b = p->w + 2 * (int64_t)p->pad_w - p->fw;
+  if (a < 0 || b < 0)
+    return fail(err, DWC_ERR_BAD_PARAM, "filter larger than the padded input (OH or OW < 1)");
+  const int64_t oh = a / p->stride_h + 1, ow = b / p->stride_w + 1;
+
+  const int dt = p->in_dtype;
+  const int64_t eb = elem_bytes(dt);
+  // 32-bit buffer offsets: one image of every tensor, and the filter, must
+  // stay below 2 GiB; counts of rows and work items must fit in int32.
+  if (p->h * p->w * p->c * 4 > kI32Max || oh * ow * p->c * 4 > kI32Max ||
+      (int64_t)p->fh * p->fw * p->c * 4 > kI32Max || p->n * std::max(oh, p->h) > kI32Max ||
+      p->c > kI32Max / 4)
+    return fail(err, DWC_ERR_UNSUPPORTED, "tensor too large for 32-bit per-image offsets");
+
+  Plan q;
+  q.op = op;
+  q.dt = dt;
+  q.oh = oh;
+  q.ow = ow;
+  q.empty = p->n == 0;
+  const int C = (int)p->c;
+  const int cblocks = (C + kWaveChannels - 1) / kWaveChannels;
+
+  // Direct kernels: instantiated filter width, equal strides of 1 or 2 (the
+  // data gradient: stride 1, where it is a forward map with the filter
+  // turned by 180 degrees).
+  const bool square_stride = p->stride_h == p->stride_w && p->stride_w <= 2;
+  bool can_direct = direct_fw(p->fw) && square_stride;
+  if (op == DWC_OP_BWD_DATA) can_direct = can_direct && p->stride_w == 1;
+  if (p->algo == DWC_ALGO_DIRECT && !can_direct)
+    return fail(err, DWC_ERR_UNSUPPORTED,
+                "no direct kernel for this filter width / stride (use DWC_ALGO_AUTO)");
+  const bool direct = p->algo != DWC_ALGO_GENERIC && can_direct;
+  q.kind = direct ? PLAN_DIRECT : PLAN_GENERIC;
+
+  if (op == DWC_OP_FWD || op == DWC_OP_BWD_DATA) {
+    // The data gradient runs the forward map on dY with the filter turned
+    // by 180 degrees and padding FH-1-pad (§5.1); its "input" is dY.
+    const bool bwd = op == DWC_OP_BWD_DATA;
+    FwdArgs f{};
+    f.N = (int)p->n;
+    f.C = C;
+    f.FH = p->fh;
+    f.FW = p->fw;
+    f.IH = bwd ? (int)oh : (int)p->h;
+    f.IW = bwd ? (int)ow : (int)p->w;
+    f.OH = bwd ? (int)p->h : (int)oh;
+    f.OW = bwd ? (int)p->w : (int)ow;
+    f.SH = p->stride_h;
+    f.SW = p->stride_w;
+    f.PH = bwd ? p->fh - 1 - p->pad_h : p->pad_h;
+    f.PW = bwd ? p->fw - 1 - p->pad_w : p->pad_w;
+    if (direct) {
+      q.flip = bwd;
+      q.tmw = strip_override("DWC_FWD_STRIP", pick_strip(f.OW));
+      f.tiles_w = (f.OW + q.tmw - 1) / q.tmw;
+      f.tiles_h = (f.OH + kFwdRows - 1) / kFwdRows;
+      f.cblocks = cblocks;
+      const int64_t items = (int64_t)f.N * cblocks * f.tiles_h * f.tiles_w;
+      if (items > kI32Max - kWavesPerBlock)
+        return fail(err, DWC_ERR_UNSUPPORTED, "too many work items for one launch");
+      f.num_items = (int)items;
+      q.blocks = (int)((items + kWavesPerBlock - 1) / kWavesPerBlock);
+      q.fa = f;
+    } else {
+      GenericArgs g{};
+      g.N = (int)p->n;
+      g.C = C;
+      g.FH = p->fh;
+      g.FW = p->fw;
+      g.SH = p->stride_h;
+      g.SW = p->stride_w;
+      if (!bwd) {
+        g.IH = (int)p->h; g.IW = (int)p->w; g.OH = (int)oh; g.OW = (int)ow;
+        g.PH = p->pad_h; g.PW = p->pad_w;
+        q.gen_kind = 0;  // GEN_FWD
+        g.total = p->n * oh * ow * p->c;
+      } else {
+        // gather form for any stride; IH/IW = dX dims, OH/OW = dY dims
+        g.IH = (int)p->h; g.IW = (int)p->w; g.OH = (int)oh; g.OW = (int)ow;
+        g.PH = p->pad_h; g.PW = p->pad_w;
+        q.gen_kind = 2;  // GEN_DGRAD
+        g.total = p->n * p->h * p->w * p->c;
+      }
+      q.ga = g;
+    }
+  } else {
+    const int64_t rows = p->n * oh;
+    const int64_t m = (int64_t)p->fh * p->fw * p->c;
+    const double flops = 2.0 * (double)p->n * oh * ow * p->c * p->fh * p->fw;
+    const double bytes = (double)eb * ((double)p->n * p->h * p->w * p->c + (double)rows * ow * p->c);
+    if (p->wgrad_split > 0 && rows > 0 && p->wgrad_split > rows)
+      return fail(err, DWC_ERR_BAD_PARAM, "wgrad_split larger than N*OH");
+    if (direct) {
+      // 7-wide strips keep the dY block, the input strip and the taps of a
+      // filter-row chunk within ~128 registers.
+      q.tj = strip_override("DWC_WGRAD_STRIP", 7);
+      q.tfh = filter_row_chunk(p->fw);
+      WgradArgs w{};
+      w.N = (int)p->n; w.IH = (int)p->h; w.IW = (int)p->w; w.C = C;
+      w.OH = (int)oh; w.OW = (int)ow;
+      w.FH = p->fh; w.FW = p->fw; w.SH = p->stride_h; w.SW = p->stride_w;
+      w.PH = p->pad_h; w.PW = p->pad_w;
+      w.cblocks = cblocks;
+      w.fh_tiles = (p->fh + q.tfh - 1) / q.tfh;
+      w.rows = (int)rows;
+      const int64_t per_slice = (int64_t)cblocks * w.fh_tiles;
+      const int64_t strips = (ow + q.tj - 1) / q.tj;
+      q.z = rows == 0 ? 1
+                      : (p->wgrad_split > 0 ? p->wgrad_split
+                                            : pick_split(rows, per_slice, strips, m, flops, bytes));
+      w.Z = q.z;
+      const int64_t items = (int64_t)q.z * per_slice;  // one workgroup each
+      if (items > kI32Max)
+        return fail(err, DWC_ERR_UNSUPPORTED, "too many work items for one launch");
+      w.num_items = (int)items;
+      q.blocks = (int)items;
+      q.wa = w;
+    } else {
+      GenericArgs g{};
+      g.N = (int)p->n; g.IH = (int)p->h; g.IW = (int)p->w; g.C = C;
+      g.OH = (int)oh; g.OW = (int)ow;
+      g.FH = p->fh; g.FW = p->fw; g.SH = p->stride_h; g.SW = p->stride_w;
+      g.PH = p->pad_h; g.PW = p->pad_w;
+      g.rows = (int)rows;
+      // one lane per (slice, tap, channel): enough slices for ~512K lanes
+      const int64_t fill = std::max<int64_t>(1, (524288 + m - 1) / m);
+      q.z = rows == 0 ? 1
+                      : (p->wgrad_split > 0 ? p->wgrad_split
+                                            : (int)std::min<int64_t>({fill, rows, 4096}));
+      g.Z = q.z;
+      g.total = (int64_t)q.z * m;
+      q.gen_kind = 3;  // GEN_WGRAD
+      q.ga = g;
+    }
+    q.ws_bytes = q.z > 1 ? (size_t)q.z * (size_t)m * 4 : 0;
+    q.ws_bytes = (q.ws_bytes + 255) / 256 * 256;
+  }
+  *pl = q;
+  return DWC_OK;
+}
+
+namespace {
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+}  // namespace
+
+int check_pointers(const dwc_problem* p, const Plan& pl, const void* in0, const void* in1,
+                   const void* out, const void* ws, size_t ws_bytes, std::string* err) {
+  const size_t eb = elem_bytes(pl.dt);
+  const size_t nx = (size_t)p->n * p->h * p->w * p->c;
+  const size_t ny = (size_t)p->n * pl.oh * pl.ow * p->c;
+  const size_t nw = (size_t)p->fh * p->fw * p->c;
+  size_t in0_bytes = 0, in1_bytes = 0, out_bytes = 0;
+  if (pl.op == DWC_OP_FWD) {
+    in0_bytes = nx * eb; in1_bytes = nw * eb; out_bytes = ny * 4;
+  } else if (pl.op == DWC_OP_BWD_DATA) {
+    in0_bytes = ny * eb; in1_bytes = nw * eb; out_bytes = nx * 4;
+  } else {
+    in0_bytes = nx * eb; in1_bytes = ny * eb; out_bytes = nw * 4;
+  }
+  const bool need_inputs = !pl.empty;
+  // A tensor with no elements may have a NULL address.
+  if (!out && out_bytes > 0) return fail(err, DWC_ERR_BAD_PARAM, "output pointer is NULL");
+  if (need_inputs && (!in0 || !in1)) return fail(err, DWC_ERR_BAD_PARAM, "input pointer is NULL");
+  if (((uintptr_t)out) % 4) return fail(err, DWC_ERR_MISALIGNED, "output not 4-byte aligned");
+  if (need_inputs && ((((uintptr_t)in0) % eb) || (((uintptr_t)in1) % eb)))
+    return fail(err, DWC_ERR_MISALIGNED, "input not aligned to its element size");
+  if (need_inputs &&
+      (overlap(out, out_bytes, in0, in0_bytes) || overlap(out, out_bytes, in1, in1_bytes)))
+    return fail(err, DWC_ERR_ALIAS, "output overlaps an input");
+  if (pl.op == DWC_OP_BWD_FILTER && pl.ws_bytes > 0 && !pl.empty) {
+    if (!ws || ws_bytes < pl.ws_bytes)
+      return fail(err, DWC_ERR_WORKSPACE, "workspace missing or smaller than required (" +
+                                              std::to_string(pl.ws_bytes) + " bytes)");
+    if (((uintptr_t)ws) % 4) return fail(err, DWC_ERR_MISALIGNED, "workspace not 4-byte aligned");
+    if (overlap(ws, pl.ws_bytes, out, out_bytes) || overlap(ws, pl.ws_bytes, in0, in0_bytes) ||
+        overlap(ws, pl.ws_bytes, in1, in1_bytes))
+      return fail(err, DWC_ERR_ALIAS, "workspace overlaps a tensor");
+  }
+  return DWC_OK;
+}
+
+std::string describe(const Plan& pl) {
+  static const char* ops[] = {"fwd", "bwd_data", "bwd_filter"};
+  char buf[512];
+  if (pl.kind == PLAN_DIRECT && pl.op != DWC_OP_BWD_FILTER) {
+    snprintf(buf, sizeof buf,
+             "%s direct dt=%s fw=%d sw=%d flip=%d tmw=%d rows=%d tiles_w=%d tiles_h=%d "
+             "cblocks=%d items=%d blocks=%d",
+             ops[pl.op], dt_name(pl.dt), pl.fa.FW, pl.fa.SW, (int)pl.flip, pl.tmw, kFwdRows,
+             pl.fa.tiles_w, pl.fa.tiles_h, pl.fa.cblocks, pl.fa.num_items, pl.blocks);
+  } else if (pl.kind == PLAN_DIRECT) {
+    snprintf(buf, sizeof buf,
+             "%s direct dt=%s fw=%d sw=%d tj=%d tfh=%d fh_tiles=%d cblocks=%d z=%d items=%d "
+             "blocks=%d ws_bytes=%zu",
+             ops[pl.op], dt_name(pl.dt), pl.wa.FW, pl.wa.SW, pl.tj, pl.tfh, pl.wa.fh_tiles,
+             pl.wa.cblocks, pl.z, pl.wa.num_items, pl.blocks, pl.ws_bytes);
+  } else {
+    snprintf(buf, sizeof buf, "%s generic dt=%s kind=%d z=%d total=%lld ws_bytes=%zu",
+             ops[pl.op], dt_name(pl.dt), pl.gen_kind, pl.z, (long long)pl.ga.total, pl.ws_bytes);
+  }
+  return buf;
+}
+
+}  // namespace dwc
+
+using namespace dwc;
+
+extern "C" {
+
+int dwc_version(void) { return DWC_VERSION; }
+
+const char* dwc_status_string(int s) {
+  switch (s) {
+    case DWC_OK: return "ok";
+    case DWC_ERR_BAD_PARAM: return "bad parameter";
+    case DWC_ERR_UNSUPPORTED: return "unsupported";
+    case DWC_ERR_MISALIGNED: return "misaligned pointer";
+    case DWC_ERR_WORKSPACE: return "workspace too small";
+    case DWC_ERR_ALIAS: return "output aliases an input";
+    case DWC_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* dwc_last_error(void) { return g_last_error.c_str(); }
+
+int dwc_output_dims(const dwc_problem* p, int64_t* oh, int64_t* ow) {
+  Plan pl;
+  std::string err;
+  const int st = make_plan(p, DWC_OP_FWD, &pl, &err);
+  if (st) {
+    set_last_error(err);
+    return st;
+  }
+  if (oh) *oh = pl.oh;
+  if (ow) *ow = pl.ow;
+  return DWC_OK;
+}
+
+int dwc_check(const dwc_problem* p, int op) {
+  Plan pl;
+  std::string err;
+  const int st = make_plan(p, op, &pl, &err);
+  if (st) set_last_error(err);
+  return st;
+}
+
+int dwc_plan_describe(const dwc_problem* p, int op, char* buf, size_t len) {
+  Plan pl;
+  std::string err;
+  const int st = make_plan(p, op, &pl, &err);
+  if (st) {
+    set_last_error(err);
+    return st;
+  }
+  if (buf && len) {
+    const std::string s = describe(pl);
+    const size_t k = std::min(len - 1, s.size());
+    s.copy(buf, k);
+    buf[k] = 0;
+  }
+  return DWC_OK;
+}
+
+int dwc_bwd_filter_workspace_size(const dwc_problem* p, size_t* bytes) {
+  Plan pl;
+  std::string err;
+  const int st = make_plan(p, DWC_OP_BWD_FILTER, &pl, &err);
+  if (st) {
+    set_last_error(err);
+    return st;
+  }
+  if (!bytes) {
+    set_last_error("bytes pointer is NULL");
+    return DWC_ERR_BAD_PARAM;
+  }
+  *bytes = pl.empty ? 0 : pl.ws_bytes;
+  return DWC_OK;
+}
+
+}  // extern "C"

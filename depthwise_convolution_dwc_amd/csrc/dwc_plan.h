@@ -1,0 +1,53 @@
+// dwc_plan.h -- host-side validation and launch planning (no HIP calls).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "../../include/dwc.h"
+#include "dwc_geom.h"
+
+namespace dwc {
+
+enum PlanKind { PLAN_NONE = 0, PLAN_DIRECT = 1, PLAN_GENERIC = 2 };
+
+struct Plan {
+  int op = 0;
+  int dt = 0;
+  int kind = PLAN_NONE;
+  int64_t oh = 0, ow = 0;
+  bool empty = false;  // n == 0
+
+  // forward-type direct kernel (forward, stride-1 data gradient)
+  int tmw = 0;
+  bool flip = false;
+  FwdArgs fa{};
+  int blocks = 0;
+
+  // filter-gradient direct kernel
+  int tj = 0, tfh = 0;
+  WgradArgs wa{};
+  int z = 1;
+  size_t ws_bytes = 0;  // 0: slice partials are written straight to dW
+
+  // generic kernels
+  int gen_kind = 0;
+  GenericArgs ga{};
+};
+
+// Validates `p` for `op` and fills `pl`.  Returns a dwc_status; on error
+// `err` holds the message.
+int make_plan(const dwc_problem* p, int op, Plan* pl, std::string* err);
+
+// Checks the tensor pointers of a call (null, alignment, overlap of the
+// output with the inputs, workspace).  No GPU access.
+int check_pointers(const dwc_problem* p, const Plan& pl, const void* in0, const void* in1,
+                   const void* out, const void* ws, size_t ws_bytes, std::string* err);
+
+std::string describe(const Plan& pl);
+
+void set_last_error(const std::string& msg);
+
+}  // namespace dwc

@@ -1,0 +1,90 @@
+// inst_direct.hip -- instantiations of the direct kernels for one operand
+// dtype.  Compiled once per dtype with -DDWC_INST_DT=<0|1|2>.
+#include "dwc_kernels.h"
+#include "dwc_launch.h"
+
+#ifndef DWC_INST_DT
+#error "DWC_INST_DT must be defined"
+#endif
+
+#define DWC_CAT2(a, b) a##b
+#define DWC_CAT(a, b) DWC_CAT2(a, b)
+
+namespace dwc {
+namespace {
+
+constexpr int kDt = DWC_INST_DT;
+
+template <int S, int TMW, bool FLIP>
+hipError_t fwd_by_fw(int fw, const FwdArgs& a, int blocks, hipStream_t s) {
+  switch (fw) {
+#define DWC_CASE(F)                                                                     \
+  case F:                                                                               \
+    hipLaunchKernelGGL((fwd_rows<kDt, F, S, TMW, FLIP>), dim3(blocks),                  \
+                       dim3(kBlockThreads), 0, s, a);                                   \
+    return hipGetLastError();
+    DWC_DIRECT_FW_LIST(DWC_CASE)
+#undef DWC_CASE
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int S, bool FLIP>
+hipError_t fwd_by_tmw(int fw, int tmw, const FwdArgs& a, int blocks, hipStream_t s) {
+  switch (tmw) {
+#define DWC_CASE(T) \
+  case T:           \
+    return fwd_by_fw<S, T, FLIP>(fw, a, blocks, s);
+    DWC_FWD_TMW_LIST(DWC_CASE)
+#undef DWC_CASE
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int S, int TJ>
+hipError_t wgrad_by_fw(int fw, const WgradArgs& a, int blocks, hipStream_t s) {
+  switch (fw) {
+#define DWC_CASE(F)                                                                     \
+  case F:                                                                               \
+    hipLaunchKernelGGL((wgrad_rows<kDt, F, S, TJ>), dim3(blocks), dim3(kBlockThreads),  \
+                       0, s, a);                                                        \
+    return hipGetLastError();
+    DWC_DIRECT_FW_LIST(DWC_CASE)
+#undef DWC_CASE
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int S>
+hipError_t wgrad_by_tj(int fw, int tj, const WgradArgs& a, int blocks, hipStream_t s) {
+  switch (tj) {
+#define DWC_CASE(T) \
+  case T:           \
+    return wgrad_by_fw<S, T>(fw, a, blocks, s);
+    DWC_WGRAD_TJ_LIST(DWC_CASE)
+#undef DWC_CASE
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+// s: the stride of both spatial axes (1 or 2; the data gradient only 1).
+hipError_t DWC_CAT(launch_fwd_direct_dt, DWC_INST_DT)(int fw, int s, int tmw, bool flip,
+                                                      const FwdArgs& a, int blocks,
+                                                      hipStream_t st) {
+  if (s == 1) return flip ? fwd_by_tmw<1, true>(fw, tmw, a, blocks, st)
+                          : fwd_by_tmw<1, false>(fw, tmw, a, blocks, st);
+  if (s == 2 && !flip) return fwd_by_tmw<2, false>(fw, tmw, a, blocks, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t DWC_CAT(launch_wgrad_direct_dt, DWC_INST_DT)(int fw, int s, int tj,
+                                                        const WgradArgs& a, int blocks,
+                                                        hipStream_t st) {
+  if (s == 1) return wgrad_by_tj<1>(fw, tj, a, blocks, st);
+  if (s == 2) return wgrad_by_tj<2>(fw, tj, a, blocks, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dwc

@@ -1,0 +1,80 @@
+// inst_generic.hip -- generic kernels (any filter size / stride) and the
+// deterministic reduction of filter-gradient partials.
+#include "dwc_kernels.h"
+#include "dwc_launch.h"
+
+namespace dwc {
+
+// Sum of the Z slice partials, deterministic.  A block of 16 waves owns 64
+// consecutive outputs (one per lane); wave w adds the contiguous slice range
+// [w*Z/16, (w+1)*Z/16) in slice order, then wave 0 adds the 16 wave sums in
+// wave order.  With Z = 0 it writes zeros (the filter gradient of an empty
+// batch).
+constexpr int kReduceWaves = 16;
+
+__global__ __launch_bounds__(64 * kReduceWaves) void reduce_partials(ReduceArgs a) {
+  __shared__ float part[kReduceWaves][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t i = (int64_t)blockIdx.x * 64 + lane;
+  const int z0 = (int)((int64_t)a.Z * wave / kReduceWaves);
+  const int z1 = (int)((int64_t)a.Z * (wave + 1) / kReduceWaves);
+  float s = 0.f;
+  if (i < a.M) {
+    const float* p = a.ws + i;
+    for (int z = z0; z < z1; ++z) s += p[(int64_t)z * a.M];
+  }
+  part[wave][lane] = s;
+  __syncthreads();
+  if (wave == 0 && i < a.M) {
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < kReduceWaves; ++w) t += part[w][lane];
+    a.out[i] = t;
+  }
+}
+
+namespace {
+
+template <int DT>
+hipError_t generic_dt(int kind, const GenericArgs& a, hipStream_t s) {
+  const int64_t blocks = (a.total + 255) / 256;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  switch (kind) {
+    case GEN_FWD:
+      hipLaunchKernelGGL((fwd_generic<DT, false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+      break;
+    case GEN_FWD_FLIP:
+      hipLaunchKernelGGL((fwd_generic<DT, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+      break;
+    case GEN_DGRAD:
+      hipLaunchKernelGGL((dgrad_generic<DT>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+      break;
+    case GEN_WGRAD:
+      hipLaunchKernelGGL((wgrad_generic<DT>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_generic(int kind, int dt, const GenericArgs& a, hipStream_t s) {
+  switch (dt) {
+    case DT_F32: return generic_dt<DT_F32>(kind, a, s);
+    case DT_BF16: return generic_dt<DT_BF16>(kind, a, s);
+    case DT_F16: return generic_dt<DT_F16>(kind, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s) {
+  const int64_t blocks = (a.M + 63) / 64;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(reduce_partials, dim3((unsigned)blocks), dim3(64 * kReduceWaves), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace dwc

@@ -1,0 +1,157 @@
+/*
+ * dwc.h -- C ABI of libdwc, depthwise convolution (DWC) for AMD MI355X
+ * (gfx950).
+ *
+ * The operations are those of "Flash-DWC: Making Depthwise Convolution
+ * Compute-Efficient on GPUs" (ACM TACO):
+ *   - forward convolution (FC), §2.1: every output pixel of channel c is the
+ *     FH x FW inner product of its input patch with channel c's own filter
+ *     (IC = OC = C), cross-correlation order (no filter flip);
+ *   - backward data convolution (BDC), §5.1: the input gradient dX, i.e. the
+ *     adjoint of the forward map in X (for stride 1: the forward map of dY
+ *     with the filter turned by 180 degrees);
+ *   - backward filter convolution (BFC), §5.1: the filter gradient
+ *     dW[fh,fw,c] = sum over n,oh,ow of Xpad[n, oh*sh-ph+fh, ow*sw-pw+fw, c]
+ *     * dY[n,oh,ow,c].
+ * Padding is implicit zeros (§4.4) and symmetric; the output size is
+ * OH = floor((H + 2*pad_h - FH) / stride_h) + 1 (likewise OW).
+ *
+ * Layouts (§2.3, unified channel-last layout), all dense and row-major:
+ *   X, dX : N  x H  x W  x C
+ *   Y, dY : N  x OH x OW x C
+ *   W, dW : FH x FW x C
+ *
+ * Precision: operands X, W, dY are fp32, bf16 or fp16 (in_dtype); every sum
+ * is accumulated in fp32 and every output (Y, dX, dW) is fp32.  §4.1 argues
+ * that fp32 accumulation is required for half-precision operands.
+ *
+ * Ownership and threading: every pointer is a device pointer owned by the
+ * caller, who allocates all tensors and the workspace.  The library keeps no
+ * state between calls except a per-process cache of device properties.
+ * Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL is
+ * the null stream); the library never synchronises.  Every call is
+ * re-entrant.
+ *
+ * Errors: a bad argument is reported synchronously, before anything is
+ * launched, and leaves every output untouched.  DWC_ERR_HIP means a launch
+ * failed; faults inside a kernel surface at the caller's next
+ * synchronisation.  dwc_last_error() returns a message for the calling
+ * thread's last failed call.
+ */
+#ifndef DWC_H
+#define DWC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DWC_VERSION 100 /* 1.0.0 */
+
+typedef enum {
+    DWC_F32 = 0,
+    DWC_BF16 = 1,
+    DWC_F16 = 2
+} dwc_dtype;
+
+typedef enum {
+    DWC_ALGO_AUTO = 0,   /* library's choice                                */
+    DWC_ALGO_DIRECT = 1, /* register-window vector kernels                  */
+    DWC_ALGO_GENERIC = 2 /* one output per lane; any filter size or stride  */
+} dwc_algo;
+
+typedef enum {
+    DWC_OK = 0,
+    DWC_ERR_BAD_PARAM = 1,   /* sizes, strides, pads or dtypes invalid         */
+    DWC_ERR_UNSUPPORTED = 2, /* valid request this build does not implement     */
+    DWC_ERR_MISALIGNED = 3,  /* pointer not aligned to its element size         */
+    DWC_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required      */
+    DWC_ERR_ALIAS = 5,       /* an output overlaps an input                     */
+    DWC_ERR_HIP = 6          /* a HIP runtime call or kernel launch failed      */
+} dwc_status;
+
+/* One convolution problem.  n, h, w, c describe X (input of the forward
+ * map).  All fields are plain integers so the struct has a fixed layout. */
+typedef struct {
+    int64_t n, h, w, c;         /* X: N x H x W x C, n >= 0, h, w, c >= 1   */
+    int32_t fh, fw;             /* filter FH x FW, >= 1                     */
+    int32_t stride_h, stride_w; /* >= 1                                     */
+    int32_t pad_h, pad_w;       /* zero padding on both sides, >= 0         */
+    int32_t in_dtype;           /* dwc_dtype of X, W, dY                    */
+    int32_t out_dtype;          /* dwc_dtype of Y, dX, dW: must be DWC_F32  */
+    int32_t algo;               /* dwc_algo                                 */
+    int32_t wgrad_split;        /* filter gradient: number of slices of the
+                                   N*OH accumulation axis; 0 = automatic    */
+} dwc_problem;
+
+/* Version number (DWC_VERSION of the built library). */
+int dwc_version(void);
+
+/* Short text for a status code. */
+const char* dwc_status_string(int status);
+
+/* Message describing the calling thread's last failed call ("" if none). */
+const char* dwc_last_error(void);
+
+/* OH and OW of a problem (the formula above).  Host only, no GPU needed.
+ * Returns DWC_ERR_BAD_PARAM if the filter does not fit the padded input. */
+int dwc_output_dims(const dwc_problem* p, int64_t* oh, int64_t* ow);
+
+/* Operation codes for dwc_check and dwc_plan_describe. */
+#define DWC_OP_FWD 0
+#define DWC_OP_BWD_DATA 1
+#define DWC_OP_BWD_FILTER 2
+
+/* Validate a problem for one operation without touching the GPU.  Returns
+ * the status the compute call would return for argument errors. */
+int dwc_check(const dwc_problem* p, int op);
+
+/* Write a one-line description of the kernels and grid the library would
+ * launch for `op` into buf (NUL-terminated, truncated to len).  Host only. */
+int dwc_plan_describe(const dwc_problem* p, int op, char* buf, size_t len);
+
+/* Forward convolution (FC, §2.1 / Fig. 1): y = DWC(x, w).
+ *   x : N x H x W x C of in_dtype          (read)
+ *   w : FH x FW x C of in_dtype            (read)
+ *   y : N x OH x OW x C fp32               (overwritten)
+ * Pointers must be aligned to their element size and y must not overlap x
+ * or w.  n == 0 is a no-op. */
+int dwc_fwd(const dwc_problem* p, const void* x, const void* w, void* y,
+            void* stream);
+
+/* Backward data convolution (BDC, §5.1): dx = adjoint of the forward map
+ * applied to dy.
+ *   dy : N x OH x OW x C of in_dtype       (read)
+ *   w  : FH x FW x C of in_dtype           (read)
+ *   dx : N x H x W x C fp32                (overwritten; pixels no window
+ *                                           reads get 0)
+ * Any stride is accepted; stride 1 runs the rotated-filter forward kernels
+ * the section describes, other strides a gather kernel. */
+int dwc_bwd_data(const dwc_problem* p, const void* dy, const void* w,
+                 void* dx, void* stream);
+
+/* Bytes of workspace dwc_bwd_filter needs for this problem (may be 0). */
+int dwc_bwd_filter_workspace_size(const dwc_problem* p, size_t* bytes);
+
+/* Backward filter convolution (BFC, §5.1): dw = sum over the batch.
+ *   x  : N x H x W x C of in_dtype         (read)
+ *   dy : N x OH x OW x C of in_dtype       (read)
+ *   dw : FH x FW x C fp32                  (overwritten, never accumulated)
+ *   workspace : device memory of at least
+ *               dwc_bwd_filter_workspace_size() bytes, 256-byte aligned,
+ *               owned by the caller; its contents are scratch.
+ * The N*OH accumulation axis is split into slices whose partial sums are
+ * added in a fixed order (the split of §5.1, reduced deterministically
+ * instead of with atomics), so results are bitwise reproducible for a given
+ * problem and wgrad_split.  n == 0 writes dw = 0. */
+int dwc_bwd_filter(const dwc_problem* p, const void* x, const void* dy,
+                   void* dw, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DWC_H */

@@ -112,19 +112,27 @@ int dwc_oracle_fwd(int64_t n, int64_t ih, int64_t iw, int64_t c, int64_t fh,
     return 0;
 }
 
+/* Channels per OpenMP work item in the two gradients. */
+#define CBLK 16
+
 /* data gradient: the adjoint of the forward map, written as the scatter of
  * every (output pixel, tap) product onto the input pixel it came from.
- * Threads own whole images, so no two threads touch the same dX element. */
+ * A thread owns one image and one block of channels, so no two threads touch
+ * the same dX element. */
 int dwc_oracle_bwd_data(int64_t n, int64_t ih, int64_t iw, int64_t c,
                         int64_t fh, int64_t fw, int64_t sh, int64_t sw,
                         int64_t ph, int64_t pw, const double* dy,
                         const double* w, double* dx) {
     dims_t d;
     if (make_dims(&d, n, ih, iw, c, fh, fw, sh, sw, ph, pw)) return -1;
+    int64_t nblk = (d.c + CBLK - 1) / CBLK;
 #pragma omp parallel for schedule(dynamic, 1)
-    for (int64_t nn = 0; nn < d.n; ++nn) {
-        double* img = &XAT(&d, dx, nn, 0, 0, 0);
-        memset(img, 0, sizeof(double) * (size_t)(d.ih * d.iw * d.c));
+    for (int64_t t = 0; t < d.n * nblk; ++t) {
+        int64_t nn = t / nblk, c0 = (t % nblk) * CBLK;
+        int64_t c1 = c0 + CBLK < d.c ? c0 + CBLK : d.c;
+        for (int64_t h = 0; h < d.ih; ++h)
+            for (int64_t ww = 0; ww < d.iw; ++ww)
+                for (int64_t cc = c0; cc < c1; ++cc) XAT(&d, dx, nn, h, ww, cc) = 0.0;
         for (int64_t oh = 0; oh < d.oh; ++oh)
             for (int64_t ow = 0; ow < d.ow; ++ow)
                 for (int64_t kh = 0; kh < d.fh; ++kh) {
@@ -136,24 +144,29 @@ int dwc_oracle_bwd_data(int64_t n, int64_t ih, int64_t iw, int64_t c,
                         double* xp = &XAT(&d, dx, nn, h, ww, 0);
                         const double* gp = &YAT(&d, dy, nn, oh, ow, 0);
                         const double* wp = &WAT(&d, w, kh, kw, 0);
-                        for (int64_t cc = 0; cc < d.c; ++cc) xp[cc] += gp[cc] * wp[cc];
+                        for (int64_t cc = c0; cc < c1; ++cc) xp[cc] += gp[cc] * wp[cc];
                     }
                 }
     }
     return 0;
 }
 
-/* filter gradient: one filter row per thread, summed over the whole batch. */
+/* filter gradient: a thread owns one filter row and one block of channels
+ * and sums over the whole batch. */
 int dwc_oracle_bwd_filter(int64_t n, int64_t ih, int64_t iw, int64_t c,
                           int64_t fh, int64_t fw, int64_t sh, int64_t sw,
                           int64_t ph, int64_t pw, const double* x,
                           const double* dy, double* dw) {
     dims_t d;
     if (make_dims(&d, n, ih, iw, c, fh, fw, sh, sw, ph, pw)) return -1;
+    int64_t nblk = (d.c + CBLK - 1) / CBLK;
 #pragma omp parallel for schedule(dynamic, 1)
-    for (int64_t kh = 0; kh < d.fh; ++kh) {
+    for (int64_t t = 0; t < d.fh * nblk; ++t) {
+        int64_t kh = t / nblk, c0 = (t % nblk) * CBLK;
+        int64_t c1 = c0 + CBLK < d.c ? c0 + CBLK : d.c;
         double* acc = &WAT(&d, dw, kh, 0, 0);
-        memset(acc, 0, sizeof(double) * (size_t)(d.fw * d.c));
+        for (int64_t kw = 0; kw < d.fw; ++kw)
+            for (int64_t cc = c0; cc < c1; ++cc) acc[kw * d.c + cc] = 0.0;
         for (int64_t nn = 0; nn < d.n; ++nn)
             for (int64_t oh = 0; oh < d.oh; ++oh) {
                 int64_t h = oh * d.sh - d.ph + kh;
@@ -165,7 +178,7 @@ int dwc_oracle_bwd_filter(int64_t n, int64_t ih, int64_t iw, int64_t c,
                         const double* xp = &XAT(&d, x, nn, h, ww, 0);
                         const double* gp = &YAT(&d, dy, nn, oh, ow, 0);
                         double* ap = &acc[kw * d.c];
-                        for (int64_t cc = 0; cc < d.c; ++cc) ap[cc] += xp[cc] * gp[cc];
+                        for (int64_t cc = c0; cc < c1; ++cc) ap[cc] += xp[cc] * gp[cc];
                     }
             }
     }

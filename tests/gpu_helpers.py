@@ -1,0 +1,59 @@
+"""Helpers for the GPU parity tests: upload seeded inputs, compare with the
+oracle by relative L2 error."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import depthwise_convolution_dwc_amd as dwc
+from dwc_inputs import Operand
+
+# Tolerances on max relative L2 error per tensor: fp32 operands 1e-5;
+# bf16/fp16 operands with fp32 accumulation 3e-3.
+TOL = {"f32": 1e-5, "bf16": 3e-3, "f16": 3e-3}
+
+
+def to_device(op: Operand, device="cuda") -> torch.Tensor:
+    if op.dtype == "f32":
+        return torch.from_numpy(op.stored).to(device)
+    if op.dtype == "f16":
+        return torch.from_numpy(op.stored).to(device)
+    # bf16 bits travel as int16 and are reinterpreted on the device
+    return torch.from_numpy(op.stored.view(np.int16)).to(device).view(torch.bfloat16)
+
+
+def rel_l2(got: np.ndarray, want: np.ndarray) -> float:
+    got = np.asarray(got, dtype=np.float64).reshape(-1)
+    want = np.asarray(want, dtype=np.float64).reshape(-1)
+    den = np.linalg.norm(want)
+    num = np.linalg.norm(got - want)
+    if den == 0.0:
+        return float(num)
+    return float(num / den)
+
+
+def sample_index(shape, k, rng) -> np.ndarray:
+    """k random multi-indices into ``shape`` (rows of an int64 array), always
+    including the first and last element."""
+    k = min(k, int(np.prod(shape)))
+    idx = np.stack([rng.integers(0, s, size=k) for s in shape], axis=1)
+    idx[0] = 0
+    idx[-1] = np.asarray(shape) - 1
+    return idx.astype(np.int64)
+
+
+def gather(t: torch.Tensor, idx: np.ndarray) -> np.ndarray:
+    it = torch.from_numpy(idx).to(t.device)
+    return t[tuple(it[:, d] for d in range(idx.shape[1]))].double().cpu().numpy()
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+def log(*a):
+    print(*a, flush=True)
+
+
+__all__ = ["TOL", "to_device", "rel_l2", "sample_index", "gather", "sync", "log", "dwc"]

@@ -1,0 +1,153 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/dwc.h declares, and rejects bad calls before touching the device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import depthwise_convolution_dwc_amd as dwc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dwc.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(dwc.LIB_PATH),
+                                reason="libdwc.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dwc_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_python_list():
+    assert declared_functions() == sorted(dwc.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(dwc.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_only_the_abi_is_exported():
+    out = os.popen(f"nm -D --defined-only {dwc.LIB_PATH}").read().split("\n")
+    names = {ln.split()[-1] for ln in out if " T " in ln}
+    assert names == set(declared_functions())
+
+
+def test_version_and_strings():
+    assert dwc.lib().dwc_version() == 100
+    assert dwc.lib().dwc_status_string(0) == b"ok"
+    assert dwc.lib().dwc_status_string(5) == b"output aliases an input"
+
+
+def test_struct_layout_matches_header():
+    # int64 x4 + int32 x10 = 72 bytes, no padding
+    assert ctypes.sizeof(dwc.Problem) == 72
+
+
+@pytest.mark.parametrize("n,h,f,s,p,want", [
+    (1, 14, 7, 1, 3, (14, 14)), (64, 56, 7, 2, 3, (28, 28)), (32, 56, 31, 1, 15, (56, 56)),
+    (64, 7, 31, 1, 15, (7, 7)), (1, 3, 3, 2, 1, (2, 2)), (2, 5, 5, 1, 0, (1, 1))])
+def test_output_dims(n, h, f, s, p, want):
+    assert dwc.output_dims(dwc.problem(n, h, h, 8, f, f, s, p)) == want
+
+
+BAD = [
+    (dict(n=-1), 1), (dict(h=0), 1), (dict(c=0), 1), (dict(fh=0), 1),
+    (dict(stride=0), 1), (dict(pad=-1), 1), (dict(dtype=7), 1),
+    (dict(h=3, fh=7, pad=1), 1),  # filter larger than padded input
+    (dict(algo=9), 1), (dict(wgrad_split=-2), 1),
+]
+
+
+@pytest.mark.parametrize("change,status", BAD)
+def test_bad_parameters_rejected(change, status):
+    kw = dict(n=2, h=9, w=9, c=16, fh=3, fw=3, stride=1, pad=1, dtype=0, algo="auto",
+              wgrad_split=0)
+    kw.update(change)
+    if "stride" in change:
+        kw["stride"] = change["stride"]
+    p = dwc.problem(kw["n"], kw["h"], kw["w"], kw["c"], kw["fh"], kw.get("fw", kw["fh"]),
+                    kw["stride"], kw["pad"], kw["dtype"], kw["algo"], kw["wgrad_split"])
+    for op in (0, 1, 2):
+        assert dwc.check(p, op) == status
+    assert dwc.last_error() != ""
+
+
+def test_fp32_output_required():
+    p = dwc.problem(1, 8, 8, 4, 3, 3, 1, 1)
+    p.out_dtype = 1
+    assert dwc.check(p, 0) == 2
+
+
+def test_direct_unavailable_is_unsupported():
+    # width 4 has no register-window kernel; forcing it is an error, auto falls back
+    p = dwc.problem(1, 8, 8, 4, 4, 4, 1, 1, algo="direct")
+    assert dwc.check(p, 0) == 2
+    p = dwc.problem(1, 8, 8, 4, 4, 4, 1, 1, algo="auto")
+    assert dwc.check(p, 0) == 0
+    assert "generic" in dwc.plan_describe(p, 0)
+    # stride-2 data gradient runs the gather kernel
+    p = dwc.problem(1, 8, 8, 4, 3, 3, 2, 1)
+    assert "bwd_data generic" in dwc.plan_describe(p, 1)
+
+
+def test_plans_for_the_named_workloads():
+    p = dwc.problem(64, 56, 56, 128, 7, 7, 1, 3)
+    d = dwc.plan_describe(p, 0)
+    assert d.startswith("fwd direct") and "tmw=14" in d and "flip=0" in d
+    assert "flip=1" in dwc.plan_describe(p, 1)
+    d = dwc.plan_describe(p, 2)
+    assert d.startswith("bwd_filter direct")
+    p = dwc.problem(64, 56, 56, 128, 7, 7, 2, 3)
+    assert "sw=2" in dwc.plan_describe(p, 0)
+    p = dwc.problem(128, 28, 28, 512, 13, 13, 1, 6, dtype=dwc.BF16)
+    assert "dt=bf16" in dwc.plan_describe(p, 0)
+
+
+def test_workspace_size_matches_split():
+    p = dwc.problem(32, 56, 56, 128, 31, 31, 1, 15, wgrad_split=8)
+    assert dwc.workspace_size(p) == 8 * 31 * 31 * 128 * 4
+    p = dwc.problem(32, 56, 56, 128, 31, 31, 1, 15, wgrad_split=1)
+    assert dwc.workspace_size(p) == 0
+    p = dwc.problem(0, 56, 56, 128, 31, 31, 1, 15)
+    assert dwc.workspace_size(p) == 0
+    p = dwc.problem(2, 8, 8, 4, 3, 3, 1, 1, wgrad_split=17)  # > N*OH = 16
+    assert dwc.check(p, 2) == 1
+
+
+def test_pointer_errors_are_reported_before_any_launch():
+    # Fake addresses: every call below must fail validation, so nothing is
+    # launched and no GPU is needed.
+    p = dwc.problem(1, 8, 8, 16, 3, 3, 1, 1)
+    L = dwc.lib()
+    pp = ctypes.byref(p)
+    assert L.dwc_fwd(pp, 0x10000, 0x20000, None, None) == 1           # null output
+    assert L.dwc_fwd(pp, None, 0x20000, 0x30000, None) == 1           # null input
+    assert L.dwc_fwd(pp, 0x10001, 0x20000, 0x30000, None) == 3        # misaligned x
+    assert L.dwc_fwd(pp, 0x10000, 0x20000, 0x30002, None) == 3        # misaligned y
+    x = 0x100000
+    assert L.dwc_fwd(pp, x, 0x200000, x + 64, None) == 5              # y overlaps x
+    assert L.dwc_bwd_data(pp, x, 0x200000, x - 64, None) == 5         # dx overlaps dy
+    q = dwc.problem(4, 32, 32, 64, 5, 5, 1, 2, wgrad_split=4)
+    need = dwc.workspace_size(q)
+    assert need > 0
+    assert L.dwc_bwd_filter(ctypes.byref(q), 0x1000000, 0x3000000, 0x5000000, None, 0, None) == 4
+    assert L.dwc_bwd_filter(ctypes.byref(q), 0x1000000, 0x3000000, 0x5000000, 0x6000000,
+                            need - 4, None) == 4
+    # workspace overlapping dW
+    assert L.dwc_bwd_filter(ctypes.byref(q), 0x1000000, 0x3000000, 0x5000000, 0x5000000,
+                            need, None) == 5
+    half = dwc.problem(1, 8, 8, 16, 3, 3, 1, 1, dtype=dwc.BF16)
+    assert L.dwc_fwd(ctypes.byref(half), 0x10001, 0x20000, 0x30000, None) == 3
+
+
+def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(dwc, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(dwc, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        dwc.lib()

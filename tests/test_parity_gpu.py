@@ -1,0 +1,148 @@
+"""GPU parity at small sizes: every element of the HIP result against the
+float64 oracle, for all three operations, all operand dtypes and both kernel
+families, over shapes that span several tiles, ragged tails and the
+degenerate cases (C not a multiple of 64, filters larger than the image,
+stride 2, N = 0, 1x1 filters, widths without a register-window kernel)."""
+
+import numpy as np
+import pytest
+
+import oracle
+from dwc_inputs import Shape, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # collected on CPU too; skipped there
+    pytest.skip("no GPU", allow_module_level=True)
+
+from gpu_helpers import TOL, dwc, log, rel_l2, sync, to_device  # noqa: E402
+
+# (n, h, w, c, fh, fw, stride, pad)
+SHAPES = [
+    (2, 14, 14, 32, 7, 7, 1, 3),
+    (2, 17, 13, 96, 3, 3, 1, 1),
+    (1, 9, 23, 33, 5, 5, 1, 2),
+    (3, 12, 12, 3, 9, 9, 1, 4),
+    (2, 10, 11, 64, 13, 13, 1, 6),
+    (1, 6, 7, 130, 31, 31, 1, 15),
+    (2, 20, 20, 64, 7, 7, 2, 3),
+    (1, 5, 40, 70, 3, 5, 1, (1, 2)),
+    (1, 7, 7, 1, 31, 31, 1, 15),
+    (2, 30, 5, 64, 17, 3, 2, (8, 1)),
+    (1, 8, 8, 16, 4, 4, 1, 2),
+    (1, 16, 16, 64, 21, 21, 1, 10),
+    (1, 16, 19, 64, 27, 27, 1, 13),
+    (2, 9, 9, 8, 1, 1, 1, 0),
+    (1, 11, 13, 40, 3, 3, 3, 1),
+    (1, 33, 35, 128, 7, 7, 1, 0),
+    (2, 12, 29, 64, 5, 5, (2, 1), 2),
+]
+
+
+def _shape(t):
+    n, h, w, c, fh, fw, s, p = t
+    sh, sw = (s, s) if isinstance(s, int) else s
+    ph, pw = (p, p) if isinstance(p, int) else p
+    return Shape(n, h, w, c, fh, fw, sh, sw, ph, pw)
+
+
+def _run(op, s: Shape, inp, algo, wgrad_split=0):
+    stride, pad = (s.stride_h, s.stride_w), (s.pad_h, s.pad_w)
+    if op == "fwd":
+        got = dwc.fwd(to_device(inp.x), to_device(inp.w), stride, pad, algo=algo)
+    elif op == "bwd_data":
+        got = dwc.bwd_data(to_device(inp.dy), to_device(inp.w), (s.h, s.w), stride, pad,
+                           algo=algo)
+    else:
+        got = dwc.bwd_filter(to_device(inp.x), to_device(inp.dy), (s.fh, s.fw), stride, pad,
+                             algo=algo, wgrad_split=wgrad_split)
+    sync()
+    return got.double().cpu().numpy()
+
+
+def _want(op, s: Shape, inp):
+    stride, pad = (s.stride_h, s.stride_w), (s.pad_h, s.pad_w)
+    if op == "fwd":
+        return oracle.fwd(inp.x.values, inp.w.values, stride, pad)
+    if op == "bwd_data":
+        return oracle.bwd_data(inp.dy.values, inp.w.values, (s.h, s.w), stride, pad)
+    return oracle.bwd_filter(inp.x.values, inp.dy.values, (s.fh, s.fw), stride, pad)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("op", ["fwd", "bwd_data", "bwd_filter"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda t: "x".join(map(str, t[:6])) + f"_s{t[6]}_p{t[7]}")
+def test_small_parity(shape, op, dtype):
+    s = _shape(shape)
+    inp = make_inputs(s, dtype, seed=sum(shape[:6]))
+    want = _want(op, s, inp)
+    for algo in ("auto", "generic"):
+        log(f"case {shape} {op} {dtype} {algo}")
+        got = _run(op, s, inp, algo)
+        assert got.shape == want.shape
+        err = rel_l2(got, want)
+        assert err <= TOL[dtype], (algo, err)
+        assert np.all(np.isfinite(got))
+
+
+@pytest.mark.parametrize("op", ["fwd", "bwd_data", "bwd_filter"])
+def test_empty_batch(op):
+    s = Shape(0, 8, 8, 16, 3, 3, 1, 1, 1, 1)
+    x = torch.zeros((0, 8, 8, 16), device="cuda")
+    w = torch.randn((3, 3, 16), device="cuda")
+    if op == "fwd":
+        assert dwc.fwd(x, w, 1, 1).shape == (0, 8, 8, 16)
+    elif op == "bwd_data":
+        assert dwc.bwd_data(x, w, (8, 8), 1, 1).shape == (0, 8, 8, 16)
+    else:
+        dw = torch.full((3, 3, 16), 7.0, device="cuda")
+        dwc.bwd_filter(x, x, (3, 3), 1, 1, out=dw)
+        sync()
+        assert torch.count_nonzero(dw).item() == 0
+    del s
+
+
+@pytest.mark.parametrize("split", [1, 2, 5, 24])
+def test_wgrad_split_invariance(split):
+    s = Shape(3, 8, 12, 80, 5, 5, 1, 1, 2, 2)
+    inp = make_inputs(s, "f32", seed=12)
+    want = _want("bwd_filter", s, inp)
+    got = _run("bwd_filter", s, inp, "auto", wgrad_split=split)
+    assert rel_l2(got, want) <= 1e-5
+
+
+@pytest.mark.parametrize("op", ["fwd", "bwd_data", "bwd_filter"])
+def test_run_to_run_bitwise(op):
+    s = Shape(4, 24, 24, 128, 13, 13, 1, 1, 6, 6)
+    inp = make_inputs(s, "f32", seed=5)
+    a = _run(op, s, inp, "auto")
+    b = _run(op, s, inp, "auto")
+    np.testing.assert_array_equal(a, b)
+
+
+def test_outputs_fully_overwritten():
+    """Outputs start as NaN; every element must be written."""
+    s = Shape(2, 13, 11, 70, 7, 7, 1, 1, 3, 3)
+    inp = make_inputs(s, "f32", seed=8)
+    y = torch.full(s.y_shape(), float("nan"), device="cuda")
+    dwc.fwd(to_device(inp.x), to_device(inp.w), 1, 3, out=y)
+    dx = torch.full(s.x_shape(), float("nan"), device="cuda")
+    dwc.bwd_data(to_device(inp.dy), to_device(inp.w), (13, 11), 1, 3, out=dx)
+    dw = torch.full(s.w_shape(), float("nan"), device="cuda")
+    dwc.bwd_filter(to_device(inp.x), to_device(inp.dy), (7, 7), 1, 3, out=dw)
+    sync()
+    for t in (y, dx, dw):
+        assert torch.isfinite(t).all().item()
+
+
+def test_caller_stream_is_used():
+    s = Shape(2, 20, 20, 64, 7, 7, 1, 1, 3, 3)
+    inp = make_inputs(s, "f32", seed=9)
+    st = torch.cuda.Stream()
+    x, w = to_device(inp.x), to_device(inp.w)
+    torch.cuda.current_stream().synchronize()
+    with torch.cuda.stream(st):
+        y = dwc.fwd(x, w, 1, 3)
+    st.synchronize()
+    assert rel_l2(y.double().cpu().numpy(), _want("fwd", s, inp)) <= 1e-5
