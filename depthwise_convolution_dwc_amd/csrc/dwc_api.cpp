@@ -24,6 +24,18 @@ hipError_t launch_fwd_type(const Plan& pl, const void* in, const void* filt, flo
     a.in = in;
     a.filt = filt;
     a.out = out;
+    if (pl.sweep) {
+      SweepArgs w = pl.sa;
+      w.in = in;
+      w.in2 = filt;
+      w.out = out;
+      switch (pl.dt) {
+        case DT_F32: return launch_fwd_sweep_dt0(w.F, pl.tmw, pl.flip, w, pl.blocks, s);
+        case DT_BF16: return launch_fwd_sweep_dt1(w.F, pl.tmw, pl.flip, w, pl.blocks, s);
+        case DT_F16: return launch_fwd_sweep_dt2(w.F, pl.tmw, pl.flip, w, pl.blocks, s);
+      }
+      return hipErrorInvalidValue;
+    }
     switch (pl.dt) {
       case DT_F32: return launch_fwd_direct_dt0(a.FW, a.SW, pl.tmw, pl.flip, a, pl.blocks, s);
       case DT_BF16: return launch_fwd_direct_dt1(a.FW, a.SW, pl.tmw, pl.flip, a, pl.blocks, s);
@@ -86,10 +98,22 @@ int dwc_bwd_filter(const dwc_problem* p, const void* x, const void* dy, void* dw
     a.x = x;
     a.dy = dy;
     a.ws = part;
-    switch (pl.dt) {
-      case DT_F32: e = launch_wgrad_direct_dt0(a.FW, a.SW, pl.tj, a, pl.blocks, s); break;
-      case DT_BF16: e = launch_wgrad_direct_dt1(a.FW, a.SW, pl.tj, a, pl.blocks, s); break;
-      default: e = launch_wgrad_direct_dt2(a.FW, a.SW, pl.tj, a, pl.blocks, s); break;
+    if (pl.sweep) {
+      SweepArgs w = pl.sa;
+      w.in = x;
+      w.in2 = dy;
+      w.out = part;
+      switch (pl.dt) {
+        case DT_F32: e = launch_wgrad_sweep_dt0(w.F, pl.tj, w, pl.blocks, s); break;
+        case DT_BF16: e = launch_wgrad_sweep_dt1(w.F, pl.tj, w, pl.blocks, s); break;
+        default: e = launch_wgrad_sweep_dt2(w.F, pl.tj, w, pl.blocks, s); break;
+      }
+    } else {
+      switch (pl.dt) {
+        case DT_F32: e = launch_wgrad_direct_dt0(a.FW, a.SW, pl.tj, a, pl.blocks, s); break;
+        case DT_BF16: e = launch_wgrad_direct_dt1(a.FW, a.SW, pl.tj, a, pl.blocks, s); break;
+        default: e = launch_wgrad_direct_dt2(a.FW, a.SW, pl.tj, a, pl.blocks, s); break;
+      }
     }
   } else {
     GenericArgs g = pl.ga;

@@ -29,6 +29,10 @@ constexpr int kBlockThreads = 64 * kWavesPerBlock;
 constexpr int kFwdRows = 4;
 constexpr int kWgradRows = 4;
 
+// Square filters up to this size with stride 1 run the sweep kernels.
+constexpr int kSweepMaxF = 9;
+#define DWC_SWEEP_F_LIST(M) M(3) M(5) M(7) M(9)
+
 // Filter rows held in registers at once by both direct kernels for a filter
 // of width FW: the whole filter up to 9x9, else a chunk of about 64-81
 // registers chosen so that common square filters split with little waste
@@ -49,6 +53,24 @@ struct FwdArgs {
   int PH, PW;        // zero padding; negative values crop
   int tiles_w, tiles_h, cblocks;
   int num_items;     // waves of work: N * cblocks * tiles_h * tiles_w
+};
+
+// Sweep kernels (stride 1, square F <= 9): waves walk down R consecutive
+// output rows of one image.  Forward-type: one wave per (image, row chunk,
+// channel block, column strip).  Filter gradient: a workgroup's 4 waves take
+// 4 consecutive (image, row chunk) chunks of one (channel block, strip).
+struct SweepArgs {
+  const void* in;    // forward-type: X (or dY);  filter gradient: X
+  const void* in2;   // forward-type: filter;     filter gradient: dY
+  float* out;        // forward-type: Y (or dX);  filter gradient: Z x F x F x C partials
+  int N, IH, IW, C;  // dims of `in`
+  int OH, OW;        // forward-type: output dims; filter gradient: dY dims
+  int F, P;          // filter size, padding (forward-type data gradient: F-1-pad)
+  int tiles_w;       // column strips
+  int R, cpi;        // output rows per chunk, chunks per image
+  int cbg;           // channel blocks: ceil(C / 64)
+  int num_items;     // forward-type: waves; filter gradient: workgroups
+  int Z;             // filter gradient: partial slices, tiles_w * ceil(N * cpi / 4)
 };
 
 // Filter gradient: partial sums over slices of the N*OH axis.  One

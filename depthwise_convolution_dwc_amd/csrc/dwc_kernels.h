@@ -124,17 +124,12 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_rows(FwdArgs a) {
         wv[k][fw] = ld<DT>(ok ? wrs : zero, voff, ok ? (uint32_t)(fhe * FW + fwe) * Cb : 0u);
       }
     }
-    // Rows of this chunk: ih_base+fh0 .. +MSPAN-1.  Skip the chunk if all of
-    // them are padding; otherwise stream them branch-free (padding rows read
-    // as zeros), loading row m+1 while row m is multiplied.
-    const int row0 = ih_base + fh0;
-    if (row0 + MSPAN <= 0 || row0 >= a.IH) continue;
-    float xv[2][SPAN];
-    load_strip<DT, SPAN>(xv[0], img, row0, a.IH, iw0, a.IW, Cb, coff);
 #pragma unroll
     for (int m = 0; m < MSPAN; ++m) {
-      if (m + 1 < MSPAN)
-        load_strip<DT, SPAN>(xv[(m + 1) & 1], img, row0 + m + 1, a.IH, iw0, a.IW, Cb, coff);
+      const int ih = ih_base + fh0 + m;
+      if ((unsigned)ih >= (unsigned)a.IH) continue;  // a padding row: contributes 0
+      float xv[SPAN];
+      load_strip<DT, SPAN>(xv, img, ih, a.IH, iw0, a.IW, Cb, coff);
 #pragma unroll
       for (int r = 0; r < TR; ++r) {
         const int k = m - r * S;
@@ -142,8 +137,7 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_rows(FwdArgs a) {
 #pragma unroll
         for (int fw = 0; fw < FW; ++fw)
 #pragma unroll
-          for (int q = 0; q < TMW; ++q)
-            acc[r][q] = fmaf(xv[m & 1][q * S + fw], wv[k][fw], acc[r][q]);
+          for (int q = 0; q < TMW; ++q) acc[r][q] = fmaf(xv[q * S + fw], wv[k][fw], acc[r][q]);
       }
     }
   }
@@ -233,15 +227,12 @@ __global__ __launch_bounds__(kBlockThreads) void wgrad_rows(WgradArgs a) {
       }
       uint32_t xoff[SPAN];
       column_offsets<SPAN>(xoff, iw0, a.IW, Cb, c, a.C, EB);
-      // Input rows ih_base .. +MSPAN-1, streamed branch-free (padding rows
-      // read as zeros), row m+1 loading while row m is multiplied.
-      if (ih_base + MSPAN <= 0 || ih_base >= a.IH) continue;
-      float xv[2][SPAN];
-      load_strip<DT, SPAN>(xv[0], ximg, ih_base, a.IH, iw0, a.IW, Cb, xoff);
 #pragma unroll
       for (int m = 0; m < MSPAN; ++m) {
-        if (m + 1 < MSPAN)
-          load_strip<DT, SPAN>(xv[(m + 1) & 1], ximg, ih_base + m + 1, a.IH, iw0, a.IW, Cb, xoff);
+        const int ih = ih_base + m;
+        if ((unsigned)ih >= (unsigned)a.IH) continue;  // padding row: contributes 0
+        float xv[SPAN];
+        load_strip<DT, SPAN>(xv, ximg, ih, a.IH, iw0, a.IW, Cb, xoff);
 #pragma unroll
         for (int r = 0; r < RY; ++r) {
           const int k = m - r * S;
@@ -249,8 +240,7 @@ __global__ __launch_bounds__(kBlockThreads) void wgrad_rows(WgradArgs a) {
 #pragma unroll
           for (int q = 0; q < TJ; ++q)
 #pragma unroll
-            for (int fw = 0; fw < FW; ++fw)
-              acc[k][fw] = fmaf(xv[m & 1][q * S + fw], dv[r][q], acc[k][fw]);
+            for (int fw = 0; fw < FW; ++fw) acc[k][fw] = fmaf(xv[q * S + fw], dv[r][q], acc[k][fw]);
         }
       }
     }
@@ -289,6 +279,238 @@ __global__ __launch_bounds__(kBlockThreads) void wgrad_rows(WgradArgs a) {
       for (int fw = 0; fw < FW; ++fw)
         ws[((size_t)fh * FW + fw) * a.C] = acc[k][fw] + red[0][k * FW + fw][lane];
     }
+  }
+}
+
+constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
+constexpr int lcm_c(int a, int b) { return a / gcd_c(a, b) * b; }
+
+// Number of input-row strips a sweep wave keeps in registers: the row in
+// use plus two in flight, so each row's loads have two steps of FMAs to
+// arrive.
+constexpr int kSweepBufs = 3;
+
+// ---------------------------------------------------------------------------
+// Forward-type sweep kernel: stride 1, square filter F <= 9.
+//
+// A wave owns 64 channels x TMW output columns x R consecutive output rows
+// of one image and walks down them.  The whole F x F filter stays in
+// registers (filter reuse, §3.2).  Input rows are read in order, each once
+// per wave: input row i feeds output rows i-F+1 .. i (one per filter row),
+// whose accumulators live in a ring of F register rows; when an output row
+// has seen all F filter rows it is stored and its ring slot reused.  Along
+// the width one strip of TMW+F-1 pixels serves all F taps of every filter
+// row (the width-first reuse and 1-D row decomposition of §3.3).  Rows are
+// loaded two steps ahead into a ring of three strip buffers.  The body is
+// unrolled over lcm(F, 3) rows, so every ring index is a compile-time
+// constant.  FLIP reads the filter turned by 180 degrees: the stride-1 data
+// gradient.
+// ---------------------------------------------------------------------------
+template <int DT, int F, int TMW, bool FLIP>
+__global__ __launch_bounds__(kBlockThreads) void fwd_sweep(SweepArgs a) {
+  constexpr int EB = Elem<DT>::bytes;
+  constexpr int SPAN = TMW + F - 1;
+  constexpr int NB = kSweepBufs;
+  constexpr int L = lcm_c(F, NB);
+  const int wave = uniform(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int item = xcd_logical_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wave;
+  if (item >= a.num_items) return;
+  int t = item;
+  const int tw = t % a.tiles_w;
+  t /= a.tiles_w;
+  const int rc = t % a.cpi;
+  t /= a.cpi;
+  const int cb = t % a.cbg;
+  const int n = t / a.cbg;
+  const int c = cb * kWaveChannels + lane;
+  const uint32_t Cb = (uint32_t)a.C * EB;
+  const char* img = (const char*)a.in + (size_t)n * a.IH * a.IW * Cb;
+  const int ow0 = tw * TMW;
+  const int o_start = rc * a.R;
+  const int o_cnt = a.OH - o_start < a.R ? a.OH - o_start : a.R;
+  const int i_start = o_start - a.P;
+  const int iw0 = ow0 - a.P;
+
+  uint32_t coff[SPAN];
+  column_offsets<SPAN>(coff, iw0, a.IW, Cb, c, a.C, EB);
+  float xb[NB][SPAN];
+  load_strip<DT, SPAN>(xb[0], img, i_start, a.IH, iw0, a.IW, Cb, coff);
+  load_strip<DT, SPAN>(xb[1], img, i_start + 1, a.IH, iw0, a.IW, Cb, coff);
+
+  float wv[F][F];
+  {
+    const auto wrs = make_rsrc(a.in2, (uint32_t)(F * F) * Cb);
+    const uint32_t voff = c < a.C ? (uint32_t)c * EB : kOOB;
+#pragma unroll
+    for (int fh = 0; fh < F; ++fh)
+#pragma unroll
+      for (int fw = 0; fw < F; ++fw) {
+        const int e = FLIP ? (F - 1 - fh) * F + (F - 1 - fw) : fh * F + fw;
+        wv[fh][fw] = ld<DT>(wrs, voff, (uint32_t)e * Cb);
+      }
+  }
+  uint32_t ooff[TMW];  // output pixel offsets within a row, from column ow0
+#pragma unroll
+  for (int q = 0; q < TMW; ++q)
+    ooff[q] = (ow0 + q < a.OW && c < a.C) ? (uint32_t)(q * a.C + c) * 4u : kOOB;
+  float acc[F][TMW];  // ring: slot s holds output row o with o = s (mod F)
+#pragma unroll
+  for (int r = 0; r < F; ++r)
+#pragma unroll
+    for (int q = 0; q < TMW; ++q) acc[r][q] = 0.f;
+
+  float* out_img = a.out + (size_t)n * a.OH * a.OW * a.C;
+  const int steps = o_cnt + F - 1;  // input rows i_start .. i_start+steps-1
+  for (int g = 0; g < steps; g += L) {
+#pragma unroll
+    for (int u = 0; u < L; ++u) {
+      const int i_rel = g + u;  // = u (mod F) and (mod NB)
+      if (i_rel >= steps) break;
+      load_strip<DT, SPAN>(xb[(u + 2) % NB], img, i_start + i_rel + 2, a.IH, iw0, a.IW, Cb, coff);
+      const float(&xv)[SPAN] = xb[u % NB];
+#pragma unroll
+      for (int fh = 0; fh < F; ++fh) {
+        const int slot = ((u - fh) % F + F) % F;  // output row i_rel - fh
+#pragma unroll
+        for (int fw = 0; fw < F; ++fw)
+#pragma unroll
+          for (int q = 0; q < TMW; ++q)
+            acc[slot][q] = fmaf(xv[q + fw], wv[fh][fw], acc[slot][q]);
+      }
+      // Output row i_rel-F+1 has seen all F filter rows: store it (rows
+      // outside [0, o_cnt) write nowhere) and free its slot.
+      const int done = (u + 1) % F;
+      const int o_rel = i_rel - (F - 1);
+      const bool ok = o_rel >= 0 && o_rel < o_cnt;
+      const float* orow = out_img + ((ptrdiff_t)(o_start + o_rel) * a.OW + ow0) * a.C;
+      const auto ors = make_rsrc(orow, ok ? (uint32_t)(TMW * a.C) * 4u : 0u);
+#pragma unroll
+      for (int q = 0; q < TMW; ++q) {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[done][q]), ors, (int)ooff[q], 0, 0);
+        acc[done][q] = 0.f;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Filter-gradient sweep kernel: stride 1, square filter F <= 9.
+//
+// A wave owns 64 channels x all F x F taps (registers) x one strip of TJ
+// columns x one chunk of R consecutive dY rows of one image, and walks down
+// the chunk.  Input rows are read in order, each once: input row i pairs
+// with dY rows i-F+1 .. i (one per filter row), held in a ring of F
+// register rows; each step does F*F*TJ FMAs on one input strip of TJ+F-1
+// pixels and one new dY strip.  Both strips are loaded two steps ahead.
+// The workgroup's 4 waves take 4 consecutive chunks of the same strip, add
+// their taps through LDS in a fixed order, and write one partial per
+// (strip, chunk group); reduce_partials sums the partials in order (the
+// split of §5.1, deterministic).
+// ---------------------------------------------------------------------------
+template <int DT, int F, int TJ>
+__global__ __launch_bounds__(kBlockThreads) void wgrad_sweep(SweepArgs a) {
+  constexpr int EB = Elem<DT>::bytes;
+  constexpr int SPAN = TJ + F - 1;
+  constexpr int NB = kSweepBufs;
+  constexpr int L = lcm_c(F, NB);
+  __shared__ float red[2][F * F][64];
+  const int wave = uniform(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
+  if (blk >= a.num_items) return;  // the whole workgroup leaves together
+  int t = blk;
+  const int s = t % a.tiles_w;
+  t /= a.tiles_w;
+  const int cb = t % a.cbg;
+  const int cg = t / a.cbg;
+  const int z = cg * a.tiles_w + s;
+  const int c = cb * kWaveChannels + lane;
+  const uint32_t Cb = (uint32_t)a.C * EB;
+  const int chunk = cg * kWavesPerBlock + wave;
+  int n = 0, o_start = 0, o_cnt = 0;
+  if (chunk < a.N * a.cpi) {
+    n = chunk / a.cpi;
+    o_start = (chunk - n * a.cpi) * a.R;
+    o_cnt = a.OH - o_start < a.R ? a.OH - o_start : a.R;
+  }
+  const int ow0 = s * TJ;
+  const int iw0 = ow0 - a.P;
+  const int i_start = o_start - a.P;
+  const char* ximg = (const char*)a.in + (size_t)n * a.IH * a.IW * Cb;
+  const char* dimg = (const char*)a.in2 + (size_t)n * a.OH * a.OW * Cb;
+  uint32_t doff[TJ], xoff[SPAN];
+  column_offsets<TJ>(doff, ow0, a.OW, Cb, c, a.C, EB);
+  column_offsets<SPAN>(xoff, iw0, a.IW, Cb, c, a.C, EB);
+  auto drow = [&](int i) { return i < o_cnt ? o_start + i : -1; };  // dY row of step i
+
+  float xb[NB][SPAN], db[NB][TJ];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    load_strip<DT, SPAN>(xb[k], ximg, i_start + k, a.IH, iw0, a.IW, Cb, xoff);
+    load_strip<DT, TJ>(db[k], dimg, drow(k), a.OH, ow0, a.OW, Cb, doff);
+  }
+  float acc[F][F];
+  float dv[F][TJ];  // ring: slot s holds dY row o with o = s (mod F)
+#pragma unroll
+  for (int k = 0; k < F; ++k) {
+#pragma unroll
+    for (int fw = 0; fw < F; ++fw) acc[k][fw] = 0.f;
+#pragma unroll
+    for (int q = 0; q < TJ; ++q) dv[k][q] = 0.f;
+  }
+
+  const int steps = o_cnt > 0 ? o_cnt + F - 1 : 0;
+  for (int g = 0; g < steps; g += L) {
+#pragma unroll
+    for (int u = 0; u < L; ++u) {
+      const int i_rel = g + u;  // = u (mod F) and (mod NB)
+      if (i_rel >= steps) break;
+      load_strip<DT, SPAN>(xb[(u + 2) % NB], ximg, i_start + i_rel + 2, a.IH, iw0, a.IW, Cb, xoff);
+      load_strip<DT, TJ>(db[(u + 2) % NB], dimg, drow(i_rel + 2), a.OH, ow0, a.OW, Cb, doff);
+#pragma unroll
+      for (int q = 0; q < TJ; ++q) dv[u % F][q] = db[u % NB][q];  // newest dY row: o = i_rel
+      const float(&xv)[SPAN] = xb[u % NB];
+#pragma unroll
+      for (int fh = 0; fh < F; ++fh) {
+        const int slot = ((u - fh) % F + F) % F;  // dY row i_rel - fh
+#pragma unroll
+        for (int q = 0; q < TJ; ++q)
+#pragma unroll
+          for (int fw = 0; fw < F; ++fw) acc[fh][fw] = fmaf(xv[q + fw], dv[slot][q], acc[fh][fw]);
+      }
+    }
+  }
+
+  // (w0 + w2) + (w1 + w3), then one store of the partial.
+  if (wave >= 2) {
+#pragma unroll
+    for (int k = 0; k < F; ++k)
+#pragma unroll
+      for (int fw = 0; fw < F; ++fw) red[wave - 2][k * F + fw][lane] = acc[k][fw];
+  }
+  __syncthreads();
+  if (wave < 2) {
+#pragma unroll
+    for (int k = 0; k < F; ++k)
+#pragma unroll
+      for (int fw = 0; fw < F; ++fw) acc[k][fw] += red[wave][k * F + fw][lane];
+  }
+  __syncthreads();
+  if (wave == 1) {
+#pragma unroll
+    for (int k = 0; k < F; ++k)
+#pragma unroll
+      for (int fw = 0; fw < F; ++fw) red[0][k * F + fw][lane] = acc[k][fw];
+  }
+  __syncthreads();
+  if (wave == 0 && c < a.C) {
+    float* ws = a.out + (size_t)z * F * F * a.C + c;
+#pragma unroll
+    for (int k = 0; k < F; ++k)
+#pragma unroll
+      for (int fw = 0; fw < F; ++fw)
+        ws[((size_t)k * F + fw) * a.C] = acc[k][fw] + red[0][k * F + fw][lane];
   }
 }
 

@@ -23,6 +23,17 @@ hipError_t launch_wgrad_direct_dt1(int fw, int s, int tj, const WgradArgs& a, in
 hipError_t launch_wgrad_direct_dt2(int fw, int s, int tj, const WgradArgs& a, int blocks,
                                    hipStream_t st);
 
+// Sweep kernels (stride 1, square filters up to 9x9).
+#define DWC_DECL_SWEEP(D)                                                                 \
+  hipError_t launch_fwd_sweep_dt##D(int f, int tmw, bool flip, const SweepArgs& a,         \
+                                    int blocks, hipStream_t st);                         \
+  hipError_t launch_wgrad_sweep_dt##D(int f, int tj, const SweepArgs& a, int blocks,       \
+                                      hipStream_t st);
+DWC_DECL_SWEEP(0)
+DWC_DECL_SWEEP(1)
+DWC_DECL_SWEEP(2)
+#undef DWC_DECL_SWEEP
+
 enum GenericKind { GEN_FWD = 0, GEN_FWD_FLIP = 1, GEN_DGRAD = 2, GEN_WGRAD = 3 };
 hipError_t launch_generic(int kind, int dt, const GenericArgs& a, hipStream_t st);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t st);

@@ -22,6 +22,13 @@ constexpr int64_t kWgradTargetWaves = 4096;
 
 int elem_bytes(int dt) { return dt == DT_F32 ? 4 : 2; }
 
+bool sweep_f(int f) {
+#define DWC_IS(F) if (f == F) return true;
+  DWC_SWEEP_F_LIST(DWC_IS)
+#undef DWC_IS
+  return false;
+}
+
 bool direct_fw(int fw) {
 #define DWC_IS(F) if (fw == F) return true;
   DWC_DIRECT_FW_LIST(DWC_IS)
@@ -60,6 +67,15 @@ int strip_override(const char* var, int fallback) {
   if (!v) return fallback;
   const int w = atoi(v);
   return (w == 7 || w == 14) ? w : fallback;
+}
+
+// Chunks per image for a sweep launch: enough waves (~3072, three per SIMD)
+// to fill the GPU, with chunks of at least F rows (each chunk re-reads F-1
+// halo rows).
+int64_t sweep_chunks(int64_t waves_per_chunk, int64_t out_h, int f) {
+  const int64_t w = std::max<int64_t>(waves_per_chunk, 1);
+  const int64_t cpi = std::max<int64_t>(1, (3072 + w - 1) / w);
+  return std::min<int64_t>(cpi, std::max<int64_t>(1, out_h / f));
 }
 
 // Number of slices of the N*OH axis for the filter gradient (§5.1 splits
@@ -136,6 +152,8 @@ int make_plan(const dwc_problem* p, int op, Plan* pl, std::string* err) {
                 "no direct kernel for this filter width / stride (use DWC_ALGO_AUTO)");
   const bool direct = p->algo != DWC_ALGO_GENERIC && can_direct;
   q.kind = direct ? PLAN_DIRECT : PLAN_GENERIC;
+  // Sweep kernels: stride 1, square filter up to 9x9.
+  const bool sweep_ok = p->stride_h == 1 && p->fh == p->fw && sweep_f(p->fw);
 
   if (op == DWC_OP_FWD || op == DWC_OP_BWD_DATA) {
     // The data gradient runs the forward map on dY with the filter turned
@@ -156,10 +174,33 @@ int make_plan(const dwc_problem* p, int op, Plan* pl, std::string* err) {
     f.PW = bwd ? p->fw - 1 - p->pad_w : p->pad_w;
     if (direct) {
       q.flip = bwd;
+      q.sweep = sweep_ok;
+      f.cblocks = cblocks;
+      if (q.sweep) {
+        SweepArgs w{};
+        w.N = f.N; w.IH = f.IH; w.IW = f.IW; w.C = C; w.OH = f.OH; w.OW = f.OW;
+        w.F = p->fw;
+        w.P = f.PH;
+        q.tmw = p->fw >= 7 ? 7 : strip_override("DWC_FWD_STRIP", pick_strip(f.OW));
+        w.tiles_w = (f.OW + q.tmw - 1) / q.tmw;
+        w.cbg = cblocks;
+        const int64_t cpi = sweep_chunks((int64_t)f.N * w.cbg * w.tiles_w, f.OH, p->fw);
+        w.R = (int)((f.OH + cpi - 1) / cpi);
+        if (const char* v = getenv("DWC_SWEEP_ROWS")) w.R = std::max(1, std::min(f.OH, atoi(v)));
+        w.cpi = (f.OH + w.R - 1) / w.R;
+        const int64_t waves = (int64_t)f.N * w.cpi * w.cbg * w.tiles_w;
+        if (waves > kI32Max - kWavesPerBlock)
+          return fail(err, DWC_ERR_UNSUPPORTED, "too many work items for one launch");
+        w.num_items = (int)waves;
+        q.blocks = (int)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
+        q.sa = w;
+        q.fa = f;
+        *pl = q;
+        return DWC_OK;
+      }
       q.tmw = strip_override("DWC_FWD_STRIP", pick_strip(f.OW));
       f.tiles_w = (f.OW + q.tmw - 1) / q.tmw;
       f.tiles_h = (f.OH + kFwdRows - 1) / kFwdRows;
-      f.cblocks = cblocks;
       const int64_t items = (int64_t)f.N * cblocks * f.tiles_h * f.tiles_w;
       if (items > kI32Max - kWavesPerBlock)
         return fail(err, DWC_ERR_UNSUPPORTED, "too many work items for one launch");
@@ -196,25 +237,58 @@ int make_plan(const dwc_problem* p, int op, Plan* pl, std::string* err) {
     if (p->wgrad_split > 0 && rows > 0 && p->wgrad_split > rows)
       return fail(err, DWC_ERR_BAD_PARAM, "wgrad_split larger than N*OH");
     if (direct) {
-      // 7-wide strips keep the dY block, the input strip and the taps of a
-      // filter-row chunk within ~128 registers.
-      q.tj = strip_override("DWC_WGRAD_STRIP", 7);
-      q.tfh = filter_row_chunk(p->fw);
       WgradArgs w{};
       w.N = (int)p->n; w.IH = (int)p->h; w.IW = (int)p->w; w.C = C;
       w.OH = (int)oh; w.OW = (int)ow;
       w.FH = p->fh; w.FW = p->fw; w.SH = p->stride_h; w.SW = p->stride_w;
       w.PH = p->pad_h; w.PW = p->pad_w;
       w.cblocks = cblocks;
-      w.fh_tiles = (p->fh + q.tfh - 1) / q.tfh;
       w.rows = (int)rows;
-      const int64_t per_slice = (int64_t)cblocks * w.fh_tiles;
-      const int64_t strips = (ow + q.tj - 1) / q.tj;
-      q.z = rows == 0 ? 1
-                      : (p->wgrad_split > 0 ? p->wgrad_split
-                                            : pick_split(rows, per_slice, strips, m, flops, bytes));
-      w.Z = q.z;
-      const int64_t items = (int64_t)q.z * per_slice;  // one workgroup each
+      q.sweep = sweep_ok;
+      int64_t items = 0;
+      if (q.sweep) {
+        SweepArgs sw{};
+        sw.N = (int)p->n; sw.IH = (int)p->h; sw.IW = (int)p->w; sw.C = C;
+        sw.OH = (int)oh; sw.OW = (int)ow;
+        sw.F = p->fw;
+        sw.P = p->pad_h;
+        q.tj = p->fw >= 7 ? 7 : strip_override("DWC_WGRAD_STRIP", pick_strip(ow));
+        q.tfh = p->fh;
+        sw.tiles_w = (int)((ow + q.tj - 1) / q.tj);
+        sw.cbg = cblocks;
+        // chunks per image: from a requested split of the N*OH axis, or
+        // enough to fill the GPU
+        const int64_t nn = std::max<int64_t>(p->n, 1);
+        int64_t cpi = p->wgrad_split > 0 ? (p->wgrad_split + nn - 1) / nn
+                                         : sweep_chunks(nn * sw.cbg * sw.tiles_w, oh, p->fw);
+        cpi = std::max<int64_t>(1, std::min<int64_t>(cpi, oh));
+        sw.R = (int)((oh + cpi - 1) / cpi);
+        if (const char* v = getenv("DWC_SWEEP_ROWS"))
+          sw.R = (int)std::max<int64_t>(1, std::min<int64_t>(oh, atoi(v)));
+        sw.cpi = (int)((oh + sw.R - 1) / sw.R);
+        const int64_t groups = (p->n * sw.cpi + kWavesPerBlock - 1) / kWavesPerBlock;
+        sw.Z = (int)(groups * sw.tiles_w);
+        q.z = rows == 0 ? 1 : std::max(1, sw.Z);
+        items = rows == 0 ? 0 : groups * sw.cbg * sw.tiles_w;  // workgroups
+        if (items > kI32Max)
+          return fail(err, DWC_ERR_UNSUPPORTED, "too many work items for one launch");
+        sw.num_items = (int)items;
+        q.blocks = (int)items;
+        q.sa = sw;
+      } else {
+        // 7-wide strips keep the dY block, the input strip and the taps of a
+        // filter-row chunk within ~128 registers.
+        q.tj = strip_override("DWC_WGRAD_STRIP", 7);
+        q.tfh = filter_row_chunk(p->fw);
+        w.fh_tiles = (p->fh + q.tfh - 1) / q.tfh;
+        const int64_t per_slice = (int64_t)cblocks * w.fh_tiles;
+        const int64_t strips = (ow + q.tj - 1) / q.tj;
+        q.z = rows == 0 ? 1
+                        : (p->wgrad_split > 0 ? p->wgrad_split
+                                              : pick_split(rows, per_slice, strips, m, flops, bytes));
+        w.Z = q.z;
+        items = (int64_t)q.z * per_slice;  // one workgroup each
+      }
       if (items > kI32Max)
         return fail(err, DWC_ERR_UNSUPPORTED, "too many work items for one launch");
       w.num_items = (int)items;
@@ -293,18 +367,28 @@ int check_pointers(const dwc_problem* p, const Plan& pl, const void* in0, const 
 std::string describe(const Plan& pl) {
   static const char* ops[] = {"fwd", "bwd_data", "bwd_filter"};
   char buf[512];
-  if (pl.kind == PLAN_DIRECT && pl.op != DWC_OP_BWD_FILTER) {
+  if (pl.kind == PLAN_DIRECT && pl.sweep) {
+    const SweepArgs& w = pl.sa;
     snprintf(buf, sizeof buf,
-             "%s direct dt=%s fw=%d sw=%d flip=%d tmw=%d rows=%d tiles_w=%d tiles_h=%d "
+             "%s sweep dt=%s f=%d strip=%d tiles_w=%d rows=%d cpi=%d cblocks=%d "
+             "items=%d blocks=%d z=%d ws_bytes=%zu",
+             ops[pl.op], dt_name(pl.dt), w.F, pl.op == DWC_OP_BWD_FILTER ? pl.tj : pl.tmw,
+             w.tiles_w, w.R, w.cpi, w.cbg, w.num_items, pl.blocks,
+             pl.op == DWC_OP_BWD_FILTER ? pl.z : 0, pl.ws_bytes);
+  } else if (pl.kind == PLAN_DIRECT && pl.op != DWC_OP_BWD_FILTER) {
+    snprintf(buf, sizeof buf,
+             "%s %s dt=%s fw=%d sw=%d flip=%d tmw=%d rows=%d tiles_w=%d tiles_h=%d "
              "cblocks=%d items=%d blocks=%d",
-             ops[pl.op], dt_name(pl.dt), pl.fa.FW, pl.fa.SW, (int)pl.flip, pl.tmw, kFwdRows,
+             ops[pl.op], "direct", dt_name(pl.dt), pl.fa.FW, pl.fa.SW,
+             (int)pl.flip, pl.tmw, kFwdRows,
              pl.fa.tiles_w, pl.fa.tiles_h, pl.fa.cblocks, pl.fa.num_items, pl.blocks);
   } else if (pl.kind == PLAN_DIRECT) {
     snprintf(buf, sizeof buf,
-             "%s direct dt=%s fw=%d sw=%d tj=%d tfh=%d fh_tiles=%d cblocks=%d z=%d items=%d "
-             "blocks=%d ws_bytes=%zu",
-             ops[pl.op], dt_name(pl.dt), pl.wa.FW, pl.wa.SW, pl.tj, pl.tfh, pl.wa.fh_tiles,
-             pl.wa.cblocks, pl.z, pl.wa.num_items, pl.blocks, pl.ws_bytes);
+             "%s %s dt=%s fw=%d sw=%d tj=%d tfh=%d fh_tiles=%d rows=%d cblocks=%d z=%d "
+             "items=%d blocks=%d ws_bytes=%zu",
+             ops[pl.op], "direct", dt_name(pl.dt), pl.wa.FW, pl.wa.SW, pl.tj,
+             pl.tfh, pl.wa.fh_tiles, kWgradRows, pl.wa.cblocks, pl.z,
+             pl.wa.num_items, pl.blocks, pl.ws_bytes);
   } else {
     snprintf(buf, sizeof buf, "%s generic dt=%s kind=%d z=%d total=%lld ws_bytes=%zu",
              ops[pl.op], dt_name(pl.dt), pl.gen_kind, pl.z, (long long)pl.ga.total, pl.ws_bytes);

@@ -17,6 +17,7 @@ struct Plan {
   int op = 0;
   int dt = 0;
   int kind = PLAN_NONE;
+  bool sweep = false;  // direct plan runs the sweep kernels
   int64_t oh = 0, ow = 0;
   bool empty = false;  // n == 0
 
@@ -31,6 +32,9 @@ struct Plan {
   WgradArgs wa{};
   int z = 1;
   size_t ws_bytes = 0;  // 0: slice partials are written straight to dW
+
+  // sweep kernels (stride 1, square filters up to 9x9)
+  SweepArgs sa{};
 
   // generic kernels
   int gen_kind = 0;

@@ -67,7 +67,59 @@ hipError_t wgrad_by_tj(int fw, int tj, const WgradArgs& a, int blocks, hipStream
   return hipErrorInvalidValue;
 }
 
+// Sweep strips: 7 columns for every filter size; 14 only up to 5x5, where
+// the ring, filter and two prefetched strips still fit in registers.
+template <int TMW, bool FLIP>
+hipError_t fwd_sweep_by_f(int f, const SweepArgs& a, int blocks, hipStream_t s) {
+  switch (f) {
+#define DWC_CASE(F)                                                                       \
+  case F:                                                                                 \
+    if constexpr (TMW == 7 || F <= 5) {                                                   \
+      hipLaunchKernelGGL((fwd_sweep<kDt, F, TMW, FLIP>), dim3(blocks), dim3(kBlockThreads), \
+                         0, s, a);                                                        \
+      return hipGetLastError();                                                           \
+    }                                                                                     \
+    break;
+    DWC_SWEEP_F_LIST(DWC_CASE)
+#undef DWC_CASE
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int TJ>
+hipError_t wgrad_sweep_by_f(int f, const SweepArgs& a, int blocks, hipStream_t s) {
+  switch (f) {
+#define DWC_CASE(F)                                                                       \
+  case F:                                                                                 \
+    if constexpr (TJ == 7 || F <= 5) {                                                    \
+      hipLaunchKernelGGL((wgrad_sweep<kDt, F, TJ>), dim3(blocks), dim3(kBlockThreads), 0, \
+                         s, a);                                                           \
+      return hipGetLastError();                                                           \
+    }                                                                                     \
+    break;
+    DWC_SWEEP_F_LIST(DWC_CASE)
+#undef DWC_CASE
+  }
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
+
+hipError_t DWC_CAT(launch_fwd_sweep_dt, DWC_INST_DT)(int f, int tmw, bool flip, const SweepArgs& a,
+                                                     int blocks, hipStream_t st) {
+  if (tmw == 7) return flip ? fwd_sweep_by_f<7, true>(f, a, blocks, st)
+                            : fwd_sweep_by_f<7, false>(f, a, blocks, st);
+  if (tmw == 14) return flip ? fwd_sweep_by_f<14, true>(f, a, blocks, st)
+                             : fwd_sweep_by_f<14, false>(f, a, blocks, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t DWC_CAT(launch_wgrad_sweep_dt, DWC_INST_DT)(int f, int tj, const SweepArgs& a,
+                                                       int blocks, hipStream_t st) {
+  if (tj == 7) return wgrad_sweep_by_f<7>(f, a, blocks, st);
+  if (tj == 14) return wgrad_sweep_by_f<14>(f, a, blocks, st);
+  return hipErrorInvalidValue;
+}
 
 // s: the stride of both spatial axes (1 or 2; the data gradient only 1).
 hipError_t DWC_CAT(launch_fwd_direct_dt, DWC_INST_DT)(int fw, int s, int tmw, bool flip,

@@ -99,10 +99,13 @@ def test_direct_unavailable_is_unsupported():
 def test_plans_for_the_named_workloads():
     p = dwc.problem(64, 56, 56, 128, 7, 7, 1, 3)
     d = dwc.plan_describe(p, 0)
-    assert d.startswith("fwd direct") and "tmw=14" in d and "flip=0" in d
-    assert "flip=1" in dwc.plan_describe(p, 1)
+    assert d.startswith("fwd sweep") and "strip=7" in d
+    assert dwc.plan_describe(p, 1).startswith("bwd_data sweep")
     d = dwc.plan_describe(p, 2)
-    assert d.startswith("bwd_filter direct")
+    assert d.startswith("bwd_filter sweep")
+    p = dwc.problem(32, 56, 56, 128, 31, 31, 1, 15)
+    assert dwc.plan_describe(p, 0).startswith("fwd direct")
+    assert dwc.plan_describe(p, 2).startswith("bwd_filter direct")
     p = dwc.problem(64, 56, 56, 128, 7, 7, 2, 3)
     assert "sw=2" in dwc.plan_describe(p, 0)
     p = dwc.problem(128, 28, 28, 512, 13, 13, 1, 6, dtype=dwc.BF16)
