@@ -10,12 +10,19 @@ bound).  The JSON line also carries the roofline of the dominant kernel and
 the CPU oracle's rate on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+       python bench.py --copy-calibration  (a plain 256 MiB device copy, for counters)
        python bench.py --sweep OUT.jsonl   (every named workload, one line per op)
+       python bench.py --summarize-profile TRACE_DIR FETCH_DIR WRITE_DIR COPYF_DIR COPYW_DIR
+           (turn rocprofv3 CSV output of this benchmark into profiles/*.md and
+            profiles/traffic.json; see profiles/README.md for the commands)
 """
 
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -33,6 +40,21 @@ PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
 PEAK_FP32_VECTOR = 157.3e12
 PEAK_BF16_MFMA = 2.5e15
 ROTATE_BYTES = 1 << 30     # buffer sets rotate over >= 1 GiB: no Infinity-Cache reuse
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["depthwise_convolution_dwc_amd/csrc/dwc_kernels.h",
+                  "depthwise_convolution_dwc_amd/csrc/dwc_plan.cpp",
+                  "depthwise_convolution_dwc_amd/csrc/inst_direct.hip",
+                  "depthwise_convolution_dwc_amd/csrc/inst_generic.hip"]
+
+
+def kernel_source_hash() -> str:
+    """Hash of the sources that decide which kernels run and what they do;
+    stored counter data is only used while it matches."""
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def log(*a):
@@ -84,6 +106,24 @@ def op_model(s: Shape, op: str, dtype: str) -> dict:
                 bytes=bytes_alg, peak=peak, roofline=r_lit,
                 bound=("hbm" if PEAK_HBM * eta / eb < peak else
                        ("alu" if dtype == "f32" else "mfma")))
+
+
+def stored_traffic(kernel_names):
+    """HBM bytes per launch of the named kernels from profiles/traffic.json,
+    or None if absent or taken on other kernel sources."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    total = 0.0
+    for k in kernel_names:
+        if k not in t["kernels"]:
+            return None
+        total += t["kernels"][k]["bytes_per_launch"]
+    return total
 
 
 def roofline_entry(m: dict, seconds: float, traffic=None) -> dict:
@@ -200,17 +240,34 @@ def cpu_baseline(inp, plan, budget_s=12.0):
 
     t1, _ = run(1)
     n = int(max(1, min(inp.shape.n, round(budget_s / max(t1, 1e-3)))))
-    t, flops = run(n)
+    t, flops, reps = 0.0, 0.0, 0
+    while t < budget_s or reps == 0:  # whole passes until the budget is spent
+        dt, df = run(n)
+        t, flops, reps = t + dt, flops + df, reps + 1
     cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
     return {"value": round(flops / t / 1e9, 3), "unit": "GFLOP/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"same step on the first {n} of {inp.shape.n} images, float64, "
-                      f"{t:.1f} s"}
+            "sample": f"the same step on the first {n} of {inp.shape.n} images, {reps} passes, "
+                      f"float64 on the host, {t:.1f} s"}
 
 
 # ------------------------------------------------------------------ main ----
 
 HEADLINE = "fwd_n64_56x56_c128_k7"
+
+
+def kernels_of(dwc, s, op):
+    """Short names of the kernels one library call launches (from its plan)."""
+    p = dwc.problem(s.n, s.h, s.w, s.c, s.fh, s.fw, (s.stride_h, s.stride_w), (s.pad_h, s.pad_w))
+    d = dwc.plan_describe(p, {"fwd": 0, "bwd_data": 1, "bwd_filter": 2}[op])
+    fam = d.split()[1]  # sweep / direct / generic
+    base = {("fwd", "sweep"): "fwd_sweep", ("bwd_data", "sweep"): "fwd_sweep",
+            ("bwd_filter", "sweep"): "wgrad_sweep", ("fwd", "direct"): "fwd_rows",
+            ("bwd_data", "direct"): "fwd_rows", ("bwd_filter", "direct"): "wgrad_rows"}
+    k = [base.get((op, fam), fam)]
+    if op == "bwd_filter" and "ws_bytes=0" not in d:
+        k.append("reduce_partials")
+    return k
 
 
 def headline_plan():
@@ -248,7 +305,27 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--sweep", default=None, help="write per-op lines of every workload here")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy 256 MiB a few times (scales the byte counters)")
+    ap.add_argument("--summarize-profile", nargs=5, default=None,
+                    metavar=("TRACE", "FETCH", "WRITE", "COPYF", "COPYW"))
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        x = torch.randn(64 * 1024 * 1024, device="cuda")  # 256 MiB
+        y = torch.empty_like(x)
+        for _ in range(5):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print("copied 256 MiB 5 times", flush=True)
+        return
+    if args.summarize_profile:
+        trace_md, traffic_md, fs, ws = summarize_profile(*args.summarize_profile)
+        print(trace_md)
+        print()
+        print(traffic_md)
+        print(f"\nFETCH_SIZE scale {fs:.3f}, WRITE_SIZE scale {ws:.3f} (from a 256 MiB copy)")
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(this DWC library runs on a single device)", file=sys.stderr)
@@ -284,8 +361,11 @@ def main():
                      "roofline_frac": round(m["flops"] / (t * 1e-3) / m["roofline"], 4),
                      "bound": m["bound"]}
     dom = int(np.argmax(per_op))
-    roof = roofline_entry(models[dom], per_op[dom] * 1e-3)
-    roof["kernel"] = names[dom]
+    s_dom, op_dom = plan[dom]
+    kern = kernels_of(dwc, s_dom, op_dom)
+    roof = roofline_entry(models[dom], per_op[dom] * 1e-3, stored_traffic(kern))
+    roof["kernel"] = "+".join(kern)
+    roof["op"] = names[dom]
     cpu = None
     if not args.no_cpu:
         log("bench: timing the CPU oracle on a sample of the batch")
@@ -312,6 +392,76 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def _kernel_short(name: str) -> str:
+    # "void dwc::fwd_sweep<0, 7, 7, false>(dwc::SweepArgs)" -> "fwd_sweep"
+    n = name.split("(")[0].replace("void ", "").replace("dwc::", "")
+    return n.split("<")[0].strip()
+
+
+def _csv_rows(d, pattern):
+    files = glob.glob(os.path.join(d, "**", pattern), recursive=True)
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def summarize_profile(trace_dir, fetch_dir, write_dir, copyf_dir, copyw_dir):
+    """Write profiles/ summaries from rocprofv3 CSV output of this benchmark."""
+    os.makedirs(PROFILES, exist_ok=True)
+    # kernel trace: per-kernel durations
+    stats = {}
+    for r in _csv_rows(trace_dir, "*kernel_trace.csv"):
+        k = r["Kernel_Name"]
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        stats.setdefault(k, []).append(d)
+    lines = ["| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    for k, v in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{k}` | {len(v)} | {np.mean(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+    trace_md = "\n".join(lines)
+
+    def per_kernel(d, counter):
+        acc = {}
+        for r in _csv_rows(d, "*counter_collection.csv"):
+            if r["Counter_Name"] != counter:
+                continue
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
+        return {k: float(np.mean(v)) for k, v in acc.items()}
+
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    cf = per_kernel(copyf_dir, "FETCH_SIZE")
+    cw = per_kernel(copyw_dir, "WRITE_SIZE")
+    copy_bytes = 256 * 1024 * 1024  # the calibration copy moves 256 MiB each way
+    ck = [k for k in cf if "copyBuffer" in k]
+    f_scale = copy_bytes / cf[ck[0]] if ck else 1.0
+    w_scale = copy_bytes / cw[ck[0]] if ck else 1.0
+    kernels = {}
+    for k in set(fetch) | set(write):
+        short = _kernel_short(k)
+        fb = fetch.get(k, 0.0) * f_scale
+        wb = write.get(k, 0.0) * w_scale
+        kernels.setdefault(short, {"fetch_bytes": 0.0, "write_bytes": 0.0, "n": 0, "names": []})
+        e = kernels[short]
+        e["fetch_bytes"] += fb
+        e["write_bytes"] += wb
+        e["n"] += 1
+        e["names"].append(k)
+    for e in kernels.values():
+        e["fetch_bytes"] /= e["n"]
+        e["write_bytes"] /= e["n"]
+        e["bytes_per_launch"] = e["fetch_bytes"] + e["write_bytes"]
+    out = {"source_hash": kernel_source_hash(), "fetch_scale": f_scale, "write_scale": w_scale,
+           "kernels": kernels}
+    with open(os.path.join(PROFILES, "traffic.json"), "w") as f:
+        json.dump(out, f, indent=1, sort_keys=True)
+    tl = ["| kernel | FETCH bytes/launch | WRITE bytes/launch | total |", "|---|---|---|---|"]
+    for k, e in sorted(kernels.items()):
+        tl.append(f"| `{k}` | {e['fetch_bytes'] / 1e6:.1f} MB | {e['write_bytes'] / 1e6:.1f} MB | "
+                  f"{e['bytes_per_launch'] / 1e6:.1f} MB |")
+    return trace_md, "\n".join(tl), f_scale, w_scale
 
 
 def sweep(dwc, torch, dev, args):
