@@ -150,8 +150,8 @@ def upload(op, torch, dev):
 class OpCall:
     """One library call on preallocated buffers."""
 
-    def __init__(self, dwc, torch, s: Shape, op: str, bufs: dict):
-        self.s, self.op, self.b = s, op, bufs
+    def __init__(self, dwc, torch, s: Shape, op: str, bufs: dict, algo: str = "auto"):
+        self.s, self.op, self.b, self.algo = s, op, bufs, algo
         self.dwc, self.torch = dwc, torch
         stride, pad = (s.stride_h, s.stride_w), (s.pad_h, s.pad_w)
         self.stride, self.pad = stride, pad
@@ -162,19 +162,20 @@ class OpCall:
             self.out = torch.empty(s.x_shape(), dtype=torch.float32, device=dev)
         else:
             self.out = torch.empty(s.w_shape(), dtype=torch.float32, device=dev)
-            p = dwc.problem(s.n, s.h, s.w, s.c, s.fh, s.fw, stride, pad, bufs["x"].dtype)
+            p = dwc.problem(s.n, s.h, s.w, s.c, s.fh, s.fw, stride, pad, bufs["x"].dtype, algo)
             need = dwc.workspace_size(p)
             self.ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
 
     def __call__(self):
         b, s = self.b, self.s
         if self.op == "fwd":
-            self.dwc.fwd(b["x"], b["w"], self.stride, self.pad, out=self.out)
+            self.dwc.fwd(b["x"], b["w"], self.stride, self.pad, out=self.out, algo=self.algo)
         elif self.op == "bwd_data":
-            self.dwc.bwd_data(b["dy"], b["w"], (s.h, s.w), self.stride, self.pad, out=self.out)
+            self.dwc.bwd_data(b["dy"], b["w"], (s.h, s.w), self.stride, self.pad, out=self.out,
+                              algo=self.algo)
         else:
             self.dwc.bwd_filter(b["x"], b["dy"], (s.fh, s.fw), self.stride, self.pad,
-                                out=self.out, workspace=self.ws)
+                                out=self.out, workspace=self.ws, algo=self.algo)
 
 
 def time_step(torch, calls_per_set, steps, warmup):
@@ -263,7 +264,8 @@ def kernels_of(dwc, s, op):
     fam = d.split()[1]  # sweep / direct / generic
     base = {("fwd", "sweep"): "fwd_sweep", ("bwd_data", "sweep"): "fwd_sweep",
             ("bwd_filter", "sweep"): "wgrad_sweep", ("fwd", "direct"): "fwd_rows",
-            ("bwd_data", "direct"): "fwd_rows", ("bwd_filter", "direct"): "wgrad_rows"}
+            ("bwd_data", "direct"): "fwd_rows", ("bwd_filter", "direct"): "wgrad_rows",
+            ("fwd", "mfma"): "fwd_mfma", ("bwd_data", "mfma"): "fwd_mfma"}
     k = [base.get((op, fam), fam)]
     if op == "bwd_filter" and "ws_bytes=0" not in d:
         k.append("reduce_partials")
@@ -275,7 +277,7 @@ def headline_plan():
     return [(s1, "fwd"), (s2, "fwd"), (s1, "bwd_data"), (s1, "bwd_filter")]
 
 
-def build_sets(dwc, torch, plan, inp, dev):
+def build_sets(dwc, torch, plan, inp, dev, algo="auto"):
     """Enough buffer sets (each a full copy of the operands) to rotate over
     ROTATE_BYTES, so no step reads a set the previous steps left in cache."""
     set_bytes = 0
@@ -292,7 +294,7 @@ def build_sets(dwc, torch, plan, inp, dev):
             b = dict(bufs)
             if op != "fwd" and (s.oh, s.ow) != tuple(bufs["dy"].shape[1:3]):
                 b["dy"] = bufs["dy"][:, :s.oh, :s.ow].contiguous()
-            calls.append(OpCall(dwc, torch, s, op, b))
+            calls.append(OpCall(dwc, torch, s, op, b, algo))
         sets.append(calls)
     return sets
 
@@ -470,17 +472,20 @@ def sweep(dwc, torch, dev, args):
         for s in wl["shapes"]:
             for dt in wl["dtypes"]:
                 inp = make_inputs(s, dt, seed=0, x_dist=wl["x_dist"], w_dist=wl["w_dist"])
-                for op in wl["ops"]:
+                # half-precision operands: the vector kernels and the library's
+                # choice (the packed-MFMA kernels where they apply) side by side
+                for op, algo in [(o, a) for o in wl["ops"]
+                                 for a in (("direct", "auto") if dt != "f32" else ("auto",))]:
                     plan = [(s, op)]
-                    sets = build_sets(dwc, torch, plan, inp, dev)
+                    sets = build_sets(dwc, torch, plan, inp, dev, algo)
                     steps = max(10, min(args.steps, 200))
                     ms, _ = time_step(torch, sets, steps, min(args.warmup, 10))
                     m = op_model(s, op, dt)
                     p = dwc.problem(s.n, s.h, s.w, s.c, s.fh, s.fw, (s.stride_h, s.stride_w),
-                                    (s.pad_h, s.pad_w), {"f32": 0, "bf16": 1, "f16": 2}[dt])
+                                    (s.pad_h, s.pad_w), {"f32": 0, "bf16": 1, "f16": 2}[dt], algo)
                     rec = {"workload": name, "shape": [s.n, s.h, s.w, s.c, s.fh, s.fw,
                                                        s.stride_h, s.pad_h],
-                           "dtype": dt, "op": op, "ms": round(ms, 5),
+                           "dtype": dt, "op": op, "algo": algo, "ms": round(ms, 5),
                            "gflops": round(m["flops"] / (ms * 1e-3) / 1e9, 1),
                            "gflops_valid": round(m["flops_valid"] / (ms * 1e-3) / 1e9, 1),
                            "valid_frac": round(m["flops_valid"] / m["flops"], 3),

@@ -38,6 +38,9 @@ def _units():
     for dt in (0, 1, 2):
         u.append(("hip", "inst_direct.hip", f"inst_direct_dt{dt}.o", [f"-DDWC_INST_DT={dt}"]))
     u.append(("hip", "inst_generic.hip", "inst_generic.o", []))
+    # MFMA accumulators in VGPRs: with AGPR accumulators the compiler moves
+    # them between registers on every filter-row iteration
+    u.append(("hip", "inst_mfma.hip", "inst_mfma.o", ["-mllvm", "-amdgpu-mfma-vgpr-form"]))
     u.append(("hip", "dwc_api.cpp", "dwc_api.o", ["-x", "hip"]))
     u.append(("cxx", "dwc_plan.cpp", "dwc_plan.o", []))
     return u

@@ -19,6 +19,13 @@ int hip_fail(hipError_t e, const char* what) {
 
 hipError_t launch_fwd_type(const Plan& pl, const void* in, const void* filt, float* out,
                            hipStream_t s) {
+  if (pl.kind == PLAN_MFMA) {
+    MfmaArgs m = pl.ma;
+    m.in = in;
+    m.filt = filt;
+    m.out = out;
+    return launch_fwd_mfma(pl.dt, pl.nf, pl.tiles, pl.flip, m, s);
+  }
   if (pl.kind == PLAN_DIRECT) {
     FwdArgs a = pl.fa;
     a.in = in;
@@ -50,10 +57,28 @@ hipError_t launch_fwd_type(const Plan& pl, const void* in, const void* filt, flo
   return launch_generic(pl.gen_kind, pl.dt, g, s);
 }
 
+bool aligned16(const void* a) { return ((uintptr_t)a & 15) == 0; }
+
 int prepare(const dwc_problem* p, int op, Plan* pl, const void* in0, const void* in1,
             const void* out, const void* ws, size_t ws_bytes) {
   std::string err;
   int st = make_plan(p, op, pl, &err);
+  // The packed-MFMA kernels move 16-byte vectors: with a tensor that is not
+  // 16-byte aligned, AUTO takes the vector kernels and MFMA is an error.
+  if (st == DWC_OK && pl->kind == PLAN_MFMA && !pl->empty &&
+      !(aligned16(in0) && aligned16(in1) && aligned16(out))) {
+    if (p->algo == DWC_ALGO_MFMA) {
+      set_last_error("packed-MFMA kernels need 16-byte aligned tensors");
+      return DWC_ERR_MISALIGNED;
+    }
+    dwc_problem d = *p;
+    d.algo = DWC_ALGO_DIRECT;
+    st = make_plan(&d, op, pl, &err);
+    if (st == DWC_ERR_UNSUPPORTED) {
+      d.algo = DWC_ALGO_GENERIC;
+      st = make_plan(&d, op, pl, &err);
+    }
+  }
   if (st == DWC_OK) st = check_pointers(p, *pl, in0, in1, out, ws, ws_bytes, &err);
   if (st != DWC_OK) set_last_error(err);
   return st;

@@ -88,6 +88,30 @@ struct WgradArgs {
   int num_items;     // workgroups: Z * cblocks * fh_tiles
 };
 
+// Packed-MFMA forward-type kernel (bf16/fp16 operands, stride 1).  Per
+// channel, a 16 x 16 block of outputs -- 16 (output row, 16-column group)
+// combinations x 16 consecutive columns -- is one v_mfma_f32_16x16x32 per
+// filter row and 16-tap fragment: A holds 32 consecutive input columns per
+// combination, B the Toeplitz band of one 16-tap slice of the filter row.
+// A workgroup owns CB channels x rblk output rows of one image.
+// LDS per packed-MFMA workgroup: at most half of a CU's 160 KiB, so two
+// workgroups share a CU and one's loads and stores overlap the other's MFMAs.
+constexpr int kMfmaMaxLds = 81920;
+
+struct MfmaArgs {
+  const void* in;    // N x IH x IW x C (X, or dY for the data gradient)
+  const void* filt;  // FH x FW x C
+  float* out;        // N x OH x OW x C
+  int N, IH, IW, C, OH, OW;
+  int FH, FW, PH, PW;  // PH/PW < 0 crop (data gradient with pad > F-1)
+  int gt;            // column groups per tile: 1, 2 or 4 (rows per tile 16 / gt)
+  int rblk;          // output rows per workgroup: tiles * 16 / gt
+  int rch, cblk;     // row chunks per image, channel blocks
+  int xr, wt;        // staged input tile: rows, columns (= row pitch)
+  int lds_bytes;
+  int num_blocks;
+};
+
 // out[i] = sum_{z < Z} ws[z * M + i], summed in order of z.
 struct ReduceArgs {
   const float* ws;

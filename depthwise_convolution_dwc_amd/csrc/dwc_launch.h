@@ -34,6 +34,12 @@ DWC_DECL_SWEEP(1)
 DWC_DECL_SWEEP(2)
 #undef DWC_DECL_SWEEP
 
+// Packed-MFMA forward-type kernel (bf16 / fp16 operands, stride 1): nf
+// 16-tap fragments per filter row (CB = 16 channels per workgroup for nf 1,
+// 8 for nf 2), tiles of 16 combinations per channel.
+hipError_t launch_fwd_mfma(int dt, int nf, int tiles, bool flip, const MfmaArgs& a,
+                           hipStream_t s);
+
 enum GenericKind { GEN_FWD = 0, GEN_FWD_FLIP = 1, GEN_DGRAD = 2, GEN_WGRAD = 3 };
 hipError_t launch_generic(int kind, int dt, const GenericArgs& a, hipStream_t st);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t st);

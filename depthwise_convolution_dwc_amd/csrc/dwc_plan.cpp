@@ -96,6 +96,61 @@ int pick_split(int64_t rows, int64_t per_slice_blocks, int64_t strips, int64_t m
   return (int)std::min<int64_t>(z, 65535);
 }
 
+// Packed-MFMA plan of a forward-type problem (the forward map, or the
+// stride-1 data gradient as the forward map of dY): false if the kernel does
+// not apply.  Tiles of 16 (row, 16-column group) combinations: gt groups x
+// 16/gt rows; 1, 2 or 4 tiles per channel and workgroup -- as many as the
+// image height asks for (each filter-row operand B is built once per tile
+// set) while the staged input tile, the filter and (afterwards) the staged
+// outputs fit the workgroup's LDS.
+bool plan_mfma(const FwdArgs& f, int dt, bool flip, Plan* q) {
+  if (dt == DT_F32 || f.SH != 1 || f.SW != 1 || f.FW > 32 || f.C % 8 != 0) return false;
+  const int groups = (f.OW + 15) / 16;
+  const int gt = groups <= 1 ? 1 : groups <= 2 ? 2 : groups <= 4 ? 4 : 0;
+  if (gt == 0) return false;
+  const int rt = 16 / gt;
+  const int nf = (f.FW + 15) / 16;
+  const int cb = nf == 1 ? 16 : 8;
+  const int need = (f.OH + rt - 1) / rt;
+  MfmaArgs m{};
+  m.N = f.N; m.IH = f.IH; m.IW = f.IW; m.C = f.C; m.OH = f.OH; m.OW = f.OW;
+  m.FH = f.FH; m.FW = f.FW; m.PH = f.PH; m.PW = f.PW;
+  m.gt = gt;
+  m.wt = 16 * (gt + nf);
+  int tiles = need <= 1 ? 1 : need <= 2 ? 2 : 4;
+  // DWC_MFMA_TILES (1, 2 or 4) caps the tiles per workgroup, for A/B timing
+  if (const char* v = getenv("DWC_MFMA_TILES")) {
+    const int t = atoi(v);
+    if (t == 1 || t == 2 || t == 4) tiles = std::min(tiles, t);
+  }
+  int64_t lds = 0;
+  for (;; tiles /= 2) {
+    m.rblk = tiles * rt;
+    m.xr = m.rblk + f.FH - 1;
+    const int64_t in_bytes =
+        (int64_t)cb * m.xr * m.wt * 2 + ((int64_t)cb * f.FH * f.FW * 2 + 15) / 16 * 16;
+    const int64_t out_bytes = (int64_t)m.rblk * f.OW * (cb + 4) * 4;
+    lds = std::max(in_bytes, out_bytes);
+    if (lds <= kMfmaMaxLds) break;
+    if (tiles == 1) return false;
+  }
+  m.lds_bytes = (int)lds;
+  m.rch = (f.OH + m.rblk - 1) / m.rblk;
+  m.cblk = (f.C + cb - 1) / cb;
+  const int64_t blocks = (int64_t)f.N * m.cblk * m.rch;
+  if (blocks > kI32Max) return false;
+  m.num_blocks = (int)blocks;
+  q->kind = PLAN_MFMA;
+  q->flip = flip;
+  q->nf = nf;
+  q->cb = cb;
+  q->tiles = tiles;
+  q->blocks = (int)blocks;
+  q->ma = m;
+  q->fa = f;
+  return true;
+}
+
 }  // namespace
 
 void set_last_error(const std::string& msg) { g_last_error = msg; }
@@ -114,7 +169,7 @@ int make_plan(const dwc_problem* p, int op, Plan* pl, std::string* err) {
     return fail(err, DWC_ERR_BAD_PARAM, "in_dtype must be DWC_F32, DWC_BF16 or DWC_F16");
   if (p->out_dtype != DWC_F32)
     return fail(err, DWC_ERR_UNSUPPORTED, "outputs are fp32 only (out_dtype must be DWC_F32)");
-  if (p->algo < DWC_ALGO_AUTO || p->algo > DWC_ALGO_GENERIC)
+  if (p->algo < DWC_ALGO_AUTO || p->algo > DWC_ALGO_MFMA)
     return fail(err, DWC_ERR_BAD_PARAM, "unknown algo");
   if (p->wgrad_split < 0) return fail(err, DWC_ERR_BAD_PARAM, "wgrad_split must be >= 0");
   const int64_t a = p->h + 2 * (int64_t)p->pad_h - p->fh;
@@ -172,6 +227,18 @@ int make_plan(const dwc_problem* p, int op, Plan* pl, std::string* err) {
     f.SW = p->stride_w;
     f.PH = bwd ? p->fh - 1 - p->pad_h : p->pad_h;
     f.PW = bwd ? p->fw - 1 - p->pad_w : p->pad_w;
+    // Packed MFMA for half-precision operands (the stride-1 data gradient
+    // too: stride 1 is part of the kernel's conditions).
+    if (p->algo == DWC_ALGO_AUTO || p->algo == DWC_ALGO_MFMA) {
+      if (plan_mfma(f, dt, bwd, &q)) {
+        *pl = q;
+        return DWC_OK;
+      }
+      if (p->algo == DWC_ALGO_MFMA)
+        return fail(err, DWC_ERR_UNSUPPORTED,
+                    "no packed-MFMA kernel for this problem (needs bf16/fp16, stride 1, "
+                    "FW <= 32, C % 8 == 0, output width <= 64)");
+    }
     if (direct) {
       q.flip = bwd;
       q.sweep = sweep_ok;
@@ -230,6 +297,8 @@ int make_plan(const dwc_problem* p, int op, Plan* pl, std::string* err) {
       q.ga = g;
     }
   } else {
+    if (p->algo == DWC_ALGO_MFMA)
+      return fail(err, DWC_ERR_UNSUPPORTED, "no packed-MFMA filter-gradient kernel");
     const int64_t rows = p->n * oh;
     const int64_t m = (int64_t)p->fh * p->fw * p->c;
     const double flops = 2.0 * (double)p->n * oh * ow * p->c * p->fh * p->fw;
@@ -367,6 +436,15 @@ int check_pointers(const dwc_problem* p, const Plan& pl, const void* in0, const 
 std::string describe(const Plan& pl) {
   static const char* ops[] = {"fwd", "bwd_data", "bwd_filter"};
   char buf[512];
+  if (pl.kind == PLAN_MFMA) {
+    const MfmaArgs& m = pl.ma;
+    snprintf(buf, sizeof buf,
+             "%s mfma dt=%s fw=%d fh=%d flip=%d nf=%d cb=%d gt=%d tiles=%d rblk=%d xr=%d wt=%d "
+             "lds=%d rch=%d cblk=%d blocks=%d",
+             ops[pl.op], dt_name(pl.dt), m.FW, m.FH, (int)pl.flip, pl.nf, pl.cb, m.gt, pl.tiles,
+             m.rblk, m.xr, m.wt, m.lds_bytes, m.rch, m.cblk, pl.blocks);
+    return buf;
+  }
   if (pl.kind == PLAN_DIRECT && pl.sweep) {
     const SweepArgs& w = pl.sa;
     snprintf(buf, sizeof buf,

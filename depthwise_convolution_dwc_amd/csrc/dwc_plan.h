@@ -11,7 +11,7 @@
 
 namespace dwc {
 
-enum PlanKind { PLAN_NONE = 0, PLAN_DIRECT = 1, PLAN_GENERIC = 2 };
+enum PlanKind { PLAN_NONE = 0, PLAN_DIRECT = 1, PLAN_GENERIC = 2, PLAN_MFMA = 3 };
 
 struct Plan {
   int op = 0;
@@ -35,6 +35,10 @@ struct Plan {
 
   // sweep kernels (stride 1, square filters up to 9x9)
   SweepArgs sa{};
+
+  // packed-MFMA forward-type kernel
+  int nf = 0, cb = 0, tiles = 0;
+  MfmaArgs ma{};
 
   // generic kernels
   int gen_kind = 0;

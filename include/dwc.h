@@ -59,7 +59,13 @@ typedef enum {
 typedef enum {
     DWC_ALGO_AUTO = 0,   /* library's choice                                */
     DWC_ALGO_DIRECT = 1, /* register-window vector kernels                  */
-    DWC_ALGO_GENERIC = 2 /* one output per lane; any filter size or stride  */
+    DWC_ALGO_GENERIC = 2, /* one output per lane; any filter size or stride */
+    DWC_ALGO_MFMA = 3     /* packed matrix-core kernels (bf16/fp16 operands,
+                             stride 1, FW <= 32, C a multiple of 8, output
+                             width <= 64, 16-byte aligned tensors): the
+                             GEMV-to-GEMM packing of §4.2 on CDNA4 MFMA.
+                             Forward and data gradient only; AUTO picks it
+                             for those when it applies                    */
 } dwc_algo;
 
 typedef enum {

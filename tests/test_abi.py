@@ -154,3 +154,35 @@ def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(dwc, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         dwc.lib()
+
+
+def test_mfma_plans_and_rejections():
+    p = dwc.problem(128, 28, 28, 512, 13, 13, 1, 6, dtype=dwc.BF16)
+    assert dwc.plan_describe(p, 0).startswith("fwd mfma")
+    assert dwc.plan_describe(p, 1).startswith("bwd_data mfma")
+    p = dwc.problem(128, 28, 28, 512, 31, 31, 1, 15, dtype=dwc.F16)
+    d = dwc.plan_describe(p, 0)
+    assert d.startswith("fwd mfma") and "nf=2" in d
+    # the vector kernels stay reachable
+    p = dwc.problem(128, 28, 28, 512, 13, 13, 1, 6, dtype=dwc.BF16, algo="direct")
+    assert dwc.plan_describe(p, 0).startswith("fwd direct")
+    # conditions of the packed kernel: half-precision operands, stride 1,
+    # C a multiple of 8, FW <= 32, output width <= 64; no filter gradient
+    for kw in (dict(dtype=dwc.F32), dict(stride=2), dict(c=12), dict(fw=33, pad=16),
+               dict(w=80)):
+        a = dict(n=2, h=20, w=20, c=16, fh=5, fw=5, stride=1, pad=2, dtype=dwc.BF16)
+        a.update(kw)
+        q = dwc.problem(a["n"], a["h"], a["w"], a["c"], a["fh"], a["fw"], a["stride"],
+                        a["pad"], dtype=a["dtype"], algo="mfma")
+        assert dwc.check(q, 0) == 2, kw
+        assert "packed-MFMA" in dwc.last_error()
+    q = dwc.problem(2, 20, 20, 16, 5, 5, 1, 2, dtype=dwc.BF16, algo="mfma")
+    assert dwc.check(q, 0) == 0 and dwc.check(q, 1) == 0
+    assert dwc.check(q, 2) == 2
+
+
+def test_mfma_forced_misaligned_is_rejected_before_launch():
+    p = dwc.problem(1, 8, 8, 16, 3, 3, 1, 1, dtype=dwc.BF16, algo="mfma")
+    L = dwc.lib()
+    assert L.dwc_fwd(ctypes.byref(p), 0x10002, 0x20000, 0x30000, None) == 3
+    assert L.dwc_bwd_data(ctypes.byref(p), 0x10000, 0x20000, 0x30008, None) == 3

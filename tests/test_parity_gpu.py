@@ -61,6 +61,21 @@ def _run(op, s: Shape, inp, algo, wgrad_split=0):
     return got.double().cpu().numpy()
 
 
+OPS = {"fwd": 0, "bwd_data": 1, "bwd_filter": 2}
+DT = {"f32": dwc.F32, "bf16": dwc.BF16, "f16": dwc.F16}
+
+
+def _algos(op, s: Shape, dtype):
+    """Every kernel family that accepts this problem."""
+    out = []
+    for algo in ("auto", "direct", "mfma", "generic"):
+        p = dwc.problem(s.n, s.h, s.w, s.c, s.fh, s.fw, (s.stride_h, s.stride_w),
+                        (s.pad_h, s.pad_w), dtype=DT[dtype], algo=algo)
+        if dwc.check(p, OPS[op]) == 0:
+            out.append(algo)
+    return out
+
+
 def _want(op, s: Shape, inp):
     stride, pad = (s.stride_h, s.stride_w), (s.pad_h, s.pad_w)
     if op == "fwd":
@@ -77,7 +92,7 @@ def test_small_parity(shape, op, dtype):
     s = _shape(shape)
     inp = make_inputs(s, dtype, seed=sum(shape[:6]))
     want = _want(op, s, inp)
-    for algo in ("auto", "generic"):
+    for algo in _algos(op, s, dtype):
         log(f"case {shape} {op} {dtype} {algo}")
         got = _run(op, s, inp, algo)
         assert got.shape == want.shape
@@ -146,3 +161,76 @@ def test_caller_stream_is_used():
         y = dwc.fwd(x, w, 1, 3)
     st.synchronize()
     assert rel_l2(y.double().cpu().numpy(), _want("fwd", s, inp)) <= 1e-5
+
+
+# Shapes for the packed-MFMA kernel (bf16/fp16, stride 1): every tile shape
+# (column groups per tile 1, 2, 4; one or two tiles), both fragment counts,
+# a half-filled channel block, FH != FW, no padding, and data-gradient
+# padding larger than F-1 (a cropping forward map).
+MFMA_SHAPES = [
+    (1, 6, 6, 16, 3, 3, 1, 1),
+    (2, 20, 13, 24, 5, 5, 1, 2),
+    (1, 28, 28, 32, 13, 13, 1, 6),
+    (1, 9, 40, 16, 7, 5, 1, 3),
+    (1, 11, 11, 8, 31, 31, 1, 15),
+    (2, 19, 21, 40, 17, 17, 1, 8),
+    (1, 12, 12, 16, 32, 32, 1, 16),
+    (2, 7, 7, 16, 3, 3, 1, 0),
+    (1, 10, 10, 16, 3, 3, 1, 4),
+    (1, 30, 64, 16, 9, 1, 1, (4, 0)),
+    (3, 16, 16, 8, 1, 31, 1, (0, 15)),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("op", ["fwd", "bwd_data"])
+@pytest.mark.parametrize("shape", MFMA_SHAPES,
+                         ids=lambda t: "x".join(map(str, t[:6])) + f"_p{t[7]}")
+def test_mfma_parity(shape, op, dtype):
+    s = _shape(shape)
+    assert "mfma" in _algos(op, s, dtype), "shape meant for the packed-MFMA kernel"
+    inp = make_inputs(s, dtype, seed=31 + sum(shape[:6]))
+    want = _want(op, s, inp)
+    log(f"case mfma {shape} {op} {dtype}")
+    got = _run(op, s, inp, "mfma")
+    err = rel_l2(got, want)
+    assert err <= TOL[dtype], err
+    assert np.all(np.isfinite(got))
+
+
+def _misaligned(t):
+    """A copy of t whose storage starts 2 bytes past a 16-byte boundary."""
+    flat = torch.empty(t.numel() + 8, dtype=t.dtype, device=t.device)
+    v = flat[1:1 + t.numel()].view(t.shape)
+    v.copy_(t)
+    assert v.data_ptr() % 16 != 0
+    return v
+
+
+def test_mfma_misaligned_tensors():
+    """AUTO falls back to the vector kernels; forcing MFMA is an error."""
+    s = Shape(2, 14, 14, 32, 7, 7, 1, 1, 3, 3)
+    inp = make_inputs(s, "bf16", seed=3)
+    want = _want("fwd", s, inp)
+    x = _misaligned(to_device(inp.x))
+    w = to_device(inp.w)
+    got = dwc.fwd(x, w, 1, 3)
+    sync()
+    assert rel_l2(got.double().cpu().numpy(), want) <= TOL["bf16"]
+    with pytest.raises(dwc.DwcError):
+        dwc.fwd(x, w, 1, 3, algo="mfma")
+
+
+@pytest.mark.parametrize("op", ["fwd", "bwd_data"])
+def test_mfma_outputs_fully_overwritten(op):
+    s = Shape(2, 21, 19, 40, 9, 9, 1, 1, 4, 4)
+    inp = make_inputs(s, "bf16", seed=4)
+    if op == "fwd":
+        y = torch.full(s.y_shape(), float("nan"), device="cuda")
+        dwc.fwd(to_device(inp.x), to_device(inp.w), 1, 4, out=y, algo="mfma")
+    else:
+        y = torch.full(s.x_shape(), float("nan"), device="cuda")
+        dwc.bwd_data(to_device(inp.dy), to_device(inp.w), (21, 19), 1, 4, out=y, algo="mfma")
+    sync()
+    assert torch.isfinite(y).all().item()
+    assert rel_l2(y.double().cpu().numpy(), _want(op, s, inp)) <= TOL["bf16"]
