@@ -94,9 +94,10 @@ struct WgradArgs {
 // filter row and 16-tap fragment: A holds 32 consecutive input columns per
 // combination, B the Toeplitz band of one 16-tap slice of the filter row.
 // A workgroup owns CB channels x rblk output rows of one image.
-// LDS per packed-MFMA workgroup: at most half of a CU's 160 KiB, so two
-// workgroups share a CU and one's loads and stores overlap the other's MFMAs.
+// Packed-MFMA workgroups: 8 waves, up to half of a CU's 160 KiB of LDS (two
+// workgroups per CU when the registers allow it).
 constexpr int kMfmaMaxLds = 81920;
+constexpr int kMfmaWaves = 8;
 
 struct MfmaArgs {
   const void* in;    // N x IH x IW x C (X, or dY for the data gradient)
@@ -107,9 +108,11 @@ struct MfmaArgs {
   int gt;            // column groups per tile: 1, 2 or 4 (rows per tile 16 / gt)
   int rblk;          // output rows per workgroup: tiles * 16 / gt
   int rch, cblk;     // row chunks per image, channel blocks
-  int xr, wt;        // staged input tile: rows, columns (= row pitch)
+  int xr, wt, wp;    // staged input tile: rows, columns, row pitch (elements)
+  int e_items;       // staging lanes per row: (wt / 2) column pairs x CB / 8 octets
+  int e2, e2_log;    // e_items rounded up to a power of two, and its log2
   int lds_bytes;
-  int num_blocks;
+  int num_blocks;    // N * cblk * rch workgroups
 };
 
 // out[i] = sum_{z < Z} ws[z * M + i], summed in order of z.

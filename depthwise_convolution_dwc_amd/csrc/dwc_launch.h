@@ -35,8 +35,7 @@ DWC_DECL_SWEEP(2)
 #undef DWC_DECL_SWEEP
 
 // Packed-MFMA forward-type kernel (bf16 / fp16 operands, stride 1): nf
-// 16-tap fragments per filter row (CB = 16 channels per workgroup for nf 1,
-// 8 for nf 2), tiles of 16 combinations per channel.
+// 16-tap fragments per filter row, tiles of 16 combinations per channel.
 hipError_t launch_fwd_mfma(int dt, int nf, int tiles, bool flip, const MfmaArgs& a,
                            hipStream_t s);
 

@@ -14,19 +14,27 @@
 // the filter rows run as a loop of accumulating MFMAs.  The 16 combinations
 // m of a tile are gt column groups x 16/gt consecutive output rows.
 //
-// Operand staging (all in LDS, §4.3 keeps the repeated filter in compact
+// Operand staging (all in LDS; §4.3 keeps the repeated filter in compact
 // form and reuses overlapping input rows):
 //   * the input tile is stored channel-major, [c][row][col], so one lane's
-//     8 consecutive columns of A are one 16-byte LDS read;
+//     8 consecutive columns of A are one 16-byte LDS read.  Only real image
+//     rows are stored, after one shared zero row that stands for every
+//     padding row;
 //   * going from filter row fh to fh+1, combination (g, r) needs the input
 //     row that combination (g, r+1) used: a DPP row shift by one lane moves
 //     it, and only the last row of each group reads LDS again;
-//   * B is built per filter row from one packed tap pair per lane,
-//     (w[i-1], w[i]), gathered with ds_bpermute -- the filter row is held
-//     once, not as a 32 x 16 matrix;
+//   * B is not stored as a 32 x 16 matrix: each (channel, filter row,
+//     fragment) keeps its 16 taps once, z[u] = w[16f + u - 16] for u in
+//     [16, 32), with 16 zeros before them, and lane (q, j) takes its 8
+//     values z[16 + 8q - j .. +7] (the zeros around the taps are the band's
+//     mask).  Rows follow each other every 32 elements, so the zeros after
+//     a row's taps are the next row's leading zeros.  A lane reads 5
+//     4-byte-aligned dwords from the even element at or below its start and
+//     shifts them by 0 or 16 bits (v_alignbit): 2-byte-aligned 16-byte LDS
+//     reads run at a quarter of the speed;
 //   * outputs pass through LDS so that global stores are channel-contiguous.
-// Zero padding: the staging loads read out-of-image pixels as 0 through the
-// buffer resource's range check.
+// Zero padding of the image: the staging loads read out-of-image pixels as
+// 0 through the buffer resource's range check.
 #pragma once
 
 #include "dwc_device.h"
@@ -58,14 +66,22 @@ __device__ __forceinline__ uint32_t row_shift_down(uint32_t v) {
 // Staging items (16-byte loads, 16-byte output stores) each thread keeps in
 // flight before it writes them on.
 constexpr int kStageBatch = 4;
+// Elements between consecutive filter-row fragments (16 zeros, 16 taps);
+// lane (q, j) reads elements [16 + 8q - j, +8) of a row, which end inside
+// the next row's leading zeros.  Two zero rows follow the last one.
+constexpr int kZRow = 32;
+constexpr int kZTail = 2;
 
-// CB channels per workgroup (CB/4 per wave), NF 16-tap fragments per filter
-// row, TILES tiles of 16 combinations per channel.  FLIP stages the filter
-// turned by 180 degrees: the stride-1 data gradient.
+// CB channels per workgroup of kMfmaWaves waves (CB / kMfmaWaves per wave),
+// NF 16-tap fragments per filter row, TILES tiles of 16 combinations per
+// channel.  FLIP stages the filter turned by 180 degrees: the stride-1 data
+// gradient.
 template <int DT, int NF, int CB, int TILES, bool FLIP>
-__global__ __launch_bounds__(kBlockThreads) void fwd_mfma(MfmaArgs a) {
+__global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma(MfmaArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
-  constexpr int CPW = CB / kWavesPerBlock;
+  constexpr int NT = 64 * kMfmaWaves;
+  constexpr int CPW = CB / kMfmaWaves;
+  static_assert(CPW >= 1 && CB % kMfmaWaves == 0, "whole channels per wave");
   constexpr int OCT = CB / 8;  // 16-byte channel octets per pixel
   const int tid = threadIdx.x;
   const int wave = uniform(tid >> 6);
@@ -79,79 +95,103 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_mfma(MfmaArgs a) {
   const int n = t / a.cblk;
   const int c0 = cbk * CB;
   const int oh0 = rc * a.rblk;
-  const int XR = a.xr, WT = a.wt;
+  const int XR = a.xr, WP = a.wp;
   const int FH = a.FH, FW = a.FW;
-  uint16_t* xs = (uint16_t*)lds;                   // [CB][XR][WT]
-  uint16_t* wsh = xs + CB * XR * WT;               // [CB][FH][FW]
-  float* os = (float*)lds;                         // [rblk * OW][CB + 4], after compute
-  constexpr int OSP = CB + 4;                      // floats per staged output pixel
+  // Image rows [r_lo, r_hi) feed this block; LDS row 0 is the zero row and
+  // image row ir sits at LDS row ir - r_lo + 1.
+  const int s_top = oh0 - a.PH;  // image row of staged index 0
+  const int r_lo = s_top > 0 ? s_top : 0;
+  const int r_end = s_top + a.rblk + FH - 1;
+  const int r_hi = r_end < a.IH ? r_end : a.IH;
+  const int nrow = r_hi > r_lo ? r_hi - r_lo : 0;
+  uint16_t* xs = (uint16_t*)lds;                     // [CB][XR][WP]
+  uint16_t* zt = xs + CB * XR * WP;                  // [CB][FH][NF][kZRow] + tail
+  float* os = (float*)lds;                           // [rblk * OW][CB + 4], after compute
+  constexpr int OSP = CB + 4;                        // floats per staged output pixel
+  const int zlen = (CB * FH * NF + kZTail) * kZRow;  // elements of zt (a multiple of 8)
 
-  // ---- stage the input tile: rows oh0-PH .., columns -PW .., CB channels.
-  // Each thread issues the loads of kStageBatch items before writing any of
-  // them to LDS, so that many loads are in flight per workgroup.
+  // ---- zero the filter-fragment rows (their taps are written after a barrier)
+  for (int i = tid; i < zlen / 8; i += NT) ((mf_u32x4*)zt)[i] = mf_u32x4{0u, 0u, 0u, 0u};
+
+  // ---- stage the input tile: LDS rows 0 .. nrow, wt columns from -PW, CB
+  // channels.  Thread tid owns one (column pair, channel octet) e of a row
+  // and visits every rs-th row; it issues kStageBatch rows of loads before
+  // writing any of them to LDS.  LDS row 0 loads out of range: zeros.
   {
     const uint32_t Cb = (uint32_t)a.C * 2u;
     const char* img = (const char*)a.in + (size_t)n * a.IH * a.IW * Cb;
-    const auto rs = make_rsrc(img, (uint32_t)(a.IH * a.IW) * Cb);
-    const int ih0 = oh0 - a.PH, iw0 = -a.PW;
-    const int half = WT / 2;
-    const int items = XR * half * OCT;
-    const int plane = XR * WT;  // elements per channel plane
-    for (int i0 = 0; i0 < items; i0 += kBlockThreads * kStageBatch) {
+    const auto rsrc = make_rsrc(img, (uint32_t)(a.IH * a.IW) * Cb);
+    const int e = tid & (a.e2 - 1);
+    const int r0 = tid >> a.e2_log;
+    const int rs = NT >> a.e2_log;
+    const int o = e % OCT, cp = e / OCT;
+    const int iw = 2 * cp - a.PW;
+    const int c = c0 + 8 * o;
+    const bool e_in = e < a.e_items;
+    const bool e_ok = e_in && c < a.C;
+    const bool ok0 = e_ok && (unsigned)iw < (unsigned)a.IW;
+    const bool ok1 = e_ok && (unsigned)(iw + 1) < (unsigned)a.IW;
+    const uint32_t col0 = ((uint32_t)iw * (uint32_t)a.C + (uint32_t)c) * 2u;
+    const uint32_t rowb = (uint32_t)a.IW * Cb;  // bytes per image row
+    const int plane2 = XR * WP / 2;             // dwords per channel plane
+    uint32_t* dst0 = (uint32_t*)xs + (8 * o) * plane2 + cp;
+    for (int rb = r0; rb <= nrow; rb += rs * kStageBatch) {
       mf_u32x4 v0[kStageBatch], v1[kStageBatch];
-      int dst[kStageBatch];
 #pragma unroll
       for (int b = 0; b < kStageBatch; ++b) {
-        const int i = i0 + b * kBlockThreads + tid;
-        const int o = i % OCT;
-        const int cp = (i / OCT) % half;
-        const int r = i / (OCT * half);
-        const int ih = ih0 + r, iw = iw0 + 2 * cp;
-        const int c = c0 + 8 * o;
-        const bool rok = i < items && (unsigned)ih < (unsigned)a.IH && c < a.C;
-        const uint32_t base = (uint32_t)(ih * a.IW) * Cb + (uint32_t)c * 2u;
-        const uint32_t off0 =
-            rok && (unsigned)iw < (unsigned)a.IW ? base + (uint32_t)iw * Cb : kOOB;
-        const uint32_t off1 =
-            rok && (unsigned)(iw + 1) < (unsigned)a.IW ? base + (uint32_t)(iw + 1) * Cb : kOOB;
-        v0[b] = __builtin_bit_cast(mf_u32x4,
-                                   __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off0, 0, 0));
-        v1[b] = __builtin_bit_cast(mf_u32x4,
-                                   __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off1, 0, 0));
-        // LDS dword (channel 8o, row r, columns 2cp, 2cp+1); -1: no item
-        dst[b] = i < items ? (((8 * o) * XR + r) * WT + 2 * cp) / 2 : -1;
+        const int r = rb + b * rs;  // LDS row
+        const bool rok = r >= 1 && r <= nrow;
+        const uint32_t off = (uint32_t)(r_lo + r - 1) * rowb + col0;
+        v0[b] = __builtin_bit_cast(mf_u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 rsrc, (int)(rok && ok0 ? off : kOOB), 0, 0));
+        v1[b] = __builtin_bit_cast(mf_u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 rsrc, (int)(rok && ok1 ? off + Cb : kOOB), 0, 0));
       }
 #pragma unroll
       for (int b = 0; b < kStageBatch; ++b) {
-        if (dst[b] < 0) continue;
+        const int r = rb + b * rs;
+        if (r > nrow || !e_in) continue;
         // channel j of a pixel is half (j & 1) of dword j / 2; the LDS dword
         // of channel j holds (pixel 0, pixel 1)
-        uint32_t* d = (uint32_t*)xs + dst[b];
+        uint32_t* d = dst0 + r * (WP / 2);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t lo = (v0[b][j >> 1] >> (16 * (j & 1))) & 0xffffu;
-          const uint32_t hi = (v1[b][j >> 1] >> (16 * (j & 1))) & 0xffffu;
-          d[j * (plane / 2)] = lo | (hi << 16);
-        }
+        for (int j = 0; j < 8; ++j)
+          d[j * plane2] = __builtin_amdgcn_perm(v1[b][j >> 1], v0[b][j >> 1],
+                                                (j & 1) ? 0x07060302u : 0x05040100u);
       }
     }
   }
-  // ---- stage the filter: [cc][fh][fw], turned by 180 degrees for FLIP.
+  __syncthreads();  // zt is zero
+  // ---- filter taps into their fragment rows, turned by 180 degrees for FLIP
   {
-    const auto rs = make_rsrc(a.filt, (uint32_t)(FH * FW) * (uint32_t)a.C * 2u);
+    const auto rsrc = make_rsrc(a.filt, (uint32_t)(FH * FW) * (uint32_t)a.C * 2u);
     const int taps = FH * FW;
     const int items = taps * OCT;
-    for (int i = tid; i < items; i += kBlockThreads) {
-      const int o = i % OCT;
-      const int e = i / OCT;
-      const int c = c0 + 8 * o;
-      const uint32_t off = c < a.C ? ((uint32_t)e * (uint32_t)a.C + (uint32_t)c) * 2u : kOOB;
-      const mf_u32x4 v = __builtin_bit_cast(
-          mf_u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0));
-      const int ed = FLIP ? taps - 1 - e : e;
+    for (int i0 = 0; i0 < items; i0 += NT * kStageBatch) {
+      mf_u32x4 v[kStageBatch];
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        wsh[(8 * o + j) * taps + ed] = (uint16_t)((v[j >> 1] >> (16 * (j & 1))) & 0xffffu);
+      for (int b = 0; b < kStageBatch; ++b) {
+        const int i = i0 + b * NT + tid;
+        const int c = c0 + 8 * (i % OCT);
+        const int te = i / OCT;  // staged tap (fh, fw)
+        const int src = FLIP ? taps - 1 - te : te;
+        const uint32_t off =
+            i < items && c < a.C ? ((uint32_t)src * (uint32_t)a.C + (uint32_t)c) * 2u : kOOB;
+        v[b] = __builtin_bit_cast(mf_u32x4,
+                                  __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)off, 0, 0));
+      }
+#pragma unroll
+      for (int b = 0; b < kStageBatch; ++b) {
+        const int i = i0 + b * NT + tid;
+        if (i >= items) continue;
+        const int te = i / OCT;
+        const int fh = te / FW, fw = te - fh * FW;
+        const int f = fw >> 4;
+        uint16_t* d = zt + ((8 * (i % OCT)) * FH * NF + fh * NF + f) * kZRow + 16 + fw - 16 * f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          d[j * FH * NF * kZRow] = (uint16_t)((v[b][j >> 1] >> (16 * (j & 1))) & 0xffffu);
+      }
     }
   }
   __syncthreads();
@@ -159,71 +199,53 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_mfma(MfmaArgs a) {
   // ---- compute.  A: lane (q, m) holds A[m][8q .. 8q+7]; B: lane (q, j=m)
   // holds B[8q .. 8q+7][j]; D: lane (q, j) holds D[4q .. 4q+3][j].  The
   // wave's CPW channels run together in the filter-row loop, and the B
-  // operands of row fh+1 are gathered while the MFMAs of row fh execute.
+  // operands of row fh+1 are read while the MFMAs of row fh execute.
   const int q = lane >> 4, m = lane & 15;
   const int RT = 16 / a.gt;
   const int gA = m / RT, rA = m % RT;
   const bool reload = rA == RT - 1;
-  // B gather: register v of fragment f holds taps (16f + d, 16f + d + 1)
-  // with d = 8q + 2v - j, from lane 16f + d + 1 of the tap-pair vector; the
-  // mask drops taps outside the fragment's diagonal band.
-  uint32_t bsrc[NF][4], bmask[4];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int d = 8 * q + 2 * v - m;
-    bmask[v] = ((d >= 0 && d < 16) ? 0x0000ffffu : 0u) |
-               ((d + 1 >= 0 && d + 1 < 16) ? 0xffff0000u : 0u);
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      int s = 16 * f + d + 1;
-      s = s < 0 ? 0 : (s > 63 ? 63 : s);
-      bsrc[f][v] = (uint32_t)s * 4u;
-    }
-  }
-  // tap pair of lane i: (w[i-1], w[i]), zero outside [0, FW); the reads are
-  // clamped into the row and masked afterwards
-  const int lo_i = lane - 1 < 0 ? 0 : (lane - 1 >= FW ? FW - 1 : lane - 1);
-  const int hi_i = lane >= FW ? FW - 1 : lane;
-  const uint32_t lo_m = (lane >= 1 && lane - 1 < FW) ? 0xffffu : 0u;
-  const uint32_t hi_m = lane < FW ? 0xffffu : 0u;
-  const uint16_t* wbase = wsh + (wave * CPW) * FH * FW;
-  auto tap_pair = [&](int k, int fh) -> uint32_t {
-    const uint16_t* row = wbase + (k * FH + fh) * FW;
-    const uint32_t lo = row[lo_i], hi = row[hi_i];
-    return (lo & lo_m) | ((hi & hi_m) << 16);
+  const uint16_t* xbase = xs + (wave * CPW) * XR * WP + 16 * gA + 8 * q;
+  // B: lane (q, j = m) starts at element 16 + 8q - m of a fragment row; it
+  // reads from the even element at or below and shifts odd starts by 16 bits
+  const int u0 = 16 + 8 * q - m;
+  const uint32_t bshift = (uint32_t)(u0 & 1) * 16u;
+  const uint32_t* zbase = (const uint32_t*)(zt + (wave * CPW) * FH * NF * kZRow + (u0 & ~1));
+  auto read_b = [&](int row) -> mf_u32x4 {  // row: fragment row of this wave
+    const uint32_t* p = zbase + row * (kZRow / 2);
+    mf_u32x4 d;
+    __builtin_memcpy(&d, p, 16);
+    const uint32_t d4 = p[4];
+    return mf_u32x4{__builtin_amdgcn_alignbit(d[1], d[0], bshift),
+                    __builtin_amdgcn_alignbit(d[2], d[1], bshift),
+                    __builtin_amdgcn_alignbit(d[3], d[2], bshift),
+                    __builtin_amdgcn_alignbit(d4, d[3], bshift)};
   };
-  const uint16_t* xbase = xs + (wave * CPW) * XR * WT;
-  // lane's element offset in a channel plane for tile tt, fragment f, at
-  // staged row `row` of its combination
-  const int col_off = 16 * gA + 8 * q;
+  // LDS row of staged index s (image row s_top + s): the zero row outside
+  // the image
+  auto lds_row = [&](int s) -> int {
+    const int ir = s_top + s;
+    return (ir >= r_lo && ir < r_hi) ? ir - r_lo + 1 : 0;
+  };
 
   mf_f32x4 acc[CPW][TILES];
   mf_u32x4 A[CPW][TILES][NF];
   mf_u32x4 B[CPW][NF];
-  uint32_t pair[CPW];
 #pragma unroll
   for (int k = 0; k < CPW; ++k) {
 #pragma unroll
     for (int tt = 0; tt < TILES; ++tt) {
       acc[k][tt] = mf_f32x4{0.f, 0.f, 0.f, 0.f};
+      const int row = lds_row(tt * RT + rA);
 #pragma unroll
       for (int f = 0; f < NF; ++f)
-        A[k][tt][f] = *(const mf_u32x4*)(xbase + (k * XR + tt * RT + rA) * WT + col_off + 16 * f);
+        A[k][tt][f] = *(const mf_u32x4*)(xbase + (k * XR + row) * WP + 16 * f);
     }
-    pair[k] = tap_pair(k, 0);
-  }
 #pragma unroll
-  for (int k = 0; k < CPW; ++k) {
-#pragma unroll
-    for (int f = 0; f < NF; ++f)
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        B[k][f][v] = (uint32_t)__builtin_amdgcn_ds_bpermute((int)bsrc[f][v], (int)pair[k]) & bmask[v];
-    pair[k] = tap_pair(k, FH > 1 ? 1 : 0);
+    for (int f = 0; f < NF; ++f) B[k][f] = read_b(k * FH * NF + f);
   }
   // One uniform body per filter row: the operands for row fh+1 are formed
-  // in the last iteration too (from clamped rows of the staged tile, never
-  // used), which keeps the accumulators in place across iterations.
+  // in the last iteration too (from rows that exist, never used), which
+  // keeps the accumulators in place across iterations.
   for (int fh = 0; fh < FH; ++fh) {
 #pragma unroll
     for (int k = 0; k < CPW; ++k)
@@ -231,17 +253,11 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_mfma(MfmaArgs a) {
       for (int tt = 0; tt < TILES; ++tt)
 #pragma unroll
         for (int f = 0; f < NF; ++f) acc[k][tt] = mfma_16x16x32<DT>(A[k][tt][f], B[k][f], acc[k][tt]);
-    const int fpair = fh + 2 < FH ? fh + 2 : FH - 1;
+    const int fn = fh + 1 < FH ? fh + 1 : fh;
 #pragma unroll
-    for (int k = 0; k < CPW; ++k) {
+    for (int k = 0; k < CPW; ++k)
 #pragma unroll
-      for (int f = 0; f < NF; ++f)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          B[k][f][v] =
-              (uint32_t)__builtin_amdgcn_ds_bpermute((int)bsrc[f][v], (int)pair[k]) & bmask[v];
-      pair[k] = tap_pair(k, fpair);
-    }
+      for (int f = 0; f < NF; ++f) B[k][f] = read_b((k * FH + fn) * NF + f);
 #pragma unroll
     for (int k = 0; k < CPW; ++k)
 #pragma unroll
@@ -250,23 +266,24 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_mfma(MfmaArgs a) {
         for (int f = 0; f < NF; ++f)
 #pragma unroll
           for (int v = 0; v < 4; ++v) A[k][tt][f][v] = row_shift_down(A[k][tt][f][v]);
+    // staged row of each tile's last combination at filter row fh+1 (the
+    // same for all its lanes)
+    int rrow[TILES];
+#pragma unroll
+    for (int tt = 0; tt < TILES; ++tt) rrow[tt] = uniform(lds_row(tt * RT + RT + fh));
     if (reload) {
 #pragma unroll
-      for (int tt = 0; tt < TILES; ++tt) {
-        // staged row of this tile's last combination at filter row fh+1
-        int row = tt * RT + RT + fh;
-        row = row < XR ? row : XR - 1;
+      for (int tt = 0; tt < TILES; ++tt)
 #pragma unroll
         for (int k = 0; k < CPW; ++k)
 #pragma unroll
           for (int f = 0; f < NF; ++f)
-            A[k][tt][f] = *(const mf_u32x4*)(xbase + (k * XR + row) * WT + col_off + 16 * f);
-      }
+            A[k][tt][f] = *(const mf_u32x4*)(xbase + (k * XR + rrow[tt]) * WP + 16 * f);
     }
   }
-  __syncthreads();  // every wave is done with the staged input
 
   // ---- outputs: registers -> LDS [pixel][channel] -> channel-contiguous stores
+  __syncthreads();  // every wave is done with the staged input
 #pragma unroll
   for (int k = 0; k < CPW; ++k) {
     const int cc = wave * CPW + k;
@@ -285,17 +302,17 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_mfma(MfmaArgs a) {
     constexpr int QU = CB / 4;
     const int items = a.rblk * a.OW * QU;
     float* out_img = a.out + (size_t)n * a.OH * a.OW * a.C;
-    for (int i0 = 0; i0 < items; i0 += kBlockThreads * kStageBatch) {
+    for (int i0 = 0; i0 < items; i0 += NT * kStageBatch) {
       mf_f32x4 v[kStageBatch];
 #pragma unroll
       for (int b = 0; b < kStageBatch; ++b) {
-        const int i = i0 + b * kBlockThreads + tid;
+        const int i = i0 + b * NT + tid;
         const int p = i / QU;
         v[b] = i < items ? *(const mf_f32x4*)(os + p * OSP + 4 * (i % QU)) : mf_f32x4{};
       }
 #pragma unroll
       for (int b = 0; b < kStageBatch; ++b) {
-        const int i = i0 + b * kBlockThreads + tid;
+        const int i = i0 + b * NT + tid;
         const int s = i % QU;
         const int p = i / QU;
         const int oh = oh0 + p / a.OW;

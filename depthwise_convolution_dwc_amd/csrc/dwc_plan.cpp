@@ -100,10 +100,16 @@ int pick_split(int64_t rows, int64_t per_slice_blocks, int64_t strips, int64_t m
 // stride-1 data gradient as the forward map of dY): false if the kernel does
 // not apply.  Tiles of 16 (row, 16-column group) combinations: gt groups x
 // 16/gt rows; 1, 2 or 4 tiles per channel and workgroup -- as many as the
-// image height asks for (each filter-row operand B is built once per tile
-// set) while the staged input tile, the filter and (afterwards) the staged
-// outputs fit the workgroup's LDS.
+// image height asks for (each B operand is read once per tile set) while
+// the staged input rows, the zero-padded filter-row fragments and
+// (afterwards) the staged outputs fit the workgroup's LDS.  The input tile
+// holds the real image rows a workgroup reads plus one zero row; its row
+// pitch gets 8 extra elements (an odd number of 16-byte units per row)
+// where LDS allows, so that lanes reading consecutive rows hit distinct
+// banks.  16 channels per workgroup (two per wave) with one 16-tap
+// fragment, 8 (one per wave) with two.
 bool plan_mfma(const FwdArgs& f, int dt, bool flip, Plan* q) {
+  constexpr int kZRowElems = 32;  // one 16-tap fragment and its 16 leading zeros
   if (dt == DT_F32 || f.SH != 1 || f.SW != 1 || f.FW > 32 || f.C % 8 != 0) return false;
   const int groups = (f.OW + 15) / 16;
   const int gt = groups <= 1 ? 1 : groups <= 2 ? 2 : groups <= 4 ? 4 : 0;
@@ -123,18 +129,33 @@ bool plan_mfma(const FwdArgs& f, int dt, bool flip, Plan* q) {
     const int t = atoi(v);
     if (t == 1 || t == 2 || t == 4) tiles = std::min(tiles, t);
   }
+  const int64_t z_bytes = ((int64_t)cb * f.FH * nf + 2) * kZRowElems * 2;
   int64_t lds = 0;
   for (;; tiles /= 2) {
     m.rblk = tiles * rt;
-    m.xr = m.rblk + f.FH - 1;
-    const int64_t in_bytes =
-        (int64_t)cb * m.xr * m.wt * 2 + ((int64_t)cb * f.FH * f.FW * 2 + 15) / 16 * 16;
+    m.xr = std::min(f.IH, m.rblk + f.FH - 1) + 1;
     const int64_t out_bytes = (int64_t)m.rblk * f.OW * (cb + 4) * 4;
-    lds = std::max(in_bytes, out_bytes);
-    if (lds <= kMfmaMaxLds) break;
+    bool fit = false;
+    for (int pad : {8, 0}) {
+      m.wp = m.wt + pad;
+      lds = std::max((int64_t)cb * m.xr * m.wp * 2 + z_bytes, out_bytes);
+      if (lds <= kMfmaMaxLds) {
+        fit = true;
+        break;
+      }
+    }
+    if (fit) break;
     if (tiles == 1) return false;
   }
   m.lds_bytes = (int)lds;
+  m.e_items = (m.wt / 2) * (cb / 8);
+  m.e2 = 1;
+  m.e2_log = 0;
+  while (m.e2 < m.e_items) {
+    m.e2 *= 2;
+    ++m.e2_log;
+  }
+  if (m.e2 > 64 * kMfmaWaves) return false;
   m.rch = (f.OH + m.rblk - 1) / m.rblk;
   m.cblk = (f.C + cb - 1) / cb;
   const int64_t blocks = (int64_t)f.N * m.cblk * m.rch;
@@ -439,10 +460,10 @@ std::string describe(const Plan& pl) {
   if (pl.kind == PLAN_MFMA) {
     const MfmaArgs& m = pl.ma;
     snprintf(buf, sizeof buf,
-             "%s mfma dt=%s fw=%d fh=%d flip=%d nf=%d cb=%d gt=%d tiles=%d rblk=%d xr=%d wt=%d "
-             "lds=%d rch=%d cblk=%d blocks=%d",
+             "%s mfma dt=%s fw=%d fh=%d flip=%d nf=%d cb=%d gt=%d tiles=%d rblk=%d "
+             "xr=%d wt=%d wp=%d lds=%d rch=%d cblk=%d blocks=%d",
              ops[pl.op], dt_name(pl.dt), m.FW, m.FH, (int)pl.flip, pl.nf, pl.cb, m.gt, pl.tiles,
-             m.rblk, m.xr, m.wt, m.lds_bytes, m.rch, m.cblk, pl.blocks);
+             m.rblk, m.xr, m.wt, m.wp, m.lds_bytes, m.rch, m.cblk, pl.blocks);
     return buf;
   }
   if (pl.kind == PLAN_DIRECT && pl.sweep) {

@@ -24,7 +24,7 @@ hipError_t go(const MfmaArgs& a, hipStream_t s) {
     const hipError_t e = allow_lds(kernel);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(kernel, dim3(a.num_blocks), dim3(kBlockThreads), a.lds_bytes, s, a);
+  hipLaunchKernelGGL(kernel, dim3(a.num_blocks), dim3(64 * kMfmaWaves), a.lds_bytes, s, a);
   return hipGetLastError();
 }
 

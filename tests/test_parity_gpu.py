@@ -234,3 +234,15 @@ def test_mfma_outputs_fully_overwritten(op):
     sync()
     assert torch.isfinite(y).all().item()
     assert rel_l2(y.double().cpu().numpy(), _want(op, s, inp)) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("op", ["fwd", "bwd_data"])
+def test_mfma_many_workgroups(dtype, op):
+    """Several row chunks and channel blocks per image: every workgroup
+    stages its own rows and filter fragments."""
+    s = _shape((3, 40, 20, 48, 7, 7, 1, 3))
+    assert "mfma" in _algos(op, s, dtype)
+    inp = make_inputs(s, dtype, seed=40)
+    got = _run(op, s, inp, "mfma")
+    assert rel_l2(got, _want(op, s, inp)) <= TOL[dtype]
