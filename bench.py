@@ -265,7 +265,8 @@ def kernels_of(dwc, s, op):
     base = {("fwd", "sweep"): "fwd_sweep", ("bwd_data", "sweep"): "fwd_sweep",
             ("bwd_filter", "sweep"): "wgrad_sweep", ("fwd", "direct"): "fwd_rows",
             ("bwd_data", "direct"): "fwd_rows", ("bwd_filter", "direct"): "wgrad_rows",
-            ("fwd", "mfma"): "fwd_mfma", ("bwd_data", "mfma"): "fwd_mfma"}
+            ("fwd", "mfma"): "fwd_mfma", ("bwd_data", "mfma"): "fwd_mfma",
+            ("bwd_filter", "mfma"): "wgrad_mfma"}
     k = [base.get((op, fam), fam)]
     if op == "bwd_filter" and "ws_bytes=0" not in d:
         k.append("reduce_partials")

@@ -65,8 +65,11 @@ int prepare(const dwc_problem* p, int op, Plan* pl, const void* in0, const void*
   int st = make_plan(p, op, pl, &err);
   // The packed-MFMA kernels move 16-byte vectors: with a tensor that is not
   // 16-byte aligned, AUTO takes the vector kernels and MFMA is an error.
+  // (The filter-gradient kernel also stores 16-byte partials into the
+  // workspace.)
   if (st == DWC_OK && pl->kind == PLAN_MFMA && !pl->empty &&
-      !(aligned16(in0) && aligned16(in1) && aligned16(out))) {
+      !(aligned16(in0) && aligned16(in1) && aligned16(out) &&
+        (op != DWC_OP_BWD_FILTER || aligned16(ws)))) {
     if (p->algo == DWC_ALGO_MFMA) {
       set_last_error("packed-MFMA kernels need 16-byte aligned tensors");
       return DWC_ERR_MISALIGNED;
@@ -118,6 +121,17 @@ int dwc_bwd_filter(const dwc_problem* p, const void* x, const void* dy, void* dw
   // One slice writes dW directly; several write partials to the workspace.
   float* part = pl.ws_bytes > 0 ? (float*)workspace : (float*)dw;
   hipError_t e;
+  if (pl.kind == PLAN_MFMA) {
+    WgradMfmaArgs w = pl.wm;
+    w.x = x;
+    w.dy = dy;
+    w.ws = (float*)workspace;
+    e = launch_wgrad_mfma(pl.dt, pl.nfm, pl.nfn, pl.nk, w, s);
+    if (e != hipSuccess) return hip_fail(e, "dwc_bwd_filter launch");
+    e = launch_reduce(
+        ReduceArgs{(const float*)workspace, (float*)dw, m, pl.z, kWgmCb, w.C, w.FH * w.FW}, s);
+    return e == hipSuccess ? DWC_OK : hip_fail(e, "dwc_bwd_filter reduce");
+  }
   if (pl.kind == PLAN_DIRECT) {
     WgradArgs a = pl.wa;
     a.x = x;

@@ -115,12 +115,39 @@ struct MfmaArgs {
   int num_blocks;    // N * cblk * rch workgroups
 };
 
-// out[i] = sum_{z < Z} ws[z * M + i], summed in order of z.
+// out[i] = sum_{z < Z} ws[z * M + j(i)], summed in order of z.  Plain
+// layout (cb = 0): j(i) = i.  Channel-blocked layout (cb > 0, C % cb == 0,
+// out = [tap][c] with C channels): each slice is [c / cb][tap][c % cb], so
+// j(i) = ((c / cb) * taps + tap) * cb + c % cb.
 struct ReduceArgs {
   const float* ws;
   float* out;
   int64_t M;
   int Z;
+  int cb, C, taps;
+};
+
+// Packed-MFMA filter-gradient kernel (bf16/fp16 operands, stride 1).  Per
+// channel and output row oh, dW[fh][fw] += sum_i dY[oh][i - fw + pw] *
+// X[oh + fh - ph][i]: a v_mfma_f32_16x16x32 with A = the Toeplitz band of
+// the dY row (16 taps fw x 32 input columns i) and B = 16 input rows (fh) x
+// the same 32 columns.  A workgroup owns kWgmCb channels (one per wave) and
+// a slice of images; it writes one partial per slice in the channel-blocked
+// layout that reduce_partials reads with cb = kWgmCb.
+constexpr int kWgmCb = 8;
+struct WgradMfmaArgs {
+  const void* x;     // N x IH x IW x C
+  const void* dy;    // N x OH x OW x C
+  float* ws;         // Z x cblk x (FH * FW) x kWgmCb partial sums
+  int N, IH, IW, C, OH, OW;
+  int FH, FW, PH, PW;
+  int cblk, Z, ipb;  // channel blocks, slices, images per slice
+  int xr, xp;        // staged X: rows (IH + 1, row 0 = zeros), pitch (elements)
+  int dyp, dpad;     // staged dY rows: pitch, zeros before column 0
+  int xe2_log;       // log2 of the X staging lanes per row (16 * NK)
+  int de_items, de2, de2_log;  // dY staging lanes per row (dyp / 2), pow2, log2
+  int lds_bytes;
+  int num_blocks;    // Z * cblk
 };
 
 // Generic kernels: one output element per lane.

@@ -324,4 +324,215 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma(MfmaArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Packed-MFMA filter gradient (bf16 / fp16 operands, stride 1).
+//
+// Per channel and output row oh (the split of the accumulation axis of
+// Flash-DWC §5.1, with the GEMV-to-GEMM packing of §4.2 applied to the
+// filter gradient):
+//   A[m][k] = dY[oh][32 kc + k - (16 fm + m) + pw]   (16 taps fw x 32 columns)
+//   B[k][n] = X[oh + 16 fn + n - ph][32 kc + k]        (32 columns x 16 rows fh)
+//   D[m][n] += sum_k A[m][k] B[k][n]  =  dW[16 fn + n][16 fm + m] contributions
+// so one 16x16x32 MFMA covers up to 16 x 16 taps over 32 input columns.  A is
+// the Toeplitz band of the zero-padded dY row (read like the forward kernel's
+// filter band: 4-byte-aligned dwords and v_alignbit); B is 16 consecutive
+// input rows, which move down one row per output row by a DPP row shift plus
+// one reloaded lane.  A workgroup owns kWgmCb channels (one per wave) and a
+// slice of ipb images, stages each image's X and dY rows in LDS
+// channel-major, and writes one channel-blocked partial per slice.
+// ---------------------------------------------------------------------------
+template <int DT, int NFM, int NFN, int NK>
+__global__ __launch_bounds__(64 * kMfmaWaves) void wgrad_mfma(WgradMfmaArgs a) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  constexpr int NT = 64 * kMfmaWaves;
+  constexpr int CB = kWgmCb;
+  static_assert(CB == kMfmaWaves, "one channel per wave");
+  const int tid = threadIdx.x;
+  const int wave = uniform(tid >> 6);
+  const int lane = tid & 63;
+  const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
+  if (blk >= a.num_blocks) return;  // the whole workgroup leaves together
+  const int cbk = blk % a.cblk;
+  const int z = blk / a.cblk;
+  const int n0 = z * a.ipb;
+  const int n1 = n0 + a.ipb < a.N ? n0 + a.ipb : a.N;
+  const int c0 = cbk * CB;
+  const int XR = a.xr, XP = a.xp, DYP = a.dyp, OH = a.OH;
+  const int taps = a.FH * a.FW;
+  uint16_t* xs = (uint16_t*)lds;        // [CB][XR][XP]
+  uint16_t* dz = xs + CB * XR * XP;     // [CB][OH][DYP]
+  float* pst = (float*)lds;             // [taps][CB], after the last image
+  const uint32_t Cb = (uint32_t)a.C * 2u;
+
+  // ---- per-lane constants.  A: lane (q, m) holds A[m][8q .. 8q+7]; B:
+  // lane (q, n = m) holds B[8q .. 8q+7][n]; D: lane (q, j) holds
+  // D[4q .. 4q+3][j].
+  const int q = lane >> 4, m = lane & 15;
+  const int cc = wave;
+  // A starts at staged dY element 32 kc + 8q - 16 fm - m + pw + dpad of its
+  // row: read from the even element at or below, shift odd starts by 16 bits
+  const int ua = 8 * q - m + a.PW + a.dpad;
+  const uint32_t ashift = (uint32_t)(ua & 1) * 16u;
+  const uint32_t* dzl = (const uint32_t*)(dz + cc * OH * DYP + (ua & ~1));
+  auto read_a = [&](int oh, int fm, int kc) -> mf_u32x4 {
+    const uint32_t* p = dzl + (oh * DYP + 32 * kc - 16 * fm) / 2;
+    mf_u32x4 d;
+    __builtin_memcpy(&d, p, 16);
+    const uint32_t d4 = p[4];
+    return mf_u32x4{__builtin_amdgcn_alignbit(d[1], d[0], ashift),
+                    __builtin_amdgcn_alignbit(d[2], d[1], ashift),
+                    __builtin_amdgcn_alignbit(d[3], d[2], ashift),
+                    __builtin_amdgcn_alignbit(d4, d[3], ashift)};
+  };
+  const uint16_t* xl = xs + cc * XR * XP + 8 * q;
+  // LDS row of input row r: row 0 is zeros, image row r sits at r + 1
+  auto x_row = [&](int r) -> int { return (unsigned)r < (unsigned)a.IH ? r + 1 : 0; };
+
+  mf_f32x4 acc[NFM][NFN];
+#pragma unroll
+  for (int fm = 0; fm < NFM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < NFN; ++fn) acc[fm][fn] = mf_f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int n = n0; n < n1; ++n) {
+    __syncthreads();  // the previous image's operands are no longer read
+    // ---- stage X rows (LDS row 0 = zeros) and the zero-padded dY rows of
+    // image n, channel-major: each thread loads a pair of pixels (8
+    // channels, 16 bytes each) and writes 8 transposed dwords.
+    {
+      const char* img = (const char*)a.x + (size_t)n * a.IH * a.IW * Cb;
+      const auto rsrc = make_rsrc(img, (uint32_t)(a.IH * a.IW) * Cb);
+      const int e = tid & ((1 << a.xe2_log) - 1);  // column pair (16 NK per row)
+      const int r0 = tid >> a.xe2_log;
+      const int rs = NT >> a.xe2_log;
+      const uint32_t col0 = (uint32_t)(2 * e) * Cb + (uint32_t)c0 * 2u;
+      const bool ok0 = 2 * e < a.IW, ok1 = 2 * e + 1 < a.IW;
+      const int plane2 = XR * XP / 2;
+      uint32_t* dst0 = (uint32_t*)xs + e;
+      for (int rb = r0; rb < XR; rb += rs * kStageBatch) {
+        mf_u32x4 v0[kStageBatch], v1[kStageBatch];
+#pragma unroll
+        for (int b = 0; b < kStageBatch; ++b) {
+          const int r = rb + b * rs;
+          const bool rok = r >= 1 && r < XR;
+          const uint32_t off = (uint32_t)((r - 1) * a.IW) * Cb + col0;
+          v0[b] = __builtin_bit_cast(mf_u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   rsrc, (int)(rok && ok0 ? off : kOOB), 0, 0));
+          v1[b] = __builtin_bit_cast(mf_u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   rsrc, (int)(rok && ok1 ? off + Cb : kOOB), 0, 0));
+        }
+#pragma unroll
+        for (int b = 0; b < kStageBatch; ++b) {
+          const int r = rb + b * rs;
+          if (r >= XR) continue;
+          uint32_t* d = dst0 + r * (XP / 2);
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            d[j * plane2] = __builtin_amdgcn_perm(v1[b][j >> 1], v0[b][j >> 1],
+                                                  (j & 1) ? 0x07060302u : 0x05040100u);
+        }
+      }
+    }
+    {
+      const char* img = (const char*)a.dy + (size_t)n * OH * a.OW * Cb;
+      const auto rsrc = make_rsrc(img, (uint32_t)(OH * a.OW) * Cb);
+      const int e = tid & (a.de2 - 1);  // column pair of the staged row
+      const int r0 = tid >> a.de2_log;
+      const int rs = NT >> a.de2_log;
+      const int t0 = 2 * e - a.dpad;  // dY column of the pair's first element
+      const bool e_in = e < a.de_items;
+      const bool ok0 = e_in && (unsigned)t0 < (unsigned)a.OW;
+      const bool ok1 = e_in && (unsigned)(t0 + 1) < (unsigned)a.OW;
+      const uint32_t col0 = (uint32_t)t0 * Cb + (uint32_t)c0 * 2u;
+      const int plane2 = OH * DYP / 2;
+      uint32_t* dst0 = (uint32_t*)dz + e;
+      for (int rb = r0; rb < OH; rb += rs * kStageBatch) {
+        mf_u32x4 v0[kStageBatch], v1[kStageBatch];
+#pragma unroll
+        for (int b = 0; b < kStageBatch; ++b) {
+          const int r = rb + b * rs;
+          const bool rok = r < OH;
+          const uint32_t off = (uint32_t)(r * a.OW) * Cb + col0;
+          v0[b] = __builtin_bit_cast(mf_u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   rsrc, (int)(rok && ok0 ? off : kOOB), 0, 0));
+          v1[b] = __builtin_bit_cast(mf_u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   rsrc, (int)(rok && ok1 ? off + Cb : kOOB), 0, 0));
+        }
+#pragma unroll
+        for (int b = 0; b < kStageBatch; ++b) {
+          const int r = rb + b * rs;
+          if (r >= OH || !e_in) continue;
+          uint32_t* d = dst0 + r * (DYP / 2);
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            d[j * plane2] = __builtin_amdgcn_perm(v1[b][j >> 1], v0[b][j >> 1],
+                                                  (j & 1) ? 0x07060302u : 0x05040100u);
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- accumulate over the image's output rows
+    mf_u32x4 A[NFM][NK], B[NFN][NK];
+#pragma unroll
+    for (int fn = 0; fn < NFN; ++fn) {
+      const int row = x_row(16 * fn + m - a.PH);
+#pragma unroll
+      for (int kc = 0; kc < NK; ++kc) B[fn][kc] = *(const mf_u32x4*)(xl + row * XP + 32 * kc);
+    }
+#pragma unroll
+    for (int fm = 0; fm < NFM; ++fm)
+#pragma unroll
+      for (int kc = 0; kc < NK; ++kc) A[fm][kc] = read_a(0, fm, kc);
+    // One uniform body per output row: the operands of row oh+1 are formed
+    // in the last iteration too (from rows that exist, never used).
+    for (int oh = 0; oh < OH; ++oh) {
+#pragma unroll
+      for (int kc = 0; kc < NK; ++kc)
+#pragma unroll
+        for (int fm = 0; fm < NFM; ++fm)
+#pragma unroll
+          for (int fn = 0; fn < NFN; ++fn)
+            acc[fm][fn] = mfma_16x16x32<DT>(A[fm][kc], B[fn][kc], acc[fm][fn]);
+      const int on = oh + 1 < OH ? oh + 1 : oh;
+#pragma unroll
+      for (int fm = 0; fm < NFM; ++fm)
+#pragma unroll
+        for (int kc = 0; kc < NK; ++kc) A[fm][kc] = read_a(on, fm, kc);
+#pragma unroll
+      for (int fn = 0; fn < NFN; ++fn)
+#pragma unroll
+        for (int kc = 0; kc < NK; ++kc)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) B[fn][kc][v] = row_shift_down(B[fn][kc][v]);
+      // lane 15 of each row group takes input row oh+1 + 16 fn + 15 - ph
+      if (m == 15) {
+#pragma unroll
+        for (int fn = 0; fn < NFN; ++fn) {
+          const int row = uniform(x_row(oh + 1 + 16 * fn + 15 - a.PH));
+#pragma unroll
+          for (int kc = 0; kc < NK; ++kc) B[fn][kc] = *(const mf_u32x4*)(xl + row * XP + 32 * kc);
+        }
+      }
+    }
+  }
+
+  // ---- the slice's partial: registers -> LDS [tap][channel] -> one
+  // contiguous run of taps * CB floats
+  __syncthreads();
+#pragma unroll
+  for (int fm = 0; fm < NFM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < NFN; ++fn)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int fw = 16 * fm + 4 * q + r, fh = 16 * fn + m;
+        if (fw < a.FW && fh < a.FH) pst[(fh * a.FW + fw) * CB + cc] = acc[fm][fn][r];
+      }
+  __syncthreads();
+  float* dst = a.ws + ((size_t)z * a.cblk + cbk) * taps * CB;
+  for (int i = tid; i < taps * CB / 4; i += NT)
+    *(mf_f32x4*)(dst + 4 * i) = *(const mf_f32x4*)(pst + 4 * i);
+}
+
 }  // namespace dwc

@@ -172,6 +172,62 @@ bool plan_mfma(const FwdArgs& f, int dt, bool flip, Plan* q) {
   return true;
 }
 
+// Packed-MFMA filter-gradient plan: false if the kernel does not apply.
+// kWgmCb channels per workgroup (one per wave); the batch is cut into Z
+// slices of whole images so that Z * cblk workgroups (about 1024, or the
+// requested split) fill the GPU; the staged X rows (plus a zero row), the
+// zero-padded dY rows and (afterwards) the slice partial fit the LDS.
+bool plan_wgrad_mfma(const dwc_problem* p, int64_t oh, int64_t ow, Plan* q) {
+  const int dt = p->in_dtype;
+  if (dt == DT_F32 || p->stride_h != 1 || p->stride_w != 1 || p->fw > 32 || p->fh > 32 ||
+      p->w > 64 || p->c % kWgmCb != 0)
+    return false;
+  WgradMfmaArgs w{};
+  w.N = (int)p->n; w.IH = (int)p->h; w.IW = (int)p->w; w.C = (int)p->c;
+  w.OH = (int)oh; w.OW = (int)ow;
+  w.FH = p->fh; w.FW = p->fw; w.PH = p->pad_h; w.PW = p->pad_w;
+  const int nfm = (p->fw + 15) / 16, nfn = (p->fh + 15) / 16, nk = (int)((p->w + 31) / 32);
+  w.cblk = w.C / kWgmCb;
+  w.xr = w.IH + 1;
+  w.xp = 32 * nk + 8;  // an odd number of 16-byte units per row
+  // the A band of lane (q, m) starts at element 8q - 16 fm - m + pw + dpad
+  // of a staged dY row and reads up to 10 elements from the even one below
+  w.dpad = std::max(0, 16 * (nfm - 1) + 15 - w.PW);
+  w.dyp = (32 * nk + w.PW + w.dpad + 2 + 7) / 8 * 8;
+  w.xe2_log = nk == 1 ? 4 : 5;  // 16 * nk column pairs per staged X row
+  w.de_items = w.dyp / 2;
+  w.de2 = 1;
+  w.de2_log = 0;
+  while (w.de2 < w.de_items) {
+    w.de2 *= 2;
+    ++w.de2_log;
+  }
+  if (w.de2 > 64 * kMfmaWaves) return false;
+  const int64_t stage = (int64_t)kWgmCb * (w.xr * w.xp + w.OH * w.dyp) * 2;
+  const int64_t part = (int64_t)p->fh * p->fw * kWgmCb * 4;
+  const int64_t lds = std::max(stage, part);
+  if (lds > kMfmaMaxLds) return false;
+  w.lds_bytes = (int)lds;
+  int z = p->wgrad_split > 0 ? p->wgrad_split
+                             : (int)std::max<int64_t>(1, (1024 + w.cblk - 1) / w.cblk);
+  const int64_t nn = std::max<int64_t>(p->n, 1);  // an empty batch only zero-fills dW
+  z = (int)std::min<int64_t>(z, nn);
+  w.ipb = (int)((nn + z - 1) / z);
+  w.Z = (int)((nn + w.ipb - 1) / w.ipb);
+  const int64_t blocks = (int64_t)w.Z * w.cblk;
+  if (blocks > kI32Max) return false;
+  w.num_blocks = (int)blocks;
+  q->kind = PLAN_MFMA;
+  q->nfm = nfm;
+  q->nfn = nfn;
+  q->nk = nk;
+  q->cb = kWgmCb;
+  q->z = w.Z;
+  q->blocks = w.num_blocks;
+  q->wm = w;
+  return true;
+}
+
 }  // namespace
 
 void set_last_error(const std::string& msg) { g_last_error = msg; }
@@ -318,14 +374,24 @@ int make_plan(const dwc_problem* p, int op, Plan* pl, std::string* err) {
       q.ga = g;
     }
   } else {
-    if (p->algo == DWC_ALGO_MFMA)
-      return fail(err, DWC_ERR_UNSUPPORTED, "no packed-MFMA filter-gradient kernel");
+    if (p->wgrad_split > 0 && p->n * oh > 0 && p->wgrad_split > p->n * oh)
+      return fail(err, DWC_ERR_BAD_PARAM, "wgrad_split larger than N*OH");
+    if (p->algo == DWC_ALGO_AUTO || p->algo == DWC_ALGO_MFMA) {
+      if (plan_wgrad_mfma(p, oh, ow, &q)) {
+        const int64_t m = (int64_t)p->fh * p->fw * p->c;
+        q.ws_bytes = ((size_t)q.z * (size_t)m * 4 + 255) / 256 * 256;
+        *pl = q;
+        return DWC_OK;
+      }
+      if (p->algo == DWC_ALGO_MFMA)
+        return fail(err, DWC_ERR_UNSUPPORTED,
+                    "no packed-MFMA filter-gradient kernel for this problem (needs bf16/fp16, "
+                    "stride 1, FH and FW <= 32, W <= 64, C % 8 == 0)");
+    }
     const int64_t rows = p->n * oh;
     const int64_t m = (int64_t)p->fh * p->fw * p->c;
     const double flops = 2.0 * (double)p->n * oh * ow * p->c * p->fh * p->fw;
     const double bytes = (double)eb * ((double)p->n * p->h * p->w * p->c + (double)rows * ow * p->c);
-    if (p->wgrad_split > 0 && rows > 0 && p->wgrad_split > rows)
-      return fail(err, DWC_ERR_BAD_PARAM, "wgrad_split larger than N*OH");
     if (direct) {
       WgradArgs w{};
       w.N = (int)p->n; w.IH = (int)p->h; w.IW = (int)p->w; w.C = C;
@@ -457,6 +523,15 @@ int check_pointers(const dwc_problem* p, const Plan& pl, const void* in0, const 
 std::string describe(const Plan& pl) {
   static const char* ops[] = {"fwd", "bwd_data", "bwd_filter"};
   char buf[512];
+  if (pl.kind == PLAN_MFMA && pl.op == DWC_OP_BWD_FILTER) {
+    const WgradMfmaArgs& w = pl.wm;
+    snprintf(buf, sizeof buf,
+             "%s mfma dt=%s fw=%d fh=%d nfm=%d nfn=%d nk=%d cb=%d xr=%d xp=%d dyp=%d dpad=%d "
+             "lds=%d z=%d ipb=%d cblk=%d blocks=%d ws_bytes=%zu",
+             ops[pl.op], dt_name(pl.dt), w.FW, w.FH, pl.nfm, pl.nfn, pl.nk, pl.cb, w.xr, w.xp,
+             w.dyp, w.dpad, w.lds_bytes, w.Z, w.ipb, w.cblk, pl.blocks, pl.ws_bytes);
+    return buf;
+  }
   if (pl.kind == PLAN_MFMA) {
     const MfmaArgs& m = pl.ma;
     snprintf(buf, sizeof buf,
@@ -568,7 +643,21 @@ int dwc_bwd_filter_workspace_size(const dwc_problem* p, size_t* bytes) {
     set_last_error("bytes pointer is NULL");
     return DWC_ERR_BAD_PARAM;
   }
-  *bytes = pl.empty ? 0 : pl.ws_bytes;
+  size_t need = pl.empty ? 0 : pl.ws_bytes;
+  // AUTO may fall back from the packed-MFMA kernels to the vector kernels
+  // at call time (tensors not 16-byte aligned): cover both plans
+  if (pl.kind == PLAN_MFMA && p->algo == DWC_ALGO_AUTO && !pl.empty) {
+    dwc_problem d = *p;
+    d.algo = DWC_ALGO_DIRECT;
+    Plan alt;
+    int s2 = make_plan(&d, DWC_OP_BWD_FILTER, &alt, &err);
+    if (s2 == DWC_ERR_UNSUPPORTED) {
+      d.algo = DWC_ALGO_GENERIC;
+      s2 = make_plan(&d, DWC_OP_BWD_FILTER, &alt, &err);
+    }
+    if (s2 == DWC_OK) need = std::max(need, alt.ws_bytes);
+  }
+  *bytes = need;
   return DWC_OK;
 }
 

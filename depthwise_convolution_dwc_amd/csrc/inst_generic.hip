@@ -9,7 +9,8 @@ namespace dwc {
 // consecutive outputs (one per lane); wave w adds the contiguous slice range
 // [w*Z/16, (w+1)*Z/16) in slice order, then wave 0 adds the 16 wave sums in
 // wave order.  With Z = 0 it writes zeros (the filter gradient of an empty
-// batch).
+// batch).  Partials in the channel-blocked layout (cb > 0) are read at the
+// permuted index of ReduceArgs.
 constexpr int kReduceWaves = 16;
 
 __global__ __launch_bounds__(64 * kReduceWaves) void reduce_partials(ReduceArgs a) {
@@ -20,7 +21,13 @@ __global__ __launch_bounds__(64 * kReduceWaves) void reduce_partials(ReduceArgs 
   const int z1 = (int)((int64_t)a.Z * (wave + 1) / kReduceWaves);
   float s = 0.f;
   if (i < a.M) {
-    const float* p = a.ws + i;
+    int64_t j = i;
+    if (a.cb > 0) {
+      const int64_t tap = i / a.C;
+      const int c = (int)(i - tap * a.C);
+      j = ((int64_t)(c / a.cb) * a.taps + tap) * a.cb + c % a.cb;
+    }
+    const float* p = a.ws + j;
     for (int z = z0; z < z1; ++z) s += p[(int64_t)z * a.M];
   }
   part[wave][lane] = s;

@@ -1,5 +1,5 @@
-// inst_mfma.hip -- instantiations and launcher of the packed-MFMA
-// forward-type kernel (bf16 / fp16 operands).
+// inst_mfma.hip -- instantiations and launchers of the packed-MFMA kernels
+// (bf16 / fp16 operands): forward-type and filter gradient.
 #include "dwc_launch.h"
 #include "dwc_mfma.h"
 
@@ -43,7 +43,46 @@ hipError_t by_nf(int nf, int tiles, const MfmaArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+template <int DT, int NFM, int NFN, int NK>
+hipError_t wg_go(const WgradMfmaArgs& a, hipStream_t s) {
+  auto kernel = wgrad_mfma<DT, NFM, NFN, NK>;
+  if (a.lds_bytes > 65536) {
+    const hipError_t e = allow_lds(kernel);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kernel, dim3(a.num_blocks), dim3(64 * kMfmaWaves), a.lds_bytes, s, a);
+  return hipGetLastError();
+}
+
+template <int DT, int NFM, int NFN>
+hipError_t wg_by_nk(int nk, const WgradMfmaArgs& a, hipStream_t s) {
+  if (nk == 1) return wg_go<DT, NFM, NFN, 1>(a, s);
+  if (nk == 2) return wg_go<DT, NFM, NFN, 2>(a, s);
+  return hipErrorInvalidValue;
+}
+
+template <int DT, int NFM>
+hipError_t wg_by_nfn(int nfn, int nk, const WgradMfmaArgs& a, hipStream_t s) {
+  if (nfn == 1) return wg_by_nk<DT, NFM, 1>(nk, a, s);
+  if (nfn == 2) return wg_by_nk<DT, NFM, 2>(nk, a, s);
+  return hipErrorInvalidValue;
+}
+
+template <int DT>
+hipError_t wg_by_nfm(int nfm, int nfn, int nk, const WgradMfmaArgs& a, hipStream_t s) {
+  if (nfm == 1) return wg_by_nfn<DT, 1>(nfn, nk, a, s);
+  if (nfm == 2) return wg_by_nfn<DT, 2>(nfn, nk, a, s);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
+
+hipError_t launch_wgrad_mfma(int dt, int nfm, int nfn, int nk, const WgradMfmaArgs& a,
+                             hipStream_t s) {
+  if (dt == DT_BF16) return wg_by_nfm<DT_BF16>(nfm, nfn, nk, a, s);
+  if (dt == DT_F16) return wg_by_nfm<DT_F16>(nfm, nfn, nk, a, s);
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_fwd_mfma(int dt, int nf, int tiles, bool flip, const MfmaArgs& a,
                            hipStream_t s) {

@@ -61,11 +61,12 @@ typedef enum {
     DWC_ALGO_DIRECT = 1, /* register-window vector kernels                  */
     DWC_ALGO_GENERIC = 2, /* one output per lane; any filter size or stride */
     DWC_ALGO_MFMA = 3     /* packed matrix-core kernels (bf16/fp16 operands,
-                             stride 1, FW <= 32, C a multiple of 8, output
-                             width <= 64, 16-byte aligned tensors): the
+                             stride 1, FW <= 32, C a multiple of 8, 16-byte
+                             aligned tensors; output width <= 64 for the
+                             forward and data gradient, input width <= 64
+                             and FH <= 32 for the filter gradient): the
                              GEMV-to-GEMM packing of §4.2 on CDNA4 MFMA.
-                             Forward and data gradient only; AUTO picks it
-                             for those when it applies                    */
+                             AUTO picks it wherever it applies            */
 } dwc_algo;
 
 typedef enum {
@@ -89,7 +90,9 @@ typedef struct {
     int32_t out_dtype;          /* dwc_dtype of Y, dX, dW: must be DWC_F32  */
     int32_t algo;               /* dwc_algo                                 */
     int32_t wgrad_split;        /* filter gradient: number of slices of the
-                                   N*OH accumulation axis; 0 = automatic    */
+                                   N*OH accumulation axis (whole images for
+                                   the packed kernel, at most N slices);
+                                   0 = automatic                            */
 } dwc_problem;
 
 /* Version number (DWC_VERSION of the built library). */
@@ -151,7 +154,9 @@ int dwc_bwd_filter_workspace_size(const dwc_problem* p, size_t* bytes);
  * The N*OH accumulation axis is split into slices whose partial sums are
  * added in a fixed order (the split of §5.1, reduced deterministically
  * instead of with atomics), so results are bitwise reproducible for a given
- * problem and wgrad_split.  n == 0 writes dw = 0. */
+ * problem, algo and wgrad_split.  The packed-MFMA kernel (DWC_ALGO_MFMA, or
+ * AUTO where it applies) slices whole images and also needs workspace and
+ * tensors 16-byte aligned.  n == 0 writes dw = 0. */
 int dwc_bwd_filter(const dwc_problem* p, const void* x, const void* dy,
                    void* dw, void* workspace, size_t workspace_bytes,
                    void* stream);

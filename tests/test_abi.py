@@ -160,25 +160,56 @@ def test_mfma_plans_and_rejections():
     p = dwc.problem(128, 28, 28, 512, 13, 13, 1, 6, dtype=dwc.BF16)
     assert dwc.plan_describe(p, 0).startswith("fwd mfma")
     assert dwc.plan_describe(p, 1).startswith("bwd_data mfma")
+    assert dwc.plan_describe(p, 2).startswith("bwd_filter mfma")
     p = dwc.problem(128, 28, 28, 512, 31, 31, 1, 15, dtype=dwc.F16)
     d = dwc.plan_describe(p, 0)
     assert d.startswith("fwd mfma") and "nf=2" in d
+    d = dwc.plan_describe(p, 2)
+    assert d.startswith("bwd_filter mfma") and "nfm=2" in d and "nfn=2" in d
     # the vector kernels stay reachable
     p = dwc.problem(128, 28, 28, 512, 13, 13, 1, 6, dtype=dwc.BF16, algo="direct")
     assert dwc.plan_describe(p, 0).startswith("fwd direct")
-    # conditions of the packed kernel: half-precision operands, stride 1,
-    # C a multiple of 8, FW <= 32, output width <= 64; no filter gradient
-    for kw in (dict(dtype=dwc.F32), dict(stride=2), dict(c=12), dict(fw=33, pad=16),
-               dict(w=80)):
-        a = dict(n=2, h=20, w=20, c=16, fh=5, fw=5, stride=1, pad=2, dtype=dwc.BF16)
-        a.update(kw)
+    assert dwc.plan_describe(p, 2).startswith("bwd_filter direct")
+    # conditions of the packed kernels: half-precision operands, stride 1,
+    # C a multiple of 8, FW <= 32, output width <= 64 (forward), input width
+    # <= 64 and FH <= 32 (filter gradient)
+    base = dict(n=2, h=20, w=20, c=16, fh=5, fw=5, stride=1, pad=2, dtype=dwc.BF16)
+    for kw, ops in ((dict(dtype=dwc.F32), (0, 1, 2)), (dict(stride=2), (0, 1, 2)),
+                    (dict(c=12), (0, 1, 2)), (dict(fw=33, pad=16), (0, 1, 2)),
+                    (dict(w=80), (0, 2)), (dict(fh=33, pad=16), (2,))):
+        a = dict(base, **kw)
         q = dwc.problem(a["n"], a["h"], a["w"], a["c"], a["fh"], a["fw"], a["stride"],
                         a["pad"], dtype=a["dtype"], algo="mfma")
-        assert dwc.check(q, 0) == 2, kw
-        assert "packed-MFMA" in dwc.last_error()
+        for op in ops:
+            assert dwc.check(q, op) == 2, (kw, op)
+            assert "packed-MFMA" in dwc.last_error()
     q = dwc.problem(2, 20, 20, 16, 5, 5, 1, 2, dtype=dwc.BF16, algo="mfma")
-    assert dwc.check(q, 0) == 0 and dwc.check(q, 1) == 0
-    assert dwc.check(q, 2) == 2
+    assert dwc.check(q, 0) == 0 and dwc.check(q, 1) == 0 and dwc.check(q, 2) == 0
+    # an empty batch plans (it only zero-fills dW) and needs no workspace
+    q = dwc.problem(0, 20, 20, 16, 5, 5, 1, 2, dtype=dwc.BF16, algo="mfma")
+    assert dwc.check(q, 2) == 0 and dwc.workspace_size(q) == 0
+
+
+def test_mfma_wgrad_plan_geometry():
+    """The packed filter gradient splits the batch into slices of whole images
+    (one workspace partial per slice and channel block), never more slices than
+    images, and AUTO's workspace also covers the vector fallback."""
+    import re
+    for n, split in ((128, 0), (3, 0), (5, 2), (7, 7), (7, 3)):
+        p = dwc.problem(n, 28, 28, 512, 13, 13, 1, 6, dtype=dwc.BF16, algo="mfma",
+                        wgrad_split=split)
+        d = dict((k, int(v)) for k, v in re.findall(r"(\w+)=(\d+)", dwc.plan_describe(p, 2)))
+        z, ipb = d["z"], d["ipb"]
+        assert 1 <= z <= n and (z - 1) * ipb < n <= z * ipb
+        if split:
+            assert z <= split
+        assert d["blocks"] == z * d["cblk"] == z * 512 // 8
+        need = z * 13 * 13 * 512 * 4
+        assert dwc.workspace_size(p) >= need
+        pa = dwc.problem(n, 28, 28, 512, 13, 13, 1, 6, dtype=dwc.BF16, wgrad_split=split)
+        pd = dwc.problem(n, 28, 28, 512, 13, 13, 1, 6, dtype=dwc.BF16, algo="direct",
+                         wgrad_split=split)
+        assert dwc.workspace_size(pa) >= max(need, dwc.workspace_size(pd))
 
 
 def test_mfma_forced_misaligned_is_rejected_before_launch():
@@ -186,3 +217,7 @@ def test_mfma_forced_misaligned_is_rejected_before_launch():
     L = dwc.lib()
     assert L.dwc_fwd(ctypes.byref(p), 0x10002, 0x20000, 0x30000, None) == 3
     assert L.dwc_bwd_data(ctypes.byref(p), 0x10000, 0x20000, 0x30008, None) == 3
+    ws = dwc.workspace_size(p)
+    # the filter gradient also stores 16-byte partials into the workspace
+    assert L.dwc_bwd_filter(ctypes.byref(p), 0x10000, 0x20000, 0x30000, 0x40008, ws + 64,
+                            None) == 3

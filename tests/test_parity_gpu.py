@@ -183,7 +183,7 @@ MFMA_SHAPES = [
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("op", ["fwd", "bwd_data"])
+@pytest.mark.parametrize("op", ["fwd", "bwd_data", "bwd_filter"])
 @pytest.mark.parametrize("shape", MFMA_SHAPES,
                          ids=lambda t: "x".join(map(str, t[:6])) + f"_p{t[7]}")
 def test_mfma_parity(shape, op, dtype):
@@ -221,13 +221,21 @@ def test_mfma_misaligned_tensors():
         dwc.fwd(x, w, 1, 3, algo="mfma")
 
 
-@pytest.mark.parametrize("op", ["fwd", "bwd_data"])
+@pytest.mark.parametrize("op", ["fwd", "bwd_data", "bwd_filter"])
 def test_mfma_outputs_fully_overwritten(op):
     s = Shape(2, 21, 19, 40, 9, 9, 1, 1, 4, 4)
     inp = make_inputs(s, "bf16", seed=4)
     if op == "fwd":
         y = torch.full(s.y_shape(), float("nan"), device="cuda")
         dwc.fwd(to_device(inp.x), to_device(inp.w), 1, 4, out=y, algo="mfma")
+    elif op == "bwd_filter":
+        # NaN in dW and in every workspace byte: each partial is written
+        # before the reduction reads it
+        y = torch.full((9, 9, 40), float("nan"), device="cuda")
+        p = dwc.problem(2, 21, 19, 40, 9, 9, 1, 4, dtype=dwc.BF16, algo="mfma")
+        ws = torch.full((dwc.workspace_size(p) // 4,), float("nan"), device="cuda")
+        dwc.bwd_filter(to_device(inp.x), to_device(inp.dy), (9, 9), 1, 4, out=y,
+                       workspace=ws, algo="mfma")
     else:
         y = torch.full(s.x_shape(), float("nan"), device="cuda")
         dwc.bwd_data(to_device(inp.dy), to_device(inp.w), (21, 19), 1, 4, out=y, algo="mfma")
@@ -237,7 +245,7 @@ def test_mfma_outputs_fully_overwritten(op):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("op", ["fwd", "bwd_data"])
+@pytest.mark.parametrize("op", ["fwd", "bwd_data", "bwd_filter"])
 def test_mfma_many_workgroups(dtype, op):
     """Several row chunks and channel blocks per image: every workgroup
     stages its own rows and filter fragments."""
@@ -246,3 +254,18 @@ def test_mfma_many_workgroups(dtype, op):
     inp = make_inputs(s, dtype, seed=40)
     got = _run(op, s, inp, "mfma")
     assert rel_l2(got, _want(op, s, inp)) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("split", [1, 2, 3, 5])
+def test_mfma_wgrad_batch_slices(split):
+    """Slices of several images each (split < N): every slice accumulates
+    its images in registers, the reduction sums the slices in a fixed order,
+    so the result is run-to-run bitwise identical."""
+    s = _shape((5, 13, 17, 24, 7, 5, 1, (3, 2)))
+    inp = make_inputs(s, "bf16", seed=50 + split)
+    want = _want("bwd_filter", s, inp)
+    log(f"case mfma wgrad split={split}")
+    got = _run("bwd_filter", s, inp, "mfma", wgrad_split=split)
+    assert rel_l2(got, want) <= TOL["bf16"]
+    again = _run("bwd_filter", s, inp, "mfma", wgrad_split=split)
+    assert np.array_equal(got, again)
