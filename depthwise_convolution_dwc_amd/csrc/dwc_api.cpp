@@ -126,7 +126,7 @@ int dwc_bwd_filter(const dwc_problem* p, const void* x, const void* dy, void* dw
     w.x = x;
     w.dy = dy;
     w.ws = (float*)workspace;
-    e = launch_wgrad_mfma(pl.dt, pl.nfm, pl.nfn, pl.nk, w, s);
+    e = launch_wgrad_mfma(pl.dt, pl.nfm, pl.nfn, pl.nk, pl.pf, w, s);
     if (e != hipSuccess) return hip_fail(e, "dwc_bwd_filter launch");
     e = launch_reduce(
         ReduceArgs{(const float*)workspace, (float*)dw, m, pl.z, kWgmCb, w.C, w.FH * w.FW}, s);

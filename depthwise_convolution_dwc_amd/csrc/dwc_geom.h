@@ -97,6 +97,9 @@ struct WgradArgs {
 // Packed-MFMA workgroups: 8 waves, up to half of a CU's 160 KiB of LDS (two
 // workgroups per CU when the registers allow it).
 constexpr int kMfmaMaxLds = 81920;
+// MI355X (gfx950): compute units and LDS bytes per compute unit.
+constexpr int kCus = 256;
+constexpr int kLdsPerCu = 163840;
 constexpr int kMfmaWaves = 8;
 
 struct MfmaArgs {
@@ -135,6 +138,16 @@ struct ReduceArgs {
 // a slice of images; it writes one partial per slice in the channel-blocked
 // layout that reduce_partials reads with cb = kWgmCb.
 constexpr int kWgmCb = 8;
+// Staging items (pairs of pixels of one row, kWgmCb channels) per thread
+// that a workgroup holds in registers while the previous image computes.
+constexpr int kWgmMaxPf = 2;
+// Waves per SIMD the filter-gradient kernel is compiled for (its register
+// budget: 512 VGPRs / waves): three 8-wave workgroups per CU (80 VGPRs)
+// while the fragments and one staging item per thread fit, else two (128),
+// else one.
+constexpr int wgm_waves_per_eu(int nfm, int nfn, int nk, int pf) {
+  return pf == 1 ? ((nk == 1 || nfm * nfn == 1) ? 6 : 4) : (nfm * nfn * nk == 8 ? 2 : 4);
+}
 struct WgradMfmaArgs {
   const void* x;     // N x IH x IW x C
   const void* dy;    // N x OH x OW x C
@@ -144,8 +157,8 @@ struct WgradMfmaArgs {
   int cblk, Z, ipb;  // channel blocks, slices, images per slice
   int xr, xp;        // staged X: rows (IH + 1, row 0 = zeros), pitch (elements)
   int dyp, dpad;     // staged dY rows: pitch, zeros before column 0
-  int xe2_log;       // log2 of the X staging lanes per row (16 * NK)
-  int de_items, de2, de2_log;  // dY staging lanes per row (dyp / 2), pow2, log2
+  int hx, ix;        // X items: pixel pairs per row ((IW + 1) / 2), IH * hx
+  int e_lo, hd, id;  // dY items: first staged pair, pairs per row, OH * hd
   int lds_bytes;
   int num_blocks;    // Z * cblk
 };

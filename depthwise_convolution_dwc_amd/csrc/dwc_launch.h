@@ -40,9 +40,10 @@ hipError_t launch_fwd_mfma(int dt, int nf, int tiles, bool flip, const MfmaArgs&
                            hipStream_t s);
 
 // Packed-MFMA filter gradient: nfm / nfn 16-tap fragments of the filter
-// width / height, nk 32-column chunks of the input width.  Writes
-// channel-blocked slice partials (reduce with cb = kWgmCb).
-hipError_t launch_wgrad_mfma(int dt, int nfm, int nfn, int nk, const WgradMfmaArgs& a,
+// width / height, nk 32-column chunks of the input width, pf staging items
+// per thread.  Writes channel-blocked slice partials (reduce with
+// cb = kWgmCb).
+hipError_t launch_wgrad_mfma(int dt, int nfm, int nfn, int nk, int pf, const WgradMfmaArgs& a,
                              hipStream_t s);
 
 enum GenericKind { GEN_FWD = 0, GEN_FWD_FLIP = 1, GEN_DGRAD = 2, GEN_WGRAD = 3 };

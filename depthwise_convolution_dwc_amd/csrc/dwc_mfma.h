@@ -341,8 +341,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma(MfmaArgs a) {
 // slice of ipb images, stages each image's X and dY rows in LDS
 // channel-major, and writes one channel-blocked partial per slice.
 // ---------------------------------------------------------------------------
-template <int DT, int NFM, int NFN, int NK>
-__global__ __launch_bounds__(64 * kMfmaWaves) void wgrad_mfma(WgradMfmaArgs a) {
+template <int DT, int NFM, int NFN, int NK, int PF>
+__global__ __launch_bounds__(64 * kMfmaWaves, wgm_waves_per_eu(NFM, NFN, NK, PF)) void wgrad_mfma(
+    WgradMfmaArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
   constexpr int NT = 64 * kMfmaWaves;
   constexpr int CB = kWgmCb;
@@ -364,18 +365,90 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void wgrad_mfma(WgradMfmaArgs a) {
   float* pst = (float*)lds;             // [taps][CB], after the last image
   const uint32_t Cb = (uint32_t)a.C * 2u;
 
+  // ---- zero both staging regions once: per image only the pixels of the
+  // image are written, so the zero row, the columns past the image and the
+  // dY padding stay zero for every image of the slice
+  {
+    const int units = CB * (XR * XP + OH * DYP) / 8;  // 16-byte units
+    for (int i = tid; i < units; i += NT) ((mf_u32x4*)lds)[i] = mf_u32x4{0u, 0u, 0u, 0u};
+  }
+
+  // ---- this thread's staging items, the same for every image: item i of
+  // X is the pixel pair (2e, 2e+1) of row r; item i of dY is the pair of
+  // staged columns (2e, 2e+1), i.e. dY columns 2e - dpad and 2e + 1 - dpad.
+  // Global byte offsets within the image (kOOB: zero) and the LDS dword of
+  // channel 0 (-1: no item).
+  uint32_t xo0[PF], xo1[PF], do0[PF], do1[PF];
+  int xw[PF], dw[PF];
+#pragma unroll
+  for (int k = 0; k < PF; ++k) {
+    const int i = tid + k * NT;
+    xo0[k] = xo1[k] = do0[k] = do1[k] = kOOB;
+    xw[k] = dw[k] = -1;
+    if (i < a.ix) {
+      const int r = i / a.hx, e = i - r * a.hx;
+      xo0[k] = (uint32_t)(r * a.IW + 2 * e) * Cb + (uint32_t)c0 * 2u;
+      if (2 * e + 1 < a.IW) xo1[k] = xo0[k] + Cb;
+      xw[k] = (r + 1) * (XP / 2) + e;
+    }
+    if (i < a.id) {
+      const int r = i / a.hd, e = a.e_lo + (i - r * a.hd);
+      const int t0 = 2 * e - a.dpad;
+      const uint32_t base = (uint32_t)(r * a.OW) * Cb + (uint32_t)c0 * 2u;
+      if ((unsigned)t0 < (unsigned)a.OW) do0[k] = base + (uint32_t)t0 * Cb;
+      if ((unsigned)(t0 + 1) < (unsigned)a.OW) do1[k] = base + (uint32_t)(t0 + 1) * Cb;
+      dw[k] = r * (DYP / 2) + e;
+    }
+  }
+  mf_u32x4 vx0[PF], vx1[PF], vd0[PF], vd1[PF];
+  auto fetch = [&](int n) {  // global -> registers, in flight during compute
+    const auto rx = make_rsrc((const char*)a.x + (size_t)n * a.IH * a.IW * Cb,
+                              (uint32_t)(a.IH * a.IW) * Cb);
+    const auto rd = make_rsrc((const char*)a.dy + (size_t)n * OH * a.OW * Cb,
+                              (uint32_t)(OH * a.OW) * Cb);
+#pragma unroll
+    for (int k = 0; k < PF; ++k) {
+      vx0[k] = __builtin_bit_cast(mf_u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)xo0[k], 0, 0));
+      vx1[k] = __builtin_bit_cast(mf_u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)xo1[k], 0, 0));
+      vd0[k] = __builtin_bit_cast(mf_u32x4, __builtin_amdgcn_raw_buffer_load_b128(rd, (int)do0[k], 0, 0));
+      vd1[k] = __builtin_bit_cast(mf_u32x4, __builtin_amdgcn_raw_buffer_load_b128(rd, (int)do1[k], 0, 0));
+    }
+  };
+  auto commit = [&]() {  // registers -> LDS, transposed to channel-major
+    const int px = XR * XP / 2, pd = OH * DYP / 2;  // dwords per channel plane
+#pragma unroll
+    for (int k = 0; k < PF; ++k) {
+      if (xw[k] >= 0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          ((uint32_t*)xs)[xw[k] + j * px] = __builtin_amdgcn_perm(
+              vx1[k][j >> 1], vx0[k][j >> 1], (j & 1) ? 0x07060302u : 0x05040100u);
+      }
+      if (dw[k] >= 0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          ((uint32_t*)dz)[dw[k] + j * pd] = __builtin_amdgcn_perm(
+              vd1[k][j >> 1], vd0[k][j >> 1], (j & 1) ? 0x07060302u : 0x05040100u);
+      }
+    }
+  };
+
   // ---- per-lane constants.  A: lane (q, m) holds A[m][8q .. 8q+7]; B:
   // lane (q, n = m) holds B[8q .. 8q+7][n]; D: lane (q, j) holds
   // D[4q .. 4q+3][j].
   const int q = lane >> 4, m = lane & 15;
   const int cc = wave;
   // A starts at staged dY element 32 kc + 8q - 16 fm - m + pw + dpad of its
-  // row: read from the even element at or below, shift odd starts by 16 bits
+  // row: five dwords from the even element at or below, odd starts shifted
+  // by 16 bits
   const int ua = 8 * q - m + a.PW + a.dpad;
   const uint32_t ashift = (uint32_t)(ua & 1) * 16u;
   const uint32_t* dzl = (const uint32_t*)(dz + cc * OH * DYP + (ua & ~1));
+  const int dyp2 = DYP / 2;
   auto read_a = [&](int oh, int fm, int kc) -> mf_u32x4 {
-    const uint32_t* p = dzl + (oh * DYP + 32 * kc - 16 * fm) / 2;
+    const uint32_t* p = dzl + oh * dyp2 + 16 * kc - 8 * fm;
+    // dword reads (paired by the compiler): a 16-byte LDS read at these
+    // lane-varying 4-byte-aligned starts runs at about a sixth of the speed
     mf_u32x4 d;
     __builtin_memcpy(&d, p, 16);
     const uint32_t d4 = p[4];
@@ -394,98 +467,35 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void wgrad_mfma(WgradMfmaArgs a) {
 #pragma unroll
     for (int fn = 0; fn < NFN; ++fn) acc[fm][fn] = mf_f32x4{0.f, 0.f, 0.f, 0.f};
 
+  if (n0 < n1) fetch(n0);
   for (int n = n0; n < n1; ++n) {
-    __syncthreads();  // the previous image's operands are no longer read
-    // ---- stage X rows (LDS row 0 = zeros) and the zero-padded dY rows of
-    // image n, channel-major: each thread loads a pair of pixels (8
-    // channels, 16 bytes each) and writes 8 transposed dwords.
-    {
-      const char* img = (const char*)a.x + (size_t)n * a.IH * a.IW * Cb;
-      const auto rsrc = make_rsrc(img, (uint32_t)(a.IH * a.IW) * Cb);
-      const int e = tid & ((1 << a.xe2_log) - 1);  // column pair (16 NK per row)
-      const int r0 = tid >> a.xe2_log;
-      const int rs = NT >> a.xe2_log;
-      const uint32_t col0 = (uint32_t)(2 * e) * Cb + (uint32_t)c0 * 2u;
-      const bool ok0 = 2 * e < a.IW, ok1 = 2 * e + 1 < a.IW;
-      const int plane2 = XR * XP / 2;
-      uint32_t* dst0 = (uint32_t*)xs + e;
-      for (int rb = r0; rb < XR; rb += rs * kStageBatch) {
-        mf_u32x4 v0[kStageBatch], v1[kStageBatch];
-#pragma unroll
-        for (int b = 0; b < kStageBatch; ++b) {
-          const int r = rb + b * rs;
-          const bool rok = r >= 1 && r < XR;
-          const uint32_t off = (uint32_t)((r - 1) * a.IW) * Cb + col0;
-          v0[b] = __builtin_bit_cast(mf_u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                   rsrc, (int)(rok && ok0 ? off : kOOB), 0, 0));
-          v1[b] = __builtin_bit_cast(mf_u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                   rsrc, (int)(rok && ok1 ? off + Cb : kOOB), 0, 0));
-        }
-#pragma unroll
-        for (int b = 0; b < kStageBatch; ++b) {
-          const int r = rb + b * rs;
-          if (r >= XR) continue;
-          uint32_t* d = dst0 + r * (XP / 2);
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            d[j * plane2] = __builtin_amdgcn_perm(v1[b][j >> 1], v0[b][j >> 1],
-                                                  (j & 1) ? 0x07060302u : 0x05040100u);
-        }
-      }
-    }
-    {
-      const char* img = (const char*)a.dy + (size_t)n * OH * a.OW * Cb;
-      const auto rsrc = make_rsrc(img, (uint32_t)(OH * a.OW) * Cb);
-      const int e = tid & (a.de2 - 1);  // column pair of the staged row
-      const int r0 = tid >> a.de2_log;
-      const int rs = NT >> a.de2_log;
-      const int t0 = 2 * e - a.dpad;  // dY column of the pair's first element
-      const bool e_in = e < a.de_items;
-      const bool ok0 = e_in && (unsigned)t0 < (unsigned)a.OW;
-      const bool ok1 = e_in && (unsigned)(t0 + 1) < (unsigned)a.OW;
-      const uint32_t col0 = (uint32_t)t0 * Cb + (uint32_t)c0 * 2u;
-      const int plane2 = OH * DYP / 2;
-      uint32_t* dst0 = (uint32_t*)dz + e;
-      for (int rb = r0; rb < OH; rb += rs * kStageBatch) {
-        mf_u32x4 v0[kStageBatch], v1[kStageBatch];
-#pragma unroll
-        for (int b = 0; b < kStageBatch; ++b) {
-          const int r = rb + b * rs;
-          const bool rok = r < OH;
-          const uint32_t off = (uint32_t)(r * a.OW) * Cb + col0;
-          v0[b] = __builtin_bit_cast(mf_u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                   rsrc, (int)(rok && ok0 ? off : kOOB), 0, 0));
-          v1[b] = __builtin_bit_cast(mf_u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                   rsrc, (int)(rok && ok1 ? off + Cb : kOOB), 0, 0));
-        }
-#pragma unroll
-        for (int b = 0; b < kStageBatch; ++b) {
-          const int r = rb + b * rs;
-          if (r >= OH || !e_in) continue;
-          uint32_t* d = dst0 + r * (DYP / 2);
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            d[j * plane2] = __builtin_amdgcn_perm(v1[b][j >> 1], v0[b][j >> 1],
-                                                  (j & 1) ? 0x07060302u : 0x05040100u);
-        }
-      }
-    }
+    __syncthreads();  // the zero fill, or the previous image's reads, are done
+    commit();
     __syncthreads();
+    if (n + 1 < n1) fetch(n + 1);
 
-    // ---- accumulate over the image's output rows
-    mf_u32x4 A[NFM][NK], B[NFN][NK];
+    // ---- accumulate over the image's output rows.  B of row oh+1 is B of
+    // row oh moved down one lane (DPP row shift) with lane 15 of each row
+    // group taking input row oh+1 + 16 fn + 15 - ph, read one row ahead into
+    // R (the DPP "old" operand, kept where the shift has no source lane).
+    mf_u32x4 A[NFM][NK], B[NFN][NK], R[NFN][NK];
 #pragma unroll
     for (int fn = 0; fn < NFN; ++fn) {
       const int row = x_row(16 * fn + m - a.PH);
+      const int rrow = uniform(x_row(1 + 16 * fn + 15 - a.PH));
 #pragma unroll
-      for (int kc = 0; kc < NK; ++kc) B[fn][kc] = *(const mf_u32x4*)(xl + row * XP + 32 * kc);
+      for (int kc = 0; kc < NK; ++kc) {
+        B[fn][kc] = *(const mf_u32x4*)(xl + row * XP + 32 * kc);
+        R[fn][kc] = *(const mf_u32x4*)(xl + rrow * XP + 32 * kc);
+      }
     }
 #pragma unroll
     for (int fm = 0; fm < NFM; ++fm)
 #pragma unroll
       for (int kc = 0; kc < NK; ++kc) A[fm][kc] = read_a(0, fm, kc);
-    // One uniform body per output row: the operands of row oh+1 are formed
-    // in the last iteration too (from rows that exist, never used).
+    // One uniform body per output row: the operands of row oh+1 (and R of
+    // row oh+2) are formed in the last iterations too, from rows that exist
+    // (the zero row past the image), and never used.
     for (int oh = 0; oh < OH; ++oh) {
 #pragma unroll
       for (int kc = 0; kc < NK; ++kc)
@@ -500,18 +510,15 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void wgrad_mfma(WgradMfmaArgs a) {
 #pragma unroll
         for (int kc = 0; kc < NK; ++kc) A[fm][kc] = read_a(on, fm, kc);
 #pragma unroll
-      for (int fn = 0; fn < NFN; ++fn)
+      for (int fn = 0; fn < NFN; ++fn) {
+        const int rrow = uniform(x_row(oh + 2 + 16 * fn + 15 - a.PH));
 #pragma unroll
-        for (int kc = 0; kc < NK; ++kc)
+        for (int kc = 0; kc < NK; ++kc) {
 #pragma unroll
-          for (int v = 0; v < 4; ++v) B[fn][kc][v] = row_shift_down(B[fn][kc][v]);
-      // lane 15 of each row group takes input row oh+1 + 16 fn + 15 - ph
-      if (m == 15) {
-#pragma unroll
-        for (int fn = 0; fn < NFN; ++fn) {
-          const int row = uniform(x_row(oh + 1 + 16 * fn + 15 - a.PH));
-#pragma unroll
-          for (int kc = 0; kc < NK; ++kc) B[fn][kc] = *(const mf_u32x4*)(xl + row * XP + 32 * kc);
+          for (int v = 0; v < 4; ++v)
+            B[fn][kc][v] = __builtin_amdgcn_update_dpp(R[fn][kc][v], B[fn][kc][v], 0x101, 0xF,
+                                                       0xF, false);
+          R[fn][kc] = *(const mf_u32x4*)(xl + rrow * XP + 32 * kc);
         }
       }
     }

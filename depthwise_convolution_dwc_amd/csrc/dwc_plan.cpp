@@ -194,24 +194,46 @@ bool plan_wgrad_mfma(const dwc_problem* p, int64_t oh, int64_t ow, Plan* q) {
   // of a staged dY row and reads up to 10 elements from the even one below
   w.dpad = std::max(0, 16 * (nfm - 1) + 15 - w.PW);
   w.dyp = (32 * nk + w.PW + w.dpad + 2 + 7) / 8 * 8;
-  w.xe2_log = nk == 1 ? 4 : 5;  // 16 * nk column pairs per staged X row
-  w.de_items = w.dyp / 2;
-  w.de2 = 1;
-  w.de2_log = 0;
-  while (w.de2 < w.de_items) {
-    w.de2 *= 2;
-    ++w.de2_log;
-  }
-  if (w.de2 > 64 * kMfmaWaves) return false;
+  // staging items: pixel pairs of the image (X) and the staged dY pairs
+  // holding at least one real column
+  w.hx = (w.IW + 1) / 2;
+  w.ix = w.IH * w.hx;
+  w.e_lo = w.dpad / 2;
+  w.hd = (w.dpad + w.OW - 1) / 2 - w.e_lo + 1;
+  w.id = w.OH * w.hd;
+  const int items = std::max(w.ix, w.id);
+  const int pf = (items + 64 * kMfmaWaves - 1) / (64 * kMfmaWaves);
+  if (pf > kWgmMaxPf) return false;
   const int64_t stage = (int64_t)kWgmCb * (w.xr * w.xp + w.OH * w.dyp) * 2;
   const int64_t part = (int64_t)p->fh * p->fw * kWgmCb * 4;
   const int64_t lds = std::max(stage, part);
   if (lds > kMfmaMaxLds) return false;
   w.lds_bytes = (int)lds;
-  int z = p->wgrad_split > 0 ? p->wgrad_split
-                             : (int)std::max<int64_t>(1, (1024 + w.cblk - 1) / w.cblk);
+  // Slices of whole images.  Workgroups resident at once: 256 CUs times
+  // what one CU holds (LDS; registers: waves per SIMD / 2 for 8-wave
+  // groups).  Unless a split is requested, pick the slice count whose
+  // dispatch rounds times images per slice (plus one image's worth of
+  // fixed cost per round) is least, preferring fewer slices.
+  const int64_t per_cu = std::max<int64_t>(
+      1, std::min<int64_t>(kLdsPerCu / lds, wgm_waves_per_eu(nfm, nfn, nk, pf) / 2));
+  const int64_t resident = kCus * per_cu;
   const int64_t nn = std::max<int64_t>(p->n, 1);  // an empty batch only zero-fills dW
-  z = (int)std::min<int64_t>(z, nn);
+  int64_t z = 1;
+  if (p->wgrad_split > 0) {
+    z = std::min<int64_t>(p->wgrad_split, nn);
+  } else {
+    int64_t best = -1;
+    for (int64_t zc = 1; zc <= std::min<int64_t>(nn, 8 * resident); ++zc) {
+      const int64_t ipb = (nn + zc - 1) / zc, zr = (nn + ipb - 1) / ipb;
+      if (zr != zc) continue;  // same split as a smaller count
+      const int64_t rounds = (zr * w.cblk + resident - 1) / resident;
+      const int64_t cost = rounds * (ipb + 1);
+      if (best < 0 || cost < best) {
+        best = cost;
+        z = zr;
+      }
+    }
+  }
   w.ipb = (int)((nn + z - 1) / z);
   w.Z = (int)((nn + w.ipb - 1) / w.ipb);
   const int64_t blocks = (int64_t)w.Z * w.cblk;
@@ -221,6 +243,7 @@ bool plan_wgrad_mfma(const dwc_problem* p, int64_t oh, int64_t ow, Plan* q) {
   q->nfm = nfm;
   q->nfn = nfn;
   q->nk = nk;
+  q->pf = pf;
   q->cb = kWgmCb;
   q->z = w.Z;
   q->blocks = w.num_blocks;
@@ -526,10 +549,12 @@ std::string describe(const Plan& pl) {
   if (pl.kind == PLAN_MFMA && pl.op == DWC_OP_BWD_FILTER) {
     const WgradMfmaArgs& w = pl.wm;
     snprintf(buf, sizeof buf,
-             "%s mfma dt=%s fw=%d fh=%d nfm=%d nfn=%d nk=%d cb=%d xr=%d xp=%d dyp=%d dpad=%d "
-             "lds=%d z=%d ipb=%d cblk=%d blocks=%d ws_bytes=%zu",
-             ops[pl.op], dt_name(pl.dt), w.FW, w.FH, pl.nfm, pl.nfn, pl.nk, pl.cb, w.xr, w.xp,
-             w.dyp, w.dpad, w.lds_bytes, w.Z, w.ipb, w.cblk, pl.blocks, pl.ws_bytes);
+             "%s mfma dt=%s fw=%d fh=%d nfm=%d nfn=%d nk=%d pf=%d cb=%d xr=%d xp=%d dyp=%d "
+             "dpad=%d hx=%d ix=%d e_lo=%d hd=%d id=%d lds=%d z=%d ipb=%d cblk=%d blocks=%d "
+             "ws_bytes=%zu",
+             ops[pl.op], dt_name(pl.dt), w.FW, w.FH, pl.nfm, pl.nfn, pl.nk, pl.pf, pl.cb, w.xr,
+             w.xp, w.dyp, w.dpad, w.hx, w.ix, w.e_lo, w.hd, w.id, w.lds_bytes, w.Z, w.ipb,
+             w.cblk, pl.blocks, pl.ws_bytes);
     return buf;
   }
   if (pl.kind == PLAN_MFMA) {

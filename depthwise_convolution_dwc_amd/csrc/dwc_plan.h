@@ -40,7 +40,7 @@ struct Plan {
   int nf = 0, cb = 0, tiles = 0;
   MfmaArgs ma{};
   // packed-MFMA filter gradient
-  int nfm = 0, nfn = 0, nk = 0;
+  int nfm = 0, nfn = 0, nk = 0, pf = 0;
   WgradMfmaArgs wm{};
 
   // generic kernels

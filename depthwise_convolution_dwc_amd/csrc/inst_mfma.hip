@@ -43,9 +43,9 @@ hipError_t by_nf(int nf, int tiles, const MfmaArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-template <int DT, int NFM, int NFN, int NK>
+template <int DT, int NFM, int NFN, int NK, int PF>
 hipError_t wg_go(const WgradMfmaArgs& a, hipStream_t s) {
-  auto kernel = wgrad_mfma<DT, NFM, NFN, NK>;
+  auto kernel = wgrad_mfma<DT, NFM, NFN, NK, PF>;
   if (a.lds_bytes > 65536) {
     const hipError_t e = allow_lds(kernel);
     if (e != hipSuccess) return e;
@@ -54,33 +54,40 @@ hipError_t wg_go(const WgradMfmaArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int DT, int NFM, int NFN, int NK>
+hipError_t wg_by_pf(int pf, const WgradMfmaArgs& a, hipStream_t s) {
+  if (pf == 1) return wg_go<DT, NFM, NFN, NK, 1>(a, s);
+  if (pf == 2) return wg_go<DT, NFM, NFN, NK, 2>(a, s);
+  return hipErrorInvalidValue;
+}
+
 template <int DT, int NFM, int NFN>
-hipError_t wg_by_nk(int nk, const WgradMfmaArgs& a, hipStream_t s) {
-  if (nk == 1) return wg_go<DT, NFM, NFN, 1>(a, s);
-  if (nk == 2) return wg_go<DT, NFM, NFN, 2>(a, s);
+hipError_t wg_by_nk(int nk, int pf, const WgradMfmaArgs& a, hipStream_t s) {
+  if (nk == 1) return wg_by_pf<DT, NFM, NFN, 1>(pf, a, s);
+  if (nk == 2) return wg_by_pf<DT, NFM, NFN, 2>(pf, a, s);
   return hipErrorInvalidValue;
 }
 
 template <int DT, int NFM>
-hipError_t wg_by_nfn(int nfn, int nk, const WgradMfmaArgs& a, hipStream_t s) {
-  if (nfn == 1) return wg_by_nk<DT, NFM, 1>(nk, a, s);
-  if (nfn == 2) return wg_by_nk<DT, NFM, 2>(nk, a, s);
+hipError_t wg_by_nfn(int nfn, int nk, int pf, const WgradMfmaArgs& a, hipStream_t s) {
+  if (nfn == 1) return wg_by_nk<DT, NFM, 1>(nk, pf, a, s);
+  if (nfn == 2) return wg_by_nk<DT, NFM, 2>(nk, pf, a, s);
   return hipErrorInvalidValue;
 }
 
 template <int DT>
-hipError_t wg_by_nfm(int nfm, int nfn, int nk, const WgradMfmaArgs& a, hipStream_t s) {
-  if (nfm == 1) return wg_by_nfn<DT, 1>(nfn, nk, a, s);
-  if (nfm == 2) return wg_by_nfn<DT, 2>(nfn, nk, a, s);
+hipError_t wg_by_nfm(int nfm, int nfn, int nk, int pf, const WgradMfmaArgs& a, hipStream_t s) {
+  if (nfm == 1) return wg_by_nfn<DT, 1>(nfn, nk, pf, a, s);
+  if (nfm == 2) return wg_by_nfn<DT, 2>(nfn, nk, pf, a, s);
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_wgrad_mfma(int dt, int nfm, int nfn, int nk, const WgradMfmaArgs& a,
+hipError_t launch_wgrad_mfma(int dt, int nfm, int nfn, int nk, int pf, const WgradMfmaArgs& a,
                              hipStream_t s) {
-  if (dt == DT_BF16) return wg_by_nfm<DT_BF16>(nfm, nfn, nk, a, s);
-  if (dt == DT_F16) return wg_by_nfm<DT_F16>(nfm, nfn, nk, a, s);
+  if (dt == DT_BF16) return wg_by_nfm<DT_BF16>(nfm, nfn, nk, pf, a, s);
+  if (dt == DT_F16) return wg_by_nfm<DT_F16>(nfm, nfn, nk, pf, a, s);
   return hipErrorInvalidValue;
 }
 

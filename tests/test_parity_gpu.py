@@ -166,7 +166,9 @@ def test_caller_stream_is_used():
 # Shapes for the packed-MFMA kernel (bf16/fp16, stride 1): every tile shape
 # (column groups per tile 1, 2, 4; one or two tiles), both fragment counts,
 # a half-filled channel block, FH != FW, no padding, and data-gradient
-# padding larger than F-1 (a cropping forward map).
+# padding larger than F-1 (a cropping forward map); for the filter gradient
+# every fragment count (16-tap slices of FW and FH, 32-column chunks of W)
+# and one or two staging items per thread.
 MFMA_SHAPES = [
     (1, 6, 6, 16, 3, 3, 1, 1),
     (2, 20, 13, 24, 5, 5, 1, 2),
@@ -179,6 +181,10 @@ MFMA_SHAPES = [
     (1, 10, 10, 16, 3, 3, 1, 4),
     (1, 30, 64, 16, 9, 1, 1, (4, 0)),
     (3, 16, 16, 8, 1, 31, 1, (0, 15)),
+    (2, 36, 32, 8, 3, 3, 1, 1),
+    (1, 22, 64, 8, 5, 3, 1, (2, 1)),
+    (2, 12, 50, 8, 20, 20, 1, (9, 10)),
+    (1, 20, 60, 8, 17, 17, 1, 8),
 ]
 
 
