@@ -65,7 +65,8 @@ struct SweepArgs {
   float* out;        // forward-type: Y (or dX);  filter gradient: Z x F x F x C partials
   int N, IH, IW, C;  // dims of `in`
   int OH, OW;        // forward-type: output dims; filter gradient: dY dims
-  int F, P;          // filter size, padding (forward-type data gradient: F-1-pad)
+  int F, P, PW;      // filter size, row / column padding (forward-type data
+                     // gradient: F-1-pad)
   int tiles_w;       // column strips
   int R, cpi;        // output rows per chunk, chunks per image
   int cbg;           // channel blocks: ceil(C / 64)

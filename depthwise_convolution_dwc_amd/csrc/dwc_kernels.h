@@ -328,9 +328,9 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_sweep(SweepArgs a) {
   const char* img = (const char*)a.in + (size_t)n * a.IH * a.IW * Cb;
   const int ow0 = tw * TMW;
   const int o_start = rc * a.R;
-  const int o_cnt = a.OH - o_start < a.R ? a.OH - o_start : a.R;
-  const int i_start = o_start - a.P;
-  const int iw0 = ow0 - a.P;
+  const int o_cnt = uniform(a.OH - o_start < a.R ? a.OH - o_start : a.R);
+  const int i_start = uniform(o_start - a.P);
+  const int iw0 = ow0 - a.PW;
 
   uint32_t coff[SPAN];
   column_offsets<SPAN>(coff, iw0, a.IW, Cb, c, a.C, EB);
@@ -369,9 +369,14 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_sweep(SweepArgs a) {
       if (i_rel >= steps) break;
       load_strip<DT, SPAN>(xb[(u + 2) % NB], img, i_start + i_rel + 2, a.IH, iw0, a.IW, Cb, coff);
       const float(&xv)[SPAN] = xb[u % NB];
+      const bool row_in = (unsigned)(i_start + i_rel) < (unsigned)a.IH;
 #pragma unroll
       for (int fh = 0; fh < F; ++fh) {
         const int slot = ((u - fh) % F + F) % F;  // output row i_rel - fh
+        // Only products of an image row with an output row of this chunk
+        // count: padding rows add zero and the halo's rows are not stored
+        // (a wave-uniform branch).
+        if (!row_in || (unsigned)(i_rel - fh) >= (unsigned)o_cnt) continue;
 #pragma unroll
         for (int fw = 0; fw < F; ++fw)
 #pragma unroll
@@ -434,9 +439,10 @@ __global__ __launch_bounds__(kBlockThreads) void wgrad_sweep(SweepArgs a) {
     o_start = (chunk - n * a.cpi) * a.R;
     o_cnt = a.OH - o_start < a.R ? a.OH - o_start : a.R;
   }
+  o_cnt = uniform(o_cnt);
   const int ow0 = s * TJ;
-  const int iw0 = ow0 - a.P;
-  const int i_start = o_start - a.P;
+  const int iw0 = ow0 - a.PW;
+  const int i_start = uniform(o_start - a.P);
   const char* ximg = (const char*)a.in + (size_t)n * a.IH * a.IW * Cb;
   const char* dimg = (const char*)a.in2 + (size_t)n * a.OH * a.OW * Cb;
   uint32_t doff[TJ], xoff[SPAN];
@@ -471,9 +477,13 @@ __global__ __launch_bounds__(kBlockThreads) void wgrad_sweep(SweepArgs a) {
 #pragma unroll
       for (int q = 0; q < TJ; ++q) dv[u % F][q] = db[u % NB][q];  // newest dY row: o = i_rel
       const float(&xv)[SPAN] = xb[u % NB];
+      const bool row_in = (unsigned)(i_start + i_rel) < (unsigned)a.IH;
 #pragma unroll
       for (int fh = 0; fh < F; ++fh) {
         const int slot = ((u - fh) % F + F) % F;  // dY row i_rel - fh
+        // Only an image row times a dY row of this chunk adds anything
+        // (a wave-uniform branch).
+        if (!row_in || (unsigned)(i_rel - fh) >= (unsigned)o_cnt) continue;
 #pragma unroll
         for (int q = 0; q < TJ; ++q)
 #pragma unroll

@@ -69,12 +69,14 @@ int strip_override(const char* var, int fallback) {
   return (w == 7 || w == 14) ? w : fallback;
 }
 
-// Chunks per image for a sweep launch: enough waves (~3072, three per SIMD)
+// Chunks per image for a sweep launch: enough waves (~2048, two per SIMD)
 // to fill the GPU, with chunks of at least F rows (each chunk re-reads F-1
 // halo rows).
 int64_t sweep_chunks(int64_t waves_per_chunk, int64_t out_h, int f) {
   const int64_t w = std::max<int64_t>(waves_per_chunk, 1);
-  const int64_t cpi = std::max<int64_t>(1, (3072 + w - 1) / w);
+  int64_t target = 2048;
+  if (const char* v = getenv("DWC_SWEEP_WAVES")) target = std::max(1, atoi(v));
+  const int64_t cpi = std::max<int64_t>(1, (target + w - 1) / w);
   return std::min<int64_t>(cpi, std::max<int64_t>(1, out_h / f));
 }
 
@@ -348,6 +350,7 @@ int make_plan(const dwc_problem* p, int op, Plan* pl, std::string* err) {
         w.N = f.N; w.IH = f.IH; w.IW = f.IW; w.C = C; w.OH = f.OH; w.OW = f.OW;
         w.F = p->fw;
         w.P = f.PH;
+        w.PW = f.PW;
         q.tmw = p->fw >= 7 ? 7 : strip_override("DWC_FWD_STRIP", pick_strip(f.OW));
         w.tiles_w = (f.OW + q.tmw - 1) / q.tmw;
         w.cbg = cblocks;
@@ -431,6 +434,7 @@ int make_plan(const dwc_problem* p, int op, Plan* pl, std::string* err) {
         sw.OH = (int)oh; sw.OW = (int)ow;
         sw.F = p->fw;
         sw.P = p->pad_h;
+        sw.PW = p->pad_w;
         q.tj = p->fw >= 7 ? 7 : strip_override("DWC_WGRAD_STRIP", pick_strip(ow));
         q.tfh = p->fh;
         sw.tiles_w = (int)((ow + q.tj - 1) / q.tj);

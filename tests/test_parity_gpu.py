@@ -37,6 +37,12 @@ SHAPES = [
     (1, 11, 13, 40, 3, 3, 3, 1),
     (1, 33, 35, 128, 7, 7, 1, 0),
     (2, 12, 29, 64, 5, 5, (2, 1), 2),
+    # square stride-1 filters with unequal row / column padding (the sweep
+    # kernels pad rows and columns separately)
+    (2, 13, 17, 64, 3, 3, 1, (1, 0)),
+    (1, 12, 15, 96, 5, 5, 1, (0, 2)),
+    (2, 11, 20, 64, 7, 7, 1, (3, 1)),
+    (1, 16, 13, 128, 9, 9, 1, (2, 4)),
 ]
 
 
@@ -275,3 +281,24 @@ def test_mfma_wgrad_batch_slices(split):
     assert rel_l2(got, want) <= TOL["bf16"]
     again = _run("bwd_filter", s, inp, "mfma", wgrad_split=split)
     assert np.array_equal(got, again)
+
+
+@pytest.mark.parametrize("rows", [1, 2, 3, 6, 7, 11])
+@pytest.mark.parametrize("op", ["fwd", "bwd_data", "bwd_filter"])
+@pytest.mark.parametrize("shape", [(2, 23, 21, 64, 7, 7, 1, 3), (2, 17, 19, 64, 3, 3, 1, 1),
+                                   (1, 20, 14, 128, 5, 5, 1, (2, 1)), (1, 19, 16, 64, 9, 9, 1, 4)],
+                         ids=lambda t: "x".join(map(str, t[:6])) + f"_p{t[7]}")
+def test_sweep_row_chunks(shape, op, rows, monkeypatch):
+    """The sweep kernels cut each image into chunks of R output rows that
+    re-read F-1 halo rows and skip the products that fall outside the
+    chunk or the image: every chunk size, including R < F and ragged last
+    chunks, matches the oracle."""
+    monkeypatch.setenv("DWC_SWEEP_ROWS", str(rows))
+    s = _shape(shape)
+    p = dwc.problem(s.n, s.h, s.w, s.c, s.fh, s.fw, 1, (s.pad_h, s.pad_w), algo="direct")
+    d = dwc.plan_describe(p, OPS[op])
+    assert " sweep " in d and f" rows={rows} " in d, d
+    inp = make_inputs(s, "f32", seed=60 + rows)
+    log(f"case sweep rows={rows} {shape} {op}")
+    got = _run(op, s, inp, "direct")
+    assert rel_l2(got, _want(op, s, inp)) <= TOL["f32"]
