@@ -12,9 +12,11 @@ the CPU oracle's rate on a bounded sample.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
        python bench.py --copy-calibration  (a plain 256 MiB device copy, for counters)
        python bench.py --sweep OUT.jsonl   (every named workload, one line per op)
-       python bench.py --summarize-profile TRACE_DIR FETCH_DIR WRITE_DIR COPYF_DIR COPYW_DIR
-           (turn rocprofv3 CSV output of this benchmark into profiles/*.md and
-            profiles/traffic.json; see profiles/README.md for the commands)
+       python bench.py --summarize-profile DIR
+           (turn the rocprofv3 CSV output of this benchmark under DIR -- trace/,
+            fetch/, write/, copyf/, copyw/ and the traced run's stdout trace.log,
+            made by the commands in profiles/README.md -- into profiles/*.md and
+            profiles/traffic.json)
 """
 
 from __future__ import annotations
@@ -179,31 +181,40 @@ class OpCall:
 
 
 def time_step(torch, calls_per_set, steps, warmup):
-    """Warm up, then time exactly `steps` steps with events between the ops.
-    Returns (ms per step, per-op mean ms)."""
+    """Warm up, then time exactly `steps` steps between two events on the
+    current stream, with nothing recorded between the ops (an event between
+    kernels adds a few microseconds of GPU time).  Returns ms per step."""
     nsets = len(calls_per_set)
-    nops = len(calls_per_set[0])
     for i in range(warmup):
         for c in calls_per_set[i % nsets]:
             c()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nops + 1)] for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     start.record()
     for i in range(steps):
-        calls = calls_per_set[i % nsets]
-        e = evs[i]
-        for j, c in enumerate(calls):
-            e[j].record()
+        for c in calls_per_set[i % nsets]:
             c()
-        e[nops].record()
     end.record()
     torch.cuda.synchronize()
-    total = start.elapsed_time(end)
-    per_op = [float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)]))
-              for j in range(nops)]
-    return total / steps, per_op
+    return start.elapsed_time(end) / steps
+
+
+def time_ops(torch, calls_per_set, reps):
+    """Mean GPU duration of each op of the step: `reps` back-to-back launches
+    of that op alone, each on the next buffer set (so none reads cached
+    data), between two events on the stream the library launches on."""
+    nsets = len(calls_per_set)
+    per_op = []
+    for j in range(len(calls_per_set[0])):
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for i in range(reps):
+            calls_per_set[i % nsets][j]()
+        end.record()
+        torch.cuda.synchronize()
+        per_op.append(start.elapsed_time(end) / reps)
+    return per_op
 
 
 # ---------------------------------------------------------- CPU oracle ------
@@ -310,8 +321,8 @@ def main():
     ap.add_argument("--sweep", default=None, help="write per-op lines of every workload here")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 256 MiB a few times (scales the byte counters)")
-    ap.add_argument("--summarize-profile", nargs=5, default=None,
-                    metavar=("TRACE", "FETCH", "WRITE", "COPYF", "COPYW"))
+    ap.add_argument("--summarize-profile", default=None, metavar="DIR",
+                    help="write profiles/ from the rocprofv3 output under DIR")
     args = ap.parse_args()
     if args.copy_calibration:
         import torch
@@ -323,11 +334,7 @@ def main():
         print("copied 256 MiB 5 times", flush=True)
         return
     if args.summarize_profile:
-        trace_md, traffic_md, fs, ws = summarize_profile(*args.summarize_profile)
-        print(trace_md)
-        print()
-        print(traffic_md)
-        print(f"\nFETCH_SIZE scale {fs:.3f}, WRITE_SIZE scale {ws:.3f} (from a 256 MiB copy)")
+        summarize_profile(args.summarize_profile)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -353,7 +360,8 @@ def main():
     inp = make_inputs(s1, "f32", seed=0, x_dist=wl["x_dist"], w_dist=wl["w_dist"])
     sets = build_sets(dwc, torch, plan, inp, dev)
     log(f"bench: {len(sets)} buffer sets, {args.warmup} warmup + {args.steps} timed steps")
-    ms, per_op = time_step(torch, sets, args.steps, args.warmup)
+    ms = time_step(torch, sets, args.steps, args.warmup)
+    per_op = time_ops(torch, sets, args.steps)
 
     models = [op_model(s, op, "f32") for s, op in plan]
     flops = sum(m["flops"] for m in models)
@@ -412,31 +420,106 @@ def _csv_rows(d, pattern):
     return rows
 
 
-def summarize_profile(trace_dir, fetch_dir, write_dir, copyf_dir, copyw_dir):
-    """Write profiles/ summaries from rocprofv3 CSV output of this benchmark."""
-    os.makedirs(PROFILES, exist_ok=True)
-    # kernel trace: per-kernel durations
-    stats = {}
-    for r in _csv_rows(trace_dir, "*kernel_trace.csv"):
-        k = r["Kernel_Name"]
-        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-        stats.setdefault(k, []).append(d)
-    lines = ["| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
-    for k, v in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
-        lines.append(f"| `{k}` | {len(v)} | {np.mean(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
-    trace_md = "\n".join(lines)
+PROFILE_STEPS, PROFILE_WARMUP = 20, 5
+PROFILE_NAME = "cnn_stage_n64_56x56_c128_k7_fp32_step"
+PROFILE_CMDS = {
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof/trace "
+             f"-o run -- python3 $R/bench.py --steps {PROFILE_STEPS} --warmup {PROFILE_WARMUP} "
+             "--no-cpu > $R/gpurun_out/prof/trace.log",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof/fetch -o run "
+             "-- python3 $R/bench.py --steps 5 --warmup 2 --no-cpu",
+    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof/write -o run "
+             "-- python3 $R/bench.py --steps 5 --warmup 2 --no-cpu",
+    "copyf": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof/copyf -o run "
+             "-- python3 $R/bench.py --copy-calibration",
+    "copyw": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof/copyw -o run "
+             "-- python3 $R/bench.py --copy-calibration",
+}
+OP_KERNELS = {"fwd_s1": ["fwd_sweep<0, 7, 7, false>"], "fwd_s2": ["fwd_rows<0, 7, 2"],
+              "bwd_data": ["fwd_sweep<0, 7, 7, true>"],
+              "bwd_filter": ["wgrad_sweep<0, 7, 7>", "reduce_partials"]}
 
-    def per_kernel(d, counter):
+
+def summarize_profile(d):
+    """Write profiles/<workload>.kernel_trace.md, .hbm_traffic.md and
+    traffic.json from the rocprofv3 output of this benchmark under d."""
+    os.makedirs(PROFILES, exist_ok=True)
+    cd = "cd /tmp && export TMPDIR=/tmp && "
+    # kernel trace: per-kernel durations in dispatch order.  The traced run
+    # launches each kernel PROFILE_WARMUP + PROFILE_STEPS times in the step
+    # loop, then PROFILE_STEPS times back to back in the per-op pass that
+    # gives the JSON line's per-op durations.
+    rows = sorted(_csv_rows(os.path.join(d, "trace"), "*kernel_trace.csv"),
+                  key=lambda r: int(r["Start_Timestamp"]))
+    stats = {}
+    for r in rows:
+        stats.setdefault(r["Kernel_Name"], []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = ["| kernel | calls | avg us (all) | min us | max us | avg us (per-op pass) |",
+             "|---|---|---|---|---|---|"]
+    passavg = {}
+    for k, v in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
+        passavg[k] = float(np.mean(v[-PROFILE_STEPS:]))
+        lines.append(f"| `{k}` | {len(v)} | {np.mean(v):.2f} | {min(v):.2f} | {max(v):.2f} | "
+                     f"{passavg[k]:.2f} |")
+    traced = None
+    log_path = os.path.join(d, "trace.log")
+    if os.path.exists(log_path):
+        for ln in open(log_path):
+            if ln.startswith("{") and '"metric"' in ln:
+                traced = json.loads(ln)
+    cmp = ["| op | kernels | rocprofv3 per-op pass, us | JSON line `ops.<op>.ms`, us |",
+           "|---|---|---|---|"]
+    for op, pats in OP_KERNELS.items():
+        ks = [k for p in pats for k in stats if p in k]
+        tr = sum(passavg[k] for k in ks)
+        js = traced["ops"][op]["ms"] * 1e3 if traced else float("nan")
+        cmp.append(f"| {op} | {' + '.join(_kernel_short(k) for k in ks)} | {tr:.2f} | {js:.2f} |")
+    trace_md = f"""# Kernel trace: CNN-stage step, N=64 56x56 C=128 7x7 pad 3, fp32
+
+One benchmark step = forward stride 1 + forward stride 2 + data gradient +
+filter gradient on the same batch (the default `bench.py` workload), on one
+MI355X, buffer sets rotating over >= 1 GiB (no Infinity-Cache reuse).  The
+traced run launches each kernel {PROFILE_WARMUP} + {PROFILE_STEPS} times in
+the step loop, then {PROFILE_STEPS} times back to back in the per-op pass
+whose event timings give the JSON line's per-op durations.
+
+Command (repository root `$R`):
+
+```
+{cd}{PROFILE_CMDS["trace"]}
+cd $R && python3 bench.py --summarize-profile gpurun_out/prof
+```
+
+Durations from the dispatch timestamps of `run_kernel_trace.csv`:
+
+{chr(10).join(lines)}
+
+`fwd_sweep<.., true>` is the data gradient (the forward sweep on dY with the
+filter turned by 180 degrees); `fwd_rows<0, 7, 2, ...>` is the stride-2
+forward; the filter gradient is `wgrad_sweep` followed by `reduce_partials`.
+
+Per-op durations of the same traced command: the kernels' rocprofv3 average
+over the per-op pass against the JSON line it printed (HIP events on the
+library's stream; under the profiler both run a few percent slower than in
+an unprofiled run):
+
+{chr(10).join(cmp)}
+"""
+    with open(os.path.join(PROFILES, PROFILE_NAME + ".kernel_trace.md"), "w") as f:
+        f.write(trace_md)
+
+    def per_kernel(sub, counter):
         acc = {}
-        for r in _csv_rows(d, "*counter_collection.csv"):
+        for r in _csv_rows(os.path.join(d, sub), "*counter_collection.csv"):
             if r["Counter_Name"] != counter:
                 continue
             acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
         return {k: float(np.mean(v)) for k, v in acc.items()}
 
-    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
-    cf = per_kernel(copyf_dir, "FETCH_SIZE")
-    cw = per_kernel(copyw_dir, "WRITE_SIZE")
+    fetch, write = per_kernel("fetch", "FETCH_SIZE"), per_kernel("write", "WRITE_SIZE")
+    cf = per_kernel("copyf", "FETCH_SIZE")
+    cw = per_kernel("copyw", "WRITE_SIZE")
     copy_bytes = 256 * 1024 * 1024  # the calibration copy moves 256 MiB each way
     ck = [k for k in cf if "copyBuffer" in k]
     f_scale = copy_bytes / cf[ck[0]] if ck else 1.0
@@ -464,7 +547,36 @@ def summarize_profile(trace_dir, fetch_dir, write_dir, copyf_dir, copyw_dir):
     for k, e in sorted(kernels.items()):
         tl.append(f"| `{k}` | {e['fetch_bytes'] / 1e6:.1f} MB | {e['write_bytes'] / 1e6:.1f} MB | "
                   f"{e['bytes_per_launch'] / 1e6:.1f} MB |")
-    return trace_md, "\n".join(tl), f_scale, w_scale
+    cmds = "\n".join(cd + PROFILE_CMDS[k] for k in ("fetch", "write", "copyf", "copyw"))
+    traffic_md = f"""# HBM traffic per launch: CNN-stage step, N=64 56x56 C=128 7x7 pad 3, fp32
+
+Per-dispatch `FETCH_SIZE` and `WRITE_SIZE` (KiB, rocprofv3 derived counters,
+each in a run of its own), averaged over the step's launches of each kernel
+and scaled by what the same counters read for a plain 256 MiB device copy
+(`bench.py --copy-calibration`, the runtime's copyBuffer kernel): on this
+MI355X `FETCH_SIZE` reads {1 / f_scale:.3f} of the copied bytes (scale
+{f_scale:.3f}) and `WRITE_SIZE` {1 / w_scale:.3f} (scale {w_scale:.3f}).
+
+Commands (repository root `$R`):
+
+```
+{cmds}
+cd $R && python3 bench.py --summarize-profile gpurun_out/prof
+```
+
+{chr(10).join(tl)}
+
+Algorithmic bytes for comparison (each operand read once, output written
+once): forward 102.8 MB in + 102.8 MB out; stride-2 forward 102.8 MB in +
+25.7 MB out; filter gradient 102.8 MB (X) + 102.8 MB (dY) in.  The same
+numbers are in `traffic.json`, which `bench.py` reads for the `traffic`
+field of its roofline entry while the kernel sources are unchanged (their
+hash is stored with the data).
+"""
+    with open(os.path.join(PROFILES, PROFILE_NAME + ".hbm_traffic.md"), "w") as f:
+        f.write(traffic_md)
+    print(trace_md)
+    print(traffic_md)
 
 
 def sweep(dwc, torch, dev, args):
@@ -480,7 +592,7 @@ def sweep(dwc, torch, dev, args):
                     plan = [(s, op)]
                     sets = build_sets(dwc, torch, plan, inp, dev, algo)
                     steps = max(10, min(args.steps, 200))
-                    ms, _ = time_step(torch, sets, steps, min(args.warmup, 10))
+                    ms = time_step(torch, sets, steps, min(args.warmup, 10))
                     m = op_model(s, op, dt)
                     p = dwc.problem(s.n, s.h, s.w, s.c, s.fh, s.fw, (s.stride_h, s.stride_w),
                                     (s.pad_h, s.pad_w), {"f32": 0, "bf16": 1, "f16": 2}[dt], algo)

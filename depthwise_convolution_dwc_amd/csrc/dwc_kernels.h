@@ -329,14 +329,22 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_sweep(SweepArgs a) {
   const int ow0 = tw * TMW;
   const int o_start = rc * a.R;
   const int o_cnt = uniform(a.OH - o_start < a.R ? a.OH - o_start : a.R);
-  const int i_start = uniform(o_start - a.P);
   const int iw0 = ow0 - a.PW;
+  // Odd chunks walk up from their last row: neighbouring chunks then reach
+  // the F-1 input rows they share at the same time and the second read
+  // hits L2.  Walking up is the same ring with the filter rows reversed:
+  // step i reads input row i_first + dir * i and output row o_rel is
+  // o_first + dir * o_rel.
+  const bool up = (rc & 1) != 0;
+  const int dir = up ? -1 : 1;
+  const int i_first = uniform(up ? o_start + o_cnt - 1 - a.P + F - 1 : o_start - a.P);
+  const int o_first = up ? o_start + o_cnt - 1 : o_start;
 
   uint32_t coff[SPAN];
   column_offsets<SPAN>(coff, iw0, a.IW, Cb, c, a.C, EB);
   float xb[NB][SPAN];
-  load_strip<DT, SPAN>(xb[0], img, i_start, a.IH, iw0, a.IW, Cb, coff);
-  load_strip<DT, SPAN>(xb[1], img, i_start + 1, a.IH, iw0, a.IW, Cb, coff);
+  load_strip<DT, SPAN>(xb[0], img, i_first, a.IH, iw0, a.IW, Cb, coff);
+  load_strip<DT, SPAN>(xb[1], img, i_first + dir, a.IH, iw0, a.IW, Cb, coff);
 
   float wv[F][F];
   {
@@ -346,7 +354,8 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_sweep(SweepArgs a) {
     for (int fh = 0; fh < F; ++fh)
 #pragma unroll
       for (int fw = 0; fw < F; ++fw) {
-        const int e = FLIP ? (F - 1 - fh) * F + (F - 1 - fw) : fh * F + fw;
+        const int fr = up ? F - 1 - fh : fh;  // filter row of ring offset fh
+        const int e = FLIP ? (F - 1 - fr) * F + (F - 1 - fw) : fr * F + fw;
         wv[fh][fw] = ld<DT>(wrs, voff, (uint32_t)e * Cb);
       }
   }
@@ -361,15 +370,16 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_sweep(SweepArgs a) {
     for (int q = 0; q < TMW; ++q) acc[r][q] = 0.f;
 
   float* out_img = a.out + (size_t)n * a.OH * a.OW * a.C;
-  const int steps = o_cnt + F - 1;  // input rows i_start .. i_start+steps-1
+  const int steps = o_cnt + F - 1;  // input rows i_first + dir * (0 .. steps-1)
   for (int g = 0; g < steps; g += L) {
 #pragma unroll
     for (int u = 0; u < L; ++u) {
       const int i_rel = g + u;  // = u (mod F) and (mod NB)
       if (i_rel >= steps) break;
-      load_strip<DT, SPAN>(xb[(u + 2) % NB], img, i_start + i_rel + 2, a.IH, iw0, a.IW, Cb, coff);
+      load_strip<DT, SPAN>(xb[(u + 2) % NB], img, i_first + dir * (i_rel + 2), a.IH, iw0, a.IW, Cb,
+                           coff);
       const float(&xv)[SPAN] = xb[u % NB];
-      const bool row_in = (unsigned)(i_start + i_rel) < (unsigned)a.IH;
+      const bool row_in = (unsigned)(i_first + dir * i_rel) < (unsigned)a.IH;
 #pragma unroll
       for (int fh = 0; fh < F; ++fh) {
         const int slot = ((u - fh) % F + F) % F;  // output row i_rel - fh
@@ -388,7 +398,7 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_sweep(SweepArgs a) {
       const int done = (u + 1) % F;
       const int o_rel = i_rel - (F - 1);
       const bool ok = o_rel >= 0 && o_rel < o_cnt;
-      const float* orow = out_img + ((ptrdiff_t)(o_start + o_rel) * a.OW + ow0) * a.C;
+      const float* orow = out_img + ((ptrdiff_t)(o_first + dir * o_rel) * a.OW + ow0) * a.C;
       const auto ors = make_rsrc(orow, ok ? (uint32_t)(TMW * a.C) * 4u : 0u);
 #pragma unroll
       for (int q = 0; q < TMW; ++q) {
@@ -433,27 +443,34 @@ __global__ __launch_bounds__(kBlockThreads) void wgrad_sweep(SweepArgs a) {
   const int c = cb * kWaveChannels + lane;
   const uint32_t Cb = (uint32_t)a.C * EB;
   const int chunk = cg * kWavesPerBlock + wave;
-  int n = 0, o_start = 0, o_cnt = 0;
+  int n = 0, rc = 0, o_start = 0, o_cnt = 0;
   if (chunk < a.N * a.cpi) {
     n = chunk / a.cpi;
-    o_start = (chunk - n * a.cpi) * a.R;
+    rc = chunk - n * a.cpi;
+    o_start = rc * a.R;
     o_cnt = a.OH - o_start < a.R ? a.OH - o_start : a.R;
   }
   o_cnt = uniform(o_cnt);
   const int ow0 = s * TJ;
   const int iw0 = ow0 - a.PW;
-  const int i_start = uniform(o_start - a.P);
+  // Odd chunks walk up from their last row (see fwd_sweep): step i reads
+  // input row i_first + dir * i and dY row o_first + dir * i, and ring
+  // offset fh then stands for filter row F-1-fh.
+  const bool up = (rc & 1) != 0;
+  const int dir = up ? -1 : 1;
+  const int i_first = uniform(up ? o_start + o_cnt - 1 - a.P + F - 1 : o_start - a.P);
+  const int o_first = up ? o_start + o_cnt - 1 : o_start;
   const char* ximg = (const char*)a.in + (size_t)n * a.IH * a.IW * Cb;
   const char* dimg = (const char*)a.in2 + (size_t)n * a.OH * a.OW * Cb;
   uint32_t doff[TJ], xoff[SPAN];
   column_offsets<TJ>(doff, ow0, a.OW, Cb, c, a.C, EB);
   column_offsets<SPAN>(xoff, iw0, a.IW, Cb, c, a.C, EB);
-  auto drow = [&](int i) { return i < o_cnt ? o_start + i : -1; };  // dY row of step i
+  auto drow = [&](int i) { return i < o_cnt ? o_first + dir * i : -1; };  // dY row of step i
 
   float xb[NB][SPAN], db[NB][TJ];
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
-    load_strip<DT, SPAN>(xb[k], ximg, i_start + k, a.IH, iw0, a.IW, Cb, xoff);
+    load_strip<DT, SPAN>(xb[k], ximg, i_first + dir * k, a.IH, iw0, a.IW, Cb, xoff);
     load_strip<DT, TJ>(db[k], dimg, drow(k), a.OH, ow0, a.OW, Cb, doff);
   }
   float acc[F][F];
@@ -472,12 +489,13 @@ __global__ __launch_bounds__(kBlockThreads) void wgrad_sweep(SweepArgs a) {
     for (int u = 0; u < L; ++u) {
       const int i_rel = g + u;  // = u (mod F) and (mod NB)
       if (i_rel >= steps) break;
-      load_strip<DT, SPAN>(xb[(u + 2) % NB], ximg, i_start + i_rel + 2, a.IH, iw0, a.IW, Cb, xoff);
+      load_strip<DT, SPAN>(xb[(u + 2) % NB], ximg, i_first + dir * (i_rel + 2), a.IH, iw0, a.IW, Cb,
+                           xoff);
       load_strip<DT, TJ>(db[(u + 2) % NB], dimg, drow(i_rel + 2), a.OH, ow0, a.OW, Cb, doff);
 #pragma unroll
       for (int q = 0; q < TJ; ++q) dv[u % F][q] = db[u % NB][q];  // newest dY row: o = i_rel
       const float(&xv)[SPAN] = xb[u % NB];
-      const bool row_in = (unsigned)(i_start + i_rel) < (unsigned)a.IH;
+      const bool row_in = (unsigned)(i_first + dir * i_rel) < (unsigned)a.IH;
 #pragma unroll
       for (int fh = 0; fh < F; ++fh) {
         const int slot = ((u - fh) % F + F) % F;  // dY row i_rel - fh
@@ -490,6 +508,17 @@ __global__ __launch_bounds__(kBlockThreads) void wgrad_sweep(SweepArgs a) {
           for (int fw = 0; fw < F; ++fw) acc[fh][fw] = fmaf(xv[q + fw], dv[slot][q], acc[fh][fw]);
       }
     }
+  }
+
+  if (up) {  // ring offset k held filter row F-1-k
+#pragma unroll
+    for (int k = 0; k < F / 2; ++k)
+#pragma unroll
+      for (int fw = 0; fw < F; ++fw) {
+        const float v = acc[k][fw];
+        acc[k][fw] = acc[F - 1 - k][fw];
+        acc[F - 1 - k][fw] = v;
+      }
   }
 
   // (w0 + w2) + (w1 + w3), then one store of the partial.
