@@ -101,6 +101,12 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_rows(FwdArgs a) {
   const auto wrs = make_rsrc(a.filt, (uint32_t)(a.FH * FW) * Cb);
   const int oh0 = th * TR, ow0 = tw * TMW;
   const int ih_base = oh0 * S - a.PH;
+  // Odd row tiles walk their input rows bottom-up, so two neighbouring
+  // tiles read the rows they share at about the same time and the second
+  // read hits L2.  Bottom-up is the same computation on the tile mirrored
+  // vertically: input row m stands for row MSPAN-1-m of the chunk, filter
+  // row k for FHC-1-k and accumulator row r for output row TR-1-r.
+  const bool up = (th & 1) != 0;
   const int iw0 = ow0 * S - a.PW;
   uint32_t coff[SPAN];
   column_offsets<SPAN>(coff, iw0, a.IW, Cb, c, a.C, EB);
@@ -115,7 +121,7 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_rows(FwdArgs a) {
     float wv[FHC][FW];
 #pragma unroll
     for (int k = 0; k < FHC; ++k) {
-      const int fh = fh0 + k;
+      const int fh = fh0 + (up ? FHC - 1 - k : k);
       const bool ok = fh < a.FH;
       const int fhe = FLIP ? a.FH - 1 - fh : fh;
 #pragma unroll
@@ -126,7 +132,7 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_rows(FwdArgs a) {
     }
 #pragma unroll
     for (int m = 0; m < MSPAN; ++m) {
-      const int ih = ih_base + fh0 + m;
+      const int ih = ih_base + fh0 + (up ? MSPAN - 1 - m : m);
       if ((unsigned)ih >= (unsigned)a.IH) continue;  // a padding row: contributes 0
       float xv[SPAN];
       load_strip<DT, SPAN>(xv, img, ih, a.IH, iw0, a.IW, Cb, coff);
@@ -146,8 +152,8 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_rows(FwdArgs a) {
     float* out = a.out + (size_t)n * a.OH * a.OW * a.C + c;
 #pragma unroll
     for (int r = 0; r < TR; ++r) {
-      const int oh = oh0 + r;
-      if (oh >= a.OH) break;
+      const int oh = oh0 + (up ? TR - 1 - r : r);
+      if (oh >= a.OH) continue;
 #pragma unroll
       for (int q = 0; q < TMW; ++q) {
         const int ow = ow0 + q;
