@@ -28,7 +28,17 @@ __global__ __launch_bounds__(64 * kReduceWaves) void reduce_partials(ReduceArgs 
       j = ((int64_t)(c / a.cb) * a.taps + tap) * a.cb + c % a.cb;
     }
     const float* p = a.ws + j;
-    for (int z = z0; z < z1; ++z) s += p[(int64_t)z * a.M];
+    // Batches of 8 loads in flight, then their sum in slice order: the same
+    // additions as one slice at a time, without a memory latency per slice.
+    int z = z0;
+    for (; z + 8 <= z1; z += 8) {
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = p[(int64_t)(z + k) * a.M];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) s += v[k];
+    }
+    for (; z < z1; ++z) s += p[(int64_t)z * a.M];
   }
   part[wave][lane] = s;
   __syncthreads();
