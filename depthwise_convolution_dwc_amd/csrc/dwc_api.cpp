@@ -19,6 +19,18 @@ int hip_fail(hipError_t e, const char* what) {
 
 hipError_t launch_fwd_type(const Plan& pl, const void* in, const void* filt, float* out,
                            hipStream_t s) {
+  if (pl.kind == PLAN_PHASE) {
+    DgradPhaseArgs g = pl.pa;
+    g.dy = in;
+    g.filt = filt;
+    g.dx = out;
+    switch (pl.dt) {
+      case DT_F32: return launch_dgrad_phase_dt0(pl.km, g, pl.blocks, s);
+      case DT_BF16: return launch_dgrad_phase_dt1(pl.km, g, pl.blocks, s);
+      case DT_F16: return launch_dgrad_phase_dt2(pl.km, g, pl.blocks, s);
+    }
+    return hipErrorInvalidValue;
+  }
   if (pl.kind == PLAN_MFMA) {
     MfmaArgs m = pl.ma;
     m.in = in;

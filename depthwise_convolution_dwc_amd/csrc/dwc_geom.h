@@ -55,6 +55,26 @@ struct FwdArgs {
   int num_items;     // waves of work: N * cblocks * tiles_h * tiles_w
 };
 
+// Strided data gradient by output phase.  For stride S, the dX pixels whose
+// row is a (mod S) and column b (mod S) form a stride-1 correlation of dY
+// with the sub-filter of taps (f0h + S k, f0w + S l), where f0h = (a + PH)
+// mod S and f0w = (b + PW) mod S.  A wave computes one phase of a tile of
+// TR x TMW phase pixels; the S*S phases of a tile are consecutive waves.
+// The sub-filter is padded to KM x KM taps (zeros past its real size).
+#define DWC_PHASE_KM_LIST(M) M(1) M(2) M(3) M(4) M(5) M(6) M(7) M(8) M(10) M(12) M(14) M(16)
+constexpr int kPhaseMaxKm = 16;
+constexpr int kPhaseTmw = 7;
+struct DgradPhaseArgs {
+  const void* dy;    // N x OH x OW x C
+  const void* filt;  // FH x FW x C
+  float* dx;         // N x IH x IW x C
+  int N, IH, IW, C, OH, OW;
+  int FH, FW, S, PH, PW;
+  int tiles_i, tiles_j;  // tiles over ceil(IH / S) x ceil(IW / S) phase pixels
+  int cblocks;
+  int num_items;     // waves: N * cblocks * tiles_i * tiles_j * S * S
+};
+
 // Sweep kernels (stride 1, square F <= 9): waves walk down R consecutive
 // output rows of one image.  Forward-type: one wave per (image, row chunk,
 // channel block, column strip).  Filter gradient: a workgroup's 4 waves take

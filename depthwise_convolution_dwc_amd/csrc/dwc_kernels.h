@@ -164,6 +164,113 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_rows(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Strided data gradient (stride S >= 2 in both dimensions) by output phase.
+//
+// dX[ih][iw] gathers dY[oh][ow] * W[fh][fw] over oh*S - PH + fh = ih and
+// ow*S - PW + fw = iw (the adjoint of the strided forward map).  For the dX
+// pixels ih = a + S i, iw = b + S j of phase (a, b), only the taps
+// fh = f0h + S k and fw = f0w + S l contribute, with oh = i + ch - k and
+// ow = j + cw - l (f0h = (a + PH) mod S, ch = (a + PH - f0h) / S; likewise
+// for columns): a stride-1 correlation of dY with that sub-filter, which
+// runs like fwd_rows -- TR x TMW outputs per lane, sub-filter rows in
+// registers in chunks of KC, one dY strip per row feeding every output row
+// that reads it, width-first reuse along the strip.  KM bounds the
+// sub-filter's rows and columns; taps past its real size are zeros.  The
+// S*S phases of a tile are consecutive waves of one workgroup, so they read
+// the same dY rows at the same time.
+// ---------------------------------------------------------------------------
+template <int DT, int KM, int TMW>
+__global__ __launch_bounds__(kBlockThreads) void dgrad_phase(DgradPhaseArgs a) {
+  constexpr int EB = Elem<DT>::bytes;
+  constexpr int TR = kFwdRows;
+  constexpr int KC = KM <= 8 ? KM : 4;  // sub-filter rows held at once
+  constexpr int SPAN = TMW + KM - 1;
+  constexpr int MSPAN = TR + KC - 1;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int item = xcd_logical_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wave;
+  if (item >= a.num_items) return;
+  const int S = a.S;
+  int t = item;
+  const int ph = t % (S * S);
+  t /= S * S;
+  const int tj = t % a.tiles_j;
+  t /= a.tiles_j;
+  const int ti = t % a.tiles_i;
+  t /= a.tiles_i;
+  const int cb = t % a.cblocks;
+  const int n = t / a.cblocks;
+  const int pa = ph / S, pb = ph - pa * S;  // row and column phase
+  const int f0h = (pa + a.PH) % S, f0w = (pb + a.PW) % S;
+  const int ch = (pa + a.PH - f0h) / S, cw = (pb + a.PW - f0w) / S;
+  const int kh = f0h < a.FH ? (a.FH - f0h + S - 1) / S : 0;  // sub-filter rows
+  const int kw = f0w < a.FW ? (a.FW - f0w + S - 1) / S : 0;  // and columns
+  const int c = cb * kWaveChannels + lane;
+  const uint32_t voff = c < a.C ? (uint32_t)c * EB : kOOB;
+  const uint32_t Cb = (uint32_t)a.C * EB;
+  const char* img = (const char*)a.dy + (size_t)n * a.OH * a.OW * Cb;
+  const auto zero = make_rsrc(a.filt, 0);
+  const auto wrs = make_rsrc(a.filt, (uint32_t)(a.FH * a.FW) * Cb);
+  const int i0 = ti * TR, j0 = tj * TMW;  // first phase row / column of the tile
+  // strip of dY columns ow0 .. ow0+SPAN-1: output column q, tap l reads
+  // strip element q - l + KM - 1
+  const int ow0 = j0 + cw - (KM - 1);
+  uint32_t coff[SPAN];
+  column_offsets<SPAN>(coff, ow0, a.OW, Cb, c, a.C, EB);
+
+  float acc[TR][TMW];
+#pragma unroll
+  for (int r = 0; r < TR; ++r)
+#pragma unroll
+    for (int q = 0; q < TMW; ++q) acc[r][q] = 0.f;
+
+  for (int k0 = 0; k0 < kh; k0 += KC) {
+    float wv[KC][KM];
+#pragma unroll
+    for (int k = 0; k < KC; ++k)
+#pragma unroll
+      for (int l = 0; l < KM; ++l) {
+        const bool ok = k0 + k < kh && l < kw;
+        const int e = (f0h + S * (k0 + k)) * a.FW + f0w + S * l;
+        wv[k][l] = ld<DT>(ok ? wrs : zero, voff, ok ? (uint32_t)e * Cb : 0u);
+      }
+    // dY row ohb + m feeds output row r through chunk row k = r + KC - 1 - m
+    const int ohb = i0 + ch - (k0 + KC - 1);
+#pragma unroll
+    for (int m = 0; m < MSPAN; ++m) {
+      const int oh = ohb + m;
+      if ((unsigned)oh >= (unsigned)a.OH) continue;  // no such dY row: contributes 0
+      float yv[SPAN];
+      load_strip<DT, SPAN>(yv, img, oh, a.OH, ow0, a.OW, Cb, coff);
+#pragma unroll
+      for (int r = 0; r < TR; ++r) {
+        const int k = r + KC - 1 - m;
+        if (k < 0 || k >= KC) continue;
+#pragma unroll
+        for (int l = 0; l < KM; ++l)
+#pragma unroll
+          for (int q = 0; q < TMW; ++q)
+            acc[r][q] = fmaf(yv[q - l + KM - 1], wv[k][l], acc[r][q]);
+      }
+    }
+  }
+
+  if (c < a.C) {
+    float* out = a.dx + (size_t)n * a.IH * a.IW * a.C + c;
+#pragma unroll
+    for (int r = 0; r < TR; ++r) {
+      const int ih = pa + S * (i0 + r);
+      if (ih >= a.IH) break;
+#pragma unroll
+      for (int q = 0; q < TMW; ++q) {
+        const int iw = pb + S * (j0 + q);
+        if (iw < a.IW) out[((size_t)ih * a.IW + iw) * a.C] = acc[r][q];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Filter-gradient direct kernel (§5.1 "accumulation-axis parallelism").
 //
 // A workgroup owns 64 channels x a chunk of TFH filter rows x all FW taps

@@ -16,6 +16,12 @@ hipError_t launch_fwd_direct_dt2(int fw, int s, int tmw, bool flip, const FwdArg
                                  int blocks, hipStream_t st);
 
 // Filter-gradient direct kernel for operand dtype dt.
+// Strided data gradient by output phase; km: padded sub-filter size (one of
+// DWC_PHASE_KM_LIST).
+hipError_t launch_dgrad_phase_dt0(int km, const DgradPhaseArgs& a, int blocks, hipStream_t s);
+hipError_t launch_dgrad_phase_dt1(int km, const DgradPhaseArgs& a, int blocks, hipStream_t s);
+hipError_t launch_dgrad_phase_dt2(int km, const DgradPhaseArgs& a, int blocks, hipStream_t s);
+
 hipError_t launch_wgrad_direct_dt0(int fw, int s, int tj, const WgradArgs& a, int blocks,
                                    hipStream_t st);
 hipError_t launch_wgrad_direct_dt1(int fw, int s, int tj, const WgradArgs& a, int blocks,

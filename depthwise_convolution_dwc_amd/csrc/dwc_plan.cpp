@@ -257,10 +257,10 @@ bool plan_wgrad_mfma(const dwc_problem* p, int64_t oh, int64_t ow, Plan* q) {
 
 void set_last_error(const std::string& msg) { g_last_error = msg; }
 
-int make_plan(const dwc_problem* p, int op, Plan* pl, std::string* err) {
+// Checks of the problem itself, shared by every entry point (not which
+// kernel would run it); on success *oh_out, *ow_out are the output dims.
+static int validate(const dwc_problem* p, int64_t* oh_out, int64_t* ow_out, std::string* err) {
   if (!p) return fail(err, DWC_ERR_BAD_PARAM, "problem pointer is NULL");
-  if (op < DWC_OP_FWD || op > DWC_OP_BWD_FILTER)
-    return fail(err, DWC_ERR_BAD_PARAM, "unknown operation code");
   if (p->n < 0 || p->h < 1 || p->w < 1 || p->c < 1)
     return fail(err, DWC_ERR_BAD_PARAM, "need n >= 0 and h, w, c >= 1");
   if (p->fh < 1 || p->fw < 1) return fail(err, DWC_ERR_BAD_PARAM, "need fh, fw >= 1");
@@ -279,15 +279,26 @@ int make_plan(const dwc_problem* p, int op, Plan* pl, std::string* err) {
   if (a < 0 || b < 0)
     return fail(err, DWC_ERR_BAD_PARAM, "filter larger than the padded input (OH or OW < 1)");
   const int64_t oh = a / p->stride_h + 1, ow = b / p->stride_w + 1;
-
-  const int dt = p->in_dtype;
-  const int64_t eb = elem_bytes(dt);
   // 32-bit buffer offsets: one image of every tensor, and the filter, must
   // stay below 2 GiB; counts of rows and work items must fit in int32.
   if (p->h * p->w * p->c * 4 > kI32Max || oh * ow * p->c * 4 > kI32Max ||
       (int64_t)p->fh * p->fw * p->c * 4 > kI32Max || p->n * std::max(oh, p->h) > kI32Max ||
       p->c > kI32Max / 4)
     return fail(err, DWC_ERR_UNSUPPORTED, "tensor too large for 32-bit per-image offsets");
+  *oh_out = oh;
+  *ow_out = ow;
+  return DWC_OK;
+}
+
+int make_plan(const dwc_problem* p, int op, Plan* pl, std::string* err) {
+  if (op < DWC_OP_FWD || op > DWC_OP_BWD_FILTER)
+    return fail(err, DWC_ERR_BAD_PARAM, "unknown operation code");
+  int64_t oh = 0, ow = 0;
+  const int vst = validate(p, &oh, &ow, err);
+  if (vst != DWC_OK) return vst;
+
+  const int dt = p->in_dtype;
+  const int64_t eb = elem_bytes(dt);
 
   Plan q;
   q.op = op;
@@ -302,8 +313,18 @@ int make_plan(const dwc_problem* p, int op, Plan* pl, std::string* err) {
   // data gradient: stride 1, where it is a forward map with the filter
   // turned by 180 degrees).
   const bool square_stride = p->stride_h == p->stride_w && p->stride_w <= 2;
+  // Strided data gradient: the phase kernel, for equal strides >= 2 whose
+  // sub-filters fit the largest instantiated size.
+  int phase_km = 0;
+  if (op == DWC_OP_BWD_DATA && p->stride_h == p->stride_w && p->stride_h >= 2) {
+    const int need = (std::max(p->fh, p->fw) + p->stride_h - 1) / p->stride_h;
+#define DWC_PICK(K) \
+  if (phase_km == 0 && need <= K) phase_km = K;
+    DWC_PHASE_KM_LIST(DWC_PICK)
+#undef DWC_PICK
+  }
   bool can_direct = direct_fw(p->fw) && square_stride;
-  if (op == DWC_OP_BWD_DATA) can_direct = can_direct && p->stride_w == 1;
+  if (op == DWC_OP_BWD_DATA) can_direct = (can_direct && p->stride_w == 1) || phase_km > 0;
   if (p->algo == DWC_ALGO_DIRECT && !can_direct)
     return fail(err, DWC_ERR_UNSUPPORTED,
                 "no direct kernel for this filter width / stride (use DWC_ALGO_AUTO)");
@@ -340,6 +361,26 @@ int make_plan(const dwc_problem* p, int op, Plan* pl, std::string* err) {
         return fail(err, DWC_ERR_UNSUPPORTED,
                     "no packed-MFMA kernel for this problem (needs bf16/fp16, stride 1, "
                     "FW <= 32, C % 8 == 0, output width <= 64)");
+    }
+    if (direct && bwd && p->stride_h > 1) {
+      const int S = p->stride_h;
+      DgradPhaseArgs g{};
+      g.N = (int)p->n; g.IH = (int)p->h; g.IW = (int)p->w; g.C = C;
+      g.OH = (int)oh; g.OW = (int)ow;
+      g.FH = p->fh; g.FW = p->fw; g.S = S; g.PH = p->pad_h; g.PW = p->pad_w;
+      g.tiles_i = (int)(((p->h + S - 1) / S + kFwdRows - 1) / kFwdRows);
+      g.tiles_j = (int)(((p->w + S - 1) / S + kPhaseTmw - 1) / kPhaseTmw);
+      g.cblocks = cblocks;
+      const int64_t items = p->n * cblocks * (int64_t)g.tiles_i * g.tiles_j * S * S;
+      if (items > kI32Max - kWavesPerBlock)
+        return fail(err, DWC_ERR_UNSUPPORTED, "too many work items for one launch");
+      g.num_items = (int)items;
+      q.kind = PLAN_PHASE;
+      q.km = phase_km;
+      q.blocks = (int)((items + kWavesPerBlock - 1) / kWavesPerBlock);
+      q.pa = g;
+      *pl = q;
+      return DWC_OK;
     }
     if (direct) {
       q.flip = bwd;
@@ -550,6 +591,15 @@ int check_pointers(const dwc_problem* p, const Plan& pl, const void* in0, const 
 std::string describe(const Plan& pl) {
   static const char* ops[] = {"fwd", "bwd_data", "bwd_filter"};
   char buf[512];
+  if (pl.kind == PLAN_PHASE) {
+    const DgradPhaseArgs& g = pl.pa;
+    snprintf(buf, sizeof buf,
+             "%s phase dt=%s fh=%d fw=%d s=%d km=%d tiles_i=%d tiles_j=%d cblocks=%d items=%d "
+             "blocks=%d",
+             ops[pl.op], dt_name(pl.dt), g.FH, g.FW, g.S, pl.km, g.tiles_i, g.tiles_j, g.cblocks,
+             g.num_items, pl.blocks);
+    return buf;
+  }
   if (pl.kind == PLAN_MFMA && pl.op == DWC_OP_BWD_FILTER) {
     const WgradMfmaArgs& w = pl.wm;
     snprintf(buf, sizeof buf,
@@ -623,15 +673,15 @@ const char* dwc_status_string(int s) {
 const char* dwc_last_error(void) { return g_last_error.c_str(); }
 
 int dwc_output_dims(const dwc_problem* p, int64_t* oh, int64_t* ow) {
-  Plan pl;
   std::string err;
-  const int st = make_plan(p, DWC_OP_FWD, &pl, &err);
+  int64_t h = 0, w = 0;
+  const int st = validate(p, &h, &w, &err);
   if (st) {
     set_last_error(err);
     return st;
   }
-  if (oh) *oh = pl.oh;
-  if (ow) *ow = pl.ow;
+  if (oh) *oh = h;
+  if (ow) *ow = w;
   return DWC_OK;
 }
 

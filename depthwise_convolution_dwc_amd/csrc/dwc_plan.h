@@ -11,7 +11,7 @@
 
 namespace dwc {
 
-enum PlanKind { PLAN_NONE = 0, PLAN_DIRECT = 1, PLAN_GENERIC = 2, PLAN_MFMA = 3 };
+enum PlanKind { PLAN_NONE = 0, PLAN_DIRECT = 1, PLAN_GENERIC = 2, PLAN_MFMA = 3, PLAN_PHASE = 4 };
 
 struct Plan {
   int op = 0;
@@ -42,6 +42,9 @@ struct Plan {
   // packed-MFMA filter gradient
   int nfm = 0, nfn = 0, nk = 0, pf = 0;
   WgradMfmaArgs wm{};
+  // strided data gradient by output phase
+  int km = 0;
+  DgradPhaseArgs pa{};
 
   // generic kernels
   int gen_kind = 0;

@@ -105,6 +105,20 @@ hipError_t wgrad_sweep_by_f(int f, const SweepArgs& a, int blocks, hipStream_t s
 
 }  // namespace
 
+hipError_t DWC_CAT(launch_dgrad_phase_dt, DWC_INST_DT)(int km, const DgradPhaseArgs& a,
+                                                       int blocks, hipStream_t s) {
+  switch (km) {
+#define DWC_CASE(K)                                                                        \
+  case K:                                                                                  \
+    hipLaunchKernelGGL((dgrad_phase<kDt, K, kPhaseTmw>), dim3(blocks), dim3(kBlockThreads), \
+                       0, s, a);                                                           \
+    return hipGetLastError();
+    DWC_PHASE_KM_LIST(DWC_CASE)
+#undef DWC_CASE
+  }
+  return hipErrorInvalidValue;
+}
+
 hipError_t DWC_CAT(launch_fwd_sweep_dt, DWC_INST_DT)(int f, int tmw, bool flip, const SweepArgs& a,
                                                      int blocks, hipStream_t st) {
   if (tmw == 7) return flip ? fwd_sweep_by_f<7, true>(f, a, blocks, st)

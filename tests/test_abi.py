@@ -91,8 +91,11 @@ def test_direct_unavailable_is_unsupported():
     p = dwc.problem(1, 8, 8, 4, 4, 4, 1, 1, algo="auto")
     assert dwc.check(p, 0) == 0
     assert "generic" in dwc.plan_describe(p, 0)
-    # stride-2 data gradient runs the gather kernel
+    # stride-2 data gradient runs the phase kernel, or the gather kernel
+    # when asked for the generic family
     p = dwc.problem(1, 8, 8, 4, 3, 3, 2, 1)
+    assert "bwd_data phase" in dwc.plan_describe(p, 1)
+    p = dwc.problem(1, 8, 8, 4, 3, 3, 2, 1, algo="generic")
     assert "bwd_data generic" in dwc.plan_describe(p, 1)
 
 
@@ -221,3 +224,33 @@ def test_mfma_forced_misaligned_is_rejected_before_launch():
     # the filter gradient also stores 16-byte partials into the workspace
     assert L.dwc_bwd_filter(ctypes.byref(p), 0x10000, 0x20000, 0x30000, 0x40008, ws + 64,
                             None) == 3
+
+
+def test_strided_data_gradient_plans():
+    """Equal strides >= 2 take the phase kernel (AUTO and DIRECT) while the
+    sub-filter fits 16 x 16 taps; unequal strides and larger sub-filters
+    take the generic kernel, and DIRECT is then an error."""
+    p = dwc.problem(64, 56, 56, 128, 7, 7, 2, 3)
+    d = dwc.plan_describe(p, 1)
+    assert d.startswith("bwd_data phase") and "km=4" in d and "s=2" in d
+    q = dwc.problem(1, 10, 10, 64, 5, 5, 3, 2, algo="direct")
+    assert dwc.check(q, 1) == 0 and "km=2" in dwc.plan_describe(q, 1)
+    big = dwc.problem(1, 40, 40, 8, 35, 35, 2, 17)
+    assert dwc.plan_describe(big, 1).startswith("bwd_data generic")
+    big.algo = dwc.ALGO["direct"]
+    assert dwc.check(big, 1) == 2
+    uneq = dwc.problem(1, 12, 12, 8, 3, 3, (2, 1), 1)
+    assert dwc.plan_describe(uneq, 1).startswith("bwd_data generic")
+
+
+def test_output_dims_do_not_depend_on_the_kernel_choice():
+    """OH and OW come from the problem alone: a problem whose forced algo has
+    no forward kernel (stride 3 forced to DIRECT) still has output dims, and
+    its data gradient plans."""
+    p = dwc.problem(1, 11, 13, 40, 3, 3, 3, 1, algo="direct")
+    assert dwc.output_dims(p) == (4, 5)
+    assert dwc.check(p, 0) == 2
+    assert dwc.check(p, 1) == 0
+    bad = dwc.problem(1, 4, 4, 8, 7, 7, 1, 0)
+    with pytest.raises(dwc.DwcError):
+        dwc.output_dims(bad)

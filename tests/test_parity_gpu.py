@@ -302,3 +302,51 @@ def test_sweep_row_chunks(shape, op, rows, monkeypatch):
     log(f"case sweep rows={rows} {shape} {op}")
     got = _run(op, s, inp, "direct")
     assert rel_l2(got, _want(op, s, inp)) <= TOL["f32"]
+
+
+# Strided data gradient (the phase kernel): strides 2 and 3, square and
+# non-square filters, even filters, sub-filters that need chunking (KM > 8),
+# padding larger than the stride, dims that are not multiples of the stride,
+# ragged channel blocks and a stride larger than the filter.
+STRIDED_DGRAD_SHAPES = [
+    (2, 9, 10, 64, 3, 3, 2, 1),
+    (1, 11, 13, 70, 31, 31, 2, 15),
+    (1, 10, 10, 64, 5, 5, 3, 2),
+    (2, 8, 8, 64, 1, 1, 2, 0),
+    (1, 9, 9, 64, 4, 6, 2, (1, 2)),
+    (2, 17, 16, 96, 7, 7, 2, 3),
+    (1, 12, 15, 130, 9, 9, 2, 4),
+    (1, 20, 9, 64, 17, 5, 2, (8, 2)),
+    (1, 7, 7, 33, 3, 3, 3, 0),
+    (1, 13, 11, 64, 21, 21, 2, 10),
+    (1, 6, 6, 64, 2, 2, 2, 0),
+    (2, 28, 28, 128, 7, 7, 2, 3),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("shape", STRIDED_DGRAD_SHAPES,
+                         ids=lambda t: "x".join(map(str, t[:6])) + f"_s{t[6]}_p{t[7]}")
+def test_strided_dgrad_phase(shape, dtype):
+    s = _shape(shape)
+    p = dwc.problem(s.n, s.h, s.w, s.c, s.fh, s.fw, (s.stride_h, s.stride_w),
+                    (s.pad_h, s.pad_w), dtype=DT[dtype])
+    assert " phase " in dwc.plan_describe(p, 1)
+    inp = make_inputs(s, dtype, seed=70 + sum(shape[:6]))
+    want = _want("bwd_data", s, inp)
+    log(f"case phase {shape} {dtype}")
+    for algo in ("auto", "direct"):
+        got = _run("bwd_data", s, inp, algo)
+        assert got.shape == want.shape
+        assert rel_l2(got, want) <= TOL[dtype], algo
+        assert np.all(np.isfinite(got))
+
+
+def test_strided_dgrad_overwrites_output():
+    s = _shape((2, 17, 16, 96, 7, 7, 2, 3))
+    inp = make_inputs(s, "f32", seed=5)
+    dx = torch.full(s.x_shape(), float("nan"), device="cuda")
+    dwc.bwd_data(to_device(inp.dy), to_device(inp.w), (17, 16), 2, 3, out=dx)
+    sync()
+    assert torch.isfinite(dx).all().item()
+    assert rel_l2(dx.double().cpu().numpy(), _want("bwd_data", s, inp)) <= TOL["f32"]
