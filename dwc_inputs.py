@@ -181,6 +181,12 @@ WORKLOADS: Dict[str, dict] = {
         shapes=[_same(64, hw, c, f) for (hw, c) in SWEEP_STAGES for f in SWEEP_FILTERS],
         x_dist=("normal", 1.0), w_dist=None,
         ops=("fwd", "bwd_data", "bwd_filter"), dtypes=("f32",)),
+    # Strided backward of the CNN stage's stride-2 forward (N=64, 56x56,
+    # C=128, 7x7, pad 3): the data and filter gradients a training step needs.
+    "strided_bwd_n64_56x56_c128_k7_s2": dict(
+        shapes=[_same(64, 56, 128, 7, stride=2)],
+        x_dist=("normal", 1.0), w_dist=None,
+        ops=("bwd_data", "bwd_filter"), dtypes=("f32",)),
     # Mixed precision: bf16/fp16 operands, fp32 accumulate/output.
     "mixed_n128_28x28_c512": dict(
         shapes=[_same(128, 28, 512, 13), _same(128, 28, 512, 31)],

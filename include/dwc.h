@@ -136,8 +136,11 @@ int dwc_fwd(const dwc_problem* p, const void* x, const void* w, void* y,
  *   w  : FH x FW x C of in_dtype           (read)
  *   dx : N x H x W x C fp32                (overwritten; pixels no window
  *                                           reads get 0)
- * Any stride is accepted; stride 1 runs the rotated-filter forward kernels
- * the section describes, other strides a gather kernel. */
+ * Any stride is accepted.  Stride 1 runs the rotated-filter forward kernels
+ * the section describes.  Equal strides S >= 2 split dx into S*S output
+ * phases, each a stride-1 correlation of dy with the sub-filter of taps
+ * (fh, fw) = (f0h + S k, f0w + S l) (DWC_ALGO_DIRECT; sub-filters up to
+ * 16 x 16).  Other strides run a gather kernel (DWC_ALGO_GENERIC). */
 int dwc_bwd_data(const dwc_problem* p, const void* dy, const void* w,
                  void* dx, void* stream);
 
