@@ -4,7 +4,9 @@ The oracle is the plain float64 direct-loop definition of DWC forward, data
 gradient and filter gradient (Flash-DWC, TACO: §2.1 for the per-channel inner
 product, §2.3 for the channel-last layouts, §5.1 for the two backward
 operators).  The arithmetic lives in ``dwc_oracle.c``; this module builds it
-with gcc and calls it through ctypes.
+with gcc and calls it through ctypes.  The fused prologue of §5.2 (per-channel
+scale and shift, then an activation, applied to X before the forward) is an
+elementwise float64 map written here in numpy.
 
 Only the tests, the smoke check and the benchmark's CPU-baseline leg may
 import this package.  The GPU library never does, and the two share no code.
@@ -226,3 +228,40 @@ def bwd_data_at(*a, **k):
 
 def bwd_filter_at(*a, **k):
     return get().bwd_filter_at(*a, **k)
+
+
+# --------------------------------------------------------------------------
+# Fused prologue (Flash-DWC, TACO, §5.2 "kernel fusion": the batch
+# normalisation and activation that usually precede a DWC, applied to X as
+# part of the forward).  Read as inference-form batch normalisation -- one
+# scale and shift per channel -- followed by the activation, in float64.
+# --------------------------------------------------------------------------
+
+ACTIVATIONS = ("none", "relu", "relu6", "silu")
+
+
+def activation(t: np.ndarray, act: str) -> np.ndarray:
+    """none: t; relu: max(t, 0); relu6: min(max(t, 0), 6);
+    silu: t * sigmoid(t) = t / (1 + exp(-t))."""
+    t = _f64(t)
+    if act == "none":
+        return t
+    if act == "relu":
+        return np.maximum(t, 0.0)
+    if act == "relu6":
+        return np.minimum(np.maximum(t, 0.0), 6.0)
+    if act == "silu":
+        with np.errstate(over="ignore"):
+            return t / (1.0 + np.exp(-t))
+    raise ValueError(f"unknown activation {act!r}")
+
+
+def prologue(x: np.ndarray, scale: np.ndarray, shift: np.ndarray, act: str) -> np.ndarray:
+    """X'[n, h, w, c] = act(X[n, h, w, c] * scale[c] + shift[c])."""
+    return activation(_f64(x) * _f64(scale) + _f64(shift), act)
+
+
+def fwd_fused(x, scale, shift, act, w, stride=1, pad=0) -> np.ndarray:
+    """Forward DWC of the prologue's output; the zero padding surrounds X'
+    (padding positions are zero after the prologue, not act(shift))."""
+    return fwd(prologue(x, scale, shift, act), w, stride, pad)
