@@ -25,13 +25,14 @@ LIB_PATH = os.path.join(_HERE, "libdwc.so")
 
 F32, BF16, F16 = 0, 1, 2
 ALGO = {"auto": 0, "direct": 1, "generic": 2, "mfma": 3}
+ACT = {"none": 0, "relu": 1, "relu6": 2, "silu": 3}
 OP_FWD, OP_BWD_DATA, OP_BWD_FILTER = 0, 1, 2
 
 _DTYPE_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
 
 EXPORTED = (
     "dwc_version", "dwc_status_string", "dwc_last_error", "dwc_output_dims",
-    "dwc_check", "dwc_plan_describe", "dwc_fwd", "dwc_bwd_data",
+    "dwc_check", "dwc_plan_describe", "dwc_fwd", "dwc_fwd_fused", "dwc_bwd_data",
     "dwc_bwd_filter_workspace_size", "dwc_bwd_filter",
 )
 
@@ -78,6 +79,7 @@ def lib() -> ctypes.CDLL:
         l.dwc_check.argtypes = [P, ctypes.c_int]
         l.dwc_plan_describe.argtypes = [P, ctypes.c_int, ctypes.c_char_p, ctypes.c_size_t]
         l.dwc_fwd.argtypes = [P, vp, vp, vp, vp]
+        l.dwc_fwd_fused.argtypes = [P, vp, vp, vp, ctypes.c_int, vp, vp, vp]
         l.dwc_bwd_data.argtypes = [P, vp, vp, vp, vp]
         l.dwc_bwd_filter_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
         l.dwc_bwd_filter.argtypes = [P, vp, vp, vp, vp, ctypes.c_size_t, vp]
@@ -143,6 +145,11 @@ def fwd_ptr(p: Problem, x: int, w: int, y: int, stream: int = 0) -> None:
     _raise(lib().dwc_fwd(ctypes.byref(p), x, w, y, stream))
 
 
+def fwd_fused_ptr(p: Problem, x: int, scale: int, shift: int, act: int, w: int, y: int,
+                  stream: int = 0) -> None:
+    _raise(lib().dwc_fwd_fused(ctypes.byref(p), x, scale, shift, act, w, y, stream))
+
+
 def bwd_data_ptr(p: Problem, dy: int, w: int, dx: int, stream: int = 0) -> None:
     _raise(lib().dwc_bwd_data(ctypes.byref(p), dy, w, dx, stream))
 
@@ -200,6 +207,34 @@ def fwd(x: torch.Tensor, w: torch.Tensor, stride=1, pad=0, out: Optional[torch.T
     if tuple(out.shape) != (n, oh, ow, c):
         raise ValueError(f"out must be {(n, oh, ow, c)}")
     fwd_ptr(p, x.data_ptr(), w.data_ptr(), out.data_ptr(), _stream(stream))
+    return out
+
+
+def fwd_fused(x: torch.Tensor, w: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor,
+              act: str = "relu", stride=1, pad=0, out: Optional[torch.Tensor] = None,
+              algo="auto", stream=None) -> torch.Tensor:
+    """Y = DWC(act(X * scale + shift), W) with the prologue fused into the
+    forward (scale, shift: C fp32 values); Y is fp32."""
+    _check_tensor(x, "x", 4)
+    _check_tensor(w, "w", 3)
+    _check_tensor(scale, "scale", 1, torch.float32)
+    _check_tensor(shift, "shift", 1, torch.float32)
+    dt = _operand_dtype(x, w)
+    n, h, wd, c = x.shape
+    fh, fw, c2 = w.shape
+    if c2 != c or scale.shape[0] != c or shift.shape[0] != c:
+        raise ValueError("x, w, scale and shift disagree on C")
+    if act not in ACT:
+        raise ValueError(f"act must be one of {sorted(ACT)}")
+    p = problem(n, h, wd, c, fh, fw, stride, pad, dt, algo)
+    oh, ow = output_dims(p)
+    if out is None:
+        out = torch.empty((n, oh, ow, c), dtype=torch.float32, device=x.device)
+    _check_tensor(out, "out", 4, torch.float32)
+    if tuple(out.shape) != (n, oh, ow, c):
+        raise ValueError(f"out must be {(n, oh, ow, c)}")
+    fwd_fused_ptr(p, x.data_ptr(), scale.data_ptr(), shift.data_ptr(), ACT[act], w.data_ptr(),
+                  out.data_ptr(), _stream(stream))
     return out
 
 

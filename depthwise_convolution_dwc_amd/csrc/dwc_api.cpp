@@ -111,6 +111,51 @@ int dwc_fwd(const dwc_problem* p, const void* x, const void* w, void* y, void* s
   return e == hipSuccess ? DWC_OK : hip_fail(e, "dwc_fwd launch");
 }
 
+int dwc_fwd_fused(const dwc_problem* p, const void* x, const float* scale, const float* shift,
+                  int act, const void* w, void* y, void* stream) {
+  if (!p) {
+    set_last_error("problem pointer is NULL");
+    return DWC_ERR_BAD_PARAM;
+  }
+  if (act < DWC_ACT_NONE || act > DWC_ACT_SILU) {
+    set_last_error("unknown activation (act must be a dwc_act)");
+    return DWC_ERR_BAD_PARAM;
+  }
+  if (p->algo != DWC_ALGO_AUTO && p->algo != DWC_ALGO_DIRECT) {
+    set_last_error("the fused prologue runs on the direct vector kernels "
+                   "(algo DWC_ALGO_AUTO or DWC_ALGO_DIRECT)");
+    return DWC_ERR_UNSUPPORTED;
+  }
+  dwc_problem d = *p;
+  d.algo = DWC_ALGO_DIRECT;
+  Plan pl;
+  std::string err;
+  int st = make_plan(&d, DWC_OP_FWD, &pl, &err);
+  if (st == DWC_OK && (pl.kind != PLAN_DIRECT || p->fw > kPrologueMaxFw)) st = DWC_ERR_UNSUPPORTED;
+  if (st == DWC_ERR_UNSUPPORTED)
+    err = "the fused prologue needs an odd filter width up to 9 and stride 1 or 2 "
+          "(the direct vector kernels)";
+  if (st == DWC_OK) st = check_pointers(&d, pl, x, w, y, nullptr, 0, &err);
+  if (st == DWC_OK) st = check_prologue(&d, pl, y, scale, shift, &err);
+  if (st != DWC_OK) {
+    set_last_error(err);
+    return st;
+  }
+  if (pl.empty) return DWC_OK;
+  const float inf = __builtin_inff();
+  Prologue pro{scale, shift, -inf, inf, 0};
+  if (act == DWC_ACT_RELU) pro.lo = 0.f;
+  if (act == DWC_ACT_RELU6) {
+    pro.lo = 0.f;
+    pro.hi = 6.f;
+  }
+  if (act == DWC_ACT_SILU) pro.silu = 1;
+  pl.fa.pro = pro;
+  pl.sa.pro = pro;
+  const hipError_t e = launch_fwd_type(pl, x, w, (float*)y, (hipStream_t)stream);
+  return e == hipSuccess ? DWC_OK : hip_fail(e, "dwc_fwd_fused launch");
+}
+
 int dwc_bwd_data(const dwc_problem* p, const void* dy, const void* w, void* dx, void* stream) {
   Plan pl;
   const int st = prepare(p, DWC_OP_BWD_DATA, &pl, dy, w, dx, nullptr, 0);

@@ -41,6 +41,21 @@ constexpr int filter_row_chunk(int fw) {
   return fw <= 9 ? fw : fw == 13 ? 5 : fw <= 27 ? 3 : 2;
 }
 
+// Fused prologue of the forward (the batch normalisation and activation
+// that precede a DWC, applied to X as it is read): X' = act(X * scale[c] +
+// shift[c]), act = clamp to [lo, hi] (identity, relu, relu6), then t *
+// sigmoid(t) when silu is set.  Padding stays zero.  scale == nullptr: no
+// prologue.
+struct Prologue {
+  const float* scale;
+  const float* shift;
+  float lo, hi;
+  int silu;
+};
+// Filters up to this width take the fused prologue (the vector kernels for
+// small filters, where the extra arithmetic fits in idle cycles).
+constexpr int kPrologueMaxFw = 9;
+
 // Forward-type kernels: the forward map and the stride-1 data gradient (the
 // forward map of dY with the filter turned by 180 degrees).
 struct FwdArgs {
@@ -53,6 +68,7 @@ struct FwdArgs {
   int PH, PW;        // zero padding; negative values crop
   int tiles_w, tiles_h, cblocks;
   int num_items;     // waves of work: N * cblocks * tiles_h * tiles_w
+  Prologue pro;      // forward only
 };
 
 // Strided data gradient by output phase.  For stride S, the dX pixels whose
@@ -92,6 +108,7 @@ struct SweepArgs {
   int cbg;           // channel blocks: ceil(C / 64)
   int num_items;     // forward-type: waves; filter gradient: workgroups
   int Z;             // filter gradient: partial slices, tiles_w * ceil(N * cpi / 4)
+  Prologue pro;      // forward only
 };
 
 // Filter gradient: partial sums over slices of the N*OH axis.  One

@@ -60,6 +60,35 @@ __device__ __forceinline__ void load_strip(float (&v)[SPAN], const char* img, in
   for (int j = 0; j < SPAN; ++j) v[j] = ld<DT>(r, o[j], 0);
 }
 
+// t * sigmoid(t) = t / (1 + e^-t), with e^-t = 2^(-t log2 e) from the
+// hardware's base-2 exponential and 1 / (1 + e^-t) from its reciprocal.
+__device__ __forceinline__ float silu_f(float t) {
+  const float e = __builtin_amdgcn_exp2f(-t * 1.44269504088896341f);
+  return t * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// The fused prologue on a strip as it is consumed: t = act(v * s + b) for
+// the pixels inside the image; a row or column outside stays 0 (the zero
+// padding surrounds X', not X).  row, col0 and p are wave-uniform.
+template <int SPAN>
+__device__ __forceinline__ void apply_prologue(float (&v)[SPAN], int row, int rows, int col0,
+                                               int cols, float s, float b, const Prologue& p) {
+  if ((unsigned)row >= (unsigned)rows) return;
+  if (p.silu) {
+#pragma unroll
+    for (int j = 0; j < SPAN; ++j) {
+      const float t = silu_f(fminf(fmaxf(fmaf(v[j], s, b), p.lo), p.hi));
+      v[j] = (unsigned)(col0 + j) < (unsigned)cols ? t : 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < SPAN; ++j) {
+      const float t = fminf(fmaxf(fmaf(v[j], s, b), p.lo), p.hi);
+      v[j] = (unsigned)(col0 + j) < (unsigned)cols ? t : 0.f;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Forward-type direct kernel ("row streaming").
 //
@@ -75,7 +104,7 @@ __device__ __forceinline__ void load_strip(float (&v)[SPAN], const char* img, in
 // and tap is a register.  FLIP reads the filter turned by 180 degrees, which
 // makes this the stride-1 data gradient (§5.1).
 // ---------------------------------------------------------------------------
-template <int DT, int FW, int S, int TMW, bool FLIP>
+template <int DT, int FW, int S, int TMW, bool FLIP, bool PRO = false>
 __global__ __launch_bounds__(kBlockThreads) void fwd_rows(FwdArgs a) {
   constexpr int EB = Elem<DT>::bytes;
   constexpr int TR = kFwdRows;
@@ -98,6 +127,13 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_rows(FwdArgs a) {
   const uint32_t Cb = (uint32_t)a.C * EB;
   const char* img = (const char*)a.in + (size_t)n * a.IH * a.IW * Cb;
   const auto zero = make_rsrc(a.in, 0);
+  float ps = 1.f, pb = 0.f;  // this lane's prologue scale and shift
+  if constexpr (PRO) {
+    if (c < a.C) {
+      ps = a.pro.scale[c];
+      pb = a.pro.shift[c];
+    }
+  }
   const auto wrs = make_rsrc(a.filt, (uint32_t)(a.FH * FW) * Cb);
   const int oh0 = th * TR, ow0 = tw * TMW;
   const int ih_base = oh0 * S - a.PH;
@@ -136,6 +172,7 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_rows(FwdArgs a) {
       if ((unsigned)ih >= (unsigned)a.IH) continue;  // a padding row: contributes 0
       float xv[SPAN];
       load_strip<DT, SPAN>(xv, img, ih, a.IH, iw0, a.IW, Cb, coff);
+      if constexpr (PRO) apply_prologue<SPAN>(xv, ih, a.IH, iw0, a.IW, ps, pb, a.pro);
 #pragma unroll
       for (int r = 0; r < TR; ++r) {
         const int k = m - r * S;
@@ -419,7 +456,7 @@ constexpr int kSweepBufs = 3;
 // constant.  FLIP reads the filter turned by 180 degrees: the stride-1 data
 // gradient.
 // ---------------------------------------------------------------------------
-template <int DT, int F, int TMW, bool FLIP>
+template <int DT, int F, int TMW, bool FLIP, bool PRO = false>
 __global__ __launch_bounds__(kBlockThreads) void fwd_sweep(SweepArgs a) {
   constexpr int EB = Elem<DT>::bytes;
   constexpr int SPAN = TMW + F - 1;
@@ -455,6 +492,13 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_sweep(SweepArgs a) {
 
   uint32_t coff[SPAN];
   column_offsets<SPAN>(coff, iw0, a.IW, Cb, c, a.C, EB);
+  float ps = 1.f, pb = 0.f;  // this lane's prologue scale and shift
+  if constexpr (PRO) {
+    if (c < a.C) {
+      ps = a.pro.scale[c];
+      pb = a.pro.shift[c];
+    }
+  }
   float xb[NB][SPAN];
   load_strip<DT, SPAN>(xb[0], img, i_first, a.IH, iw0, a.IW, Cb, coff);
   load_strip<DT, SPAN>(xb[1], img, i_first + dir, a.IH, iw0, a.IW, Cb, coff);
@@ -491,6 +535,9 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_sweep(SweepArgs a) {
       if (i_rel >= steps) break;
       load_strip<DT, SPAN>(xb[(u + 2) % NB], img, i_first + dir * (i_rel + 2), a.IH, iw0, a.IW, Cb,
                            coff);
+      // the prologue runs on a row when it is used, after its loads arrive
+      if constexpr (PRO)
+        apply_prologue<SPAN>(xb[u % NB], i_first + dir * i_rel, a.IH, iw0, a.IW, ps, pb, a.pro);
       const float(&xv)[SPAN] = xb[u % NB];
       const bool row_in = (unsigned)(i_first + dir * i_rel) < (unsigned)a.IH;
 #pragma unroll

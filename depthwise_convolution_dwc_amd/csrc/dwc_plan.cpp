@@ -588,6 +588,19 @@ int check_pointers(const dwc_problem* p, const Plan& pl, const void* in0, const 
   return DWC_OK;
 }
 
+int check_prologue(const dwc_problem* p, const Plan& pl, const void* out, const float* scale,
+                   const float* shift, std::string* err) {
+  if (pl.empty) return DWC_OK;
+  if (!scale || !shift) return fail(err, DWC_ERR_BAD_PARAM, "scale or shift pointer is NULL");
+  if (((uintptr_t)scale) % 4 || ((uintptr_t)shift) % 4)
+    return fail(err, DWC_ERR_MISALIGNED, "scale or shift not 4-byte aligned");
+  const size_t out_bytes = (size_t)p->n * pl.oh * pl.ow * p->c * 4;
+  const size_t vec_bytes = (size_t)p->c * 4;
+  if (overlap(out, out_bytes, scale, vec_bytes) || overlap(out, out_bytes, shift, vec_bytes))
+    return fail(err, DWC_ERR_ALIAS, "output overlaps scale or shift");
+  return DWC_OK;
+}
+
 std::string describe(const Plan& pl) {
   static const char* ops[] = {"fwd", "bwd_data", "bwd_filter"};
   char buf[512];

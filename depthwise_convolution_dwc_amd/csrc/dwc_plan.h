@@ -60,6 +60,11 @@ int make_plan(const dwc_problem* p, int op, Plan* pl, std::string* err);
 int check_pointers(const dwc_problem* p, const Plan& pl, const void* in0, const void* in1,
                    const void* out, const void* ws, size_t ws_bytes, std::string* err);
 
+// Checks the scale and shift vectors of a fused-prologue forward (null,
+// alignment, overlap with the output).
+int check_prologue(const dwc_problem* p, const Plan& pl, const void* out, const float* scale,
+                   const float* shift, std::string* err);
+
 std::string describe(const Plan& pl);
 
 void set_last_error(const std::string& msg);

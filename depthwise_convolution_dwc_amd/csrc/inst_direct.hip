@@ -15,11 +15,20 @@ namespace {
 
 constexpr int kDt = DWC_INST_DT;
 
+// a.pro.scale set: the fused-prologue variant (forward, FW <= kPrologueMaxFw)
 template <int S, int TMW, bool FLIP>
 hipError_t fwd_by_fw(int fw, const FwdArgs& a, int blocks, hipStream_t s) {
   switch (fw) {
 #define DWC_CASE(F)                                                                     \
   case F:                                                                               \
+    if (a.pro.scale) {                                                                  \
+      if constexpr (!FLIP && F <= kPrologueMaxFw) {                                     \
+        hipLaunchKernelGGL((fwd_rows<kDt, F, S, TMW, FLIP, true>), dim3(blocks),        \
+                           dim3(kBlockThreads), 0, s, a);                               \
+        return hipGetLastError();                                                       \
+      }                                                                                 \
+      return hipErrorInvalidValue;                                                      \
+    }                                                                                   \
     hipLaunchKernelGGL((fwd_rows<kDt, F, S, TMW, FLIP>), dim3(blocks),                  \
                        dim3(kBlockThreads), 0, s, a);                                   \
     return hipGetLastError();
@@ -75,6 +84,14 @@ hipError_t fwd_sweep_by_f(int f, const SweepArgs& a, int blocks, hipStream_t s) 
 #define DWC_CASE(F)                                                                       \
   case F:                                                                                 \
     if constexpr (TMW == 7 || F <= 5) {                                                   \
+      if (a.pro.scale) {                                                                  \
+        if constexpr (!FLIP) {                                                            \
+          hipLaunchKernelGGL((fwd_sweep<kDt, F, TMW, FLIP, true>), dim3(blocks),          \
+                             dim3(kBlockThreads), 0, s, a);                               \
+          return hipGetLastError();                                                       \
+        }                                                                                 \
+        return hipErrorInvalidValue;                                                      \
+      }                                                                                   \
       hipLaunchKernelGGL((fwd_sweep<kDt, F, TMW, FLIP>), dim3(blocks), dim3(kBlockThreads), \
                          0, s, a);                                                        \
       return hipGetLastError();                                                           \

@@ -70,6 +70,13 @@ typedef enum {
 } dwc_algo;
 
 typedef enum {
+    DWC_ACT_NONE = 0,   /* t                                   */
+    DWC_ACT_RELU = 1,   /* max(t, 0)                           */
+    DWC_ACT_RELU6 = 2,  /* min(max(t, 0), 6)                   */
+    DWC_ACT_SILU = 3    /* t * sigmoid(t) = t / (1 + exp(-t))  */
+} dwc_act;
+
+typedef enum {
     DWC_OK = 0,
     DWC_ERR_BAD_PARAM = 1,   /* sizes, strides, pads or dtypes invalid         */
     DWC_ERR_UNSUPPORTED = 2, /* valid request this build does not implement     */
@@ -129,6 +136,25 @@ int dwc_plan_describe(const dwc_problem* p, int op, char* buf, size_t len);
  * or w.  n == 0 is a no-op. */
 int dwc_fwd(const dwc_problem* p, const void* x, const void* w, void* y,
             void* stream);
+
+/* Forward convolution with a fused prologue (Flash-DWC §5.2, "kernel
+ * fusion": the batch normalisation and activation that usually precede a
+ * DWC, applied to X as the forward reads it, so X' never goes to memory):
+ *   X'[n,h,w,c] = act(x[n,h,w,c] * scale[c] + shift[c])    (fp32)
+ *   y = DWC(X', w), with the zero padding around X' (padding stays 0).
+ * Inference-form batch normalisation gives scale = gamma / sqrt(var + eps)
+ * and shift = beta - mean * scale.
+ *   x, w, y : as dwc_fwd
+ *   scale, shift : C fp32 values each, device memory, 4-byte aligned (read;
+ *                  may be NULL when n == 0)
+ *   act : a dwc_act
+ * Runs the register-window vector kernels (the pages fuse on their CUDA-core
+ * kernels, for small filters): odd filter widths up to 9, stride 1 or 2,
+ * any dtype; algo AUTO or DIRECT.  Otherwise DWC_ERR_UNSUPPORTED.  y must
+ * not overlap x, w, scale or shift. */
+int dwc_fwd_fused(const dwc_problem* p, const void* x, const float* scale,
+                  const float* shift, int act, const void* w, void* y,
+                  void* stream);
 
 /* Backward data convolution (BDC, §5.1): dx = adjoint of the forward map
  * applied to dy.

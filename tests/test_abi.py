@@ -254,3 +254,29 @@ def test_output_dims_do_not_depend_on_the_kernel_choice():
     bad = dwc.problem(1, 4, 4, 8, 7, 7, 1, 0)
     with pytest.raises(dwc.DwcError):
         dwc.output_dims(bad)
+
+
+def test_fwd_fused_rejections_before_any_launch():
+    """The fused-prologue forward checks its activation, kernel family and
+    scale/shift vectors synchronously; none of these calls launches."""
+    L = dwc.lib()
+    P = ctypes.byref
+    X, W, Y, SC, SH = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000
+    p = dwc.problem(2, 8, 8, 64, 3, 3, 1, 1)
+    assert L.dwc_fwd_fused(P(p), X, SC, SH, 7, W, Y, None) == 1  # unknown activation
+    assert "activation" in dwc.last_error()
+    for algo in ("mfma", "generic"):
+        q = dwc.problem(2, 8, 8, 64, 3, 3, 1, 1, algo=algo)
+        assert L.dwc_fwd_fused(P(q), X, SC, SH, 1, W, Y, None) == 2
+    for fh, fw, pad in ((11, 11, 5), (4, 4, 1), (3, 3, 1)):
+        q = dwc.problem(2, 16, 16, 64, fh, fw, 3 if fw == 3 else 1, pad)
+        assert L.dwc_fwd_fused(P(q), X, SC, SH, 1, W, Y, None) == 2, (fh, fw)
+        assert "fused prologue" in dwc.last_error()
+    assert L.dwc_fwd_fused(P(p), X, None, SH, 1, W, Y, None) == 1       # NULL scale
+    assert L.dwc_fwd_fused(P(p), X, SC + 2, SH, 1, W, Y, None) == 3     # misaligned
+    assert L.dwc_fwd_fused(P(p), X, Y + 64, SH, 1, W, Y, None) == 5     # scale inside y
+    empty = dwc.problem(0, 8, 8, 64, 3, 3, 1, 1)
+    assert L.dwc_fwd_fused(P(empty), None, None, None, 3, None, None, None) == 0
+    # a 9-wide filter at stride 2 and a tall 31 x 9 filter are accepted
+    for q in (dwc.problem(1, 16, 16, 64, 9, 9, 2, 4), dwc.problem(1, 40, 16, 64, 31, 9, 1, 4)):
+        assert L.dwc_fwd_fused(P(q), X, SC + 2, SH, 0, W, Y, None) == 3  # reaches the checks
