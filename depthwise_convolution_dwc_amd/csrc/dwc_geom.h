@@ -109,6 +109,7 @@ struct SweepArgs {
   int num_items;     // forward-type: waves; filter gradient: workgroups
   int Z;             // filter gradient: partial slices, tiles_w * ceil(N * cpi / 4)
   Prologue pro;      // forward only
+  int hybrid;        // filter gradient of fp16 operands: fp16 sub-unit sums
 };
 
 // Filter gradient: partial sums over slices of the N*OH axis.  One

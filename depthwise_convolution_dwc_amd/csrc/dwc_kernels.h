@@ -714,6 +714,180 @@ __global__ __launch_bounds__(kBlockThreads) void wgrad_sweep(SweepArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Filter-gradient sweep with hybrid accumulation (Flash-DWC §5.1, "hybrid
+// accumulation"; fp16 operands only).  The same walk as wgrad_sweep, but the
+// operands stay fp16 and each step accumulates into fp16 sub-unit sums with
+// packed FMAs (two adjacent taps fw, fw+1 per instruction, exact products
+// and one rounding per FMA).  Every HS input rows -- at most 63 products
+// per tap -- the fp16 sums are added into fp32 accumulators and cleared, so
+// rounding error grows only within a short sub-unit; the cross-wave
+// reduction and the partials are fp32 as in wgrad_sweep.  An fp16 sub-unit
+// sum can overflow (|sum| > 65504) where fp32 would not: the option is for
+// activations and gradients of ordinary magnitude.
+// ---------------------------------------------------------------------------
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+
+template <int SPAN>
+__device__ __forceinline__ void load_strip_h(_Float16 (&v)[SPAN], const char* img, int row,
+                                             int rows, int col0, int cols, uint32_t pix_bytes,
+                                             const uint32_t (&o)[SPAN]) {
+  const bool row_ok = (unsigned)row < (unsigned)rows;
+  const char* base = img + ((ptrdiff_t)row * cols + col0) * (ptrdiff_t)pix_bytes;
+  const auto r = make_rsrc(base, row_ok ? (uint32_t)SPAN * pix_bytes : 0u);
+#pragma unroll
+  for (int j = 0; j < SPAN; ++j)
+    v[j] = __builtin_bit_cast(_Float16, (unsigned short)__builtin_amdgcn_raw_buffer_load_b16(
+                                            r, (int)o[j], 0, 0));
+}
+
+template <int F, int TJ>
+__global__ __launch_bounds__(kBlockThreads) void wgrad_sweep_hyb(SweepArgs a) {
+  constexpr int EB = 2;
+  constexpr int SPAN = TJ + F - 1;
+  constexpr int NB = kSweepBufs;
+  constexpr int L = lcm_c(F, NB);
+  constexpr int HP = (F + 1) / 2;   // tap pairs per filter row
+  constexpr int HS = 63 / TJ;       // input rows per fp16 sub-unit
+  __shared__ float red[2][F * F][64];
+  const int wave = uniform(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
+  if (blk >= a.num_items) return;  // the whole workgroup leaves together
+  int t = blk;
+  const int s = t % a.tiles_w;
+  t /= a.tiles_w;
+  const int cb = t % a.cbg;
+  const int cg = t / a.cbg;
+  const int z = cg * a.tiles_w + s;
+  const int c = cb * kWaveChannels + lane;
+  const uint32_t Cb = (uint32_t)a.C * EB;
+  const int chunk = cg * kWavesPerBlock + wave;
+  int n = 0, rc = 0, o_start = 0, o_cnt = 0;
+  if (chunk < a.N * a.cpi) {
+    n = chunk / a.cpi;
+    rc = chunk - n * a.cpi;
+    o_start = rc * a.R;
+    o_cnt = a.OH - o_start < a.R ? a.OH - o_start : a.R;
+  }
+  o_cnt = uniform(o_cnt);
+  const int ow0 = s * TJ;
+  const int iw0 = ow0 - a.PW;
+  // odd chunks walk up from their last row (see wgrad_sweep)
+  const bool up = (rc & 1) != 0;
+  const int dir = up ? -1 : 1;
+  const int i_first = uniform(up ? o_start + o_cnt - 1 - a.P + F - 1 : o_start - a.P);
+  const int o_first = up ? o_start + o_cnt - 1 : o_start;
+  const char* ximg = (const char*)a.in + (size_t)n * a.IH * a.IW * Cb;
+  const char* dimg = (const char*)a.in2 + (size_t)n * a.OH * a.OW * Cb;
+  uint32_t doff[TJ], xoff[SPAN];
+  column_offsets<TJ>(doff, ow0, a.OW, Cb, c, a.C, EB);
+  column_offsets<SPAN>(xoff, iw0, a.IW, Cb, c, a.C, EB);
+  auto drow = [&](int i) { return i < o_cnt ? o_first + dir * i : -1; };
+
+  _Float16 xb[NB][SPAN], db[NB][TJ];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    load_strip_h<SPAN>(xb[k], ximg, i_first + dir * k, a.IH, iw0, a.IW, Cb, xoff);
+    load_strip_h<TJ>(db[k], dimg, drow(k), a.OH, ow0, a.OW, Cb, doff);
+  }
+  float acc[F][F];
+  h2_t hacc[F][HP];
+  _Float16 dv[F][TJ];  // ring: slot s holds dY row o with o = s (mod F)
+#pragma unroll
+  for (int k = 0; k < F; ++k) {
+#pragma unroll
+    for (int fw = 0; fw < F; ++fw) acc[k][fw] = 0.f;
+#pragma unroll
+    for (int j = 0; j < HP; ++j) hacc[k][j] = h2_t{(_Float16)0.f, (_Float16)0.f};
+#pragma unroll
+    for (int q = 0; q < TJ; ++q) dv[k][q] = (_Float16)0.f;
+  }
+  auto merge = [&]() {  // fp16 sub-unit sums into the fp32 accumulators
+#pragma unroll
+    for (int k = 0; k < F; ++k)
+#pragma unroll
+      for (int j = 0; j < HP; ++j) {
+        acc[k][2 * j] += (float)hacc[k][j].x;
+        if (2 * j + 1 < F) acc[k][2 * j + 1] += (float)hacc[k][j].y;
+        hacc[k][j] = h2_t{(_Float16)0.f, (_Float16)0.f};
+      }
+  };
+
+  const int steps = o_cnt > 0 ? o_cnt + F - 1 : 0;
+  for (int g = 0; g < steps; g += L) {
+#pragma unroll
+    for (int u = 0; u < L; ++u) {
+      const int i_rel = g + u;
+      if (i_rel >= steps) break;
+      load_strip_h<SPAN>(xb[(u + 2) % NB], ximg, i_first + dir * (i_rel + 2), a.IH, iw0, a.IW, Cb,
+                         xoff);
+      load_strip_h<TJ>(db[(u + 2) % NB], dimg, drow(i_rel + 2), a.OH, ow0, a.OW, Cb, doff);
+#pragma unroll
+      for (int q = 0; q < TJ; ++q) dv[u % F][q] = db[u % NB][q];
+      const _Float16(&xv)[SPAN] = xb[u % NB];
+      const bool row_in = (unsigned)(i_first + dir * i_rel) < (unsigned)a.IH;
+#pragma unroll
+      for (int fh = 0; fh < F; ++fh) {
+        const int slot = ((u - fh) % F + F) % F;
+        if (!row_in || (unsigned)(i_rel - fh) >= (unsigned)o_cnt) continue;
+#pragma unroll
+        for (int q = 0; q < TJ; ++q) {
+          const h2_t d2 = h2_t{dv[slot][q], dv[slot][q]};
+#pragma unroll
+          for (int j = 0; j < HP; ++j) {
+            const h2_t x2 = h2_t{xv[q + 2 * j], 2 * j + 1 < F ? xv[q + 2 * j + 1] : (_Float16)0.f};
+            hacc[fh][j] = x2 * d2 + hacc[fh][j];
+          }
+        }
+      }
+      if ((i_rel + 1) % HS == 0) merge();
+    }
+  }
+  merge();
+  if (up) {  // ring offset k held filter row F-1-k
+#pragma unroll
+    for (int k = 0; k < F / 2; ++k)
+#pragma unroll
+      for (int fw = 0; fw < F; ++fw) {
+        const float v = acc[k][fw];
+        acc[k][fw] = acc[F - 1 - k][fw];
+        acc[F - 1 - k][fw] = v;
+      }
+  }
+
+  // (w0 + w2) + (w1 + w3), then one store of the partial (as wgrad_sweep).
+  if (wave >= 2) {
+#pragma unroll
+    for (int k = 0; k < F; ++k)
+#pragma unroll
+      for (int fw = 0; fw < F; ++fw) red[wave - 2][k * F + fw][lane] = acc[k][fw];
+  }
+  __syncthreads();
+  if (wave < 2) {
+#pragma unroll
+    for (int k = 0; k < F; ++k)
+#pragma unroll
+      for (int fw = 0; fw < F; ++fw) acc[k][fw] += red[wave][k * F + fw][lane];
+  }
+  __syncthreads();
+  if (wave == 1) {
+#pragma unroll
+    for (int k = 0; k < F; ++k)
+#pragma unroll
+      for (int fw = 0; fw < F; ++fw) red[0][k * F + fw][lane] = acc[k][fw];
+  }
+  __syncthreads();
+  if (wave == 0 && c < a.C) {
+    float* ws = a.out + (size_t)z * F * F * a.C + c;
+#pragma unroll
+    for (int k = 0; k < F; ++k)
+#pragma unroll
+      for (int fw = 0; fw < F; ++fw)
+        ws[((size_t)k * F + fw) * a.C] = acc[k][fw] + red[0][k * F + fw][lane];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Generic kernels: one output element per lane, any filter size and stride.
 // Element index i runs channel-fastest, so a wave reads 64 consecutive
 // channels of one pixel.

@@ -271,7 +271,7 @@ static int validate(const dwc_problem* p, int64_t* oh_out, int64_t* ow_out, std:
     return fail(err, DWC_ERR_BAD_PARAM, "in_dtype must be DWC_F32, DWC_BF16 or DWC_F16");
   if (p->out_dtype != DWC_F32)
     return fail(err, DWC_ERR_UNSUPPORTED, "outputs are fp32 only (out_dtype must be DWC_F32)");
-  if (p->algo < DWC_ALGO_AUTO || p->algo > DWC_ALGO_MFMA)
+  if (p->algo < DWC_ALGO_AUTO || p->algo > DWC_ALGO_HYBRID)
     return fail(err, DWC_ERR_BAD_PARAM, "unknown algo");
   if (p->wgrad_split < 0) return fail(err, DWC_ERR_BAD_PARAM, "wgrad_split must be >= 0");
   const int64_t a = p->h + 2 * (int64_t)p->pad_h - p->fh;
@@ -332,6 +332,11 @@ int make_plan(const dwc_problem* p, int op, Plan* pl, std::string* err) {
   q.kind = direct ? PLAN_DIRECT : PLAN_GENERIC;
   // Sweep kernels: stride 1, square filter up to 9x9.
   const bool sweep_ok = p->stride_h == 1 && p->fh == p->fw && sweep_f(p->fw);
+  const bool hybrid = p->algo == DWC_ALGO_HYBRID;
+  if (hybrid && (op != DWC_OP_BWD_FILTER || dt != DT_F16 || !sweep_ok))
+    return fail(err, DWC_ERR_UNSUPPORTED,
+                "hybrid accumulation is for the filter gradient of fp16 operands at stride 1 "
+                "with a square 3x3, 5x5, 7x7 or 9x9 filter");
 
   if (op == DWC_OP_FWD || op == DWC_OP_BWD_DATA) {
     // The data gradient runs the forward map on dY with the filter turned
@@ -476,6 +481,7 @@ int make_plan(const dwc_problem* p, int op, Plan* pl, std::string* err) {
         sw.F = p->fw;
         sw.P = p->pad_h;
         sw.PW = p->pad_w;
+        sw.hybrid = hybrid ? 1 : 0;
         q.tj = p->fw >= 7 ? 7 : strip_override("DWC_WGRAD_STRIP", pick_strip(ow));
         q.tfh = p->fh;
         sw.tiles_w = (int)((ow + q.tj - 1) / q.tj);
@@ -637,10 +643,10 @@ std::string describe(const Plan& pl) {
     const SweepArgs& w = pl.sa;
     snprintf(buf, sizeof buf,
              "%s sweep dt=%s f=%d strip=%d tiles_w=%d rows=%d cpi=%d cblocks=%d "
-             "items=%d blocks=%d z=%d ws_bytes=%zu",
+             "items=%d blocks=%d z=%d ws_bytes=%zu%s",
              ops[pl.op], dt_name(pl.dt), w.F, pl.op == DWC_OP_BWD_FILTER ? pl.tj : pl.tmw,
              w.tiles_w, w.R, w.cpi, w.cbg, w.num_items, pl.blocks,
-             pl.op == DWC_OP_BWD_FILTER ? pl.z : 0, pl.ws_bytes);
+             pl.op == DWC_OP_BWD_FILTER ? pl.z : 0, pl.ws_bytes, w.hybrid ? " hybrid=1" : "");
   } else if (pl.kind == PLAN_DIRECT && pl.op != DWC_OP_BWD_FILTER) {
     snprintf(buf, sizeof buf,
              "%s %s dt=%s fw=%d sw=%d flip=%d tmw=%d rows=%d tiles_w=%d tiles_h=%d "

@@ -103,12 +103,21 @@ hipError_t fwd_sweep_by_f(int f, const SweepArgs& a, int blocks, hipStream_t s) 
   return hipErrorInvalidValue;
 }
 
+// a.hybrid: fp16 sub-unit accumulation (fp16 operands only)
 template <int TJ>
 hipError_t wgrad_sweep_by_f(int f, const SweepArgs& a, int blocks, hipStream_t s) {
   switch (f) {
 #define DWC_CASE(F)                                                                       \
   case F:                                                                                 \
     if constexpr (TJ == 7 || F <= 5) {                                                    \
+      if (a.hybrid) {                                                                     \
+        if constexpr (kDt == DT_F16) {                                                    \
+          hipLaunchKernelGGL((wgrad_sweep_hyb<F, TJ>), dim3(blocks), dim3(kBlockThreads), \
+                             0, s, a);                                                    \
+          return hipGetLastError();                                                       \
+        }                                                                                 \
+        return hipErrorInvalidValue;                                                      \
+      }                                                                                   \
       hipLaunchKernelGGL((wgrad_sweep<kDt, F, TJ>), dim3(blocks), dim3(kBlockThreads), 0, \
                          s, a);                                                           \
       return hipGetLastError();                                                           \

@@ -280,3 +280,23 @@ def test_fwd_fused_rejections_before_any_launch():
     # a 9-wide filter at stride 2 and a tall 31 x 9 filter are accepted
     for q in (dwc.problem(1, 16, 16, 64, 9, 9, 2, 4), dwc.problem(1, 40, 16, 64, 31, 9, 1, 4)):
         assert L.dwc_fwd_fused(P(q), X, SC + 2, SH, 0, W, Y, None) == 3  # reaches the checks
+
+
+def test_hybrid_accumulation_plans():
+    """DWC_ALGO_HYBRID: the filter gradient of fp16 operands on the sweep
+    kernels only; everything else is DWC_ERR_UNSUPPORTED before a launch."""
+    ok = dwc.problem(64, 56, 56, 128, 7, 7, 1, 3, dtype=dwc.F16, algo="hybrid")
+    assert dwc.check(ok, 2) == 0
+    d = dwc.plan_describe(ok, 2)
+    assert d.startswith("bwd_filter sweep") and d.endswith("hybrid=1")
+    assert dwc.workspace_size(ok) > 0
+    assert "hybrid" not in dwc.plan_describe(dwc.problem(64, 56, 56, 128, 7, 7, 1, 3,
+                                                         dtype=dwc.F16), 2)
+    for kw, op in ((dict(dtype=dwc.F32), 2), (dict(dtype=dwc.BF16), 2), (dict(), 0), (dict(), 1),
+                   (dict(fh=5, fw=3), 2), (dict(stride=2), 2), (dict(fh=11, fw=11, pad=5), 2)):
+        a = dict(fh=7, fw=7, stride=1, pad=3, dtype=dwc.F16)
+        a.update(kw)
+        q = dwc.problem(8, 20, 20, 64, a["fh"], a["fw"], a["stride"], a["pad"], dtype=a["dtype"],
+                        algo="hybrid")
+        assert dwc.check(q, op) == 2, (kw, op)
+        assert "hybrid accumulation" in dwc.last_error()
