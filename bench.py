@@ -435,8 +435,9 @@ PROFILE_CMDS = {
     "copyw": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof/copyw -o run "
              "-- python3 $R/bench.py --copy-calibration",
 }
-OP_KERNELS = {"fwd_s1": ["fwd_sweep<0, 7, 7, false>"], "fwd_s2": ["fwd_rows<0, 7, 2"],
-              "bwd_data": ["fwd_sweep<0, 7, 7, true>"],
+# kernel-name prefixes: fwd_sweep<DT, F, TMW, FLIP, PROLOGUE>
+OP_KERNELS = {"fwd_s1": ["fwd_sweep<0, 7, 7, false"], "fwd_s2": ["fwd_rows<0, 7, 2"],
+              "bwd_data": ["fwd_sweep<0, 7, 7, true"],
               "bwd_filter": ["wgrad_sweep<0, 7, 7>", "reduce_partials"]}
 
 
@@ -495,7 +496,7 @@ Durations from the dispatch timestamps of `run_kernel_trace.csv`:
 
 {chr(10).join(lines)}
 
-`fwd_sweep<.., true>` is the data gradient (the forward sweep on dY with the
+`fwd_sweep<0, 7, 7, true, ..>` is the data gradient (the forward sweep on dY with the
 filter turned by 180 degrees); `fwd_rows<0, 7, 2, ...>` is the stride-2
 forward; the filter gradient is `wgrad_sweep` followed by `reduce_partials`.
 
