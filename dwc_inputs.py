@@ -26,7 +26,8 @@ from typing import Dict, Optional, Tuple
 
 import numpy as np
 
-DTYPES = ("f32", "bf16", "f16")
+DTYPES = ("f32", "bf16", "f16", "e4m3", "e5m2")
+FP8_DTYPES = ("e4m3", "e5m2")
 
 
 @dataclasses.dataclass(frozen=True)
@@ -68,10 +69,10 @@ class Shape:
 class Operand:
     """A tensor in two forms: exact float32 values and the stored bits.
 
-    ``values`` holds the operand as float32 (bf16/fp16 values are exactly
+    ``values`` holds the operand as float32 (bf16/fp16/fp8 values are exactly
     representable in float32, so converting them to float64 for the oracle is
-    exact).  ``stored`` is what goes to the device: float32, float16, or the
-    raw bf16 bit patterns as uint16.
+    exact).  ``stored`` is what goes to the device: float32, float16, the
+    raw bf16 bit patterns as uint16, or the fp8 codes as uint8.
     """
 
     values: np.ndarray
@@ -100,6 +101,14 @@ def to_operand(x32: np.ndarray, dtype: str) -> Operand:
     if dtype == "f16":
         h = x32.astype(np.float16)  # numpy rounds to nearest even
         return Operand(values=h.astype(np.float32), stored=h, dtype=dtype)
+    if dtype in FP8_DTYPES:
+        # OCP fp8 (e4m3 without infinities, e5m2), rounded to nearest even by
+        # torch's conversion; stored as the raw codes (uint8)
+        import torch
+        tdt = torch.float8_e4m3fn if dtype == "e4m3" else torch.float8_e5m2
+        q = torch.from_numpy(x32).to(tdt)
+        return Operand(values=q.to(torch.float32).numpy(),
+                       stored=q.view(torch.uint8).numpy().copy(), dtype=dtype)
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
@@ -192,4 +201,10 @@ WORKLOADS: Dict[str, dict] = {
         shapes=[_same(128, 28, 512, 13), _same(128, 28, 512, 31)],
         x_dist=("normal", 1.0), w_dist=None,
         ops=("fwd", "bwd_data", "bwd_filter"), dtypes=("bf16", "f16")),
+    # Low-bit operands on the same shapes: OCP fp8 (e4m3, e5m2) operands,
+    # fp32 accumulate/output.
+    "lowbit_n128_28x28_c512": dict(
+        shapes=[_same(128, 28, 512, 13), _same(128, 28, 512, 31)],
+        x_dist=("normal", 1.0), w_dist=None,
+        ops=("fwd", "bwd_data", "bwd_filter"), dtypes=("e4m3", "e5m2")),
 }

@@ -265,3 +265,41 @@ def fwd_fused(x, scale, shift, act, w, stride=1, pad=0) -> np.ndarray:
     """Forward DWC of the prologue's output; the zero padding surrounds X'
     (padding positions are zero after the prologue, not act(shift))."""
     return fwd(prologue(x, scale, shift, act), w, stride, pad)
+
+
+# --------------------------------------------------------------------------
+# Low-bit operands (Flash-DWC, TACO, §7 "scalability", low-bit data types:
+# operands stored and multiplied in 8 bits, sums kept in higher precision).
+# The pages name FP8 without fixing an encoding; read here as the two OCP
+# 8-bit floating-point formats that CDNA4 matrix cores take:
+#   e4m3: sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent field 0
+#         is subnormal (m / 8 * 2^-6); S.1111.111 is NaN; no infinities, so
+#         exponent field 15 with mantissa 0..6 are ordinary numbers (max 448);
+#   e5m2: sign, 5 exponent bits (bias 15), 2 mantissa bits, IEEE-754 style:
+#         exponent field 0 is subnormal (m / 4 * 2^-14), 31 is +-inf (m = 0)
+#         or NaN (m != 0); max 57344.
+# Dequantisation is exact in float64, so the convolution of fp8 operands is
+# the float64 oracle applied to the decoded values.
+# --------------------------------------------------------------------------
+
+FP8_FORMATS = ("e4m3", "e5m2")
+_FP8_LAYOUT = {"e4m3": (4, 3, 7), "e5m2": (5, 2, 15)}  # exponent bits, mantissa bits, bias
+
+
+def fp8_decode(codes: np.ndarray, fmt: str) -> np.ndarray:
+    """float64 values of fp8 codes (uint8) in format fmt (``FP8_FORMATS``)."""
+    if fmt not in _FP8_LAYOUT:
+        raise ValueError(f"unknown fp8 format {fmt!r}")
+    eb, mb, bias = _FP8_LAYOUT[fmt]
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> mb) & ((1 << eb) - 1)
+    m = (c & ((1 << mb) - 1)).astype(np.float64)
+    frac = m / float(1 << mb)
+    mag = np.where(e == 0, np.ldexp(frac, 1 - bias), np.ldexp(1.0 + frac, e - bias))
+    top = (1 << eb) - 1
+    if fmt == "e4m3":
+        mag = np.where((e == top) & ((c & 7) == 7), np.nan, mag)
+    else:
+        mag = np.where(e == top, np.where(m == 0, np.inf, np.nan), mag)
+    return sign * mag
