@@ -23,12 +23,13 @@ import torch  # loaded first: libdwc then binds to the HIP runtime torch uses
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdwc.so")
 
-F32, BF16, F16 = 0, 1, 2
+F32, BF16, F16, FP8_E4M3, FP8_E5M2 = 0, 1, 2, 3, 4
 ALGO = {"auto": 0, "direct": 1, "generic": 2, "mfma": 3, "hybrid": 4}
 ACT = {"none": 0, "relu": 1, "relu6": 2, "silu": 3}
 OP_FWD, OP_BWD_DATA, OP_BWD_FILTER = 0, 1, 2
 
-_DTYPE_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+_DTYPE_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16,
+               torch.float8_e4m3fn: FP8_E4M3, torch.float8_e5m2: FP8_E5M2}
 
 EXPORTED = (
     "dwc_version", "dwc_status_string", "dwc_last_error", "dwc_output_dims",
@@ -185,7 +186,8 @@ def _check_tensor(t: torch.Tensor, name: str, ndim: int, dtype=None):
 def _operand_dtype(*ts: torch.Tensor) -> int:
     dts = {t.dtype for t in ts}
     if len(dts) != 1 or next(iter(dts)) not in _DTYPE_CODE:
-        raise TypeError(f"operands must share one of float32/bfloat16/float16, got {dts}")
+        raise TypeError("operands must share one of float32/bfloat16/float16/"
+                        f"float8_e4m3fn/float8_e5m2, got {dts}")
     return _DTYPE_CODE[ts[0].dtype]
 
 

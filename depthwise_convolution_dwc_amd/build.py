@@ -38,7 +38,7 @@ def _units():
     # the sweep kernels' row loops (lcm(F, 3) rows, 21 at 7x7) must unroll
     # completely, also with the fused prologue, so that every register-ring
     # index is a constant; LLVM's default size limit for that stops short
-    for dt in (0, 1, 2):
+    for dt in (0, 1, 2, 3, 4):
         u.append(("hip", "inst_direct.hip", f"inst_direct_dt{dt}.o",
                   [f"-DDWC_INST_DT={dt}", "-mllvm", "-pragma-unroll-threshold=30000"]))
     u.append(("hip", "inst_generic.hip", "inst_generic.o", []))

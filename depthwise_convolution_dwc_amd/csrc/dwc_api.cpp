@@ -25,9 +25,10 @@ hipError_t launch_fwd_type(const Plan& pl, const void* in, const void* filt, flo
     g.filt = filt;
     g.dx = out;
     switch (pl.dt) {
-      case DT_F32: return launch_dgrad_phase_dt0(pl.km, g, pl.blocks, s);
-      case DT_BF16: return launch_dgrad_phase_dt1(pl.km, g, pl.blocks, s);
-      case DT_F16: return launch_dgrad_phase_dt2(pl.km, g, pl.blocks, s);
+#define DWC_CASE(D) \
+  case D: return launch_dgrad_phase_dt##D(pl.km, g, pl.blocks, s);
+      DWC_DT_LIST(DWC_CASE)
+#undef DWC_CASE
     }
     return hipErrorInvalidValue;
   }
@@ -49,16 +50,18 @@ hipError_t launch_fwd_type(const Plan& pl, const void* in, const void* filt, flo
       w.in2 = filt;
       w.out = out;
       switch (pl.dt) {
-        case DT_F32: return launch_fwd_sweep_dt0(w.F, pl.tmw, pl.flip, w, pl.blocks, s);
-        case DT_BF16: return launch_fwd_sweep_dt1(w.F, pl.tmw, pl.flip, w, pl.blocks, s);
-        case DT_F16: return launch_fwd_sweep_dt2(w.F, pl.tmw, pl.flip, w, pl.blocks, s);
+#define DWC_CASE(D) \
+  case D: return launch_fwd_sweep_dt##D(w.F, pl.tmw, pl.flip, w, pl.blocks, s);
+        DWC_DT_LIST(DWC_CASE)
+#undef DWC_CASE
       }
       return hipErrorInvalidValue;
     }
     switch (pl.dt) {
-      case DT_F32: return launch_fwd_direct_dt0(a.FW, a.SW, pl.tmw, pl.flip, a, pl.blocks, s);
-      case DT_BF16: return launch_fwd_direct_dt1(a.FW, a.SW, pl.tmw, pl.flip, a, pl.blocks, s);
-      case DT_F16: return launch_fwd_direct_dt2(a.FW, a.SW, pl.tmw, pl.flip, a, pl.blocks, s);
+#define DWC_CASE(D) \
+  case D: return launch_fwd_direct_dt##D(a.FW, a.SW, pl.tmw, pl.flip, a, pl.blocks, s);
+      DWC_DT_LIST(DWC_CASE)
+#undef DWC_CASE
     }
     return hipErrorInvalidValue;
   }
@@ -200,15 +203,19 @@ int dwc_bwd_filter(const dwc_problem* p, const void* x, const void* dy, void* dw
       w.in2 = dy;
       w.out = part;
       switch (pl.dt) {
-        case DT_F32: e = launch_wgrad_sweep_dt0(w.F, pl.tj, w, pl.blocks, s); break;
-        case DT_BF16: e = launch_wgrad_sweep_dt1(w.F, pl.tj, w, pl.blocks, s); break;
-        default: e = launch_wgrad_sweep_dt2(w.F, pl.tj, w, pl.blocks, s); break;
+#define DWC_CASE(D) \
+  case D: e = launch_wgrad_sweep_dt##D(w.F, pl.tj, w, pl.blocks, s); break;
+        DWC_DT_LIST(DWC_CASE)
+#undef DWC_CASE
+        default: e = hipErrorInvalidValue; break;
       }
     } else {
       switch (pl.dt) {
-        case DT_F32: e = launch_wgrad_direct_dt0(a.FW, a.SW, pl.tj, a, pl.blocks, s); break;
-        case DT_BF16: e = launch_wgrad_direct_dt1(a.FW, a.SW, pl.tj, a, pl.blocks, s); break;
-        default: e = launch_wgrad_direct_dt2(a.FW, a.SW, pl.tj, a, pl.blocks, s); break;
+#define DWC_CASE(D) \
+  case D: e = launch_wgrad_direct_dt##D(a.FW, a.SW, pl.tj, a, pl.blocks, s); break;
+        DWC_DT_LIST(DWC_CASE)
+#undef DWC_CASE
+        default: e = hipErrorInvalidValue; break;
       }
     }
   } else {

@@ -8,11 +8,21 @@
 
 namespace dwc {
 
-// Operand storage types.  bf16 is kept as its raw 16 bits.
+// Operand storage types.  bf16 is kept as its raw 16 bits, fp8 as its code.
 template <int DT> struct Elem;
 template <> struct Elem<DT_F32> { static constexpr int bytes = 4; };
 template <> struct Elem<DT_BF16> { static constexpr int bytes = 2; };
 template <> struct Elem<DT_F16> { static constexpr int bytes = 2; };
+template <> struct Elem<DT_E4M3> { static constexpr int bytes = 1; };
+template <> struct Elem<DT_E5M2> { static constexpr int bytes = 1; };
+
+// An fp8 code (the low byte of c) as float: the hardware conversion, which
+// reads the OCP e4m3 / e5m2 encodings on gfx950.  Exact.
+template <int DT>
+__device__ __forceinline__ float fp8_to_f32(uint32_t c) {
+  if constexpr (DT == DT_E4M3) return __builtin_amdgcn_cvt_f32_fp8((int)c, 0);
+  else return __builtin_amdgcn_cvt_f32_bf8((int)c, 0);
+}
 
 // Buffer resource over [base, base + bytes).  A raw buffer load whose
 // per-lane offset is >= bytes returns 0, which is how every kernel reads the

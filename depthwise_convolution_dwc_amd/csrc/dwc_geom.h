@@ -6,7 +6,7 @@
 
 namespace dwc {
 
-enum { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
+enum { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2, DT_E4M3 = 3, DT_E5M2 = 4 };
 
 // Channels per wave: one channel per lane, 64 lanes.  In the channel-last
 // layout a wave's load of one pixel is 64 consecutive channels, i.e. one

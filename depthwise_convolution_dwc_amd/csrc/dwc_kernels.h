@@ -26,9 +26,11 @@ __device__ __forceinline__ float ld(__amdgpu_buffer_rsrc_t r, uint32_t voff, uin
   } else if constexpr (DT == DT_BF16) {
     uint32_t b = __builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
     return __uint_as_float(b << 16);
-  } else {
+  } else if constexpr (DT == DT_F16) {
     unsigned short h = __builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
     return (float)__builtin_bit_cast(_Float16, h);
+  } else {
+    return fp8_to_f32<DT>(__builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 0));
   }
 }
 
@@ -898,8 +900,10 @@ __device__ __forceinline__ float load_at(const void* p, int64_t i) {
     return ((const float*)p)[i];
   } else if constexpr (DT == DT_BF16) {
     return __uint_as_float((uint32_t)((const unsigned short*)p)[i] << 16);
-  } else {
+  } else if constexpr (DT == DT_F16) {
     return (float)((const _Float16*)p)[i];
+  } else {
+    return fp8_to_f32<DT>(((const unsigned char*)p)[i]);
   }
 }
 

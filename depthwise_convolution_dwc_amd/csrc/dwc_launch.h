@@ -7,38 +7,29 @@
 
 namespace dwc {
 
-// Forward-type direct kernel for operand dtype dt (one object per dtype).
-hipError_t launch_fwd_direct_dt0(int fw, int s, int tmw, bool flip, const FwdArgs& a,
-                                 int blocks, hipStream_t st);
-hipError_t launch_fwd_direct_dt1(int fw, int s, int tmw, bool flip, const FwdArgs& a,
-                                 int blocks, hipStream_t st);
-hipError_t launch_fwd_direct_dt2(int fw, int s, int tmw, bool flip, const FwdArgs& a,
-                                 int blocks, hipStream_t st);
+// Operand dtypes with their own instantiation of the direct kernels (one
+// object per dtype, DWC_INST_DT): fp32, bf16, fp16, fp8 e4m3, fp8 e5m2.
+#define DWC_DT_LIST(X) X(0) X(1) X(2) X(3) X(4)
 
-// Filter-gradient direct kernel for operand dtype dt.
-// Strided data gradient by output phase; km: padded sub-filter size (one of
-// DWC_PHASE_KM_LIST).
-hipError_t launch_dgrad_phase_dt0(int km, const DgradPhaseArgs& a, int blocks, hipStream_t s);
-hipError_t launch_dgrad_phase_dt1(int km, const DgradPhaseArgs& a, int blocks, hipStream_t s);
-hipError_t launch_dgrad_phase_dt2(int km, const DgradPhaseArgs& a, int blocks, hipStream_t s);
-
-hipError_t launch_wgrad_direct_dt0(int fw, int s, int tj, const WgradArgs& a, int blocks,
-                                   hipStream_t st);
-hipError_t launch_wgrad_direct_dt1(int fw, int s, int tj, const WgradArgs& a, int blocks,
-                                   hipStream_t st);
-hipError_t launch_wgrad_direct_dt2(int fw, int s, int tj, const WgradArgs& a, int blocks,
-                                   hipStream_t st);
-
-// Sweep kernels (stride 1, square filters up to 9x9).
-#define DWC_DECL_SWEEP(D)                                                                 \
-  hipError_t launch_fwd_sweep_dt##D(int f, int tmw, bool flip, const SweepArgs& a,         \
-                                    int blocks, hipStream_t st);                         \
-  hipError_t launch_wgrad_sweep_dt##D(int f, int tj, const SweepArgs& a, int blocks,       \
+// Per operand dtype D:
+//  * forward-type direct kernel (s: stride; flip: the stride-1 data gradient);
+//  * strided data gradient by output phase (km: padded sub-filter size, one
+//    of DWC_PHASE_KM_LIST);
+//  * filter-gradient direct kernel;
+//  * sweep kernels (stride 1, square filters up to 9x9).
+#define DWC_DECL_DT(D)                                                                    \
+  hipError_t launch_fwd_direct_dt##D(int fw, int s, int tmw, bool flip, const FwdArgs& a, \
+                                     int blocks, hipStream_t st);                         \
+  hipError_t launch_dgrad_phase_dt##D(int km, const DgradPhaseArgs& a, int blocks,        \
+                                      hipStream_t s);                                     \
+  hipError_t launch_wgrad_direct_dt##D(int fw, int s, int tj, const WgradArgs& a,         \
+                                       int blocks, hipStream_t st);                       \
+  hipError_t launch_fwd_sweep_dt##D(int f, int tmw, bool flip, const SweepArgs& a,        \
+                                    int blocks, hipStream_t st);                          \
+  hipError_t launch_wgrad_sweep_dt##D(int f, int tj, const SweepArgs& a, int blocks,      \
                                       hipStream_t st);
-DWC_DECL_SWEEP(0)
-DWC_DECL_SWEEP(1)
-DWC_DECL_SWEEP(2)
-#undef DWC_DECL_SWEEP
+DWC_DT_LIST(DWC_DECL_DT)
+#undef DWC_DECL_DT
 
 // Packed-MFMA forward-type kernel (bf16 / fp16 operands, stride 1): nf
 // 16-tap fragments per filter row, tiles of 16 combinations per channel.

@@ -20,7 +20,7 @@ constexpr int64_t kI32Max = 0x7fffffff;
 // about four waves per SIMD.
 constexpr int64_t kWgradTargetWaves = 4096;
 
-int elem_bytes(int dt) { return dt == DT_F32 ? 4 : 2; }
+int elem_bytes(int dt) { return dt == DT_F32 ? 4 : dt == DT_BF16 || dt == DT_F16 ? 2 : 1; }
 
 bool sweep_f(int f) {
 #define DWC_IS(F) if (f == F) return true;
@@ -36,7 +36,10 @@ bool direct_fw(int fw) {
   return false;
 }
 
-const char* dt_name(int dt) { return dt == DT_F32 ? "f32" : dt == DT_BF16 ? "bf16" : "f16"; }
+const char* dt_name(int dt) {
+  static const char* const names[] = {"f32", "bf16", "f16", "e4m3", "e5m2"};
+  return names[dt];
+}
 
 int fail(std::string* err, int code, const std::string& msg) {
   if (err) *err = msg;
@@ -112,7 +115,8 @@ int pick_split(int64_t rows, int64_t per_slice_blocks, int64_t strips, int64_t m
 // fragment, 8 (one per wave) with two.
 bool plan_mfma(const FwdArgs& f, int dt, bool flip, Plan* q) {
   constexpr int kZRowElems = 32;  // one 16-tap fragment and its 16 leading zeros
-  if (dt == DT_F32 || f.SH != 1 || f.SW != 1 || f.FW > 32 || f.C % 8 != 0) return false;
+  if ((dt != DT_BF16 && dt != DT_F16) || f.SH != 1 || f.SW != 1 || f.FW > 32 || f.C % 8 != 0)
+    return false;
   const int groups = (f.OW + 15) / 16;
   const int gt = groups <= 1 ? 1 : groups <= 2 ? 2 : groups <= 4 ? 4 : 0;
   if (gt == 0) return false;
@@ -181,8 +185,8 @@ bool plan_mfma(const FwdArgs& f, int dt, bool flip, Plan* q) {
 // zero-padded dY rows and (afterwards) the slice partial fit the LDS.
 bool plan_wgrad_mfma(const dwc_problem* p, int64_t oh, int64_t ow, Plan* q) {
   const int dt = p->in_dtype;
-  if (dt == DT_F32 || p->stride_h != 1 || p->stride_w != 1 || p->fw > 32 || p->fh > 32 ||
-      p->w > 64 || p->c % kWgmCb != 0)
+  if ((dt != DT_BF16 && dt != DT_F16) || p->stride_h != 1 || p->stride_w != 1 || p->fw > 32 ||
+      p->fh > 32 || p->w > 64 || p->c % kWgmCb != 0)
     return false;
   WgradMfmaArgs w{};
   w.N = (int)p->n; w.IH = (int)p->h; w.IW = (int)p->w; w.C = (int)p->c;
@@ -267,8 +271,9 @@ static int validate(const dwc_problem* p, int64_t* oh_out, int64_t* ow_out, std:
   if (p->stride_h < 1 || p->stride_w < 1)
     return fail(err, DWC_ERR_BAD_PARAM, "need stride_h, stride_w >= 1");
   if (p->pad_h < 0 || p->pad_w < 0) return fail(err, DWC_ERR_BAD_PARAM, "need pad_h, pad_w >= 0");
-  if (p->in_dtype < DWC_F32 || p->in_dtype > DWC_F16)
-    return fail(err, DWC_ERR_BAD_PARAM, "in_dtype must be DWC_F32, DWC_BF16 or DWC_F16");
+  if (p->in_dtype < DWC_F32 || p->in_dtype > DWC_FP8_E5M2)
+    return fail(err, DWC_ERR_BAD_PARAM,
+                "in_dtype must be DWC_F32, DWC_BF16, DWC_F16, DWC_FP8_E4M3 or DWC_FP8_E5M2");
   if (p->out_dtype != DWC_F32)
     return fail(err, DWC_ERR_UNSUPPORTED, "outputs are fp32 only (out_dtype must be DWC_F32)");
   if (p->algo < DWC_ALGO_AUTO || p->algo > DWC_ALGO_HYBRID)

@@ -83,6 +83,8 @@ hipError_t launch_generic(int kind, int dt, const GenericArgs& a, hipStream_t s)
     case DT_F32: return generic_dt<DT_F32>(kind, a, s);
     case DT_BF16: return generic_dt<DT_BF16>(kind, a, s);
     case DT_F16: return generic_dt<DT_F16>(kind, a, s);
+    case DT_E4M3: return generic_dt<DT_E4M3>(kind, a, s);
+    case DT_E5M2: return generic_dt<DT_E5M2>(kind, a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -21,9 +21,17 @@
  *   Y, dY : N  x OH x OW x C
  *   W, dW : FH x FW x C
  *
- * Precision: operands X, W, dY are fp32, bf16 or fp16 (in_dtype); every sum
- * is accumulated in fp32 and every output (Y, dX, dW) is fp32.  §4.1 argues
- * that fp32 accumulation is required for half-precision operands.
+ * Precision: operands X, W, dY are fp32, bf16, fp16 or fp8 (in_dtype, one
+ * dtype for all operands of a call); every sum is accumulated in fp32 and
+ * every output (Y, dX, dW) is fp32.  §4.1 argues that fp32 accumulation is
+ * required for half-precision operands; §7 (low-bit data types) keeps the
+ * same split for 8-bit operands: stored and multiplied in 8 bits, summed in
+ * higher precision.  fp8 operands are the raw codes (one byte each) with no
+ * scale factor; a per-tensor scale of a quantised tensor multiplies the
+ * fp32 output.  Products of fp8 values are exact in fp32; the fp8 matrix
+ * cores sum each group of products with an error of up to about 2^-12 of
+ * the sum of their magnitudes (measured on MI355X), wider than fp32
+ * rounding, while the vector kernels round every fp32 addition.
  *
  * Ownership and threading: every pointer is a device pointer owned by the
  * caller, who allocates all tensors and the workspace.  The library keeps no
@@ -53,7 +61,11 @@ extern "C" {
 typedef enum {
     DWC_F32 = 0,
     DWC_BF16 = 1,
-    DWC_F16 = 2
+    DWC_F16 = 2,
+    DWC_FP8_E4M3 = 3, /* OCP fp8: 4 exponent bits (bias 7), 3 mantissa bits,
+                         no infinities, S.1111.111 = NaN, max 448           */
+    DWC_FP8_E5M2 = 4  /* OCP fp8: 5 exponent bits (bias 15), 2 mantissa
+                         bits, IEEE-style infinities and NaNs, max 57344    */
 } dwc_dtype;
 
 typedef enum {

@@ -10,8 +10,15 @@ import depthwise_convolution_dwc_amd as dwc
 from dwc_inputs import Operand
 
 # Tolerances on max relative L2 error per tensor: fp32 operands 1e-5;
-# bf16/fp16 operands with fp32 accumulation 3e-3.
-TOL = {"f32": 1e-5, "bf16": 3e-3, "f16": 3e-3}
+# bf16/fp16 operands with fp32 accumulation 3e-3; fp8 operands (exact
+# products, fp32 outputs) the same reduced-precision budget, 3e-3 -- their
+# elementwise bound (fp8 matrix-core sums) is checked separately.
+TOL = {"f32": 1e-5, "bf16": 3e-3, "f16": 3e-3, "e4m3": 3e-3, "e5m2": 3e-3}
+# Elementwise bound for fp8 operands: |got - want| <= FP8_EL_TOL * the same
+# operation on |operands|.  The fp8 MFMAs sum each group of products with an
+# error up to about 2^-12 of the sum of their magnitudes (measured on
+# MI355X); the vector kernels round in fp32 (2^-24 per addition).
+FP8_EL_TOL = 2.0 ** -11
 
 
 def to_device(op: Operand, device="cuda") -> torch.Tensor:
@@ -19,6 +26,9 @@ def to_device(op: Operand, device="cuda") -> torch.Tensor:
         return torch.from_numpy(op.stored).to(device)
     if op.dtype == "f16":
         return torch.from_numpy(op.stored).to(device)
+    if op.dtype in ("e4m3", "e5m2"):
+        tdt = torch.float8_e4m3fn if op.dtype == "e4m3" else torch.float8_e5m2
+        return torch.from_numpy(op.stored).to(device).view(tdt)
     # bf16 bits travel as int16 and are reinterpreted on the device
     return torch.from_numpy(op.stored.view(np.int16)).to(device).view(torch.bfloat16)
 
@@ -56,4 +66,4 @@ def log(*a):
     print(*a, flush=True)
 
 
-__all__ = ["TOL", "to_device", "rel_l2", "sample_index", "gather", "sync", "log", "dwc"]
+__all__ = ["TOL", "FP8_EL_TOL", "to_device", "rel_l2", "sample_index", "gather", "sync", "log", "dwc"]

@@ -58,7 +58,7 @@ def test_output_dims(n, h, f, s, p, want):
 
 BAD = [
     (dict(n=-1), 1), (dict(h=0), 1), (dict(c=0), 1), (dict(fh=0), 1),
-    (dict(stride=0), 1), (dict(pad=-1), 1), (dict(dtype=7), 1),
+    (dict(stride=0), 1), (dict(pad=-1), 1), (dict(dtype=7), 1), (dict(dtype=5), 1),
     (dict(h=3, fh=7, pad=1), 1),  # filter larger than padded input
     (dict(algo=9), 1), (dict(wgrad_split=-2), 1),
 ]
@@ -300,3 +300,24 @@ def test_hybrid_accumulation_plans():
                         algo="hybrid")
         assert dwc.check(q, op) == 2, (kw, op)
         assert "hybrid accumulation" in dwc.last_error()
+
+
+def test_fp8_operand_plans():
+    """fp8 operands (one byte per element): the vector, sweep, phase and
+    generic kernels take them for every shape; the planner reports the
+    dtype; workspace sizes count one-byte operands like any other."""
+    for dt, name in ((dwc.FP8_E4M3, "e4m3"), (dwc.FP8_E5M2, "e5m2")):
+        for shape, op, kind in (((64, 56, 56, 128, 7, 7, 1, 3), 0, "sweep"),
+                                ((64, 56, 56, 128, 7, 7, 2, 3), 0, "direct"),
+                                ((64, 56, 56, 128, 7, 7, 2, 3), 1, "phase"),
+                                ((64, 56, 56, 128, 7, 7, 1, 3), 2, "sweep"),
+                                ((2, 9, 9, 8, 4, 6, 3, 1), 0, "generic")):
+            p = dwc.problem(*shape, dtype=dt)
+            assert dwc.check(p, op) == 0, (name, shape, op)
+            d = dwc.plan_describe(p, op)
+            assert name in d and kind in d, d
+        for algo in ("direct", "generic"):
+            p = dwc.problem(2, 9, 9, 16, 3, 3, 1, 1, dtype=dt, algo=algo)
+            assert all(dwc.check(p, op) == 0 for op in (0, 1, 2))
+        hy = dwc.problem(64, 56, 56, 128, 7, 7, 1, 3, dtype=dt, algo="hybrid")
+        assert dwc.check(hy, 2) == 2

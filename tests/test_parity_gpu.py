@@ -68,7 +68,16 @@ def _run(op, s: Shape, inp, algo, wgrad_split=0):
 
 
 OPS = {"fwd": 0, "bwd_data": 1, "bwd_filter": 2}
-DT = {"f32": dwc.F32, "bf16": dwc.BF16, "f16": dwc.F16}
+DT = {"f32": dwc.F32, "bf16": dwc.BF16, "f16": dwc.F16, "e4m3": dwc.FP8_E4M3,
+      "e5m2": dwc.FP8_E5M2}
+
+
+def _vals(op):
+    """Operand values for the oracle: fp8 codes through the oracle's own
+    decoder, other dtypes as generated (exact in float32)."""
+    if op.dtype in oracle.FP8_FORMATS:
+        return oracle.fp8_decode(op.stored, op.dtype)
+    return op.values
 
 
 def _algos(op, s: Shape, dtype):
@@ -85,13 +94,13 @@ def _algos(op, s: Shape, dtype):
 def _want(op, s: Shape, inp):
     stride, pad = (s.stride_h, s.stride_w), (s.pad_h, s.pad_w)
     if op == "fwd":
-        return oracle.fwd(inp.x.values, inp.w.values, stride, pad)
+        return oracle.fwd(_vals(inp.x), _vals(inp.w), stride, pad)
     if op == "bwd_data":
-        return oracle.bwd_data(inp.dy.values, inp.w.values, (s.h, s.w), stride, pad)
-    return oracle.bwd_filter(inp.x.values, inp.dy.values, (s.fh, s.fw), stride, pad)
+        return oracle.bwd_data(_vals(inp.dy), _vals(inp.w), (s.h, s.w), stride, pad)
+    return oracle.bwd_filter(_vals(inp.x), _vals(inp.dy), (s.fh, s.fw), stride, pad)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16", "e4m3", "e5m2"])
 @pytest.mark.parametrize("op", ["fwd", "bwd_data", "bwd_filter"])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda t: "x".join(map(str, t[:6])) + f"_s{t[6]}_p{t[7]}")
 def test_small_parity(shape, op, dtype):
