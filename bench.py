@@ -41,6 +41,8 @@ METRIC = "DWC fwd/dgrad/wgrad GFLOP/s + % of roofline (HBM×η_D vs FP32/MFMA pe
 PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
 PEAK_FP32_VECTOR = 157.3e12
 PEAK_BF16_MFMA = 2.5e15
+PEAK_FP8_MFMA = 5.0e15     # dense fp8 MFMA
+DTYPE_CODE = {"f32": 0, "bf16": 1, "f16": 2, "e4m3": 3, "e5m2": 4}
 ROTATE_BYTES = 1 << 30     # buffer sets rotate over >= 1 GiB: no Infinity-Cache reuse
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["depthwise_convolution_dwc_amd/csrc/dwc_kernels.h",
@@ -66,7 +68,7 @@ def log(*a):
 # ----------------------------------------------------------------- model ----
 
 def elem_bytes(dtype: str) -> int:
-    return 4 if dtype == "f32" else 2
+    return {"f32": 4, "bf16": 2, "f16": 2, "e4m3": 1, "e5m2": 1}[dtype]
 
 
 def valid_taps(size_in, size_out, f, s, p):
@@ -102,7 +104,8 @@ def op_model(s: Shape, op: str, dtype: str) -> dict:
     eta = f_nom / operands
     bytes_operands = eb * operands
     bytes_alg = bytes_operands + 4 * out
-    peak = PEAK_FP32_VECTOR if dtype == "f32" else PEAK_BF16_MFMA
+    peak = {"f32": PEAK_FP32_VECTOR, "bf16": PEAK_BF16_MFMA, "f16": PEAK_BF16_MFMA,
+            "e4m3": PEAK_FP8_MFMA, "e5m2": PEAK_FP8_MFMA}[dtype]
     r_lit = min(PEAK_HBM * eta / eb, peak)
     return dict(flops=f_nom, flops_valid=f_valid, eta_d=eta, bytes_operands=bytes_operands,
                 bytes=bytes_alg, peak=peak, roofline=r_lit,
@@ -146,6 +149,9 @@ def roofline_entry(m: dict, seconds: float, traffic=None) -> dict:
 def upload(op, torch, dev):
     if op.dtype == "bf16":
         return torch.from_numpy(op.stored.view(np.int16)).to(dev).view(torch.bfloat16)
+    if op.dtype in ("e4m3", "e5m2"):
+        tdt = torch.float8_e4m3fn if op.dtype == "e4m3" else torch.float8_e5m2
+        return torch.from_numpy(op.stored).to(dev).view(tdt)
     return torch.from_numpy(op.stored).to(dev)
 
 
@@ -596,7 +602,7 @@ def sweep(dwc, torch, dev, args):
                     ms = time_step(torch, sets, steps, min(args.warmup, 10))
                     m = op_model(s, op, dt)
                     p = dwc.problem(s.n, s.h, s.w, s.c, s.fh, s.fw, (s.stride_h, s.stride_w),
-                                    (s.pad_h, s.pad_w), {"f32": 0, "bf16": 1, "f16": 2}[dt], algo)
+                                    (s.pad_h, s.pad_w), DTYPE_CODE[dt], algo)
                     rec = {"workload": name, "shape": [s.n, s.h, s.w, s.c, s.fh, s.fw,
                                                        s.stride_h, s.pad_h],
                            "dtype": dt, "op": op, "algo": algo, "ms": round(ms, 5),

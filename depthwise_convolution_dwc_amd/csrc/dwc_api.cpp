@@ -37,6 +37,8 @@ hipError_t launch_fwd_type(const Plan& pl, const void* in, const void* filt, flo
     m.in = in;
     m.filt = filt;
     m.out = out;
+    if (pl.dt == DT_E4M3 || pl.dt == DT_E5M2)
+      return launch_fwd_mfma8(pl.dt, pl.nf, pl.tiles, pl.flip, m, s);
     return launch_fwd_mfma(pl.dt, pl.nf, pl.tiles, pl.flip, m, s);
   }
   if (pl.kind == PLAN_DIRECT) {

@@ -140,6 +140,12 @@ constexpr int kMfmaMaxLds = 81920;
 constexpr int kCus = 256;
 constexpr int kLdsPerCu = 163840;
 constexpr int kMfmaWaves = 8;
+// Packed fp8 forward-type kernel: channels per workgroup (one 16-byte load
+// holds 16 fp8 channels of a pixel), bytes per zero-padded filter fragment
+// row (16 zeros, 16 taps) and zero rows after the last one.
+constexpr int kMfma8Cb = 16;
+constexpr int kZ8Row = 32;
+constexpr int kZ8Tail = 2;
 
 struct MfmaArgs {
   const void* in;    // N x IH x IW x C (X, or dY for the data gradient)

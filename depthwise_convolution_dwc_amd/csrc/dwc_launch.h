@@ -36,6 +36,13 @@ DWC_DT_LIST(DWC_DECL_DT)
 hipError_t launch_fwd_mfma(int dt, int nf, int tiles, bool flip, const MfmaArgs& a,
                            hipStream_t s);
 
+// Packed fp8 MFMA forward-type kernel (e4m3 / e5m2 operands, stride 1,
+// 16x16x128 MFMAs over four filter rows each): nf 16-tap fragments per
+// filter row, tiles of 16 combinations per channel, 16 channels per
+// workgroup.
+hipError_t launch_fwd_mfma8(int dt, int nf, int tiles, bool flip, const MfmaArgs& a,
+                            hipStream_t s);
+
 // Packed-MFMA filter gradient: nfm / nfn 16-tap fragments of the filter
 // width / height, nk 32-column chunks of the input width, pf staging items
 // per thread.  Writes channel-blocked slice partials (reduce with

@@ -178,6 +178,76 @@ bool plan_mfma(const FwdArgs& f, int dt, bool flip, Plan* q) {
   return true;
 }
 
+// Packed fp8 MFMA plan of a forward-type problem (e4m3 / e5m2 operands):
+// false if the kernel does not apply.  The tiling of plan_mfma, in bytes:
+// kMfma8Cb channels per workgroup, each 16x16x128 MFMA covering four filter
+// rows (the fragment rows are padded to a multiple of four), the staged
+// input row pitch an odd number of 16-byte units where LDS allows.
+bool plan_mfma8(const FwdArgs& f, int dt, bool flip, Plan* q) {
+  if ((dt != DT_E4M3 && dt != DT_E5M2) || f.SH != 1 || f.SW != 1 || f.FW > 32 ||
+      f.C % kMfma8Cb != 0)
+    return false;
+  const int groups = (f.OW + 15) / 16;
+  const int gt = groups <= 1 ? 1 : groups <= 2 ? 2 : groups <= 4 ? 4 : 0;
+  if (gt == 0) return false;
+  const int rt = 16 / gt;
+  const int nf = (f.FW + 15) / 16;
+  const int cb = kMfma8Cb;
+  const int fhp = 4 * ((f.FH + 3) / 4);
+  const int need = (f.OH + rt - 1) / rt;
+  MfmaArgs m{};
+  m.N = f.N; m.IH = f.IH; m.IW = f.IW; m.C = f.C; m.OH = f.OH; m.OW = f.OW;
+  m.FH = f.FH; m.FW = f.FW; m.PH = f.PH; m.PW = f.PW;
+  m.gt = gt;
+  m.wt = 16 * (gt + nf);
+  int tiles = need <= 1 ? 1 : need <= 2 ? 2 : 4;
+  if (const char* v = getenv("DWC_MFMA_TILES")) {
+    const int t = atoi(v);
+    if (t == 1 || t == 2 || t == 4) tiles = std::min(tiles, t);
+  }
+  const int64_t z_bytes = ((int64_t)cb * fhp * nf + kZ8Tail) * kZ8Row;
+  int64_t lds = 0;
+  for (;; tiles /= 2) {
+    m.rblk = tiles * rt;
+    m.xr = std::min(f.IH, m.rblk + f.FH - 1) + 1;
+    const int64_t out_bytes = (int64_t)m.rblk * f.OW * (cb + 4) * 4;
+    bool fit = false;
+    for (int pad : {(m.wt / 16) % 2 == 0 ? 16 : 0, 0}) {
+      m.wp = m.wt + pad;
+      lds = std::max((int64_t)cb * m.xr * m.wp + z_bytes, out_bytes);
+      if (lds <= kMfmaMaxLds) {
+        fit = true;
+        break;
+      }
+    }
+    if (fit) break;
+    if (tiles == 1) return false;
+  }
+  m.lds_bytes = (int)lds;
+  m.e_items = m.wt / 4;  // column quads of one staged row
+  m.e2 = 1;
+  m.e2_log = 0;
+  while (m.e2 < m.e_items) {
+    m.e2 *= 2;
+    ++m.e2_log;
+  }
+  if (m.e2 > 64 * kMfmaWaves) return false;
+  m.rch = (f.OH + m.rblk - 1) / m.rblk;
+  m.cblk = f.C / cb;
+  const int64_t blocks = (int64_t)f.N * m.cblk * m.rch;
+  if (blocks > kI32Max) return false;
+  m.num_blocks = (int)blocks;
+  q->kind = PLAN_MFMA;
+  q->flip = flip;
+  q->nf = nf;
+  q->cb = cb;
+  q->tiles = tiles;
+  q->blocks = (int)blocks;
+  q->ma = m;
+  q->fa = f;
+  return true;
+}
+
 // Packed-MFMA filter-gradient plan: false if the kernel does not apply.
 // kWgmCb channels per workgroup (one per wave); the batch is cut into Z
 // slices of whole images so that Z * cblk workgroups (about 1024, or the
@@ -363,14 +433,14 @@ int make_plan(const dwc_problem* p, int op, Plan* pl, std::string* err) {
     // Packed MFMA for half-precision operands (the stride-1 data gradient
     // too: stride 1 is part of the kernel's conditions).
     if (p->algo == DWC_ALGO_AUTO || p->algo == DWC_ALGO_MFMA) {
-      if (plan_mfma(f, dt, bwd, &q)) {
+      if (plan_mfma(f, dt, bwd, &q) || plan_mfma8(f, dt, bwd, &q)) {
         *pl = q;
         return DWC_OK;
       }
       if (p->algo == DWC_ALGO_MFMA)
         return fail(err, DWC_ERR_UNSUPPORTED,
-                    "no packed-MFMA kernel for this problem (needs bf16/fp16, stride 1, "
-                    "FW <= 32, C % 8 == 0, output width <= 64)");
+                    "no packed-MFMA kernel for this problem (needs bf16/fp16 with C % 8 == 0 "
+                    "or fp8 with C % 16 == 0, stride 1, FW <= 32, output width <= 64)");
     }
     if (direct && bwd && p->stride_h > 1) {
       const int S = p->stride_h;

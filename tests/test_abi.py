@@ -307,10 +307,10 @@ def test_fp8_operand_plans():
     generic kernels take them for every shape; the planner reports the
     dtype; workspace sizes count one-byte operands like any other."""
     for dt, name in ((dwc.FP8_E4M3, "e4m3"), (dwc.FP8_E5M2, "e5m2")):
-        for shape, op, kind in (((64, 56, 56, 128, 7, 7, 1, 3), 0, "sweep"),
+        for shape, op, kind in (((16, 80, 80, 128, 7, 7, 1, 3), 0, "sweep"),
                                 ((64, 56, 56, 128, 7, 7, 2, 3), 0, "direct"),
                                 ((64, 56, 56, 128, 7, 7, 2, 3), 1, "phase"),
-                                ((64, 56, 56, 128, 7, 7, 1, 3), 2, "sweep"),
+                                ((16, 80, 80, 128, 7, 7, 1, 3), 2, "sweep"),
                                 ((2, 9, 9, 8, 4, 6, 3, 1), 0, "generic")):
             p = dwc.problem(*shape, dtype=dt)
             assert dwc.check(p, op) == 0, (name, shape, op)
@@ -321,3 +321,26 @@ def test_fp8_operand_plans():
             assert all(dwc.check(p, op) == 0 for op in (0, 1, 2))
         hy = dwc.problem(64, 56, 56, 128, 7, 7, 1, 3, dtype=dt, algo="hybrid")
         assert dwc.check(hy, 2) == 2
+
+
+def test_fp8_mfma_plans_and_rejections():
+    """The packed fp8 kernel (16x16x128 MFMAs over four filter rows): 16
+    channels per workgroup, C a multiple of 16, stride 1, FW <= 32, output
+    width <= 64; LDS within the per-workgroup limit."""
+    for dt, name in ((dwc.FP8_E4M3, "e4m3"), (dwc.FP8_E5M2, "e5m2")):
+        for f in (3, 7, 13, 17, 31):
+            p = dwc.problem(128, 28, 28, 512, f, f, 1, f // 2, dtype=dt)
+            for op in (0, 1):
+                d = dwc.plan_describe(p, op)
+                assert d.startswith(("fwd mfma", "bwd_data mfma")), d
+                g = dict(kv.split("=") for kv in d.split()[2:])
+                assert g["dt"] == name and g["cb"] == "16" and g["flip"] == str(op)
+                assert int(g["lds"]) <= 81920
+                assert int(g["wp"]) % 16 == 0 and int(g["wt"]) == 16 * (int(g["gt"]) + int(g["nf"]))
+        for kw in (dict(c=24), dict(stride=2), dict(fw=33, fh=3, pad=(1, 16), w=40), dict(w=80, h=20)):
+            a = dict(n=2, h=20, w=20, c=32, fh=5, fw=5, stride=1, pad=2)
+            a.update(kw)
+            q = dwc.problem(a["n"], a["h"], a["w"], a["c"], a["fh"], a["fw"], a["stride"],
+                            a["pad"], dtype=dt, algo="mfma")
+            assert dwc.check(q, 0) == 2, kw
+            assert "no packed-MFMA kernel" in dwc.last_error()
