@@ -188,7 +188,9 @@ int dwc_bwd_filter(const dwc_problem* p, const void* x, const void* dy, void* dw
     w.x = x;
     w.dy = dy;
     w.ws = (float*)workspace;
-    e = launch_wgrad_mfma(pl.dt, pl.nfm, pl.nfn, pl.nk, pl.pf, w, s);
+    e = (pl.dt == DT_E4M3 || pl.dt == DT_E5M2)
+            ? launch_wgrad_mfma8(pl.dt, pl.nfm, pl.nfn, pl.nk, pl.pf, w, s)
+            : launch_wgrad_mfma(pl.dt, pl.nfm, pl.nfn, pl.nk, pl.pf, w, s);
     if (e != hipSuccess) return hip_fail(e, "dwc_bwd_filter launch");
     e = launch_reduce(
         ReduceArgs{(const float*)workspace, (float*)dw, m, pl.z, kWgmCb, w.C, w.FH * w.FW}, s);

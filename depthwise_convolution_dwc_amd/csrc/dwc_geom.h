@@ -193,6 +193,9 @@ constexpr int kWgmMaxPf = 2;
 constexpr int wgm_waves_per_eu(int nfm, int nfn, int nk, int pf) {
   return pf == 1 ? ((nk == 1 || nfm * nfn == 1) ? 6 : 4) : (nfm * nfn * nk == 8 ? 2 : 4);
 }
+// The same for the fp8 kernel: two 8-wave workgroups per CU (128 VGPRs)
+// with one staging item per thread, else one.
+constexpr int wgm8_waves_per_eu(int pf) { return pf == 1 ? 4 : 2; }
 struct WgradMfmaArgs {
   const void* x;     // N x IH x IW x C
   const void* dy;    // N x OH x OW x C

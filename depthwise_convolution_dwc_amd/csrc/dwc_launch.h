@@ -49,6 +49,9 @@ hipError_t launch_fwd_mfma8(int dt, int nf, int tiles, bool flip, const MfmaArgs
 // cb = kWgmCb).
 hipError_t launch_wgrad_mfma(int dt, int nfm, int nfn, int nk, int pf, const WgradMfmaArgs& a,
                              hipStream_t s);
+// The same for fp8 operands (16x16x128 MFMAs over four output rows each).
+hipError_t launch_wgrad_mfma8(int dt, int nfm, int nfn, int nk, int pf, const WgradMfmaArgs& a,
+                              hipStream_t s);
 
 enum GenericKind { GEN_FWD = 0, GEN_FWD_FLIP = 1, GEN_DGRAD = 2, GEN_WGRAD = 3 };
 hipError_t launch_generic(int kind, int dt, const GenericArgs& a, hipStream_t st);

@@ -318,3 +318,233 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma8(MfmaArgs a) {
 }
 
 }  // namespace dwc
+
+namespace dwc {
+
+// ---------------------------------------------------------------------------
+// Packed fp8 MFMA filter gradient (e4m3 / e5m2 operands, stride 1).
+//
+// The 16x16x32 product of the 16-bit filter-gradient kernel (A: the band of
+// one zero-padded dY row, 16 taps fw x 32 columns; B: 16 consecutive input
+// rows fh over the same 32 columns), four output rows side by side along
+// the fp8 MFMA's K = 128:
+//   A[m][32 s + k] = dY[oh + s][32 kc + k - (16 fm + m) + pw]
+//   B[32 s + k][n] = X[oh + s + 16 fn + n - ph][32 kc + k]
+//   D[m][n] += contributions to dW[16 fn + n][16 fm + m] of output rows
+//              oh .. oh + 3 (rows past OH are zero rows of the staged dY)
+// K slice s (lanes 16 s .. 16 s + 15) holds output row oh + s.  A is read
+// like the forward kernel's filter band: nine dwords from the dword at or
+// below the lane's first byte, shifted by v_alignbit.  B moves down four
+// rows per step: a DPP row shift by four lanes, the last four lanes of each
+// row group reading LDS again.  A workgroup owns kWgmCb channels (one per
+// wave) and a slice of ipb images, stages each image's X and dY rows in LDS
+// channel-major (one dword = four columns of one channel), and writes the
+// same channel-blocked partial as the 16-bit kernel.
+// ---------------------------------------------------------------------------
+template <int DT, int NFM, int NFN, int NK, int PF>
+__global__ __launch_bounds__(64 * kMfmaWaves, wgm8_waves_per_eu(PF)) void wgrad_mfma8(
+    WgradMfmaArgs a) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  constexpr int NT = 64 * kMfmaWaves;
+  constexpr int CB = kWgmCb;
+  static_assert(CB == kMfmaWaves, "one channel per wave");
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const int tid = threadIdx.x;
+  const int wave = uniform(tid >> 6);
+  const int lane = tid & 63;
+  const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
+  if (blk >= a.num_blocks) return;  // the whole workgroup leaves together
+  const int cbk = blk % a.cblk;
+  const int z = blk / a.cblk;
+  const int n0 = z * a.ipb;
+  const int n1 = n0 + a.ipb < a.N ? n0 + a.ipb : a.N;
+  const int c0 = cbk * CB;
+  const int XR = a.xr, XP = a.xp, DYP = a.dyp, OH = a.OH;
+  const int OHP = 4 * ((OH + 3) / 4);  // staged dY rows: whole groups of four
+  const int taps = a.FH * a.FW;
+  unsigned char* xs = lds;              // [CB][XR][XP]
+  unsigned char* dz = xs + CB * XR * XP;  // [CB][OHP][DYP]
+  float* pst = (float*)lds;             // [taps][CB], after the last image
+  const uint32_t Cb = (uint32_t)a.C;    // bytes per pixel
+
+  // ---- zero both staging regions once: per image only the pixels of the
+  // image are written, so the zero row, the columns past the image, the dY
+  // padding and the dY rows past OH stay zero for every image of the slice
+  {
+    const int units = CB * (XR * XP + OHP * DYP) / 16;
+    for (int i = tid; i < units; i += NT) ((mf8_u32x4*)lds)[i] = mf8_u32x4{0u, 0u, 0u, 0u};
+  }
+
+  // ---- this thread's staging items, the same for every image: item i of
+  // X is the column quad (4e .. 4e+3) of row r; item i of dY is the staged
+  // column quad e, i.e. dY columns 4e - dpad .. 4e + 3 - dpad.  Byte
+  // offsets of the four pixels within the image (kOOB: zero) and the LDS
+  // dword of channel 0 (-1: no item).
+  uint32_t xo[PF][4], dof[PF][4];
+  int xw[PF], dw[PF];
+#pragma unroll
+  for (int k = 0; k < PF; ++k) {
+    const int i = tid + k * NT;
+    xw[k] = dw[k] = -1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xo[k][j] = dof[k][j] = kOOB;
+    if (i < a.ix) {
+      const int r = i / a.hx, e = i - r * a.hx;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (4 * e + j < a.IW) xo[k][j] = (uint32_t)(r * a.IW + 4 * e + j) * Cb + (uint32_t)c0;
+      xw[k] = ((r + 1) * XP) / 4 + e;
+    }
+    if (i < a.id) {
+      const int r = i / a.hd, e = a.e_lo + (i - r * a.hd);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t0 = 4 * e + j - a.dpad;
+        if ((unsigned)t0 < (unsigned)a.OW) dof[k][j] = (uint32_t)(r * a.OW + t0) * Cb + (uint32_t)c0;
+      }
+      dw[k] = (r * DYP) / 4 + e;
+    }
+  }
+  u32x2 vx[PF][4], vd[PF][4];
+  auto fetch = [&](int n) {  // global -> registers, in flight during compute
+    const auto rx = make_rsrc((const char*)a.x + (size_t)n * a.IH * a.IW * Cb,
+                              (uint32_t)(a.IH * a.IW) * Cb);
+    const auto rd = make_rsrc((const char*)a.dy + (size_t)n * OH * a.OW * Cb,
+                              (uint32_t)(OH * a.OW) * Cb);
+#pragma unroll
+    for (int k = 0; k < PF; ++k)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        vx[k][j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rx, (int)xo[k][j], 0, 0));
+        vd[k][j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rd, (int)dof[k][j], 0, 0));
+      }
+  };
+  auto commit = [&]() {  // registers -> LDS, transposed to channel-major
+    const int px = XR * XP / 4, pd = OHP * DYP / 4;  // dwords per channel plane
+#pragma unroll
+    for (int k = 0; k < PF; ++k) {
+      if (xw[k] >= 0) {
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          uint32_t ch[4];
+          transpose4(vx[k][0][w], vx[k][1][w], vx[k][2][w], vx[k][3][w], ch);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ((uint32_t*)xs)[xw[k] + (4 * w + i) * px] = ch[i];
+        }
+      }
+      if (dw[k] >= 0) {
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          uint32_t ch[4];
+          transpose4(vd[k][0][w], vd[k][1][w], vd[k][2][w], vd[k][3][w], ch);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ((uint32_t*)dz)[dw[k] + (4 * w + i) * pd] = ch[i];
+        }
+      }
+    }
+  };
+
+  // ---- per-lane constants.  Lane (s, m): K slice s (output row oh + s);
+  // A row m, B column m; D: lane (s, j) holds D[4s .. 4s+3][j].
+  const int s = lane >> 4, m = lane & 15;
+  const int cc = wave;
+  // A starts at staged dY byte 32 kc - 16 fm - m + pw + dpad of row oh + s
+  const int ua = a.PW + a.dpad - m;
+  const uint32_t ashift = (uint32_t)(ua & 3) * 8u;
+  const uint32_t* dzl = (const uint32_t*)(dz + cc * OHP * DYP + s * DYP) + (ua >> 2);
+  auto read_a = [&](int oh, int fm, int kc) -> mf8_i32x8 {
+    const uint32_t* p = dzl + (oh * DYP + 32 * kc - 16 * fm) / 4;
+    uint32_t d[9];
+#pragma unroll
+    for (int i = 0; i < 9; ++i) d[i] = p[i];
+    mf8_i32x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = (int)__builtin_amdgcn_alignbit(d[i + 1], d[i], ashift);
+    return r;
+  };
+  const unsigned char* xl = xs + cc * XR * XP;
+  // LDS row of input row r: row 0 is zeros, image row r sits at r + 1
+  auto x_row = [&](int r) -> int { return (unsigned)r < (unsigned)a.IH ? r + 1 : 0; };
+  auto read_b = [&](int row, int kc) -> mf8_i32x8 {
+    const mf8_u32x4* p = (const mf8_u32x4*)(xl + row * XP + 32 * kc);
+    const mf8_u32x4 lo = p[0], hi = p[1];
+    return mf8_i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
+
+  mf8_f32x4 acc[NFM][NFN];
+#pragma unroll
+  for (int fm = 0; fm < NFM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < NFN; ++fn) acc[fm][fn] = mf8_f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (n0 < n1) fetch(n0);
+  for (int n = n0; n < n1; ++n) {
+    __syncthreads();  // the zero fill, or the previous image's reads, are done
+    commit();
+    __syncthreads();
+    if (n + 1 < n1) fetch(n + 1);
+
+    mf8_i32x8 A[NFM][NK], B[NFN][NK];
+#pragma unroll
+    for (int fn = 0; fn < NFN; ++fn) {
+      const int row = x_row(s + 16 * fn + m - a.PH);
+#pragma unroll
+      for (int kc = 0; kc < NK; ++kc) B[fn][kc] = read_b(row, kc);
+    }
+#pragma unroll
+    for (int fm = 0; fm < NFM; ++fm)
+#pragma unroll
+      for (int kc = 0; kc < NK; ++kc) A[fm][kc] = read_a(0, fm, kc);
+    // One uniform body per group of four output rows: the operands of the
+    // next group are formed in the last iteration too (from staged rows,
+    // never used).
+    for (int oh = 0; oh < OH; oh += 4) {
+#pragma unroll
+      for (int kc = 0; kc < NK; ++kc)
+#pragma unroll
+        for (int fm = 0; fm < NFM; ++fm)
+#pragma unroll
+          for (int fn = 0; fn < NFN; ++fn)
+            acc[fm][fn] = mfma_f8<DT>(A[fm][kc], B[fn][kc], acc[fm][fn]);
+      const int on = oh + 4 < OHP ? oh + 4 : oh;
+#pragma unroll
+      for (int fm = 0; fm < NFM; ++fm)
+#pragma unroll
+        for (int kc = 0; kc < NK; ++kc) A[fm][kc] = read_a(on, fm, kc);
+#pragma unroll
+      for (int fn = 0; fn < NFN; ++fn)
+#pragma unroll
+        for (int kc = 0; kc < NK; ++kc)
+#pragma unroll
+          for (int v = 0; v < 8; ++v) B[fn][kc][v] = row_shift_down4(B[fn][kc][v]);
+      if (m >= 12) {
+#pragma unroll
+        for (int fn = 0; fn < NFN; ++fn) {
+          const int row = x_row(oh + 4 + s + 16 * fn + m - a.PH);
+#pragma unroll
+          for (int kc = 0; kc < NK; ++kc) B[fn][kc] = read_b(row, kc);
+        }
+      }
+    }
+  }
+
+  // ---- the slice's partial: registers -> LDS [tap][channel] -> one
+  // contiguous run of taps * CB floats
+  __syncthreads();
+#pragma unroll
+  for (int fm = 0; fm < NFM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < NFN; ++fn)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int fw = 16 * fm + 4 * s + r, fh = 16 * fn + m;
+        if (fw < a.FW && fh < a.FH) pst[(fh * a.FW + fw) * CB + cc] = acc[fm][fn][r];
+      }
+  __syncthreads();
+  float* dst = a.ws + ((size_t)z * a.cblk + cbk) * taps * CB;
+  for (int i = tid; i < taps * CB / 4; i += NT)
+    *(mf8_f32x4*)(dst + 4 * i) = *(const mf8_f32x4*)(pst + 4 * i);
+}
+
+}  // namespace dwc

@@ -327,6 +327,84 @@ bool plan_wgrad_mfma(const dwc_problem* p, int64_t oh, int64_t ow, Plan* q) {
   return true;
 }
 
+
+// Packed fp8 MFMA filter-gradient plan (e4m3 / e5m2 operands): false if
+// the kernel does not apply.  The slicing of plan_wgrad_mfma; staging in
+// bytes, four columns of one channel per LDS dword: X rows at a pitch of an
+// odd number of 16-byte units, dY rows zero-padded so that every lane's
+// 36-byte band read stays in its row, and zero rows up to a multiple of
+// four output rows (one MFMA sums four).
+bool plan_wgrad_mfma8(const dwc_problem* p, int64_t oh, int64_t ow, Plan* q) {
+  const int dt = p->in_dtype;
+  if ((dt != DT_E4M3 && dt != DT_E5M2) || p->stride_h != 1 || p->stride_w != 1 || p->fw > 32 ||
+      p->fh > 32 || p->w > 64 || p->c % kWgmCb != 0)
+    return false;
+  WgradMfmaArgs w{};
+  w.N = (int)p->n; w.IH = (int)p->h; w.IW = (int)p->w; w.C = (int)p->c;
+  w.OH = (int)oh; w.OW = (int)ow;
+  w.FH = p->fh; w.FW = p->fw; w.PH = p->pad_h; w.PW = p->pad_w;
+  const int nfm = (p->fw + 15) / 16, nfn = (p->fh + 15) / 16, nk = (int)((p->w + 31) / 32);
+  w.cblk = w.C / kWgmCb;
+  w.xr = w.IH + 1;
+  w.xp = 32 * nk + 16;  // an odd number of 16-byte units per row
+  // lane m's band starts at byte 32 kc - 16 fm - m + pw + dpad >= 0 of a
+  // staged dY row
+  w.dpad = std::max(0, 16 * (nfm - 1) + 15 - w.PW);
+  // staging items: column quads of the image (X) and the staged dY quads
+  // holding at least one real column
+  w.hx = (w.IW + 3) / 4;
+  w.ix = w.IH * w.hx;
+  w.e_lo = w.dpad / 4;
+  w.hd = (w.dpad + w.OW - 1) / 4 - w.e_lo + 1;
+  w.id = w.OH * w.hd;
+  w.dyp = (std::max(32 * nk + w.PW + w.dpad + 4, 4 * (w.e_lo + w.hd)) + 15) / 16 * 16;
+  const int items = std::max(w.ix, w.id);
+  const int pf = (items + 64 * kMfmaWaves - 1) / (64 * kMfmaWaves);
+  if (pf > kWgmMaxPf) return false;
+  const int ohp = (w.OH + 3) / 4 * 4;
+  const int64_t stage = (int64_t)kWgmCb * ((int64_t)w.xr * w.xp + (int64_t)ohp * w.dyp);
+  const int64_t part = (int64_t)p->fh * p->fw * kWgmCb * 4;
+  const int64_t lds = std::max(stage, part);
+  if (lds > kMfmaMaxLds) return false;
+  w.lds_bytes = (int)lds;
+  // slices of whole images, chosen as in plan_wgrad_mfma
+  const int64_t per_cu =
+      std::max<int64_t>(1, std::min<int64_t>(kLdsPerCu / lds, wgm8_waves_per_eu(pf) / 2));
+  const int64_t resident = kCus * per_cu;
+  const int64_t nn = std::max<int64_t>(p->n, 1);
+  int64_t z = 1;
+  if (p->wgrad_split > 0) {
+    z = std::min<int64_t>(p->wgrad_split, nn);
+  } else {
+    int64_t best = -1;
+    for (int64_t zc = 1; zc <= std::min<int64_t>(nn, 8 * resident); ++zc) {
+      const int64_t ipb = (nn + zc - 1) / zc, zr = (nn + ipb - 1) / ipb;
+      if (zr != zc) continue;
+      const int64_t rounds = (zr * w.cblk + resident - 1) / resident;
+      const int64_t cost = rounds * (ipb + 1);
+      if (best < 0 || cost < best) {
+        best = cost;
+        z = zr;
+      }
+    }
+  }
+  w.ipb = (int)((nn + z - 1) / z);
+  w.Z = (int)((nn + w.ipb - 1) / w.ipb);
+  const int64_t blocks = (int64_t)w.Z * w.cblk;
+  if (blocks > kI32Max) return false;
+  w.num_blocks = (int)blocks;
+  q->kind = PLAN_MFMA;
+  q->nfm = nfm;
+  q->nfn = nfn;
+  q->nk = nk;
+  q->pf = pf;
+  q->cb = kWgmCb;
+  q->z = w.Z;
+  q->blocks = w.num_blocks;
+  q->wm = w;
+  return true;
+}
+
 }  // namespace
 
 void set_last_error(const std::string& msg) { g_last_error = msg; }
@@ -524,7 +602,7 @@ int make_plan(const dwc_problem* p, int op, Plan* pl, std::string* err) {
     if (p->wgrad_split > 0 && p->n * oh > 0 && p->wgrad_split > p->n * oh)
       return fail(err, DWC_ERR_BAD_PARAM, "wgrad_split larger than N*OH");
     if (p->algo == DWC_ALGO_AUTO || p->algo == DWC_ALGO_MFMA) {
-      if (plan_wgrad_mfma(p, oh, ow, &q)) {
+      if (plan_wgrad_mfma(p, oh, ow, &q) || plan_wgrad_mfma8(p, oh, ow, &q)) {
         const int64_t m = (int64_t)p->fh * p->fw * p->c;
         q.ws_bytes = ((size_t)q.z * (size_t)m * 4 + 255) / 256 * 256;
         *pl = q;

@@ -1,5 +1,5 @@
-// inst_mfma8.hip -- instantiations and launcher of the packed-MFMA
-// forward-type kernel for fp8 operands (e4m3 / e5m2).
+// inst_mfma8.hip -- instantiations and launchers of the packed-MFMA
+// kernels for fp8 operands (e4m3 / e5m2): forward-type and filter gradient.
 #include "dwc_launch.h"
 #include "dwc_mfma8.h"
 
@@ -40,7 +40,53 @@ hipError_t by_nf(int nf, int tiles, const MfmaArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+template <int DT, int NFM, int NFN, int NK, int PF>
+hipError_t wg_go(const WgradMfmaArgs& a, hipStream_t s) {
+  auto kernel = wgrad_mfma8<DT, NFM, NFN, NK, PF>;
+  if (a.lds_bytes > 65536) {
+    const hipError_t e = allow_lds(kernel);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kernel, dim3(a.num_blocks), dim3(64 * kMfmaWaves), a.lds_bytes, s, a);
+  return hipGetLastError();
+}
+
+template <int DT, int NFM, int NFN, int NK>
+hipError_t wg_by_pf(int pf, const WgradMfmaArgs& a, hipStream_t s) {
+  if (pf == 1) return wg_go<DT, NFM, NFN, NK, 1>(a, s);
+  if (pf == 2) return wg_go<DT, NFM, NFN, NK, 2>(a, s);
+  return hipErrorInvalidValue;
+}
+
+template <int DT, int NFM, int NFN>
+hipError_t wg_by_nk(int nk, int pf, const WgradMfmaArgs& a, hipStream_t s) {
+  if (nk == 1) return wg_by_pf<DT, NFM, NFN, 1>(pf, a, s);
+  if (nk == 2) return wg_by_pf<DT, NFM, NFN, 2>(pf, a, s);
+  return hipErrorInvalidValue;
+}
+
+template <int DT, int NFM>
+hipError_t wg_by_nfn(int nfn, int nk, int pf, const WgradMfmaArgs& a, hipStream_t s) {
+  if (nfn == 1) return wg_by_nk<DT, NFM, 1>(nk, pf, a, s);
+  if (nfn == 2) return wg_by_nk<DT, NFM, 2>(nk, pf, a, s);
+  return hipErrorInvalidValue;
+}
+
+template <int DT>
+hipError_t wg_by_nfm(int nfm, int nfn, int nk, int pf, const WgradMfmaArgs& a, hipStream_t s) {
+  if (nfm == 1) return wg_by_nfn<DT, 1>(nfn, nk, pf, a, s);
+  if (nfm == 2) return wg_by_nfn<DT, 2>(nfn, nk, pf, a, s);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
+
+hipError_t launch_wgrad_mfma8(int dt, int nfm, int nfn, int nk, int pf, const WgradMfmaArgs& a,
+                              hipStream_t s) {
+  if (dt == DT_E4M3) return wg_by_nfm<DT_E4M3>(nfm, nfn, nk, pf, a, s);
+  if (dt == DT_E5M2) return wg_by_nfm<DT_E5M2>(nfm, nfn, nk, pf, a, s);
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_fwd_mfma8(int dt, int nf, int tiles, bool flip, const MfmaArgs& a,
                             hipStream_t s) {

@@ -344,3 +344,23 @@ def test_fp8_mfma_plans_and_rejections():
                             a["pad"], dtype=dt, algo="mfma")
             assert dwc.check(q, 0) == 2, kw
             assert "no packed-MFMA kernel" in dwc.last_error()
+
+
+def test_fp8_mfma_wgrad_plans():
+    """The packed fp8 filter gradient: kWgmCb (8) channels per workgroup,
+    dY rows padded so that every 36-byte band read stays in its row, X row
+    pitch an odd number of 16-byte units, LDS within the limit."""
+    for dt in (dwc.FP8_E4M3, dwc.FP8_E5M2):
+        for f in (3, 7, 13, 31):
+            p = dwc.problem(128, 28, 28, 512, f, f, 1, f // 2, dtype=dt)
+            d = dwc.plan_describe(p, 2)
+            assert d.startswith("bwd_filter mfma"), d
+            g = dict(kv.split("=") for kv in d.split()[2:])
+            nk, nfm = int(g["nk"]), int(g["nfm"])
+            assert int(g["cb"]) == 8 and (int(g["xp"]) // 16) % 2 == 1
+            assert int(g["dyp"]) % 16 == 0
+            assert int(g["dyp"]) >= 32 * nk + f // 2 + int(g["dpad"]) + 4
+            assert int(g["dpad"]) + f // 2 >= 16 * (nfm - 1) + 15
+            assert int(g["lds"]) <= 81920
+        q = dwc.problem(2, 20, 80, 16, 5, 5, 1, 2, dtype=dt, algo="mfma")
+        assert dwc.check(q, 2) == 2

@@ -15,7 +15,7 @@ torch = pytest.importorskip("torch")
 if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
-from gpu_helpers import TOL, dwc, gather, log, rel_l2, sample_index, sync, to_device  # noqa: E402
+from gpu_helpers import FP8_EL_TOL, TOL, dwc, gather, log, rel_l2, sample_index, sync, to_device  # noqa: E402
 
 
 def _cases(name):
@@ -33,18 +33,35 @@ def _id(c):
     return f"{name}-{s.h}x{s.w}c{s.c}k{s.fh}s{s.stride_h}-{dt}"
 
 
+def _vals(op):
+    """Operand values for the oracle: fp8 codes through the oracle's own
+    decoder, other dtypes as generated (exact in float32)."""
+    if op.dtype in oracle.FP8_FORMATS:
+        return oracle.fp8_decode(op.stored, op.dtype)
+    return op.values
+
+
 def _check_sampled(op, s, inp, got, k, rng):
+    """Relative L2 error over k sampled outputs; for fp8 operands also the
+    elementwise bound against the same outputs on |operands|."""
     stride, pad = (s.stride_h, s.stride_w), (s.pad_h, s.pad_w)
     if op == "fwd":
         idx = sample_index(s.y_shape(), k, rng)
-        want = oracle.fwd_at(inp.x.values, inp.w.values, idx, stride, pad)
+        a, b = _vals(inp.x), _vals(inp.w)
+        f = lambda u, v: oracle.fwd_at(u, v, idx, stride, pad)
     elif op == "bwd_data":
         idx = sample_index(s.x_shape(), k, rng)
-        want = oracle.bwd_data_at(inp.dy.values, inp.w.values, (s.h, s.w), idx, stride, pad)
+        a, b = _vals(inp.dy), _vals(inp.w)
+        f = lambda u, v: oracle.bwd_data_at(u, v, (s.h, s.w), idx, stride, pad)
     else:
         idx = sample_index(s.w_shape(), k, rng)
-        want = oracle.bwd_filter_at(inp.x.values, inp.dy.values, (s.fh, s.fw), idx, stride, pad)
-    return rel_l2(gather(got, idx), want)
+        a, b = _vals(inp.x), _vals(inp.dy)
+        f = lambda u, v: oracle.bwd_filter_at(u, v, (s.fh, s.fw), idx, stride, pad)
+    g, want = gather(got, idx), f(a, b)
+    if inp.dtype in oracle.FP8_FORMATS:
+        mag = f(np.abs(a), np.abs(b))
+        assert np.all(np.abs(g - want) <= FP8_EL_TOL * mag + 1e-30), op
+    return rel_l2(g, want)
 
 
 @pytest.mark.parametrize("case", ALL_CASES, ids=_id)
@@ -69,10 +86,10 @@ def test_workload_parity(case):
         sync()
         assert torch.isfinite(got).all().item()
         if small:
-            want = {"fwd": lambda: oracle.fwd(inp.x.values, inp.w.values, stride, pad),
-                    "bwd_data": lambda: oracle.bwd_data(inp.dy.values, inp.w.values,
+            want = {"fwd": lambda: oracle.fwd(_vals(inp.x), _vals(inp.w), stride, pad),
+                    "bwd_data": lambda: oracle.bwd_data(_vals(inp.dy), _vals(inp.w),
                                                         (s.h, s.w), stride, pad),
-                    "bwd_filter": lambda: oracle.bwd_filter(inp.x.values, inp.dy.values,
+                    "bwd_filter": lambda: oracle.bwd_filter(_vals(inp.x), _vals(inp.dy),
                                                             (s.fh, s.fw), stride, pad)}[op]()
             err = rel_l2(got.double().cpu().numpy(), want)
         else:
