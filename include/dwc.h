@@ -72,13 +72,17 @@ typedef enum {
     DWC_ALGO_AUTO = 0,   /* library's choice                                */
     DWC_ALGO_DIRECT = 1, /* register-window vector kernels                  */
     DWC_ALGO_GENERIC = 2, /* one output per lane; any filter size or stride */
-    DWC_ALGO_MFMA = 3,    /* packed matrix-core kernels (bf16/fp16 operands,
-                             stride 1, FW <= 32, C a multiple of 8, 16-byte
-                             aligned tensors; output width <= 64 for the
-                             forward and data gradient, input width <= 64
-                             and FH <= 32 for the filter gradient): the
-                             GEMV-to-GEMM packing of §4.2 on CDNA4 MFMA.
-                             AUTO picks it wherever it applies            */
+    DWC_ALGO_MFMA = 3,    /* packed matrix-core kernels (bf16/fp16 or fp8
+                             operands, stride 1, FW <= 32, C a multiple of
+                             8 -- of 16 for the fp8 forward and data
+                             gradient --, 16-byte aligned tensors; output
+                             width <= 64 for the forward and data
+                             gradient, input width <= 64 and FH <= 32 for
+                             the filter gradient): the GEMV-to-GEMM
+                             packing of §4.2 on CDNA4 MFMA (fp8: the K=128
+                             fp8 MFMA, four filter or output rows per
+                             instruction, §7).  AUTO picks it wherever it
+                             applies                                      */
     DWC_ALGO_HYBRID = 4   /* filter gradient of fp16 operands only (stride
                              1, square filter 3, 5, 7 or 9): the vector
                              sweep kernels with the hybrid accumulation of
