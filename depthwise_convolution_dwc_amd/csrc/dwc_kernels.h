@@ -196,7 +196,7 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_rows(FwdArgs a) {
 #pragma unroll
       for (int q = 0; q < TMW; ++q) {
         const int ow = ow0 + q;
-        if (ow < a.OW) out[((size_t)oh * a.OW + ow) * a.C] = acc[r][q];
+        if (ow < a.OW) store_nt(&out[((size_t)oh * a.OW + ow) * a.C], acc[r][q]);
       }
     }
   }
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(kBlockThreads) void dgrad_phase(DgradPhaseArgs a) {
 #pragma unroll
       for (int q = 0; q < TMW; ++q) {
         const int iw = pb + S * (j0 + q);
-        if (iw < a.IW) out[((size_t)ih * a.IW + iw) * a.C] = acc[r][q];
+        if (iw < a.IW) store_nt(&out[((size_t)ih * a.IW + iw) * a.C], acc[r][q]);
       }
     }
   }
@@ -564,7 +564,7 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_sweep(SweepArgs a) {
       const auto ors = make_rsrc(orow, ok ? (uint32_t)(TMW * a.C) * 4u : 0u);
 #pragma unroll
       for (int q = 0; q < TMW; ++q) {
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[done][q]), ors, (int)ooff[q], 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[done][q]), ors, (int)ooff[q], 0, kStoreNT);
         acc[done][q] = 0.f;
       }
     }
@@ -932,7 +932,7 @@ __global__ __launch_bounds__(256) void fwd_generic(GenericArgs a) {
                load_at<DT>(a.b, ((int64_t)fhe * a.FW + fwe) * a.C + c), s);
     }
   }
-  a.out[i] = s;
+  store_nt(&a.out[i], s);
 }
 
 // Data gradient for any stride: every (tap, output) pair whose window reads
@@ -962,7 +962,7 @@ __global__ __launch_bounds__(256) void dgrad_generic(GenericArgs a) {
                load_at<DT>(a.b, ((int64_t)fh * a.FW + fw) * a.C + c), s);
     }
   }
-  a.out[i] = s;
+  store_nt(&a.out[i], s);
 }
 
 // Filter gradient partials: work item (z, fh, fw, c), channel fastest; the
@@ -993,7 +993,7 @@ __global__ __launch_bounds__(256) void wgrad_generic(GenericArgs a) {
                load_at<DT>(a.b, ((n * a.OH + oh) * a.OW + ow) * a.C + c), s);
     }
   }
-  a.out[i] = s;
+  store_nt(&a.out[i], s);
 }
 
 }  // namespace dwc

@@ -318,7 +318,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma(MfmaArgs a) {
         const int oh = oh0 + p / a.OW;
         const int c = c0 + 4 * s;
         if (i < items && oh < a.OH && c < a.C)
-          *(mf_f32x4*)(out_img + ((size_t)oh * a.OW + p % a.OW) * a.C + c) = v[b];
+          store_nt((mf_f32x4*)(out_img + ((size_t)oh * a.OW + p % a.OW) * a.C + c), v[b]);
       }
     }
   }

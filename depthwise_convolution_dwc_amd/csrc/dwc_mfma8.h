@@ -311,7 +311,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma8(MfmaArgs a) {
         const int oh = oh0 + p / a.OW;
         const int c = c0 + 4 * q4;
         if (i < items && oh < a.OH && c < a.C)
-          *(mf8_f32x4*)(out_img + ((size_t)oh * a.OW + p % a.OW) * a.C + c) = v[b];
+          store_nt((mf8_f32x4*)(out_img + ((size_t)oh * a.OW + p % a.OW) * a.C + c), v[b]);
       }
     }
   }
