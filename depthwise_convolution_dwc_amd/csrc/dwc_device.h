@@ -46,6 +46,11 @@ __device__ __forceinline__ void store_nt(T* p, T v) {
   __builtin_nontemporal_store(v, p);
 }
 
+// floor(p / d) from m = div_magic(d), for p, d < 2^16.
+__device__ __forceinline__ int fast_div(int p, uint64_t m) {
+  return (int)(((uint64_t)(uint32_t)p * m) >> 32);
+}
+
 // An offset that is always outside any resource built above.
 constexpr uint32_t kOOB = 0x80000000u;
 

@@ -147,6 +147,13 @@ constexpr int kMfma8Cb = 16;
 constexpr int kZ8Row = 32;
 constexpr int kZ8Tail = 2;
 
+// Multiplier m = ceil(2^32 / d) with which floor(p / d) = (p * m) >> 32 for
+// all p, d < 2^16: writing p = q d + r, p m / 2^32 = q + (r + p e / 2^32) / d
+// with e = m d - 2^32 < d, and p e < 2^32 keeps the fraction below 1.  The
+// kernels divide small pixel and tap indices by runtime widths this way (one
+// 64-bit multiply instead of a division sequence).
+inline constexpr uint64_t div_magic(uint32_t d) { return ((1ull << 32) + d - 1) / d; }
+
 struct MfmaArgs {
   const void* in;    // N x IH x IW x C (X, or dY for the data gradient)
   const void* filt;  // FH x FW x C
@@ -154,6 +161,7 @@ struct MfmaArgs {
   int N, IH, IW, C, OH, OW;
   int FH, FW, PH, PW;  // PH/PW < 0 crop (data gradient with pad > F-1)
   int gt;            // column groups per tile: 1, 2 or 4 (rows per tile 16 / gt)
+  int rt_log;        // log2 of the rows per tile, 4 - log2(gt)
   int rblk;          // output rows per workgroup: tiles * 16 / gt
   int rch, cblk;     // row chunks per image, channel blocks
   int xr, wt, wp;    // staged input tile: rows, columns, row pitch (elements)
@@ -161,6 +169,8 @@ struct MfmaArgs {
   int e2, e2_log;    // e_items rounded up to a power of two, and its log2
   int lds_bytes;
   int num_blocks;    // N * cblk * rch workgroups
+  uint64_t ow_magic;  // div_magic(OW): staged output pixel -> (row, column)
+  uint64_t fw_magic;  // div_magic(FW): filter tap -> (row, column)
 };
 
 // out[i] = sum_{z < Z} ws[z * M + j(i)], summed in order of z.  Plain

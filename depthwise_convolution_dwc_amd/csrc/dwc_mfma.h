@@ -185,7 +185,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma(MfmaArgs a) {
         const int i = i0 + b * NT + tid;
         if (i >= items) continue;
         const int te = i / OCT;
-        const int fh = te / FW, fw = te - fh * FW;
+        const int fh = fast_div(te, a.fw_magic), fw = te - fh * FW;
         const int f = fw >> 4;
         uint16_t* d = zt + ((8 * (i % OCT)) * FH * NF + fh * NF + f) * kZRow + 16 + fw - 16 * f;
 #pragma unroll
@@ -201,8 +201,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma(MfmaArgs a) {
   // wave's CPW channels run together in the filter-row loop, and the B
   // operands of row fh+1 are read while the MFMAs of row fh execute.
   const int q = lane >> 4, m = lane & 15;
-  const int RT = 16 / a.gt;
-  const int gA = m / RT, rA = m % RT;
+  const int RT = 1 << a.rt_log;
+  const int gA = m >> a.rt_log, rA = m & (RT - 1);
   const bool reload = rA == RT - 1;
   const uint16_t* xbase = xs + (wave * CPW) * XR * WP + 16 * gA + 8 * q;
   // B: lane (q, j = m) starts at element 16 + 8q - m of a fragment row; it
@@ -292,8 +292,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma(MfmaArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int mm = 4 * q + r;
-        const int ol = tt * RT + mm % RT;
-        const int ow = 16 * (mm / RT) + m;
+        const int ol = tt * RT + (mm & (RT - 1));
+        const int ow = 16 * (mm >> a.rt_log) + m;
         if (ow < a.OW) os[(ol * a.OW + ow) * OSP + cc] = acc[k][tt][r];
       }
   }
@@ -315,10 +315,11 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma(MfmaArgs a) {
         const int i = i0 + b * NT + tid;
         const int s = i % QU;
         const int p = i / QU;
-        const int oh = oh0 + p / a.OW;
+        const int pr = fast_div(p, a.ow_magic);  // staged output row
+        const int oh = oh0 + pr;
         const int c = c0 + 4 * s;
         if (i < items && oh < a.OH && c < a.C)
-          store_nt((mf_f32x4*)(out_img + ((size_t)oh * a.OW + p % a.OW) * a.C + c), v[b]);
+          store_nt((mf_f32x4*)(out_img + ((size_t)oh * a.OW + (p - pr * a.OW)) * a.C + c), v[b]);
       }
     }
   }

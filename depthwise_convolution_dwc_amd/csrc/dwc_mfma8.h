@@ -179,7 +179,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma8(MfmaArgs a) {
       for (int b = 0; b < kMfma8Batch; ++b) {
         const int te = i0 + b * NT + tid;
         if (te >= taps) continue;
-        const int fh = te / FW, fw = te - fh * FW;
+        const int fh = fast_div(te, a.fw_magic), fw = te - fh * FW;
         const int f = fw >> 4;
         unsigned char* d = zt + (fh * NF + f) * kZ8Row + 16 + fw - 16 * f;
 #pragma unroll
@@ -194,8 +194,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma8(MfmaArgs a) {
   // instruction's four); A row m, B column m; D: lane (s, j) holds
   // D[4s .. 4s+3][j].  The wave's CPW channels run together.
   const int s = lane >> 4, m = lane & 15;
-  const int RT = 16 / a.gt;
-  const int gA = m / RT, rA = m % RT;
+  const int RT = 1 << a.rt_log;
+  const int gA = m >> a.rt_log, rA = m & (RT - 1);
   const bool reload = rA >= RT - 4;
   const unsigned char* xbase = xs + (wave * CPW) * XR * WP + 16 * gA;
   // B: lane (s, j = m) reads bytes [16 - m, 48 - m) of its fragment row
@@ -285,8 +285,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma8(MfmaArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int mm = 4 * s + r;
-        const int ol = tt * RT + mm % RT;
-        const int ow = 16 * (mm / RT) + m;
+        const int ol = tt * RT + (mm & (RT - 1));
+        const int ow = 16 * (mm >> a.rt_log) + m;
         if (ow < a.OW) os[(ol * a.OW + ow) * OSP + cc] = acc[k][tt][r];
       }
   }
@@ -308,10 +308,11 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma8(MfmaArgs a) {
         const int i = i0 + b * NT + tid;
         const int q4 = i % QU;
         const int p = i / QU;
-        const int oh = oh0 + p / a.OW;
+        const int pr = fast_div(p, a.ow_magic);  // staged output row
+        const int oh = oh0 + pr;
         const int c = c0 + 4 * q4;
         if (i < items && oh < a.OH && c < a.C)
-          store_nt((mf8_f32x4*)(out_img + ((size_t)oh * a.OW + p % a.OW) * a.C + c), v[b]);
+          store_nt((mf8_f32x4*)(out_img + ((size_t)oh * a.OW + (p - pr * a.OW)) * a.C + c), v[b]);
       }
     }
   }

@@ -128,6 +128,7 @@ bool plan_mfma(const FwdArgs& f, int dt, bool flip, Plan* q) {
   m.N = f.N; m.IH = f.IH; m.IW = f.IW; m.C = f.C; m.OH = f.OH; m.OW = f.OW;
   m.FH = f.FH; m.FW = f.FW; m.PH = f.PH; m.PW = f.PW;
   m.gt = gt;
+  m.rt_log = gt == 1 ? 4 : gt == 2 ? 3 : 2;
   m.wt = 16 * (gt + nf);
   int tiles = need <= 1 ? 1 : need <= 2 ? 2 : 4;
   // DWC_MFMA_TILES (1, 2 or 4) caps the tiles per workgroup, for A/B timing
@@ -167,6 +168,10 @@ bool plan_mfma(const FwdArgs& f, int dt, bool flip, Plan* q) {
   const int64_t blocks = (int64_t)f.N * m.cblk * m.rch;
   if (blocks > kI32Max) return false;
   m.num_blocks = (int)blocks;
+  // the kernels split staged output pixels and filter taps with fast_div
+  if ((int64_t)m.rblk * f.OW >= 65536 || (int64_t)f.FH * f.FW >= 65536) return false;
+  m.ow_magic = div_magic((uint32_t)f.OW);
+  m.fw_magic = div_magic((uint32_t)f.FW);
   q->kind = PLAN_MFMA;
   q->flip = flip;
   q->nf = nf;
@@ -199,6 +204,7 @@ bool plan_mfma8(const FwdArgs& f, int dt, bool flip, Plan* q) {
   m.N = f.N; m.IH = f.IH; m.IW = f.IW; m.C = f.C; m.OH = f.OH; m.OW = f.OW;
   m.FH = f.FH; m.FW = f.FW; m.PH = f.PH; m.PW = f.PW;
   m.gt = gt;
+  m.rt_log = gt == 1 ? 4 : gt == 2 ? 3 : 2;
   m.wt = 16 * (gt + nf);
   int tiles = need <= 1 ? 1 : need <= 2 ? 2 : 4;
   if (const char* v = getenv("DWC_MFMA_TILES")) {
@@ -237,6 +243,10 @@ bool plan_mfma8(const FwdArgs& f, int dt, bool flip, Plan* q) {
   const int64_t blocks = (int64_t)f.N * m.cblk * m.rch;
   if (blocks > kI32Max) return false;
   m.num_blocks = (int)blocks;
+  // the kernels split staged output pixels and filter taps with fast_div
+  if ((int64_t)m.rblk * f.OW >= 65536 || (int64_t)f.FH * f.FW >= 65536) return false;
+  m.ow_magic = div_magic((uint32_t)f.OW);
+  m.fw_magic = div_magic((uint32_t)f.FW);
   q->kind = PLAN_MFMA;
   q->flip = flip;
   q->nf = nf;
