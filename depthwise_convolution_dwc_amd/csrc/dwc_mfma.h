@@ -135,13 +135,18 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma(MfmaArgs a) {
     const uint32_t rowb = (uint32_t)a.IW * Cb;  // bytes per image row
     const int plane2 = XR * WP / 2;             // dwords per channel plane
     uint32_t* dst0 = (uint32_t*)xs + (8 * o) * plane2 + cp;
-    for (int rb = r0; rb <= nrow; rb += rs * kStageBatch) {
+    // byte offset of LDS row r's pixel pair is (r_lo + r - 1) * rowb + col0;
+    // LDS dwords of row r start at dst0 + r * (WP / 2).  Both advance by
+    // fixed steps from row to row.
+    const uint32_t row_step = (uint32_t)rs * rowb;
+    uint32_t off_rb = (uint32_t)(r_lo + r0 - 1) * rowb + col0;
+    for (int rb = r0; rb <= nrow; rb += rs * kStageBatch, off_rb += kStageBatch * row_step) {
       mf_u32x4 v0[kStageBatch], v1[kStageBatch];
 #pragma unroll
       for (int b = 0; b < kStageBatch; ++b) {
         const int r = rb + b * rs;  // LDS row
         const bool rok = r >= 1 && r <= nrow;
-        const uint32_t off = (uint32_t)(r_lo + r - 1) * rowb + col0;
+        const uint32_t off = off_rb + (uint32_t)b * row_step;
         v0[b] = __builtin_bit_cast(mf_u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                                  rsrc, (int)(rok && ok0 ? off : kOOB), 0, 0));
         v1[b] = __builtin_bit_cast(mf_u32x4, __builtin_amdgcn_raw_buffer_load_b128(
@@ -153,10 +158,10 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma(MfmaArgs a) {
         if (r > nrow || !e_in) continue;
         // channel j of a pixel is half (j & 1) of dword j / 2; the LDS dword
         // of channel j holds (pixel 0, pixel 1)
-        uint32_t* d = dst0 + r * (WP / 2);
+        uint32_t* d = dst0 + rb * (WP / 2) + b * (rs * (WP / 2));
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          d[j * plane2] = __builtin_amdgcn_perm(v1[b][j >> 1], v0[b][j >> 1],
+        for (int j = 0; j < 8; ++j, d += plane2)
+          *d = __builtin_amdgcn_perm(v1[b][j >> 1], v0[b][j >> 1],
                                                 (j & 1) ? 0x07060302u : 0x05040100u);
       }
     }
@@ -171,6 +176,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma(MfmaArgs a) {
       mf_u32x4 v[kStageBatch];
 #pragma unroll
       for (int b = 0; b < kStageBatch; ++b) {
+        if (i0 + b * NT >= items) break;  // uniform: no item left in this batch
         const int i = i0 + b * NT + tid;
         const int c = c0 + 8 * (i % OCT);
         const int te = i / OCT;  // staged tap (fh, fw)
@@ -182,15 +188,17 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma(MfmaArgs a) {
       }
 #pragma unroll
       for (int b = 0; b < kStageBatch; ++b) {
+        if (i0 + b * NT >= items) break;
         const int i = i0 + b * NT + tid;
         if (i >= items) continue;
         const int te = i / OCT;
         const int fh = fast_div(te, a.fw_magic), fw = te - fh * FW;
         const int f = fw >> 4;
+        const int zstep = FH * NF * kZRow;  // elements from one channel's rows to the next
         uint16_t* d = zt + ((8 * (i % OCT)) * FH * NF + fh * NF + f) * kZRow + 16 + fw - 16 * f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          d[j * FH * NF * kZRow] = (uint16_t)((v[b][j >> 1] >> (16 * (j & 1))) & 0xffffu);
+        for (int j = 0; j < 8; ++j, d += zstep)
+          *d = (uint16_t)((v[b][j >> 1] >> (16 * (j & 1))) & 0xffffu);
       }
     }
   }
@@ -284,42 +292,48 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma(MfmaArgs a) {
 
   // ---- outputs: registers -> LDS [pixel][channel] -> channel-contiguous stores
   __syncthreads();  // every wave is done with the staged input
+  // Lane (q, m) holds row mm = 4q + r of every tile at column m: output
+  // row tt * RT + (mm mod RT), column 16 (mm / RT) + m.  One address and one
+  // bounds test per mm; tiles and the wave's channels are fixed offsets.
+  {
+    const int tile_step = RT * a.OW * OSP;  // floats from one tile to the next
 #pragma unroll
-  for (int k = 0; k < CPW; ++k) {
-    const int cc = wave * CPW + k;
+    for (int r = 0; r < 4; ++r) {
+      const int mm = 4 * q + r;
+      const int ow = 16 * (mm >> a.rt_log) + m;
+      if (ow < a.OW) {
+        float* p = os + ((mm & (RT - 1)) * a.OW + ow) * OSP + wave * CPW;
 #pragma unroll
-    for (int tt = 0; tt < TILES; ++tt)
+        for (int tt = 0; tt < TILES; ++tt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int mm = 4 * q + r;
-        const int ol = tt * RT + (mm & (RT - 1));
-        const int ow = 16 * (mm >> a.rt_log) + m;
-        if (ow < a.OW) os[(ol * a.OW + ow) * OSP + cc] = acc[k][tt][r];
+          for (int k = 0; k < CPW; ++k) p[tt * tile_step + k] = acc[k][tt][r];
       }
+    }
   }
   __syncthreads();
+  // The block's output rows are consecutive, so staged pixel p is output
+  // pixel oh0 * OW + p.  Thread tid keeps one 16-byte channel quad sq of
+  // pixels pt, pt + PSTEP, ...
   {
-    constexpr int QU = CB / 4;
-    const int items = a.rblk * a.OW * QU;
-    float* out_img = a.out + (size_t)n * a.OH * a.OW * a.C;
-    for (int i0 = 0; i0 < items; i0 += NT * kStageBatch) {
+    constexpr int QU = CB / 4;      // channel quads per pixel
+    constexpr int PSTEP = NT / QU;  // pixels per pass of the workgroup
+    const int rows = a.OH - oh0 < a.rblk ? a.OH - oh0 : a.rblk;
+    const int npix = rows * a.OW;
+    const int sq = tid % QU, pt = tid / QU;
+    const bool c_ok = c0 + 4 * sq < a.C;
+    const float* src = os + pt * OSP + 4 * sq;
+    float* dst = a.out + ((size_t)n * a.OH * a.OW + (size_t)oh0 * a.OW + pt) * a.C + c0 + 4 * sq;
+    for (int p0 = 0; p0 < npix; p0 += PSTEP * kStageBatch) {
       mf_f32x4 v[kStageBatch];
 #pragma unroll
       for (int b = 0; b < kStageBatch; ++b) {
-        const int i = i0 + b * NT + tid;
-        const int p = i / QU;
-        v[b] = i < items ? *(const mf_f32x4*)(os + p * OSP + 4 * (i % QU)) : mf_f32x4{};
+        const int pb = p0 + b * PSTEP;  // uniform
+        v[b] = pb + pt < npix ? *(const mf_f32x4*)(src + pb * OSP) : mf_f32x4{};
       }
 #pragma unroll
       for (int b = 0; b < kStageBatch; ++b) {
-        const int i = i0 + b * NT + tid;
-        const int s = i % QU;
-        const int p = i / QU;
-        const int pr = fast_div(p, a.ow_magic);  // staged output row
-        const int oh = oh0 + pr;
-        const int c = c0 + 4 * s;
-        if (i < items && oh < a.OH && c < a.C)
-          store_nt((mf_f32x4*)(out_img + ((size_t)oh * a.OW + (p - pr * a.OW)) * a.C + c), v[b]);
+        const int pb = p0 + b * PSTEP;
+        if (pb + pt < npix && c_ok) store_nt((mf_f32x4*)(dst + (size_t)pb * a.C), v[b]);
       }
     }
   }

@@ -132,13 +132,18 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma8(MfmaArgs a) {
     const uint32_t rowb = (uint32_t)a.IW * Cb;
     const int plane4 = XR * WP / 4;  // dwords per channel plane
     uint32_t* dst0 = (uint32_t*)xs + e;
-    for (int rb = r0; rb <= nrow; rb += rs * kMfma8Batch) {
+    // byte offset of LDS row r's pixel quad is (r_lo + r - 1) * rowb + col0;
+    // LDS dwords of row r start at dst0 + r * (WP / 4).  Both advance by
+    // fixed steps from row to row.
+    const uint32_t row_step = (uint32_t)rs * rowb;
+    uint32_t off_rb = (uint32_t)(r_lo + r0 - 1) * rowb + col0;
+    for (int rb = r0; rb <= nrow; rb += rs * kMfma8Batch, off_rb += kMfma8Batch * row_step) {
       mf8_u32x4 v[kMfma8Batch][4];
 #pragma unroll
       for (int b = 0; b < kMfma8Batch; ++b) {
         const int r = rb + b * rs;  // LDS row
         const bool rok = r >= 1 && r <= nrow;
-        const uint32_t off = (uint32_t)(r_lo + r - 1) * rowb + col0;
+        const uint32_t off = off_rb + (uint32_t)b * row_step;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           v[b][i] = __builtin_bit_cast(
@@ -149,13 +154,13 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma8(MfmaArgs a) {
       for (int b = 0; b < kMfma8Batch; ++b) {
         const int r = rb + b * rs;
         if (r > nrow || !e_in) continue;
-        uint32_t* d = dst0 + r * (WP / 4);
+        uint32_t* d = dst0 + rb * (WP / 4) + b * (rs * (WP / 4));
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           uint32_t ch[4];
           transpose4(v[b][0][w], v[b][1][w], v[b][2][w], v[b][3][w], ch);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) d[(4 * w + i) * plane4] = ch[i];
+          for (int i = 0; i < 4; ++i, d += plane4) *d = ch[i];
         }
       }
     }
@@ -169,6 +174,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma8(MfmaArgs a) {
       mf8_u32x4 v[kMfma8Batch];
 #pragma unroll
       for (int b = 0; b < kMfma8Batch; ++b) {
+        if (i0 + b * NT >= taps) break;  // uniform: no tap left in this batch
         const int te = i0 + b * NT + tid;  // staged tap (fh, fw)
         const int src = FLIP ? taps - 1 - te : te;
         const uint32_t off = te < taps ? (uint32_t)src * (uint32_t)a.C + (uint32_t)c0 : kOOB;
@@ -177,14 +183,16 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma8(MfmaArgs a) {
       }
 #pragma unroll
       for (int b = 0; b < kMfma8Batch; ++b) {
+        if (i0 + b * NT >= taps) break;
         const int te = i0 + b * NT + tid;
         if (te >= taps) continue;
         const int fh = fast_div(te, a.fw_magic), fw = te - fh * FW;
         const int f = fw >> 4;
+        const int zstep = FHP * NF * kZ8Row;  // bytes from one channel's rows to the next
         unsigned char* d = zt + (fh * NF + f) * kZ8Row + 16 + fw - 16 * f;
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
-          d[j * FHP * NF * kZ8Row] = (unsigned char)(v[b][j >> 2] >> (8 * (j & 3)));
+        for (int j = 0; j < 16; ++j, d += zstep)
+          *d = (unsigned char)(v[b][j >> 2] >> (8 * (j & 3)));
       }
     }
   }
@@ -277,42 +285,48 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma8(MfmaArgs a) {
 
   // ---- outputs: registers -> LDS [pixel][channel] -> channel-contiguous stores
   __syncthreads();  // every wave is done with the staged operands
+  // Lane (s, m) holds row mm = 4s + r of every tile at column m: output
+  // row tt * RT + (mm mod RT), column 16 (mm / RT) + m.  One address and one
+  // bounds test per mm; tiles and the wave's channels are fixed offsets.
+  {
+    const int tile_step = RT * a.OW * OSP;  // floats from one tile to the next
 #pragma unroll
-  for (int k = 0; k < CPW; ++k) {
-    const int cc = wave * CPW + k;
+    for (int r = 0; r < 4; ++r) {
+      const int mm = 4 * s + r;
+      const int ow = 16 * (mm >> a.rt_log) + m;
+      if (ow < a.OW) {
+        float* p = os + ((mm & (RT - 1)) * a.OW + ow) * OSP + wave * CPW;
 #pragma unroll
-    for (int tt = 0; tt < TILES; ++tt)
+        for (int tt = 0; tt < TILES; ++tt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int mm = 4 * s + r;
-        const int ol = tt * RT + (mm & (RT - 1));
-        const int ow = 16 * (mm >> a.rt_log) + m;
-        if (ow < a.OW) os[(ol * a.OW + ow) * OSP + cc] = acc[k][tt][r];
+          for (int k = 0; k < CPW; ++k) p[tt * tile_step + k] = acc[k][tt][r];
       }
+    }
   }
   __syncthreads();
+  // The block's output rows are consecutive, so staged pixel p is output
+  // pixel oh0 * OW + p.  Thread tid keeps one 16-byte channel quad sq of
+  // pixels pt, pt + PSTEP, ...
   {
-    constexpr int QU = CB / 4;
-    const int items = a.rblk * a.OW * QU;
-    float* out_img = a.out + (size_t)n * a.OH * a.OW * a.C;
-    for (int i0 = 0; i0 < items; i0 += NT * kMfma8Batch) {
+    constexpr int QU = CB / 4;      // channel quads per pixel
+    constexpr int PSTEP = NT / QU;  // pixels per pass of the workgroup
+    const int rows = a.OH - oh0 < a.rblk ? a.OH - oh0 : a.rblk;
+    const int npix = rows * a.OW;
+    const int sq = tid % QU, pt = tid / QU;
+    const bool c_ok = c0 + 4 * sq < a.C;
+    const float* src = os + pt * OSP + 4 * sq;
+    float* dst = a.out + ((size_t)n * a.OH * a.OW + (size_t)oh0 * a.OW + pt) * a.C + c0 + 4 * sq;
+    for (int p0 = 0; p0 < npix; p0 += PSTEP * kMfma8Batch) {
       mf8_f32x4 v[kMfma8Batch];
 #pragma unroll
       for (int b = 0; b < kMfma8Batch; ++b) {
-        const int i = i0 + b * NT + tid;
-        const int p = i / QU;
-        v[b] = i < items ? *(const mf8_f32x4*)(os + p * OSP + 4 * (i % QU)) : mf8_f32x4{};
+        const int pb = p0 + b * PSTEP;  // uniform
+        v[b] = pb + pt < npix ? *(const mf8_f32x4*)(src + pb * OSP) : mf8_f32x4{};
       }
 #pragma unroll
       for (int b = 0; b < kMfma8Batch; ++b) {
-        const int i = i0 + b * NT + tid;
-        const int q4 = i % QU;
-        const int p = i / QU;
-        const int pr = fast_div(p, a.ow_magic);  // staged output row
-        const int oh = oh0 + pr;
-        const int c = c0 + 4 * q4;
-        if (i < items && oh < a.OH && c < a.C)
-          store_nt((mf8_f32x4*)(out_img + ((size_t)oh * a.OW + (p - pr * a.OW)) * a.C + c), v[b]);
+        const int pb = p0 + b * PSTEP;
+        if (pb + pt < npix && c_ok) store_nt((mf8_f32x4*)(dst + (size_t)pb * a.C), v[b]);
       }
     }
   }
