@@ -97,8 +97,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma(MfmaArgs a) {
   const int oh0 = rc * a.rblk;
   const int XR = a.xr, WP = a.wp;
   const int FH = a.FH, FW = a.FW;
-  // Image rows [r_lo, r_hi) feed this block; LDS row 0 is the zero row and
-  // image row ir sits at LDS row ir - r_lo + 1.
+  // Image rows [r_lo, r_hi) feed this block: image row ir sits at LDS row
+  // ir - r_lo + 1, between two zero rows (0 and nrow + 1) that stand for
+  // every row above and below.
   const int s_top = oh0 - a.PH;  // image row of staged index 0
   const int r_lo = s_top > 0 ? s_top : 0;
   const int r_end = s_top + a.rblk + FH - 1;
@@ -113,8 +114,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma(MfmaArgs a) {
   // ---- zero the filter-fragment rows (their taps are written after a barrier)
   for (int i = tid; i < zlen / 8; i += NT) ((mf_u32x4*)zt)[i] = mf_u32x4{0u, 0u, 0u, 0u};
 
-  // ---- stage the input tile: LDS rows 0 .. nrow, wt columns from -PW, CB
-  // channels.  Thread tid owns one (column pair, channel octet) e of a row
+  // ---- stage the input tile: LDS rows 0 .. nrow + 1, wt columns from -PW,
+  // CB channels (rows 0 and nrow + 1 are zeros).  Thread tid owns one (column pair, channel octet) e of a row
   // and visits every rs-th row; it issues kStageBatch rows of loads before
   // writing any of them to LDS.  LDS row 0 loads out of range: zeros.
   {
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma(MfmaArgs a) {
     // fixed steps from row to row.
     const uint32_t row_step = (uint32_t)rs * rowb;
     uint32_t off_rb = (uint32_t)(r_lo + r0 - 1) * rowb + col0;
-    for (int rb = r0; rb <= nrow; rb += rs * kStageBatch, off_rb += kStageBatch * row_step) {
+    for (int rb = r0; rb <= nrow + 1; rb += rs * kStageBatch, off_rb += kStageBatch * row_step) {
       mf_u32x4 v0[kStageBatch], v1[kStageBatch];
 #pragma unroll
       for (int b = 0; b < kStageBatch; ++b) {
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma(MfmaArgs a) {
 #pragma unroll
       for (int b = 0; b < kStageBatch; ++b) {
         const int r = rb + b * rs;
-        if (r > nrow || !e_in) continue;
+        if (r > nrow + 1 || !e_in) continue;
         // channel j of a pixel is half (j & 1) of dword j / 2; the LDS dword
         // of channel j holds (pixel 0, pixel 1)
         uint32_t* d = dst0 + rb * (WP / 2) + b * (rs * (WP / 2));
@@ -212,7 +213,19 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma(MfmaArgs a) {
   const int RT = 1 << a.rt_log;
   const int gA = m >> a.rt_log, rA = m & (RT - 1);
   const bool reload = rA == RT - 1;
-  const uint16_t* xbase = xs + (wave * CPW) * XR * WP + 16 * gA + 8 * q;
+  // A of tile tt at filter row fh is staged row s = tt * RT + rA + fh, at
+  // byte offset clamp((s_top - r_lo + 1 + s) * 2 WP, 0, (nrow + 1) * 2 WP)
+  // of the channel's plane: rows above the image clamp to zero row 0, rows
+  // below to zero row nrow + 1.
+  const int rowb2 = 2 * WP;
+  const int top_b = (nrow + 1) * rowb2;
+  const int a0 = (s_top - r_lo + 1 + rA) * rowb2;
+  const unsigned char* xb8 =
+      (const unsigned char*)(xs + (wave * CPW) * XR * WP + 16 * gA + 8 * q);
+  auto a_at = [&](int k, int tt, int f, int fh) -> mf_u32x4 {
+    const int o = min(max(a0 + (tt * RT + fh) * rowb2, 0), top_b);
+    return *(const mf_u32x4*)(xb8 + k * XR * rowb2 + o + 32 * f);
+  };
   // B: lane (q, j = m) starts at element 16 + 8q - m of a fragment row; it
   // reads from the even element at or below and shifts odd starts by 16 bits
   const int u0 = 16 + 8 * q - m;
@@ -228,13 +241,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma(MfmaArgs a) {
                     __builtin_amdgcn_alignbit(d[3], d[2], bshift),
                     __builtin_amdgcn_alignbit(d4, d[3], bshift)};
   };
-  // LDS row of staged index s (image row s_top + s): the zero row outside
-  // the image
-  auto lds_row = [&](int s) -> int {
-    const int ir = s_top + s;
-    return (ir >= r_lo && ir < r_hi) ? ir - r_lo + 1 : 0;
-  };
-
+  constexpr int TD = TILES / 2;  // tiles whose A moves by DPP row shifts
   mf_f32x4 acc[CPW][TILES];
   mf_u32x4 A[CPW][TILES][NF];
   mf_u32x4 B[CPW][NF];
@@ -243,10 +250,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma(MfmaArgs a) {
 #pragma unroll
     for (int tt = 0; tt < TILES; ++tt) {
       acc[k][tt] = mf_f32x4{0.f, 0.f, 0.f, 0.f};
-      const int row = lds_row(tt * RT + rA);
 #pragma unroll
-      for (int f = 0; f < NF; ++f)
-        A[k][tt][f] = *(const mf_u32x4*)(xbase + (k * XR + row) * WP + 16 * f);
+      for (int f = 0; f < NF; ++f) A[k][tt][f] = a_at(k, tt, f, 0);
     }
 #pragma unroll
     for (int f = 0; f < NF; ++f) B[k][f] = read_b(k * FH * NF + f);
@@ -266,28 +271,32 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma(MfmaArgs a) {
     for (int k = 0; k < CPW; ++k)
 #pragma unroll
       for (int f = 0; f < NF; ++f) B[k][f] = read_b((k * FH + fn) * NF + f);
+    // Tiles below TD move A down one combination with DPP row shifts (VALU)
+    // and reload only the last combination of each row group; tiles from
+    // TD on read all of A again (LDS).  The split keeps both pipes below
+    // the MFMA time: DPP alone costs four VALU instructions per MFMA.
 #pragma unroll
     for (int k = 0; k < CPW; ++k)
 #pragma unroll
-      for (int tt = 0; tt < TILES; ++tt)
+      for (int tt = 0; tt < TD; ++tt)
 #pragma unroll
         for (int f = 0; f < NF; ++f)
 #pragma unroll
           for (int v = 0; v < 4; ++v) A[k][tt][f][v] = row_shift_down(A[k][tt][f][v]);
-    // staged row of each tile's last combination at filter row fh+1 (the
-    // same for all its lanes)
-    int rrow[TILES];
-#pragma unroll
-    for (int tt = 0; tt < TILES; ++tt) rrow[tt] = uniform(lds_row(tt * RT + RT + fh));
     if (reload) {
 #pragma unroll
-      for (int tt = 0; tt < TILES; ++tt)
+      for (int tt = 0; tt < TD; ++tt)
 #pragma unroll
         for (int k = 0; k < CPW; ++k)
 #pragma unroll
-          for (int f = 0; f < NF; ++f)
-            A[k][tt][f] = *(const mf_u32x4*)(xbase + (k * XR + rrow[tt]) * WP + 16 * f);
+          for (int f = 0; f < NF; ++f) A[k][tt][f] = a_at(k, tt, f, fh + 1);
     }
+#pragma unroll
+    for (int tt = TD; tt < TILES; ++tt)
+#pragma unroll
+      for (int k = 0; k < CPW; ++k)
+#pragma unroll
+        for (int f = 0; f < NF; ++f) A[k][tt][f] = a_at(k, tt, f, fh + 1);
   }
 
   // ---- outputs: registers -> LDS [pixel][channel] -> channel-contiguous stores

@@ -108,7 +108,7 @@ int pick_split(int64_t rows, int64_t per_slice_blocks, int64_t strips, int64_t m
 // image height asks for (each B operand is read once per tile set) while
 // the staged input rows, the zero-padded filter-row fragments and
 // (afterwards) the staged outputs fit the workgroup's LDS.  The input tile
-// holds the real image rows a workgroup reads plus one zero row; its row
+// holds the real image rows a workgroup reads between two zero rows; its row
 // pitch gets 8 extra elements (an odd number of 16-byte units per row)
 // where LDS allows, so that lanes reading consecutive rows hit distinct
 // banks.  16 channels per workgroup (two per wave) with one 16-tap
@@ -140,7 +140,7 @@ bool plan_mfma(const FwdArgs& f, int dt, bool flip, Plan* q) {
   int64_t lds = 0;
   for (;; tiles /= 2) {
     m.rblk = tiles * rt;
-    m.xr = std::min(f.IH, m.rblk + f.FH - 1) + 1;
+    m.xr = std::min(f.IH, m.rblk + f.FH - 1) + 2;  // real rows between two zero rows
     const int64_t out_bytes = (int64_t)m.rblk * f.OW * (cb + 4) * 4;
     bool fit = false;
     for (int pad : {8, 0}) {
