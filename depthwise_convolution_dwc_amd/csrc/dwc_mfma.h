@@ -520,7 +520,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves, wgm_waves_per_eu(NFM, NFN, NK, PF)
     // One uniform body per output row: the operands of row oh+1 (and R of
     // row oh+2) are formed in the last iterations too, from rows that exist
     // (the zero row past the image), and never used.
-    for (int oh = 0; oh < OH; ++oh) {
+    auto row_step = [&](int oh) {
 #pragma unroll
       for (int kc = 0; kc < NK; ++kc)
 #pragma unroll
@@ -545,7 +545,16 @@ __global__ __launch_bounds__(64 * kMfmaWaves, wgm_waves_per_eu(NFM, NFN, NK, PF)
           R[fn][kc] = *(const mf_u32x4*)(xl + rrow * XP + 32 * kc);
         }
       }
+    };
+    // Two rows per iteration: the shifted B lands in the registers R held
+    // (the DPP keeps its destination's old value where no lane feeds it),
+    // so B and R trade registers every row and are back in place after two.
+    int oh = 0;
+    for (; oh + 1 < OH; oh += 2) {
+      row_step(oh);
+      row_step(oh + 1);
     }
+    if (oh < OH) row_step(oh);
   }
 
   // ---- the slice's partial: registers -> LDS [tap][channel] -> one
