@@ -11,7 +11,8 @@ the CPU oracle's rate on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
        python bench.py --copy-calibration  (a plain 256 MiB device copy, for counters)
-       python bench.py --sweep OUT.jsonl   (every named workload, one line per op)
+       python bench.py --sweep OUT.jsonl [--only WORKLOAD]
+                                           (every named workload, one line per op)
        python bench.py --summarize-profile DIR
            (turn the rocprofv3 CSV output of this benchmark under DIR -- trace/,
             fetch/, write/, copyf/, copyw/ and the traced run's stdout trace.log,
@@ -325,6 +326,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--sweep", default=None, help="write per-op lines of every workload here")
+    ap.add_argument("--only", default=None, metavar="WORKLOAD",
+                    help="with --sweep: only this named workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 256 MiB a few times (scales the byte counters)")
     ap.add_argument("--summarize-profile", default=None, metavar="DIR",
@@ -589,6 +592,8 @@ hash is stored with the data).
 def sweep(dwc, torch, dev, args):
     out = open(args.sweep, "w")
     for name, wl in WORKLOADS.items():
+        if args.only and name != args.only:
+            continue
         for s in wl["shapes"]:
             for dt in wl["dtypes"]:
                 inp = make_inputs(s, dt, seed=0, x_dist=wl["x_dist"], w_dist=wl["w_dist"])
