@@ -604,7 +604,11 @@ def sweep(dwc, torch, dev, args):
                     plan = [(s, op)]
                     sets = build_sets(dwc, torch, plan, inp, dev, algo)
                     steps = max(10, min(args.steps, 200))
-                    ms = time_step(torch, sets, steps, min(args.warmup, 10))
+                    # ten warm-up launches right after the upload timed short
+                    # kernels up to 25% slow: run the op for ~50 ms first
+                    t1 = time_step(torch, sets, 3, 1)
+                    warm = int(min(2000, max(args.warmup, 50.0 / max(t1, 1e-3))))
+                    ms = time_step(torch, sets, steps, warm)
                     m = op_model(s, op, dt)
                     p = dwc.problem(s.n, s.h, s.w, s.c, s.fh, s.fw, (s.stride_h, s.stride_w),
                                     (s.pad_h, s.pad_w), DTYPE_CODE[dt], algo)
