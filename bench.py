@@ -297,13 +297,12 @@ def headline_plan():
 
 
 def build_sets(dwc, torch, plan, inp, dev, algo="auto"):
-    """Enough buffer sets (each a full copy of the operands) to rotate over
-    ROTATE_BYTES, so no step reads a set the previous steps left in cache."""
-    set_bytes = 0
-    for s, op in plan:
-        m = op_model(s, op, inp.dtype)
-        set_bytes += m["bytes"]
-    nsets = max(1, min(8, -(-ROTATE_BYTES // max(1, int(set_bytes)))))
+    """Enough buffer sets (each a full copy of the operands) that every op of
+    the plan, run alone on consecutive sets, rotates over ROTATE_BYTES: no
+    launch reads data an earlier launch left in the caches, in the step loop
+    or in the per-op pass."""
+    op_bytes = min(op_model(s, op, inp.dtype)["bytes"] for s, op in plan)
+    nsets = max(1, min(16, -(-ROTATE_BYTES // max(1, int(op_bytes)))))
     host = {"x": inp.x, "w": inp.w, "dy": inp.dy}
     sets = []
     for _ in range(nsets):

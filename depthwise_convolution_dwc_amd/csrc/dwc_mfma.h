@@ -111,6 +111,47 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma(MfmaArgs a) {
   constexpr int OSP = CB + 4;                        // floats per staged output pixel
   const int zlen = (CB * FH * NF + kZTail) * kZRow;  // elements of zt (a multiple of 8)
 
+  // ---- filter taps: 16-byte loads of kStageBatch items per thread.  The
+  // first batch is issued before the input tile's loads, so the two wait
+  // for memory together; the taps go into their zero-padded fragment rows
+  // (turned by 180 degrees for FLIP) after the barrier that ends the zero
+  // fill.
+  const auto frsrc = make_rsrc(a.filt, (uint32_t)(FH * FW) * (uint32_t)a.C * 2u);
+  const int ftaps = FH * FW;
+  const int fitems = ftaps * OCT;
+  auto load_taps = [&](int i0, mf_u32x4 (&v)[kStageBatch]) {
+#pragma unroll
+    for (int b = 0; b < kStageBatch; ++b) {
+      if (i0 + b * NT >= fitems) break;  // uniform: no item left in this batch
+      const int i = i0 + b * NT + tid;
+      const int c = c0 + 8 * (i % OCT);
+      const int te = i / OCT;  // staged tap (fh, fw)
+      const int src = FLIP ? ftaps - 1 - te : te;
+      const uint32_t off =
+          i < fitems && c < a.C ? ((uint32_t)src * (uint32_t)a.C + (uint32_t)c) * 2u : kOOB;
+      v[b] = __builtin_bit_cast(mf_u32x4,
+                                __builtin_amdgcn_raw_buffer_load_b128(frsrc, (int)off, 0, 0));
+    }
+  };
+  auto store_taps = [&](int i0, const mf_u32x4 (&v)[kStageBatch]) {
+#pragma unroll
+    for (int b = 0; b < kStageBatch; ++b) {
+      if (i0 + b * NT >= fitems) break;
+      const int i = i0 + b * NT + tid;
+      if (i >= fitems) continue;
+      const int te = i / OCT;
+      const int fh = fast_div(te, a.fw_magic), fw = te - fh * FW;
+      const int f = fw >> 4;
+      const int zstep = FH * NF * kZRow;  // elements from one channel's rows to the next
+      uint16_t* d = zt + ((8 * (i % OCT)) * FH * NF + fh * NF + f) * kZRow + 16 + fw - 16 * f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j, d += zstep)
+        *d = (uint16_t)((v[b][j >> 1] >> (16 * (j & 1))) & 0xffffu);
+    }
+  };
+  mf_u32x4 fv0[kStageBatch];
+  load_taps(0, fv0);
+
   // ---- zero the filter-fragment rows (their taps are written after a barrier)
   for (int i = tid; i < zlen / 8; i += NT) ((mf_u32x4*)zt)[i] = mf_u32x4{0u, 0u, 0u, 0u};
 
@@ -168,40 +209,11 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma(MfmaArgs a) {
     }
   }
   __syncthreads();  // zt is zero
-  // ---- filter taps into their fragment rows, turned by 180 degrees for FLIP
-  {
-    const auto rsrc = make_rsrc(a.filt, (uint32_t)(FH * FW) * (uint32_t)a.C * 2u);
-    const int taps = FH * FW;
-    const int items = taps * OCT;
-    for (int i0 = 0; i0 < items; i0 += NT * kStageBatch) {
-      mf_u32x4 v[kStageBatch];
-#pragma unroll
-      for (int b = 0; b < kStageBatch; ++b) {
-        if (i0 + b * NT >= items) break;  // uniform: no item left in this batch
-        const int i = i0 + b * NT + tid;
-        const int c = c0 + 8 * (i % OCT);
-        const int te = i / OCT;  // staged tap (fh, fw)
-        const int src = FLIP ? taps - 1 - te : te;
-        const uint32_t off =
-            i < items && c < a.C ? ((uint32_t)src * (uint32_t)a.C + (uint32_t)c) * 2u : kOOB;
-        v[b] = __builtin_bit_cast(mf_u32x4,
-                                  __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)off, 0, 0));
-      }
-#pragma unroll
-      for (int b = 0; b < kStageBatch; ++b) {
-        if (i0 + b * NT >= items) break;
-        const int i = i0 + b * NT + tid;
-        if (i >= items) continue;
-        const int te = i / OCT;
-        const int fh = fast_div(te, a.fw_magic), fw = te - fh * FW;
-        const int f = fw >> 4;
-        const int zstep = FH * NF * kZRow;  // elements from one channel's rows to the next
-        uint16_t* d = zt + ((8 * (i % OCT)) * FH * NF + fh * NF + f) * kZRow + 16 + fw - 16 * f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j, d += zstep)
-          *d = (uint16_t)((v[b][j >> 1] >> (16 * (j & 1))) & 0xffffu);
-      }
-    }
+  store_taps(0, fv0);
+  for (int i0 = NT * kStageBatch; i0 < fitems; i0 += NT * kStageBatch) {
+    mf_u32x4 v[kStageBatch];
+    load_taps(i0, v);
+    store_taps(i0, v);
   }
   __syncthreads();
 
