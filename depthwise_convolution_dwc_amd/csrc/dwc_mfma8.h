@@ -96,8 +96,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma8(MfmaArgs a) {
   const int FH = a.FH, FW = a.FW;
   const int G4 = (FH + 3) / 4;  // MFMAs per fragment: four filter rows each
   const int FHP = 4 * G4;
-  // image rows [r_lo, r_hi) feed this block; LDS row 0 is the zero row and
-  // image row ir sits at LDS row ir - r_lo + 1
+  // image rows [r_lo, r_hi) feed this block: image row ir sits at LDS row
+  // ir - r_lo + 1, between the zero rows 0 and nrow + 1 that stand for
+  // every row above and below
   const int s_top = oh0 - a.PH;  // image row of staged index 0
   const int r_lo = s_top > 0 ? s_top : 0;
   const int r_end = s_top + a.rblk + FH - 1;
@@ -112,7 +113,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma8(MfmaArgs a) {
   // ---- zero the filter-fragment rows (taps are written after a barrier)
   for (int i = tid; i < zlen / 16; i += NT) ((mf8_u32x4*)zt)[i] = mf8_u32x4{0u, 0u, 0u, 0u};
 
-  // ---- stage the input tile: LDS rows 0 .. nrow, wt columns from -PW.
+  // ---- stage the input tile: LDS rows 0 .. nrow + 1 (0 and nrow + 1 are
+  // zeros), wt columns from -PW.
   // Thread tid owns column quad e (4 pixels x 16 channels, four 16-byte
   // loads) of a row and visits every rs-th row, kMfma8Batch rows of loads
   // in flight before any LDS write.  LDS row 0 loads out of range: zeros.
@@ -137,7 +139,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma8(MfmaArgs a) {
     // fixed steps from row to row.
     const uint32_t row_step = (uint32_t)rs * rowb;
     uint32_t off_rb = (uint32_t)(r_lo + r0 - 1) * rowb + col0;
-    for (int rb = r0; rb <= nrow; rb += rs * kMfma8Batch, off_rb += kMfma8Batch * row_step) {
+    for (int rb = r0; rb <= nrow + 1; rb += rs * kMfma8Batch, off_rb += kMfma8Batch * row_step) {
       mf8_u32x4 v[kMfma8Batch][4];
 #pragma unroll
       for (int b = 0; b < kMfma8Batch; ++b) {
@@ -153,7 +155,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma8(MfmaArgs a) {
 #pragma unroll
       for (int b = 0; b < kMfma8Batch; ++b) {
         const int r = rb + b * rs;
-        if (r > nrow || !e_in) continue;
+        if (r > nrow + 1 || !e_in) continue;
         uint32_t* d = dst0 + rb * (WP / 4) + b * (rs * (WP / 4));
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -220,19 +222,21 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma8(MfmaArgs a) {
     for (int i = 0; i < 8; ++i) r[i] = (int)__builtin_amdgcn_alignbit(d[i + 1], d[i], bshift);
     return r;
   };
-  // LDS row of staged index si (image row s_top + si): the zero row outside
-  // the image
-  auto lds_row = [&](int si) -> int {
-    const int ir = s_top + si;
-    return (ir >= r_lo && ir < r_hi) ? ir - r_lo + 1 : 0;
-  };
-  auto read_a = [&](int k, int row, int f) -> mf8_i32x8 {
-    const mf8_u32x4* p = (const mf8_u32x4*)(xbase + (k * XR + row) * WP + 16 * f);
+  // A of tile tt in row group h is staged row tt * RT + rA + s + 4h, at
+  // byte offset clamp((s_top - r_lo + 1 + row) * WP, 0, (nrow + 1) * WP) of
+  // the channel's plane: rows above the image clamp to zero row 0, rows
+  // below to zero row nrow + 1.
+  const int top_b = (nrow + 1) * WP;
+  const int a0 = (s_top - r_lo + 1 + rA + s) * WP;
+  auto read_a = [&](int k, int tt, int f, int h) -> mf8_i32x8 {
+    const int o = min(max(a0 + (tt * RT + 4 * h) * WP, 0), top_b);
+    const mf8_u32x4* p = (const mf8_u32x4*)(xbase + k * XR * WP + o + 16 * f);
     const mf8_u32x4 lo = p[0], hi = p[1];
     return mf8_i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   };
 
+  constexpr int TD = TILES / 2;  // tiles whose A moves by DPP row shifts
   mf8_f32x4 acc[CPW][TILES];
   mf8_i32x8 A[CPW][TILES][NF];
   mf8_i32x8 B[CPW][NF];
@@ -241,9 +245,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma8(MfmaArgs a) {
 #pragma unroll
     for (int tt = 0; tt < TILES; ++tt) {
       acc[k][tt] = mf8_f32x4{0.f, 0.f, 0.f, 0.f};
-      const int row = lds_row(tt * RT + rA + s);
 #pragma unroll
-      for (int f = 0; f < NF; ++f) A[k][tt][f] = read_a(k, row, f);
+      for (int f = 0; f < NF; ++f) A[k][tt][f] = read_a(k, tt, f, 0);
     }
 #pragma unroll
     for (int f = 0; f < NF; ++f) B[k][f] = read_b(k, 0, f);
@@ -263,24 +266,32 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma8(MfmaArgs a) {
     for (int k = 0; k < CPW; ++k)
 #pragma unroll
       for (int f = 0; f < NF; ++f) B[k][f] = read_b(k, hn, f);
+    // Tiles below TD move A down four combinations with DPP row shifts and
+    // reload the last four of each row group; tiles from TD on read all of
+    // A again from LDS (eight DPP instructions per MFMA alone take longer
+    // to issue than the MFMA; a full re-read costs 2 KB of LDS bandwidth).
 #pragma unroll
     for (int k = 0; k < CPW; ++k)
 #pragma unroll
-      for (int tt = 0; tt < TILES; ++tt)
+      for (int tt = 0; tt < TD; ++tt)
 #pragma unroll
         for (int f = 0; f < NF; ++f)
 #pragma unroll
           for (int v = 0; v < 8; ++v) A[k][tt][f][v] = row_shift_down4(A[k][tt][f][v]);
     if (reload) {
 #pragma unroll
-      for (int tt = 0; tt < TILES; ++tt) {
-        const int row = lds_row(tt * RT + rA + s + 4 * (h + 1));
+      for (int tt = 0; tt < TD; ++tt)
 #pragma unroll
         for (int k = 0; k < CPW; ++k)
 #pragma unroll
-          for (int f = 0; f < NF; ++f) A[k][tt][f] = read_a(k, row, f);
-      }
+          for (int f = 0; f < NF; ++f) A[k][tt][f] = read_a(k, tt, f, h + 1);
     }
+#pragma unroll
+    for (int tt = TD; tt < TILES; ++tt)
+#pragma unroll
+      for (int k = 0; k < CPW; ++k)
+#pragma unroll
+        for (int f = 0; f < NF; ++f) A[k][tt][f] = read_a(k, tt, f, h + 1);
   }
 
   // ---- outputs: registers -> LDS [pixel][channel] -> channel-contiguous stores

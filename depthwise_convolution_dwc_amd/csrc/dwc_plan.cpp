@@ -215,7 +215,7 @@ bool plan_mfma8(const FwdArgs& f, int dt, bool flip, Plan* q) {
   int64_t lds = 0;
   for (;; tiles /= 2) {
     m.rblk = tiles * rt;
-    m.xr = std::min(f.IH, m.rblk + f.FH - 1) + 1;
+    m.xr = std::min(f.IH, m.rblk + f.FH - 1) + 2;  // real rows between two zero rows
     const int64_t out_bytes = (int64_t)m.rblk * f.OW * (cb + 4) * 4;
     bool fit = false;
     for (int pad : {(m.wt / 16) % 2 == 0 ? 16 : 0, 0}) {
