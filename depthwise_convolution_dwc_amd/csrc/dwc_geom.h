@@ -150,8 +150,8 @@ constexpr int kZ8Tail = 2;
 // Multiplier m = ceil(2^32 / d) with which floor(p / d) = (p * m) >> 32 for
 // all p, d < 2^16: writing p = q d + r, p m / 2^32 = q + (r + p e / 2^32) / d
 // with e = m d - 2^32 < d, and p e < 2^32 keeps the fraction below 1.  The
-// kernels divide small pixel and tap indices by runtime widths this way (one
-// 64-bit multiply instead of a division sequence).
+// packed-MFMA kernels split filter tap indices by the runtime filter width
+// this way (one 64-bit multiply instead of a division sequence).
 inline constexpr uint64_t div_magic(uint32_t d) { return ((1ull << 32) + d - 1) / d; }
 
 struct MfmaArgs {
@@ -169,7 +169,6 @@ struct MfmaArgs {
   int e2, e2_log;    // e_items rounded up to a power of two, and its log2
   int lds_bytes;
   int num_blocks;    // N * cblk * rch workgroups
-  uint64_t ow_magic;  // div_magic(OW): staged output pixel -> (row, column)
   uint64_t fw_magic;  // div_magic(FW): filter tap -> (row, column)
 };
 

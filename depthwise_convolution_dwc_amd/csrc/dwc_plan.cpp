@@ -168,9 +168,8 @@ bool plan_mfma(const FwdArgs& f, int dt, bool flip, Plan* q) {
   const int64_t blocks = (int64_t)f.N * m.cblk * m.rch;
   if (blocks > kI32Max) return false;
   m.num_blocks = (int)blocks;
-  // the kernels split staged output pixels and filter taps with fast_div
-  if ((int64_t)m.rblk * f.OW >= 65536 || (int64_t)f.FH * f.FW >= 65536) return false;
-  m.ow_magic = div_magic((uint32_t)f.OW);
+  // the kernels split filter taps into (row, column) with fast_div
+  if ((int64_t)f.FH * f.FW >= 65536) return false;
   m.fw_magic = div_magic((uint32_t)f.FW);
   q->kind = PLAN_MFMA;
   q->flip = flip;
@@ -243,9 +242,8 @@ bool plan_mfma8(const FwdArgs& f, int dt, bool flip, Plan* q) {
   const int64_t blocks = (int64_t)f.N * m.cblk * m.rch;
   if (blocks > kI32Max) return false;
   m.num_blocks = (int)blocks;
-  // the kernels split staged output pixels and filter taps with fast_div
-  if ((int64_t)m.rblk * f.OW >= 65536 || (int64_t)f.FH * f.FW >= 65536) return false;
-  m.ow_magic = div_magic((uint32_t)f.OW);
+  // the kernels split filter taps into (row, column) with fast_div
+  if ((int64_t)f.FH * f.FW >= 65536) return false;
   m.fw_magic = div_magic((uint32_t)f.FW);
   q->kind = PLAN_MFMA;
   q->flip = flip;
