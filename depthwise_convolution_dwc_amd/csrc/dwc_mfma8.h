@@ -110,6 +110,42 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma8(MfmaArgs a) {
   constexpr int OSP = CB + 4;
   const int zlen = (CB * FHP * NF + kZ8Tail) * kZ8Row;  // a multiple of 16
 
+  // ---- filter taps: 16-byte loads (16 channels of one tap) of
+  // kMfma8Batch taps per thread.  The first batch is issued before the input
+  // tile's loads, so the two wait for memory together; the taps go into
+  // their zero-padded fragment rows (turned by 180 degrees for FLIP) after
+  // the barrier that ends the zero fill.
+  const auto frsrc = make_rsrc(a.filt, (uint32_t)(FH * FW) * (uint32_t)a.C);
+  const int ftaps = FH * FW;
+  auto load_taps = [&](int i0, mf8_u32x4 (&v)[kMfma8Batch]) {
+#pragma unroll
+    for (int b = 0; b < kMfma8Batch; ++b) {
+      if (i0 + b * NT >= ftaps) break;  // uniform: no tap left in this batch
+      const int te = i0 + b * NT + tid;  // staged tap (fh, fw)
+      const int src = FLIP ? ftaps - 1 - te : te;
+      const uint32_t off = te < ftaps ? (uint32_t)src * (uint32_t)a.C + (uint32_t)c0 : kOOB;
+      v[b] = __builtin_bit_cast(mf8_u32x4,
+                                __builtin_amdgcn_raw_buffer_load_b128(frsrc, (int)off, 0, 0));
+    }
+  };
+  auto store_taps = [&](int i0, const mf8_u32x4 (&v)[kMfma8Batch]) {
+#pragma unroll
+    for (int b = 0; b < kMfma8Batch; ++b) {
+      if (i0 + b * NT >= ftaps) break;
+      const int te = i0 + b * NT + tid;
+      if (te >= ftaps) continue;
+      const int fh = fast_div(te, a.fw_magic), fw = te - fh * FW;
+      const int f = fw >> 4;
+      const int zstep = FHP * NF * kZ8Row;  // bytes from one channel's rows to the next
+      unsigned char* d = zt + (fh * NF + f) * kZ8Row + 16 + fw - 16 * f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j, d += zstep)
+        *d = (unsigned char)(v[b][j >> 2] >> (8 * (j & 3)));
+    }
+  };
+  mf8_u32x4 fv0[kMfma8Batch];
+  load_taps(0, fv0);
+
   // ---- zero the filter-fragment rows (taps are written after a barrier)
   for (int i = tid; i < zlen / 16; i += NT) ((mf8_u32x4*)zt)[i] = mf8_u32x4{0u, 0u, 0u, 0u};
 
@@ -168,35 +204,11 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void fwd_mfma8(MfmaArgs a) {
     }
   }
   __syncthreads();  // zt is zero
-  // ---- filter taps into their fragment rows, turned by 180 degrees for FLIP
-  {
-    const auto rsrc = make_rsrc(a.filt, (uint32_t)(FH * FW) * (uint32_t)a.C);
-    const int taps = FH * FW;
-    for (int i0 = 0; i0 < taps; i0 += NT * kMfma8Batch) {
-      mf8_u32x4 v[kMfma8Batch];
-#pragma unroll
-      for (int b = 0; b < kMfma8Batch; ++b) {
-        if (i0 + b * NT >= taps) break;  // uniform: no tap left in this batch
-        const int te = i0 + b * NT + tid;  // staged tap (fh, fw)
-        const int src = FLIP ? taps - 1 - te : te;
-        const uint32_t off = te < taps ? (uint32_t)src * (uint32_t)a.C + (uint32_t)c0 : kOOB;
-        v[b] = __builtin_bit_cast(mf8_u32x4,
-                                  __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)off, 0, 0));
-      }
-#pragma unroll
-      for (int b = 0; b < kMfma8Batch; ++b) {
-        if (i0 + b * NT >= taps) break;
-        const int te = i0 + b * NT + tid;
-        if (te >= taps) continue;
-        const int fh = fast_div(te, a.fw_magic), fw = te - fh * FW;
-        const int f = fw >> 4;
-        const int zstep = FHP * NF * kZ8Row;  // bytes from one channel's rows to the next
-        unsigned char* d = zt + (fh * NF + f) * kZ8Row + 16 + fw - 16 * f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j, d += zstep)
-          *d = (unsigned char)(v[b][j >> 2] >> (8 * (j & 3)));
-      }
-    }
+  store_taps(0, fv0);
+  for (int i0 = NT * kMfma8Batch; i0 < ftaps; i0 += NT * kMfma8Batch) {
+    mf8_u32x4 v[kMfma8Batch];
+    load_taps(i0, v);
+    store_taps(i0, v);
   }
   __syncthreads();
 
