@@ -296,13 +296,19 @@ def headline_plan():
     return [(s1, "fwd"), (s2, "fwd"), (s1, "bwd_data"), (s1, "bwd_filter")]
 
 
+def rotation_sets(plan, dtype) -> int:
+    """Buffer sets for `plan`: the smallest op's algorithmic bytes times the
+    set count reach ROTATE_BYTES (at most 16 sets)."""
+    op_bytes = min(op_model(s, op, dtype)["bytes"] for s, op in plan)
+    return max(1, min(16, -(-ROTATE_BYTES // max(1, int(op_bytes)))))
+
+
 def build_sets(dwc, torch, plan, inp, dev, algo="auto"):
     """Enough buffer sets (each a full copy of the operands) that every op of
     the plan, run alone on consecutive sets, rotates over ROTATE_BYTES: no
     launch reads data an earlier launch left in the caches, in the step loop
     or in the per-op pass."""
-    op_bytes = min(op_model(s, op, inp.dtype)["bytes"] for s, op in plan)
-    nsets = max(1, min(16, -(-ROTATE_BYTES // max(1, int(op_bytes)))))
+    nsets = rotation_sets(plan, inp.dtype)
     host = {"x": inp.x, "w": inp.w, "dy": inp.dy}
     sets = []
     for _ in range(nsets):
