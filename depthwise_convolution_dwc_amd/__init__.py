@@ -24,7 +24,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdwc.so")
 
 F32, BF16, F16, FP8_E4M3, FP8_E5M2 = 0, 1, 2, 3, 4
-ALGO = {"auto": 0, "direct": 1, "generic": 2, "mfma": 3, "hybrid": 4}
+ALGO = {"auto": 0, "vector": 1, "direct": 1, "mfma": 2, "generic": 3, "hybrid": 4}
 ACT = {"none": 0, "relu": 1, "relu6": 2, "silu": 3}
 OP_FWD, OP_BWD_DATA, OP_BWD_FILTER = 0, 1, 2
 

@@ -69,10 +69,11 @@ typedef enum {
 } dwc_dtype;
 
 typedef enum {
-    DWC_ALGO_AUTO = 0,   /* library's choice                                */
-    DWC_ALGO_DIRECT = 1, /* register-window vector kernels                  */
-    DWC_ALGO_GENERIC = 2, /* one output per lane; any filter size or stride */
-    DWC_ALGO_MFMA = 3,    /* packed matrix-core kernels (bf16/fp16 or fp8
+    DWC_ALGO_AUTO = 0,    /* library's choice                               */
+    DWC_ALGO_VECTOR = 1,  /* register-window vector kernels (one channel per
+                             lane, fp32 FMAs)                               */
+    DWC_ALGO_DIRECT = 1,  /* the same value under its earlier name          */
+    DWC_ALGO_MFMA = 2,    /* packed matrix-core kernels (bf16/fp16 or fp8
                              operands, stride 1, FW <= 32, C a multiple of
                              8 -- of 16 for the fp8 forward and data
                              gradient --, 16-byte aligned tensors; output
@@ -82,7 +83,16 @@ typedef enum {
                              packing of §4.2 on CDNA4 MFMA (fp8: the K=128
                              fp8 MFMA, four filter or output rows per
                              instruction, §7).  AUTO picks it wherever it
-                             applies                                      */
+                             applies.  Operands must be finite: the packed
+                             band multiplies every staged element by
+                             structural zeros as well, so an inf or NaN
+                             operand turns the outputs of its 32-column
+                             window (forward, data gradient) or of its
+                             channel's filter gradient into NaN, where the
+                             definition gives +-inf or a finite value.  The
+                             vector and generic kernels follow IEEE
+                             arithmetic on non-finite operands           */
+    DWC_ALGO_GENERIC = 3, /* one output per lane; any filter size or stride */
     DWC_ALGO_HYBRID = 4   /* filter gradient of fp16 operands only (stride
                              1, square filter 3, 5, 7 or 9): the vector
                              sweep kernels with the hybrid accumulation of

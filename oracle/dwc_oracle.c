@@ -39,6 +39,7 @@
  *
  * Return value of every entry point: 0 on success, -1 on bad arguments.
  */
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -112,8 +113,17 @@ int dwc_oracle_fwd(int64_t n, int64_t ih, int64_t iw, int64_t c, int64_t fh,
     return 0;
 }
 
-/* Channels per OpenMP work item in the two gradients. */
-#define CBLK 16
+/* Channels per OpenMP work item in the two gradients: the widest of 128,
+ * 64, 32, 16 that still leaves four work items per thread.  This only splits
+ * independent outputs between threads; each output's sum runs over the same
+ * terms in the same order whatever the block, so results do not depend on
+ * it. */
+static int64_t channel_block(int64_t outer, int64_t c) {
+    int64_t want = 4 * (int64_t)omp_get_max_threads();
+    int64_t b = 128;
+    while (b > 16 && outer * ((c + b - 1) / b) < want) b /= 2;
+    return b;
+}
 
 /* data gradient: the adjoint of the forward map, written as the scatter of
  * every (output pixel, tap) product onto the input pixel it came from.
@@ -125,11 +135,12 @@ int dwc_oracle_bwd_data(int64_t n, int64_t ih, int64_t iw, int64_t c,
                         const double* w, double* dx) {
     dims_t d;
     if (make_dims(&d, n, ih, iw, c, fh, fw, sh, sw, ph, pw)) return -1;
-    int64_t nblk = (d.c + CBLK - 1) / CBLK;
+    const int64_t cblk = channel_block(d.n, d.c);
+    int64_t nblk = (d.c + cblk - 1) / cblk;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t t = 0; t < d.n * nblk; ++t) {
-        int64_t nn = t / nblk, c0 = (t % nblk) * CBLK;
-        int64_t c1 = c0 + CBLK < d.c ? c0 + CBLK : d.c;
+        int64_t nn = t / nblk, c0 = (t % nblk) * cblk;
+        int64_t c1 = c0 + cblk < d.c ? c0 + cblk : d.c;
         for (int64_t h = 0; h < d.ih; ++h)
             for (int64_t ww = 0; ww < d.iw; ++ww)
                 for (int64_t cc = c0; cc < c1; ++cc) XAT(&d, dx, nn, h, ww, cc) = 0.0;
@@ -159,11 +170,12 @@ int dwc_oracle_bwd_filter(int64_t n, int64_t ih, int64_t iw, int64_t c,
                           const double* dy, double* dw) {
     dims_t d;
     if (make_dims(&d, n, ih, iw, c, fh, fw, sh, sw, ph, pw)) return -1;
-    int64_t nblk = (d.c + CBLK - 1) / CBLK;
+    const int64_t cblk = channel_block(d.fh, d.c);
+    int64_t nblk = (d.c + cblk - 1) / cblk;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t t = 0; t < d.fh * nblk; ++t) {
-        int64_t kh = t / nblk, c0 = (t % nblk) * CBLK;
-        int64_t c1 = c0 + CBLK < d.c ? c0 + CBLK : d.c;
+        int64_t kh = t / nblk, c0 = (t % nblk) * cblk;
+        int64_t c1 = c0 + cblk < d.c ? c0 + cblk : d.c;
         double* acc = &WAT(&d, dw, kh, 0, 0);
         for (int64_t kw = 0; kw < d.fw; ++kw)
             for (int64_t cc = c0; cc < c1; ++cc) acc[kw * d.c + cc] = 0.0;

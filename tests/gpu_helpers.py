@@ -1,5 +1,5 @@
 """Helpers for the GPU parity tests: upload seeded inputs, compare with the
-oracle by relative L2 error."""
+oracle by relative L2 error and by an elementwise error bound."""
 
 from __future__ import annotations
 
@@ -19,6 +19,63 @@ TOL = {"f32": 1e-5, "bf16": 3e-3, "f16": 3e-3, "e4m3": 3e-3, "e5m2": 3e-3}
 # error up to about 2^-12 of the sum of their magnitudes (measured on
 # MI355X); the vector kernels round in fp32 (2^-24 per addition).
 FP8_EL_TOL = 2.0 ** -11
+# fp32 unit roundoff.
+U32 = 2.0 ** -24
+
+
+def gamma(k: int) -> float:
+    """k*u / (1 - k*u), u = 2^-24: a sum of k terms, each a product, computed
+    in fp32 in any order (any summation tree, FMA or separate rounding) is
+    off by at most gamma(k+1) times the sum of the terms' magnitudes
+    (the classical bound for floating-point inner products, Higham, Accuracy
+    and Stability of Numerical Algorithms, chapter 3)."""
+    ku = k * U32
+    return ku / (1.0 - ku)
+
+
+def terms_per_output(op: str, shape) -> int:
+    """Most products in one output's sum: the taps of one output pixel
+    (forward), the taps that land on one input pixel (data gradient: every
+    stride-th tap in each direction), or every output pixel of the batch
+    (filter gradient)."""
+    s = shape
+    if op == "fwd":
+        return s.fh * s.fw
+    if op == "bwd_data":
+        return -(-s.fh // s.stride_h) * -(-s.fw // s.stride_w)
+    return s.n * s.oh * s.ow
+
+
+def el_bound(op: str, shape, dtype: str) -> float:
+    """Elementwise bound, as a multiple of the same operation on |operands|:
+    fp32 summation of the output's terms, plus for fp8 operands the matrix
+    cores' group sums (FP8_EL_TOL)."""
+    b = gamma(terms_per_output(op, shape) + 1)
+    if dtype in ("e4m3", "e5m2"):
+        b += FP8_EL_TOL
+    return b
+
+
+def check_parity(got, want, mag, op: str, shape, dtype: str, what=""):
+    """Asserts relative L2 <= TOL[dtype] over the whole tensor and
+    |got - want| <= el_bound * mag for every element, where mag is the same
+    operation on |operands| (so the bound scales with each output's own
+    terms).  Returns (rel_l2, worst |got - want| / (el_bound * mag))."""
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    mag = np.asarray(mag, dtype=np.float64)
+    assert got.shape == want.shape == mag.shape, (what, got.shape, want.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = rel_l2(got, want)
+    assert err <= TOL[dtype], f"{what}: rel_l2 {err:.3e} > {TOL[dtype]}"
+    lim = el_bound(op, shape, dtype) * mag + 1e-300
+    d = np.abs(got - want)
+    worst = float(np.max(d / lim)) if d.size else 0.0
+    if worst > 1.0:
+        i = np.unravel_index(int(np.argmax(d / lim)), d.shape)
+        raise AssertionError(f"{what}: elementwise bound broken at {i}: got {got[i]!r} "
+                             f"want {want[i]!r} bound {lim[i]:.3e} ({worst:.3g}x)")
+    return err, worst
 
 
 def to_device(op: Operand, device="cuda") -> torch.Tensor:
@@ -66,4 +123,5 @@ def log(*a):
     print(*a, flush=True)
 
 
-__all__ = ["TOL", "FP8_EL_TOL", "to_device", "rel_l2", "sample_index", "gather", "sync", "log", "dwc"]
+__all__ = ["TOL", "FP8_EL_TOL", "U32", "gamma", "terms_per_output", "el_bound", "check_parity",
+           "to_device", "rel_l2", "sample_index", "gather", "sync", "log", "dwc"]

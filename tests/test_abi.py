@@ -364,3 +364,34 @@ def test_fp8_mfma_wgrad_plans():
             assert int(g["lds"]) <= 81920
         q = dwc.problem(2, 20, 80, 16, 5, 5, 1, 2, dtype=dt, algo="mfma")
         assert dwc.check(q, 2) == 2
+
+
+def _header_enum(prefix):
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    return {m.group(1): int(m.group(2))
+            for m in re.finditer(r"\b(" + prefix + r"[A-Z0-9_]+)\s*=\s*(\d+)", text)}
+
+
+def test_algo_codes_match_the_header():
+    """The binding's algo names map to the header's dwc_algo values: AUTO 0,
+    VECTOR (= DIRECT) 1, MFMA 2, then GENERIC 3 and HYBRID 4."""
+    h = _header_enum("DWC_ALGO_")
+    assert h == {"DWC_ALGO_AUTO": 0, "DWC_ALGO_VECTOR": 1, "DWC_ALGO_DIRECT": 1,
+                 "DWC_ALGO_MFMA": 2, "DWC_ALGO_GENERIC": 3, "DWC_ALGO_HYBRID": 4}
+    for name, code in dwc.ALGO.items():
+        assert h["DWC_ALGO_" + name.upper()] == code
+    # algo 2 asks for the packed-MFMA kernels: bf16 at stride 1 has them,
+    # fp32 does not
+    p = dwc.problem(1, 16, 16, 16, 5, 5, 1, 2, dtype=dwc.BF16, algo=2)
+    assert dwc.check(p, 0) == 0 and " mfma " in dwc.plan_describe(p, 0)
+    q = dwc.problem(1, 16, 16, 16, 5, 5, 1, 2, dtype=dwc.F32, algo=2)
+    assert dwc.check(q, 0) == 2
+
+
+def test_dtype_and_status_codes_match_the_header():
+    d = _header_enum("DWC_")
+    assert (d["DWC_F32"], d["DWC_BF16"], d["DWC_F16"], d["DWC_FP8_E4M3"], d["DWC_FP8_E5M2"]) == \
+        (dwc.F32, dwc.BF16, dwc.F16, dwc.FP8_E4M3, dwc.FP8_E5M2)
+    assert [d[k] for k in ("DWC_OK", "DWC_ERR_BAD_PARAM", "DWC_ERR_UNSUPPORTED",
+                           "DWC_ERR_MISALIGNED", "DWC_ERR_WORKSPACE", "DWC_ERR_ALIAS",
+                           "DWC_ERR_HIP")] == list(range(7))

@@ -16,7 +16,7 @@ torch = pytest.importorskip("torch")
 if not torch.cuda.is_available():  # collected on CPU too; skipped there
     pytest.skip("no GPU", allow_module_level=True)
 
-from gpu_helpers import TOL, dwc, log, rel_l2, sync, to_device  # noqa: E402
+from gpu_helpers import TOL, check_parity, dwc, el_bound, log, rel_l2, sync, to_device  # noqa: E402
 
 # (n, h, w, c, fh, fw, stride, pad)
 SHAPES = [
@@ -43,6 +43,10 @@ SHAPES = [
     (1, 12, 15, 96, 5, 5, 1, (0, 2)),
     (2, 11, 20, 64, 7, 7, 1, (3, 1)),
     (1, 16, 13, 128, 9, 9, 1, (2, 4)),
+    # padding beyond F-1: the stride-1 data gradient is a forward map with a
+    # negative (cropping) padding F-1-pad
+    (1, 10, 10, 16, 3, 3, 1, 4),
+    (2, 12, 12, 64, 13, 13, 1, 14),
 ]
 
 
@@ -91,13 +95,32 @@ def _algos(op, s: Shape, dtype):
     return out
 
 
-def _want(op, s: Shape, inp):
+def _oracle_op(op, s: Shape):
     stride, pad = (s.stride_h, s.stride_w), (s.pad_h, s.pad_w)
     if op == "fwd":
-        return oracle.fwd(_vals(inp.x), _vals(inp.w), stride, pad)
+        return lambda a, b: oracle.fwd(a, b, stride, pad)
     if op == "bwd_data":
-        return oracle.bwd_data(_vals(inp.dy), _vals(inp.w), (s.h, s.w), stride, pad)
-    return oracle.bwd_filter(_vals(inp.x), _vals(inp.dy), (s.fh, s.fw), stride, pad)
+        return lambda a, b: oracle.bwd_data(a, b, (s.h, s.w), stride, pad)
+    return lambda a, b: oracle.bwd_filter(a, b, (s.fh, s.fw), stride, pad)
+
+
+def _operands(op, inp):
+    if op == "fwd":
+        return _vals(inp.x), _vals(inp.w)
+    if op == "bwd_data":
+        return _vals(inp.dy), _vals(inp.w)
+    return _vals(inp.x), _vals(inp.dy)
+
+
+def _want(op, s: Shape, inp):
+    return _oracle_op(op, s)(*_operands(op, inp))
+
+
+def _want_mag(op, s: Shape, inp):
+    """The oracle's result and the same operation on |operands| (the scale
+    of the elementwise bound)."""
+    f, (a, b) = _oracle_op(op, s), _operands(op, inp)
+    return f(a, b), f(np.abs(a), np.abs(b))
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16", "e4m3", "e5m2"])
@@ -106,14 +129,11 @@ def _want(op, s: Shape, inp):
 def test_small_parity(shape, op, dtype):
     s = _shape(shape)
     inp = make_inputs(s, dtype, seed=sum(shape[:6]))
-    want = _want(op, s, inp)
+    want, mag = _want_mag(op, s, inp)
     for algo in _algos(op, s, dtype):
         log(f"case {shape} {op} {dtype} {algo}")
         got = _run(op, s, inp, algo)
-        assert got.shape == want.shape
-        err = rel_l2(got, want)
-        assert err <= TOL[dtype], (algo, err)
-        assert np.all(np.isfinite(got))
+        check_parity(got, want, mag, op, s, dtype, what=algo)
 
 
 @pytest.mark.parametrize("op", ["fwd", "bwd_data", "bwd_filter"])
@@ -137,9 +157,9 @@ def test_empty_batch(op):
 def test_wgrad_split_invariance(split):
     s = Shape(3, 8, 12, 80, 5, 5, 1, 1, 2, 2)
     inp = make_inputs(s, "f32", seed=12)
-    want = _want("bwd_filter", s, inp)
+    want, mag = _want_mag("bwd_filter", s, inp)
     got = _run("bwd_filter", s, inp, "auto", wgrad_split=split)
-    assert rel_l2(got, want) <= 1e-5
+    check_parity(got, want, mag, "bwd_filter", s, "f32")
 
 
 @pytest.mark.parametrize("op", ["fwd", "bwd_data", "bwd_filter"])
@@ -211,12 +231,10 @@ def test_mfma_parity(shape, op, dtype):
     s = _shape(shape)
     assert "mfma" in _algos(op, s, dtype), "shape meant for the packed-MFMA kernel"
     inp = make_inputs(s, dtype, seed=31 + sum(shape[:6]))
-    want = _want(op, s, inp)
+    want, mag = _want_mag(op, s, inp)
     log(f"case mfma {shape} {op} {dtype}")
     got = _run(op, s, inp, "mfma")
-    err = rel_l2(got, want)
-    assert err <= TOL[dtype], err
-    assert np.all(np.isfinite(got))
+    check_parity(got, want, mag, op, s, dtype, what="mfma")
 
 
 def _misaligned(t):
@@ -261,8 +279,8 @@ def test_mfma_outputs_fully_overwritten(op):
         y = torch.full(s.x_shape(), float("nan"), device="cuda")
         dwc.bwd_data(to_device(inp.dy), to_device(inp.w), (21, 19), 1, 4, out=y, algo="mfma")
     sync()
-    assert torch.isfinite(y).all().item()
-    assert rel_l2(y.double().cpu().numpy(), _want(op, s, inp)) <= TOL["bf16"]
+    want, mag = _want_mag(op, s, inp)
+    check_parity(y.double().cpu().numpy(), want, mag, op, s, "bf16")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
@@ -274,7 +292,8 @@ def test_mfma_many_workgroups(dtype, op):
     assert "mfma" in _algos(op, s, dtype)
     inp = make_inputs(s, dtype, seed=40)
     got = _run(op, s, inp, "mfma")
-    assert rel_l2(got, _want(op, s, inp)) <= TOL[dtype]
+    want, mag = _want_mag(op, s, inp)
+    check_parity(got, want, mag, op, s, dtype)
 
 
 @pytest.mark.parametrize("split", [1, 2, 3, 5])
@@ -284,10 +303,10 @@ def test_mfma_wgrad_batch_slices(split):
     so the result is run-to-run bitwise identical."""
     s = _shape((5, 13, 17, 24, 7, 5, 1, (3, 2)))
     inp = make_inputs(s, "bf16", seed=50 + split)
-    want = _want("bwd_filter", s, inp)
+    want, mag = _want_mag("bwd_filter", s, inp)
     log(f"case mfma wgrad split={split}")
     got = _run("bwd_filter", s, inp, "mfma", wgrad_split=split)
-    assert rel_l2(got, want) <= TOL["bf16"]
+    check_parity(got, want, mag, "bwd_filter", s, "bf16")
     again = _run("bwd_filter", s, inp, "mfma", wgrad_split=split)
     assert np.array_equal(got, again)
 
@@ -310,7 +329,8 @@ def test_sweep_row_chunks(shape, op, rows, monkeypatch):
     inp = make_inputs(s, "f32", seed=60 + rows)
     log(f"case sweep rows={rows} {shape} {op}")
     got = _run(op, s, inp, "direct")
-    assert rel_l2(got, _want(op, s, inp)) <= TOL["f32"]
+    want, mag = _want_mag(op, s, inp)
+    check_parity(got, want, mag, op, s, "f32")
 
 
 # Strided data gradient (the phase kernel): strides 2 and 3, square and
@@ -342,13 +362,11 @@ def test_strided_dgrad_phase(shape, dtype):
                     (s.pad_h, s.pad_w), dtype=DT[dtype])
     assert " phase " in dwc.plan_describe(p, 1)
     inp = make_inputs(s, dtype, seed=70 + sum(shape[:6]))
-    want = _want("bwd_data", s, inp)
+    want, mag = _want_mag("bwd_data", s, inp)
     log(f"case phase {shape} {dtype}")
     for algo in ("auto", "direct"):
         got = _run("bwd_data", s, inp, algo)
-        assert got.shape == want.shape
-        assert rel_l2(got, want) <= TOL[dtype], algo
-        assert np.all(np.isfinite(got))
+        check_parity(got, want, mag, "bwd_data", s, dtype, what=algo)
 
 
 def test_strided_dgrad_overwrites_output():
@@ -357,5 +375,53 @@ def test_strided_dgrad_overwrites_output():
     dx = torch.full(s.x_shape(), float("nan"), device="cuda")
     dwc.bwd_data(to_device(inp.dy), to_device(inp.w), (17, 16), 2, 3, out=dx)
     sync()
-    assert torch.isfinite(dx).all().item()
-    assert rel_l2(dx.double().cpu().numpy(), _want("bwd_data", s, inp)) <= TOL["f32"]
+    want, mag = _want_mag("bwd_data", s, inp)
+    check_parity(dx.double().cpu().numpy(), want, mag, "bwd_data", s, "f32")
+
+
+# Non-finite operands on the vector kernels: IEEE arithmetic, as in the
+# oracle.  One +inf and one -inf element (two rows apart, same channel) in
+# the input the operation reads pixel by pixel (X for the forward and the
+# filter gradient, dY for the data gradient): outputs whose sums take one of
+# them are +-inf, those that take both (with products of opposite signs) are
+# NaN, and every other output is unaffected.  The packed-MFMA kernels are
+# not covered: their Toeplitz band multiplies each staged element by
+# structural zeros too, so a non-finite operand turns nearby outputs into NaN
+# there; the header states that those kernels need finite operands.
+NONFINITE_SHAPES = [
+    (2, 14, 14, 64, 7, 7, 1, 3),       # sweep kernels
+    (2, 16, 15, 64, 13, 13, 1, 6),     # register-window kernels
+    (2, 12, 13, 40, 5, 3, 1, (2, 1)),  # register-window, non-square
+    (2, 15, 15, 64, 7, 7, 2, 3),       # stride 2: phase data gradient
+    (1, 11, 13, 40, 3, 3, 3, 1),       # stride 3: generic kernels
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("op", ["fwd", "bwd_data", "bwd_filter"])
+@pytest.mark.parametrize("shape", NONFINITE_SHAPES,
+                         ids=lambda t: "x".join(map(str, t[:6])) + f"_s{t[6]}")
+def test_nonfinite_operands_vector_kernels(shape, op, dtype):
+    s = _shape(shape)
+    inp = make_inputs(s, dtype, seed=80 + sum(shape[:6]))
+    src = inp.dy if op == "bwd_data" else inp.x
+    h = src.values.shape[1]
+    for row, val in ((h // 2 - 1, np.inf), (h // 2 + 1, -np.inf)):
+        idx = (1, row, src.values.shape[2] // 2, 3)
+        src.values[idx] = val
+        if dtype == "bf16":
+            src.stored[idx] = 0x7F80 if val > 0 else 0xFF80
+        else:
+            src.stored[idx] = val
+    want, mag = _want_mag(op, s, inp)
+    assert (~np.isfinite(want)).any() and np.isfinite(want).any()
+    algos = ["auto", "direct", "generic"] if dtype == "f32" else ["direct", "generic"]
+    for algo in [a for a in _algos(op, s, dtype) if a in algos]:
+        log(f"case nonfinite {shape} {op} {dtype} {algo}")
+        got = _run(op, s, inp, algo)
+        for cls in (np.isnan, np.isposinf, np.isneginf):
+            bad = cls(got) != cls(want)
+            assert not bad.any(), (algo, cls.__name__, np.argwhere(bad)[:4].tolist())
+        fin = np.isfinite(want)
+        d = np.abs(got[fin] - want[fin])
+        assert np.all(d <= el_bound(op, s, dtype) * mag[fin] + 1e-300), algo
