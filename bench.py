@@ -1,15 +1,20 @@
 #!/usr/bin/env python3
 """Benchmark of libdwc on one MI355X.
 
-One step = one pass of the whole DWC path over one batch of the CNN-stage
-workload (N=64, 56x56, C=128, 7x7 filter, pad 3, fp32, synthetic inputs):
-forward at stride 1, forward at stride 2 on the same input, data gradient and
-filter gradient at stride 1.  ``value`` is the nominal GFLOP/s of the step
-(2*N*OH*OW*C*FH*FW per operation, the numerator of the pages' intensity
-bound).  The JSON line also carries the roofline of the dominant kernel and
-the CPU oracle's rate on a bounded sample.
+One step = one pass of the whole DWC path -- forward, data gradient and
+filter gradient -- over one batch of the largest single-GPU workload: N=128,
+28x28, C=512, 31x31 filter, pad 15, fp16 operands with fp32 accumulation and
+outputs, synthetic inputs, every operation through the library's own kernel
+choice (the packed-MFMA kernels here).  ``value`` is the nominal GFLOP/s of
+the step (2*N*OH*OW*C*FH*FW per operation, the numerator of the pages'
+intensity bound).  The JSON line also carries the roofline of the dominant
+kernel, the CPU oracle's rate on a bounded sample, and per-configuration
+entries (every named workload, each operation timed alone: ms and fraction
+of its literal roofline), whose full records (nominal and valid GFLOP/s,
+GB/s, full-traffic fraction, kernels) go to --details.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+                       [--config-reps R] [--no-configs] [--details FILE]
        python bench.py --copy-calibration  (a plain 256 MiB device copy, for counters)
        python bench.py --sweep OUT.jsonl [--only WORKLOAD]
                                            (every named workload, one line per op)
@@ -36,7 +41,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from dwc_inputs import WORKLOADS, Shape, make_inputs  # noqa: E402
+from dwc_inputs import SWEEP_FILTERS, WORKLOADS, Shape, make_inputs  # noqa: E402
 
 METRIC = "DWC fwd/dgrad/wgrad GFLOP/s + % of roofline (HBM×η_D vs FP32/MFMA peak)"
 PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
@@ -46,10 +51,10 @@ PEAK_FP8_MFMA = 5.0e15     # dense fp8 MFMA
 DTYPE_CODE = {"f32": 0, "bf16": 1, "f16": 2, "e4m3": 3, "e5m2": 4}
 ROTATE_BYTES = 1 << 30     # buffer sets rotate over >= 1 GiB: no Infinity-Cache reuse
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["depthwise_convolution_dwc_amd/csrc/dwc_kernels.h",
-                  "depthwise_convolution_dwc_amd/csrc/dwc_plan.cpp",
-                  "depthwise_convolution_dwc_amd/csrc/inst_direct.hip",
-                  "depthwise_convolution_dwc_amd/csrc/inst_generic.hip"]
+KERNEL_SOURCES = sorted(
+    os.path.join("depthwise_convolution_dwc_amd", "csrc", f)
+    for f in os.listdir(os.path.join(ROOT, "depthwise_convolution_dwc_amd", "csrc"))
+    if f.endswith((".h", ".hip", ".cpp")))
 
 
 def kernel_source_hash() -> str:
@@ -114,9 +119,10 @@ def op_model(s: Shape, op: str, dtype: str) -> dict:
                        ("alu" if dtype == "f32" else "mfma")))
 
 
-def stored_traffic(kernel_names):
-    """HBM bytes per launch of the named kernels from profiles/traffic.json,
-    or None if absent or taken on other kernel sources."""
+def stored_traffic(kernel_specs):
+    """HBM bytes per launch of the given kernels (kernels_of() entries) from
+    profiles/traffic.json, or None if absent or taken on other kernel
+    sources."""
     path = os.path.join(PROFILES, "traffic.json")
     if not os.path.exists(path):
         return None
@@ -125,10 +131,11 @@ def stored_traffic(kernel_names):
     if t.get("source_hash") != kernel_source_hash():
         return None
     total = 0.0
-    for k in kernel_names:
-        if k not in t["kernels"]:
+    for spec in kernel_specs:
+        ks = kernel_matches(t["kernels"], spec)
+        if len(ks) != 1:
             return None
-        total += t["kernels"][k]["bytes_per_launch"]
+        total += t["kernels"][ks[0]]["bytes_per_launch"]
     return total
 
 
@@ -265,54 +272,87 @@ def cpu_baseline(inp, plan, budget_s=12.0):
         t, flops, reps = t + dt, flops + df, reps + 1
     cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
     return {"value": round(flops / t / 1e9, 3), "unit": "GFLOP/s", "cores": cores,
-            "kind": "oracle",
+            "cpu": cpu_model(), "kind": "oracle",
             "sample": f"the same step on the first {n} of {inp.shape.n} images, {reps} passes, "
                       f"float64 on the host, {t:.1f} s"}
 
 
 # ------------------------------------------------------------------ main ----
 
-HEADLINE = "fwd_n64_56x56_c128_k7"
+HEADLINE = "mixed_n128_28x28_c512"
+HEADLINE_SHAPE = 1          # the 31x31 shape of that workload
+HEADLINE_DTYPE = "f16"
+HEADLINE_OPS = ("fwd", "bwd_data", "bwd_filter")
 
 
-def kernels_of(dwc, s, op):
-    """Short names of the kernels one library call launches (from its plan)."""
-    p = dwc.problem(s.n, s.h, s.w, s.c, s.fh, s.fw, (s.stride_h, s.stride_w), (s.pad_h, s.pad_w))
+def kernels_of(dwc, s, op, dtype="f32", algo="auto"):
+    """The kernels one library call launches, each as 'name<template
+    arguments the plan fixes|workgroups' (a prefix of the full kernel name
+    in a rocprofv3 trace, and its launch size)."""
+    p = dwc.problem(s.n, s.h, s.w, s.c, s.fh, s.fw, (s.stride_h, s.stride_w),
+                    (s.pad_h, s.pad_w), DTYPE_CODE[dtype], algo)
     d = dwc.plan_describe(p, {"fwd": 0, "bwd_data": 1, "bwd_filter": 2}[op])
-    fam = d.split()[1]  # sweep / direct / generic
-    base = {("fwd", "sweep"): "fwd_sweep", ("bwd_data", "sweep"): "fwd_sweep",
-            ("bwd_filter", "sweep"): "wgrad_sweep", ("fwd", "direct"): "fwd_rows",
-            ("bwd_data", "direct"): "fwd_rows", ("bwd_filter", "direct"): "wgrad_rows",
-            ("fwd", "mfma"): "fwd_mfma", ("bwd_data", "mfma"): "fwd_mfma",
-            ("bwd_filter", "mfma"): "wgrad_mfma"}
-    k = [base.get((op, fam), fam)]
+    fam = d.split()[1]  # sweep / direct / generic / mfma / phase
+    kv = dict(t.split("=", 1) for t in d.split()[2:] if "=" in t)
+    dt = DTYPE_CODE[dtype]
+    flip = "true" if kv.get("flip") == "1" or (op == "bwd_data" and fam in ("mfma", "sweep")) \
+        else "false"
+    blocks = kv.get("blocks")
+    if fam == "mfma":
+        if op == "bwd_filter":
+            k = f"wgrad_mfma{'8' if dt >= 3 else ''}<{dt}, {kv['nfm']}, {kv['nfn']}, {kv['nk']}, " \
+                f"{kv['pf']}>"
+        elif dt >= 3:
+            k = f"fwd_mfma8<{dt}, {kv['nf']}, {kv['tiles']}, {flip}>"
+        else:
+            k = f"fwd_mfma<{dt}, {kv['nf']}, {kv['cb']}, {kv['tiles']}, {flip}>"
+    elif fam == "sweep":
+        k = (f"wgrad_sweep<{dt}, {kv['f']}, {kv['strip']}>" if op == "bwd_filter" else
+             f"fwd_sweep<{dt}, {kv['f']}, {kv['strip']}, {flip}")
+    elif fam == "direct":
+        k = (f"wgrad_rows<{dt}, {kv['fw']}, {kv['sw']}, {kv['tj']}>" if op == "bwd_filter" else
+             f"fwd_rows<{dt}, {kv['fw']}, {kv['sw']}, {kv['tmw']}, {flip}")
+    elif fam == "phase":
+        k = f"dgrad_phase<{dt}, {kv['km']}, "
+    else:  # generic: one lane per output, 256 per workgroup
+        k = {"fwd": f"fwd_generic<{dt}, false>", "bwd_data": f"dgrad_generic<{dt}>",
+             "bwd_filter": f"wgrad_generic<{dt}>"}[op]
+        blocks = str(-(-int(kv["total"]) // 256))
+    ks = [f"{k}|{blocks}"]
     if op == "bwd_filter" and "ws_bytes=0" not in d:
-        k.append("reduce_partials")
-    return k
+        ks.append(f"reduce_partials|{-(-(s.fh * s.fw * s.c) // 64)}")
+    return ks
+
+
+def kernel_matches(keys, spec):
+    """The keys ('full name|workgroups') that a kernels_of() entry names."""
+    pre, blocks = spec.split("|")
+    return [k for k in keys if k.split("|")[0].startswith(pre) and k.split("|")[1] == blocks]
 
 
 def headline_plan():
-    s1, s2 = WORKLOADS[HEADLINE]["shapes"]
-    return [(s1, "fwd"), (s2, "fwd"), (s1, "bwd_data"), (s1, "bwd_filter")]
+    s = WORKLOADS[HEADLINE]["shapes"][HEADLINE_SHAPE]
+    return [(s, op) for op in HEADLINE_OPS]
 
 
 def rotation_sets(plan, dtype) -> int:
     """Buffer sets for `plan`: the smallest op's algorithmic bytes times the
-    set count reach ROTATE_BYTES (at most 16 sets)."""
+    set count reach ROTATE_BYTES (at most 64 sets)."""
     op_bytes = min(op_model(s, op, dtype)["bytes"] for s, op in plan)
-    return max(1, min(16, -(-ROTATE_BYTES // max(1, int(op_bytes)))))
+    return max(1, min(64, -(-ROTATE_BYTES // max(1, int(op_bytes)))))
 
 
 def build_sets(dwc, torch, plan, inp, dev, algo="auto"):
     """Enough buffer sets (each a full copy of the operands) that every op of
     the plan, run alone on consecutive sets, rotates over ROTATE_BYTES: no
     launch reads data an earlier launch left in the caches, in the step loop
-    or in the per-op pass."""
+    or in the per-op pass.  The operands are uploaded once and copied on
+    the device."""
     nsets = rotation_sets(plan, inp.dtype)
-    host = {"x": inp.x, "w": inp.w, "dy": inp.dy}
+    first = {k: upload(v, torch, dev) for k, v in {"x": inp.x, "w": inp.w, "dy": inp.dy}.items()}
     sets = []
-    for _ in range(nsets):
-        bufs = {k: upload(v, torch, dev) for k, v in host.items()}
+    for i in range(nsets):
+        bufs = first if i == 0 else {k: v.clone() for k, v in first.items()}
         calls = []
         for s, op in plan:
             b = dict(bufs)
@@ -323,6 +363,103 @@ def build_sets(dwc, torch, plan, inp, dev, algo="auto"):
     return sets
 
 
+def config_label(name, s, dt):
+    """Short key of one measured configuration."""
+    tag = {"fwd_n1_14x14_c32_k7": "c1", "fwd_n64_56x56_c128_k7": "c2",
+           "all_n32_56x56_c128_k31": "c3", "sweep_n64_stages": "c4",
+           "mixed_n128_28x28_c512": "c5", "strided_bwd_n64_56x56_c128_k7_s2": "f1",
+           "lowbit_n128_28x28_c512": "f4"}[name]
+    return tag, f"{s.h}x{s.w}c{s.c}k{s.fh}s{s.stride_h}-{dt}"
+
+
+def config_cases(fp8_formats=("e4m3",)):
+    """(workload, shape, dtype, op, algo) of every per-configuration entry:
+    all five configurations of the target (half-precision ones on the
+    library's choice and on the vector kernels) and the measured "next"
+    rows (strided backward; fp8 operands, e4m3 -- e5m2 runs the same
+    kernels)."""
+    for name, wl in WORKLOADS.items():
+        for s in wl["shapes"]:
+            for dt in wl["dtypes"]:
+                if dt in ("e4m3", "e5m2") and dt not in fp8_formats:
+                    continue
+                algos = ("auto",) if dt == "f32" else ("auto", "direct")
+                for op in wl["ops"]:
+                    for algo in algos:
+                        yield name, s, dt, op, algo
+
+
+def measure_configs(dwc, torch, dev, reps, warmup_ms=50.0):
+    """Every configuration entry timed alone: `reps` back-to-back launches
+    on rotating buffer sets between two events, after ~warmup_ms of the
+    same launches.  Returns (compact summary for the JSON line, full
+    records)."""
+    records = []
+    groups = {}
+    for case in config_cases():
+        name, s, dt, op, algo = case
+        groups.setdefault((name, s, dt), []).append((op, algo))
+    for (name, s, dt), ops in groups.items():
+        wl = WORKLOADS[name]
+        inp = make_inputs(s, dt, seed=0, x_dist=wl["x_dist"], w_dist=wl["w_dist"])
+        for algo in sorted({a for _, a in ops}):
+            plan = [(s, op) for op, a in ops if a == algo]
+            sets = build_sets(dwc, torch, plan, inp, dev, algo)
+            t1 = time_ops(torch, sets, 3)
+            warm = [int(min(2000, max(5, warmup_ms / max(t, 1e-3)))) for t in t1]
+            time_ops(torch, sets, max(warm))
+            per_op = time_ops(torch, sets, reps)
+            for (s_, op), ms in zip(plan, per_op):
+                m = op_model(s_, op, dt)
+                tag, key = config_label(name, s_, dt)
+                full_peak = min(PEAK_HBM * m["flops"] / m["bytes"], m["peak"])
+                records.append({
+                    "config": tag, "workload": name, "case": key, "op": op, "algo": algo,
+                    "kernels": "+".join(kernels_of(dwc, s_, op, dt, algo)),
+                    "ms": round(ms, 5),
+                    "gflops": round(m["flops"] / (ms * 1e-3) / 1e9, 1),
+                    "gflops_valid": round(m["flops_valid"] / (ms * 1e-3) / 1e9, 1),
+                    "valid_frac": round(m["flops_valid"] / m["flops"], 3),
+                    "gbps": round(m["bytes"] / (ms * 1e-3) / 1e9, 1),
+                    "roofline_frac": round(m["flops"] / (ms * 1e-3) / m["roofline"], 4),
+                    "full_traffic_frac": round(m["flops"] / (ms * 1e-3) / full_peak, 4),
+                    "bound": m["bound"]})
+                log(json.dumps(records[-1]))
+            del sets
+        torch.cuda.empty_cache()
+    return compact_configs(records), records
+
+
+def compact_configs(records):
+    """The per-configuration entries of the JSON line: for each
+    configuration and case, op (and, for half-precision operands, the
+    vector kernels as op@vector) -> [ms, fraction of the literal roofline];
+    the 36-point filter sweep as per-stage lists over its nine filters."""
+    out = {}
+    for r in records:
+        op = r["op"] + ("" if r["algo"] == "auto" else "@vector")
+        v = [r["ms"], r["roofline_frac"]]
+        if r["config"] == "c4":
+            stage, f = r["case"].split("k")[0], int(r["case"].split("k")[1].split("s")[0])
+            d = out.setdefault("c4", {"filters": list(SWEEP_FILTERS)}).setdefault(stage, {})
+            d.setdefault(op + ".ms", []).append(r["ms"])
+            d.setdefault(op + ".frac", []).append(r["roofline_frac"])
+            assert SWEEP_FILTERS[len(d[op + ".ms"]) - 1] == f
+        else:
+            out.setdefault(r["config"], {}).setdefault(r["case"], {})[op] = v
+    return out
+
+
+def cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -330,6 +467,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--config-reps", type=int, default=500,
+                    help="launches per timed per-configuration entry")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-configuration entries")
+    ap.add_argument("--details", default=None,
+                    help="write the full per-configuration records here (JSON lines)")
     ap.add_argument("--sweep", default=None, help="write per-op lines of every workload here")
     ap.add_argument("--only", default=None, metavar="WORKLOAD",
                     help="with --sweep: only this named workload")
@@ -371,26 +514,36 @@ def main():
     plan = headline_plan()
     wl = WORKLOADS[HEADLINE]
     s1 = plan[0][0]
-    inp = make_inputs(s1, "f32", seed=0, x_dist=wl["x_dist"], w_dist=wl["w_dist"])
+    dt = HEADLINE_DTYPE
+    inp = make_inputs(s1, dt, seed=0, x_dist=wl["x_dist"], w_dist=wl["w_dist"])
     sets = build_sets(dwc, torch, plan, inp, dev)
     log(f"bench: {len(sets)} buffer sets, {args.warmup} warmup + {args.steps} timed steps")
     ms = time_step(torch, sets, args.steps, args.warmup)
     per_op = time_ops(torch, sets, args.steps)
+    del sets
+    torch.cuda.empty_cache()
 
-    models = [op_model(s, op, "f32") for s, op in plan]
+    models = [op_model(s, op, dt) for s, op in plan]
     flops = sum(m["flops"] for m in models)
-    names = ["fwd_s1", "fwd_s2", "bwd_data", "bwd_filter"]
     ops = {}
-    for name, m, t in zip(names, models, per_op):
-        ops[name] = {"ms": round(t, 5), "gflops": round(m["flops"] / (t * 1e-3) / 1e9, 1),
-                     "roofline_frac": round(m["flops"] / (t * 1e-3) / m["roofline"], 4),
-                     "bound": m["bound"]}
+    for (s, op), m, t in zip(plan, models, per_op):
+        ops[op] = {"ms": round(t, 5), "gflops": round(m["flops"] / (t * 1e-3) / 1e9, 1),
+                   "roofline_frac": round(m["flops"] / (t * 1e-3) / m["roofline"], 4),
+                   "bound": m["bound"]}
     dom = int(np.argmax(per_op))
     s_dom, op_dom = plan[dom]
-    kern = kernels_of(dwc, s_dom, op_dom)
+    kern = kernels_of(dwc, s_dom, op_dom, dt)
     roof = roofline_entry(models[dom], per_op[dom] * 1e-3, stored_traffic(kern))
     roof["kernel"] = "+".join(kern)
-    roof["op"] = names[dom]
+    roof["op"] = op_dom
+    configs = None
+    if not args.no_configs:
+        log(f"bench: per-configuration entries, {args.config_reps} launches each")
+        configs, records = measure_configs(dwc, torch, dev, args.config_reps)
+        if args.details:
+            with open(args.details, "w") as f:
+                for r in records:
+                    f.write(json.dumps(r) + "\n")
     cpu = None
     if not args.no_cpu:
         log("bench: timing the CPU oracle on a sample of the batch")
@@ -406,17 +559,18 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": dt,
         "data": "synthetic",
-        "config": {"workload": "CNN stage N=64 56x56 C=128 7x7 pad 3, fp32: "
-                               "fwd stride 1 + fwd stride 2 + bwd_data + bwd_filter",
-                   "n": 64, "h": 56, "w": 56, "c": 128, "filter": 7, "pad": 3,
-                   "global_batch": 64, "parallelism": "single-gpu"},
+        "config": {"workload": "mixed precision N=128 28x28 C=512 31x31 pad 15, fp16 operands, "
+                               "fp32 accumulation and outputs: fwd + bwd_data + bwd_filter",
+                   "n": 128, "h": 28, "w": 28, "c": 512, "filter": 31, "pad": 15,
+                   "global_batch": 128, "parallelism": "single-gpu"},
         "ops": ops,
         "roofline": roof,
         "cpu_baseline": cpu,
+        "configs": configs,
     }
-    print(json.dumps(line), flush=True)
+    print(json.dumps(line, separators=(",", ":")), flush=True)
 
 
 def _kernel_short(name: str) -> str:
@@ -434,70 +588,95 @@ def _csv_rows(d, pattern):
     return rows
 
 
-PROFILE_STEPS, PROFILE_WARMUP = 20, 5
-PROFILE_NAME = "cnn_stage_n64_56x56_c128_k7_fp32_step"
+PROFILE_STEPS, PROFILE_WARMUP, PROFILE_REPS = 20, 5, 20
+PROFILE_NAME = "mixed_n128_28x28_c512_k31_f16_step"
+_BENCH = "python3 $R/bench.py --no-cpu"
 PROFILE_CMDS = {
     "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof/trace "
-             f"-o run -- python3 $R/bench.py --steps {PROFILE_STEPS} --warmup {PROFILE_WARMUP} "
-             "--no-cpu > $R/gpurun_out/prof/trace.log",
+             f"-o run -- {_BENCH} --steps {PROFILE_STEPS} --warmup {PROFILE_WARMUP} "
+             f"--config-reps {PROFILE_REPS} --details $R/gpurun_out/prof/details.jsonl "
+             "> $R/gpurun_out/prof/trace.log",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof/fetch -o run "
-             "-- python3 $R/bench.py --steps 5 --warmup 2 --no-cpu",
+             f"-- {_BENCH} --steps 5 --warmup 2 --config-reps 5",
     "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof/write -o run "
-             "-- python3 $R/bench.py --steps 5 --warmup 2 --no-cpu",
+             f"-- {_BENCH} --steps 5 --warmup 2 --config-reps 5",
     "copyf": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof/copyf -o run "
              "-- python3 $R/bench.py --copy-calibration",
     "copyw": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof/copyw -o run "
              "-- python3 $R/bench.py --copy-calibration",
 }
-# kernel-name prefixes: fwd_sweep<DT, F, TMW, FLIP, PROLOGUE>
-OP_KERNELS = {"fwd_s1": ["fwd_sweep<0, 7, 7, false"], "fwd_s2": ["fwd_rows<0, 7, 2"],
-              "bwd_data": ["fwd_sweep<0, 7, 7, true"],
-              "bwd_filter": ["wgrad_sweep<0, 7, 7>", "reduce_partials"]}
+
+
+def _kernel_key(name: str, blocks: int) -> str:
+    """A kernel instantiation at one launch size: 'fwd_mfma<2, 2, 8, 4, false>|4096'."""
+    n = name.split("(")[0].replace("void ", "").replace("dwc::", "").strip()
+    return f"{n}|{blocks}"
+
+
+def _trace_groups(d):
+    """Durations (us) of every traced dispatch, grouped by kernel key, in
+    dispatch order."""
+    rows = sorted(_csv_rows(os.path.join(d, "trace"), "*kernel_trace.csv"),
+                  key=lambda r: int(r["Start_Timestamp"]))
+    g = {}
+    for r in rows:
+        blocks = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+        g.setdefault(_kernel_key(r["Kernel_Name"], blocks), []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return g
+
+
+def _match(groups, spec):
+    """Trace groups that a kernels_of() entry names."""
+    return {k: groups[k] for k in kernel_matches(groups, spec)}
 
 
 def summarize_profile(d):
-    """Write profiles/<workload>.kernel_trace.md, .hbm_traffic.md and
-    traffic.json from the rocprofv3 output of this benchmark under d."""
+    """Write profiles/<headline>.kernel_trace.md, profiles/configs.kernel_trace.md,
+    the HBM traffic summary and traffic.json from the rocprofv3 output of
+    this benchmark under d."""
     os.makedirs(PROFILES, exist_ok=True)
     cd = "cd /tmp && export TMPDIR=/tmp && "
-    # kernel trace: per-kernel durations in dispatch order.  The traced run
-    # launches each kernel PROFILE_WARMUP + PROFILE_STEPS times in the step
-    # loop, then PROFILE_STEPS times back to back in the per-op pass that
-    # gives the JSON line's per-op durations.
-    rows = sorted(_csv_rows(os.path.join(d, "trace"), "*kernel_trace.csv"),
-                  key=lambda r: int(r["Start_Timestamp"]))
-    stats = {}
-    for r in rows:
-        stats.setdefault(r["Kernel_Name"], []).append(
-            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    lines = ["| kernel | calls | avg us (all) | min us | max us | avg us (per-op pass) |",
-             "|---|---|---|---|---|---|"]
-    passavg = {}
-    for k, v in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
-        passavg[k] = float(np.mean(v[-PROFILE_STEPS:]))
-        lines.append(f"| `{k}` | {len(v)} | {np.mean(v):.2f} | {min(v):.2f} | {max(v):.2f} | "
-                     f"{passavg[k]:.2f} |")
+    groups = _trace_groups(d)
     traced = None
-    log_path = os.path.join(d, "trace.log")
-    if os.path.exists(log_path):
-        for ln in open(log_path):
-            if ln.startswith("{") and '"metric"' in ln:
-                traced = json.loads(ln)
-    cmp = ["| op | kernels | rocprofv3 per-op pass, us | JSON line `ops.<op>.ms`, us |",
-           "|---|---|---|---|"]
-    for op, pats in OP_KERNELS.items():
-        ks = [k for p in pats for k in stats if p in k]
-        tr = sum(passavg[k] for k in ks)
+    for ln in open(os.path.join(d, "trace.log")):
+        if ln.startswith("{") and '"metric"' in ln:
+            traced = json.loads(ln)
+    details = [json.loads(ln) for ln in open(os.path.join(d, "details.jsonl"))]
+    # headline step: the per-op pass launches each op PROFILE_STEPS times
+    # back to back after the step loop; its kernels' last PROFILE_STEPS
+    # dispatches are that pass
+    lines = ["| op | kernel (template arguments), workgroups | calls | avg us (all) | "
+             "avg us (per-op pass) | JSON line `ops.<op>.ms`, us |", "|---|---|---|---|---|---|"]
+    import depthwise_convolution_dwc_amd as dwc
+    s_h = WORKLOADS[HEADLINE]["shapes"][HEADLINE_SHAPE]
+    for op in HEADLINE_OPS:
+        ks = kernels_of(dwc, s_h, op, HEADLINE_DTYPE)
+        tot = 0.0
+        for kp in ks:
+            m = _match(groups, kp)
+            # the headline launches come first: the group with the most
+            # dispatches among same-name keys is the headline shape
+            k = max(m, key=lambda q: len(m[q]))
+            v = m[k]
+            head = v[:PROFILE_WARMUP + 2 * PROFILE_STEPS]
+            pas = float(np.mean(head[-PROFILE_STEPS:]))
+            tot += pas
+            lines.append(f"| {op} | `{k.replace('|', '`, ')} | {len(v)} | {np.mean(v):.2f} | "
+                         f"{pas:.2f} | |")
         js = traced["ops"][op]["ms"] * 1e3 if traced else float("nan")
-        cmp.append(f"| {op} | {' + '.join(_kernel_short(k) for k in ks)} | {tr:.2f} | {js:.2f} |")
-    trace_md = f"""# Kernel trace: CNN-stage step, N=64 56x56 C=128 7x7 pad 3, fp32
+        lines.append(f"| {op} | sum | | | **{tot:.2f}** | **{js:.2f}** |")
+    trace_md = f"""# Kernel trace: mixed-precision step, N=128 28x28 C=512 31x31 pad 15, fp16 operands
 
-One benchmark step = forward stride 1 + forward stride 2 + data gradient +
-filter gradient on the same batch (the default `bench.py` workload), on one
+One benchmark step = forward + data gradient + filter gradient on the same
+batch (the default `bench.py` workload; fp16 operands, fp32 accumulation and
+outputs, the library's kernel choice: the packed-MFMA kernels), on one
 MI355X, buffer sets rotating over >= 1 GiB (no Infinity-Cache reuse).  The
-traced run launches each kernel {PROFILE_WARMUP} + {PROFILE_STEPS} times in
-the step loop, then {PROFILE_STEPS} times back to back in the per-op pass
-whose event timings give the JSON line's per-op durations.
+traced run launches each op {PROFILE_WARMUP} + {PROFILE_STEPS} times in the
+step loop, then {PROFILE_STEPS} times back to back in the per-op pass whose
+HIP-event timings give the JSON line's per-op durations (`ops`), and then
+every per-configuration entry ({PROFILE_REPS} timed launches each); the
+kernel names below carry their template arguments and the workgroup count.
 
 Command (repository root `$R`):
 
@@ -506,71 +685,126 @@ Command (repository root `$R`):
 cd $R && python3 bench.py --summarize-profile gpurun_out/prof
 ```
 
-Durations from the dispatch timestamps of `run_kernel_trace.csv`:
+Durations from the dispatch timestamps of `run_kernel_trace.csv`; the last
+two columns compare the kernels' rocprofv3 average over the per-op pass with
+the event time the JSON line printed for that op (under the profiler both
+run a few percent slower than in an unprofiled run):
 
 {chr(10).join(lines)}
 
-`fwd_sweep<0, 7, 7, true, ..>` is the data gradient (the forward sweep on dY with the
-filter turned by 180 degrees); `fwd_rows<0, 7, 2, ...>` is the stride-2
-forward; the filter gradient is `wgrad_sweep` followed by `reduce_partials`.
-
-Per-op durations of the same traced command: the kernels' rocprofv3 average
-over the per-op pass against the JSON line it printed (HIP events on the
-library's stream; under the profiler both run a few percent slower than in
-an unprofiled run):
-
-{chr(10).join(cmp)}
+`fwd_mfma<2, 2, 8, 4, true>` is the data gradient (the packed forward on dY
+with the filter turned by 180 degrees); the filter gradient is `wgrad_mfma`
+followed by `reduce_partials`.  Template arguments: operand dtype (2 = fp16),
+16-tap filter fragments, channels per workgroup, tiles; for the filter
+gradient fragments of FW and FH, 32-column chunks, staging items per thread.
 """
     with open(os.path.join(PROFILES, PROFILE_NAME + ".kernel_trace.md"), "w") as f:
         f.write(trace_md)
+
+    # every per-configuration entry: its kernels' traced durations (the
+    # last PROFILE_REPS dispatches of each at that launch size) beside the
+    # bench's event time
+    clines = ["| config | case | op | algo | kernels, workgroups | rocprofv3 avg us | event us | "
+              "GFLOP/s | fraction |", "|---|---|---|---|---|---|---|---|---|"]
+    for r in details:
+        parts, tot = [], 0.0
+        for kp in r["kernels"].split("+"):
+            m = _match(groups, kp)
+            if not m:
+                parts.append(f"{kp} (not traced)")
+                continue
+            # several launch sizes share a name: take the one whose traced
+            # average is closest to this record's share of its event time
+            best = min(m, key=lambda q: abs(np.mean(m[q][-PROFILE_REPS:]) - r["ms"] * 1e3))
+            v = float(np.mean(m[best][-PROFILE_REPS:]))
+            tot += v
+            parts.append(f"`{best.replace('|', '`, ')}: {v:.1f}")
+        clines.append(f"| {r['config']} | {r['case']} | {r['op']} | {r['algo']} | "
+                      f"{'; '.join(parts)} | {tot:.1f} | {r['ms'] * 1e3:.1f} | {r['gflops']:.0f} | "
+                      f"{r['roofline_frac']:.3f} |")
+    cfg_md = f"""# Kernel trace: every per-configuration entry of the benchmark
+
+The same traced run as `{PROFILE_NAME}.kernel_trace.md` (command there).
+Each configuration entry (the five configurations of the target and the
+measured "next" rows) is timed alone, {PROFILE_REPS} launches back to back on
+rotating buffer sets after a warm-up; "event us" is the bench's HIP-event
+time per launch of that entry, "rocprofv3 avg us" the traced durations of
+its kernels over their last {PROFILE_REPS} dispatches at that launch size.
+Kernels that several entries share at one launch size are matched by
+duration.  Fraction: of the literal roofline min(8 TB/s x eta_D / operand
+bytes, peak), peak 157.3 TFLOP/s (fp32 operands), 2.5 PFLOP/s (bf16/fp16
+operands), 5.0 PFLOP/s (fp8 operands).
+
+{chr(10).join(clines)}
+"""
+    with open(os.path.join(PROFILES, "configs.kernel_trace.md"), "w") as f:
+        f.write(cfg_md)
 
     def per_kernel(sub, counter):
         acc = {}
         for r in _csv_rows(os.path.join(d, sub), "*counter_collection.csv"):
             if r["Counter_Name"] != counter:
                 continue
-            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
+            blocks = int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"]))
+            acc.setdefault(_kernel_key(r["Kernel_Name"], blocks), []).append(
+                float(r["Counter_Value"]) * 1024.0)
         return {k: float(np.mean(v)) for k, v in acc.items()}
 
     fetch, write = per_kernel("fetch", "FETCH_SIZE"), per_kernel("write", "WRITE_SIZE")
-    cf = per_kernel("copyf", "FETCH_SIZE")
-    cw = per_kernel("copyw", "WRITE_SIZE")
+    cf, cw = per_kernel("copyf", "FETCH_SIZE"), per_kernel("copyw", "WRITE_SIZE")
     copy_bytes = 256 * 1024 * 1024  # the calibration copy moves 256 MiB each way
     ck = [k for k in cf if "copyBuffer" in k]
+    ckw = [k for k in cw if "copyBuffer" in k]
     f_scale = copy_bytes / cf[ck[0]] if ck else 1.0
-    w_scale = copy_bytes / cw[ck[0]] if ck else 1.0
+    w_scale = copy_bytes / cw[ckw[0]] if ckw else 1.0
     kernels = {}
-    for k in set(fetch) | set(write):
-        short = _kernel_short(k)
-        fb = fetch.get(k, 0.0) * f_scale
-        wb = write.get(k, 0.0) * w_scale
-        kernels.setdefault(short, {"fetch_bytes": 0.0, "write_bytes": 0.0, "n": 0, "names": []})
-        e = kernels[short]
-        e["fetch_bytes"] += fb
-        e["write_bytes"] += wb
-        e["n"] += 1
-        e["names"].append(k)
-    for e in kernels.values():
-        e["fetch_bytes"] /= e["n"]
-        e["write_bytes"] /= e["n"]
-        e["bytes_per_launch"] = e["fetch_bytes"] + e["write_bytes"]
+    for k in sorted(set(fetch) | set(write)):
+        fb, wb = fetch.get(k, 0.0) * f_scale, write.get(k, 0.0) * w_scale
+        kernels[k] = {"fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb}
     out = {"source_hash": kernel_source_hash(), "fetch_scale": f_scale, "write_scale": w_scale,
            "kernels": kernels}
     with open(os.path.join(PROFILES, "traffic.json"), "w") as f:
         json.dump(out, f, indent=1, sort_keys=True)
-    tl = ["| kernel | FETCH bytes/launch | WRITE bytes/launch | total |", "|---|---|---|---|"]
-    for k, e in sorted(kernels.items()):
-        tl.append(f"| `{k}` | {e['fetch_bytes'] / 1e6:.1f} MB | {e['write_bytes'] / 1e6:.1f} MB | "
-                  f"{e['bytes_per_launch'] / 1e6:.1f} MB |")
+    # algorithmic bytes of each traced configuration's kernels, for the table
+    alg = {}
+    for r in details:
+        s = None
+        for name, wl in WORKLOADS.items():
+            for sh in wl["shapes"]:
+                for dt in wl["dtypes"]:
+                    if config_label(name, sh, dt)[1] == r["case"] and name == r["workload"]:
+                        s, dtt = sh, dt
+        if s is not None:
+            alg[(r["kernels"].split("+")[0], r["case"], r["op"], r["algo"])] = \
+                op_model(s, r["op"], dtt)["bytes"]
+    tl = ["| kernel, workgroups | FETCH bytes/launch | WRITE bytes/launch | total |",
+          "|---|---|---|---|"]
+    for k, e in kernels.items():
+        if any(x in k for x in ("copyBuffer", "elementwise", "fill", "Kernel")):
+            continue
+        tl.append(f"| `{k.replace('|', '`, ')} | {e['fetch_bytes'] / 1e6:.1f} MB | "
+                  f"{e['write_bytes'] / 1e6:.1f} MB | {e['bytes_per_launch'] / 1e6:.1f} MB |")
     cmds = "\n".join(cd + PROFILE_CMDS[k] for k in ("fetch", "write", "copyf", "copyw"))
-    traffic_md = f"""# HBM traffic per launch: CNN-stage step, N=64 56x56 C=128 7x7 pad 3, fp32
+    hk = [kernels_of(dwc, s_h, op, HEADLINE_DTYPE) for op in HEADLINE_OPS]
+    hl = []
+    for op, ks in zip(HEADLINE_OPS, hk):
+        m = op_model(s_h, op, HEADLINE_DTYPE)
+        got = sum(kernels[k]["bytes_per_launch"] for kp in ks for k in kernels if k.startswith(kp)
+                  and kernels[k]["bytes_per_launch"] == max(
+                      kernels[q]["bytes_per_launch"] for q in kernels if q.startswith(kp)))
+        hl.append(f"| {op} | {' + '.join(ks)} | {m['bytes'] / 1e6:.1f} MB | {got / 1e6:.1f} MB | "
+                  f"{got / m['bytes']:.3f} |")
+    traffic_md = f"""# HBM traffic per launch: every kernel of the benchmark
 
 Per-dispatch `FETCH_SIZE` and `WRITE_SIZE` (KiB, rocprofv3 derived counters,
-each in a run of its own), averaged over the step's launches of each kernel
-and scaled by what the same counters read for a plain 256 MiB device copy
-(`bench.py --copy-calibration`, the runtime's copyBuffer kernel): on this
-MI355X `FETCH_SIZE` reads {1 / f_scale:.3f} of the copied bytes (scale
-{f_scale:.3f}) and `WRITE_SIZE` {1 / w_scale:.3f} (scale {w_scale:.3f}).
+each in a run of its own), averaged over the launches of each kernel at each
+launch size and scaled by what the same counters read for a plain 256 MiB
+device copy (`bench.py --copy-calibration`, the runtime's copyBuffer
+kernel): on this MI355X `FETCH_SIZE` reads {1 / f_scale:.3f} of the copied
+bytes (scale {f_scale:.3f}) and `WRITE_SIZE` {1 / w_scale:.3f} (scale
+{w_scale:.3f}).  One calibration serves every kernel; it assumes the
+counters see a kernel's requests as they see the copy's (whole 64-byte and
+128-byte lines).
 
 Commands (repository root `$R`):
 
@@ -579,14 +813,20 @@ Commands (repository root `$R`):
 cd $R && python3 bench.py --summarize-profile gpurun_out/prof
 ```
 
+Headline step (N=128 28x28 C=512 31x31 pad 15, fp16 operands): measured
+against algorithmic bytes (operands read once, fp32 output written once):
+
+| op | kernels | algorithmic | measured | ratio |
+|---|---|---|---|---|
+{chr(10).join(hl)}
+
+Every kernel at every launch size of the run:
+
 {chr(10).join(tl)}
 
-Algorithmic bytes for comparison (each operand read once, output written
-once): forward 102.8 MB in + 102.8 MB out; stride-2 forward 102.8 MB in +
-25.7 MB out; filter gradient 102.8 MB (X) + 102.8 MB (dY) in.  The same
-numbers are in `traffic.json`, which `bench.py` reads for the `traffic`
-field of its roofline entry while the kernel sources are unchanged (their
-hash is stored with the data).
+The same numbers are in `traffic.json`, which `bench.py` reads for the
+`traffic` field of its roofline entry while the kernel sources are unchanged
+(their hash is stored with the data).
 """
     with open(os.path.join(PROFILES, PROFILE_NAME + ".hbm_traffic.md"), "w") as f:
         f.write(traffic_md)

@@ -289,3 +289,4 @@ def bwd_filter(x: torch.Tensor, dy: torch.Tensor, f_hw: Sequence[int], stride=1,
     bwd_filter_ptr(p, x.data_ptr(), dy.data_ptr(), out.data_ptr(), ws_ptr, ws_bytes,
                    _stream(stream))
     return out
+

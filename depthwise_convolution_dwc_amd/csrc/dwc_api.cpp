@@ -104,6 +104,72 @@ int prepare(const dwc_problem* p, int op, Plan* pl, const void* in0, const void*
   return st;
 }
 
+// Launches a validated filter-gradient plan: the slice kernel, then the
+// deterministic reduction of the slice partials held in `workspace`.
+int run_bwd_filter(const dwc_problem* p, const Plan& pl, const void* x, const void* dy,
+                   void* dw, void* workspace, hipStream_t s) {
+  const int64_t m = (int64_t)p->fh * p->fw * p->c;
+  if (pl.empty) {  // empty batch: dW = 0 (a sum over no terms)
+    const hipError_t e = launch_reduce(ReduceArgs{nullptr, (float*)dw, m, 0}, s);
+    return e == hipSuccess ? DWC_OK : hip_fail(e, "dwc_bwd_filter zero fill");
+  }
+  // One slice writes dW directly; several write partials to the workspace.
+  float* part = pl.ws_bytes > 0 ? (float*)workspace : (float*)dw;
+  hipError_t e;
+  if (pl.kind == PLAN_MFMA) {
+    WgradMfmaArgs w = pl.wm;
+    w.x = x;
+    w.dy = dy;
+    w.ws = (float*)workspace;
+    e = (pl.dt == DT_E4M3 || pl.dt == DT_E5M2)
+            ? launch_wgrad_mfma8(pl.dt, pl.nfm, pl.nfn, pl.nk, pl.pf, w, s)
+            : launch_wgrad_mfma(pl.dt, pl.nfm, pl.nfn, pl.nk, pl.pf, w, s);
+    if (e != hipSuccess) return hip_fail(e, "dwc_bwd_filter launch");
+    e = launch_reduce(
+        ReduceArgs{(const float*)workspace, (float*)dw, m, pl.z, kWgmCb, w.C, w.FH * w.FW}, s);
+    return e == hipSuccess ? DWC_OK : hip_fail(e, "dwc_bwd_filter reduce");
+  }
+  if (pl.kind == PLAN_DIRECT) {
+    WgradArgs a = pl.wa;
+    a.x = x;
+    a.dy = dy;
+    a.ws = part;
+    if (pl.sweep) {
+      SweepArgs w = pl.sa;
+      w.in = x;
+      w.in2 = dy;
+      w.out = part;
+      switch (pl.dt) {
+#define DWC_CASE(D) \
+  case D: e = launch_wgrad_sweep_dt##D(w.F, pl.tj, w, pl.blocks, s); break;
+        DWC_DT_LIST(DWC_CASE)
+#undef DWC_CASE
+        default: e = hipErrorInvalidValue; break;
+      }
+    } else {
+      switch (pl.dt) {
+#define DWC_CASE(D) \
+  case D: e = launch_wgrad_direct_dt##D(a.FW, a.SW, pl.tj, a, pl.blocks, s); break;
+        DWC_DT_LIST(DWC_CASE)
+#undef DWC_CASE
+        default: e = hipErrorInvalidValue; break;
+      }
+    }
+  } else {
+    GenericArgs g = pl.ga;
+    g.a = x;
+    g.b = dy;
+    g.out = part;
+    e = launch_generic(pl.gen_kind, pl.dt, g, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "dwc_bwd_filter launch");
+  if (pl.ws_bytes > 0) {
+    e = launch_reduce(ReduceArgs{(const float*)workspace, (float*)dw, m, pl.z}, s);
+    if (e != hipSuccess) return hip_fail(e, "dwc_bwd_filter reduce");
+  }
+  return DWC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -174,67 +240,7 @@ int dwc_bwd_filter(const dwc_problem* p, const void* x, const void* dy, void* dw
   Plan pl;
   const int st = prepare(p, DWC_OP_BWD_FILTER, &pl, x, dy, dw, workspace, workspace_bytes);
   if (st != DWC_OK) return st;
-  const hipStream_t s = (hipStream_t)stream;
-  const int64_t m = (int64_t)p->fh * p->fw * p->c;
-  if (pl.empty) {  // empty batch: dW = 0 (a sum over no terms)
-    const hipError_t e = launch_reduce(ReduceArgs{nullptr, (float*)dw, m, 0}, s);
-    return e == hipSuccess ? DWC_OK : hip_fail(e, "dwc_bwd_filter zero fill");
-  }
-  // One slice writes dW directly; several write partials to the workspace.
-  float* part = pl.ws_bytes > 0 ? (float*)workspace : (float*)dw;
-  hipError_t e;
-  if (pl.kind == PLAN_MFMA) {
-    WgradMfmaArgs w = pl.wm;
-    w.x = x;
-    w.dy = dy;
-    w.ws = (float*)workspace;
-    e = (pl.dt == DT_E4M3 || pl.dt == DT_E5M2)
-            ? launch_wgrad_mfma8(pl.dt, pl.nfm, pl.nfn, pl.nk, pl.pf, w, s)
-            : launch_wgrad_mfma(pl.dt, pl.nfm, pl.nfn, pl.nk, pl.pf, w, s);
-    if (e != hipSuccess) return hip_fail(e, "dwc_bwd_filter launch");
-    e = launch_reduce(
-        ReduceArgs{(const float*)workspace, (float*)dw, m, pl.z, kWgmCb, w.C, w.FH * w.FW}, s);
-    return e == hipSuccess ? DWC_OK : hip_fail(e, "dwc_bwd_filter reduce");
-  }
-  if (pl.kind == PLAN_DIRECT) {
-    WgradArgs a = pl.wa;
-    a.x = x;
-    a.dy = dy;
-    a.ws = part;
-    if (pl.sweep) {
-      SweepArgs w = pl.sa;
-      w.in = x;
-      w.in2 = dy;
-      w.out = part;
-      switch (pl.dt) {
-#define DWC_CASE(D) \
-  case D: e = launch_wgrad_sweep_dt##D(w.F, pl.tj, w, pl.blocks, s); break;
-        DWC_DT_LIST(DWC_CASE)
-#undef DWC_CASE
-        default: e = hipErrorInvalidValue; break;
-      }
-    } else {
-      switch (pl.dt) {
-#define DWC_CASE(D) \
-  case D: e = launch_wgrad_direct_dt##D(a.FW, a.SW, pl.tj, a, pl.blocks, s); break;
-        DWC_DT_LIST(DWC_CASE)
-#undef DWC_CASE
-        default: e = hipErrorInvalidValue; break;
-      }
-    }
-  } else {
-    GenericArgs g = pl.ga;
-    g.a = x;
-    g.b = dy;
-    g.out = part;
-    e = launch_generic(pl.gen_kind, pl.dt, g, s);
-  }
-  if (e != hipSuccess) return hip_fail(e, "dwc_bwd_filter launch");
-  if (pl.ws_bytes > 0) {
-    e = launch_reduce(ReduceArgs{(const float*)workspace, (float*)dw, m, pl.z}, s);
-    if (e != hipSuccess) return hip_fail(e, "dwc_bwd_filter reduce");
-  }
-  return DWC_OK;
+  return run_bwd_filter(p, pl, x, dy, dw, workspace, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -156,6 +156,11 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_rows(FwdArgs a) {
     for (int q = 0; q < TMW; ++q) acc[r][q] = 0.f;
 
   for (int fh0 = 0; fh0 < a.FH; fh0 += FHC) {
+    // chunk rows k in [klo, khi) are filter rows; the last chunk's others
+    // are past FH and take no products (a zero tap times an inf input would
+    // be NaN, where the definition has no such term)
+    const int nk = a.FH - fh0;
+    const int klo = up ? FHC - nk : 0, khi = up ? FHC : nk;
     float wv[FHC][FW];
 #pragma unroll
     for (int k = 0; k < FHC; ++k) {
@@ -178,7 +183,7 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_rows(FwdArgs a) {
 #pragma unroll
       for (int r = 0; r < TR; ++r) {
         const int k = m - r * S;
-        if (k < 0 || k >= FHC) continue;
+        if (k < 0 || k >= FHC || k < klo || k >= khi) continue;
 #pragma unroll
         for (int fw = 0; fw < FW; ++fw)
 #pragma unroll
@@ -284,12 +289,16 @@ __global__ __launch_bounds__(kBlockThreads) void dgrad_phase(DgradPhaseArgs a) {
 #pragma unroll
       for (int r = 0; r < TR; ++r) {
         const int k = r + KC - 1 - m;
-        if (k < 0 || k >= KC) continue;
+        // sub-filter rows past kh and columns past kw are zero taps: they
+        // take no products (zero times an inf dY would be NaN)
+        if (k < 0 || k >= KC || k0 + k >= kh) continue;
 #pragma unroll
-        for (int l = 0; l < KM; ++l)
+        for (int l = 0; l < KM; ++l) {
+          if (l >= kw) break;
 #pragma unroll
           for (int q = 0; q < TMW; ++q)
             acc[r][q] = fmaf(yv[q - l + KM - 1], wv[k][l], acc[r][q]);
+        }
       }
     }
   }

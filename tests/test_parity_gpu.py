@@ -405,9 +405,9 @@ def test_nonfinite_operands_vector_kernels(shape, op, dtype):
     s = _shape(shape)
     inp = make_inputs(s, dtype, seed=80 + sum(shape[:6]))
     src = inp.dy if op == "bwd_data" else inp.x
-    h = src.values.shape[1]
+    nn, h = src.values.shape[:2]
     for row, val in ((h // 2 - 1, np.inf), (h // 2 + 1, -np.inf)):
-        idx = (1, row, src.values.shape[2] // 2, 3)
+        idx = (nn - 1, row, src.values.shape[2] // 2, 3)
         src.values[idx] = val
         if dtype == "bf16":
             src.stored[idx] = 0x7F80 if val > 0 else 0xFF80
