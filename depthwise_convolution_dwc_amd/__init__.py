@@ -27,6 +27,8 @@ F32, BF16, F16, FP8_E4M3, FP8_E5M2 = 0, 1, 2, 3, 4
 ALGO = {"auto": 0, "vector": 1, "direct": 1, "mfma": 2, "generic": 3, "hybrid": 4}
 ACT = {"none": 0, "relu": 1, "relu6": 2, "silu": 3}
 OP_FWD, OP_BWD_DATA, OP_BWD_FILTER = 0, 1, 2
+# DWC_NOALLOC_SCRATCH_BYTES: the fixed scratch of dwc_bwd_filter_noalloc
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 _DTYPE_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16,
                torch.float8_e4m3fn: FP8_E4M3, torch.float8_e5m2: FP8_E5M2}
@@ -34,7 +36,7 @@ _DTYPE_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16,
 EXPORTED = (
     "dwc_version", "dwc_status_string", "dwc_last_error", "dwc_output_dims",
     "dwc_check", "dwc_plan_describe", "dwc_fwd", "dwc_fwd_fused", "dwc_bwd_data",
-    "dwc_bwd_filter_workspace_size", "dwc_bwd_filter",
+    "dwc_bwd_filter_workspace_size", "dwc_bwd_filter", "dwc_bwd_filter_noalloc",
 )
 
 
@@ -84,6 +86,7 @@ def lib() -> ctypes.CDLL:
         l.dwc_bwd_data.argtypes = [P, vp, vp, vp, vp]
         l.dwc_bwd_filter_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
         l.dwc_bwd_filter.argtypes = [P, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        l.dwc_bwd_filter_noalloc.argtypes = [P, vp, vp, vp, vp]
         for name in EXPORTED:
             if name not in ("dwc_status_string", "dwc_last_error"):
                 getattr(l, name).restype = ctypes.c_int
@@ -158,6 +161,10 @@ def bwd_data_ptr(p: Problem, dy: int, w: int, dx: int, stream: int = 0) -> None:
 def bwd_filter_ptr(p: Problem, x: int, dy: int, dw: int, ws: int, ws_bytes: int,
                    stream: int = 0) -> None:
     _raise(lib().dwc_bwd_filter(ctypes.byref(p), x, dy, dw, ws, ws_bytes, stream))
+
+
+def bwd_filter_noalloc_ptr(p: Problem, x: int, dy: int, dw: int, stream: int = 0) -> None:
+    _raise(lib().dwc_bwd_filter_noalloc(ctypes.byref(p), x, dy, dw, stream))
 
 
 # --------------------------------------------------------------------------
@@ -290,3 +297,27 @@ def bwd_filter(x: torch.Tensor, dy: torch.Tensor, f_hw: Sequence[int], stride=1,
                    _stream(stream))
     return out
 
+
+def bwd_filter_noalloc(x: torch.Tensor, dy: torch.Tensor, f_hw: Sequence[int], stride=1, pad=0,
+                       out: torch.Tensor = None, wgrad_split: int = 0, algo="auto",
+                       stream=None) -> torch.Tensor:
+    """dW (FH x FW x C, fp32) from X and dY through the entry point that
+    allocates nothing: the slice partials live in the library's fixed
+    per-device scratch.  ``out`` must be given (this call allocates no
+    device memory, torch's included)."""
+    _check_tensor(x, "x", 4)
+    _check_tensor(dy, "dy", 4)
+    dt = _operand_dtype(x, dy)
+    n, h, wd, c = x.shape
+    fh, fw = int(f_hw[0]), int(f_hw[1])
+    p = problem(n, h, wd, c, fh, fw, stride, pad, dt, algo, wgrad_split)
+    oh, ow = output_dims(p)
+    if tuple(dy.shape) != (n, oh, ow, c):
+        raise ValueError(f"dy must be {(n, oh, ow, c)}")
+    if out is None:
+        raise ValueError("out must be given: bwd_filter_noalloc allocates nothing")
+    _check_tensor(out, "out", 3, torch.float32)
+    if tuple(out.shape) != (fh, fw, c):
+        raise ValueError(f"out must be {(fh, fw, c)}")
+    bwd_filter_noalloc_ptr(p, x.data_ptr(), dy.data_ptr(), out.data_ptr(), _stream(stream))
+    return out

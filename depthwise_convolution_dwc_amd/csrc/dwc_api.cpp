@@ -3,6 +3,8 @@
 // launches the planned kernels on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "dwc_launch.h"
@@ -170,6 +172,38 @@ int run_bwd_filter(const dwc_problem* p, const Plan& pl, const void* x, const vo
   return DWC_OK;
 }
 
+// Fixed scratch of dwc_bwd_filter_noalloc: the filter gradient's slice
+// partials, for callers that cannot allocate device memory.  Each device
+// holds its own copy for the life of the process; host code reaches it only
+// through the address hipGetSymbolAddress returns on that device.
+constexpr size_t kScratchBytes = DWC_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// The scratch's device address on the current device, looked up once per
+// device with that device current.
+int scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) {
+    set_last_error("device index beyond the scratch table");
+    return DWC_ERR_UNSUPPORTED;
+  }
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? ptr : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return hip_fail(g_scratch_err[dev], "hipGetSymbolAddress");
+  *out = g_scratch_ptr[dev];
+  return DWC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -241,6 +275,61 @@ int dwc_bwd_filter(const dwc_problem* p, const void* x, const void* dy, void* dw
   const int st = prepare(p, DWC_OP_BWD_FILTER, &pl, x, dy, dw, workspace, workspace_bytes);
   if (st != DWC_OK) return st;
   return run_bwd_filter(p, pl, x, dy, dw, workspace, (hipStream_t)stream);
+}
+
+int dwc_bwd_filter_noalloc(const dwc_problem* p, const void* x, const void* dy, void* dw,
+                           void* stream) {
+  if (!p) {
+    set_last_error("problem pointer is NULL");
+    return DWC_ERR_BAD_PARAM;
+  }
+  void* ws = nullptr;
+  int st = scratch_of_current_device(&ws);
+  if (st != DWC_OK) return st;
+  // The automatic split is kept when its partial sums fit the scratch (the
+  // same kernels and summation order as dwc_bwd_filter); otherwise the
+  // largest split whose partials fit is taken (the planners' workspace grows
+  // with the requested split), then, under AUTO, the vector kernels, whose
+  // single slice needs no workspace.  A split the caller asked for is kept
+  // or rejected.
+  dwc_problem d = *p;
+  Plan pl;
+  st = prepare(&d, DWC_OP_BWD_FILTER, &pl, x, dy, dw, ws, kScratchBytes);
+  const size_t first_need = pl.ws_bytes;
+  if (st == DWC_ERR_WORKSPACE && p->wgrad_split == 0) {
+    for (int32_t algo : {p->algo, (int32_t)DWC_ALGO_VECTOR, (int32_t)DWC_ALGO_GENERIC}) {
+      if (algo != p->algo && p->algo != DWC_ALGO_AUTO) break;
+      d = *p;
+      d.algo = algo;
+      int64_t lo = 1, hi = std::max<int64_t>(1, std::min<int64_t>(p->n * p->h, 0x7fffffff));
+      d.wgrad_split = 1;
+      st = prepare(&d, DWC_OP_BWD_FILTER, &pl, x, dy, dw, ws, kScratchBytes);
+      if (st != DWC_OK) continue;
+      while (lo < hi) {  // largest split that still fits
+        const int64_t mid = lo + (hi - lo + 1) / 2;
+        dwc_problem t = d;
+        t.wgrad_split = (int32_t)mid;
+        Plan q;
+        std::string err;
+        if (make_plan(&t, DWC_OP_BWD_FILTER, &q, &err) == DWC_OK && q.ws_bytes <= kScratchBytes)
+          lo = mid;
+        else
+          hi = mid - 1;
+      }
+      d.wgrad_split = (int32_t)lo;
+      st = prepare(&d, DWC_OP_BWD_FILTER, &pl, x, dy, dw, ws, kScratchBytes);
+      if (st == DWC_OK) break;
+    }
+  }
+  if (st == DWC_ERR_WORKSPACE) {
+    set_last_error("the filter gradient needs " + std::to_string(first_need) +
+                   " bytes of partial sums; dwc_bwd_filter_noalloc's fixed scratch holds " +
+                   std::to_string(kScratchBytes) +
+                   " bytes (use dwc_bwd_filter with a caller-owned workspace)");
+    return st;
+  }
+  if (st != DWC_OK) return st;
+  return run_bwd_filter(&d, pl, x, dy, dw, ws, (hipStream_t)stream);
 }
 
 }  // extern "C"

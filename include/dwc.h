@@ -223,6 +223,29 @@ int dwc_bwd_filter(const dwc_problem* p, const void* x, const void* dy,
                    void* dw, void* workspace, size_t workspace_bytes,
                    void* stream);
 
+/* Filter gradient that allocates nothing, for callers that cannot allocate
+ * device memory or pass a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same operation,
+ * arguments and results as dwc_bwd_filter without the workspace: the slice
+ * partials go to a fixed scratch array of DWC_NOALLOC_SCRATCH_BYTES inside
+ * the library, one copy per device, held from the first call on that device
+ * until the process ends.
+ *   - The automatic split (wgrad_split == 0) is used when its partials fit
+ *     the scratch, with the kernels and summation order of dwc_bwd_filter
+ *     (bitwise the same result); otherwise the largest split that fits, then
+ *     (AUTO) the vector kernels, whose single slice needs no scratch.  A
+ *     split the caller sets is used as is.
+ *   - A problem whose partials cannot fit returns DWC_ERR_WORKSPACE before
+ *     anything is launched.
+ *   - Nothing in the scratch needs to start at zero (every partial is
+ *     written before it is read), and a call leaves its partials there.
+ *   - Calls share their device's scratch: two calls that overlap in time on
+ *     one device (different streams, or different threads) race on it and
+ *     give wrong results.  Calls on one stream are ordered and safe. */
+#define DWC_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int dwc_bwd_filter_noalloc(const dwc_problem* p, const void* x, const void* dy,
+                           void* dw, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
