@@ -302,6 +302,8 @@ def kernels_of(dwc, s, op, dtype="f32", algo="auto"):
         if op == "bwd_filter":
             k = f"wgrad_mfma{'8' if dt >= 3 else ''}<{dt}, {kv['nfm']}, {kv['nfn']}, {kv['nk']}, " \
                 f"{kv['pf']}>"
+        elif kv.get("batch") == "1":
+            k = f"fwd_mfma_batch<{dt}, {flip}>"
         elif dt >= 3:
             k = f"fwd_mfma8<{dt}, {kv['nf']}, {kv['tiles']}, {flip}>"
         else:
@@ -406,8 +408,8 @@ def measure_configs(dwc, torch, dev, reps, warmup_ms=50.0):
             plan = [(s, op) for op, a in ops if a == algo]
             sets = build_sets(dwc, torch, plan, inp, dev, algo)
             t1 = time_ops(torch, sets, 3)
-            warm = [int(min(2000, max(5, warmup_ms / max(t, 1e-3)))) for t in t1]
-            time_ops(torch, sets, max(warm))
+            warm = max(int(min(2000, max(5, warmup_ms / max(t, 1e-3)))) for t in t1)
+            time_ops(torch, sets, warm)
             per_op = time_ops(torch, sets, reps)
             for (s_, op), ms in zip(plan, per_op):
                 m = op_model(s_, op, dt)
@@ -423,8 +425,9 @@ def measure_configs(dwc, torch, dev, reps, warmup_ms=50.0):
                     "gbps": round(m["bytes"] / (ms * 1e-3) / 1e9, 1),
                     "roofline_frac": round(m["flops"] / (ms * 1e-3) / m["roofline"], 4),
                     "full_traffic_frac": round(m["flops"] / (ms * 1e-3) / full_peak, 4),
-                    "bound": m["bound"]})
-                log(json.dumps(records[-1]))
+                    "bound": m["bound"], "warm": warm, "reps": reps})
+            log(f"bench: {name} {key} {algo}: " +
+                ", ".join(f"{r['op']} {r['ms'] * 1e3:.1f} us" for r in records[-len(plan):]))
             del sets
         torch.cuda.empty_cache()
     return compact_configs(records), records
@@ -432,21 +435,24 @@ def measure_configs(dwc, torch, dev, reps, warmup_ms=50.0):
 
 def compact_configs(records):
     """The per-configuration entries of the JSON line: for each
-    configuration and case, op (and, for half-precision operands, the
-    vector kernels as op@vector) -> [ms, fraction of the literal roofline];
-    the 36-point filter sweep as per-stage lists over its nine filters."""
+    configuration and case, op -> [microseconds, fraction of the literal
+    roofline]; half-precision cases also on the vector kernels (op@vector);
+    the 36-point filter sweep as per-stage lists over its nine filters.  The
+    fp8 row's vector-kernel times stay in the detail records only."""
     out = {}
     for r in records:
+        if r["algo"] != "auto" and r["config"] == "f4":
+            continue
         op = r["op"] + ("" if r["algo"] == "auto" else "@vector")
-        v = [r["ms"], r["roofline_frac"]]
+        us, fr = round(r["ms"] * 1e3, 1), round(r["roofline_frac"], 3)
         if r["config"] == "c4":
             stage, f = r["case"].split("k")[0], int(r["case"].split("k")[1].split("s")[0])
             d = out.setdefault("c4", {"filters": list(SWEEP_FILTERS)}).setdefault(stage, {})
-            d.setdefault(op + ".ms", []).append(r["ms"])
-            d.setdefault(op + ".frac", []).append(r["roofline_frac"])
-            assert SWEEP_FILTERS[len(d[op + ".ms"]) - 1] == f
+            d.setdefault(op + ".us", []).append(us)
+            d.setdefault(op + ".frac", []).append(fr)
+            assert SWEEP_FILTERS[len(d[op + ".us"]) - 1] == f
         else:
-            out.setdefault(r["config"], {}).setdefault(r["case"], {})[op] = v
+            out.setdefault(r["config"], {}).setdefault(r["case"], {})[op] = [us, fr]
     return out
 
 
@@ -613,22 +619,67 @@ def _kernel_key(name: str, blocks: int) -> str:
     return f"{n}|{blocks}"
 
 
-def _trace_groups(d):
-    """Durations (us) of every traced dispatch, grouped by kernel key, in
-    dispatch order."""
+def _trace_dispatches(d):
+    """(kernel key, duration us) of every traced libdwc dispatch, in
+    dispatch order (the library's kernels run on one stream)."""
     rows = sorted(_csv_rows(os.path.join(d, "trace"), "*kernel_trace.csv"),
                   key=lambda r: int(r["Start_Timestamp"]))
-    g = {}
+    out = []
     for r in rows:
+        if "dwc::" not in r["Kernel_Name"]:
+            continue  # torch's own copies and fills
         blocks = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
-        g.setdefault(_kernel_key(r["Kernel_Name"], blocks), []).append(
-            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    return g
+        out.append((_kernel_key(r["Kernel_Name"], blocks),
+                    (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    return out
 
 
-def _match(groups, spec):
-    """Trace groups that a kernels_of() entry names."""
-    return {k: groups[k] for k in kernel_matches(groups, spec)}
+def _expected_launches(dwc, details):
+    """The library calls of the traced run in order, each as (tag, kernel
+    specs): the headline step loop, its per-op pass, then every
+    configuration group's three passes (3 launches per op, the warm-up,
+    the timed launches), as bench.py issues them."""
+    seq = []
+    s_h = WORKLOADS[HEADLINE]["shapes"][HEADLINE_SHAPE]
+    hk = [(op, kernels_of(dwc, s_h, op, HEADLINE_DTYPE)) for op in HEADLINE_OPS]
+    for _ in range(PROFILE_WARMUP + PROFILE_STEPS):
+        seq += [(None, k) for _, k in hk]
+    for op, k in hk:
+        seq += [(("head", op), k)] * PROFILE_STEPS
+    groups = []
+    for i, r in enumerate(details):
+        key = (r["workload"], r["case"], r["algo"])
+        if not groups or groups[-1][0] != key:
+            groups.append((key, []))
+        groups[-1][1].append(i)
+    for _, idx in groups:
+        for phase in ("t1", "warm", "timed"):
+            for i in idx:
+                r = details[i]
+                n = {"t1": 3, "warm": r["warm"], "timed": r["reps"]}[phase]
+                tag = ("cfg", i) if phase == "timed" else None
+                seq += [(tag, r["kernels"].split("+"))] * n
+    return seq
+
+
+def _align(dispatches, seq):
+    """Per tag, the summed kernel time of each of its launches, walking the
+    traced dispatches against the expected launches (names and launch
+    sizes must agree)."""
+    out, pos = {}, 0
+    for tag, specs in seq:
+        t = 0.0
+        for spec in specs:
+            key, us = dispatches[pos]
+            if not kernel_matches([key], spec):
+                raise RuntimeError(f"trace dispatch {pos} is {key}, expected {spec}")
+            t += us
+            pos += 1
+        if tag is not None:
+            out.setdefault(tag, []).append(t)
+    if pos != len(dispatches):
+        raise RuntimeError(f"{len(dispatches) - pos} traced dispatches left over")
+    return out
 
 
 def summarize_profile(d):
@@ -637,35 +688,29 @@ def summarize_profile(d):
     this benchmark under d."""
     os.makedirs(PROFILES, exist_ok=True)
     cd = "cd /tmp && export TMPDIR=/tmp && "
-    groups = _trace_groups(d)
     traced = None
     for ln in open(os.path.join(d, "trace.log")):
         if ln.startswith("{") and '"metric"' in ln:
             traced = json.loads(ln)
     details = [json.loads(ln) for ln in open(os.path.join(d, "details.jsonl"))]
-    # headline step: the per-op pass launches each op PROFILE_STEPS times
-    # back to back after the step loop; its kernels' last PROFILE_STEPS
-    # dispatches are that pass
-    lines = ["| op | kernel (template arguments), workgroups | calls | avg us (all) | "
-             "avg us (per-op pass) | JSON line `ops.<op>.ms`, us |", "|---|---|---|---|---|---|"]
     import depthwise_convolution_dwc_amd as dwc
+    disp = _trace_dispatches(d)
+    per = _align(disp, _expected_launches(dwc, details))
     s_h = WORKLOADS[HEADLINE]["shapes"][HEADLINE_SHAPE]
+    # headline step: the per-op pass (PROFILE_STEPS launches of each op back
+    # to back) against the JSON line's event times
+    names = {}
+    for k, _ in disp:
+        names.setdefault(k, 0)
+        names[k] += 1
+    lines = ["| op | kernels (template arguments, workgroups) | rocprofv3 avg us, per-op pass | "
+             "JSON line `ops.<op>.ms`, us |", "|---|---|---|---|"]
     for op in HEADLINE_OPS:
         ks = kernels_of(dwc, s_h, op, HEADLINE_DTYPE)
-        tot = 0.0
-        for kp in ks:
-            m = _match(groups, kp)
-            # the headline launches come first: the group with the most
-            # dispatches among same-name keys is the headline shape
-            k = max(m, key=lambda q: len(m[q]))
-            v = m[k]
-            head = v[:PROFILE_WARMUP + 2 * PROFILE_STEPS]
-            pas = float(np.mean(head[-PROFILE_STEPS:]))
-            tot += pas
-            lines.append(f"| {op} | `{k.replace('|', '`, ')} | {len(v)} | {np.mean(v):.2f} | "
-                         f"{pas:.2f} | |")
+        full = [kernel_matches(names, k)[0] for k in ks]
         js = traced["ops"][op]["ms"] * 1e3 if traced else float("nan")
-        lines.append(f"| {op} | sum | | | **{tot:.2f}** | **{js:.2f}** |")
+        lines.append(f"| {op} | {' + '.join('`' + f.replace('|', '`, ') for f in full)} | "
+                     f"{np.mean(per[('head', op)]):.2f} | {js:.2f} |")
     trace_md = f"""# Kernel trace: mixed-precision step, N=128 28x28 C=512 31x31 pad 15, fp16 operands
 
 One benchmark step = forward + data gradient + filter gradient on the same
@@ -685,10 +730,12 @@ Command (repository root `$R`):
 cd $R && python3 bench.py --summarize-profile gpurun_out/prof
 ```
 
-Durations from the dispatch timestamps of `run_kernel_trace.csv`; the last
-two columns compare the kernels' rocprofv3 average over the per-op pass with
-the event time the JSON line printed for that op (under the profiler both
-run a few percent slower than in an unprofiled run):
+Durations from the dispatch timestamps of `run_kernel_trace.csv`, each
+dispatch matched to the launch bench.py issued (kernel name and workgroup
+count checked in order); the last two columns compare the kernels' rocprofv3
+average over the per-op pass with the event time the JSON line printed for
+that op (under the profiler both run a few percent slower than in an
+unprofiled run):
 
 {chr(10).join(lines)}
 
@@ -701,27 +748,16 @@ gradient fragments of FW and FH, 32-column chunks, staging items per thread.
     with open(os.path.join(PROFILES, PROFILE_NAME + ".kernel_trace.md"), "w") as f:
         f.write(trace_md)
 
-    # every per-configuration entry: its kernels' traced durations (the
-    # last PROFILE_REPS dispatches of each at that launch size) beside the
-    # bench's event time
+    # every per-configuration entry: the traced durations of its timed
+    # launches beside the bench's event time
     clines = ["| config | case | op | algo | kernels, workgroups | rocprofv3 avg us | event us | "
               "GFLOP/s | fraction |", "|---|---|---|---|---|---|---|---|---|"]
-    for r in details:
-        parts, tot = [], 0.0
-        for kp in r["kernels"].split("+"):
-            m = _match(groups, kp)
-            if not m:
-                parts.append(f"{kp} (not traced)")
-                continue
-            # several launch sizes share a name: take the one whose traced
-            # average is closest to this record's share of its event time
-            best = min(m, key=lambda q: abs(np.mean(m[q][-PROFILE_REPS:]) - r["ms"] * 1e3))
-            v = float(np.mean(m[best][-PROFILE_REPS:]))
-            tot += v
-            parts.append(f"`{best.replace('|', '`, ')}: {v:.1f}")
+    for i, r in enumerate(details):
+        full = [kernel_matches(names, k)[0] for k in r["kernels"].split("+")]
+        v = float(np.mean(per[("cfg", i)]))
         clines.append(f"| {r['config']} | {r['case']} | {r['op']} | {r['algo']} | "
-                      f"{'; '.join(parts)} | {tot:.1f} | {r['ms'] * 1e3:.1f} | {r['gflops']:.0f} | "
-                      f"{r['roofline_frac']:.3f} |")
+                      f"{'; '.join('`' + f.replace('|', '`, ') for f in full)} | {v:.1f} | "
+                      f"{r['ms'] * 1e3:.1f} | {r['gflops']:.0f} | {r['roofline_frac']:.3f} |")
     cfg_md = f"""# Kernel trace: every per-configuration entry of the benchmark
 
 The same traced run as `{PROFILE_NAME}.kernel_trace.md` (command there).
@@ -729,9 +765,9 @@ Each configuration entry (the five configurations of the target and the
 measured "next" rows) is timed alone, {PROFILE_REPS} launches back to back on
 rotating buffer sets after a warm-up; "event us" is the bench's HIP-event
 time per launch of that entry, "rocprofv3 avg us" the traced durations of
-its kernels over their last {PROFILE_REPS} dispatches at that launch size.
-Kernels that several entries share at one launch size are matched by
-duration.  Fraction: of the literal roofline min(8 TB/s x eta_D / operand
+its kernels summed per launch and averaged over its {PROFILE_REPS} timed
+launches (each traced dispatch matched in order to the launch bench.py
+issued, kernel name and workgroup count checked).  Fraction: of the literal roofline min(8 TB/s x eta_D / operand
 bytes, peak), peak 157.3 TFLOP/s (fp32 operands), 2.5 PFLOP/s (bf16/fp16
 operands), 5.0 PFLOP/s (fp8 operands).
 

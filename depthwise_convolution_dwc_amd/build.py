@@ -46,6 +46,8 @@ def _units():
     # them between registers on every filter-row iteration
     u.append(("hip", "inst_mfma.hip", "inst_mfma.o", ["-mllvm", "-amdgpu-mfma-vgpr-form"]))
     u.append(("hip", "inst_mfma8.hip", "inst_mfma8.o", ["-mllvm", "-amdgpu-mfma-vgpr-form"]))
+    u.append(("hip", "inst_mfma_batch.hip", "inst_mfma_batch.o",
+              ["-mllvm", "-amdgpu-mfma-vgpr-form"]))
     u.append(("hip", "dwc_api.cpp", "dwc_api.o", ["-x", "hip"]))
     u.append(("cxx", "dwc_plan.cpp", "dwc_plan.o", []))
     return u

@@ -172,6 +172,44 @@ struct MfmaArgs {
   uint64_t fw_magic;  // div_magic(FW): filter tap -> (row, column)
 };
 
+// Packed-MFMA forward-type kernel with the batch in the matrix rows (bf16 /
+// fp16 operands, stride 1, input and output widths up to 32): per channel,
+// output row, filter row and 16-column input chunk, one
+// v_mfma_f32_32x32x16 computes 32 images x 32 output columns against the
+// Toeplitz band of the filter row.  A workgroup owns kBatchCb channels (one
+// per wave) x kBatchImg images x kBatchRows output rows.
+constexpr int kBatchCb = 8;
+constexpr int kBatchImg = 32;
+constexpr int kBatchRows = 7;
+// Input rows in flight in LDS (two per barrier), and bytes per staged
+// (channel, chunk, 8-column half) plane -- 32 images x 16 bytes and a
+// 64-byte pad, so that the four planes a wave's staging writes touch start
+// 16 banks apart.
+constexpr int kBatchSlots = 4;
+// Batches of two input rows loaded ahead of the one being staged.
+constexpr int kBatchPrefetch = 1;
+constexpr int kBatchHalfPitch = kBatchImg * 16 + 64;
+constexpr int kBatchMaxCols = 32;
+// AUTO takes the batch-packed kernel from this filter height on; below it
+// the row-packed kernel is faster (13x13 at N=128 28x28 C=512: 111 against
+// 160 us), its matrix cores being idle either way.
+constexpr int kBatchMinFh = 17;
+struct MfmaBatchArgs {
+  const void* in;    // N x IH x IW x C (X, or dY for the data gradient)
+  const void* filt;  // FH x FW x C
+  float* out;        // N x OH x OW x C
+  int N, IH, IW, C, OH, OW;
+  int FH, FW, PH, PW;  // 0 <= PW <= 31, PH >= 0
+  int cb;              // channels per workgroup (one per wave): kBatchCb
+  int rch, cblk, ng;   // row chunks (OH / kBatchRows), channel blocks, image groups
+  int nq;              // input rows streamed per workgroup: kBatchRows + FH - 1
+  int two_rows;        // the whole LDS holds two output rows' staging
+  uint64_t ow_magic;   // div_magic(OW): staged pixel -> (image, column)
+  int lds_bytes;
+  int num_blocks;      // ng * cblk * rch workgroups
+  uint64_t fw_magic;   // div_magic(FW): filter tap -> (row, column)
+};
+
 // out[i] = sum_{z < Z} ws[z * M + j(i)], summed in order of z.  Plain
 // layout (cb = 0): j(i) = i.  Channel-blocked layout (cb > 0, C % cb == 0,
 // out = [tap][c] with C channels): each slice is [c / cb][tap][c % cb], so

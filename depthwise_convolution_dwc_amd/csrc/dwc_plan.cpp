@@ -182,6 +182,54 @@ bool plan_mfma(const FwdArgs& f, int dt, bool flip, Plan* q) {
   return true;
 }
 
+// Packed-MFMA plan with the batch in the matrix rows (bf16 / fp16, stride
+// 1): false if the kernel does not apply.  Input and output widths up to 32
+// (one 32-column output tile, two 16-column input chunks), 0 <= PW <= 31
+// and FW <= 32 (the band rows' zeros), C % 8 == 0 (16-byte channel octets),
+// and a batch of at least 16 images (the matrix rows are images: smaller
+// batches leave most of each instruction idle).
+bool plan_mfma_batch(const FwdArgs& f, int dt, bool flip, Plan* q) {
+  if ((dt != DT_BF16 && dt != DT_F16) || f.SH != 1 || f.SW != 1 || f.C % kBatchCb != 0 ||
+      f.IW > kBatchMaxCols || f.OW > kBatchMaxCols || f.PW < 0 || f.PW > 31 || f.FW > 32 ||
+      f.PH < 0 || f.FH > 64 || f.N < 16)
+    return false;
+  // DWC_MFMA_BATCH: 0 never, 1 wherever it applies (for tests and A/B
+  // timing); unset: from kBatchMinFh filter rows on
+  const char* env = getenv("DWC_MFMA_BATCH");
+  if (env ? atoi(env) == 0 : f.FH < kBatchMinFh) return false;
+  // 32-bit offsets into one image group's input and output
+  if ((int64_t)kBatchImg * f.IH * f.IW * f.C * 2 > kI32Max ||
+      (int64_t)kBatchImg * f.OH * f.OW * f.C > kI32Max)
+    return false;
+  MfmaBatchArgs m{};
+  m.N = f.N; m.IH = f.IH; m.IW = f.IW; m.C = f.C; m.OH = f.OH; m.OW = f.OW;
+  m.FH = f.FH; m.FW = f.FW; m.PH = f.PH; m.PW = f.PW;
+  m.cb = kBatchCb;
+  m.rch = (f.OH + kBatchRows - 1) / kBatchRows;
+  m.cblk = f.C / m.cb;
+  m.ng = (f.N + kBatchImg - 1) / kBatchImg;
+  m.nq = kBatchRows + f.FH - 1;
+  const int64_t band = (int64_t)m.cb * (f.FH + 1) * 64 * 2;
+  const int64_t ring = (int64_t)kBatchSlots * m.cb * 4 * kBatchHalfPitch;
+  const int64_t outs = (int64_t)kBatchImg * f.OW * 12 * 4;  // one output row's staging
+  const int64_t lds = std::max(band + ring, outs);
+  if (lds > kLdsPerCu) return false;
+  m.lds_bytes = (int)lds;
+  m.two_rows = 2 * outs <= lds ? 1 : 0;
+  m.ow_magic = div_magic((uint32_t)f.OW);
+  const int64_t blocks = (int64_t)m.cblk * m.rch * m.ng;
+  if (blocks > kI32Max) return false;
+  m.num_blocks = (int)blocks;
+  m.fw_magic = div_magic((uint32_t)f.FW);
+  q->kind = PLAN_MFMA;
+  q->batch = true;
+  q->flip = flip;
+  q->blocks = (int)blocks;
+  q->mb = m;
+  q->fa = f;
+  return true;
+}
+
 // Packed fp8 MFMA plan of a forward-type problem (e4m3 / e5m2 operands):
 // false if the kernel does not apply.  The tiling of plan_mfma, in bytes:
 // kMfma8Cb channels per workgroup, each 16x16x128 MFMA covering four filter
@@ -519,7 +567,8 @@ int make_plan(const dwc_problem* p, int op, Plan* pl, std::string* err) {
     // Packed MFMA for half-precision operands (the stride-1 data gradient
     // too: stride 1 is part of the kernel's conditions).
     if (p->algo == DWC_ALGO_AUTO || p->algo == DWC_ALGO_MFMA) {
-      if (plan_mfma(f, dt, bwd, &q) || plan_mfma8(f, dt, bwd, &q)) {
+      if (plan_mfma_batch(f, dt, bwd, &q) || plan_mfma(f, dt, bwd, &q) ||
+          plan_mfma8(f, dt, bwd, &q)) {
         *pl = q;
         return DWC_OK;
       }
@@ -789,6 +838,15 @@ std::string describe(const Plan& pl) {
              ops[pl.op], dt_name(pl.dt), w.FW, w.FH, pl.nfm, pl.nfn, pl.nk, pl.pf, pl.cb, w.xr,
              w.xp, w.dyp, w.dpad, w.hx, w.ix, w.e_lo, w.hd, w.id, w.lds_bytes, w.Z, w.ipb,
              w.cblk, pl.blocks, pl.ws_bytes);
+    return buf;
+  }
+  if (pl.kind == PLAN_MFMA && pl.batch) {
+    const MfmaBatchArgs& m = pl.mb;
+    snprintf(buf, sizeof buf,
+             "%s mfma dt=%s fw=%d fh=%d flip=%d batch=1 cb=%d imgs=%d rows=%d ng=%d "
+             "rch=%d cblk=%d nq=%d lds=%d blocks=%d",
+             ops[pl.op], dt_name(pl.dt), m.FW, m.FH, (int)pl.flip, m.cb, kBatchImg, kBatchRows,
+             m.ng, m.rch, m.cblk, m.nq, m.lds_bytes, pl.blocks);
     return buf;
   }
   if (pl.kind == PLAN_MFMA) {

@@ -39,6 +39,9 @@ struct Plan {
   // packed-MFMA forward-type kernel
   int nf = 0, cb = 0, tiles = 0;
   MfmaArgs ma{};
+  // ... with the batch in the matrix rows
+  bool batch = false;
+  MfmaBatchArgs mb{};
   // packed-MFMA filter gradient
   int nfm = 0, nfn = 0, nk = 0, pf = 0;
   WgradMfmaArgs wm{};

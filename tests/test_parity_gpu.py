@@ -425,3 +425,54 @@ def test_nonfinite_operands_vector_kernels(shape, op, dtype):
         fin = np.isfinite(want)
         d = np.abs(got[fin] - want[fin])
         assert np.all(d <= el_bound(op, s, dtype) * mag[fin] + 1e-300), algo
+
+
+# Shapes for the packed-MFMA kernel with the batch in the matrix rows
+# (bf16/fp16, stride 1, input and output widths up to 32, N >= 16): a
+# ragged last image group (N not a multiple of 32), ragged last row chunk
+# (OH not a multiple of 7), the widest input (32 columns), FH != FW, a
+# one-column filter, FW = 32 with PW = 16, several channel blocks, filters
+# taller than the image, and both padding extremes the kernel takes.
+BATCH_SHAPES = [
+    (16, 28, 28, 16, 31, 31, 1, 15),
+    (33, 14, 13, 24, 5, 5, 1, 2),
+    (40, 12, 32, 8, 3, 7, 1, (1, 3)),
+    (20, 20, 20, 16, 13, 13, 1, 6),
+    (16, 9, 30, 8, 9, 1, 1, (4, 0)),
+    (17, 8, 8, 8, 32, 32, 1, 16),
+    (18, 30, 31, 8, 17, 17, 1, 8),
+    (64, 7, 7, 32, 7, 7, 1, 3),
+    (16, 11, 26, 8, 11, 27, 1, (0, 13)),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("op", ["fwd", "bwd_data"])
+@pytest.mark.parametrize("shape", BATCH_SHAPES,
+                         ids=lambda t: "x".join(map(str, t[:6])) + f"_p{t[7]}")
+def test_mfma_batch_parity(shape, op, dtype, monkeypatch):
+    monkeypatch.setenv("DWC_MFMA_BATCH", "1")  # every filter height, not only AUTO's
+    s = _shape(shape)
+    p = dwc.problem(s.n, s.h, s.w, s.c, s.fh, s.fw, 1, (s.pad_h, s.pad_w), dtype=DT[dtype])
+    d = dwc.plan_describe(p, OPS[op])
+    assert " batch=1 " in d, d
+    inp = make_inputs(s, dtype, seed=90 + sum(shape[:6]))
+    want, mag = _want_mag(op, s, inp)
+    log(f"case mfma batch {shape} {op} {dtype}")
+    for algo in ("auto", "mfma"):
+        got = _run(op, s, inp, algo)
+        check_parity(got, want, mag, op, s, dtype, what=algo)
+
+
+def test_mfma_batch_outputs_fully_overwritten(monkeypatch):
+    monkeypatch.setenv("DWC_MFMA_BATCH", "1")
+    s = _shape((33, 14, 13, 24, 5, 5, 1, 2))
+    inp = make_inputs(s, "bf16", seed=91)
+    y = torch.full(s.y_shape(), float("nan"), device="cuda")
+    dwc.fwd(to_device(inp.x), to_device(inp.w), 1, 2, out=y)
+    dx = torch.full(s.x_shape(), float("nan"), device="cuda")
+    dwc.bwd_data(to_device(inp.dy), to_device(inp.w), (14, 13), 1, 2, out=dx)
+    sync()
+    for op, t in (("fwd", y), ("bwd_data", dx)):
+        want, mag = _want_mag(op, s, inp)
+        check_parity(t.double().cpu().numpy(), want, mag, op, s, "bf16", what=op)
