@@ -16,17 +16,20 @@ constexpr int kReduceWaves = 16;
 __global__ __launch_bounds__(64 * kReduceWaves) void reduce_partials(ReduceArgs a) {
   __shared__ float part[kReduceWaves][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t i = (int64_t)blockIdx.x * 64 + lane;
+  // Thread index j runs over the partials' layout, so every slice is read
+  // in whole contiguous rows; i is where element j goes in dW.
+  const int64_t j = (int64_t)blockIdx.x * 64 + lane;
+  int64_t i = j;
+  if (a.cb > 0 && j < a.M) {
+    const int blk_elems = a.taps * a.cb;  // one channel block's partial: [tap][cb]
+    const int cbk = (int)j / blk_elems, rem = (int)j - cbk * blk_elems;
+    const int tap = rem / a.cb, c = cbk * a.cb + rem - tap * a.cb;
+    i = (int64_t)tap * a.C + c;
+  }
   const int z0 = (int)((int64_t)a.Z * wave / kReduceWaves);
   const int z1 = (int)((int64_t)a.Z * (wave + 1) / kReduceWaves);
   float s = 0.f;
-  if (i < a.M) {
-    int64_t j = i;
-    if (a.cb > 0) {
-      const int64_t tap = i / a.C;
-      const int c = (int)(i - tap * a.C);
-      j = ((int64_t)(c / a.cb) * a.taps + tap) * a.cb + c % a.cb;
-    }
+  if (j < a.M) {
     const float* p = a.ws + j;
     // Batches of 8 loads in flight, then their sum in slice order: the same
     // additions as one slice at a time, without a memory latency per slice.
@@ -42,7 +45,7 @@ __global__ __launch_bounds__(64 * kReduceWaves) void reduce_partials(ReduceArgs 
   }
   part[wave][lane] = s;
   __syncthreads();
-  if (wave == 0 && i < a.M) {
+  if (wave == 0 && j < a.M) {
     float t = 0.f;
 #pragma unroll
     for (int w = 0; w < kReduceWaves; ++w) t += part[w][lane];

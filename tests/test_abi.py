@@ -164,9 +164,23 @@ def test_mfma_plans_and_rejections():
     assert dwc.plan_describe(p, 0).startswith("fwd mfma")
     assert dwc.plan_describe(p, 1).startswith("bwd_data mfma")
     assert dwc.plan_describe(p, 2).startswith("bwd_filter mfma")
+    # 13x13: the row-packed kernel; 31x31: the batch-packed kernel (AUTO
+    # takes it from 17 filter rows on, with N >= 16 and widths up to 32)
+    assert " batch=1 " not in dwc.plan_describe(p, 0)
     p = dwc.problem(128, 28, 28, 512, 31, 31, 1, 15, dtype=dwc.F16)
     d = dwc.plan_describe(p, 0)
-    assert d.startswith("fwd mfma") and "nf=2" in d
+    assert d.startswith("fwd mfma") and " batch=1 " in d and "ng=4" in d
+    assert " batch=1 " in dwc.plan_describe(p, 1)
+    for kw in (dict(n=8), dict(w=40)):
+        a = dict(n=128, w=28, pad=15, **{})
+        a.update(kw)
+        q = dwc.problem(a["n"], 28, a["w"], 512, 31, 31, 1, a["pad"], dtype=dwc.F16)
+        d = dwc.plan_describe(q, 0)
+        assert d.startswith("fwd mfma") and " batch=1 " not in d, (kw, d)
+    q = dwc.problem(128, 28, 28, 512, 31, 31, 1, 15, dtype=dwc.F16)
+    q2 = dwc.problem(128, 28, 28, 512, 31, 15, 1, (15, 7), dtype=dwc.F16)
+    assert " batch=1 " in dwc.plan_describe(q2, 0)  # FH decides, not FW
+    del q
     d = dwc.plan_describe(p, 2)
     assert d.startswith("bwd_filter mfma") and "nfm=2" in d and "nfn=2" in d
     # the vector kernels stay reachable
