@@ -231,6 +231,46 @@ def time_ops(torch, calls_per_set, reps):
     return per_op
 
 
+def time_ops_graph(torch, calls_per_set, reps):
+    """time_ops() without the host: the `reps` launches of each op are
+    captured once in a HIP graph (on rotating buffer sets, as above) and the
+    graph is replayed between two events, so short kernels are not timed at
+    the rate the host can issue them.  The graph's last output of one set
+    must equal an eager launch's bit for bit (the library is deterministic).
+    Returns (per-op ms, "graph"), or time_ops() and "eager" if a capture is
+    refused."""
+    nsets = len(calls_per_set)
+    per_op = []
+    try:
+        for j in range(len(calls_per_set[0])):
+            g = torch.cuda.CUDAGraph()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                for i in range(reps):
+                    calls_per_set[i % nsets][j]()
+            g.replay()  # warm
+            torch.cuda.synchronize()
+            start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            start.record()
+            g.replay()
+            end.record()
+            torch.cuda.synchronize()
+            per_op.append(start.elapsed_time(end) / reps)
+            last = calls_per_set[(reps - 1) % nsets][j]
+            got = last.out.clone()
+            last()
+            torch.cuda.synchronize()
+            if not torch.equal(got, last.out):
+                raise RuntimeError("graph replay differs from an eager launch")
+            del g
+        return per_op, "graph"
+    except RuntimeError as e:
+        if "differs" in str(e):
+            raise
+        log(f"bench: graph capture refused ({e}); timing eager launches")
+        return time_ops(torch, calls_per_set, reps), "eager"
+
+
 # ---------------------------------------------------------- CPU oracle ------
 
 def cpu_baseline(inp, plan, budget_s=12.0):
@@ -303,7 +343,7 @@ def kernels_of(dwc, s, op, dtype="f32", algo="auto"):
             k = f"wgrad_mfma{'8' if dt >= 3 else ''}<{dt}, {kv['nfm']}, {kv['nfn']}, {kv['nk']}, " \
                 f"{kv['pf']}>"
         elif kv.get("batch") == "1":
-            k = f"fwd_mfma_batch<{dt}, {flip}>"
+            k = f"fwd_mfma_batch<{dt}, {kv['cb']}, {flip}>"
         elif dt >= 3:
             k = f"fwd_mfma8<{dt}, {kv['nf']}, {kv['tiles']}, {flip}>"
         else:
@@ -410,7 +450,7 @@ def measure_configs(dwc, torch, dev, reps, warmup_ms=50.0):
             t1 = time_ops(torch, sets, 3)
             warm = max(int(min(2000, max(5, warmup_ms / max(t, 1e-3)))) for t in t1)
             time_ops(torch, sets, warm)
-            per_op = time_ops(torch, sets, reps)
+            per_op, how = time_ops_graph(torch, sets, reps)
             for (s_, op), ms in zip(plan, per_op):
                 m = op_model(s_, op, dt)
                 tag, key = config_label(name, s_, dt)
@@ -425,7 +465,7 @@ def measure_configs(dwc, torch, dev, reps, warmup_ms=50.0):
                     "gbps": round(m["bytes"] / (ms * 1e-3) / 1e9, 1),
                     "roofline_frac": round(m["flops"] / (ms * 1e-3) / m["roofline"], 4),
                     "full_traffic_frac": round(m["flops"] / (ms * 1e-3) / full_peak, 4),
-                    "bound": m["bound"], "warm": warm, "reps": reps})
+                    "bound": m["bound"], "warm": warm, "reps": reps, "timing": how})
             log(f"bench: {name} {key} {algo}: " +
                 ", ".join(f"{r['op']} {r['ms'] * 1e3:.1f} us" for r in records[-len(plan):]))
             del sets
@@ -634,6 +674,16 @@ def _trace_dispatches(d):
     return out
 
 
+def case_shape(workload, case):
+    """(Shape, dtype) of a per-configuration entry's case key."""
+    wl = WORKLOADS[workload]
+    for sh in wl["shapes"]:
+        for dt in wl["dtypes"]:
+            if config_label(workload, sh, dt)[1] == case:
+                return sh, dt
+    raise KeyError((workload, case))
+
+
 def _expected_launches(dwc, details):
     """The library calls of the traced run in order, each as (tag, kernel
     specs): the headline step loop, its per-op pass, then every
@@ -653,12 +703,18 @@ def _expected_launches(dwc, details):
             groups.append((key, []))
         groups[-1][1].append(i)
     for _, idx in groups:
-        for phase in ("t1", "warm", "timed"):
+        for phase in ("t1", "warm"):
             for i in idx:
                 r = details[i]
-                n = {"t1": 3, "warm": r["warm"], "timed": r["reps"]}[phase]
-                tag = ("cfg", i) if phase == "timed" else None
-                seq += [(tag, r["kernels"].split("+"))] * n
+                n = {"t1": 3, "warm": r["warm"]}[phase]
+                seq += [(None, r["kernels"].split("+"))] * n
+        for i in idx:  # per op: a graph replayed twice (the second timed), one eager check
+            r = details[i]
+            k = r["kernels"].split("+")
+            if r.get("timing") == "graph":
+                seq += [(None, k)] * r["reps"] + [(("cfg", i), k)] * r["reps"] + [(None, k)]
+            else:
+                seq += [(("cfg", i), k)] * r["reps"]
     return seq
 
 
@@ -694,6 +750,9 @@ def summarize_profile(d):
             traced = json.loads(ln)
     details = [json.loads(ln) for ln in open(os.path.join(d, "details.jsonl"))]
     import depthwise_convolution_dwc_amd as dwc
+    for r in details:  # the kernels each entry launches, from its plan
+        s_r, dt_r = case_shape(r["workload"], r["case"])
+        r["kernels"] = "+".join(kernels_of(dwc, s_r, r["op"], dt_r, r["algo"]))
     disp = _trace_dispatches(d)
     per = _align(disp, _expected_launches(dwc, details))
     s_h = WORKLOADS[HEADLINE]["shapes"][HEADLINE_SHAPE]
@@ -762,9 +821,11 @@ gradient fragments of FW and FH, 32-column chunks, staging items per thread.
 
 The same traced run as `{PROFILE_NAME}.kernel_trace.md` (command there).
 Each configuration entry (the five configurations of the target and the
-measured "next" rows) is timed alone, {PROFILE_REPS} launches back to back on
-rotating buffer sets after a warm-up; "event us" is the bench's HIP-event
-time per launch of that entry, "rocprofv3 avg us" the traced durations of
+measured "next" rows) is timed alone: {PROFILE_REPS} launches on rotating
+buffer sets, captured in a HIP graph that is replayed between two events
+after a warm-up (so short kernels are not timed at the rate the host
+issues them); "event us" is the bench's HIP-event time per launch of that
+entry, "rocprofv3 avg us" the traced durations of
 its kernels summed per launch and averaged over its {PROFILE_REPS} timed
 launches (each traced dispatch matched in order to the launch bench.py
 issued, kernel name and workgroup count checked).  Fraction: of the literal roofline min(8 TB/s x eta_D / operand
@@ -801,18 +862,6 @@ operands), 5.0 PFLOP/s (fp8 operands).
            "kernels": kernels}
     with open(os.path.join(PROFILES, "traffic.json"), "w") as f:
         json.dump(out, f, indent=1, sort_keys=True)
-    # algorithmic bytes of each traced configuration's kernels, for the table
-    alg = {}
-    for r in details:
-        s = None
-        for name, wl in WORKLOADS.items():
-            for sh in wl["shapes"]:
-                for dt in wl["dtypes"]:
-                    if config_label(name, sh, dt)[1] == r["case"] and name == r["workload"]:
-                        s, dtt = sh, dt
-        if s is not None:
-            alg[(r["kernels"].split("+")[0], r["case"], r["op"], r["algo"])] = \
-                op_model(s, r["op"], dtt)["bytes"]
     tl = ["| kernel, workgroups | FETCH bytes/launch | WRITE bytes/launch | total |",
           "|---|---|---|---|"]
     for k, e in kernels.items():
