@@ -650,6 +650,9 @@ PROFILE_CMDS = {
              "-- python3 $R/bench.py --copy-calibration",
     "copyw": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof/copyw -o run "
              "-- python3 $R/bench.py --copy-calibration",
+    "sq": "rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_WAVES SQ_BUSY_CYCLES "
+          "SQ_VALU_MFMA_BUSY_CYCLES SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_LDS --output-format csv "
+          f"-d $R/gpurun_out/prof/sq -o run -- {_BENCH} --no-configs --steps 5 --warmup 2",
 }
 
 
@@ -915,6 +918,47 @@ The same numbers are in `traffic.json`, which `bench.py` reads for the
 """
     with open(os.path.join(PROFILES, PROFILE_NAME + ".hbm_traffic.md"), "w") as f:
         f.write(traffic_md)
+
+    # SQ counters of the step's kernels: per-wave instruction mix, matrix-core
+    # busy fraction and LDS bank conflicts
+    sq = {}
+    for r in _csv_rows(os.path.join(d, "sq"), "*counter_collection.csv"):
+        if "dwc::" not in r["Kernel_Name"]:
+            continue
+        blocks = int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"]))
+        key = _kernel_key(r["Kernel_Name"], blocks)
+        sq.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    sl = ["| kernel, workgroups | VALU / wave | MFMA / wave | LDS / wave | matrix cores busy | "
+          "LDS bank-conflict cycles / LDS active cycles |", "|---|---|---|---|---|---|"]
+    for key, c in sorted(sq.items()):
+        m = {k: float(np.mean(v)) for k, v in c.items()}
+        w = max(m.get("SQ_WAVES", 1.0), 1.0)
+        # SQ_BUSY_CYCLES sums the shader engines (32 on MI355X, 8 CUs each);
+        # SQ_VALU_MFMA_BUSY_CYCLES sums the SIMDs (1024)
+        busy = m.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / 1024 / max(m["SQ_BUSY_CYCLES"] / 32, 1.0)
+        conf = m.get("SQ_LDS_BANK_CONFLICT", 0.0) / max(m.get("SQ_ACTIVE_INST_LDS", 1.0), 1.0)
+        sl.append(f"| `{key.replace('|', '`, ')} | {m['SQ_INSTS_VALU'] / w:.0f} | "
+                  f"{m['SQ_INSTS_MFMA'] / w:.0f} | {m['SQ_INSTS_LDS'] / w:.0f} | {busy:.2f} | "
+                  f"{conf:.2f} |")
+    sq_md = f"""# SQ counters: mixed-precision step, N=128 28x28 C=512 31x31 pad 15, fp16 operands
+
+Per-wave instruction counts (each counter averaged over the dispatches of a
+kernel and divided by `SQ_WAVES`), the fraction of the launch the matrix
+cores were busy (`SQ_VALU_MFMA_BUSY_CYCLES` per SIMD over `SQ_BUSY_CYCLES`
+per shader engine) and LDS bank-conflict cycles relative to LDS active
+cycles, for the default benchmark step's kernels.
+
+Command (repository root `$R`):
+
+```
+{cd}{PROFILE_CMDS["sq"]}
+cd $R && python3 bench.py --summarize-profile gpurun_out/prof
+```
+
+{chr(10).join(sl)}
+"""
+    with open(os.path.join(PROFILES, PROFILE_NAME + ".sq_counters.md"), "w") as f:
+        f.write(sq_md)
     print(trace_md)
     print(traffic_md)
 
