@@ -211,6 +211,31 @@ int scratch_of_current_device(void** out) {
   return DWC_OK;
 }
 
+// Compute units per device, read once per device (the planner's fill
+// targets scale with them: a partitioned GPU shows fewer).
+std::once_flag g_cus_once[kMaxDevices];
+int g_cus[kMaxDevices];
+
+int current_device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();  // no device: the planner's default
+    return 0;
+  }
+  std::call_once(g_cus_once[dev], [dev] {
+    int v = 0;
+    g_cus[dev] = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) ==
+                         hipSuccess
+                     ? v
+                     : 0;
+  });
+  return g_cus[dev];
+}
+
+struct InstallCusHook {
+  InstallCusHook() { set_device_cus_hook(current_device_cus); }
+} g_install_cus_hook;
+
 }  // namespace
 
 extern "C" {

@@ -14,11 +14,9 @@ namespace dwc {
 namespace {
 
 thread_local std::string g_last_error;
+int (*g_cus_hook)() = nullptr;
 
 constexpr int64_t kI32Max = 0x7fffffff;
-// Fill target of the filter-gradient split: waves in flight on 256 CUs at
-// about four waves per SIMD.
-constexpr int64_t kWgradTargetWaves = 4096;
 
 int elem_bytes(int dt) { return dt == DT_F32 ? 4 : dt == DT_BF16 || dt == DT_F16 ? 2 : 1; }
 
@@ -77,7 +75,7 @@ int strip_override(const char* var, int fallback) {
 // halo rows).
 int64_t sweep_chunks(int64_t waves_per_chunk, int64_t out_h, int f) {
   const int64_t w = std::max<int64_t>(waves_per_chunk, 1);
-  int64_t target = 2048;
+  int64_t target = 8 * (int64_t)device_cus();  // two waves per SIMD
   if (const char* v = getenv("DWC_SWEEP_WAVES")) target = std::max(1, atoi(v));
   const int64_t cpi = std::max<int64_t>(1, (target + w - 1) / w);
   return std::min<int64_t>(cpi, std::max<int64_t>(1, out_h / f));
@@ -91,7 +89,8 @@ int64_t sweep_chunks(int64_t waves_per_chunk, int64_t out_h, int f) {
 // estimated time.
 int pick_split(int64_t rows, int64_t per_slice_blocks, int64_t strips, int64_t m, double flops,
                double bytes) {
-  const int64_t fill = (1024 + per_slice_blocks - 1) / per_slice_blocks;
+  const int64_t target = 4 * (int64_t)device_cus();  // ~4 workgroups per CU
+  const int64_t fill = (target + per_slice_blocks - 1) / per_slice_blocks;
   const int64_t groups_per_wave_set = (4 + strips - 1) / strips;  // row groups for 4 units
   const int64_t by_units = std::max<int64_t>(1, rows / (kWgradRows * groups_per_wave_set));
   const double t_est = std::max(flops / 100e12, bytes / 5e12);
@@ -348,7 +347,7 @@ bool plan_wgrad_mfma(const dwc_problem* p, int64_t oh, int64_t ow, Plan* q) {
   // fixed cost per round) is least, preferring fewer slices.
   const int64_t per_cu = std::max<int64_t>(
       1, std::min<int64_t>(kLdsPerCu / lds, wgm_waves_per_eu(nfm, nfn, nk, pf) / 2));
-  const int64_t resident = kCus * per_cu;
+  const int64_t resident = (int64_t)device_cus() * per_cu;
   const int64_t nn = std::max<int64_t>(p->n, 1);  // an empty batch only zero-fills dW
   int64_t z = 1;
   if (p->wgrad_split > 0) {
@@ -426,7 +425,7 @@ bool plan_wgrad_mfma8(const dwc_problem* p, int64_t oh, int64_t ow, Plan* q) {
   // slices of whole images, chosen as in plan_wgrad_mfma
   const int64_t per_cu =
       std::max<int64_t>(1, std::min<int64_t>(kLdsPerCu / lds, wgm8_waves_per_eu(pf) / 2));
-  const int64_t resident = kCus * per_cu;
+  const int64_t resident = (int64_t)device_cus() * per_cu;
   const int64_t nn = std::max<int64_t>(p->n, 1);
   int64_t z = 1;
   if (p->wgrad_split > 0) {
@@ -464,6 +463,13 @@ bool plan_wgrad_mfma8(const dwc_problem* p, int64_t oh, int64_t ow, Plan* q) {
 }  // namespace
 
 void set_last_error(const std::string& msg) { g_last_error = msg; }
+
+void set_device_cus_hook(int (*hook)()) { g_cus_hook = hook; }
+
+int device_cus() {
+  const int c = g_cus_hook ? g_cus_hook() : 0;
+  return c > 0 ? c : kCus;
+}
 
 // Checks of the problem itself, shared by every entry point (not which
 // kernel would run it); on success *oh_out, *ow_out are the output dims.

@@ -72,4 +72,11 @@ std::string describe(const Plan& pl);
 
 void set_last_error(const std::string& msg);
 
+// Compute units of the device the calls run on, which the planner's fill
+// targets scale with: read once per device by the HIP side of the library
+// (through the hook it installs when the library loads); MI355X's 256 when
+// no device is visible (planning on a host without a GPU).
+int device_cus();
+void set_device_cus_hook(int (*hook)());
+
 }  // namespace dwc
