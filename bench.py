@@ -801,11 +801,12 @@ unprofiled run):
 
 {chr(10).join(lines)}
 
-`fwd_mfma<2, 2, 8, 4, true>` is the data gradient (the packed forward on dY
-with the filter turned by 180 degrees); the filter gradient is `wgrad_mfma`
-followed by `reduce_partials`.  Template arguments: operand dtype (2 = fp16),
-16-tap filter fragments, channels per workgroup, tiles; for the filter
-gradient fragments of FW and FH, 32-column chunks, staging items per thread.
+The data gradient is the forward kernel on dY with the filter turned by
+180 degrees (`FLIP` = true); the filter gradient is `wgrad_mfma` followed by
+`reduce_partials`.  Template arguments: `fwd_mfma_batch` operand dtype
+(2 = fp16), channels per workgroup, FLIP; `fwd_mfma` dtype, 16-tap filter
+fragments, channels per workgroup, tiles, FLIP; `wgrad_mfma` dtype, 16-tap
+fragments of FW and FH, 32-column chunks, staging items per thread.
 """
     with open(os.path.join(PROFILES, PROFILE_NAME + ".kernel_trace.md"), "w") as f:
         f.write(trace_md)

@@ -38,9 +38,10 @@
 //     of the rate);
 //   * outputs pass through LDS, one output row at a time, so that global
 //     stores are channel-contiguous 16-byte writes.
-// A workgroup keeps its channels' band for every image group of the batch
-// (it loops over them), and the next group's first rows load while the
-// current group's outputs are written.
+// A workgroup computes one image group of 32 (a loop over several groups
+// made the compiler keep per-group offsets live across the row loop and
+// spill).  Its LDS (the band and four row slots: 92-104 KB from 17 to 31
+// filter rows) and registers leave room for one workgroup per CU.
 // Zero padding: staged columns and images past the input read 0 through
 // the buffer resource's range check; padding rows are never staged nor
 // multiplied.
