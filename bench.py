@@ -342,6 +342,8 @@ def kernels_of(dwc, s, op, dtype="f32", algo="auto"):
         if op == "bwd_filter":
             k = f"wgrad_mfma{'8' if dt >= 3 else ''}<{dt}, {kv['nfm']}, {kv['nfn']}, {kv['nk']}, " \
                 f"{kv['pf']}>"
+        elif kv.get("batch") == "1" and kv.get("imgs") == "16":
+            k = f"fwd_mfma_batch16<{dt}, {kv['ocg']}, {flip}>"
         elif kv.get("batch") == "1":
             k = f"fwd_mfma_batch<{dt}, {kv['cb']}, {flip}>"
         elif dt >= 3:

@@ -39,6 +39,7 @@ hipError_t launch_fwd_type(const Plan& pl, const void* in, const void* filt, flo
     m.in = in;
     m.filt = filt;
     m.out = out;
+    if (pl.bimg == kB16Img) return launch_fwd_mfma_batch16(pl.dt, pl.bng, pl.flip, m, s);
     return launch_fwd_mfma_batch(pl.dt, pl.flip, m, s);
   }
   if (pl.kind == PLAN_MFMA) {

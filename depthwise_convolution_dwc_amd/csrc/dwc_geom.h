@@ -194,6 +194,20 @@ constexpr int kBatchMaxCols = 32;
 // the row-packed kernel is faster (13x13 at N=128 28x28 C=512: 111 against
 // 160 us), its matrix cores being idle either way.
 constexpr int kBatchMinFh = 17;
+// The same packing with 16 images per v_mfma_f32_16x16x32 and two channels
+// per wave: a workgroup owns kB16Cb channels x kB16Img images x kB16Rows
+// output rows.  Staged rows: per channel, 4 column groups of 16 images x 16
+// bytes; the pitches (kB16KqPitch bytes per column group, kB16ChPitch per
+// channel) put the 64 dword writes of one staging instruction on 64
+// different banks.  Staged outputs: kB16Opitch floats per pixel (16
+// channels and a pad that keeps every pixel 16-byte aligned).
+constexpr int kB16Cb = 16;
+constexpr int kB16Img = 16;
+constexpr int kB16Rows = 7;
+constexpr int kB16Slots = 4;
+constexpr int kB16KqPitch = kB16Img * 16 + 32;
+constexpr int kB16ChPitch = 4 * kB16KqPitch + 16;
+constexpr int kB16Opitch = 20;
 struct MfmaBatchArgs {
   const void* in;    // N x IH x IW x C (X, or dY for the data gradient)
   const void* filt;  // FH x FW x C
@@ -204,6 +218,7 @@ struct MfmaBatchArgs {
   int rch, cblk, ng;   // row chunks (OH / kBatchRows), channel blocks, image groups
   int nq;              // input rows streamed per workgroup: kBatchRows + FH - 1
   int two_rows;        // the whole LDS holds two output rows' staging
+  int orows;           // output rows staged per round (16-image kernel)
   uint64_t ow_magic;   // div_magic(OW): staged pixel -> (image, column)
   int lds_bytes;
   int num_blocks;      // ng * cblk * rch workgroups

@@ -39,6 +39,10 @@ hipError_t launch_fwd_mfma(int dt, int nf, int tiles, bool flip, const MfmaArgs&
 // Packed-MFMA forward-type kernel with the batch in the matrix rows (bf16 /
 // fp16 operands, stride 1, widths up to 32).
 hipError_t launch_fwd_mfma_batch(int dt, bool flip, const MfmaBatchArgs& a, hipStream_t s);
+// ... with 16 images per instruction and two channels per wave (ng output
+// column groups of 16).
+hipError_t launch_fwd_mfma_batch16(int dt, int ng, bool flip, const MfmaBatchArgs& a,
+                                   hipStream_t s);
 
 // Packed fp8 MFMA forward-type kernel (e4m3 / e5m2 operands, stride 1,
 // 16x16x128 MFMAs over four filter rows each): nf 16-tap fragments per

@@ -1,0 +1,285 @@
+// dwc_mfma_batch16.h -- packed-MFMA forward-type kernel of libdwc with 16
+// images in the matrix rows and two channels per wave (bf16/fp16 operands,
+// gfx950 v_mfma_f32_16x16x32_{bf16,f16}, fp32 accumulation).
+//
+// The same packing as fwd_mfma_batch (Flash-DWC §4.2, Fig. 8, with the
+// batch as the second matrix dimension): for one output row oh, one filter
+// row fh and the input row r = oh + fh - PH,
+//   A[i][k] = x[n0 + i][r][k]                        (16 images x 32 input columns)
+//   B[k][j] = w[fh][k - (16 g + j) + PW]  (0 <= . < FW, else 0)   (32 x 16 output columns)
+//   D[i][j] += sum_k A[i][k] B[k][j]
+// accumulates output column 16 g + j of row oh for 16 images; NG = 1 or 2
+// column groups cover output widths up to 16 or 32.  K = 32 covers the
+// whole input row (widths up to 32), so one A per staged row and channel.
+//
+// Why 16 images and 16 channels per workgroup instead of 32 x 8: a
+// workgroup's global loads and stores touch one 128-byte line per pixel
+// whatever part of it they use.  With 16 channels (32 bytes of a pixel)
+// the loads and stores of one output row touch half as many lines as with
+// 8 channels, at the same register cost: a wave holds two channels' 16
+// images where the 32-image kernel holds one channel's 32.
+//
+// A workgroup owns 16 channels (two per wave) x 16 images x R output rows;
+// the R rows at filter row fh read stream rows fh .. fh + R - 1, so each
+// channel keeps a ring of R A registers that takes one new row per filter
+// row (nothing moves between lanes), and the band B of (channel, fh, g) is
+// read once per filter row and serves all R output rows.
+//
+// Operand staging (LDS):
+//   * input rows stream through kB16Slots row slots, two rows per barrier,
+//     the next two rows' global loads in flight during the current rows'
+//     MFMAs.  A slot holds, per channel and 8-column group q, the 16
+//     images' 8 columns: lane (q, i) of the A read takes 16 contiguous
+//     bytes.  Thread (image, column pair p, channel half h) loads the two
+//     pixels' 8 channels (16 bytes each; the two halves of a pixel are
+//     neighbouring lanes, one 32-byte piece of the line) and writes 8
+//     dwords of column pairs.  The pitches put the 64 dword writes of one
+//     instruction on 64 different banks;
+//   * the filter band, as in fwd_mfma_batch: per channel and filter row, 32
+//     zeros, the FW taps (turned by 180 degrees for FLIP) and 32 - FW zeros;
+//     the next row's leading zeros end the row.  Lane (q, j) of column
+//     group g needs elements e = 32 + 8 q - 16 g - j + PW .. e + 7, read as
+//     5 aligned dwords and shifted by v_alignbit;
+//   * outputs pass through LDS, as many rows at a time as the LDS holds, so
+//     that global stores are 16-byte writes of 64-byte pixel pieces.
+// Zero padding: staged columns and images past the input read 0 through
+// the buffer resource's range check; padding rows are never staged nor
+// multiplied.
+#pragma once
+
+#include "dwc_device.h"
+#include "dwc_mfma.h"
+
+namespace dwc {
+
+template <int DT, int NG, bool FLIP>
+__global__ __launch_bounds__(512, 1) void fwd_mfma_batch16(MfmaBatchArgs a) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  constexpr int NT = 512;
+  constexpr int CB = kB16Cb;                   // 16 channels, two per wave
+  constexpr int R = kB16Rows;
+  constexpr int ZROW = 64;                      // band elements per filter row
+  constexpr int KQP = kB16KqPitch;              // bytes per (channel, 8-column group)
+  constexpr int CHP = kB16ChPitch;              // bytes per channel in a staged row
+  constexpr int SLOT = CB * CHP;                // bytes per staged input row
+  constexpr int OPITCH = kB16Opitch;            // floats per staged output pixel
+  const int tid = threadIdx.x;
+  const int wave = uniform(tid >> 6);
+  const int lane = tid & 63;
+  const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
+  if (blk >= a.num_blocks) return;  // the whole workgroup leaves together
+  // Workgroup (channel block, row chunk, image group); logical ids run over
+  // groups of gw channel blocks first (64 channels: whole lines of each
+  // pixel), then row chunks, so that the workgroups an XCD holds at once
+  // read the same input rows and write whole output lines.
+  int t = blk;
+  const int gw = a.cblk % (64 / CB) == 0 ? 64 / CB : 1;
+  const int cbg = t % gw;
+  t /= gw;
+  const int rc = t % a.rch;
+  t /= a.rch;
+  const int ncg = a.cblk / gw;
+  const int cbk = (t % ncg) * gw + cbg;
+  const int ig = t / ncg;
+  const int n0 = ig * kB16Img;
+  const int c0 = cbk * CB, oh0 = rc * R;
+  const int FH = a.FH, FW = a.FW;
+  const int zrows = FH + 1;                     // one zero row after the last
+  uint16_t* zt = (uint16_t*)lds;                // [CB ch][FH + 1][ZROW]
+  unsigned char* ring = lds + CB * zrows * ZROW * 2;  // kB16Slots staged rows
+
+  // ---- filter band: zero it, then write the taps after a barrier
+  const int zlen8 = CB * zrows * ZROW / 8;
+  for (int i = tid; i < zlen8; i += NT) ((mf_u32x4*)zt)[i] = mf_u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
+  {
+    const auto frsrc = make_rsrc(a.filt, (uint32_t)(FH * FW) * (uint32_t)a.C * 2u);
+    const int ftaps = FH * FW;
+    for (int te = tid; te < 2 * ftaps; te += NT) {
+      const int hf = te & 1, tap = te >> 1;     // channel half, tap
+      const int src = FLIP ? ftaps - 1 - tap : tap;
+      const mf_u32x4 v = __builtin_bit_cast(
+          mf_u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                        frsrc, (int)(((uint32_t)src * (uint32_t)a.C + (uint32_t)(c0 + 8 * hf)) * 2u),
+                        0, 0));
+      const int fh = fast_div(tap, a.fw_magic), fw = tap - fh * FW;
+      uint16_t* d = zt + (8 * hf * zrows + fh) * ZROW + 32 + fw;
+#pragma unroll
+      for (int j = 0; j < 8; ++j, d += zrows * ZROW)
+        *d = (uint16_t)((v[j >> 1] >> (16 * (j & 1))) & 0xffffu);
+    }
+  }
+
+  // ---- staging of input rows: thread (image si, column pair sp, channel
+  // half sh), tid = (si * 16 + sp) * 2 + sh.  One buffer resource over the
+  // image group (wave-uniform); an item's image is part of its offset, and
+  // images past N fall outside the range.
+  const uint32_t Cb = (uint32_t)a.C * 2u;
+  const int sh = tid & 1, sp = (tid >> 1) & 15, si = tid >> 5;
+  const uint32_t img_bytes = (uint32_t)(a.IH * a.IW) * Cb;
+  const int scol = 2 * sp;
+  const bool ok0 = scol < a.IW, ok1 = scol + 1 < a.IW;
+  const uint32_t scoff = (uint32_t)si * img_bytes +
+                         ((uint32_t)scol * (uint32_t)a.C + (uint32_t)(c0 + 8 * sh)) * 2u;
+  // staged element (ch, col = 8 q + e, image i) sits at byte
+  // ch * CHP + q * KQP + i * 16 + e * 2; the item writes the dword of
+  // columns (scol, scol + 1) of each of its 8 channels
+  const int s_dst = 8 * sh * CHP + (sp >> 2) * KQP + si * 16 + (sp & 3) * 4;
+  const int r_base = oh0 - a.PH;  // image row of stream row q = 0
+  auto row_ok = [&](int q) { return q < a.nq && (unsigned)(r_base + q) < (unsigned)a.IH; };
+  const auto rs = make_rsrc((const char*)a.in + (size_t)n0 * img_bytes,
+                            (uint32_t)min(kB16Img, a.N - n0) * img_bytes);
+  struct Stage {
+    mf_u32x4 v0, v1;
+  };
+  auto stage_load = [&](int q, Stage& st) {
+    const bool rok = row_ok(q);
+    const uint32_t o = (uint32_t)(r_base + q) * (uint32_t)a.IW * Cb + scoff;
+    st.v0 = __builtin_bit_cast(
+        mf_u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(rok && ok0 ? o : kOOB), 0, 0));
+    st.v1 = __builtin_bit_cast(
+        mf_u32x4,
+        __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(rok && ok1 ? o + Cb : kOOB), 0, 0));
+  };
+  auto stage_store = [&](int q, const Stage& st) {
+    if (!row_ok(q)) return;  // a padding row is never read
+    unsigned char* d = ring + (q % kB16Slots) * SLOT + s_dst;
+#pragma unroll
+    for (int j = 0; j < 8; ++j, d += CHP)
+      *(uint32_t*)d = __builtin_amdgcn_perm(st.v1[j >> 1], st.v0[j >> 1],
+                                            (j & 1) ? 0x07060302u : 0x05040100u);
+  };
+
+  // ---- compute operands.  A: lane (q, i) reads the 16 bytes of image i,
+  // column group q of a staged row.  B: lane (q, j) of column group g
+  // starts at element e = 32 + 8 q - 16 g - j + PW of its channel's band
+  // row.  D: lane (q, j) holds images 4 q .. 4 q + 3 at column 16 g + j.
+  const int lq = lane >> 4, lm = lane & 15;
+  const int a_lane = 2 * wave * CHP + lq * KQP + lm * 16;
+  auto read_a = [&](int q, int cc) -> mf_u32x4 {
+    return *(const mf_u32x4*)(ring + (q % kB16Slots) * SLOT + a_lane + cc * CHP);
+  };
+  const int e0 = 32 + 8 * lq - lm + a.PW;        // element of column group 0
+  const uint32_t bshift = (uint32_t)(e0 & 1) * 16u;
+  const uint32_t* zrow0 = (const uint32_t*)(zt + 2 * wave * zrows * ZROW + (e0 & ~1));
+  auto read_b = [&](int cc, int fh, int g) -> mf_u32x4 {
+    const uint32_t* p = zrow0 + (cc * zrows + fh) * (ZROW / 2) - 8 * g;
+    mf_u32x4 d;
+    __builtin_memcpy(&d, p, 16);
+    const uint32_t d4 = p[4];
+    return mf_u32x4{__builtin_amdgcn_alignbit(d[1], d[0], bshift),
+                    __builtin_amdgcn_alignbit(d[2], d[1], bshift),
+                    __builtin_amdgcn_alignbit(d[3], d[2], bshift),
+                    __builtin_amdgcn_alignbit(d4, d[3], bshift)};
+  };
+
+  Stage pf[2];
+  stage_load(0, pf[0]);
+  stage_load(1, pf[1]);
+  mf_f32x4 acc[2][R][NG];
+#pragma unroll
+  for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+#pragma unroll
+      for (int g = 0; g < NG; ++g) acc[cc][j][g] = mf_f32x4{0.f, 0.f, 0.f, 0.f};
+  mf_u32x4 ringA[2][R];  // stream row q of channel cc in ringA[cc][q % R]
+
+  // Stream rows q = 0 .. nq - 1 (nq = R + FH - 1); row q completes the
+  // operands of filter row fh = q - R + 1.  Rows 2 b, 2 b + 1 go to LDS at
+  // barrier b while rows 2 b + 2, 2 b + 3 are loaded.  The loop body covers
+  // 2 R rows, so that ring indices are compile-time.
+  for (int q0 = 0; q0 < a.nq; q0 += 2 * R) {
+#pragma unroll
+    for (int bq = 0; bq < R; ++bq) {
+      const int qa = q0 + 2 * bq;
+      if (qa >= a.nq) break;                  // uniform
+      // slots of rows qa, qa + 1 were last read before the previous barrier
+      stage_store(qa, pf[0]);
+      stage_store(qa + 1, pf[1]);
+      stage_load(qa + 2, pf[0]);
+      stage_load(qa + 3, pf[1]);
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int q = qa + u;
+        const int slot = (2 * bq + u) % R;    // q % R: q0 is a multiple of R
+        if (q >= a.nq) break;
+        if (row_ok(q)) {
+          ringA[0][slot] = read_a(q, 0);
+          ringA[1][slot] = read_a(q, 1);
+        }
+        const int fh = q - (R - 1);
+        if (fh < 0) continue;                 // still filling the ring
+        mf_u32x4 b[2][NG];
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+          for (int g = 0; g < NG; ++g) b[cc][g] = read_b(cc, fh, g);
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+          // output row oh0 + j reads stream row fh + j = q - (R - 1) + j
+          const int r = r_base + fh + j;
+          if ((unsigned)r >= (unsigned)a.IH || oh0 + j >= a.OH) continue;  // uniform
+          const int s = (2 * bq + u + 1 + j) % R;  // (q - R + 1 + j) % R
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+            for (int g = 0; g < NG; ++g)
+              acc[cc][j][g] = mfma_16x16x32<DT>(ringA[cc][s], b[cc][g], acc[cc][j][g]);
+        }
+      }
+    }
+  }
+
+  // ---- outputs: registers -> LDS [image][column][channel] -> 16-byte
+  // stores of 4 channels, a.orows output rows per pair of barriers.  Lane
+  // (q, j), register v of (channel cc, group g) holds image 4 q + v at
+  // column 16 g + j; the wave's two channels are neighbouring floats.
+  const int oimgs = min(kB16Img, a.N - n0);
+  const int ipitch = a.OW * OPITCH + 4;        // floats per staged image
+  const int row_floats = kB16Img * ipitch;
+  float* const ostage = (float*)lds;
+  float* const obase = a.out + ((size_t)n0 * a.OH + oh0) * a.OW * a.C + c0;
+  const uint32_t row_step = (uint32_t)a.OW * (uint32_t)a.C;  // floats per output row
+  const int nitems = kB16Img * a.OW * 4;       // (pixel, channel quad) items per row
+  auto stage_row = [&](int j, float* dst) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const int col = 16 * g + lm;
+      if (col < a.OW) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float* d = dst + (4 * lq + v) * ipitch + col * OPITCH + 2 * wave;
+          *(float2*)d = float2{acc[0][j][g][v], acc[1][j][g][v]};
+        }
+      }
+    }
+  };
+  auto store_row = [&](int j, const float* src) {
+    for (int it = tid; it < nitems; it += NT) {
+      const int qd = it & 3, pc = it >> 2;
+      const int img = fast_div(pc, a.ow_magic), col = pc - img * a.OW;
+      if (img >= oimgs) break;                 // items run image by image
+      const mf_f32x4 v = *(const mf_f32x4*)(src + img * ipitch + col * OPITCH + 4 * qd);
+      const uint32_t og = ((uint32_t)img * (uint32_t)a.OH * (uint32_t)a.OW + (uint32_t)col) *
+                              (uint32_t)a.C + 4u * (uint32_t)qd;
+      *(mf_f32x4*)(obase + (og + (uint32_t)j * row_step)) = v;
+    }
+  };
+  int nb = 0;  // rows staged in the current round
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    if (oh0 + j >= a.OH) break;               // uniform
+    if (nb == 0) __syncthreads();             // the staging area is free
+    stage_row(j, ostage + nb * row_floats);
+    ++nb;
+    if (nb == a.orows || j + 1 == R || oh0 + j + 1 >= a.OH) {
+      __syncthreads();
+      for (int k = 0; k < nb; ++k) store_row(j + 1 - nb + k, ostage + k * row_floats);
+      nb = 0;
+    }
+  }
+}
+
+}  // namespace dwc

@@ -5,6 +5,7 @@
 
 #include <stdio.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include <algorithm>
 #include <cmath>
@@ -181,21 +182,70 @@ bool plan_mfma(const FwdArgs& f, int dt, bool flip, Plan* q) {
   return true;
 }
 
+// The 16-image form of the batch-packed plan (fwd_mfma_batch16): C % 16 ==
+// 0 (two 16-byte channel octets per pixel), a batch of at least 8 images,
+// the band and four row slots within one CU's LDS.  As many output rows as
+// the LDS holds are staged per round.
+static bool plan_mfma_batch16(const FwdArgs& f, Plan* q) {
+  if (f.C % kB16Cb != 0 || f.N < 8) return false;
+  if ((int64_t)kB16Img * f.IH * f.IW * f.C * 2 > kI32Max ||
+      (int64_t)kB16Img * f.OH * f.OW * f.C > kI32Max)
+    return false;
+  MfmaBatchArgs m{};
+  m.N = f.N; m.IH = f.IH; m.IW = f.IW; m.C = f.C; m.OH = f.OH; m.OW = f.OW;
+  m.FH = f.FH; m.FW = f.FW; m.PH = f.PH; m.PW = f.PW;
+  m.cb = kB16Cb;
+  m.rch = (f.OH + kB16Rows - 1) / kB16Rows;
+  m.cblk = f.C / m.cb;
+  m.ng = (f.N + kB16Img - 1) / kB16Img;
+  m.nq = kB16Rows + f.FH - 1;
+  const int64_t band = (int64_t)kB16Cb * (f.FH + 1) * 64 * 2;
+  const int64_t ring = (int64_t)kB16Slots * kB16Cb * kB16ChPitch;
+  const int64_t orow = (int64_t)kB16Img * (f.OW * kB16Opitch + 4) * 4;  // one output row
+  const int64_t lds = std::max(band + ring, orow);
+  if (lds > kLdsPerCu) return false;
+  m.lds_bytes = (int)lds;
+  m.orows = (int)std::min<int64_t>(kB16Rows, lds / orow);
+  m.ow_magic = div_magic((uint32_t)f.OW);
+  const int64_t blocks = (int64_t)m.cblk * m.rch * m.ng;
+  if (blocks > kI32Max) return false;
+  m.num_blocks = (int)blocks;
+  m.fw_magic = div_magic((uint32_t)f.FW);
+  q->bimg = kB16Img;
+  q->bng = f.OW > 16 ? 2 : 1;
+  q->blocks = (int)blocks;
+  q->mb = m;
+  return true;
+}
+
 // Packed-MFMA plan with the batch in the matrix rows (bf16 / fp16, stride
 // 1): false if the kernel does not apply.  Input and output widths up to 32
 // (one 32-column output tile, two 16-column input chunks), 0 <= PW <= 31
-// and FW <= 32 (the band rows' zeros), C % 8 == 0 (16-byte channel octets),
-// and a batch of at least 16 images (the matrix rows are images: smaller
-// batches leave most of each instruction idle).
+// and FW <= 32 (the band rows' zeros).  The 16-image kernel where it
+// applies (DWC_MFMA_BATCH_IMG=32 picks the 32-image one), else the 32-image
+// kernel: C % 8 == 0 (16-byte channel octets) and a batch of at least 16
+// images (the matrix rows are images: smaller batches leave most of each
+// instruction idle).
 bool plan_mfma_batch(const FwdArgs& f, int dt, bool flip, Plan* q) {
-  if ((dt != DT_BF16 && dt != DT_F16) || f.SH != 1 || f.SW != 1 || f.C % kBatchCb != 0 ||
+  if ((dt != DT_BF16 && dt != DT_F16) || f.SH != 1 || f.SW != 1 ||
       f.IW > kBatchMaxCols || f.OW > kBatchMaxCols || f.PW < 0 || f.PW > 31 || f.FW > 32 ||
-      f.PH < 0 || f.FH > 64 || f.N < 16)
+      f.PH < 0 || f.FH > 64)
     return false;
   // DWC_MFMA_BATCH: 0 never, 1 wherever it applies (for tests and A/B
   // timing); unset: from kBatchMinFh filter rows on
   const char* env = getenv("DWC_MFMA_BATCH");
   if (env ? atoi(env) == 0 : f.FH < kBatchMinFh) return false;
+  Plan t = *q;  // q changes only when a kernel applies
+  t.kind = PLAN_MFMA;
+  t.batch = true;
+  t.flip = flip;
+  t.fa = f;
+  const char* img = getenv("DWC_MFMA_BATCH_IMG");
+  if (!(img && atoi(img) == kBatchImg) && plan_mfma_batch16(f, &t)) {
+    *q = t;
+    return true;
+  }
+  if (f.C % kBatchCb != 0 || f.N < 16) return false;
   // 32-bit offsets into one image group's input and output
   if ((int64_t)kBatchImg * f.IH * f.IW * f.C * 2 > kI32Max ||
       (int64_t)kBatchImg * f.OH * f.OW * f.C > kI32Max)
@@ -220,12 +270,10 @@ bool plan_mfma_batch(const FwdArgs& f, int dt, bool flip, Plan* q) {
   if (blocks > kI32Max) return false;
   m.num_blocks = (int)blocks;
   m.fw_magic = div_magic((uint32_t)f.FW);
-  q->kind = PLAN_MFMA;
-  q->batch = true;
-  q->flip = flip;
-  q->blocks = (int)blocks;
-  q->mb = m;
-  q->fa = f;
+  t.bimg = kBatchImg;
+  t.blocks = (int)blocks;
+  t.mb = m;
+  *q = t;
   return true;
 }
 
@@ -851,8 +899,13 @@ std::string describe(const Plan& pl) {
     snprintf(buf, sizeof buf,
              "%s mfma dt=%s fw=%d fh=%d flip=%d batch=1 cb=%d imgs=%d rows=%d ng=%d "
              "rch=%d cblk=%d nq=%d lds=%d blocks=%d",
-             ops[pl.op], dt_name(pl.dt), m.FW, m.FH, (int)pl.flip, m.cb, kBatchImg, kBatchRows,
-             m.ng, m.rch, m.cblk, m.nq, m.lds_bytes, pl.blocks);
+             ops[pl.op], dt_name(pl.dt), m.FW, m.FH, (int)pl.flip, m.cb, pl.bimg,
+             pl.bimg == kB16Img ? kB16Rows : kBatchRows, m.ng, m.rch, m.cblk, m.nq, m.lds_bytes,
+             pl.blocks);
+    if (pl.bimg == kB16Img) {
+      const size_t k = strlen(buf);
+      snprintf(buf + k, sizeof buf - k, " ocg=%d orows=%d", pl.bng, m.orows);
+    }
     return buf;
   }
   if (pl.kind == PLAN_MFMA) {

@@ -41,6 +41,8 @@ struct Plan {
   MfmaArgs ma{};
   // ... with the batch in the matrix rows
   bool batch = false;
+  int bimg = 0;  // images per instruction: 32 (fwd_mfma_batch) or 16 (fwd_mfma_batch16)
+  int bng = 0;   // 16-column output groups of fwd_mfma_batch16 (1 or 2)
   MfmaBatchArgs mb{};
   // packed-MFMA filter gradient
   int nfm = 0, nfn = 0, nk = 0, pf = 0;

@@ -2,6 +2,7 @@
 // forward-type kernel with the batch in the matrix rows (bf16 / fp16).
 #include "dwc_launch.h"
 #include "dwc_mfma_batch.h"
+#include "dwc_mfma_batch16.h"
 
 namespace dwc {
 namespace {
@@ -33,7 +34,32 @@ hipError_t by_cb(const MfmaBatchArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+template <int DT, int NG, bool FLIP>
+hipError_t go16(const MfmaBatchArgs& a, hipStream_t s) {
+  auto kernel = fwd_mfma_batch16<DT, NG, FLIP>;
+  if (a.lds_bytes > 65536) {
+    const hipError_t e = allow_lds(kernel);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kernel, dim3(a.num_blocks), dim3(512), a.lds_bytes, s, a);
+  return hipGetLastError();
+}
+
+template <int DT, bool FLIP>
+hipError_t by_ng(int ng, const MfmaBatchArgs& a, hipStream_t s) {
+  if (ng == 1) return go16<DT, 1, FLIP>(a, s);
+  if (ng == 2) return go16<DT, 2, FLIP>(a, s);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
+
+hipError_t launch_fwd_mfma_batch16(int dt, int ng, bool flip, const MfmaBatchArgs& a,
+                                   hipStream_t s) {
+  if (dt == DT_BF16) return flip ? by_ng<DT_BF16, true>(ng, a, s) : by_ng<DT_BF16, false>(ng, a, s);
+  if (dt == DT_F16) return flip ? by_ng<DT_F16, true>(ng, a, s) : by_ng<DT_F16, false>(ng, a, s);
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_fwd_mfma_batch(int dt, bool flip, const MfmaBatchArgs& a, hipStream_t s) {
   if (dt == DT_BF16) return flip ? by_cb<DT_BF16, true>(a, s) : by_cb<DT_BF16, false>(a, s);

@@ -159,19 +159,32 @@ def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
         dwc.lib()
 
 
-def test_mfma_plans_and_rejections():
+def test_mfma_plans_and_rejections(monkeypatch):
     p = dwc.problem(128, 28, 28, 512, 13, 13, 1, 6, dtype=dwc.BF16)
     assert dwc.plan_describe(p, 0).startswith("fwd mfma")
     assert dwc.plan_describe(p, 1).startswith("bwd_data mfma")
     assert dwc.plan_describe(p, 2).startswith("bwd_filter mfma")
     # 13x13: the row-packed kernel; 31x31: the batch-packed kernel (AUTO
-    # takes it from 17 filter rows on, with N >= 16 and widths up to 32)
+    # takes it from 17 filter rows on, with widths up to 32): 16 images x 16
+    # channels per workgroup (two 16-column output groups, three output
+    # rows staged per round), or 32 x 8 when asked for
     assert " batch=1 " not in dwc.plan_describe(p, 0)
     p = dwc.problem(128, 28, 28, 512, 31, 31, 1, 15, dtype=dwc.F16)
     d = dwc.plan_describe(p, 0)
-    assert d.startswith("fwd mfma") and " batch=1 " in d and "ng=4" in d
+    assert d.startswith("fwd mfma") and " batch=1 cb=16 imgs=16 rows=7 ng=8 " in d, d
+    assert " ocg=2 orows=3" in d and " blocks=1024" in d, d
     assert " batch=1 " in dwc.plan_describe(p, 1)
-    for kw in (dict(n=8), dict(w=40)):
+    monkeypatch.setenv("DWC_MFMA_BATCH_IMG", "32")
+    d = dwc.plan_describe(p, 0)
+    assert " batch=1 cb=8 imgs=32 rows=7 ng=4 " in d and " blocks=1024" in d, d
+    monkeypatch.delenv("DWC_MFMA_BATCH_IMG")
+    # the 16-image kernel from 8 images (one output group up to 16 columns)
+    q = dwc.problem(8, 16, 16, 32, 17, 9, 1, (8, 4), dtype=dwc.BF16)
+    assert " imgs=16 " in dwc.plan_describe(q, 0) and " ocg=1 " in dwc.plan_describe(q, 0)
+    # C % 16 != 0: the 32-image kernel
+    q = dwc.problem(32, 16, 16, 24, 17, 9, 1, (8, 4), dtype=dwc.BF16)
+    assert " imgs=32 " in dwc.plan_describe(q, 0)
+    for kw in (dict(n=4), dict(w=40)):
         a = dict(n=128, w=28, pad=15, **{})
         a.update(kw)
         q = dwc.problem(a["n"], 28, a["w"], 512, 31, 31, 1, a["pad"], dtype=dwc.F16)

@@ -427,12 +427,16 @@ def test_nonfinite_operands_vector_kernels(shape, op, dtype):
         assert np.all(d <= el_bound(op, s, dtype) * mag[fin] + 1e-300), algo
 
 
-# Shapes for the packed-MFMA kernel with the batch in the matrix rows
-# (bf16/fp16, stride 1, input and output widths up to 32, N >= 16): a
-# ragged last image group (N not a multiple of 32), ragged last row chunk
-# (OH not a multiple of 7), the widest input (32 columns), FH != FW, a
-# one-column filter, FW = 32 with PW = 16, several channel blocks, filters
-# taller than the image, and both padding extremes the kernel takes.
+# Shapes for the packed-MFMA kernels with the batch in the matrix rows
+# (bf16/fp16, stride 1, input and output widths up to 32): the 32-image
+# kernel (C % 8 == 0, N >= 16) and the 16-image kernel (C % 16 == 0,
+# N >= 8, one or two 16-column output groups).  A ragged last image group
+# (N not a multiple of 16 or 32), ragged last row chunk (OH not a multiple
+# of 7), the widest input (32 columns), FH != FW, a one-column filter,
+# FW = 32 with PW = 16, several channel blocks (and channel-block counts
+# that are not a multiple of the neighbour group), filters taller than the
+# image, output widths of 13, 16, 17 and 32, and both padding extremes the
+# kernels take.
 BATCH_SHAPES = [
     (16, 28, 28, 16, 31, 31, 1, 15),
     (33, 14, 13, 24, 5, 5, 1, 2),
@@ -443,30 +447,53 @@ BATCH_SHAPES = [
     (18, 30, 31, 8, 17, 17, 1, 8),
     (64, 7, 7, 32, 7, 7, 1, 3),
     (16, 11, 26, 8, 11, 27, 1, (0, 13)),
+    (25, 14, 13, 48, 5, 5, 1, 2),
+    (9, 30, 32, 64, 17, 17, 1, 8),
+    (12, 10, 17, 16, 3, 31, 1, (1, 15)),
+    (8, 16, 16, 32, 9, 9, 1, 4),
+    (19, 9, 12, 80, 21, 11, 1, (10, 3)),
 ]
 
 
+def _batch_imgs(s, img):
+    """Images per instruction of the batch-packed plan when img (16 or 32)
+    is asked for: the 16-image kernel where it applies, else the 32-image
+    one, else None."""
+    if img == 16 and s.c % 16 == 0 and s.n >= 8:
+        return 16
+    if s.c % 8 == 0 and s.n >= 16:
+        return 32
+    return None
+
+
+@pytest.mark.parametrize("img", [16, 32])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("op", ["fwd", "bwd_data"])
 @pytest.mark.parametrize("shape", BATCH_SHAPES,
                          ids=lambda t: "x".join(map(str, t[:6])) + f"_p{t[7]}")
-def test_mfma_batch_parity(shape, op, dtype, monkeypatch):
+def test_mfma_batch_parity(shape, op, dtype, img, monkeypatch):
     monkeypatch.setenv("DWC_MFMA_BATCH", "1")  # every filter height, not only AUTO's
+    monkeypatch.setenv("DWC_MFMA_BATCH_IMG", str(img))
     s = _shape(shape)
+    want_imgs = _batch_imgs(s, img)
+    if want_imgs is None or (img == 32 and want_imgs != 32):
+        pytest.skip("the batch-packed kernel asked for does not take this shape")
     p = dwc.problem(s.n, s.h, s.w, s.c, s.fh, s.fw, 1, (s.pad_h, s.pad_w), dtype=DT[dtype])
     d = dwc.plan_describe(p, OPS[op])
-    assert " batch=1 " in d, d
+    assert " batch=1 " in d and f" imgs={want_imgs} " in d, d
     inp = make_inputs(s, dtype, seed=90 + sum(shape[:6]))
     want, mag = _want_mag(op, s, inp)
-    log(f"case mfma batch {shape} {op} {dtype}")
+    log(f"case mfma batch {shape} {op} {dtype} imgs={want_imgs}")
     for algo in ("auto", "mfma"):
         got = _run(op, s, inp, algo)
         check_parity(got, want, mag, op, s, dtype, what=algo)
 
 
-def test_mfma_batch_outputs_fully_overwritten(monkeypatch):
+@pytest.mark.parametrize("shape", [(33, 14, 13, 24, 5, 5, 1, 2), (25, 14, 13, 48, 5, 5, 1, 2)],
+                         ids=["imgs32", "imgs16"])
+def test_mfma_batch_outputs_fully_overwritten(shape, monkeypatch):
     monkeypatch.setenv("DWC_MFMA_BATCH", "1")
-    s = _shape((33, 14, 13, 24, 5, 5, 1, 2))
+    s = _shape(shape)
     inp = make_inputs(s, "bf16", seed=91)
     y = torch.full(s.y_shape(), float("nan"), device="cuda")
     dwc.fwd(to_device(inp.x), to_device(inp.w), 1, 2, out=y)
