@@ -173,9 +173,19 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_batch16(MfmaBatchArgs a) {
                     __builtin_amdgcn_alignbit(d4, d[3], bshift)};
   };
 
+  // Stream rows q = 0 .. nq - 1 (nq = R + FH - 1); row q completes the
+  // operands of filter row fh = q - R + 1.  Only rows q_lo .. q_hi - 1 are
+  // image rows; the stream runs from q_lo (earlier rows are padding, whose
+  // products are never formed) to q_hi + R - 1 (later filter rows read
+  // padding rows only), so that a workgroup whose window hangs over the
+  // image spends no barriers on padding.  Row q sits in LDS slot
+  // q % kB16Slots and in ring register (q - q_lo) % R.
+  const int q_lo = max(0, a.PH - oh0);
+  const int q_hi = min(a.nq, a.IH + a.PH - oh0);
+  const int nloc = max(0, min(a.nq, q_hi + R - 1) - q_lo);  // rows streamed
   Stage pf[2];
-  stage_load(0, pf[0]);
-  stage_load(1, pf[1]);
+  stage_load(q_lo, pf[0]);
+  stage_load(q_lo + 1, pf[1]);
   mf_f32x4 acc[2][R][NG];
 #pragma unroll
   for (int cc = 0; cc < 2; ++cc)
@@ -183,17 +193,17 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_batch16(MfmaBatchArgs a) {
     for (int j = 0; j < R; ++j)
 #pragma unroll
       for (int g = 0; g < NG; ++g) acc[cc][j][g] = mf_f32x4{0.f, 0.f, 0.f, 0.f};
-  mf_u32x4 ringA[2][R];  // stream row q of channel cc in ringA[cc][q % R]
+  mf_u32x4 ringA[2][R];  // stream row q of channel cc in ringA[cc][(q - q_lo) % R]
 
-  // Stream rows q = 0 .. nq - 1 (nq = R + FH - 1); row q completes the
-  // operands of filter row fh = q - R + 1.  Rows 2 b, 2 b + 1 go to LDS at
-  // barrier b while rows 2 b + 2, 2 b + 3 are loaded.  The loop body covers
-  // 2 R rows, so that ring indices are compile-time.
-  for (int q0 = 0; q0 < a.nq; q0 += 2 * R) {
+  // Rows 2 b, 2 b + 1 (from q_lo) go to LDS at barrier b while rows
+  // 2 b + 2, 2 b + 3 are loaded.  The loop body covers 2 R rows, so that
+  // ring indices are compile-time.
+  for (int l0 = 0; l0 < nloc; l0 += 2 * R) {
 #pragma unroll
     for (int bq = 0; bq < R; ++bq) {
-      const int qa = q0 + 2 * bq;
-      if (qa >= a.nq) break;                  // uniform
+      const int la = l0 + 2 * bq;
+      if (la >= nloc) break;                  // uniform
+      const int qa = q_lo + la;
       // slots of rows qa, qa + 1 were last read before the previous barrier
       stage_store(qa, pf[0]);
       stage_store(qa + 1, pf[1]);
@@ -203,8 +213,8 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_batch16(MfmaBatchArgs a) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int q = qa + u;
-        const int slot = (2 * bq + u) % R;    // q % R: q0 is a multiple of R
-        if (q >= a.nq) break;
+        const int slot = (2 * bq + u) % R;    // (q - q_lo) % R: l0 is a multiple of R
+        if (la + u >= nloc) break;
         if (row_ok(q)) {
           ringA[0][slot] = read_a(q, 0);
           ringA[1][slot] = read_a(q, 1);
@@ -218,10 +228,12 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_batch16(MfmaBatchArgs a) {
           for (int g = 0; g < NG; ++g) b[cc][g] = read_b(cc, fh, g);
 #pragma unroll
         for (int j = 0; j < R; ++j) {
-          // output row oh0 + j reads stream row fh + j = q - (R - 1) + j
+          // output row oh0 + j reads stream row fh + j = q - (R - 1) + j,
+          // which is an image row only from q_lo on (so its ring register
+          // has been written)
           const int r = r_base + fh + j;
           if ((unsigned)r >= (unsigned)a.IH || oh0 + j >= a.OH) continue;  // uniform
-          const int s = (2 * bq + u + 1 + j) % R;  // (q - R + 1 + j) % R
+          const int s = (2 * bq + u + 1 + j) % R;  // (q - q_lo - R + 1 + j) % R
 #pragma unroll
           for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
