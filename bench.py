@@ -364,7 +364,11 @@ def kernels_of(dwc, s, op, dtype="f32", algo="auto"):
         blocks = str(-(-int(kv["total"]) // 256))
     ks = [f"{k}|{blocks}"]
     if op == "bwd_filter" and "ws_bytes=0" not in d:
-        ks.append(f"reduce_partials|{-(-(s.fh * s.fw * s.c) // 64)}")
+        # four partial elements per thread where 16-byte accesses line up
+        # (the channel-blocked partials of the packed kernels need C % 4 == 0)
+        m = s.fh * s.fw * s.c
+        v4 = s.c % 4 == 0 if fam == "mfma" else m % 4 == 0
+        ks.append(f"reduce_partials|{-(-(m // 4 if v4 else m) // 256)}")
     return ks
 
 

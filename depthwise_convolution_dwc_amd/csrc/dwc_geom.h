@@ -205,9 +205,15 @@ constexpr int kB16Cb = 16;
 constexpr int kB16Img = 16;
 constexpr int kB16Rows = 7;
 constexpr int kB16Slots = 4;
+// Batches of two input rows loaded ahead of the one being staged.
+constexpr int kB16Prefetch = 1;
 constexpr int kB16KqPitch = kB16Img * 16 + 32;
 constexpr int kB16ChPitch = 4 * kB16KqPitch + 16;
 constexpr int kB16Opitch = 20;
+// Filter-tap items (16-byte loads) per thread at the largest filter the
+// 16-image kernel takes (FH <= 64, FW <= 32: 2 * 64 * 32 items over 512
+// threads).
+constexpr int kB16TapItems = 8;
 struct MfmaBatchArgs {
   const void* in;    // N x IH x IW x C (X, or dY for the data gradient)
   const void* filt;  // FH x FW x C

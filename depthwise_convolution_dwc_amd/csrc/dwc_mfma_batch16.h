@@ -88,28 +88,6 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_batch16(MfmaBatchArgs a) {
   uint16_t* zt = (uint16_t*)lds;                // [CB ch][FH + 1][ZROW]
   unsigned char* ring = lds + CB * zrows * ZROW * 2;  // kB16Slots staged rows
 
-  // ---- filter band: zero it, then write the taps after a barrier
-  const int zlen8 = CB * zrows * ZROW / 8;
-  for (int i = tid; i < zlen8; i += NT) ((mf_u32x4*)zt)[i] = mf_u32x4{0u, 0u, 0u, 0u};
-  __syncthreads();
-  {
-    const auto frsrc = make_rsrc(a.filt, (uint32_t)(FH * FW) * (uint32_t)a.C * 2u);
-    const int ftaps = FH * FW;
-    for (int te = tid; te < 2 * ftaps; te += NT) {
-      const int hf = te & 1, tap = te >> 1;     // channel half, tap
-      const int src = FLIP ? ftaps - 1 - tap : tap;
-      const mf_u32x4 v = __builtin_bit_cast(
-          mf_u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                        frsrc, (int)(((uint32_t)src * (uint32_t)a.C + (uint32_t)(c0 + 8 * hf)) * 2u),
-                        0, 0));
-      const int fh = fast_div(tap, a.fw_magic), fw = tap - fh * FW;
-      uint16_t* d = zt + (8 * hf * zrows + fh) * ZROW + 32 + fw;
-#pragma unroll
-      for (int j = 0; j < 8; ++j, d += zrows * ZROW)
-        *d = (uint16_t)((v[j >> 1] >> (16 * (j & 1))) & 0xffffu);
-    }
-  }
-
   // ---- staging of input rows: thread (image si, column pair sp, channel
   // half sh), tid = (si * 16 + sp) * 2 + sh.  One buffer resource over the
   // image group (wave-uniform); an item's image is part of its offset, and
@@ -150,6 +128,52 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_batch16(MfmaBatchArgs a) {
                                             (j & 1) ? 0x07060302u : 0x05040100u);
   };
 
+  // ---- start-up: the first two stream rows' loads and the filter taps'
+  // loads go out first, so that their latency overlaps the band's zero fill.
+  const int q_lo = max(0, a.PH - oh0);
+  constexpr int PD = kB16Prefetch;
+  Stage pf[PD][2];
+#pragma unroll
+  for (int k = 0; k < PD; ++k) {
+    stage_load(q_lo + 2 * k, pf[k][0]);
+    stage_load(q_lo + 2 * k + 1, pf[k][1]);
+  }
+  // filter band: per channel and filter row, 32 zeros, the taps, zeros up
+  // to the next row; item te = (tap, channel half) of thread te % NT
+  const int ftaps = FH * FW;
+  const int titems = uniform((2 * ftaps + NT - 1) / NT);  // <= kB16TapItems
+  mf_u32x4 tv[kB16TapItems];
+  {
+    const auto frsrc = make_rsrc(a.filt, (uint32_t)ftaps * (uint32_t)a.C * 2u);
+#pragma unroll
+    for (int k = 0; k < kB16TapItems; ++k) {
+      if (k >= titems) break;                   // uniform
+      const int te = tid + k * NT;
+      const int hf = te & 1, tap = te >> 1;     // channel half, tap
+      const int src = FLIP ? ftaps - 1 - tap : tap;
+      const uint32_t off =
+          te < 2 * ftaps ? ((uint32_t)src * (uint32_t)a.C + (uint32_t)(c0 + 8 * hf)) * 2u : kOOB;
+      tv[k] = __builtin_bit_cast(mf_u32x4,
+                                 __builtin_amdgcn_raw_buffer_load_b128(frsrc, (int)off, 0, 0));
+    }
+  }
+  const int zlen8 = CB * zrows * ZROW / 8;
+  for (int i = tid; i < zlen8; i += NT) ((mf_u32x4*)zt)[i] = mf_u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kB16TapItems; ++k) {
+    if (k >= titems) break;                     // uniform
+    const int te = tid + k * NT;
+    if (te < 2 * ftaps) {
+      const int hf = te & 1, tap = te >> 1;
+      const int fh = fast_div(tap, a.fw_magic), fw = tap - fh * FW;
+      uint16_t* d = zt + (8 * hf * zrows + fh) * ZROW + 32 + fw;
+#pragma unroll
+      for (int j = 0; j < 8; ++j, d += zrows * ZROW)
+        *d = (uint16_t)((tv[k][j >> 1] >> (16 * (j & 1))) & 0xffffu);
+    }
+  }
+
   // ---- compute operands.  A: lane (q, i) reads the 16 bytes of image i,
   // column group q of a staged row.  B: lane (q, j) of column group g
   // starts at element e = 32 + 8 q - 16 g - j + PW of its channel's band
@@ -180,12 +204,19 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_batch16(MfmaBatchArgs a) {
   // padding rows only), so that a workgroup whose window hangs over the
   // image spends no barriers on padding.  Row q sits in LDS slot
   // q % kB16Slots and in ring register (q - q_lo) % R.
-  const int q_lo = max(0, a.PH - oh0);
   const int q_hi = min(a.nq, a.IH + a.PH - oh0);
   const int nloc = max(0, min(a.nq, q_hi + R - 1) - q_lo);  // rows streamed
-  Stage pf[2];
-  stage_load(q_lo, pf[0]);
-  stage_load(q_lo + 1, pf[1]);
+  // band of the next filter row, read during the current row's MFMAs (the
+  // band does not change, so this read may cross a barrier); rows clamp to
+  // [0, FH - 1] where no filter row follows.  The first read waits for
+  // every wave's tap writes.
+  auto fh_clamp = [&](int fh) { return min(max(fh, 0), FH - 1); };
+  __syncthreads();
+  mf_u32x4 bn[2][NG];
+#pragma unroll
+  for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+    for (int g = 0; g < NG; ++g) bn[cc][g] = read_b(cc, fh_clamp(q_lo - (R - 1)), g);
   mf_f32x4 acc[2][R][NG];
 #pragma unroll
   for (int cc = 0; cc < 2; ++cc)
@@ -196,19 +227,20 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_batch16(MfmaBatchArgs a) {
   mf_u32x4 ringA[2][R];  // stream row q of channel cc in ringA[cc][(q - q_lo) % R]
 
   // Rows 2 b, 2 b + 1 (from q_lo) go to LDS at barrier b while rows
-  // 2 b + 2, 2 b + 3 are loaded.  The loop body covers 2 R rows, so that
-  // ring indices are compile-time.
-  for (int l0 = 0; l0 < nloc; l0 += 2 * R) {
+  // 2 (b + PD), 2 (b + PD) + 1 are loaded.  The loop body covers 2 PD R
+  // rows, so that ring and prefetch indices are compile-time.
+  for (int l0 = 0; l0 < nloc; l0 += 2 * PD * R) {
 #pragma unroll
-    for (int bq = 0; bq < R; ++bq) {
+    for (int bq = 0; bq < PD * R; ++bq) {
       const int la = l0 + 2 * bq;
       if (la >= nloc) break;                  // uniform
       const int qa = q_lo + la;
+      const int k = bq % PD;                  // l0 is a multiple of 2 PD
       // slots of rows qa, qa + 1 were last read before the previous barrier
-      stage_store(qa, pf[0]);
-      stage_store(qa + 1, pf[1]);
-      stage_load(qa + 2, pf[0]);
-      stage_load(qa + 3, pf[1]);
+      stage_store(qa, pf[k][0]);
+      stage_store(qa + 1, pf[k][1]);
+      stage_load(qa + 2 * PD, pf[k][0]);
+      stage_load(qa + 2 * PD + 1, pf[k][1]);
       __syncthreads();
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -220,12 +252,15 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_batch16(MfmaBatchArgs a) {
           ringA[1][slot] = read_a(q, 1);
         }
         const int fh = q - (R - 1);
-        if (fh < 0) continue;                 // still filling the ring
         mf_u32x4 b[2][NG];
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-          for (int g = 0; g < NG; ++g) b[cc][g] = read_b(cc, fh, g);
+          for (int g = 0; g < NG; ++g) {
+            b[cc][g] = bn[cc][g];
+            bn[cc][g] = read_b(cc, fh_clamp(fh + 1), g);
+          }
+        if (fh < 0) continue;                 // still filling the ring
 #pragma unroll
         for (int j = 0; j < R; ++j) {
           // output row oh0 + j reads stream row fh + j = q - (R - 1) + j,

@@ -202,10 +202,12 @@ static bool plan_mfma_batch16(const FwdArgs& f, Plan* q) {
   const int64_t band = (int64_t)kB16Cb * (f.FH + 1) * 64 * 2;
   const int64_t ring = (int64_t)kB16Slots * kB16Cb * kB16ChPitch;
   const int64_t orow = (int64_t)kB16Img * (f.OW * kB16Opitch + 4) * 4;  // one output row
-  const int64_t lds = std::max(band + ring, orow);
-  if (lds > kLdsPerCu) return false;
+  if (band + ring > kLdsPerCu || orow > kLdsPerCu) return false;
+  // one workgroup per CU (registers), so the output staging may take the
+  // whole LDS: as many rows per round as fit
+  m.orows = (int)std::min<int64_t>(kB16Rows, kLdsPerCu / orow);
+  const int64_t lds = std::max(band + ring, m.orows * orow);
   m.lds_bytes = (int)lds;
-  m.orows = (int)std::min<int64_t>(kB16Rows, lds / orow);
   m.ow_magic = div_magic((uint32_t)f.OW);
   const int64_t blocks = (int64_t)m.cblk * m.rch * m.ng;
   if (blocks > kI32Max) return false;

@@ -166,13 +166,13 @@ def test_mfma_plans_and_rejections(monkeypatch):
     assert dwc.plan_describe(p, 2).startswith("bwd_filter mfma")
     # 13x13: the row-packed kernel; 31x31: the batch-packed kernel (AUTO
     # takes it from 17 filter rows on, with widths up to 32): 16 images x 16
-    # channels per workgroup (two 16-column output groups, three output
+    # channels per workgroup (two 16-column output groups, four output
     # rows staged per round), or 32 x 8 when asked for
     assert " batch=1 " not in dwc.plan_describe(p, 0)
     p = dwc.problem(128, 28, 28, 512, 31, 31, 1, 15, dtype=dwc.F16)
     d = dwc.plan_describe(p, 0)
     assert d.startswith("fwd mfma") and " batch=1 cb=16 imgs=16 rows=7 ng=8 " in d, d
-    assert " ocg=2 orows=3" in d and " blocks=1024" in d, d
+    assert " ocg=2 orows=4" in d and " blocks=1024" in d, d
     assert " batch=1 " in dwc.plan_describe(p, 1)
     monkeypatch.setenv("DWC_MFMA_BATCH_IMG", "32")
     d = dwc.plan_describe(p, 0)
