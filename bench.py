@@ -364,11 +364,14 @@ def kernels_of(dwc, s, op, dtype="f32", algo="auto"):
         blocks = str(-(-int(kv["total"]) // 256))
     ks = [f"{k}|{blocks}"]
     if op == "bwd_filter" and "ws_bytes=0" not in d:
-        # four partial elements per thread where 16-byte accesses line up
-        # (the channel-blocked partials of the packed kernels need C % 4 == 0)
         m = s.fh * s.fw * s.c
-        v4 = s.c % 4 == 0 if fam == "mfma" else m % 4 == 0
-        ks.append(f"reduce_partials|{-(-(m // 4 if v4 else m) // 256)}")
+        if int(kv.get("z", 1)) > 32:  # many slices: 16 waves split them, 64 elements a block
+            ks.append(f"reduce_partials_split|{-(-m // 64)}")
+        else:
+            # four partial elements per thread where 16-byte accesses line up
+            # (the channel-blocked partials of the packed kernels need C % 4 == 0)
+            v4 = s.c % 4 == 0 if fam == "mfma" else m % 4 == 0
+            ks.append(f"reduce_partials<{4 if v4 else 1}>|{-(-(m // 4 if v4 else m) // 256)}")
     return ks
 
 

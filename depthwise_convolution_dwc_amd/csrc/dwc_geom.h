@@ -191,9 +191,14 @@ constexpr int kBatchPrefetch = 1;
 constexpr int kBatchHalfPitch = kBatchImg * 16 + 64;
 constexpr int kBatchMaxCols = 32;
 // AUTO takes the batch-packed kernel from this filter height on; below it
-// the row-packed kernel is faster (13x13 at N=128 28x28 C=512: 111 against
-// 160 us), its matrix cores being idle either way.
+// the row-packed kernel is as fast or faster (13x13 at N=128 28x28 C=512
+// fp16: 114-120 against 121-124 us for the 16-image kernel, 163-167 for the
+// 32-image one), its matrix cores being idle either way.
 constexpr int kBatchMinFh = 17;
+// ... for fp8 operands, where it takes the 16-image kernel from this filter
+// height on (13x13 at N=128 28x28 C=512 e4m3: 106 against 126 us for the
+// row-packed kernel).
+constexpr int kBatchMinFh8 = 13;
 // The same packing with 16 images per v_mfma_f32_16x16x32 and two channels
 // per wave: a workgroup owns kB16Cb channels x kB16Img images x kB16Rows
 // output rows.  Staged rows: per channel, 4 column groups of 16 images x 16
@@ -210,6 +215,11 @@ constexpr int kB16Prefetch = 1;
 constexpr int kB16KqPitch = kB16Img * 16 + 32;
 constexpr int kB16ChPitch = 4 * kB16KqPitch + 16;
 constexpr int kB16Opitch = 20;
+// fp8 operands: 8-byte groups, 16 images x 8 bytes per column group; the
+// pitches put the 64 dword writes of one staging instruction (lanes of 4
+// images x 16 column pairs x 2 channel halves) on 64 different banks.
+constexpr int kB16KqPitch8 = 160;
+constexpr int kB16ChPitch8 = 4 * kB16KqPitch8 + 16;
 // Filter-tap items (16-byte loads) per thread at the largest filter the
 // 16-image kernel takes (FH <= 64, FW <= 32: 2 * 64 * 32 items over 512
 // threads).

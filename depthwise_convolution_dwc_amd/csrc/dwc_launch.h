@@ -40,7 +40,7 @@ hipError_t launch_fwd_mfma(int dt, int nf, int tiles, bool flip, const MfmaArgs&
 // fp16 operands, stride 1, widths up to 32).
 hipError_t launch_fwd_mfma_batch(int dt, bool flip, const MfmaBatchArgs& a, hipStream_t s);
 // ... with 16 images per instruction and two channels per wave (ng output
-// column groups of 16).
+// column groups of 16); bf16 / fp16 and fp8 (e4m3 / e5m2) operands.
 hipError_t launch_fwd_mfma_batch16(int dt, int ng, bool flip, const MfmaBatchArgs& a,
                                    hipStream_t s);
 

@@ -182,13 +182,16 @@ bool plan_mfma(const FwdArgs& f, int dt, bool flip, Plan* q) {
   return true;
 }
 
-// The 16-image form of the batch-packed plan (fwd_mfma_batch16): C % 16 ==
-// 0 (two 16-byte channel octets per pixel), a batch of at least 8 images,
+// The 16-image form of the batch-packed plan (fwd_mfma_batch16): bf16 /
+// fp16 or fp8 operands, C % 16 == 0 (16 channels of a pixel: two 16-byte
+// loads, or one for fp8), a batch of at least 8 images,
 // the band and four row slots within one CU's LDS.  As many output rows as
 // the LDS holds are staged per round.
-static bool plan_mfma_batch16(const FwdArgs& f, Plan* q) {
+static bool plan_mfma_batch16(const FwdArgs& f, int dt, Plan* q) {
   if (f.C % kB16Cb != 0 || f.N < 8) return false;
-  if ((int64_t)kB16Img * f.IH * f.IW * f.C * 2 > kI32Max ||
+  const bool b8 = dt == DT_E4M3 || dt == DT_E5M2;
+  const int eb = b8 ? 1 : 2;
+  if ((int64_t)kB16Img * f.IH * f.IW * f.C * eb > kI32Max ||
       (int64_t)kB16Img * f.OH * f.OW * f.C > kI32Max)
     return false;
   MfmaBatchArgs m{};
@@ -199,8 +202,8 @@ static bool plan_mfma_batch16(const FwdArgs& f, Plan* q) {
   m.cblk = f.C / m.cb;
   m.ng = (f.N + kB16Img - 1) / kB16Img;
   m.nq = kB16Rows + f.FH - 1;
-  const int64_t band = (int64_t)kB16Cb * (f.FH + 1) * 64 * 2;
-  const int64_t ring = (int64_t)kB16Slots * kB16Cb * kB16ChPitch;
+  const int64_t band = (int64_t)kB16Cb * (f.FH + 1) * 64 * eb;
+  const int64_t ring = (int64_t)kB16Slots * kB16Cb * (b8 ? kB16ChPitch8 : kB16ChPitch);
   const int64_t orow = (int64_t)kB16Img * (f.OW * kB16Opitch + 4) * 4;  // one output row
   if (band + ring > kLdsPerCu || orow > kLdsPerCu) return false;
   // one workgroup per CU (registers), so the output staging may take the
@@ -229,25 +232,27 @@ static bool plan_mfma_batch16(const FwdArgs& f, Plan* q) {
 // images (the matrix rows are images: smaller batches leave most of each
 // instruction idle).
 bool plan_mfma_batch(const FwdArgs& f, int dt, bool flip, Plan* q) {
-  if ((dt != DT_BF16 && dt != DT_F16) || f.SH != 1 || f.SW != 1 ||
+  const bool b8 = dt == DT_E4M3 || dt == DT_E5M2;
+  if ((dt != DT_BF16 && dt != DT_F16 && !b8) || f.SH != 1 || f.SW != 1 ||
       f.IW > kBatchMaxCols || f.OW > kBatchMaxCols || f.PW < 0 || f.PW > 31 || f.FW > 32 ||
       f.PH < 0 || f.FH > 64)
     return false;
   // DWC_MFMA_BATCH: 0 never, 1 wherever it applies (for tests and A/B
-  // timing); unset: from kBatchMinFh filter rows on
+  // timing); unset: from kBatchMinFh (fp8: kBatchMinFh8) filter rows on
   const char* env = getenv("DWC_MFMA_BATCH");
-  if (env ? atoi(env) == 0 : f.FH < kBatchMinFh) return false;
+  if (env ? atoi(env) == 0 : f.FH < (b8 ? kBatchMinFh8 : kBatchMinFh)) return false;
   Plan t = *q;  // q changes only when a kernel applies
   t.kind = PLAN_MFMA;
   t.batch = true;
   t.flip = flip;
   t.fa = f;
   const char* img = getenv("DWC_MFMA_BATCH_IMG");
-  if (!(img && atoi(img) == kBatchImg) && plan_mfma_batch16(f, &t)) {
+  if ((b8 || !(img && atoi(img) == kBatchImg)) && plan_mfma_batch16(f, dt, &t)) {
     *q = t;
     return true;
   }
-  if (f.C % kBatchCb != 0 || f.N < 16) return false;
+  // the 32-image kernel takes bf16 / fp16 operands only
+  if (b8 || f.C % kBatchCb != 0 || f.N < 16) return false;
   // 32-bit offsets into one image group's input and output
   if ((int64_t)kBatchImg * f.IH * f.IW * f.C * 2 > kI32Max ||
       (int64_t)kBatchImg * f.OH * f.OW * f.C > kI32Max)

@@ -58,6 +58,8 @@ hipError_t launch_fwd_mfma_batch16(int dt, int ng, bool flip, const MfmaBatchArg
                                    hipStream_t s) {
   if (dt == DT_BF16) return flip ? by_ng<DT_BF16, true>(ng, a, s) : by_ng<DT_BF16, false>(ng, a, s);
   if (dt == DT_F16) return flip ? by_ng<DT_F16, true>(ng, a, s) : by_ng<DT_F16, false>(ng, a, s);
+  if (dt == DT_E4M3) return flip ? by_ng<DT_E4M3, true>(ng, a, s) : by_ng<DT_E4M3, false>(ng, a, s);
+  if (dt == DT_E5M2) return flip ? by_ng<DT_E5M2, true>(ng, a, s) : by_ng<DT_E5M2, false>(ng, a, s);
   return hipErrorInvalidValue;
 }
 

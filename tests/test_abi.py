@@ -351,9 +351,11 @@ def test_fp8_operand_plans():
 
 
 def test_fp8_mfma_plans_and_rejections():
-    """The packed fp8 kernel (16x16x128 MFMAs over four filter rows): 16
-    channels per workgroup, C a multiple of 16, stride 1, FW <= 32, output
-    width <= 64; LDS within the per-workgroup limit."""
+    """The packed fp8 kernels, 16 channels per workgroup, C a multiple of
+    16, stride 1, FW <= 32: the 16-image batch-packed kernel (16x16x32 fp8
+    MFMAs) from 13 filter rows on, where widths are up to 32, within one
+    CU's LDS; otherwise the row-packed kernel (16x16x128 MFMAs over four
+    filter rows, output width <= 64, LDS within its per-workgroup limit)."""
     for dt, name in ((dwc.FP8_E4M3, "e4m3"), (dwc.FP8_E5M2, "e5m2")):
         for f in (3, 7, 13, 17, 31):
             p = dwc.problem(128, 28, 28, 512, f, f, 1, f // 2, dtype=dt)
@@ -362,8 +364,14 @@ def test_fp8_mfma_plans_and_rejections():
                 assert d.startswith(("fwd mfma", "bwd_data mfma")), d
                 g = dict(kv.split("=") for kv in d.split()[2:])
                 assert g["dt"] == name and g["cb"] == "16" and g["flip"] == str(op)
-                assert int(g["lds"]) <= 81920
-                assert int(g["wp"]) % 16 == 0 and int(g["wt"]) == 16 * (int(g["gt"]) + int(g["nf"]))
+                if f >= 13:
+                    assert g.get("batch") == "1" and g["imgs"] == "16", d
+                    assert int(g["lds"]) <= 163840
+                else:
+                    assert "batch" not in g, d
+                    assert int(g["lds"]) <= 81920
+                    assert int(g["wp"]) % 16 == 0
+                    assert int(g["wt"]) == 16 * (int(g["gt"]) + int(g["nf"]))
         for kw in (dict(c=24), dict(stride=2), dict(fw=33, fh=3, pad=(1, 16), w=40), dict(w=80, h=20)):
             a = dict(n=2, h=20, w=20, c=32, fh=5, fw=5, stride=1, pad=2)
             a.update(kw)

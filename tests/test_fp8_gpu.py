@@ -109,3 +109,43 @@ def test_fp8_parity(shape, op, dtype):
         assert err <= TOL[dtype], (algo, err)
         bad = np.abs(got - want) > FP8_EL_TOL * mag + 1e-30
         assert not np.any(bad), (algo, int(bad.sum()), np.argwhere(bad)[:3])
+
+
+# The 16-image batch-packed kernel with fp8 operands (v_mfma_f32_16x16x32
+# fp8 / bf8; C % 16 == 0, N >= 8, input and output widths up to 32), forced
+# for every filter height: ragged image groups and row chunks, channel-block
+# counts that are not a multiple of the neighbour group, one and two 16-column
+# output groups, FH != FW, the widest input, wide padding.
+BATCH16_SHAPES = [
+    (16, 28, 28, 16, 31, 31, 1, 15),
+    (25, 14, 13, 48, 5, 5, 1, 2),
+    (9, 30, 32, 64, 17, 17, 1, 8),
+    (12, 10, 17, 16, 3, 31, 1, (1, 15)),
+    (8, 16, 16, 32, 9, 9, 1, 4),
+    (19, 9, 12, 80, 21, 11, 1, (10, 3)),
+]
+
+
+@pytest.mark.parametrize("dtype", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("op", ["fwd", "bwd_data"])
+@pytest.mark.parametrize("shape", BATCH16_SHAPES,
+                         ids=lambda t: "x".join(map(str, t[:6])) + f"_p{t[7]}")
+def test_fp8_batch16_parity(shape, op, dtype, monkeypatch):
+    monkeypatch.setenv("DWC_MFMA_BATCH", "1")
+    s = _shape(shape)
+    p = dwc.problem(s.n, s.h, s.w, s.c, s.fh, s.fw, 1, (s.pad_h, s.pad_w), dtype=DT[dtype])
+    d = dwc.plan_describe(p, OPS[op])
+    assert " batch=1 " in d and " imgs=16 " in d, d
+    inp = make_inputs(s, dtype, seed=11 + sum(shape[:6]))
+    a, b = _operands(op, inp)
+    va, vb = oracle.fp8_decode(a.stored, dtype), oracle.fp8_decode(b.stored, dtype)
+    want = _oracle(op, s, va, vb)
+    mag = _oracle(op, s, np.abs(va), np.abs(vb))
+    for algo in ("auto", "mfma"):
+        log(f"case fp8 batch16 {shape} {op} {dtype} {algo}")
+        got = _run(op, s, inp, algo)
+        assert np.all(np.isfinite(got))
+        err = rel_l2(got, want)
+        assert err <= TOL[dtype], (algo, err)
+        bad = np.abs(got - want) > FP8_EL_TOL * mag + 1e-30
+        assert not np.any(bad), (algo, int(bad.sum()), np.argwhere(bad)[:3])
