@@ -661,7 +661,11 @@ PROFILE_CMDS = {
              "-- python3 $R/bench.py --copy-calibration",
     "sq": "rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_WAVES SQ_BUSY_CYCLES "
           "SQ_VALU_MFMA_BUSY_CYCLES SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_LDS --output-format csv "
-          f"-d $R/gpurun_out/prof/sq -o run -- {_BENCH} --no-configs --steps 5 --warmup 2",
+          f"-d $R/gpurun_out/prof/sq -o run -- {_BENCH} --steps 5 --warmup 2 --config-reps 5",
+    "pipe": "rocprofv3 --pmc SQ_WAVES SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_ACTIVE_INST_ANY "
+            "SQ_ACTIVE_INST_VALU SQ_INSTS_VMEM_RD GRBM_GUI_ACTIVE TA_TA_BUSY_sum TD_TD_BUSY_sum "
+            "TCP_TOTAL_CACHE_ACCESSES_sum --output-format csv "
+            f"-d $R/gpurun_out/prof/pipe -o run -- {_BENCH} --steps 5 --warmup 2 --config-reps 5",
 }
 
 
@@ -929,44 +933,124 @@ The same numbers are in `traffic.json`, which `bench.py` reads for the
     with open(os.path.join(PROFILES, PROFILE_NAME + ".hbm_traffic.md"), "w") as f:
         f.write(traffic_md)
 
-    # SQ counters of the step's kernels: per-wave instruction mix, matrix-core
-    # busy fraction and LDS bank conflicts
-    sq = {}
-    for r in _csv_rows(os.path.join(d, "sq"), "*counter_collection.csv"):
+    # SQ, memory-pipeline and occupancy figures of every kernel: per-wave
+    # instruction mix, matrix-core busy fraction, LDS bank conflicts, the
+    # waves' issue and wait fractions, TA/TD busy fractions, L1 accesses per
+    # load instruction, and the waves per SIMD its resources allow
+    def counters(sub):
+        out = {}
+        for r in _csv_rows(os.path.join(d, sub), "*counter_collection.csv"):
+            if "dwc::" not in r["Kernel_Name"]:
+                continue
+            blocks = int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"]))
+            key = _kernel_key(r["Kernel_Name"], blocks)
+            out.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+        return {k: {c: float(np.mean(v)) for c, v in cs.items()} for k, cs in out.items()}
+    sq, pipe = counters("sq"), counters("pipe")
+    res = {}  # kernel key -> (VGPRs + AGPRs, LDS bytes, workgroup size, workgroups)
+    for r in _csv_rows(os.path.join(d, "trace"), "*kernel_trace.csv"):
         if "dwc::" not in r["Kernel_Name"]:
             continue
-        blocks = int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"]))
-        key = _kernel_key(r["Kernel_Name"], blocks)
-        sq.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
-    sl = ["| kernel, workgroups | VALU / wave | MFMA / wave | LDS / wave | matrix cores busy | "
-          "LDS bank-conflict cycles / LDS active cycles |", "|---|---|---|---|---|---|"]
-    for key, c in sorted(sq.items()):
-        m = {k: float(np.mean(v)) for k, v in c.items()}
+        wg = int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"])
+        blocks = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+        res[_kernel_key(r["Kernel_Name"], blocks)] = (
+            int(r["VGPR_Count"]) + int(r["Accum_VGPR_Count"]), int(r["LDS_Block_Size"]), wg, blocks)
+
+    def occupancy(key):
+        """Waves per SIMD: the lowest of 8, the register file (512 per lane),
+        the LDS (160 KiB per CU, whole workgroups) and what the launch
+        provides (1024 SIMDs)."""
+        if key not in res:
+            return "-"
+        regs, lds_b, wg, blocks = res[key]
+        wpg = max(1, -(-wg // 64))
+        by_regs = 512 // max(regs, 1)
+        by_lds = (163840 // lds_b) * wpg / 4 if lds_b else 8
+        by_launch = blocks * wpg / 1024
+        return (f"{min(8, by_regs, by_lds, by_launch):.1f} ({regs} regs, "
+                f"{lds_b / 1024:.0f} KiB)")
+
+    def sq_row(key):
+        m = sq.get(key, {})
         w = max(m.get("SQ_WAVES", 1.0), 1.0)
         # SQ_BUSY_CYCLES sums the shader engines (32 on MI355X, 8 CUs each);
         # SQ_VALU_MFMA_BUSY_CYCLES sums the SIMDs (1024)
-        busy = m.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / 1024 / max(m["SQ_BUSY_CYCLES"] / 32, 1.0)
+        busy = m.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / 1024 / max(m.get("SQ_BUSY_CYCLES", 0) / 32,
+                                                                     1.0)
         conf = m.get("SQ_LDS_BANK_CONFLICT", 0.0) / max(m.get("SQ_ACTIVE_INST_LDS", 1.0), 1.0)
-        sl.append(f"| `{key.replace('|', '`, ')} | {m['SQ_INSTS_VALU'] / w:.0f} | "
-                  f"{m['SQ_INSTS_MFMA'] / w:.0f} | {m['SQ_INSTS_LDS'] / w:.0f} | {busy:.2f} | "
-                  f"{conf:.2f} |")
-    sq_md = f"""# SQ counters: mixed-precision step, N=128 28x28 C=512 31x31 pad 15, fp16 operands
+        p = pipe.get(key, {})
+        wc = max(p.get("SQ_WAVE_CYCLES", 0.0), 1.0)
+        # GRBM_GUI_ACTIVE sums the 8 XCDs; the TA and TD counters the 256 CUs
+        kc = max(p.get("GRBM_GUI_ACTIVE", 0.0) / 8, 1.0)
+        vm = max(p.get("SQ_INSTS_VMEM_RD", 0.0), 1.0)
+        return (f"| `{key.replace('|', '`, ')} | {occupancy(key)} | "
+                f"{m.get('SQ_INSTS_VALU', 0) / w:.0f} | {m.get('SQ_INSTS_MFMA', 0) / w:.0f} | "
+                f"{m.get('SQ_INSTS_LDS', 0) / w:.0f} | {busy:.2f} | {conf:.2f} | "
+                f"{p.get('SQ_ACTIVE_INST_ANY', 0) / wc:.2f} | {p.get('SQ_WAIT_ANY', 0) / wc:.2f} | "
+                f"{p.get('TA_TA_BUSY_sum', 0) / 256 / kc:.2f} | "
+                f"{p.get('TD_TD_BUSY_sum', 0) / 256 / kc:.2f} | "
+                f"{p.get('TCP_TOTAL_CACHE_ACCESSES_sum', 0) / vm:.1f} |")
 
-Per-wave instruction counts (each counter averaged over the dispatches of a
-kernel and divided by `SQ_WAVES`), the fraction of the launch the matrix
-cores were busy (`SQ_VALU_MFMA_BUSY_CYCLES` per SIMD over `SQ_BUSY_CYCLES`
-per shader engine) and LDS bank-conflict cycles relative to LDS active
-cycles, for the default benchmark step's kernels.
+    sq_head = ["| kernel, workgroups | waves / SIMD | VALU / wave | MFMA / wave | LDS / wave | "
+               "matrix cores busy | LDS conflict / LDS active | issuing | waiting | TA busy | "
+               "TD busy | L1 accesses / load |", "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    step_keys = set()
+    for op in HEADLINE_OPS:
+        for k in kernels_of(dwc, s_h, op, HEADLINE_DTYPE):
+            step_keys.update(kernel_matches(list(sq), k))
+    sl = sq_head + [sq_row(k) for k in sorted(step_keys)]
+    cl = sq_head + [sq_row(k) for k in sorted(sq) if k not in step_keys]
+    legend = f"""Columns, each counter averaged over the dispatches of one kernel at one
+launch size (rocprofv3 derived counters, two runs of their own):
+- waves / SIMD: what the kernel's registers (VGPRs + AGPRs of 512 per
+  lane), LDS (160 KiB per CU, whole workgroups) and launch size allow, from
+  the kernel trace's resource columns;
+- VALU, MFMA, LDS: instructions per wave (`SQ_INSTS_*` / `SQ_WAVES`);
+- matrix cores busy: `SQ_VALU_MFMA_BUSY_CYCLES` per SIMD over
+  `SQ_BUSY_CYCLES` per shader engine;
+- LDS conflict / LDS active: `SQ_LDS_BANK_CONFLICT` over
+  `SQ_ACTIVE_INST_LDS`;
+- issuing, waiting: `SQ_ACTIVE_INST_ANY` and `SQ_WAIT_ANY` over
+  `SQ_WAVE_CYCLES` (fractions of the waves' resident time);
+- TA busy, TD busy: `TA_TA_BUSY_sum` and `TD_TD_BUSY_sum` per CU over
+  `GRBM_GUI_ACTIVE` per XCD (the vector-memory address and data units);
+- L1 accesses / load: `TCP_TOTAL_CACHE_ACCESSES_sum` over
+  `SQ_INSTS_VMEM_RD`: cache lines a load instruction touches (2 for a
+  wave's 256 contiguous bytes, up to 64 for 64 scattered pieces).
 
-Command (repository root `$R`):
+Commands (repository root `$R`):
 
 ```
 {cd}{PROFILE_CMDS["sq"]}
+{cd}{PROFILE_CMDS["pipe"]}
 cd $R && python3 bench.py --summarize-profile gpurun_out/prof
 ```
+"""
+    sq_md = f"""# SQ and memory-pipeline counters: mixed-precision step, N=128 28x28 C=512 31x31 pad 15, fp16 operands
 
+The default benchmark step's kernels (forward, data gradient, filter
+gradient and its reduction).  The same figures for every other kernel of
+the benchmark's per-configuration entries are in `configs.sq_counters.md`.
+
+{legend}
 {chr(10).join(sl)}
 """
+    cfg_sq_md = f"""# SQ and memory-pipeline counters: every per-configuration entry's kernels
+
+Every kernel the benchmark's per-configuration entries launch (the five
+configurations of the target, the strided backward and fp8 rows), except
+the default step's, which are in `{PROFILE_NAME}.sq_counters.md`.  Kernel
+names carry their template arguments (operand dtype first: 0 fp32, 1 bf16,
+2 fp16, 3 e4m3, 4 e5m2) and the workgroup count, which tells the launch
+sizes of one kernel apart; `configs.kernel_trace.md` maps them to the
+configurations.
+
+{legend}
+{chr(10).join(cl)}
+"""
+    with open(os.path.join(PROFILES, "configs.sq_counters.md"), "w") as f:
+        f.write(cfg_sq_md)
     with open(os.path.join(PROFILES, PROFILE_NAME + ".sq_counters.md"), "w") as f:
         f.write(sq_md)
     print(trace_md)
