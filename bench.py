@@ -948,27 +948,54 @@ The same numbers are in `traffic.json`, which `bench.py` reads for the
                 float(r["Counter_Value"]))
         return {k: {c: float(np.mean(v)) for c, v in cs.items()} for k, cs in out.items()}
     sq, pipe = counters("sq"), counters("pipe")
-    res = {}  # kernel key -> (VGPRs + AGPRs, LDS bytes, workgroup size, workgroups)
+    res = {}  # kernel key -> (LDS bytes, workgroup size, workgroups), from the trace
     for r in _csv_rows(os.path.join(d, "trace"), "*kernel_trace.csv"):
         if "dwc::" not in r["Kernel_Name"]:
             continue
         wg = int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"])
         blocks = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
-        res[_kernel_key(r["Kernel_Name"], blocks)] = (
-            int(r["VGPR_Count"]) + int(r["Accum_VGPR_Count"]), int(r["LDS_Block_Size"]), wg, blocks)
+        res[_kernel_key(r["Kernel_Name"], blocks)] = (int(r["LDS_Block_Size"]), wg, blocks)
+    # dynamic LDS of the packed kernels: the trace's LDS column shows static
+    # LDS only, so take the plan's figure for each launch
+    def plan_lds(s_, op, dt_, algo="auto"):
+        p_ = dwc.problem(s_.n, s_.h, s_.w, s_.c, s_.fh, s_.fw, (s_.stride_h, s_.stride_w),
+                         (s_.pad_h, s_.pad_w), DTYPE_CODE[dt_], algo)
+        desc = dwc.plan_describe(p_, {"fwd": 0, "bwd_data": 1, "bwd_filter": 2}[op])
+        kv_ = dict(t.split("=", 1) for t in desc.split()[2:] if "=" in t)
+        return int(kv_.get("lds", 0))
+    for s_, op, dt_, algo, ks_ in (
+            [(s_h, op, HEADLINE_DTYPE, "auto", kernels_of(dwc, s_h, op, HEADLINE_DTYPE))
+             for op in HEADLINE_OPS] +
+            [(case_shape(r["workload"], r["case"])[0], r["op"],
+              case_shape(r["workload"], r["case"])[1], r["algo"], r["kernels"].split("+"))
+             for r in details]):
+        lds_b = plan_lds(s_, op, dt_, algo)
+        if lds_b:
+            for k in kernel_matches(list(res), ks_[0]):
+                res[k] = (max(res[k][0], lds_b),) + res[k][1:]
+    # registers: the compiler's resource usage, recorded when the library was
+    # built (the trace's register columns are not used: on this device they
+    # read half the allocation)
+    regs_of = {}
+    rpath = os.path.join(ROOT, "depthwise_convolution_dwc_amd", "kernel_resources.json")
+    if os.path.exists(rpath):
+        for k, v in json.load(open(rpath)).items():
+            regs_of[k.replace("dwc::", "")] = v
 
     def occupancy(key):
-        """Waves per SIMD: the lowest of 8, the register file (512 per lane),
-        the LDS (160 KiB per CU, whole workgroups) and what the launch
-        provides (1024 SIMDs)."""
+        """Waves per SIMD: the lowest of what the registers allow (the
+        compiler's figure), the LDS (160 KiB per CU, whole workgroups) and
+        what the launch provides (1024 SIMDs)."""
         if key not in res:
             return "-"
-        regs, lds_b, wg, blocks = res[key]
+        lds_b, wg, blocks = res[key]
+        rv = regs_of.get(key.split("|")[0], {})
         wpg = max(1, -(-wg // 64))
-        by_regs = 512 // max(regs, 1)
+        by_regs = rv.get("waves_per_simd", 8)
         by_lds = (163840 // lds_b) * wpg / 4 if lds_b else 8
         by_launch = blocks * wpg / 1024
-        return (f"{min(8, by_regs, by_lds, by_launch):.1f} ({regs} regs, "
+        regs = rv.get("vgprs", 0) + rv.get("agprs", 0)
+        return (f"{min(8, by_regs, by_lds, by_launch):.1f} ({regs or '?'} VGPRs, "
                 f"{lds_b / 1024:.0f} KiB)")
 
     def sq_row(key):
@@ -1003,9 +1030,11 @@ The same numbers are in `traffic.json`, which `bench.py` reads for the
     cl = sq_head + [sq_row(k) for k in sorted(sq) if k not in step_keys]
     legend = f"""Columns, each counter averaged over the dispatches of one kernel at one
 launch size (rocprofv3 derived counters, two runs of their own):
-- waves / SIMD: what the kernel's registers (VGPRs + AGPRs of 512 per
-  lane), LDS (160 KiB per CU, whole workgroups) and launch size allow, from
-  the kernel trace's resource columns;
+- waves / SIMD: the lowest of what the kernel's registers allow (the
+  compiler's resource usage, recorded in `kernel_resources.json` when the
+  library is built), its LDS (160 KiB per CU, whole workgroups; the plan's
+  dynamic LDS, else the trace's static figure) and its launch size (1024
+  SIMDs);
 - VALU, MFMA, LDS: instructions per wave (`SQ_INSTS_*` / `SQ_WAVES`);
 - matrix cores busy: `SQ_VALU_MFMA_BUSY_CYCLES` per SIMD over
   `SQ_BUSY_CYCLES` per shader engine;

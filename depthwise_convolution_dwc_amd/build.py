@@ -8,7 +8,9 @@ this file as ``libdwc.so``.
 from __future__ import annotations
 
 import concurrent.futures as cf
+import json
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -22,6 +24,9 @@ LIB = os.path.join(PKG, "libdwc.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
+# Registers, occupancy and spills of every kernel, from the compiler's
+# resource-usage remarks (the profile summaries read it)
+RESOURCES = os.path.join(PKG, "kernel_resources.json")
 
 # Every HIP translation unit is built without packed-fp32 instructions.
 HIP_FLAGS = [
@@ -53,25 +58,67 @@ def _units():
     return u
 
 
+_REMARK = re.compile(r"remark:\s+(Function Name|VGPRs|AGPRs|Occupancy \[waves/SIMD\]|"
+                     r"VGPRs Spill|SGPRs Spill|LDS Size \[bytes/block\]):\s+(\S+)")
+_FIELDS = {"VGPRs": "vgprs", "AGPRs": "agprs", "Occupancy [waves/SIMD]": "waves_per_simd",
+           "VGPRs Spill": "vgpr_spill", "SGPRs Spill": "sgpr_spill",
+           "LDS Size [bytes/block]": "lds_static"}
+
+
+def _resource_remarks(text):
+    """{mangled kernel name: {field: int}} from -Rpass-analysis remarks."""
+    out, cur = {}, None
+    for m in _REMARK.finditer(text):
+        k, v = m.group(1), m.group(2)
+        if k == "Function Name":
+            cur = out.setdefault(v, {})
+        elif cur is not None:
+            cur[_FIELDS[k]] = int(v)
+    return out
+
+
 def _compile(unit, verbose):
     kind, src, obj, extra = unit
     src_p = os.path.join(CSRC, src)
     obj_p = os.path.join(BUILD, obj)
     if kind == "hip":
-        cmd = [HIPCC] + HIP_FLAGS + extra + ["-c", src_p, "-o", obj_p]
+        cmd = [HIPCC] + HIP_FLAGS + extra + ["-Rpass-analysis=kernel-resource-usage", "-c", src_p,
+                                             "-o", obj_p]
     else:
         cmd = ["g++"] + CXX_FLAGS + extra + ["-c", src_p, "-o", obj_p]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
-    # hipcc's host pass warns that it does not know the packed-fp32 feature
-    msgs = [ln for ln in (r.stdout + r.stderr).splitlines()
-            if "is not a recognized feature" not in ln]
+    text = r.stdout + r.stderr
+    res = _resource_remarks(text)
+    # hipcc's host pass warns that it does not know the packed-fp32 feature;
+    # the resource remarks are kept apart
+    msgs = [ln for ln in text.splitlines()
+            if "is not a recognized feature" not in ln and "kernel-resource-usage" not in ln]
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {src}\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs), flush=True)
-    return obj_p
+    return obj_p, res
+
+
+def _write_resources(res):
+    """Demangled kernel names ('dwc::fwd_sweep<0, 7, 7, false, false>') to
+    their registers, occupancy and spills."""
+    names = sorted(res)
+    demangled = names
+    if shutil.which("c++filt"):
+        r = subprocess.run(["c++filt"], input="\n".join(names), capture_output=True, text=True)
+        if r.returncode == 0 and len(r.stdout.splitlines()) == len(names):
+            demangled = r.stdout.splitlines()
+    table = {}
+    for mangled, dem in zip(names, demangled):
+        key = dem.split("(")[0].replace("void ", "").strip()
+        table[key] = res[mangled]
+    tmp = RESOURCES + ".tmp"
+    with open(tmp, "w") as f:
+        json.dump(table, f, indent=1, sort_keys=True)
+    os.replace(tmp, RESOURCES)
 
 
 def build(verbose: bool = False, jobs: int = 0) -> str:
@@ -82,7 +129,12 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
     units = _units()
     jobs = jobs or min(len(units), max(1, min(8, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda u: _compile(u, verbose), units))
+        done = list(ex.map(lambda u: _compile(u, verbose), units))
+    objs = [o for o, _ in done]
+    res = {}
+    for _, r in done:
+        res.update(r)
+    _write_resources(res)
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC",
            f"-Wl,--version-script={os.path.join(CSRC, 'libdwc.map')}", "-o", tmp] + objs
