@@ -33,11 +33,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            0x00020000);
 }
 
-// Cache-policy operand of a buffer store that marks it non-temporal.  Every
-// kernel output is written once and not read back by the same launch, so
-// streaming it past the caches keeps them for the operands: measured on
-// MI355X, the 7x7 forward sweep at N=64 56x56 C=128 fp32 drops from ~50 to
-// ~44 us.
+// Cache-policy operand of a buffer store that marks it non-temporal.  The
+// vector kernels write each output once, in whole lines per wave, and
+// nothing reads it back in the same launch, so their stores stream past
+// the caches and leave them to the operands (measured on MI355X with every
+// op rotating over >= 1 GiB: the stride-2 7x7 forward 34.8 -> 32.0 us, the
+// 7x7 sweeps within 1%).  The packed kernels, whose workgroups write parts
+// of a line that the L2 has to merge, use plain stores.
 constexpr int kStoreNT = 2;
 
 // Non-temporal store of one value at a per-lane address.

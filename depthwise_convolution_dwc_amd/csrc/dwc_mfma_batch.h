@@ -1,6 +1,8 @@
 // dwc_mfma_batch.h -- packed-MFMA forward-type kernel of libdwc with the
-// batch in the matrix rows (bf16/fp16 operands, gfx950
-// v_mfma_f32_32x32x16_{bf16,f16}, fp32 accumulation).
+// batch in the matrix rows, 32-image form (bf16/fp16 operands, gfx950
+// v_mfma_f32_32x32x16_{bf16,f16}, fp32 accumulation).  The planner takes it
+// where the 16-image form (dwc_mfma_batch16.h: half the cache lines per
+// staged row) does not apply, i.e. C % 16 != 0, or when asked for.
 //
 // The GEMV-to-GEMM packing of Flash-DWC (§4.2, Fig. 8) needs a second
 // matrix dimension next to the filter's Toeplitz band.  Here that dimension

@@ -80,8 +80,11 @@ typedef enum {
                              width <= 64 for the forward and data
                              gradient, input width <= 64 and FH <= 32 for
                              the filter gradient): the GEMV-to-GEMM
-                             packing of §4.2 on CDNA4 MFMA (fp8: the K=128
-                             fp8 MFMA, four filter or output rows per
+                             packing of §4.2 on CDNA4 MFMA, with the batch
+                             as the second matrix dimension of the
+                             forward and data gradient for widths up to 32
+                             and tall filters (fp8: also the K=128 fp8
+                             MFMA, four filter or output rows per
                              instruction, §7).  AUTO picks it wherever it
                              applies.  Operands must be finite: the packed
                              band multiplies every staged element by
