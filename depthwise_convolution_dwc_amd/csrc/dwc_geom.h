@@ -241,6 +241,45 @@ struct MfmaBatchArgs {
   uint64_t fw_magic;   // div_magic(FW): filter tap -> (row, column)
 };
 
+// fp32 matrix-core forward-type kernel (fwd_mfma_f32, stride 1, fp32
+// operands): v_mfma_f32_4x4x1_16b_f32 runs 16 independent 4 x 4 outer
+// products per instruction.  Block b is channel c0 + b, its 4 rows are 4
+// consecutive output rows, its 4 columns 4 consecutive output columns, and
+// the K step is one input column: a wave owns 16 channels x 4 output rows
+// x 4T output columns of one image.  The filter band (per filter row:
+// three zeros, the taps, zeros up to FWI + 3) sits in LDS, shared by the
+// workgroup's waves, which all take the same 16 channels.
+// Instantiated band widths (FWI); a filter of width FW <= 31 runs on the
+// smallest FWI >= FW, the missing taps being zeros.
+#define DWC_F32M_FW_LIST(M) M(13) M(17) M(21) M(27) M(31)
+#define DWC_F32M_T_LIST(M) M(2) M(4) M(7)
+constexpr int kF32mCb = 16;         // channels per wave (the 16 blocks)
+constexpr int kF32mRows = 4;        // output rows per wave (the matrix rows)
+constexpr int kF32mMaxWaves = 8;    // waves per workgroup
+constexpr int kF32mMinFh = 13;      // AUTO: from this many filter rows and columns
+constexpr int kF32mMinOw = 24;      // ... on outputs at least this wide
+constexpr int kF32mStageBatch = 8;  // 16-byte band loads in flight per thread
+constexpr int f32m_fwi(int fw) {
+  return fw <= 13 ? 13 : fw <= 17 ? 17 : fw <= 21 ? 21 : fw <= 27 ? 27 : fw <= 31 ? 31 : 0;
+}
+struct MfmaF32Args {
+  const void* in;    // N x IH x IW x C fp32 (X, or dY for the data gradient)
+  const void* filt;  // FH x FW x C fp32
+  float* out;        // N x OH x OW x C
+  int N, IH, IW, C, OH, OW;
+  int FH, FW, PH, PW;
+  int cblk;          // channel blocks of kF32mCb
+  int rg, cg;        // row groups (OH / 4) and column groups (OW / 4T) per image
+  int tiles;         // N * rg * cg wave tiles per channel block
+  int nw;            // waves per workgroup
+  int same;          // PW == (FWI - 1) / 2, FW == FWI and IW == OW: the first and
+                     // last column groups skip their padding columns
+  int groups;        // workgroups per channel block: ceil(tiles / nw)
+  int lds_bytes;     // FH x (FWI + 6) x 16 floats
+  int num_blocks;    // cblk * groups
+  uint64_t fw_magic; // div_magic(FW): filter tap -> (row, column)
+};
+
 // out[i] = sum_{z < Z} ws[z * M + j(i)], summed in order of z.  Plain
 // layout (cb = 0): j(i) = i.  Channel-blocked layout (cb > 0, C % cb == 0,
 // out = [tap][c] with C channels): each slice is [c / cb][tap][c % cb], so

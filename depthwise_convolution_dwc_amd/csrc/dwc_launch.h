@@ -44,6 +44,11 @@ hipError_t launch_fwd_mfma_batch(int dt, bool flip, const MfmaBatchArgs& a, hipS
 hipError_t launch_fwd_mfma_batch16(int dt, int ng, bool flip, const MfmaBatchArgs& a,
                                    hipStream_t s);
 
+// fp32 matrix-core forward-type kernel (fp32 operands, stride 1, FW <= 31,
+// C % 16 == 0): fwi the instantiated band width (DWC_F32M_FW_LIST), t the
+// 4-column output tiles per wave (DWC_F32M_T_LIST).
+hipError_t launch_fwd_mfma_f32(int fwi, int t, bool flip, const MfmaF32Args& a, hipStream_t s);
+
 // Packed fp8 MFMA forward-type kernel (e4m3 / e5m2 operands, stride 1,
 // 16x16x128 MFMAs over four filter rows each): nf 16-tap fragments per
 // filter row, tiles of 16 combinations per channel, 16 channels per

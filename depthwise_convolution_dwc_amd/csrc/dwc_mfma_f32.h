@@ -1,0 +1,239 @@
+// dwc_mfma_f32.h -- fp32 matrix-core forward-type kernel of libdwc (gfx950
+// v_mfma_f32_4x4x1_16b_f32, fp32 operands and accumulation).
+//
+// The GEMV-to-GEMM packing of Flash-DWC (§4.2, Fig. 8) turns one filter row
+// into a Toeplitz band so that adjacent outputs share one matrix operation.
+// On the fp32 matrix cores the narrowest such operation is the 16-block
+// 4x4x1 form: per block b, D[i][j] += A[i] * B[j].  Here
+//   block b      = channel c0 + b (16 channels per wave),
+//   row i        = output row oh0 + i (4 consecutive rows),
+//   column j     = output column ow0 + 4m + j of tile m (T tiles per wave),
+//   the K step   = one input column u, at filter row fh:
+//   A[i]         = x[oh0 + i + fh - PH][ow0 - PW + u]   (the same column, 4 rows)
+//   B[j]         = w[fh][u - 4m - j]                   (0 outside 0 .. FW-1)
+// A tile's 4 columns read the input columns u = 4m .. 4m + FW + 2, so
+// FW + 3 instructions cover 4 x FW taps: 31 / 34 of the work is useful at
+// FW = 31 (a 16-wide tile would keep 31 / 46).  The band depends on t = u - 4m
+// only, so one B register (per filter row and t) serves all T tiles, and
+// one A register (per input column) serves every tile whose taps reach it.
+//
+// Registers: A holds the wave's NA = 4T + FWI - 1 input columns for its 4
+// rows at the current filter row; moving to the next filter row shifts
+// every column down one row inside each lane quad (DPP) and brings the new
+// bottom row in, loaded 4 columns per instruction one filter row ahead.
+// The band (per filter row: 3 zeros, the taps, zeros to FWI + 3) sits in
+// LDS, shared by the workgroup's waves, which all take the same channels;
+// lane (b, j) reads its B at t as one dword, 64 lanes on 64 banks.
+// Instructions whose input column is padding are skipped (a uniform
+// branch); padding rows are never loaded (the row's buffer range is 0).
+// The waves need no barrier after the band is staged.
+#pragma once
+
+#include <type_traits>
+
+#include "dwc_device.h"
+
+namespace dwc {
+
+typedef float f32m_x4 __attribute__((ext_vector_type(4)));
+
+// Calls f(std::integral_constant<int, I>) for I = B .. E-1.
+template <int B, int E, typename F>
+__device__ __forceinline__ void f32m_static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    f32m_static_for<B + 1, E>(f);
+  }
+}
+
+// Lane q of each quad takes lane (q + 1) mod 4's value.
+__device__ __forceinline__ float quad_rotate_down(float v) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x39, 0xF, 0xF, false));
+}
+// Every lane of a quad takes lane K's value.
+template <int K>
+__device__ __forceinline__ float quad_bcast(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x55 * K, 0xF, 0xF, false));
+}
+
+template <int FWI, int T, bool FLIP>
+__global__ __launch_bounds__(64 * kF32mMaxWaves) void fwd_mfma_f32(MfmaF32Args a) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  constexpr int NT = FWI + 3;            // K steps (taps t) of one 4-column tile
+  constexpr int NA = 4 * T + FWI - 1;    // input columns a wave holds
+  constexpr int NS = (NA + 3) / 4;       // 4-column loads of a new row
+  constexpr int ZP = FWI + 6;            // band entries per filter row
+  float* band = reinterpret_cast<float*>(lds);  // [FH][ZP][kF32mCb]
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
+  if (blk >= a.num_blocks) return;  // the whole workgroup leaves together
+  // Logical ids run over the channel blocks first: neighbouring blocks read
+  // the two halves of the same 128-byte lines of a pixel.
+  const int cbk = blk % a.cblk;
+  const int grp = blk / a.cblk;
+  const int c0 = cbk * kF32mCb;
+  const int FH = a.FH, FW = a.FW, C = a.C;
+
+  // ---- the band: zeros, then the taps (turned by 180 degrees for FLIP),
+  // 4 channels per 16-byte load, kF32mStageBatch loads in flight per thread
+  const int bn = FH * ZP * kF32mCb / 4;
+  for (int e = tid; e < bn; e += nthr)
+    reinterpret_cast<f32m_x4*>(band)[e] = f32m_x4{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
+  {
+    const int taps = FH * FW;
+    const int items = taps * (kF32mCb / 4);
+    const auto frs = make_rsrc(a.filt, (uint32_t)taps * (uint32_t)C * 4u);
+    for (int e0 = 0; e0 < items; e0 += kF32mStageBatch * nthr) {
+      f32m_x4 v[kF32mStageBatch];
+#pragma unroll
+      for (int j = 0; j < kF32mStageBatch; ++j) {
+        const int e = e0 + j * nthr + tid;
+        const int tap = e >> 2, c4 = (e & 3) * 4;
+        const int src = FLIP ? taps - 1 - tap : tap;
+        const uint32_t off = e < items ? ((uint32_t)src * (uint32_t)C + (uint32_t)(c0 + c4)) * 4u : kOOB;
+        v[j] = __builtin_bit_cast(f32m_x4, __builtin_amdgcn_raw_buffer_load_b128(frs, (int)off, 0, 0));
+      }
+#pragma unroll
+      for (int j = 0; j < kF32mStageBatch; ++j) {
+        const int e = e0 + j * nthr + tid;
+        if (e < items) {
+          const int tap = e >> 2, c4 = (e & 3) * 4;
+          const int fh = fast_div(tap, a.fw_magic), fw = tap - fh * FW;
+          *reinterpret_cast<f32m_x4*>(band + (fh * ZP + fw + 3) * kF32mCb + c4) = v[j];
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- the wave's tile: image n, output rows oh0 .. oh0 + 3, columns
+  // ow0 .. ow0 + 4T - 1 (tiles of a channel block run over column groups,
+  // then row groups, then images).  The last column group ends at the
+  // image's right edge (it may overlap the one before it, whose shared
+  // columns both compute alike).
+  const int wave = uniform(tid >> 6);
+  const int tile = grp * a.nw + wave;
+  if (tile >= a.tiles) return;
+  int rest = tile;
+  const int cgi = rest % a.cg;
+  rest /= a.cg;
+  const int rgi = rest % a.rg;
+  const int n = rest / a.rg;
+  const int oh0 = rgi * kF32mRows;
+  const int ow0 = a.OW >= 4 * T ? min(cgi * 4 * T, a.OW - 4 * T) : 0;
+  const int lane = tid & 63, b = lane >> 2, q = lane & 3;
+  const int IH = a.IH, IW = a.IW, PH = a.PH, PW = a.PW;
+
+  const float* ximg = reinterpret_cast<const float*>(a.in) + (size_t)n * IH * IW * C;
+  const uint32_t rowb = (uint32_t)IW * (uint32_t)C * 4u;
+  // Lane (b, q) of a 4-column load takes column ow0 - PW + 4s + q of a row;
+  // negative columns wrap to offsets past any row's range.
+  const uint32_t loff = (uint32_t)(((ow0 - PW + q) * C + c0 + b) * 4);
+  const uint32_t sstep = (uint32_t)C * 16u;
+
+  // Filter rows whose 4 input rows are not all padding.
+  const int k_lo = max(0, PH - oh0 - (kF32mRows - 1));
+  const int k_hi = min(FH, IH + PH - oh0);
+
+  f32m_x4 D[T];
+#pragma unroll
+  for (int m = 0; m < T; ++m) D[m] = f32m_x4{0.f, 0.f, 0.f, 0.f};
+
+  // The filter rows of the tile.  L (R) leading (trailing) input columns of
+  // the window are known to be padding: their instructions are not issued.
+  auto run = [&](auto lc, auto rc) {
+    constexpr int L = decltype(lc)::value, R = decltype(rc)::value;
+    float A[NA];
+    {
+      // lane q: input row oh0 + q + k_lo - PH, every column of the window
+      const int r = oh0 + q + k_lo - PH;
+      const bool ok = r >= 0 && r < IH;
+      const auto irs = make_rsrc(ximg, (uint32_t)IH * rowb);
+      const uint32_t rbase = ok ? (uint32_t)r * rowb + (uint32_t)(c0 + b) * 4u : kOOB;
+#pragma unroll
+      for (int u = 0; u < NA; ++u) {
+        const int col = ow0 - PW + u;
+        A[u] = 0.f;
+        if (u >= L && u < NA - R && col >= 0 && col < IW)
+          A[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                               irs, (int)(rbase + (uint32_t)col * (uint32_t)C * 4u), 0, 0));
+      }
+    }
+    // every load above has landed before the loop (whose first instructions
+    // would otherwise wait for the loads it issues itself)
+    __builtin_amdgcn_s_waitcnt(0);
+    float nv[NS];
+    // lane (b, j): band entry t - j + 3 of channel b
+    const float* bl = band + (3 - q) * kF32mCb + b;
+    for (int k = k_lo; k < k_hi; ++k) {
+      const bool more = k + 1 < k_hi;
+      if (more) {
+        // the row that enters next: oh0 + 4 + k - PH for lane 3
+        const int r = oh0 + kF32mRows + k - PH;
+        const bool ok = r >= 0 && r < IH;
+        const auto rs = make_rsrc(ximg + (size_t)(ok ? r : 0) * IW * C, ok ? rowb : 0u);
+#pragma unroll
+        for (int s2 = 0; s2 < NS; ++s2)
+          nv[s2] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                 rs, (int)(loff + (uint32_t)s2 * sstep), 0, 0));
+      }
+      const float* bk = bl + k * (ZP * kF32mCb);
+      float bcur = bk[0];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const float bnext = t + 1 < NT ? bk[(t + 1) * kF32mCb] : 0.f;
+#pragma unroll
+        for (int m = 0; m < T; ++m) {
+          const int u = 4 * m + t;
+          if (u >= L && u < NA - R)
+            D[m] = __builtin_amdgcn_mfma_f32_4x4x1f32(A[u], bcur, D[m], 0, 0, 0);
+        }
+        bcur = bnext;
+      }
+      if (more) {
+        // lane q takes lane q + 1's row; lane 3 the new row (through lane 0:
+        // Y = new row in lane 0, then a rotation of the quad)
+        f32m_static_for<L, NA - R>([&](auto uc) {
+          constexpr int u = decltype(uc)::value;
+          const float nb = quad_bcast<u & 3>(nv[u >> 2]);  // outside the select: DPP reads every lane
+          const float y = q != 0 ? A[u] : nb;
+          A[u] = quad_rotate_down(y);
+        });
+      }
+    }
+  };
+  if (k_lo < k_hi) {
+    using Z = std::integral_constant<int, 0>;
+    using P = std::integral_constant<int, (FWI - 1) / 2>;
+    const bool el = a.same && ow0 == 0, er = a.same && ow0 + 4 * T == a.OW;
+    if (el && er) run(P{}, P{});
+    else if (el) run(P{}, Z{});
+    else if (er) run(Z{}, P{});
+    else run(Z{}, Z{});
+  }
+
+  // ---- outputs: register i of tile m is row oh0 + i, column ow0 + 4m + q
+  float* yimg = a.out + (size_t)n * a.OH * a.OW * C;
+  const uint32_t orowb = (uint32_t)a.OW * (uint32_t)C * 4u;
+  const uint32_t ooff = (uint32_t)(((ow0 + q) * C + c0 + b) * 4);
+#pragma unroll
+  for (int i = 0; i < kF32mRows; ++i) {
+    const int oh = oh0 + i;
+    if (oh >= a.OH) break;  // uniform
+    const auto ors = make_rsrc(yimg + (size_t)oh * a.OW * C, orowb);
+#pragma unroll
+    for (int m = 0; m < T; ++m) {
+      // the element is copied out first: this compiler's __builtin_bit_cast
+      // of a vector element expression reads element 0
+      const float v = D[m][i];
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ors,
+                                            (int)(ooff + (uint32_t)m * sstep), 0, 0);
+    }
+  }
+}
+
+}  // namespace dwc

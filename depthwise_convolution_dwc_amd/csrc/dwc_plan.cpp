@@ -284,6 +284,90 @@ bool plan_mfma_batch(const FwdArgs& f, int dt, bool flip, Plan* q) {
   return true;
 }
 
+// Issued 4x4x1 instructions per filter row of one row group for T-tile
+// waves (the column groups of plan_mfma_f32, the first and last skipping
+// their padding columns when `same`).
+static int64_t f32m_cost(int ow, int fwi, int t, bool same) {
+  const int na = 4 * t + fwi - 1, pwc = (fwi - 1) / 2;
+  const int cg = ow >= 4 * t ? (ow + 4 * t - 1) / (4 * t) : 1;
+  int64_t n = 0;
+  for (int g = 0; g < cg; ++g) {
+    const int ow0 = ow >= 4 * t ? std::min(g * 4 * t, ow - 4 * t) : 0;
+    const int l = same && ow0 == 0 ? pwc : 0;
+    const int r = same && ow0 + 4 * t == ow ? pwc : 0;
+    for (int m = 0; m < t; ++m)
+      for (int k = 0; k < fwi + 3; ++k) n += (4 * m + k >= l && 4 * m + k < na - r) ? 1 : 0;
+  }
+  return n;
+}
+
+// fp32 matrix-core plan (fwd_mfma_f32): false if the kernel does not apply.
+// fp32 operands, stride 1, C % 16 == 0, FW <= 31, FH <= 64 (the band of
+// every filter row in LDS), 32-bit offsets within one image.  AUTO takes it
+// from kF32mMinFh filter rows and columns (DWC_MFMA_F32: 0 never, 1 wherever
+// it applies).  The tile width T (4-column tiles per wave) issues the fewest
+// instructions over the output width; ties go to the wider tile.
+static bool plan_mfma_f32(const FwdArgs& f, int dt, bool flip, bool forced, Plan* q) {
+  if (dt != DT_F32 || f.SH != 1 || f.SW != 1 || f.C % kF32mCb != 0 || f.FW < 1 || f.FW > 31 ||
+      f.FH < 1 || f.FH > 64)
+    return false;
+  // AUTO: filters of at least kF32mMinFh rows and columns on outputs at
+  // least kF32mMinOw wide (MI355X, N=64 stages: 1.0-1.5x the vector kernels
+  // from 13x13 on at widths 56 and 28, slower at width 14), and the largest
+  // filters on the narrowest outputs (width 7: 1.07x at 27x27, 1.18x at
+  // 31x31).
+  const bool pick = f.FH >= kF32mMinFh && f.FW >= kF32mMinFh &&
+                    (f.OW >= kF32mMinOw || (f.OW <= 8 && f.FW >= 27));
+  const char* env = getenv("DWC_MFMA_F32");
+  if (!forced && (env ? atoi(env) == 0 : !pick)) return false;
+  if ((int64_t)f.IH * f.IW * f.C * 4 >= kI32Max || (int64_t)f.OH * f.OW * f.C * 4 >= kI32Max)
+    return false;
+  const int fwi = f32m_fwi(f.FW);
+  const bool same = f.PW == (fwi - 1) / 2 && f.FW == fwi && f.IW == f.OW;
+  int best_t = 0;
+  int64_t best = 0;
+  for (int t : {7, 4, 2}) {
+    const int64_t c = f32m_cost(f.OW, fwi, t, same);
+    if (best_t == 0 || c < best) {
+      best = c;
+      best_t = t;
+    }
+  }
+  if (const char* v = getenv("DWC_MFMA_F32_T")) {
+    const int t = atoi(v);
+    if (t == 7 || t == 4 || t == 2) best_t = t;
+  }
+  const int t = best_t;
+  MfmaF32Args m{};
+  m.N = f.N; m.IH = f.IH; m.IW = f.IW; m.C = f.C; m.OH = f.OH; m.OW = f.OW;
+  m.FH = f.FH; m.FW = f.FW; m.PH = f.PH; m.PW = f.PW;
+  m.cblk = f.C / kF32mCb;
+  m.rg = (f.OH + kF32mRows - 1) / kF32mRows;
+  m.cg = f.OW >= 4 * t ? (f.OW + 4 * t - 1) / (4 * t) : 1;
+  const int64_t tiles = (int64_t)f.N * m.rg * m.cg;
+  if (tiles > kI32Max) return false;
+  m.tiles = (int)tiles;
+  m.nw = (int)std::min<int64_t>(kF32mMaxWaves, tiles);
+  m.same = same ? 1 : 0;
+  m.groups = (int)((tiles + m.nw - 1) / m.nw);
+  const int64_t lds = (int64_t)f.FH * (fwi + 6) * kF32mCb * 4;
+  if (lds > kLdsPerCu) return false;
+  m.lds_bytes = (int)lds;
+  const int64_t blocks = (int64_t)m.cblk * m.groups;
+  if (blocks > kI32Max) return false;
+  m.num_blocks = (int)blocks;
+  m.fw_magic = div_magic((uint32_t)f.FW);
+  q->kind = PLAN_MFMA;
+  q->f32m = true;
+  q->f32m_fwi = fwi;
+  q->f32m_t = t;
+  q->flip = flip;
+  q->blocks = (int)blocks;
+  q->mf = m;
+  q->fa = f;
+  return true;
+}
+
 // Packed fp8 MFMA plan of a forward-type problem (e4m3 / e5m2 operands):
 // false if the kernel does not apply.  The tiling of plan_mfma, in bytes:
 // kMfma8Cb channels per workgroup, each 16x16x128 MFMA covering four filter
@@ -629,14 +713,16 @@ int make_plan(const dwc_problem* p, int op, Plan* pl, std::string* err) {
     // too: stride 1 is part of the kernel's conditions).
     if (p->algo == DWC_ALGO_AUTO || p->algo == DWC_ALGO_MFMA) {
       if (plan_mfma_batch(f, dt, bwd, &q) || plan_mfma(f, dt, bwd, &q) ||
-          plan_mfma8(f, dt, bwd, &q)) {
+          plan_mfma8(f, dt, bwd, &q) ||
+          plan_mfma_f32(f, dt, bwd, p->algo == DWC_ALGO_MFMA, &q)) {
         *pl = q;
         return DWC_OK;
       }
       if (p->algo == DWC_ALGO_MFMA)
         return fail(err, DWC_ERR_UNSUPPORTED,
-                    "no packed-MFMA kernel for this problem (needs bf16/fp16 with C % 8 == 0 "
-                    "or fp8 with C % 16 == 0, stride 1, FW <= 32, output width <= 64)");
+                    "no packed-MFMA kernel for this problem (needs bf16/fp16 with C % 8 == 0, "
+                    "fp8 with C % 16 == 0 or fp32 with C % 16 == 0 and FW <= 31, stride 1, "
+                    "FW <= 32, output width <= 64)");
     }
     if (direct && bwd && p->stride_h > 1) {
       const int S = p->stride_h;
@@ -899,6 +985,15 @@ std::string describe(const Plan& pl) {
              ops[pl.op], dt_name(pl.dt), w.FW, w.FH, pl.nfm, pl.nfn, pl.nk, pl.pf, pl.cb, w.xr,
              w.xp, w.dyp, w.dpad, w.hx, w.ix, w.e_lo, w.hd, w.id, w.lds_bytes, w.Z, w.ipb,
              w.cblk, pl.blocks, pl.ws_bytes);
+    return buf;
+  }
+  if (pl.kind == PLAN_MFMA && pl.f32m) {
+    const MfmaF32Args& m = pl.mf;
+    snprintf(buf, sizeof buf,
+             "%s mfma dt=%s fw=%d fh=%d flip=%d f32=1 fwi=%d t=%d rg=%d cg=%d tiles=%d nw=%d "
+             "same=%d cblk=%d lds=%d blocks=%d",
+             ops[pl.op], dt_name(pl.dt), m.FW, m.FH, (int)pl.flip, pl.f32m_fwi, pl.f32m_t, m.rg,
+             m.cg, m.tiles, m.nw, m.same, m.cblk, m.lds_bytes, pl.blocks);
     return buf;
   }
   if (pl.kind == PLAN_MFMA && pl.batch) {

@@ -44,6 +44,10 @@ struct Plan {
   int bimg = 0;  // images per instruction: 32 (fwd_mfma_batch) or 16 (fwd_mfma_batch16)
   int bng = 0;   // 16-column output groups of fwd_mfma_batch16 (1 or 2)
   MfmaBatchArgs mb{};
+  // fp32 matrix-core forward-type kernel
+  bool f32m = false;
+  int f32m_fwi = 0, f32m_t = 0;  // instantiated band width, 4-column tiles per wave
+  MfmaF32Args mf{};
   // packed-MFMA filter gradient
   int nfm = 0, nfn = 0, nk = 0, pf = 0;
   WgradMfmaArgs wm{};

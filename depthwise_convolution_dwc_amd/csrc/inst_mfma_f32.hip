@@ -1,0 +1,47 @@
+// inst_mfma_f32.hip -- instantiations and launcher of the fp32 matrix-core
+// forward-type kernel (fwd_mfma_f32).
+#include "dwc_launch.h"
+#include "dwc_mfma_f32.h"
+
+namespace dwc {
+namespace {
+
+template <int FWI, int T, bool FLIP>
+hipError_t go(const MfmaF32Args& a, hipStream_t s) {
+  auto kernel = fwd_mfma_f32<FWI, T, FLIP>;
+  if (a.lds_bytes > 65536) {
+    // dynamic LDS above the default 64 KiB is allowed once per kernel
+    static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                                    hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                    kLdsPerCu);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kernel, dim3(a.num_blocks), dim3(64 * a.nw), a.lds_bytes, s, a);
+  return hipGetLastError();
+}
+
+template <int FWI, bool FLIP>
+hipError_t by_t(int t, const MfmaF32Args& a, hipStream_t s) {
+#define DWC_CASE(TT) \
+  if (t == TT) return go<FWI, TT, FLIP>(a, s);
+  DWC_F32M_T_LIST(DWC_CASE)
+#undef DWC_CASE
+  return hipErrorInvalidValue;
+}
+
+template <bool FLIP>
+hipError_t by_fw(int fwi, int t, const MfmaF32Args& a, hipStream_t s) {
+#define DWC_CASE(F) \
+  if (fwi == F) return by_t<F, FLIP>(t, a, s);
+  DWC_F32M_FW_LIST(DWC_CASE)
+#undef DWC_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_fwd_mfma_f32(int fwi, int t, bool flip, const MfmaF32Args& a, hipStream_t s) {
+  return flip ? by_fw<true>(fwi, t, a, s) : by_fw<false>(fwi, t, a, s);
+}
+
+}  // namespace dwc

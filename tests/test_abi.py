@@ -107,12 +107,47 @@ def test_plans_for_the_named_workloads():
     d = dwc.plan_describe(p, 2)
     assert d.startswith("bwd_filter sweep")
     p = dwc.problem(32, 56, 56, 128, 31, 31, 1, 15)
-    assert dwc.plan_describe(p, 0).startswith("fwd direct")
+    d = dwc.plan_describe(p, 0)
+    assert d.startswith("fwd mfma dt=f32") and " f32=1 fwi=31 t=7 " in d and " same=1 " in d, d
+    assert " rg=14 cg=2 tiles=896 " in d, d
+    assert dwc.plan_describe(p, 1).startswith("bwd_data mfma dt=f32")
     assert dwc.plan_describe(p, 2).startswith("bwd_filter direct")
     p = dwc.problem(64, 56, 56, 128, 7, 7, 2, 3)
     assert "sw=2" in dwc.plan_describe(p, 0)
     p = dwc.problem(128, 28, 28, 512, 13, 13, 1, 6, dtype=dwc.BF16)
     assert "dt=bf16" in dwc.plan_describe(p, 0)
+
+
+def test_fp32_mfma_plans_and_rejections(monkeypatch):
+    monkeypatch.delenv("DWC_MFMA_F32", raising=False)
+    # AUTO: large filters on outputs at least 24 wide, and 27x27 and up on
+    # outputs at most 8 wide; the vector kernels elsewhere
+    for (h, c, f, want) in ((56, 128, 13, True), (28, 256, 31, True), (14, 512, 31, False),
+                            (7, 1024, 31, True), (7, 1024, 21, False), (56, 128, 9, False)):
+        p = dwc.problem(64, h, h, c, f, f, 1, f // 2)
+        d = dwc.plan_describe(p, 0)
+        assert (" f32=1 " in d) == want, (h, f, d)
+    # the band width rounds the filter width up; tiles per wave and groups
+    d = dwc.plan_describe(dwc.problem(2, 12, 20, 16, 5, 11, 1, (2, 3), algo="mfma"), 0)
+    assert " fw=11 fh=5 " in d and " fwi=13 " in d and " same=0 " in d, d
+    # width 57: four right-aligned 16-column groups issue fewer instructions
+    # than three 28-column ones (the last two overlapping in 27 columns)
+    d = dwc.plan_describe(dwc.problem(2, 30, 57, 16, 21, 21, 1, 10, algo="mfma"), 0)
+    assert " t=4 " in d and " cg=4 " in d and " rg=8 " in d and " same=1 " in d, d
+    monkeypatch.setenv("DWC_MFMA_F32_T", "2")
+    d = dwc.plan_describe(dwc.problem(2, 30, 57, 16, 21, 21, 1, 10, algo="mfma"), 0)
+    assert " t=2 " in d and " cg=8 " in d, d
+    monkeypatch.delenv("DWC_MFMA_F32_T")
+    # the band of 64 filter rows of width 31 fits one CU's LDS
+    d = dwc.plan_describe(dwc.problem(1, 70, 40, 16, 64, 31, 1, 0, algo="mfma"), 0)
+    assert " lds=151552 " in d, d
+    # rejections: C % 16, FW > 31, FH > 64, stride 2, half precision
+    for args, kw in (((1, 20, 20, 24, 13, 13, 1, 6), {}), ((1, 40, 40, 16, 32, 32, 1, 0), {}),
+                     ((1, 70, 8, 16, 65, 3, 1, 0), {}), ((1, 20, 20, 16, 13, 13, 2, 6), {})):
+        p = dwc.problem(*args, algo="mfma")
+        assert dwc.check(p, 0) == 2, args  # DWC_ERR_UNSUPPORTED
+    monkeypatch.setenv("DWC_MFMA_F32", "0")
+    assert " f32=1 " not in dwc.plan_describe(dwc.problem(32, 56, 56, 128, 31, 31, 1, 15), 0)
 
 
 def test_workspace_size_matches_split():
@@ -200,11 +235,13 @@ def test_mfma_plans_and_rejections(monkeypatch):
     p = dwc.problem(128, 28, 28, 512, 13, 13, 1, 6, dtype=dwc.BF16, algo="direct")
     assert dwc.plan_describe(p, 0).startswith("fwd direct")
     assert dwc.plan_describe(p, 2).startswith("bwd_filter direct")
-    # conditions of the packed kernels: half-precision operands, stride 1,
-    # C a multiple of 8, FW <= 32, output width <= 64 (forward), input width
-    # <= 64 and FH <= 32 (filter gradient)
+    # conditions of the packed kernels: half-precision operands (fp32: the
+    # forward and data gradient, C a multiple of 16), stride 1, C a multiple
+    # of 8, FW <= 32, output width <= 64 (forward), input width <= 64 and FH
+    # <= 32 (filter gradient)
     base = dict(n=2, h=20, w=20, c=16, fh=5, fw=5, stride=1, pad=2, dtype=dwc.BF16)
-    for kw, ops in ((dict(dtype=dwc.F32), (0, 1, 2)), (dict(stride=2), (0, 1, 2)),
+    for kw, ops in ((dict(dtype=dwc.F32), (2,)), (dict(dtype=dwc.F32, c=24), (0, 1, 2)),
+                    (dict(stride=2), (0, 1, 2)),
                     (dict(c=12), (0, 1, 2)), (dict(fw=33, pad=16), (0, 1, 2)),
                     (dict(w=80), (0, 2)), (dict(fh=33, pad=16), (2,))):
         a = dict(base, **kw)
@@ -416,10 +453,13 @@ def test_algo_codes_match_the_header():
     for name, code in dwc.ALGO.items():
         assert h["DWC_ALGO_" + name.upper()] == code
     # algo 2 asks for the packed-MFMA kernels: bf16 at stride 1 has them,
-    # fp32 does not
+    # fp32 for the forward-type ops only, and not at stride 2
     p = dwc.problem(1, 16, 16, 16, 5, 5, 1, 2, dtype=dwc.BF16, algo=2)
     assert dwc.check(p, 0) == 0 and " mfma " in dwc.plan_describe(p, 0)
     q = dwc.problem(1, 16, 16, 16, 5, 5, 1, 2, dtype=dwc.F32, algo=2)
+    assert dwc.check(q, 0) == 0 and " f32=1 " in dwc.plan_describe(q, 0)
+    assert dwc.check(q, 2) == 2
+    q = dwc.problem(1, 16, 16, 16, 5, 5, 2, 2, dtype=dwc.F32, algo=2)
     assert dwc.check(q, 0) == 2
 
 

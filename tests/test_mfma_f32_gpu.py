@@ -1,0 +1,89 @@
+"""GPU parity of the fp32 matrix-core forward-type kernel (fwd_mfma_f32)
+against the float64 oracle: every element, forward and data gradient, each
+tile width (2, 4 and 7 four-column tiles per wave) and each instantiated band
+width, over shapes with ragged batches, rows, columns and channel blocks,
+filters narrower than their band (zero taps), unequal and cropping padding,
+images smaller than the filter, and outputs that must be overwritten
+completely."""
+
+import pytest
+
+from dwc_inputs import make_inputs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # collected on CPU too; skipped there
+    pytest.skip("no GPU", allow_module_level=True)
+
+from gpu_helpers import check_parity, dwc, log, sync, to_device  # noqa: E402
+from test_parity_gpu import DT, OPS, _run, _shape, _want_mag  # noqa: E402
+
+# (n, h, w, c, fh, fw, stride, pad)
+F32M_SHAPES = [
+    (2, 14, 14, 32, 13, 13, 1, 6),
+    (3, 9, 23, 16, 17, 17, 1, 8),
+    (1, 28, 28, 48, 31, 31, 1, 15),
+    (2, 30, 57, 16, 21, 21, 1, 10),
+    (2, 11, 13, 32, 9, 13, 1, (4, 6)),
+    (1, 7, 7, 16, 31, 31, 1, 15),
+    (2, 16, 16, 64, 27, 27, 1, 13),
+    (2, 12, 20, 16, 5, 11, 1, (2, 3)),
+    (1, 10, 10, 16, 13, 13, 1, 14),
+    (2, 20, 9, 32, 15, 3, 1, (7, 1)),
+    (5, 6, 40, 16, 1, 31, 1, (0, 15)),
+    (1, 40, 8, 16, 64, 7, 1, (31, 3)),
+    (3, 56, 56, 16, 31, 31, 1, 15),
+]
+
+
+def _ids(t):
+    return "x".join(map(str, t[:6])) + f"_p{t[7]}"
+
+
+@pytest.mark.parametrize("tile", ["auto", "2", "4", "7"])
+@pytest.mark.parametrize("op", ["fwd", "bwd_data"])
+@pytest.mark.parametrize("shape", F32M_SHAPES, ids=_ids)
+def test_mfma_f32_parity(shape, op, tile, monkeypatch):
+    if tile != "auto":
+        monkeypatch.setenv("DWC_MFMA_F32_T", tile)
+    s = _shape(shape)
+    p = dwc.problem(s.n, s.h, s.w, s.c, s.fh, s.fw, 1, (s.pad_h, s.pad_w), dtype=DT["f32"],
+                    algo="mfma")
+    d = dwc.plan_describe(p, OPS[op])
+    assert " f32=1 " in d, d
+    if tile != "auto":
+        assert f" t={tile} " in d, d
+    inp = make_inputs(s, "f32", seed=70 + sum(shape[:6]))
+    want, mag = _want_mag(op, s, inp)
+    log(f"case mfma f32 {shape} {op} t={tile}: {d}")
+    got = _run(op, s, inp, "mfma")
+    check_parity(got, want, mag, op, s, "f32", what=f"t={tile}")
+
+
+@pytest.mark.parametrize("shape", [(2, 14, 14, 32, 13, 13, 1, 6), (2, 30, 57, 16, 21, 21, 1, 10)],
+                         ids=_ids)
+def test_mfma_f32_outputs_fully_overwritten(shape):
+    s = _shape(shape)
+    inp = make_inputs(s, "f32", seed=71)
+    pad = (s.pad_h, s.pad_w)
+    y = torch.full(s.y_shape(), float("nan"), device="cuda")
+    dwc.fwd(to_device(inp.x), to_device(inp.w), 1, pad, out=y, algo="mfma")
+    dx = torch.full(s.x_shape(), float("nan"), device="cuda")
+    dwc.bwd_data(to_device(inp.dy), to_device(inp.w), (s.h, s.w), 1, pad, out=dx, algo="mfma")
+    sync()
+    for op, t in (("fwd", y), ("bwd_data", dx)):
+        want, mag = _want_mag(op, s, inp)
+        check_parity(t.double().cpu().numpy(), want, mag, op, s, "f32", what=op)
+
+
+def test_mfma_f32_deterministic():
+    """Overlapping column groups write the same values: two runs agree bit
+    for bit."""
+    s = _shape((2, 30, 57, 16, 21, 21, 1, 10))
+    inp = make_inputs(s, "f32", seed=72)
+    x, w = to_device(inp.x), to_device(inp.w)
+    a = dwc.fwd(x, w, 1, 10, algo="mfma")
+    b = dwc.fwd(x, w, 1, 10, algo="mfma")
+    sync()
+    assert torch.equal(a, b)
