@@ -46,16 +46,23 @@ __device__ __forceinline__ void f32m_static_for(F&& f) {
   }
 }
 
-// Lane q of each quad takes lane (q + 1) mod 4's value.
-__device__ __forceinline__ float quad_rotate_down(float v) {
-  return __builtin_bit_cast(float,
-                            __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x39, 0xF, 0xF, false));
-}
-// Every lane of a quad takes lane K's value.
+// One filter row down in a quad of rows: lanes 0-2 take lanes 1-3 of a,
+// lane 3 takes lane K of n (keep = 1, put = 0 in lanes 0-2; the reverse in
+// lane 3).  Two VALU instructions: a v_mul_f32 with the rotation as its DPP
+// source (the compiler folds the move into it), then a v_fmac_f32 with the
+// broadcast of n as its DPP source, which the compiler does not form.  The
+// products by 1 and 0 are exact, so are the sums with one zero term, for
+// finite operands.  The fmac's DPP operand comes from a load (no VALU
+// write before a DPP read), its accumulator from the preceding VALU
+// instruction (not a DPP operand).
 template <int K>
-__device__ __forceinline__ float quad_bcast(float v) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x55 * K, 0xF, 0xF, false));
+__device__ __forceinline__ float quad_shift_in(float a, float n, float keep, float put) {
+  float x = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, a),
+                                                                  0x39, 0xF, 0xF, true)) * keep;
+  asm("v_fmac_f32_dpp %0, %1, %2 quad_perm:[%3,%3,%3,%3] row_mask:0xf bank_mask:0xf bound_ctrl:1"
+      : "+v"(x)
+      : "v"(n), "v"(put), "i"(K));
+  return x;
 }
 
 template <int FWI, int T, bool FLIP>
@@ -167,6 +174,8 @@ __global__ __launch_bounds__(64 * kF32mMaxWaves) void fwd_mfma_f32(MfmaF32Args a
     // would otherwise wait for the loads it issues itself)
     __builtin_amdgcn_s_waitcnt(0);
     float nv[NS];
+    // 1 in lanes 0-2 of each quad, 0 in lane 3; and the reverse
+    const float keep = q == kF32mRows - 1 ? 0.f : 1.f, put = 1.f - keep;
     // lane (b, j): band entry t - j + 3 of channel b
     const float* bl = band + (3 - q) * kF32mCb + b;
     for (int k = k_lo; k < k_hi; ++k) {
@@ -199,9 +208,7 @@ __global__ __launch_bounds__(64 * kF32mMaxWaves) void fwd_mfma_f32(MfmaF32Args a
         // Y = new row in lane 0, then a rotation of the quad)
         f32m_static_for<L, NA - R>([&](auto uc) {
           constexpr int u = decltype(uc)::value;
-          const float nb = quad_bcast<u & 3>(nv[u >> 2]);  // outside the select: DPP reads every lane
-          const float y = q != 0 ? A[u] : nb;
-          A[u] = quad_rotate_down(y);
+          A[u] = quad_shift_in<u & 3>(A[u], nv[u >> 2], keep, put);
         });
       }
     }
