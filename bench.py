@@ -339,7 +339,10 @@ def kernels_of(dwc, s, op, dtype="f32", algo="auto"):
         else "false"
     blocks = kv.get("blocks")
     if fam == "mfma":
-        if op == "bwd_filter":
+        if kv.get("f32") == "1":  # fp32 matrix-core kernels
+            k = (f"wgrad_mfma_f32<{kv['tw']}, {kv['nb']}>" if op == "bwd_filter" else
+                 f"fwd_mfma_f32<{kv['fwi']}, {kv['t']}, {flip}>")
+        elif op == "bwd_filter":
             k = f"wgrad_mfma{'8' if dt >= 3 else ''}<{dt}, {kv['nfm']}, {kv['nfn']}, {kv['nk']}, " \
                 f"{kv['pf']}>"
         elif kv.get("batch") == "1" and kv.get("imgs") == "16":

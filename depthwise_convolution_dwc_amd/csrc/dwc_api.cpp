@@ -133,6 +133,17 @@ int run_bwd_filter(const dwc_problem* p, const Plan& pl, const void* x, const vo
   // One slice writes dW directly; several write partials to the workspace.
   float* part = pl.ws_bytes > 0 ? (float*)workspace : (float*)dw;
   hipError_t e;
+  if (pl.kind == PLAN_MFMA && pl.wf32) {
+    WgradF32Args w = pl.wf;
+    w.x = x;
+    w.dy = dy;
+    w.ws = (float*)workspace;
+    e = launch_wgrad_mfma_f32(pl.wf32_tw, pl.wf32_nb, w, s);
+    if (e != hipSuccess) return hip_fail(e, "dwc_bwd_filter launch");
+    e = launch_reduce(
+        ReduceArgs{(const float*)workspace, (float*)dw, m, pl.z, kWf32Cb, w.C, w.FH * w.FW}, s);
+    return e == hipSuccess ? DWC_OK : hip_fail(e, "dwc_bwd_filter reduce");
+  }
   if (pl.kind == PLAN_MFMA) {
     WgradMfmaArgs w = pl.wm;
     w.x = x;

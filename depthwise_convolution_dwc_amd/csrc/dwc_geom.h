@@ -280,6 +280,36 @@ struct MfmaF32Args {
   uint64_t fw_magic; // div_magic(FW): filter tap -> (row, column)
 };
 
+// fp32 matrix-core filter gradient (wgrad_mfma_f32, stride 1): per block
+// b (channel c0 + b) of v_mfma_f32_4x4x1_16b_f32,
+//   D[i][j] = dW[4h + j][4f + i] += x[r][ow + 4f + i - PW] * dy[r - 4h - j + PH][ow]
+// over the K steps (image, input row r, output column ow).  A wave owns one
+// filter-row tile h (4 rows) and every column tile f < TW of a channel
+// block, over OWW = 4 NB output columns; a workgroup's waves are the
+// ceil(FH / 4) row tiles, sharing one staged X row at a time (LDS, double
+// buffered); each wave keeps its 4 dY rows per output column in registers,
+// moved down a lane quad per input row.  Slices of consecutive (image,
+// input row) pairs, times the column groups, write channel-blocked partials
+// (cb = 16) that reduce_partials sums.
+#define DWC_WF32_TW_LIST(M) M(1) M(2) M(3) M(4) M(5) M(6) M(7) M(8)
+#define DWC_WF32_NB_LIST(M) M(2) M(4) M(7) M(14)
+constexpr int kWf32Cb = 16;          // channels per workgroup (the 16 blocks)
+constexpr int kWf32MaxWaves = 8;     // FH <= 32
+constexpr int kWf32StageItems = 2;   // 16-byte X staging items per thread, at most
+constexpr int kWf32MinF = 12;        // AUTO: from this filter size (rows and columns)
+struct WgradF32Args {
+  const void* x;     // N x IH x IW x C fp32
+  const void* dy;    // N x OH x OW x C fp32
+  float* ws;         // (Z * cg) x cblk x (FH * FW) x 16 partial sums
+  int N, IH, IW, C, OH, OW;
+  int FH, FW, PH, PW;
+  int cblk, cg, Z;   // channel blocks, column groups, row slices
+  int rps;           // (image, input row) pairs per slice
+  int nw;            // waves per workgroup: filter-row tiles
+  int lds_bytes;
+  int num_blocks;    // cblk * cg * Z
+};
+
 // out[i] = sum_{z < Z} ws[z * M + j(i)], summed in order of z.  Plain
 // layout (cb = 0): j(i) = i.  Channel-blocked layout (cb > 0, C % cb == 0,
 // out = [tap][c] with C channels): each slice is [c / cb][tap][c % cb], so

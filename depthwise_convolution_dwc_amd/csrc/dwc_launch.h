@@ -49,6 +49,12 @@ hipError_t launch_fwd_mfma_batch16(int dt, int ng, bool flip, const MfmaBatchArg
 // 4-column output tiles per wave (DWC_F32M_T_LIST).
 hipError_t launch_fwd_mfma_f32(int fwi, int t, bool flip, const MfmaF32Args& a, hipStream_t s);
 
+// fp32 matrix-core filter gradient (fp32 operands, stride 1, FH and FW <=
+// 32, C % 16 == 0): tw = ceil(FW / 4) column tiles, nb 4-column output
+// groups per wave (DWC_WF32_NB_LIST).  Writes channel-blocked slice
+// partials (reduce with cb = kWf32Cb).
+hipError_t launch_wgrad_mfma_f32(int tw, int nb, const WgradF32Args& a, hipStream_t s);
+
 // Packed fp8 MFMA forward-type kernel (e4m3 / e5m2 operands, stride 1,
 // 16x16x128 MFMAs over four filter rows each): nf 16-tap fragments per
 // filter row, tiles of 16 combinations per channel, 16 channels per

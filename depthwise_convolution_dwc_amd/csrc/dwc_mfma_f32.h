@@ -65,6 +65,20 @@ __device__ __forceinline__ float quad_shift_in(float a, float n, float keep, flo
   return x;
 }
 
+// One input row on in a quad of dY rows (lane j holds row r - j): lanes 1-3
+// take lanes 0-2 of a, lane 0 takes lane K of n (keep = 0 in lane 0, 1
+// elsewhere; put the reverse).  The same two instructions as quad_shift_in,
+// with the rotation the other way.
+template <int K>
+__device__ __forceinline__ float quad_shift_up_in(float a, float n, float keep, float put) {
+  float x = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, a),
+                                                                  0x93, 0xF, 0xF, true)) * keep;
+  asm("v_fmac_f32_dpp %0, %1, %2 quad_perm:[%3,%3,%3,%3] row_mask:0xf bank_mask:0xf bound_ctrl:1"
+      : "+v"(x)
+      : "v"(n), "v"(put), "i"(K));
+  return x;
+}
+
 template <int FWI, int T, bool FLIP>
 __global__ __launch_bounds__(64 * kF32mMaxWaves) void fwd_mfma_f32(MfmaF32Args a) {
   extern __shared__ __align__(16) unsigned char lds[];
@@ -240,6 +254,163 @@ __global__ __launch_bounds__(64 * kF32mMaxWaves) void fwd_mfma_f32(MfmaF32Args a
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ors,
                                             (int)(ooff + (uint32_t)m * sstep), 0, 0);
     }
+  }
+}
+
+// ---- filter gradient (layout and mapping: WgradF32Args)
+template <int TW, int NB>
+__global__ __launch_bounds__(64 * kWf32MaxWaves, 4) void wgrad_mfma_f32(WgradF32Args a) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  constexpr int OWW = 4 * NB;             // output columns per wave
+  constexpr int NU = OWW + 4 * TW - 3;    // 4-column X windows u
+  constexpr int XP = NU + 3;              // staged pixels per X row
+  float* xb = reinterpret_cast<float*>(lds);  // [2][XP][kWf32Cb]
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
+  if (blk >= a.num_blocks) return;  // the whole workgroup leaves together
+  // channel blocks first (neighbours share the lines of a pixel), then
+  // column groups, then row slices
+  const int cbk = blk % a.cblk;
+  int rest = blk / a.cblk;
+  const int cgi = rest % a.cg;
+  const int z = rest / a.cg;
+  const int c0 = cbk * kWf32Cb;
+  const int ow0 = cgi * OWW;
+  const int h = uniform(tid >> 6);        // the wave's filter-row tile
+  const int lane = tid & 63, b = lane >> 2, q = lane & 3;
+  const int C = a.C, IH = a.IH, IW = a.IW, OH = a.OH, OW = a.OW, PH = a.PH, PW = a.PW;
+  const int npairs = a.N * IH;
+  const int p0 = z * a.rps;
+  const int p1 = min(p0 + a.rps, npairs);
+  const uint32_t xrow = (uint32_t)IW * (uint32_t)C * 4u;
+
+  // ---- X staging: item e = (pixel e / 4, channels 4 (e % 4) .. + 3) of the
+  // row; pixel p is input column ow0 - PW + p
+  const int items = XP * (kWf32Cb / 4);
+  f32m_x4 xv[kWf32StageItems];
+  auto x_fetch = [&](int n, int r) {
+    const auto rs = make_rsrc(reinterpret_cast<const float*>(a.x) + ((size_t)n * IH + r) * IW * C,
+                              xrow);
+#pragma unroll
+    for (int k = 0; k < kWf32StageItems; ++k) {
+      const int e = tid + k * nthr;
+      const int col = ow0 - PW + (e >> 2);
+      const uint32_t off = e < items ? (uint32_t)((col * C + c0 + (e & 3) * 4) * 4) : kOOB;
+      xv[k] = __builtin_bit_cast(f32m_x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0));
+    }
+  };
+  auto x_commit = [&](int buf) {
+#pragma unroll
+    for (int k = 0; k < kWf32StageItems; ++k) {
+      const int e = tid + k * nthr;
+      if (e < items)
+        *reinterpret_cast<f32m_x4*>(xb + (buf * XP + (e >> 2)) * kWf32Cb + (e & 3) * 4) = xv[k];
+    }
+  };
+
+  // ---- dY rows: lane (b, j) of Bw[o] holds dy[r - 4h - j + PH][ow0 + o]
+  float Bw[OWW];
+  float nv[NB];
+  const float keep = q != 0 ? 1.f : 0.f, put = 1.f - keep;
+  // Each load below has its own buffer resource (scalar registers) starting
+  // at its column, so that all of them share one lane offset register; the
+  // resource's range still ends at the row's (image's) end.
+  const float* dyc = reinterpret_cast<const float*>(a.dy) + (size_t)ow0 * C;  // column ow0
+  const int wcols = OW - ow0;  // columns of the row from ow0 on
+  const uint32_t qoff = (uint32_t)((q * C + c0 + b) * 4);
+  auto dy_fetch = [&](int n, int row) {  // row `row` of image n, 4 columns per load
+    const bool ok = row >= 0 && row < OH;
+    const float* rp = dyc + ((size_t)n * OH + (ok ? row : 0)) * OW * C;
+#pragma unroll
+    for (int s2 = 0; s2 < NB; ++s2) {
+      const int left = wcols - 4 * s2;  // columns of the row from this load's first on
+      const auto rs = make_rsrc(rp + (size_t)(4 * s2) * C,
+                                ok && left > 0 ? (uint32_t)(left * C) * 4u : 0u);
+      nv[s2] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)qoff, 0, 0));
+    }
+  };
+  auto dy_shift = [&]() {  // the fetched row into lane 0, the others one lane on
+    f32m_static_for<0, OWW>([&](auto oc) {
+      constexpr int o = decltype(oc)::value;
+      Bw[o] = quad_shift_up_in<o & 3>(Bw[o], nv[o >> 2], keep, put);
+    });
+  };
+  // the window of image n at input row r: its 4 rows shifted in, the
+  // highest last
+  auto dy_init = [&](int n, int r) {
+#pragma unroll
+    for (int o = 0; o < OWW; ++o) Bw[o] = 0.f;
+    for (int j = 3; j >= 0; --j) {
+      dy_fetch(n, r - 4 * h - j + PH);
+      dy_shift();
+    }
+  };
+
+  f32m_x4 D[TW];
+#pragma unroll
+  for (int f = 0; f < TW; ++f) D[f] = f32m_x4{0.f, 0.f, 0.f, 0.f};
+  if (p0 < p1) {
+    int n = p0 / IH, r = p0 - (p0 / IH) * IH;
+    x_fetch(n, r);
+    x_commit(0);
+    dy_init(n, r);
+    // every load above has landed before the loop (whose first instructions
+    // would otherwise wait for the loads it issues itself)
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // lane (b, i) of window u reads staged pixel u + i, channel b
+    const float* xl = xb + q * kWf32Cb + b;
+    for (int p = p0; p < p1; ++p) {
+      const int buf = (p - p0) & 1;
+      const bool more = p + 1 < p1;
+      const bool same_img = r + 1 < IH;
+      if (more) {
+        x_fetch(same_img ? n : n + 1, same_img ? r + 1 : 0);
+        if (same_img) dy_fetch(n, r + 1 - 4 * h + PH);
+      }
+      // this wave's 4 dY rows r - 4h - 3 + PH .. r - 4h + PH
+      const int hi = r - 4 * h + PH;
+      if (hi >= 0 && hi - 3 < OH && 4 * h < a.FH) {
+        const float* xr = xl + buf * (XP * kWf32Cb);
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+          const float xa = xr[u * kWf32Cb];
+#pragma unroll
+          for (int f = 0; f < TW; ++f) {
+            const int o = u - 4 * f;
+            if (o >= 0 && o < OWW) D[f] = __builtin_amdgcn_mfma_f32_4x4x1f32(xa, Bw[o], D[f], 0, 0, 0);
+          }
+        }
+      }
+      if (more) {
+        x_commit(buf ^ 1);
+        if (same_img) {
+          dy_shift();
+          ++r;
+        } else {
+          ++n;
+          r = 0;
+          dy_init(n, 0);
+          __builtin_amdgcn_s_waitcnt(0);
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- the slice's partial: register i of tile f is dW[4h + q][4f + i]
+  const int taps = a.FH * a.FW;
+  float* part = a.ws + ((size_t)(z * a.cg + cgi) * a.cblk + cbk) * taps * kWf32Cb + b;
+  const int fh = 4 * h + q;
+  if (fh < a.FH) {
+#pragma unroll
+    for (int f = 0; f < TW; ++f)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int fw = 4 * f + i;
+        if (fw < a.FW) part[(fh * a.FW + fw) * kWf32Cb] = D[f][i];
+      }
   }
 }
 

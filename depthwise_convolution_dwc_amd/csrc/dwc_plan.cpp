@@ -522,6 +522,76 @@ bool plan_wgrad_mfma(const dwc_problem* p, int64_t oh, int64_t ow, Plan* q) {
 }
 
 
+// fp32 matrix-core filter-gradient plan (wgrad_mfma_f32): false if the
+// kernel does not apply.  fp32 operands, stride 1, FH and FW <= 32, C % 16
+// == 0, 32-bit offsets within one image.  AUTO takes it from kWf32MinF
+// filter rows and columns (DWC_MFMA_F32: 0 never, 1 wherever it applies).
+// The output width is cut into column groups of 4 NB columns (the smallest
+// NB that covers it, else 14); the (image, input row) pairs into Z slices
+// so that the workgroups fill the GPU once (or the requested split).
+static bool plan_wgrad_mfma_f32(const dwc_problem* p, int64_t oh, int64_t ow, bool forced,
+                                Plan* q) {
+  if (p->in_dtype != DT_F32 || p->stride_h != 1 || p->stride_w != 1 || p->fw > 32 ||
+      p->fh > 32 || p->c % kWf32Cb != 0)
+    return false;
+  // AUTO: where the 4x4 tiles cover the filter with little waste (at least
+  // 85% of the computed taps are real ones) and the filter has at least
+  // kWf32MinF rows and columns; on outputs at most 8 wide only the largest
+  // filters (MI355X, N=64 stages: 1.2-1.3x the vector kernels at 27x27 and
+  // 31x31 on 56, 28 and 14 wide outputs, 0.7-0.9x at 17x17 and 21x21, whose
+  // tiles are 72-77% real taps; at width 7, 1.10x at 31x31, 0.91x at 27x27).
+  const int64_t tiles = (int64_t)((p->fh + 3) / 4) * ((p->fw + 3) / 4);
+  const bool pick = p->fh >= kWf32MinF && p->fw >= kWf32MinF &&
+                    (int64_t)p->fh * p->fw * 100 >= tiles * 16 * 85 && (ow > 8 || p->fw >= 29);
+  const char* env = getenv("DWC_MFMA_F32");
+  if (!forced && (env ? atoi(env) == 0 : !pick)) return false;
+  if (p->h * p->w * p->c * 4 >= kI32Max || oh * ow * p->c * 4 >= kI32Max) return false;
+  WgradF32Args w{};
+  w.N = (int)p->n; w.IH = (int)p->h; w.IW = (int)p->w; w.C = (int)p->c;
+  w.OH = (int)oh; w.OW = (int)ow;
+  w.FH = p->fh; w.FW = p->fw; w.PH = p->pad_h; w.PW = p->pad_w;
+  const int tw = (p->fw + 3) / 4;
+  int nb = 14;
+  for (int c : {2, 4, 7, 14})
+    if (4 * c >= ow) {
+      nb = c;
+      break;
+    }
+  w.cblk = w.C / kWf32Cb;
+  w.cg = (int)((ow + 4 * nb - 1) / (4 * nb));
+  const int xp = 4 * nb + 4 * tw;  // staged pixels per X row
+  const int items = xp * (kWf32Cb / 4);
+  w.nw = std::max((p->fh + 3) / 4, (items + 64 * kWf32StageItems - 1) / (64 * kWf32StageItems));
+  if (w.nw > kWf32MaxWaves) return false;
+  w.lds_bytes = 2 * xp * kWf32Cb * 4;
+  const int64_t npairs = p->n * p->h;
+  const int64_t nn = std::max<int64_t>(npairs, 1);  // an empty batch only zero-fills dW
+  int64_t z;
+  if (p->wgrad_split > 0) {
+    z = std::min<int64_t>(p->wgrad_split, nn);
+  } else {
+    // one dispatch round: 16 waves per CU (four per SIMD, the registers of
+    // the widest tiles)
+    const int64_t resident = (int64_t)device_cus() * std::max(1, 16 / w.nw);
+    z = std::max<int64_t>(1, std::min<int64_t>(nn, resident / ((int64_t)w.cblk * w.cg)));
+  }
+  const int64_t rps = (nn + z - 1) / z;
+  w.rps = (int)rps;
+  w.Z = (int)((nn + rps - 1) / rps);
+  const int64_t blocks = (int64_t)w.cblk * w.cg * w.Z;
+  if (blocks > kI32Max) return false;
+  w.num_blocks = (int)blocks;
+  q->kind = PLAN_MFMA;
+  q->wf32 = true;
+  q->wf32_tw = tw;
+  q->wf32_nb = nb;
+  q->cb = kWf32Cb;
+  q->z = w.Z * w.cg;
+  q->blocks = w.num_blocks;
+  q->wf = w;
+  return true;
+}
+
 // Packed fp8 MFMA filter-gradient plan (e4m3 / e5m2 operands): false if
 // the kernel does not apply.  The slicing of plan_wgrad_mfma; staging in
 // bytes, four columns of one channel per LDS dword: X rows at a pitch of an
@@ -806,7 +876,8 @@ int make_plan(const dwc_problem* p, int op, Plan* pl, std::string* err) {
     if (p->wgrad_split > 0 && p->n * oh > 0 && p->wgrad_split > p->n * oh)
       return fail(err, DWC_ERR_BAD_PARAM, "wgrad_split larger than N*OH");
     if (p->algo == DWC_ALGO_AUTO || p->algo == DWC_ALGO_MFMA) {
-      if (plan_wgrad_mfma(p, oh, ow, &q) || plan_wgrad_mfma8(p, oh, ow, &q)) {
+      if (plan_wgrad_mfma(p, oh, ow, &q) || plan_wgrad_mfma8(p, oh, ow, &q) ||
+          plan_wgrad_mfma_f32(p, oh, ow, p->algo == DWC_ALGO_MFMA, &q)) {
         const int64_t m = (int64_t)p->fh * p->fw * p->c;
         q.ws_bytes = ((size_t)q.z * (size_t)m * 4 + 255) / 256 * 256;
         *pl = q;
@@ -814,8 +885,9 @@ int make_plan(const dwc_problem* p, int op, Plan* pl, std::string* err) {
       }
       if (p->algo == DWC_ALGO_MFMA)
         return fail(err, DWC_ERR_UNSUPPORTED,
-                    "no packed-MFMA filter-gradient kernel for this problem (needs bf16/fp16, "
-                    "stride 1, FH and FW <= 32, W <= 64, C % 8 == 0)");
+                    "no packed-MFMA filter-gradient kernel for this problem (needs bf16/fp16 "
+                    "with W <= 64 and C % 8 == 0, or fp32 with C % 16 == 0; stride 1, FH and "
+                    "FW <= 32)");
     }
     const int64_t rows = p->n * oh;
     const int64_t m = (int64_t)p->fh * p->fw * p->c;
@@ -974,6 +1046,15 @@ std::string describe(const Plan& pl) {
              "blocks=%d",
              ops[pl.op], dt_name(pl.dt), g.FH, g.FW, g.S, pl.km, g.tiles_i, g.tiles_j, g.cblocks,
              g.num_items, pl.blocks);
+    return buf;
+  }
+  if (pl.kind == PLAN_MFMA && pl.op == DWC_OP_BWD_FILTER && pl.wf32) {
+    const WgradF32Args& w = pl.wf;
+    snprintf(buf, sizeof buf,
+             "%s mfma dt=%s fw=%d fh=%d f32=1 tw=%d nb=%d cg=%d nw=%d rps=%d zr=%d z=%d cblk=%d "
+             "lds=%d blocks=%d ws_bytes=%zu",
+             ops[pl.op], dt_name(pl.dt), w.FW, w.FH, pl.wf32_tw, pl.wf32_nb, w.cg, w.nw, w.rps,
+             w.Z, pl.z, w.cblk, w.lds_bytes, pl.blocks, pl.ws_bytes);
     return buf;
   }
   if (pl.kind == PLAN_MFMA && pl.op == DWC_OP_BWD_FILTER) {

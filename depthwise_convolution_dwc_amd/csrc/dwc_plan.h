@@ -48,6 +48,10 @@ struct Plan {
   bool f32m = false;
   int f32m_fwi = 0, f32m_t = 0;  // instantiated band width, 4-column tiles per wave
   MfmaF32Args mf{};
+  // fp32 matrix-core filter gradient
+  bool wf32 = false;
+  int wf32_tw = 0, wf32_nb = 0;  // column tiles, 4-column output groups per wave
+  WgradF32Args wf{};
   // packed-MFMA filter gradient
   int nfm = 0, nfn = 0, nk = 0, pf = 0;
   WgradMfmaArgs wm{};

@@ -38,7 +38,31 @@ hipError_t by_fw(int fwi, int t, const MfmaF32Args& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+template <int TW, int NB>
+hipError_t go_w(const WgradF32Args& a, hipStream_t s) {
+  auto kernel = wgrad_mfma_f32<TW, NB>;
+  hipLaunchKernelGGL(kernel, dim3(a.num_blocks), dim3(64 * a.nw), a.lds_bytes, s, a);
+  return hipGetLastError();
+}
+
+template <int TW>
+hipError_t by_nb(int nb, const WgradF32Args& a, hipStream_t s) {
+#define DWC_CASE(B) \
+  if (nb == B) return go_w<TW, B>(a, s);
+  DWC_WF32_NB_LIST(DWC_CASE)
+#undef DWC_CASE
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
+
+hipError_t launch_wgrad_mfma_f32(int tw, int nb, const WgradF32Args& a, hipStream_t s) {
+#define DWC_CASE(W) \
+  if (tw == W) return by_nb<W>(nb, a, s);
+  DWC_WF32_TW_LIST(DWC_CASE)
+#undef DWC_CASE
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_fwd_mfma_f32(int fwi, int t, bool flip, const MfmaF32Args& a, hipStream_t s) {
   return flip ? by_fw<true>(fwi, t, a, s) : by_fw<false>(fwi, t, a, s);

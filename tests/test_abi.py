@@ -111,7 +111,8 @@ def test_plans_for_the_named_workloads():
     assert d.startswith("fwd mfma dt=f32") and " f32=1 fwi=31 t=7 " in d and " same=1 " in d, d
     assert " rg=14 cg=2 tiles=896 " in d, d
     assert dwc.plan_describe(p, 1).startswith("bwd_data mfma dt=f32")
-    assert dwc.plan_describe(p, 2).startswith("bwd_filter direct")
+    d = dwc.plan_describe(p, 2)
+    assert d.startswith("bwd_filter mfma dt=f32") and " tw=8 nb=14 cg=1 nw=8 " in d, d
     p = dwc.problem(64, 56, 56, 128, 7, 7, 2, 3)
     assert "sw=2" in dwc.plan_describe(p, 0)
     p = dwc.problem(128, 28, 28, 512, 13, 13, 1, 6, dtype=dwc.BF16)
@@ -150,11 +151,41 @@ def test_fp32_mfma_plans_and_rejections(monkeypatch):
     assert " f32=1 " not in dwc.plan_describe(dwc.problem(32, 56, 56, 128, 31, 31, 1, 15), 0)
 
 
+def test_fp32_mfma_wgrad_plans(monkeypatch):
+    monkeypatch.delenv("DWC_MFMA_F32", raising=False)
+    # AUTO: 4x4 tiles at least 85% real taps, 12+ rows and columns, outputs
+    # wider than 8 unless the filter is 29+ wide
+    for (h, c, f, want) in ((56, 128, 31, True), (28, 256, 27, True), (56, 128, 17, False),
+                            (56, 128, 21, False), (7, 1024, 27, False), (7, 1024, 31, True),
+                            (56, 128, 16, True), (56, 128, 9, False)):
+        p = dwc.problem(64, h, h, c, f, f, 1, f // 2)
+        d = dwc.plan_describe(p, 2)
+        assert (" f32=1 " in d) == want, (h, f, d)
+    # one column group per 56 output columns; the requested split is the
+    # number of row slices; slices times column groups partials
+    d = dwc.plan_describe(dwc.problem(2, 10, 70, 16, 21, 21, 1, 10, algo="mfma", wgrad_split=7), 2)
+    assert " tw=6 nb=14 cg=2 nw=6 rps=3 zr=7 z=14 " in d, d
+    p = dwc.problem(2, 10, 70, 16, 21, 21, 1, 10, algo="mfma", wgrad_split=7)
+    assert dwc.workspace_size(p) == (7 * 2 * 21 * 21 * 16 * 4 + 255) // 256 * 256
+    d = dwc.plan_describe(dwc.problem(5, 6, 40, 16, 1, 31, 1, (0, 15), algo="mfma"), 2)
+    assert " tw=8 nb=14 " in d and " nw=3 " in d, d  # three waves to stage a row
+    # rejections: C % 16, FH or FW > 32, stride 2
+    for args in ((1, 20, 20, 24, 13, 13, 1, 6), (1, 40, 40, 16, 33, 3, 1, 0),
+                 (1, 40, 40, 16, 3, 33, 1, 0), (1, 20, 20, 16, 13, 13, 2, 6)):
+        assert dwc.check(dwc.problem(*args, algo="mfma"), 2) == 2, args
+
+
 def test_workspace_size_matches_split():
+    # the vector kernels: one partial per slice, none for one slice
+    p = dwc.problem(32, 56, 56, 128, 31, 31, 1, 15, wgrad_split=8, algo="direct")
+    assert dwc.workspace_size(p) == 8 * 31 * 31 * 128 * 4
+    p = dwc.problem(32, 56, 56, 128, 31, 31, 1, 15, wgrad_split=1, algo="direct")
+    assert dwc.workspace_size(p) == 0
+    # the matrix-core kernels always write partials (one per slice)
     p = dwc.problem(32, 56, 56, 128, 31, 31, 1, 15, wgrad_split=8)
     assert dwc.workspace_size(p) == 8 * 31 * 31 * 128 * 4
     p = dwc.problem(32, 56, 56, 128, 31, 31, 1, 15, wgrad_split=1)
-    assert dwc.workspace_size(p) == 0
+    assert dwc.workspace_size(p) == (31 * 31 * 128 * 4 + 255) // 256 * 256
     p = dwc.problem(0, 56, 56, 128, 31, 31, 1, 15)
     assert dwc.workspace_size(p) == 0
     p = dwc.problem(2, 8, 8, 4, 3, 3, 1, 1, wgrad_split=17)  # > N*OH = 16
@@ -240,7 +271,7 @@ def test_mfma_plans_and_rejections(monkeypatch):
     # of 8, FW <= 32, output width <= 64 (forward), input width <= 64 and FH
     # <= 32 (filter gradient)
     base = dict(n=2, h=20, w=20, c=16, fh=5, fw=5, stride=1, pad=2, dtype=dwc.BF16)
-    for kw, ops in ((dict(dtype=dwc.F32), (2,)), (dict(dtype=dwc.F32, c=24), (0, 1, 2)),
+    for kw, ops in ((dict(dtype=dwc.F32, c=24), (0, 1, 2)),
                     (dict(stride=2), (0, 1, 2)),
                     (dict(c=12), (0, 1, 2)), (dict(fw=33, pad=16), (0, 1, 2)),
                     (dict(w=80), (0, 2)), (dict(fh=33, pad=16), (2,))):
@@ -458,7 +489,7 @@ def test_algo_codes_match_the_header():
     assert dwc.check(p, 0) == 0 and " mfma " in dwc.plan_describe(p, 0)
     q = dwc.problem(1, 16, 16, 16, 5, 5, 1, 2, dtype=dwc.F32, algo=2)
     assert dwc.check(q, 0) == 0 and " f32=1 " in dwc.plan_describe(q, 0)
-    assert dwc.check(q, 2) == 2
+    assert dwc.check(q, 2) == 0 and " f32=1 " in dwc.plan_describe(q, 2)
     q = dwc.problem(1, 16, 16, 16, 5, 5, 2, 2, dtype=dwc.F32, algo=2)
     assert dwc.check(q, 0) == 2
 

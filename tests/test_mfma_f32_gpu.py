@@ -87,3 +87,47 @@ def test_mfma_f32_deterministic():
     b = dwc.fwd(x, w, 1, 10, algo="mfma")
     sync()
     assert torch.equal(a, b)
+
+
+# (n, h, w, c, fh, fw, stride, pad): the filter gradient's column tiles
+# (FW 1 .. 32), output widths of each column-group size and wider than one
+# group, filter heights up to 32, cropping padding
+F32W_SHAPES = [
+    (2, 14, 14, 32, 13, 13, 1, 6),
+    (3, 9, 23, 16, 17, 17, 1, 8),
+    (1, 28, 28, 48, 31, 31, 1, 15),
+    (2, 10, 70, 16, 21, 21, 1, 10),
+    (2, 11, 13, 32, 9, 13, 1, (4, 6)),
+    (1, 7, 7, 16, 31, 31, 1, 15),
+    (2, 12, 20, 16, 5, 11, 1, (2, 3)),
+    (1, 10, 10, 16, 13, 13, 1, 14),
+    (2, 20, 9, 32, 15, 3, 1, (7, 1)),
+    (5, 6, 40, 16, 1, 31, 1, (0, 15)),
+    (1, 40, 8, 16, 32, 32, 1, (16, 16)),
+    (3, 30, 30, 16, 27, 27, 1, 13),
+]
+
+
+@pytest.mark.parametrize("split", [0, 1, 7])
+@pytest.mark.parametrize("shape", F32W_SHAPES, ids=_ids)
+def test_mfma_f32_wgrad_parity(shape, split):
+    s = _shape(shape)
+    p = dwc.problem(s.n, s.h, s.w, s.c, s.fh, s.fw, 1, (s.pad_h, s.pad_w), dtype=DT["f32"],
+                    algo="mfma", wgrad_split=split)
+    d = dwc.plan_describe(p, OPS["bwd_filter"])
+    assert d.startswith("bwd_filter mfma dt=f32") and " f32=1 " in d, d
+    inp = make_inputs(s, "f32", seed=80 + sum(shape[:6]))
+    want, mag = _want_mag("bwd_filter", s, inp)
+    log(f"case mfma f32 wgrad {shape} split={split}: {d}")
+    got = _run("bwd_filter", s, inp, "mfma", wgrad_split=split)
+    check_parity(got, want, mag, "bwd_filter", s, "f32", what=f"split={split}")
+
+
+def test_mfma_f32_wgrad_deterministic():
+    s = _shape((3, 30, 30, 16, 27, 27, 1, 13))
+    inp = make_inputs(s, "f32", seed=81)
+    x, dy = to_device(inp.x), to_device(inp.dy)
+    a = dwc.bwd_filter(x, dy, (27, 27), 1, 13, algo="mfma")
+    b = dwc.bwd_filter(x, dy, (27, 27), 1, 13, algo="mfma")
+    sync()
+    assert torch.equal(a, b)
