@@ -73,28 +73,32 @@ typedef enum {
     DWC_ALGO_VECTOR = 1,  /* register-window vector kernels (one channel per
                              lane, fp32 FMAs)                               */
     DWC_ALGO_DIRECT = 1,  /* the same value under its earlier name          */
-    DWC_ALGO_MFMA = 2,    /* packed matrix-core kernels (bf16/fp16 or fp8
-                             operands, stride 1, FW <= 32, C a multiple of
-                             8 -- of 16 for the fp8 forward and data
-                             gradient --, 16-byte aligned tensors; output
-                             width <= 64 for the forward and data
-                             gradient, input width <= 64 and FH <= 32 for
-                             the filter gradient): the GEMV-to-GEMM
-                             packing of §4.2 on CDNA4 MFMA, with the batch
-                             as the second matrix dimension of the
-                             forward and data gradient for widths up to 32
-                             and tall filters (fp8: also the K=128 fp8
-                             MFMA, four filter or output rows per
-                             instruction, §7).  AUTO picks it wherever it
-                             applies.  Operands must be finite: the packed
-                             band multiplies every staged element by
+    DWC_ALGO_MFMA = 2,    /* matrix-core kernels (stride 1, 16-byte aligned
+                             tensors): the GEMV-to-GEMM packing of §4.2 on
+                             CDNA4 MFMA.  bf16/fp16 operands: C a multiple
+                             of 8, FW <= 32, output width <= 64 for the
+                             forward and data gradient (the batch as the
+                             second matrix dimension for widths up to 32
+                             and tall filters), input width <= 64 and
+                             FH <= 32 for the filter gradient; fp8: the
+                             same with C a multiple of 16 for the forward
+                             and data gradient (also the K=128 fp8 MFMA,
+                             four filter or output rows per instruction,
+                             §7); fp32: C a multiple of 16, FW <= 31 and
+                             FH <= 64 for the forward and data gradient,
+                             FH and FW <= 32 for the filter gradient
+                             (4x4 outer products per channel, 16 channels
+                             per instruction).  AUTO takes them for the
+                             problems where they beat the vector kernels
+                             (large filters).  Operands must be finite:
+                             the packing multiplies staged elements by
                              structural zeros as well, so an inf or NaN
-                             operand turns the outputs of its 32-column
-                             window (forward, data gradient) or of its
-                             channel's filter gradient into NaN, where the
-                             definition gives +-inf or a finite value.  The
-                             vector and generic kernels follow IEEE
-                             arithmetic on non-finite operands           */
+                             operand turns outputs that share an
+                             instruction with it (forward, data gradient)
+                             or its channel's filter gradient into NaN,
+                             where the definition gives +-inf or a finite
+                             value.  The vector and generic kernels follow
+                             IEEE arithmetic on non-finite operands      */
     DWC_ALGO_GENERIC = 3, /* one output per lane; any filter size or stride */
     DWC_ALGO_HYBRID = 4   /* filter gradient of fp16 operands only (stride
                              1, square filter 3, 5, 7 or 9): the vector
@@ -134,7 +138,9 @@ typedef struct {
     int32_t algo;               /* dwc_algo                                 */
     int32_t wgrad_split;        /* filter gradient: number of slices of the
                                    N*OH accumulation axis (whole images for
-                                   the packed kernel, at most N slices);
+                                   the half-precision packed kernels, at most
+                                   N slices; runs of input rows for the fp32
+                                   matrix-core kernel, at most N*H slices);
                                    0 = automatic                            */
 } dwc_problem;
 
@@ -219,9 +225,11 @@ int dwc_bwd_filter_workspace_size(const dwc_problem* p, size_t* bytes);
  * The N*OH accumulation axis is split into slices whose partial sums are
  * added in a fixed order (the split of §5.1, reduced deterministically
  * instead of with atomics), so results are bitwise reproducible for a given
- * problem, algo and wgrad_split.  The packed-MFMA kernel (DWC_ALGO_MFMA, or
- * AUTO where it applies) slices whole images and also needs workspace and
- * tensors 16-byte aligned.  n == 0 writes dw = 0. */
+ * problem, algo and wgrad_split.  The matrix-core kernels (DWC_ALGO_MFMA,
+ * or AUTO where it applies) always write their slices' partial sums to the
+ * workspace (one slice too) and need tensors 16-byte aligned; the fp32 one
+ * slices runs of consecutive (image, input row) pairs, times the 56-column
+ * groups of the output width.  n == 0 writes dw = 0. */
 int dwc_bwd_filter(const dwc_problem* p, const void* x, const void* dy,
                    void* dw, void* workspace, size_t workspace_bytes,
                    void* stream);
