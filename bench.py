@@ -850,7 +850,11 @@ its kernels summed per launch and averaged over its {PROFILE_REPS} timed
 launches (each traced dispatch matched in order to the launch bench.py
 issued, kernel name and workgroup count checked).  Fraction: of the literal roofline min(8 TB/s x eta_D / operand
 bytes, peak), peak 157.3 TFLOP/s (fp32 operands), 2.5 PFLOP/s (bf16/fp16
-operands), 5.0 PFLOP/s (fp8 operands).
+operands), 5.0 PFLOP/s (fp8 operands).  Template arguments: the operand
+dtype first (0 fp32, 1 bf16, 2 fp16, 3 e4m3), except for the fp32
+matrix-core kernels: `fwd_mfma_f32<band width, 4-column tiles per wave,
+FLIP>`, `wgrad_mfma_f32<4-column filter tiles, 4-column output groups per
+wave>`.
 
 {chr(10).join(clines)}
 """
@@ -1074,9 +1078,11 @@ Every kernel the benchmark's per-configuration entries launch (the five
 configurations of the target, the strided backward and fp8 rows), except
 the default step's, which are in `{PROFILE_NAME}.sq_counters.md`.  Kernel
 names carry their template arguments (operand dtype first: 0 fp32, 1 bf16,
-2 fp16, 3 e4m3, 4 e5m2) and the workgroup count, which tells the launch
-sizes of one kernel apart; `configs.kernel_trace.md` maps them to the
-configurations.
+2 fp16, 3 e4m3, 4 e5m2; the fp32 matrix-core kernels, fp32 only, take
+`fwd_mfma_f32<band width, 4-column tiles per wave, FLIP>` and
+`wgrad_mfma_f32<4-column filter tiles, 4-column output groups per wave>`)
+and the workgroup count, which tells the launch sizes of one kernel apart;
+`configs.kernel_trace.md` maps them to the configurations.
 
 {legend}
 {chr(10).join(cl)}
