@@ -258,6 +258,7 @@ constexpr int kF32mRows = 4;        // output rows per wave (the matrix rows)
 constexpr int kF32mMaxWaves = 8;    // waves per workgroup
 constexpr int kF32mMinFh = 13;      // AUTO: from this many filter rows and columns
 constexpr int kF32mMinOw = 24;      // ... on outputs at least this wide
+constexpr int kF32mFillWaves = 2048;  // 8 waves per CU of the MI355X
 constexpr int kF32mStageBatch = 8;  // 16-byte band loads in flight per thread
 constexpr int f32m_fwi(int fw) {
   return fw <= 13 ? 13 : fw <= 17 ? 17 : fw <= 21 ? 21 : fw <= 27 ? 27 : fw <= 31 ? 31 : 0;

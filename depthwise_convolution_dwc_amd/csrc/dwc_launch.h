@@ -46,8 +46,10 @@ hipError_t launch_fwd_mfma_batch16(int dt, int ng, bool flip, const MfmaBatchArg
 
 // fp32 matrix-core forward-type kernel (fp32 operands, stride 1, FW <= 31,
 // C % 16 == 0): fwi the instantiated band width (DWC_F32M_FW_LIST), t the
-// 4-column output tiles per wave (DWC_F32M_T_LIST).
-hipError_t launch_fwd_mfma_f32(int fwi, int t, bool flip, const MfmaF32Args& a, hipStream_t s);
+// 4-column output tiles per wave (DWC_F32M_T_LIST; 2 or 4 with img), img
+// 4 images instead of 4 output rows as the matrix rows (fwd_mfma_f32n).
+hipError_t launch_fwd_mfma_f32(int fwi, int t, bool img, bool flip, const MfmaF32Args& a,
+                               hipStream_t s);
 
 // fp32 matrix-core filter gradient (fp32 operands, stride 1, FH and FW <=
 // 32, C % 16 == 0): tw = ceil(FW / 4) column tiles, nb 4-column output

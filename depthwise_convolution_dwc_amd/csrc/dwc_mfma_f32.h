@@ -257,6 +257,166 @@ __global__ __launch_bounds__(64 * kF32mMaxWaves) void fwd_mfma_f32(MfmaF32Args a
   }
 }
 
+// ---- forward-type kernel with 4 images as the matrix rows: per block b
+// (channel c0 + b), D[i][j] of tile m and ring row q is output pixel
+// (n0 + i, oh0 + q, ow0 + 4m + j); the K step is one input column u of one
+// input row r, A[i] = x[n0 + i][r][ow0 - PW + u] (the same column of 4
+// images: no data moves between lanes) and B[j] = w[r - oh0 - q + PH][u -
+// 4m - j], the band row of that ring row.  A wave streams the FH + RR - 1
+// input rows of its RR output rows, loading each once; padding rows are
+// skipped.  The band staging, the edge variants and the output layout are
+// those of fwd_mfma_f32.
+template <int FWI, int T, bool FLIP>
+__global__ __launch_bounds__(64 * kF32mMaxWaves) void fwd_mfma_f32n(MfmaF32Args a) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  constexpr int RR = kF32mRows;          // output rows per wave (accumulator ring)
+  constexpr int NT = FWI + 3;
+  constexpr int NA = 4 * T + FWI - 1;
+  constexpr int ZP = FWI + 6;
+  float* band = reinterpret_cast<float*>(lds);  // [FH][ZP][kF32mCb]
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  const int blk = xcd_logical_block(blockIdx.x, gridDim.x);
+  if (blk >= a.num_blocks) return;  // the whole workgroup leaves together
+  const int cbk = blk % a.cblk;
+  const int grp = blk / a.cblk;
+  const int c0 = cbk * kF32mCb;
+  const int FH = a.FH, FW = a.FW, C = a.C;
+
+  const int bn = FH * ZP * kF32mCb / 4;
+  for (int e = tid; e < bn; e += nthr)
+    reinterpret_cast<f32m_x4*>(band)[e] = f32m_x4{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
+  {
+    const int taps = FH * FW;
+    const int items = taps * (kF32mCb / 4);
+    const auto frs = make_rsrc(a.filt, (uint32_t)taps * (uint32_t)C * 4u);
+    for (int e0 = 0; e0 < items; e0 += kF32mStageBatch * nthr) {
+      f32m_x4 v[kF32mStageBatch];
+#pragma unroll
+      for (int j = 0; j < kF32mStageBatch; ++j) {
+        const int e = e0 + j * nthr + tid;
+        const int tap = e >> 2, c4 = (e & 3) * 4;
+        const int src = FLIP ? taps - 1 - tap : tap;
+        const uint32_t off = e < items ? ((uint32_t)src * (uint32_t)C + (uint32_t)(c0 + c4)) * 4u : kOOB;
+        v[j] = __builtin_bit_cast(f32m_x4, __builtin_amdgcn_raw_buffer_load_b128(frs, (int)off, 0, 0));
+      }
+#pragma unroll
+      for (int j = 0; j < kF32mStageBatch; ++j) {
+        const int e = e0 + j * nthr + tid;
+        if (e < items) {
+          const int tap = e >> 2, c4 = (e & 3) * 4;
+          const int fh = fast_div(tap, a.fw_magic), fw = tap - fh * FW;
+          *reinterpret_cast<f32m_x4*>(band + (fh * ZP + fw + 3) * kF32mCb + c4) = v[j];
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- the wave's tile: images n0 .. n0 + 3, output rows oh0 .. oh0 + 3,
+  // columns ow0 .. ow0 + 4T - 1 (column groups, then row groups, then image
+  // groups; the last column group ends at the right edge)
+  const int wave = uniform(tid >> 6);
+  const int tile = grp * a.nw + wave;
+  if (tile >= a.tiles) return;
+  int rest = tile;
+  const int cgi = rest % a.cg;
+  rest /= a.cg;
+  const int rgi = rest % a.rg;
+  const int n0 = (rest / a.rg) * 4;
+  const int oh0 = rgi * RR;
+  const int ow0 = a.OW >= 4 * T ? min(cgi * 4 * T, a.OW - 4 * T) : 0;
+  const int lane = tid & 63, b = lane >> 2, q = lane & 3;
+  const int IH = a.IH, IW = a.IW, PH = a.PH, PW = a.PW;
+  // lane (b, i): image n0 + i (kOOB past the batch), channel c0 + b
+  const uint32_t img_bytes = (uint32_t)IH * (uint32_t)IW * (uint32_t)C * 4u;
+  const uint32_t loff = n0 + q < a.N ? (uint32_t)q * img_bytes + (uint32_t)(c0 + b) * 4u : kOOB;
+  const auto xrs = make_rsrc(reinterpret_cast<const float*>(a.in) + (size_t)n0 * IH * IW * C,
+                             (uint32_t)(a.N - n0) * img_bytes);  // images n0 .. N - 1
+
+  f32m_x4 D[RR][T];
+#pragma unroll
+  for (int j = 0; j < RR; ++j)
+#pragma unroll
+    for (int m = 0; m < T; ++m) D[j][m] = f32m_x4{0.f, 0.f, 0.f, 0.f};
+  // input rows that reach the wave's output rows and are not padding
+  const int r_lo = max(0, oh0 - PH);
+  const int r_hi = min(IH, oh0 + RR - 1 + FH - PH);  // exclusive
+  const float* bl = band + (3 - q) * kF32mCb + b;
+
+  auto run = [&](auto lc, auto rc) {
+    constexpr int L = decltype(lc)::value, R = decltype(rc)::value;
+    for (int r = r_lo; r < r_hi; ++r) {
+      // the row's columns of the window, one load each: the lane offset
+      // (image, channel) is the same for all, the pixel's offset goes in the
+      // scalar offset (a padding column is not loaded)
+      float A[NA];
+      int so = (r * IW + ow0 - PW) * C * 4;  // bytes to column u
+      int col = ow0 - PW;                    // column u
+#pragma unroll
+      for (int u = 0; u < NA; ++u) {
+        A[u] = 0.f;
+        if (u >= L && u < NA - R && col >= 0 && col < IW)
+          A[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(xrs, (int)loff, so, 0));
+        so += C * 4;
+        ++col;
+        // scalar adds per column: keep the compiler from holding every
+        // column's offset and bounds in scalar registers across the row loop
+        asm volatile("" : "+s"(so), "+s"(col));
+      }
+#pragma unroll
+      for (int j = 0; j < RR; ++j) {
+        const int fh = r - oh0 - j + PH;
+        if (fh < 0 || fh >= FH) continue;  // uniform
+        const float* bk = bl + fh * (ZP * kF32mCb);
+        f32m_static_for<0, NT>([&](auto tc) {
+          constexpr int t = decltype(tc)::value;
+          const float bv = bk[t * kF32mCb];
+          constexpr int mlo = (L - t + 3) / 4 > 0 ? (L - t + 3) / 4 : 0;
+          constexpr int mhi0 = (NA - R - t + 3) / 4;
+          constexpr int mhi = mhi0 < T ? mhi0 : T;
+#pragma unroll
+          for (int m = mlo; m < mhi; ++m)
+            D[j][m] = __builtin_amdgcn_mfma_f32_4x4x1f32(A[4 * m + t], bv, D[j][m], 0, 0, 0);
+        });
+      }
+    }
+  };
+  {
+    using Z = std::integral_constant<int, 0>;
+    using P = std::integral_constant<int, (FWI - 1) / 2>;
+    const bool el = a.same && ow0 == 0, er = a.same && ow0 + 4 * T == a.OW;
+    if (el && er) run(P{}, P{});
+    else if (el) run(P{}, Z{});
+    else if (er) run(Z{}, P{});
+    else run(Z{}, Z{});
+  }
+
+  // ---- outputs: register i of D[j][m] is image n0 + i, row oh0 + j,
+  // column ow0 + 4m + q
+  const uint32_t orowb = (uint32_t)a.OW * (uint32_t)C * 4u;
+  const uint32_t ooff = (uint32_t)(((ow0 + q) * C + c0 + b) * 4);
+  const uint32_t sstep = (uint32_t)C * 16u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (n0 + i >= a.N) break;  // uniform
+    float* yimg = a.out + (size_t)(n0 + i) * a.OH * a.OW * C;
+#pragma unroll
+    for (int j = 0; j < RR; ++j) {
+      const int oh = oh0 + j;
+      if (oh >= a.OH) break;  // uniform
+      const auto ors = make_rsrc(yimg + (size_t)oh * a.OW * C, orowb);
+#pragma unroll
+      for (int m = 0; m < T; ++m) {
+        const float v = D[j][m][i];  // copied out: see fwd_mfma_f32's store
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ors,
+                                              (int)(ooff + (uint32_t)m * sstep), 0, 0);
+      }
+    }
+  }
+}
+
 // ---- filter gradient (layout and mapping: WgradF32Args)
 template <int TW, int NB>
 __global__ __launch_bounds__(64 * kWf32MaxWaves, 4) void wgrad_mfma_f32(WgradF32Args a) {

@@ -301,29 +301,53 @@ static int64_t f32m_cost(int ow, int fwi, int t, bool same) {
   return n;
 }
 
-// fp32 matrix-core plan (fwd_mfma_f32): false if the kernel does not apply.
-// fp32 operands, stride 1, C % 16 == 0, FW <= 31, FH <= 64 (the band of
-// every filter row in LDS), 32-bit offsets within one image.  AUTO takes it
-// from kF32mMinFh filter rows and columns (DWC_MFMA_F32: 0 never, 1 wherever
-// it applies).  The tile width T (4-column tiles per wave) issues the fewest
-// instructions over the output width; ties go to the wider tile.
+// fp32 matrix-core plan (fwd_mfma_f32, fwd_mfma_f32n): false if the kernels
+// do not apply.  fp32 operands, stride 1, C % 16 == 0, FW <= 31, FH <= 64
+// (the band of every filter row in LDS), 32-bit offsets within one image
+// (within the batch for the images kernel).  DWC_MFMA_F32: 0 never, 1
+// wherever it applies.
 static bool plan_mfma_f32(const FwdArgs& f, int dt, bool flip, bool forced, Plan* q) {
   if (dt != DT_F32 || f.SH != 1 || f.SW != 1 || f.C % kF32mCb != 0 || f.FW < 1 || f.FW > 31 ||
       f.FH < 1 || f.FH > 64)
     return false;
-  // AUTO: filters of at least kF32mMinFh rows and columns on outputs at
-  // least kF32mMinOw wide (MI355X, N=64 stages: 1.0-1.5x the vector kernels
-  // from 13x13 on at widths 56 and 28, slower at width 14), and the largest
-  // filters on the narrowest outputs (width 7: 1.07x at 27x27, 1.18x at
-  // 31x31).
-  const bool pick = f.FH >= kF32mMinFh && f.FW >= kF32mMinFh &&
-                    (f.OW >= kF32mMinOw || (f.OW <= 8 && f.FW >= 27));
-  const char* env = getenv("DWC_MFMA_F32");
-  if (!forced && (env ? atoi(env) == 0 : !pick)) return false;
   if ((int64_t)f.IH * f.IW * f.C * 4 >= kI32Max || (int64_t)f.OH * f.OW * f.C * 4 >= kI32Max)
     return false;
   const int fwi = f32m_fwi(f.FW);
   const bool same = f.PW == (fwi - 1) / 2 && f.FW == fwi && f.IW == f.OW;
+  const int rg = (f.OH + kF32mRows - 1) / kF32mRows;
+  auto groups = [&](int t) { return f.OW >= 4 * t ? (f.OW + 4 * t - 1) / (4 * t) : 1; };
+  // Images as the matrix rows (fwd_mfma_f32n: no row moves between lanes,
+  // each input row loaded as the wave reaches it): 4 tiles per wave above
+  // width 8, else 2.  It wins on outputs at most 16 wide with large filters
+  // while it has 8 waves per CU (MI355X, N=64 C=512 14x14: 63-78 against
+  // 66-97 us from 21x21 on; width 7: 27 and 39 against 37 and 42 us at
+  // 27x27 and 31x31), and loses at widths 28 and 56 (1.2-1.35x: its loads'
+  // latency is exposed per row) and with fewer waves.
+  const int img_t = f.OW > 8 ? 4 : 2;
+  const bool img_fill = f.N >= 4 && (int64_t)((f.N + 3) / 4) * rg * groups(img_t) * (f.C / kF32mCb) >=
+                                        kF32mFillWaves;
+  const bool img_auto = f.OW <= 16 && img_fill && f.FW >= (f.OW > 8 ? 21 : 27);
+  // AUTO, from kF32mMinFh filter rows and columns:
+  // - outputs at least kF32mMinOw wide (MI355X, N=64 stages: 1.0-1.5x the
+  //   vector kernels from 13x13 on at widths 56 and 28);
+  // - the largest filters on the narrowest outputs (width 7: 1.07x at 27x27,
+  //   1.18x at 31x31), and the images kernel's cases above;
+  // - outputs at most 16 wide whose vector kernel (a wave per 64 channels,
+  //   4 rows, the whole width) has fewer than 8 waves per CU: 3-4x faster
+  //   (N=8 14x14 C=512 31x31: 21 against 79 us; N=16 C=256 21x21: 17
+  //   against 50 us).
+  const bool vec_few = f.OW <= 16 && (int64_t)f.N * ((f.C + 63) / 64) * rg < kF32mFillWaves;
+  const bool pick = f.FH >= kF32mMinFh && f.FW >= kF32mMinFh &&
+                    (f.OW >= kF32mMinOw || (f.OW <= 8 && f.FW >= 27) || img_auto || vec_few);
+  const char* env = getenv("DWC_MFMA_F32");
+  if (!forced && (env ? atoi(env) == 0 : !pick)) return false;
+  // the images kernel addresses 4 images of X from one buffer resource
+  const bool img_ok = f.N >= 4 && (int64_t)f.N * f.IH * f.IW * f.C * 4 < kI32Max;
+  // DWC_MFMA_F32_IMG: 0 never, 1 for every batch of 4 or more
+  const char* iv = getenv("DWC_MFMA_F32_IMG");
+  const bool img = img_ok && (iv ? atoi(iv) != 0 : img_auto);
+  // The rows kernel's tile width T (4-column tiles per wave) issues the
+  // fewest instructions over the output width; ties go to the wider tile.
   int best_t = 0;
   int64_t best = 0;
   for (int t : {7, 4, 2}) {
@@ -333,18 +357,19 @@ static bool plan_mfma_f32(const FwdArgs& f, int dt, bool flip, bool forced, Plan
       best_t = t;
     }
   }
+  if (img) best_t = img_t;
   if (const char* v = getenv("DWC_MFMA_F32_T")) {
     const int t = atoi(v);
-    if (t == 7 || t == 4 || t == 2) best_t = t;
+    if ((t == 7 && !img) || t == 4 || t == 2) best_t = t;
   }
   const int t = best_t;
   MfmaF32Args m{};
   m.N = f.N; m.IH = f.IH; m.IW = f.IW; m.C = f.C; m.OH = f.OH; m.OW = f.OW;
   m.FH = f.FH; m.FW = f.FW; m.PH = f.PH; m.PW = f.PW;
   m.cblk = f.C / kF32mCb;
-  m.rg = (f.OH + kF32mRows - 1) / kF32mRows;
-  m.cg = f.OW >= 4 * t ? (f.OW + 4 * t - 1) / (4 * t) : 1;
-  const int64_t tiles = (int64_t)f.N * m.rg * m.cg;
+  m.rg = rg;
+  m.cg = groups(t);
+  const int64_t tiles = (int64_t)(img ? (f.N + 3) / 4 : f.N) * m.rg * m.cg;
   if (tiles > kI32Max) return false;
   m.tiles = (int)tiles;
   m.nw = (int)std::min<int64_t>(kF32mMaxWaves, tiles);
@@ -361,6 +386,7 @@ static bool plan_mfma_f32(const FwdArgs& f, int dt, bool flip, bool forced, Plan
   q->f32m = true;
   q->f32m_fwi = fwi;
   q->f32m_t = t;
+  q->f32m_img = img;
   q->flip = flip;
   q->blocks = (int)blocks;
   q->mf = m;
@@ -1071,10 +1097,10 @@ std::string describe(const Plan& pl) {
   if (pl.kind == PLAN_MFMA && pl.f32m) {
     const MfmaF32Args& m = pl.mf;
     snprintf(buf, sizeof buf,
-             "%s mfma dt=%s fw=%d fh=%d flip=%d f32=1 fwi=%d t=%d rg=%d cg=%d tiles=%d nw=%d "
-             "same=%d cblk=%d lds=%d blocks=%d",
-             ops[pl.op], dt_name(pl.dt), m.FW, m.FH, (int)pl.flip, pl.f32m_fwi, pl.f32m_t, m.rg,
-             m.cg, m.tiles, m.nw, m.same, m.cblk, m.lds_bytes, pl.blocks);
+             "%s mfma dt=%s fw=%d fh=%d flip=%d f32=1 fwi=%d t=%d img=%d rg=%d cg=%d tiles=%d "
+             "nw=%d same=%d cblk=%d lds=%d blocks=%d",
+             ops[pl.op], dt_name(pl.dt), m.FW, m.FH, (int)pl.flip, pl.f32m_fwi, pl.f32m_t,
+             (int)pl.f32m_img, m.rg, m.cg, m.tiles, m.nw, m.same, m.cblk, m.lds_bytes, pl.blocks);
     return buf;
   }
   if (pl.kind == PLAN_MFMA && pl.batch) {

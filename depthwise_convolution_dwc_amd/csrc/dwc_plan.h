@@ -47,6 +47,7 @@ struct Plan {
   // fp32 matrix-core forward-type kernel
   bool f32m = false;
   int f32m_fwi = 0, f32m_t = 0;  // instantiated band width, 4-column tiles per wave
+  bool f32m_img = false;         // 4 images (not 4 output rows) as the matrix rows
   MfmaF32Args mf{};
   // fp32 matrix-core filter gradient
   bool wf32 = false;

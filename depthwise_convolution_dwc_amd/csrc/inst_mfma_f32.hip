@@ -6,9 +6,11 @@
 namespace dwc {
 namespace {
 
-template <int FWI, int T, bool FLIP>
+template <int FWI, int T, bool FLIP, bool IMG>
 hipError_t go(const MfmaF32Args& a, hipStream_t s) {
-  auto kernel = fwd_mfma_f32<FWI, T, FLIP>;
+  void (*kernel)(MfmaF32Args);
+  if constexpr (IMG) kernel = fwd_mfma_f32n<FWI, T, FLIP>;
+  else kernel = fwd_mfma_f32<FWI, T, FLIP>;
   if (a.lds_bytes > 65536) {
     // dynamic LDS above the default 64 KiB is allowed once per kernel
     static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
@@ -21,18 +23,23 @@ hipError_t go(const MfmaF32Args& a, hipStream_t s) {
 }
 
 template <int FWI, bool FLIP>
-hipError_t by_t(int t, const MfmaF32Args& a, hipStream_t s) {
+hipError_t by_t(int t, bool img, const MfmaF32Args& a, hipStream_t s) {
+  if (img) {  // 2 or 4 tiles: the accumulator ring takes the registers of more
+    if (t == 2) return go<FWI, 2, FLIP, true>(a, s);
+    if (t == 4) return go<FWI, 4, FLIP, true>(a, s);
+    return hipErrorInvalidValue;
+  }
 #define DWC_CASE(TT) \
-  if (t == TT) return go<FWI, TT, FLIP>(a, s);
+  if (t == TT) return go<FWI, TT, FLIP, false>(a, s);
   DWC_F32M_T_LIST(DWC_CASE)
 #undef DWC_CASE
   return hipErrorInvalidValue;
 }
 
 template <bool FLIP>
-hipError_t by_fw(int fwi, int t, const MfmaF32Args& a, hipStream_t s) {
+hipError_t by_fw(int fwi, int t, bool img, const MfmaF32Args& a, hipStream_t s) {
 #define DWC_CASE(F) \
-  if (fwi == F) return by_t<F, FLIP>(t, a, s);
+  if (fwi == F) return by_t<F, FLIP>(t, img, a, s);
   DWC_F32M_FW_LIST(DWC_CASE)
 #undef DWC_CASE
   return hipErrorInvalidValue;
@@ -64,8 +71,9 @@ hipError_t launch_wgrad_mfma_f32(int tw, int nb, const WgradF32Args& a, hipStrea
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_fwd_mfma_f32(int fwi, int t, bool flip, const MfmaF32Args& a, hipStream_t s) {
-  return flip ? by_fw<true>(fwi, t, a, s) : by_fw<false>(fwi, t, a, s);
+hipError_t launch_fwd_mfma_f32(int fwi, int t, bool img, bool flip, const MfmaF32Args& a,
+                               hipStream_t s) {
+  return flip ? by_fw<true>(fwi, t, img, a, s) : by_fw<false>(fwi, t, img, a, s);
 }
 
 }  // namespace dwc

@@ -88,7 +88,8 @@ typedef enum {
                              FH <= 64 for the forward and data gradient,
                              FH and FW <= 32 for the filter gradient
                              (4x4 outer products per channel, 16 channels
-                             per instruction).  AUTO takes them for the
+                             per instruction; output rows or images by
+                             output columns, filter columns by rows).  AUTO takes them for the
                              problems where they beat the vector kernels
                              (large filters).  Operands must be finite:
                              the packing multiplies staged elements by

@@ -108,8 +108,8 @@ def test_plans_for_the_named_workloads():
     assert d.startswith("bwd_filter sweep")
     p = dwc.problem(32, 56, 56, 128, 31, 31, 1, 15)
     d = dwc.plan_describe(p, 0)
-    assert d.startswith("fwd mfma dt=f32") and " f32=1 fwi=31 t=7 " in d and " same=1 " in d, d
-    assert " rg=14 cg=2 tiles=896 " in d, d
+    assert d.startswith("fwd mfma dt=f32") and " f32=1 fwi=31 t=7 img=0 " in d, d
+    assert " rg=14 cg=2 tiles=896 " in d and " same=1 " in d, d
     assert dwc.plan_describe(p, 1).startswith("bwd_data mfma dt=f32")
     d = dwc.plan_describe(p, 2)
     assert d.startswith("bwd_filter mfma dt=f32") and " tw=8 nb=14 cg=1 nw=8 " in d, d
@@ -121,20 +121,45 @@ def test_plans_for_the_named_workloads():
 
 def test_fp32_mfma_plans_and_rejections(monkeypatch):
     monkeypatch.delenv("DWC_MFMA_F32", raising=False)
-    # AUTO: large filters on outputs at least 24 wide, and 27x27 and up on
-    # outputs at most 8 wide; the vector kernels elsewhere
-    for (h, c, f, want) in ((56, 128, 13, True), (28, 256, 31, True), (14, 512, 31, False),
-                            (7, 1024, 31, True), (7, 1024, 21, False), (56, 128, 9, False)):
-        p = dwc.problem(64, h, h, c, f, f, 1, f // 2)
+    # AUTO: large filters on outputs at least 24 wide; on outputs at most 16
+    # wide, 21x21 and up (width 7: 27x27 and up) where the images kernel has
+    # 8 waves per CU, and wherever the vector kernel has fewer; the vector
+    # kernels elsewhere
+    for (n, h, c, f, want, img) in ((64, 56, 128, 13, True, 0), (64, 28, 256, 31, True, 0),
+                                    (64, 14, 512, 31, True, 1), (64, 14, 512, 21, True, 1),
+                                    (64, 14, 512, 17, False, 0), (64, 7, 1024, 31, True, 1),
+                                    (64, 7, 1024, 21, False, 0), (64, 56, 128, 9, False, 0),
+                                    (32, 14, 512, 31, True, 0), (32, 14, 512, 13, True, 0),
+                                    (8, 14, 512, 31, True, 0), (64, 14, 1024, 13, False, 0),
+                                    (16, 14, 256, 21, True, 0), (64, 20, 256, 21, False, 0)):
+        p = dwc.problem(n, h, h, c, f, f, 1, f // 2)
         d = dwc.plan_describe(p, 0)
-        assert (" f32=1 " in d) == want, (h, f, d)
+        assert (" f32=1 " in d) == want, (n, h, c, f, d)
+        if want:
+            assert f" img={img} " in d, (n, h, c, f, d)
+    # the images kernel: 4 tiles per wave above width 8, else 2
+    d = dwc.plan_describe(dwc.problem(64, 14, 14, 512, 31, 31, 1, 15), 0)
+    assert " t=4 img=1 rg=4 cg=1 tiles=64 " in d, d  # 16 image groups x 4 row groups
+    d = dwc.plan_describe(dwc.problem(64, 7, 7, 1024, 27, 27, 1, 13), 0)
+    assert " t=2 img=1 rg=2 cg=1 tiles=32 " in d, d
+    # fewer than 4 images, or too few waves: the rows kernel
+    d = dwc.plan_describe(dwc.problem(3, 14, 14, 512, 31, 31, 1, 15), 0)
+    assert " img=0 " in d, d
+    monkeypatch.setenv("DWC_MFMA_F32_IMG", "1")
+    d = dwc.plan_describe(dwc.problem(6, 14, 14, 16, 21, 21, 1, 10, algo="mfma"), 0)
+    assert " t=4 img=1 rg=4 cg=1 tiles=8 " in d, d
+    d = dwc.plan_describe(dwc.problem(3, 14, 14, 16, 21, 21, 1, 10, algo="mfma"), 0)
+    assert " img=0 " in d, d
+    monkeypatch.setenv("DWC_MFMA_F32_IMG", "0")
+    assert " img=0 " in dwc.plan_describe(dwc.problem(64, 14, 14, 512, 31, 31, 1, 15), 0)
+    monkeypatch.delenv("DWC_MFMA_F32_IMG")
     # the band width rounds the filter width up; tiles per wave and groups
     d = dwc.plan_describe(dwc.problem(2, 12, 20, 16, 5, 11, 1, (2, 3), algo="mfma"), 0)
     assert " fw=11 fh=5 " in d and " fwi=13 " in d and " same=0 " in d, d
     # width 57: four right-aligned 16-column groups issue fewer instructions
     # than three 28-column ones (the last two overlapping in 27 columns)
     d = dwc.plan_describe(dwc.problem(2, 30, 57, 16, 21, 21, 1, 10, algo="mfma"), 0)
-    assert " t=4 " in d and " cg=4 " in d and " rg=8 " in d and " same=1 " in d, d
+    assert " t=4 img=0 " in d and " cg=4 " in d and " rg=8 " in d and " same=1 " in d, d
     monkeypatch.setenv("DWC_MFMA_F32_T", "2")
     d = dwc.plan_describe(dwc.problem(2, 30, 57, 16, 21, 21, 1, 10, algo="mfma"), 0)
     assert " t=2 " in d and " cg=8 " in d, d

@@ -41,17 +41,36 @@ def _ids(t):
     return "x".join(map(str, t[:6])) + f"_p{t[7]}"
 
 
+# batches of 4 and more: the images kernel (fwd_mfma_f32n), ragged last
+# image groups included
+F32N_SHAPES = [
+    (4, 14, 14, 32, 13, 13, 1, 6),
+    (6, 9, 23, 16, 17, 17, 1, 8),
+    (5, 28, 28, 16, 31, 31, 1, 15),
+    (4, 10, 57, 16, 21, 21, 1, 10),
+    (7, 12, 20, 16, 5, 11, 1, (2, 3)),
+    (4, 10, 10, 16, 13, 13, 1, 14),
+    (9, 7, 7, 16, 31, 31, 1, 15),
+    (4, 40, 8, 16, 64, 7, 1, (31, 3)),
+    (5, 6, 40, 16, 1, 31, 1, (0, 15)),
+]
+
+
+@pytest.mark.parametrize("img", [0, 1])
 @pytest.mark.parametrize("tile", ["auto", "2", "4", "7"])
 @pytest.mark.parametrize("op", ["fwd", "bwd_data"])
-@pytest.mark.parametrize("shape", F32M_SHAPES, ids=_ids)
-def test_mfma_f32_parity(shape, op, tile, monkeypatch):
+@pytest.mark.parametrize("shape", F32M_SHAPES + F32N_SHAPES, ids=_ids)
+def test_mfma_f32_parity(shape, op, tile, img, monkeypatch):
+    s = _shape(shape)
+    if img and (s.n < 4 or tile == "7"):
+        pytest.skip("the images kernel takes batches of 4 and more, 2 or 4 tiles per wave")
     if tile != "auto":
         monkeypatch.setenv("DWC_MFMA_F32_T", tile)
-    s = _shape(shape)
+    monkeypatch.setenv("DWC_MFMA_F32_IMG", str(img))
     p = dwc.problem(s.n, s.h, s.w, s.c, s.fh, s.fw, 1, (s.pad_h, s.pad_w), dtype=DT["f32"],
                     algo="mfma")
     d = dwc.plan_describe(p, OPS[op])
-    assert " f32=1 " in d, d
+    assert " f32=1 " in d and f" img={img} " in d, d
     if tile != "auto":
         assert f" t={tile} " in d, d
     inp = make_inputs(s, "f32", seed=70 + sum(shape[:6]))
@@ -61,7 +80,8 @@ def test_mfma_f32_parity(shape, op, tile, monkeypatch):
     check_parity(got, want, mag, op, s, "f32", what=f"t={tile}")
 
 
-@pytest.mark.parametrize("shape", [(2, 14, 14, 32, 13, 13, 1, 6), (2, 30, 57, 16, 21, 21, 1, 10)],
+@pytest.mark.parametrize("shape", [(2, 14, 14, 32, 13, 13, 1, 6), (2, 30, 57, 16, 21, 21, 1, 10),
+                                   (5, 14, 14, 32, 13, 13, 1, 6), (6, 30, 57, 16, 21, 21, 1, 10)],
                          ids=_ids)
 def test_mfma_f32_outputs_fully_overwritten(shape):
     s = _shape(shape)
@@ -77,10 +97,11 @@ def test_mfma_f32_outputs_fully_overwritten(shape):
         check_parity(t.double().cpu().numpy(), want, mag, op, s, "f32", what=op)
 
 
-def test_mfma_f32_deterministic():
+@pytest.mark.parametrize("n", [2, 6])
+def test_mfma_f32_deterministic(n):
     """Overlapping column groups write the same values: two runs agree bit
     for bit."""
-    s = _shape((2, 30, 57, 16, 21, 21, 1, 10))
+    s = _shape((n, 30, 57, 16, 21, 21, 1, 10))
     inp = make_inputs(s, "f32", seed=72)
     x, w = to_device(inp.x), to_device(inp.w)
     a = dwc.fwd(x, w, 1, 10, algo="mfma")
