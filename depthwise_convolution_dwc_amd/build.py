@@ -54,6 +54,7 @@ def _units():
     u.append(("hip", "inst_mfma_batch.hip", "inst_mfma_batch.o",
               ["-mllvm", "-amdgpu-mfma-vgpr-form"]))
     u.append(("hip", "inst_mfma_f32.hip", "inst_mfma_f32.o", ["-mllvm", "-amdgpu-mfma-vgpr-form"]))
+    u.append(("hip", "inst_mfma_h4.hip", "inst_mfma_h4.o", ["-mllvm", "-amdgpu-mfma-vgpr-form"]))
     u.append(("hip", "dwc_api.cpp", "dwc_api.o", ["-x", "hip"]))
     u.append(("cxx", "dwc_plan.cpp", "dwc_plan.o", []))
     return u

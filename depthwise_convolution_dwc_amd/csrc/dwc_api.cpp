@@ -34,6 +34,13 @@ hipError_t launch_fwd_type(const Plan& pl, const void* in, const void* filt, flo
     }
     return hipErrorInvalidValue;
   }
+  if (pl.kind == PLAN_MFMA && pl.h4m) {
+    MfmaF32Args m = pl.mf;
+    m.in = in;
+    m.filt = filt;
+    m.out = out;
+    return launch_fwd_mfma_h4(pl.dt, pl.h4m_fwi, pl.h4m_t, pl.flip, m, s);
+  }
   if (pl.kind == PLAN_MFMA && pl.f32m) {
     MfmaF32Args m = pl.mf;
     m.in = in;

@@ -263,9 +263,24 @@ constexpr int kF32mStageBatch = 8;  // 16-byte band loads in flight per thread
 constexpr int f32m_fwi(int fw) {
   return fw <= 13 ? 13 : fw <= 17 ? 17 : fw <= 21 ? 21 : fw <= 27 ? 27 : fw <= 31 ? 31 : 0;
 }
+// 16-bit forward-type kernel on the 4x4x4 matrix instructions with 4 images
+// as the matrix rows (fwd_mfma_h4n; arguments: MfmaF32Args with 16-bit X
+// and filter): instantiated band widths and 4-column tiles per wave.
+#define DWC_H4M_FW_LIST(M) M(9) M(13) M(17)
+#define DWC_H4M_T_LIST(M) M(4) M(7)
+constexpr int kH4mCb = 16;         // channels per wave (the 16 blocks)
+constexpr int kH4mRows = 4;        // output rows per wave (the accumulator ring)
+constexpr int kH4mMaxWaves = 8;    // waves per workgroup
+constexpr int kH4mStageBatch = 4;  // band entries (4 two-byte loads each) in flight per thread
+constexpr int kH4mMinF = 9;        // AUTO: filters from this many rows and columns
+constexpr int kH4mMaxF = 13;       // ... up to this many columns
+constexpr int kH4mMaxOw = 16;      // ... on outputs at most this wide
+constexpr int kH4mFillWaves = 2048;  // ... with 8 waves per CU of the MI355X
+constexpr int h4m_fwi(int fw) { return fw <= 9 ? 9 : fw <= 13 ? 13 : fw <= 17 ? 17 : 0; }
 struct MfmaF32Args {
-  const void* in;    // N x IH x IW x C fp32 (X, or dY for the data gradient)
-  const void* filt;  // FH x FW x C fp32
+  const void* in;    // N x IH x IW x C fp32 (X, or dY for the data gradient);
+                     // bf16/fp16 for fwd_mfma_h4n
+  const void* filt;  // FH x FW x C, the same type
   float* out;        // N x OH x OW x C
   int N, IH, IW, C, OH, OW;
   int FH, FW, PH, PW;
@@ -276,7 +291,7 @@ struct MfmaF32Args {
   int same;          // PW == (FWI - 1) / 2, FW == FWI and IW == OW: the first and
                      // last column groups skip their padding columns
   int groups;        // workgroups per channel block: ceil(tiles / nw)
-  int lds_bytes;     // FH x (FWI + 6) x 16 floats
+  int lds_bytes;     // FH x (FWI + 6) x 16 floats; fwd_mfma_h4n: FH x S x 64 x 8 bytes
   int num_blocks;    // cblk * groups
   uint64_t fw_magic; // div_magic(FW): filter tap -> (row, column)
 };

@@ -48,6 +48,10 @@ hipError_t launch_fwd_mfma_batch16(int dt, int ng, bool flip, const MfmaBatchArg
 // C % 16 == 0): fwi the instantiated band width (DWC_F32M_FW_LIST), t the
 // 4-column output tiles per wave (DWC_F32M_T_LIST; 2 or 4 with img), img
 // 4 images instead of 4 output rows as the matrix rows (fwd_mfma_f32n).
+// 16-bit forward-type kernel on the 4x4x4 matrix instructions, 4 images as
+// the matrix rows (fwd_mfma_h4n).
+hipError_t launch_fwd_mfma_h4(int dt, int fwi, int t, bool flip, const MfmaF32Args& a,
+                              hipStream_t s);
 hipError_t launch_fwd_mfma_f32(int fwi, int t, bool img, bool flip, const MfmaF32Args& a,
                                hipStream_t s);
 

@@ -301,6 +301,72 @@ static int64_t f32m_cost(int ow, int fwi, int t, bool same) {
   return n;
 }
 
+// 16-bit plan on the 4x4x4 matrix instructions (fwd_mfma_h4n): false if the
+// kernel does not apply.  bf16/fp16 operands, stride 1, C % 16 == 0,
+// FW <= 17, the band of every filter row and the waves' row buffers in one
+// CU's LDS, 32-bit offsets within the batch.  DWC_MFMA_H4: 0 never, 1
+// wherever it applies.  AUTO takes it for filters of kH4mMinF to kH4mMaxF
+// rows and columns on outputs at most kH4mMaxOw wide while its waves fill
+// the GPU (MI355X, bf16, N=64: width 14 C=512 9x9 / 13x13 19 / 24 us
+// against 28 / 32 us; width 7 C=1024 14 / 17 us against 42 / 48 us; at
+// widths 28 and 56, at 17x17 and with fewer waves the other kernels are
+// as fast or faster: the 13x13 N=128 28x28 C=512 forward 143 against
+// 113 us).  T: 7 tiles per wave where the output is at least 28 wide, else
+// 4.
+static bool plan_mfma_h4(const FwdArgs& f, int dt, bool flip, Plan* q) {
+  if ((dt != DT_BF16 && dt != DT_F16) || f.SH != 1 || f.SW != 1 || f.C % kH4mCb != 0 ||
+      f.FW < 1 || f.FW > 17 || f.FH < 1)
+    return false;
+  const int64_t waves = (int64_t)((f.N + 3) / 4) * ((f.OH + kH4mRows - 1) / kH4mRows) *
+                        ((f.OW + 15) / 16) * (f.C / kH4mCb);
+  const bool pick = f.FH >= kH4mMinF && f.FH <= kH4mMaxF && f.FW >= kH4mMinF &&
+                    f.FW <= kH4mMaxF && f.OW <= kH4mMaxOw && waves >= kH4mFillWaves;
+  const char* env = getenv("DWC_MFMA_H4");
+  if (env ? atoi(env) == 0 : !pick) return false;
+  if ((int64_t)f.N * f.IH * f.IW * f.C * 2 >= kI32Max || (int64_t)f.OH * f.OW * f.C * 4 >= kI32Max)
+    return false;
+  const int fwi = h4m_fwi(f.FW);
+  const int S = (fwi + 6) / 4;
+  const int64_t lds = (int64_t)f.FH * S * 64 * 8;  // one channel block's band
+  const bool same = f.PW == (fwi - 1) / 2 && f.FW == fwi && f.IW == f.OW;
+  int t = f.OW >= 28 ? 7 : 4;
+  if (const char* v = getenv("DWC_MFMA_H4_T")) {
+    const int tv = atoi(v);
+    if (tv == 4 || tv == 7) t = tv;
+  }
+  MfmaF32Args m{};
+  m.N = f.N; m.IH = f.IH; m.IW = f.IW; m.C = f.C; m.OH = f.OH; m.OW = f.OW;
+  m.FH = f.FH; m.FW = f.FW; m.PH = f.PH; m.PW = f.PW;
+  // a wave: 4 images x kH4mRows rows x 4t columns x kH4mCb channels; the
+  // workgroup's waves share the band of their channel block
+  m.cblk = f.C / kH4mCb;
+  m.rg = (f.OH + kH4mRows - 1) / kH4mRows;
+  m.cg = f.OW >= 4 * t ? (f.OW + 4 * t - 1) / (4 * t) : 1;
+  const int64_t tiles = (int64_t)((f.N + 3) / 4) * m.rg * m.cg;
+  if (tiles > kI32Max) return false;
+  m.tiles = (int)tiles;
+  m.nw = (int)std::min<int64_t>(kH4mMaxWaves, tiles);
+  m.same = same ? 1 : 0;
+  m.groups = (int)((tiles + m.nw - 1) / m.nw);
+  // the band, then each wave's row buffer (4 images x NAP columns x 32 bytes)
+  const int na = 4 * (t + S - 1), nap = na + ((2 - na % 8) + 8) % 8;
+  const int64_t lds_all = lds + (int64_t)m.nw * 4 * nap * 32;
+  if (lds_all > kLdsPerCu) return false;
+  m.lds_bytes = (int)lds_all;
+  const int64_t blocks = (int64_t)m.cblk * m.groups;
+  if (blocks > kI32Max) return false;
+  m.num_blocks = (int)blocks;
+  q->kind = PLAN_MFMA;
+  q->h4m = true;
+  q->h4m_fwi = fwi;
+  q->h4m_t = t;
+  q->flip = flip;
+  q->blocks = (int)blocks;
+  q->mf = m;
+  q->fa = f;
+  return true;
+}
+
 // fp32 matrix-core plan (fwd_mfma_f32, fwd_mfma_f32n): false if the kernels
 // do not apply.  fp32 operands, stride 1, C % 16 == 0, FW <= 31, FH <= 64
 // (the band of every filter row in LDS), 32-bit offsets within one image
@@ -808,7 +874,7 @@ int make_plan(const dwc_problem* p, int op, Plan* pl, std::string* err) {
     // Packed MFMA for half-precision operands (the stride-1 data gradient
     // too: stride 1 is part of the kernel's conditions).
     if (p->algo == DWC_ALGO_AUTO || p->algo == DWC_ALGO_MFMA) {
-      if (plan_mfma_batch(f, dt, bwd, &q) || plan_mfma(f, dt, bwd, &q) ||
+      if (plan_mfma_h4(f, dt, bwd, &q) || plan_mfma_batch(f, dt, bwd, &q) || plan_mfma(f, dt, bwd, &q) ||
           plan_mfma8(f, dt, bwd, &q) ||
           plan_mfma_f32(f, dt, bwd, p->algo == DWC_ALGO_MFMA, &q)) {
         *pl = q;
@@ -1092,6 +1158,15 @@ std::string describe(const Plan& pl) {
              ops[pl.op], dt_name(pl.dt), w.FW, w.FH, pl.nfm, pl.nfn, pl.nk, pl.pf, pl.cb, w.xr,
              w.xp, w.dyp, w.dpad, w.hx, w.ix, w.e_lo, w.hd, w.id, w.lds_bytes, w.Z, w.ipb,
              w.cblk, pl.blocks, pl.ws_bytes);
+    return buf;
+  }
+  if (pl.kind == PLAN_MFMA && pl.h4m) {
+    const MfmaF32Args& m = pl.mf;
+    snprintf(buf, sizeof buf,
+             "%s mfma dt=%s fw=%d fh=%d flip=%d h4=1 fwi=%d t=%d rg=%d cg=%d tiles=%d "
+             "nw=%d same=%d cblk=%d lds=%d blocks=%d",
+             ops[pl.op], dt_name(pl.dt), m.FW, m.FH, (int)pl.flip, pl.h4m_fwi, pl.h4m_t, m.rg,
+             m.cg, m.tiles, m.nw, m.same, m.cblk, m.lds_bytes, pl.blocks);
     return buf;
   }
   if (pl.kind == PLAN_MFMA && pl.f32m) {

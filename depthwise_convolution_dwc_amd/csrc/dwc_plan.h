@@ -49,6 +49,9 @@ struct Plan {
   int f32m_fwi = 0, f32m_t = 0;  // instantiated band width, 4-column tiles per wave
   bool f32m_img = false;         // 4 images (not 4 output rows) as the matrix rows
   MfmaF32Args mf{};
+  // 16-bit forward-type kernel on 4x4x4 matrix instructions (arguments in mf)
+  bool h4m = false;
+  int h4m_fwi = 0, h4m_t = 0;  // instantiated band width, 4-column tiles per wave
   // fp32 matrix-core filter gradient
   bool wf32 = false;
   int wf32_tw = 0, wf32_nb = 0;  // column tiles, 4-column output groups per wave

@@ -79,7 +79,9 @@ typedef enum {
                              of 8, FW <= 32, output width <= 64 for the
                              forward and data gradient (the batch as the
                              second matrix dimension for widths up to 32
-                             and tall filters), input width <= 64 and
+                             and tall filters; the 4x4x4 form with 4
+                             images as the matrix rows for FW <= 17 on
+                             narrow outputs), input width <= 64 and
                              FH <= 32 for the filter gradient; fp8: the
                              same with C a multiple of 16 for the forward
                              and data gradient (also the K=128 fp8 MFMA,

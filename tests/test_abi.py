@@ -526,3 +526,34 @@ def test_dtype_and_status_codes_match_the_header():
     assert [d[k] for k in ("DWC_OK", "DWC_ERR_BAD_PARAM", "DWC_ERR_UNSUPPORTED",
                            "DWC_ERR_MISALIGNED", "DWC_ERR_WORKSPACE", "DWC_ERR_ALIAS",
                            "DWC_ERR_HIP")] == list(range(7))
+
+
+def test_h4_plans(monkeypatch):
+    """The 16-bit 4x4x4 kernel (fwd_mfma_h4n): AUTO on outputs up to 16
+    wide with 9x9 to 13x13 filters while its waves fill the GPU; its tile
+    shape; fp32 and fp8 never take it."""
+    monkeypatch.delenv("DWC_MFMA_H4", raising=False)
+    for (n, h, c, f, want) in ((64, 14, 512, 13, True), (64, 7, 1024, 9, True),
+                               (64, 14, 512, 17, False), (64, 28, 256, 13, False),
+                               (16, 14, 512, 13, False), (64, 14, 512, 7, False),
+                               (128, 28, 512, 13, False)):
+        for dt in (dwc.BF16, dwc.F16):
+            d = dwc.plan_describe(dwc.problem(n, h, h, c, f, f, 1, f // 2, dtype=dt), 0)
+            assert (" h4=1 " in d) == want, (n, h, c, f, d)
+    d = dwc.plan_describe(dwc.problem(64, 14, 14, 512, 13, 13, 1, 6, dtype=dwc.BF16), 1)
+    assert d.startswith("bwd_data mfma") and " flip=1 h4=1 fwi=13 t=4 " in d, d
+    # 16 image groups x 4 row groups; the band (13 x 4 steps x 512 bytes) and
+    # 8 row buffers of 4 images x 34 columns x 32 bytes
+    assert " rg=4 cg=1 tiles=64 nw=8 same=1 cblk=32 lds=61440 " in d, d
+    for dt in (dwc.F32, dwc.FP8_E4M3):
+        d = dwc.plan_describe(dwc.problem(64, 14, 14, 512, 13, 13, 1, 6, dtype=dt), 0)
+        assert " h4=1 " not in d, d
+    monkeypatch.setenv("DWC_MFMA_H4", "0")
+    assert " h4=1 " not in dwc.plan_describe(dwc.problem(64, 14, 14, 512, 13, 13, 1, 6,
+                                                         dtype=dwc.BF16), 0)
+    # forced: every 16-bit stride-1 problem with C % 16 == 0 and FW <= 17
+    monkeypatch.setenv("DWC_MFMA_H4", "1")
+    d = dwc.plan_describe(dwc.problem(2, 30, 57, 16, 17, 17, 1, 8, dtype=dwc.F16), 0)
+    assert " h4=1 fwi=17 t=7 rg=8 cg=3 " in d, d
+    d = dwc.plan_describe(dwc.problem(2, 30, 57, 24, 17, 17, 1, 8, dtype=dwc.F16), 0)
+    assert " h4=1 " not in d, d  # C % 16 != 0
