@@ -238,9 +238,17 @@ __global__ __launch_bounds__(64 * kH4mMaxWaves) void fwd_mfma_h4n(MfmaF32Args a)
 
   // ---- outputs: register i of D[j][m] is image n0 + i, row oh0 + j,
   // column ow0 + 4m + q
+  // The last column group, moved left to end at the right edge, writes only
+  // the columns that no other group owns: its K steps group the taps of a
+  // column differently, so a second write could differ in the last bits
+  // (and the last writer would decide)
+  const int own0 = cgi * 4 * T;
   const uint32_t orowb = (uint32_t)a.OW * (uint32_t)C * 4u;
   const uint32_t ooff = (uint32_t)(((ow0 + q) * C + c0 + b) * 4);
   const uint32_t sstep = (uint32_t)C * 16u;
+  uint32_t mo[T];
+#pragma unroll
+  for (int m = 0; m < T; ++m) mo[m] = ow0 + 4 * m + q >= own0 ? ooff + (uint32_t)m * sstep : kOOB;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (n0 + i >= a.N) break;  // uniform
@@ -255,8 +263,7 @@ __global__ __launch_bounds__(64 * kH4mMaxWaves) void fwd_mfma_h4n(MfmaF32Args a)
         // the element is copied out first: this compiler's __builtin_bit_cast
         // of a vector element expression reads element 0
         const float v = D[j][m][i];
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ors,
-                                              (int)(ooff + (uint32_t)m * sstep), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ors, (int)mo[m], 0, 0);
       }
     }
   }

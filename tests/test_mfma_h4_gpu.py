@@ -81,14 +81,18 @@ def test_mfma_h4_outputs_fully_overwritten(shape, monkeypatch):
         check_parity(t.double().cpu().numpy(), want, mag, op, s, "bf16", what=op)
 
 
-def test_mfma_h4_deterministic(monkeypatch):
-    """Overlapping column groups write the same values: two runs agree bit
-    for bit."""
+@pytest.mark.parametrize("tile", ["4", "7"])
+def test_mfma_h4_deterministic(tile, monkeypatch):
+    """The last column group overlaps the one before it and groups a
+    column's taps differently; only one of them writes each column, so
+    repeated runs agree bit for bit."""
     monkeypatch.setenv("DWC_MFMA_H4", "1")
+    monkeypatch.setenv("DWC_MFMA_H4_T", tile)
     s = _shape((6, 30, 57, 16, 17, 17, 1, 8))
     inp = make_inputs(s, "f16", seed=172)
     x, w = to_device(inp.x), to_device(inp.w)
     a = dwc.fwd(x, w, 1, 8, algo="mfma")
-    b = dwc.fwd(x, w, 1, 8, algo="mfma")
-    sync()
-    assert torch.equal(a, b)
+    for _ in range(4):
+        b = dwc.fwd(x, w, 1, 8, algo="mfma")
+        sync()
+        assert torch.equal(a, b)
