@@ -346,6 +346,11 @@ struct ReduceArgs {
 // a slice of images; it writes one partial per slice in the channel-blocked
 // layout that reduce_partials reads with cb = kWgmCb.
 constexpr int kWgmCb = 8;
+// Slices of the packed filter gradients (wgm_slices): partial bytes of all
+// slices at most this fraction of the operands' bytes, and about this many
+// rounds of resident workgroups
+constexpr double kWgmPartFrac = 1.0 / 6.0;
+constexpr double kWgmFill = 4.0;
 // Staging items (pairs of pixels of one row, kWgmCb channels) per thread
 // that a workgroup holds in registers while the previous image computes.
 constexpr int kWgmMaxPf = 2;

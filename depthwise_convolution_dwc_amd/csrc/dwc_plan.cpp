@@ -534,6 +534,44 @@ bool plan_mfma8(const FwdArgs& f, int dt, bool flip, Plan* q) {
   return true;
 }
 
+// Slices of whole images for the packed filter gradients (Z * cblk
+// workgroups, `resident` of them at once).  A requested split is taken as
+// it is.  Otherwise, where the slice partials are cheap (at most kWgmPartFrac
+// of the operands' bytes with at least one round of workgroups), about
+// kWgmFill rounds of workgroups: more, shorter slices measured faster than
+// one round of long ones (MI355X, N=128 28x28 C=512: bf16 13x13 118 -> 98
+// us at 43 slices instead of 12, e4m3 13x13 96 -> 80 us at 32 instead of
+// 8, fp16 31x31 166 -> 158 us at 16 instead of 12).  Where they are not
+// (a slice's partial outweighs the images it saves), the count whose
+// dispatch rounds times images per slice (plus one image's worth of fixed
+// cost per round) is least, preferring fewer slices (e4m3 31x31: 8).
+static int64_t wgm_slices(const dwc_problem* p, int64_t nn, int64_t cblk, int64_t resident,
+                          int64_t eb) {
+  if (p->wgrad_split > 0) return std::min<int64_t>(p->wgrad_split, nn);
+  const double part = (double)p->fh * p->fw * cblk * kWgmCb * 4;  // bytes per slice
+  const double ops = (double)nn * ((double)p->h * p->w * 2) * p->c * eb;  // X and dY, about
+  const int64_t cap = (int64_t)(kWgmPartFrac * ops / part);
+  const int64_t floor_z = (resident + cblk - 1) / cblk;
+  if (cap >= floor_z) {
+    const int64_t target = (int64_t)(kWgmFill * (double)resident / (double)cblk + 0.999);
+    const int64_t z = std::min(std::min(std::max(target, floor_z), cap), nn);
+    const int64_t ipb = (nn + z - 1) / z;
+    return (nn + ipb - 1) / ipb;
+  }
+  int64_t z = 1, best = -1;
+  for (int64_t zc = 1; zc <= std::min<int64_t>(nn, 8 * resident); ++zc) {
+    const int64_t ipb = (nn + zc - 1) / zc, zr = (nn + ipb - 1) / ipb;
+    if (zr != zc) continue;  // same split as a smaller count
+    const int64_t rounds = (zr * cblk + resident - 1) / resident;
+    const int64_t cost = rounds * (ipb + 1);
+    if (best < 0 || cost < best) {
+      best = cost;
+      z = zr;
+    }
+  }
+  return z;
+}
+
 // Packed-MFMA filter-gradient plan: false if the kernel does not apply.
 // kWgmCb channels per workgroup (one per wave); the batch is cut into Z
 // slices of whole images so that Z * cblk workgroups (about 1024, or the
@@ -571,31 +609,14 @@ bool plan_wgrad_mfma(const dwc_problem* p, int64_t oh, int64_t ow, Plan* q) {
   const int64_t lds = std::max(stage, part);
   if (lds > kMfmaMaxLds) return false;
   w.lds_bytes = (int)lds;
-  // Slices of whole images.  Workgroups resident at once: 256 CUs times
-  // what one CU holds (LDS; registers: waves per SIMD / 2 for 8-wave
-  // groups).  Unless a split is requested, pick the slice count whose
-  // dispatch rounds times images per slice (plus one image's worth of
-  // fixed cost per round) is least, preferring fewer slices.
+  // Slices of whole images (wgm_slices).  Workgroups resident at once: the
+  // CUs times what one CU holds (LDS; registers: waves per SIMD / 2 for
+  // 8-wave groups).
   const int64_t per_cu = std::max<int64_t>(
       1, std::min<int64_t>(kLdsPerCu / lds, wgm_waves_per_eu(nfm, nfn, nk, pf) / 2));
   const int64_t resident = (int64_t)device_cus() * per_cu;
   const int64_t nn = std::max<int64_t>(p->n, 1);  // an empty batch only zero-fills dW
-  int64_t z = 1;
-  if (p->wgrad_split > 0) {
-    z = std::min<int64_t>(p->wgrad_split, nn);
-  } else {
-    int64_t best = -1;
-    for (int64_t zc = 1; zc <= std::min<int64_t>(nn, 8 * resident); ++zc) {
-      const int64_t ipb = (nn + zc - 1) / zc, zr = (nn + ipb - 1) / ipb;
-      if (zr != zc) continue;  // same split as a smaller count
-      const int64_t rounds = (zr * w.cblk + resident - 1) / resident;
-      const int64_t cost = rounds * (ipb + 1);
-      if (best < 0 || cost < best) {
-        best = cost;
-        z = zr;
-      }
-    }
-  }
+  const int64_t z = wgm_slices(p, nn, w.cblk, resident, elem_bytes(dt));
   w.ipb = (int)((nn + z - 1) / z);
   w.Z = (int)((nn + w.ipb - 1) / w.ipb);
   const int64_t blocks = (int64_t)w.Z * w.cblk;
@@ -728,22 +749,7 @@ bool plan_wgrad_mfma8(const dwc_problem* p, int64_t oh, int64_t ow, Plan* q) {
       std::max<int64_t>(1, std::min<int64_t>(kLdsPerCu / lds, wgm8_waves_per_eu(pf) / 2));
   const int64_t resident = (int64_t)device_cus() * per_cu;
   const int64_t nn = std::max<int64_t>(p->n, 1);
-  int64_t z = 1;
-  if (p->wgrad_split > 0) {
-    z = std::min<int64_t>(p->wgrad_split, nn);
-  } else {
-    int64_t best = -1;
-    for (int64_t zc = 1; zc <= std::min<int64_t>(nn, 8 * resident); ++zc) {
-      const int64_t ipb = (nn + zc - 1) / zc, zr = (nn + ipb - 1) / ipb;
-      if (zr != zc) continue;
-      const int64_t rounds = (zr * w.cblk + resident - 1) / resident;
-      const int64_t cost = rounds * (ipb + 1);
-      if (best < 0 || cost < best) {
-        best = cost;
-        z = zr;
-      }
-    }
-  }
+  const int64_t z = wgm_slices(p, nn, w.cblk, resident, elem_bytes(dt));
   w.ipb = (int)((nn + z - 1) / z);
   w.Z = (int)((nn + w.ipb - 1) / w.ipb);
   const int64_t blocks = (int64_t)w.Z * w.cblk;
