@@ -73,13 +73,19 @@ int strip_override(const char* var, int fallback) {
 
 // Chunks per image for a sweep launch: enough waves (~2048, two per SIMD)
 // to fill the GPU, with chunks of at least F rows (each chunk re-reads F-1
-// halo rows).
+// halo rows).  A launch that would still hold less than one wave per CU
+// takes chunks down to one row: its time is one wave's dependent chain, not
+// the halo traffic (N=1 14x14 C=32 7x7: 10.1 -> 5.2 us with 14 one-row
+// chunks instead of 2 of 7 rows; with full batches shorter chunks than F
+// rows were slower).
 int64_t sweep_chunks(int64_t waves_per_chunk, int64_t out_h, int f) {
   const int64_t w = std::max<int64_t>(waves_per_chunk, 1);
   int64_t target = 8 * (int64_t)device_cus();  // two waves per SIMD
   if (const char* v = getenv("DWC_SWEEP_WAVES")) target = std::max(1, atoi(v));
   const int64_t cpi = std::max<int64_t>(1, (target + w - 1) / w);
-  return std::min<int64_t>(cpi, std::max<int64_t>(1, out_h / f));
+  const int64_t whole = std::max<int64_t>(1, out_h / f);  // chunks of at least F rows
+  if (w * whole < (int64_t)device_cus()) return std::min<int64_t>(cpi, std::max<int64_t>(1, out_h));
+  return std::min<int64_t>(cpi, whole);
 }
 
 // Number of slices of the N*OH axis for the filter gradient (§5.1 splits
