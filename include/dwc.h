@@ -122,7 +122,7 @@ typedef enum {
 typedef enum {
     DWC_OK = 0,
     DWC_ERR_BAD_PARAM = 1,   /* sizes, strides, pads or dtypes invalid         */
-    DWC_ERR_UNSUPPORTED = 2, /* valid request this build does not implement     */
+    DWC_ERR_UNSUPPORTED = 2, /* valid request the library does not implement   */
     DWC_ERR_MISALIGNED = 3,  /* pointer not aligned to its element size         */
     DWC_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required      */
     DWC_ERR_ALIAS = 5,       /* an output overlaps an input                     */
