@@ -557,3 +557,39 @@ def test_h4_plans(monkeypatch):
     assert " h4=1 fwi=17 t=7 rg=8 cg=3 " in d, d
     d = dwc.plan_describe(dwc.problem(2, 30, 57, 24, 17, 17, 1, 8, dtype=dwc.F16), 0)
     assert " h4=1 " not in d, d  # C % 16 != 0
+
+
+def test_packed_wgrad_slices():
+    """Packed filter gradients: where the slice partials are cheap, about
+    four rounds of workgroups (N=128 28x28 C=512: 43 slices of 3 images at
+    13x13 in 16 bits, 32 of 4 in fp8, 16 of 8 at 31x31 in 16 bits); where
+    they are dear (fp8 31x31) the rounds-times-images choice; a requested
+    split as it is."""
+    def zs(f, dt, split=0):
+        d = dwc.plan_describe(dwc.problem(128, 28, 28, 512, f, f, 1, f // 2, dtype=dt,
+                                          wgrad_split=split), 2)
+        return [t for t in d.split() if t.startswith(("z=", "ipb="))]
+    assert zs(13, dwc.BF16) == ["z=43", "ipb=3"]
+    assert zs(13, dwc.F16) == ["z=43", "ipb=3"]
+    assert zs(31, dwc.F16) == ["z=16", "ipb=8"]
+    assert zs(13, dwc.FP8_E4M3) == ["z=32", "ipb=4"]
+    assert zs(31, dwc.FP8_E4M3) == ["z=8", "ipb=16"]
+    assert zs(13, dwc.BF16, split=12) == ["z=12", "ipb=11"]
+    # the partials of all slices stay within a sixth of the operand bytes
+    x_dy = 128 * 28 * 28 * 512 * 2 * 2
+    for f in (13, 31):
+        p = dwc.problem(128, 28, 28, 512, f, f, 1, f // 2, dtype=dwc.F16)
+        z = int(zs(f, dwc.F16)[0][2:])
+        assert z * f * f * 512 * 4 <= x_dy / 6
+
+
+def test_sweep_chunks_small_launches():
+    """Sweep launches under one wave per CU take one-row chunks; larger ones
+    keep chunks of at least F rows."""
+    d = dwc.plan_describe(dwc.problem(1, 14, 14, 32, 7, 7, 1, 3), 0)
+    assert " sweep " in d and " rows=1 cpi=14 " in d, d
+    d = dwc.plan_describe(dwc.problem(64, 7, 7, 1024, 7, 7, 1, 3), 0)
+    assert " rows=7 cpi=1 " in d, d
+    d = dwc.plan_describe(dwc.problem(64, 56, 56, 128, 7, 7, 1, 3), 0)
+    rows = int([t for t in d.split() if t.startswith("rows=")][0][5:])
+    assert rows >= 7, d
