@@ -191,14 +191,20 @@ constexpr int kBatchPrefetch = 1;
 constexpr int kBatchHalfPitch = kBatchImg * 16 + 64;
 constexpr int kBatchMaxCols = 32;
 // AUTO takes the batch-packed kernel from this filter height on; below it
-// the row-packed kernel is as fast or faster (13x13 at N=128 28x28 C=512
-// fp16: 114-120 against 121-124 us for the 16-image kernel, 163-167 for the
-// 32-image one), its matrix cores being idle either way.
+// the row-packed kernel is as fast or faster at N=128 28x28 C=512 (bf16
+// 7x7-15x15: 101-120 against 103-127 us for the 16-image kernel; fp16
+// 13x13: 114-120 against 121-124 us, 163-167 for the 32-image one), its
+// matrix cores being idle either way.
 constexpr int kBatchMinFh = 17;
+// ... from this height on for outputs at most 16 wide (bf16 N=64 14x14
+// C=512 15x15: 22 against 34 us).
+constexpr int kBatchMinFhNarrow = 14;
+constexpr int kBatchNarrowOw = 16;
 // ... for fp8 operands, where it takes the 16-image kernel from this filter
-// height on (13x13 at N=128 28x28 C=512 e4m3: 106 against 126 us for the
-// row-packed kernel).
-constexpr int kBatchMinFh8 = 13;
+// height on (e4m3, N=128 28x28 C=512 5x5-15x15: 85-109 against 103-125 us
+// for the row-packed kernel; N=64 28x28 C=256 9x9-15x15: 26-30 against
+// 32-34 us).
+constexpr int kBatchMinFh8 = 5;
 // The same packing with 16 images per v_mfma_f32_16x16x32 and two channels
 // per wave: a workgroup owns kB16Cb channels x kB16Img images x kB16Rows
 // output rows.  Staged rows: per channel, 4 column groups of 16 images x 16

@@ -246,7 +246,8 @@ bool plan_mfma_batch(const FwdArgs& f, int dt, bool flip, Plan* q) {
   // DWC_MFMA_BATCH: 0 never, 1 wherever it applies (for tests and A/B
   // timing); unset: from kBatchMinFh (fp8: kBatchMinFh8) filter rows on
   const char* env = getenv("DWC_MFMA_BATCH");
-  if (env ? atoi(env) == 0 : f.FH < (b8 ? kBatchMinFh8 : kBatchMinFh)) return false;
+  const int min_fh = b8 ? kBatchMinFh8 : f.OW <= kBatchNarrowOw ? kBatchMinFhNarrow : kBatchMinFh;
+  if (env ? atoi(env) == 0 : f.FH < min_fh) return false;
   Plan t = *q;  // q changes only when a kernel applies
   t.kind = PLAN_MFMA;
   t.batch = true;
