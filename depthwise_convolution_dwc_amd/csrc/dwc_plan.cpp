@@ -655,14 +655,17 @@ static bool plan_wgrad_mfma_f32(const dwc_problem* p, int64_t oh, int64_t ow, bo
       p->fh > 32 || p->c % kWf32Cb != 0)
     return false;
   // AUTO: where the 4x4 tiles cover the filter with little waste (at least
-  // 85% of the computed taps are real ones) and the filter has at least
-  // kWf32MinF rows and columns; on outputs at most 8 wide only the largest
-  // filters (MI355X, N=64 stages: 1.2-1.3x the vector kernels at 27x27 and
-  // 31x31 on 56, 28 and 14 wide outputs, 0.7-0.9x at 17x17 and 21x21, whose
-  // tiles are 72-77% real taps; at width 7, 1.10x at 31x31, 0.91x at 27x27).
+  // 85% of the computed taps are real ones; 64% for filters at most 16
+  // wide) and the filter has at least kWf32MinF rows and columns; on
+  // outputs at most 8 wide only the largest filters (MI355X, N=64 stages:
+  // 1.2-1.3x the vector kernels at 27x27 and 31x31 on 56, 28 and 14 wide
+  // outputs, 0.7-0.9x at 17x17 and 21x21, whose tiles are 72-77% real taps;
+  // 1.00-1.06x at 13x13 (66%); at width 7, 1.10x at 31x31, 0.91x at 27x27).
   const int64_t tiles = (int64_t)((p->fh + 3) / 4) * ((p->fw + 3) / 4);
+  const int fill = p->fw <= 16 ? 64 : 85;
   const bool pick = p->fh >= kWf32MinF && p->fw >= kWf32MinF &&
-                    (int64_t)p->fh * p->fw * 100 >= tiles * 16 * 85 && (ow > 8 || p->fw >= 29);
+                    (int64_t)p->fh * p->fw * 100 >= tiles * 16 * fill &&
+                    (ow > 8 || p->fw >= 29 || p->fw <= 16);
   const char* env = getenv("DWC_MFMA_F32");
   if (!forced && (env ? atoi(env) == 0 : !pick)) return false;
   if (p->h * p->w * p->c * 4 >= kI32Max || oh * ow * p->c * 4 >= kI32Max) return false;

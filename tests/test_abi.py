@@ -178,11 +178,13 @@ def test_fp32_mfma_plans_and_rejections(monkeypatch):
 
 def test_fp32_mfma_wgrad_plans(monkeypatch):
     monkeypatch.delenv("DWC_MFMA_F32", raising=False)
-    # AUTO: 4x4 tiles at least 85% real taps, 12+ rows and columns, outputs
-    # wider than 8 unless the filter is 29+ wide
+    # AUTO: 4x4 tiles at least 85% real taps (64% up to 16 columns), 12+
+    # rows and columns, outputs wider than 8 unless the filter is 29+ or at
+    # most 16 wide
     for (h, c, f, want) in ((56, 128, 31, True), (28, 256, 27, True), (56, 128, 17, False),
                             (56, 128, 21, False), (7, 1024, 27, False), (7, 1024, 31, True),
-                            (56, 128, 16, True), (56, 128, 9, False)):
+                            (56, 128, 16, True), (56, 128, 9, False), (56, 128, 13, True),
+                            (7, 1024, 13, True)):
         p = dwc.problem(64, h, h, c, f, f, 1, f // 2)
         d = dwc.plan_describe(p, 2)
         assert (" f32=1 " in d) == want, (h, f, d)
