@@ -200,6 +200,12 @@ constexpr int kBatchMinFh = 17;
 // C=512 15x15: 22 against 34 us).
 constexpr int kBatchMinFhNarrow = 14;
 constexpr int kBatchNarrowOw = 16;
+// ... and from this height on where its workgroups make a single round of
+// at least 3/4 of the CUs (one workgroup per CU: no second workgroup's
+// start-up or output phase to wait for; bf16 28x28 with 256 workgroups,
+// N=64 C=256 5x5-15x15 and N=32 C=512 9x9-13x13: 26-34 against 31-38 us;
+// with 512 or 1024 workgroups, or 128, slower than the row-packed kernel).
+constexpr int kBatchMinFhRound = 5;
 // ... for fp8 operands, where it takes the 16-image kernel from this filter
 // height on (e4m3, N=128 28x28 C=512 5x5-15x15: 85-109 against 103-125 us
 // for the row-packed kernel; N=64 28x28 C=256 9x9-15x15: 26-30 against

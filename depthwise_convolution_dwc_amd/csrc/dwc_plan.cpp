@@ -244,10 +244,14 @@ bool plan_mfma_batch(const FwdArgs& f, int dt, bool flip, Plan* q) {
       f.PH < 0 || f.FH > 64)
     return false;
   // DWC_MFMA_BATCH: 0 never, 1 wherever it applies (for tests and A/B
-  // timing); unset: from kBatchMinFh (fp8: kBatchMinFh8) filter rows on
+  // timing); unset: from kBatchMinFh (fp8: kBatchMinFh8) filter rows on,
+  // and for 16-bit operands from kBatchMinFhRound rows where the 16-image
+  // kernel's workgroups make one round of at least 3/4 of the CUs
   const char* env = getenv("DWC_MFMA_BATCH");
+  if (env && atoi(env) == 0) return false;
   const int min_fh = b8 ? kBatchMinFh8 : f.OW <= kBatchNarrowOw ? kBatchMinFhNarrow : kBatchMinFh;
-  if (env ? atoi(env) == 0 : f.FH < min_fh) return false;
+  const bool by_height = env || f.FH >= min_fh;
+  if (!by_height && (b8 || f.FH < kBatchMinFhRound)) return false;
   Plan t = *q;  // q changes only when a kernel applies
   t.kind = PLAN_MFMA;
   t.batch = true;
@@ -255,9 +259,12 @@ bool plan_mfma_batch(const FwdArgs& f, int dt, bool flip, Plan* q) {
   t.fa = f;
   const char* img = getenv("DWC_MFMA_BATCH_IMG");
   if ((b8 || !(img && atoi(img) == kBatchImg)) && plan_mfma_batch16(f, dt, &t)) {
+    const int64_t cus = device_cus();
+    if (!by_height && !(4 * (int64_t)t.blocks >= 3 * cus && t.blocks <= cus)) return false;
     *q = t;
     return true;
   }
+  if (!by_height) return false;
   // the 32-image kernel takes bf16 / fp16 operands only
   if (b8 || f.C % kBatchCb != 0 || f.N < 16) return false;
   // 32-bit offsets into one image group's input and output

@@ -595,3 +595,13 @@ def test_sweep_chunks_small_launches():
     d = dwc.plan_describe(dwc.problem(64, 56, 56, 128, 7, 7, 1, 3), 0)
     rows = int([t for t in d.split() if t.startswith("rows=")][0][5:])
     assert rows >= 7, d
+
+
+def test_batch_kernel_one_round():
+    """16-bit batch-packed forward below 17 filter rows only where its
+    workgroups make one round of at least 3/4 of the CUs (256 here)."""
+    for (n, c, f, want) in ((64, 256, 5, True), (32, 512, 13, True), (16, 1024, 13, True),
+                            (64, 512, 13, False), (32, 256, 13, False), (128, 512, 13, False),
+                            (64, 256, 3, False), (128, 512, 31, True)):
+        d = dwc.plan_describe(dwc.problem(n, 28, 28, c, f, f, 1, f // 2, dtype=dwc.BF16), 0)
+        assert (" batch=1 " in d) == want, (n, c, f, d)
