@@ -12,6 +12,9 @@ enum { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2, DT_E4M3 = 3, DT_E5M2 = 4 };
 // layout a wave's load of one pixel is 64 consecutive channels, i.e. one
 // 256-byte (fp32) or 128-byte (bf16/fp16) contiguous segment.
 constexpr int kWaveChannels = 64;
+// AUTO: 16-bit and fp8 operands stay on the sweep kernels up to this
+// square filter size (stride 1); the packed matrix-core kernels from above
+constexpr int kSweepAutoMaxF = 7;
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlockThreads = 64 * kWavesPerBlock;
 

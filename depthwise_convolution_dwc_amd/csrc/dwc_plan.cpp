@@ -871,6 +871,13 @@ int make_plan(const dwc_problem* p, int op, Plan* pl, std::string* err) {
   q.kind = direct ? PLAN_DIRECT : PLAN_GENERIC;
   // Sweep kernels: stride 1, square filter up to 9x9.
   const bool sweep_ok = p->stride_h == 1 && p->fh == p->fw && sweep_f(p->fw);
+  // AUTO keeps the sweeps for the smallest filters with any operand type:
+  // the packed matrix-core kernels lose there (MI355X, bf16 N=128 28x28
+  // C=512 3x3 / 5x5 / 7x7: forward 64 / 68 / 93 against 96 / 97 / 98 us,
+  // filter gradient 47 / 52 / 80 against 97 / 94 / 92 us; e4m3 N=64 7x7
+  // C=1024 3x3 forward 12 against 47 us; from 9x9 on the matrix cores win)
+  const bool sweep_auto = p->algo == DWC_ALGO_AUTO && sweep_ok && direct_fw(p->fw) &&
+                          p->fw <= kSweepAutoMaxF && p->in_dtype != DT_F32;
   const bool hybrid = p->algo == DWC_ALGO_HYBRID;
   if (hybrid && (op != DWC_OP_BWD_FILTER || dt != DT_F16 || !sweep_ok))
     return fail(err, DWC_ERR_UNSUPPORTED,
@@ -896,7 +903,7 @@ int make_plan(const dwc_problem* p, int op, Plan* pl, std::string* err) {
     f.PW = bwd ? p->fw - 1 - p->pad_w : p->pad_w;
     // Packed MFMA for half-precision operands (the stride-1 data gradient
     // too: stride 1 is part of the kernel's conditions).
-    if (p->algo == DWC_ALGO_AUTO || p->algo == DWC_ALGO_MFMA) {
+    if ((p->algo == DWC_ALGO_AUTO && !sweep_auto) || p->algo == DWC_ALGO_MFMA) {
       if (plan_mfma_h4(f, dt, bwd, &q) || plan_mfma_batch(f, dt, bwd, &q) || plan_mfma(f, dt, bwd, &q) ||
           plan_mfma8(f, dt, bwd, &q) ||
           plan_mfma_f32(f, dt, bwd, p->algo == DWC_ALGO_MFMA, &q)) {
@@ -990,7 +997,7 @@ int make_plan(const dwc_problem* p, int op, Plan* pl, std::string* err) {
   } else {
     if (p->wgrad_split > 0 && p->n * oh > 0 && p->wgrad_split > p->n * oh)
       return fail(err, DWC_ERR_BAD_PARAM, "wgrad_split larger than N*OH");
-    if (p->algo == DWC_ALGO_AUTO || p->algo == DWC_ALGO_MFMA) {
+    if ((p->algo == DWC_ALGO_AUTO && !sweep_auto) || p->algo == DWC_ALGO_MFMA) {
       if (plan_wgrad_mfma(p, oh, ow, &q) || plan_wgrad_mfma8(p, oh, ow, &q) ||
           plan_wgrad_mfma_f32(p, oh, ow, p->algo == DWC_ALGO_MFMA, &q)) {
         const int64_t m = (int64_t)p->fh * p->fw * p->c;

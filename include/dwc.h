@@ -93,7 +93,8 @@ typedef enum {
                              per instruction; output rows or images by
                              output columns, filter columns by rows).  AUTO takes them for the
                              problems where they beat the vector kernels
-                             (large filters).  Operands must be finite:
+                             (filters from 9x9 on, or outside the sweeps'
+                             square 3x3-9x9 stride-1 set).  Operands must be finite:
                              the packing multiplies staged elements by
                              structural zeros as well, so an inf or NaN
                              operand turns outputs that share an

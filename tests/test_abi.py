@@ -453,7 +453,7 @@ def test_fp8_mfma_plans_and_rejections():
     filter rows, output width <= 64, LDS within its per-workgroup limit)."""
     for dt, name in ((dwc.FP8_E4M3, "e4m3"), (dwc.FP8_E5M2, "e5m2")):
         for f in (3, 7, 13, 17, 31):
-            p = dwc.problem(128, 28, 28, 512, f, f, 1, f // 2, dtype=dt)
+            p = dwc.problem(128, 28, 28, 512, f, f, 1, f // 2, dtype=dt, algo="mfma")
             for op in (0, 1):
                 d = dwc.plan_describe(p, op)
                 assert d.startswith(("fwd mfma", "bwd_data mfma")), d
@@ -482,7 +482,7 @@ def test_fp8_mfma_wgrad_plans():
     pitch an odd number of 16-byte units, LDS within the limit."""
     for dt in (dwc.FP8_E4M3, dwc.FP8_E5M2):
         for f in (3, 7, 13, 31):
-            p = dwc.problem(128, 28, 28, 512, f, f, 1, f // 2, dtype=dt)
+            p = dwc.problem(128, 28, 28, 512, f, f, 1, f // 2, dtype=dt, algo="mfma")
             d = dwc.plan_describe(p, 2)
             assert d.startswith("bwd_filter mfma"), d
             g = dict(kv.split("=") for kv in d.split()[2:])
@@ -597,11 +597,33 @@ def test_sweep_chunks_small_launches():
     assert rows >= 7, d
 
 
+def test_small_filters_stay_on_sweeps():
+    """AUTO keeps 16-bit and fp8 problems with square filters up to 7x7 at
+    stride 1 on the sweep kernels (all three operations); from 9x9 on, and
+    with algo=mfma, the packed matrix-core kernels."""
+    for dt in (dwc.BF16, dwc.F16, dwc.FP8_E4M3, dwc.FP8_E5M2):
+        for f in (3, 5, 7, 9):
+            p = dwc.problem(128, 28, 28, 512, f, f, 1, f // 2, dtype=dt)
+            for op in (0, 1, 2):
+                d = dwc.plan_describe(p, op)
+                assert (" sweep " in d) == (f <= 7), (dt, f, op, d)
+            q = dwc.problem(128, 28, 28, 512, f, f, 1, f // 2, dtype=dt, algo="mfma")
+            assert " mfma " in dwc.plan_describe(q, 0)
+    # fp32 keeps its own rules (the sweeps up to 9x9)
+    d = dwc.plan_describe(dwc.problem(64, 56, 56, 128, 9, 9, 1, 4), 0)
+    assert " sweep " in d, d
+
+
 def test_batch_kernel_one_round():
     """16-bit batch-packed forward below 17 filter rows only where its
     workgroups make one round of at least 3/4 of the CUs (256 here)."""
-    for (n, c, f, want) in ((64, 256, 5, True), (32, 512, 13, True), (16, 1024, 13, True),
+    for (n, c, f, want) in ((64, 256, 9, True), (32, 512, 13, True), (16, 1024, 13, True),
                             (64, 512, 13, False), (32, 256, 13, False), (128, 512, 13, False),
-                            (64, 256, 3, False), (128, 512, 31, True)):
+                            (128, 512, 31, True)):
         d = dwc.plan_describe(dwc.problem(n, 28, 28, c, f, f, 1, f // 2, dtype=dwc.BF16), 0)
         assert (" batch=1 " in d) == want, (n, c, f, d)
+    # with algo=mfma the rule picks between the packed kernels from 5 rows on
+    for (f, want) in ((5, True), (3, False)):
+        d = dwc.plan_describe(dwc.problem(64, 28, 28, 256, f, f, 1, f // 2, dtype=dwc.BF16,
+                                          algo="mfma"), 0)
+        assert (" batch=1 " in d) == want, (f, d)

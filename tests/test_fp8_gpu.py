@@ -133,7 +133,8 @@ BATCH16_SHAPES = [
 def test_fp8_batch16_parity(shape, op, dtype, monkeypatch):
     monkeypatch.setenv("DWC_MFMA_BATCH", "1")
     s = _shape(shape)
-    p = dwc.problem(s.n, s.h, s.w, s.c, s.fh, s.fw, 1, (s.pad_h, s.pad_w), dtype=DT[dtype])
+    p = dwc.problem(s.n, s.h, s.w, s.c, s.fh, s.fw, 1, (s.pad_h, s.pad_w), dtype=DT[dtype],
+                    algo="mfma")
     d = dwc.plan_describe(p, OPS[op])
     assert " batch=1 " in d and " imgs=16 " in d, d
     inp = make_inputs(s, dtype, seed=11 + sum(shape[:6]))

@@ -484,7 +484,8 @@ def test_mfma_batch_parity(shape, op, dtype, img, monkeypatch):
     want_imgs = _batch_imgs(s, img)
     if want_imgs is None or (img == 32 and want_imgs != 32):
         pytest.skip("the batch-packed kernel asked for does not take this shape")
-    p = dwc.problem(s.n, s.h, s.w, s.c, s.fh, s.fw, 1, (s.pad_h, s.pad_w), dtype=DT[dtype])
+    p = dwc.problem(s.n, s.h, s.w, s.c, s.fh, s.fw, 1, (s.pad_h, s.pad_w), dtype=DT[dtype],
+                    algo="mfma")
     d = dwc.plan_describe(p, OPS[op])
     assert " batch=1 " in d and f" imgs={want_imgs} " in d, d
     inp = make_inputs(s, dtype, seed=90 + sum(shape[:6]))
