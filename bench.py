@@ -360,8 +360,8 @@ def kernels_of(dwc, s, op, dtype="f32", algo="auto"):
         k = (f"wgrad_sweep<{dt}, {kv['f']}, {kv['strip']}>" if op == "bwd_filter" else
              f"fwd_sweep<{dt}, {kv['f']}, {kv['strip']}, {flip}")
     elif fam == "direct":
-        k = (f"wgrad_rows<{dt}, {kv['fw']}, {kv['sw']}, {kv['tj']}>" if op == "bwd_filter" else
-             f"fwd_rows<{dt}, {kv['fw']}, {kv['sw']}, {kv['tmw']}, {flip}")
+        k = (f"wgrad_rows<{dt}, {kv['kfw']}, {kv['sw']}, {kv['tj']}>" if op == "bwd_filter" else
+             f"fwd_rows<{dt}, {kv['kfw']}, {kv['sw']}, {kv['tmw']}, {flip}")
     elif fam == "phase":
         k = f"dgrad_phase<{dt}, {kv['km']}, "
     else:  # generic: one lane per output, 256 per workgroup

@@ -44,8 +44,10 @@ def _units():
     # completely, also with the fused prologue, so that every register-ring
     # index is a constant; LLVM's default size limit for that stops short
     for dt in (0, 1, 2, 3, 4):
-        u.append(("hip", "inst_direct.hip", f"inst_direct_dt{dt}.o",
-                  [f"-DDWC_INST_DT={dt}", "-mllvm", "-pragma-unroll-threshold=30000"]))
+        for pad in (0, 1):
+            u.append(("hip", "inst_direct.hip", f"inst_direct_dt{dt}{'_pad' if pad else ''}.o",
+                      [f"-DDWC_INST_DT={dt}", f"-DDWC_INST_PAD={pad}", "-mllvm",
+                       "-pragma-unroll-threshold=30000"]))
     u.append(("hip", "inst_generic.hip", "inst_generic.o", []))
     # MFMA accumulators in VGPRs: with AGPR accumulators the compiler moves
     # them between registers on every filter-row iteration
@@ -61,10 +63,11 @@ def _units():
 
 
 _REMARK = re.compile(r"remark:\s+(Function Name|VGPRs|AGPRs|Occupancy \[waves/SIMD\]|"
-                     r"VGPRs Spill|SGPRs Spill|LDS Size \[bytes/block\]):\s+(\S+)")
+                     r"VGPRs Spill|SGPRs Spill|LDS Size \[bytes/block\]|"
+                     r"ScratchSize \[bytes/lane\]):\s+(\S+)")
 _FIELDS = {"VGPRs": "vgprs", "AGPRs": "agprs", "Occupancy [waves/SIMD]": "waves_per_simd",
            "VGPRs Spill": "vgpr_spill", "SGPRs Spill": "sgpr_spill",
-           "LDS Size [bytes/block]": "lds_static"}
+           "LDS Size [bytes/block]": "lds_static", "ScratchSize [bytes/lane]": "scratch"}
 
 
 def _resource_remarks(text):

@@ -85,7 +85,9 @@ hipError_t launch_fwd_type(const Plan& pl, const void* in, const void* filt, flo
     }
     switch (pl.dt) {
 #define DWC_CASE(D) \
-  case D: return launch_fwd_direct_dt##D(a.FW, a.SW, pl.tmw, pl.flip, a, pl.blocks, s);
+  case D:                                                                            \
+    return pl.kfw == a.FW ? launch_fwd_direct_dt##D(pl.kfw, a.SW, pl.tmw, pl.flip, a, pl.blocks, s) \
+                          : launch_fwd_direct_pad_dt##D(pl.kfw, a.SW, pl.tmw, pl.flip, a, pl.blocks, s);
       DWC_DT_LIST(DWC_CASE)
 #undef DWC_CASE
     }
@@ -184,7 +186,7 @@ int run_bwd_filter(const dwc_problem* p, const Plan& pl, const void* x, const vo
     } else {
       switch (pl.dt) {
 #define DWC_CASE(D) \
-  case D: e = launch_wgrad_direct_dt##D(a.FW, a.SW, pl.tj, a, pl.blocks, s); break;
+  case D: e = launch_wgrad_direct_dt##D(pl.kfw, a.SW, pl.tj, a, pl.blocks, s); break;
         DWC_DT_LIST(DWC_CASE)
 #undef DWC_CASE
         default: e = hipErrorInvalidValue; break;
@@ -296,7 +298,7 @@ int dwc_fwd_fused(const dwc_problem* p, const void* x, const float* scale, const
   int st = make_plan(&d, DWC_OP_FWD, &pl, &err);
   if (st == DWC_OK && (pl.kind != PLAN_DIRECT || p->fw > kPrologueMaxFw)) st = DWC_ERR_UNSUPPORTED;
   if (st == DWC_ERR_UNSUPPORTED)
-    err = "the fused prologue needs an odd filter width up to 9 and stride 1 or 2 "
+    err = "the fused prologue needs a filter width up to 9 and stride 1 or 2 "
           "(the direct vector kernels)";
   if (st == DWC_OK) st = check_pointers(&d, pl, x, w, y, nullptr, 0, &err);
   if (st == DWC_OK) st = check_prologue(&d, pl, y, scale, shift, &err);

@@ -18,9 +18,22 @@ constexpr int kSweepAutoMaxF = 7;
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlockThreads = 64 * kWavesPerBlock;
 
-// Filter widths with register-window (direct) kernels; other widths run the
-// generic kernels.  X-macro: DWC_DIRECT_FW_LIST(M) expands M(F) per width.
+// Filter widths with register-window (direct) kernels; a width between two
+// of them runs on the next wider one, widths past 31 on the generic kernels.
+// X-macro: DWC_DIRECT_FW_LIST(M) expands M(F) per width.
 #define DWC_DIRECT_FW_LIST(M) M(3) M(5) M(7) M(9) M(13) M(17) M(21) M(27) M(31)
+
+// The widest listed width below f (0: none): every filter that runs on the
+// f-wide body is wider than this, so its first direct_fw_below(f) + 1 taps
+// are real ones.
+constexpr int direct_fw_below(int f) {
+  int b = 0;
+#define DWC_BELOW(F) \
+  if (F < f) b = F;
+  DWC_DIRECT_FW_LIST(DWC_BELOW)
+#undef DWC_BELOW
+  return b;
+}
 
 // Output columns per lane (forward-type kernel) and per strip (filter-gradient
 // kernel) that have instantiations.

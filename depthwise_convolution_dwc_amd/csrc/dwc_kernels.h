@@ -104,15 +104,20 @@ __device__ __forceinline__ void apply_prologue(float (&v)[SPAN], int row, int ro
 // width-first reuse of §3.3, run as 1-D filters along the width accumulated
 // over filter rows).  All loop bounds are compile-time, so every accumulator
 // and tap is a register.  FLIP reads the filter turned by 180 degrees, which
-// makes this the stride-1 data gradient (§5.1).
+// makes this the stride-1 data gradient (§5.1).  PAD runs a filter a.FW < FW
+// columns wide on the FW-wide body: its taps a.FW .. FW-1 take no products
+// (a zero tap times an inf input would give NaN).  Taps that may be past
+// a.FW keep the accumulator by a select, not a branch, so the whole row body
+// stays one block that the compiler schedules loads across.
 // ---------------------------------------------------------------------------
-template <int DT, int FW, int S, int TMW, bool FLIP, bool PRO = false>
+template <int DT, int FW, int S, int TMW, bool FLIP, bool PRO = false, bool PAD = false>
 __global__ __launch_bounds__(kBlockThreads) void fwd_rows(FwdArgs a) {
   constexpr int EB = Elem<DT>::bytes;
   constexpr int TR = kFwdRows;
   constexpr int FHC = filter_row_chunk(FW);
   constexpr int SPAN = (TMW - 1) * S + FW;
   constexpr int MSPAN = (TR - 1) * S + FHC;
+  constexpr int FWLO = PAD ? direct_fw_below(FW) + 1 : FW;  // taps always real
   const int wave = uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int item = xcd_logical_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wave;
@@ -136,7 +141,8 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_rows(FwdArgs a) {
       pb = a.pro.shift[c];
     }
   }
-  const auto wrs = make_rsrc(a.filt, (uint32_t)(a.FH * FW) * Cb);
+  const int fwn = PAD ? a.FW : FW;  // the filter's real width
+  const auto wrs = make_rsrc(a.filt, (uint32_t)(a.FH * fwn) * Cb);
   const int oh0 = th * TR, ow0 = tw * TMW;
   const int ih_base = oh0 * S - a.PH;
   // Odd row tiles walk their input rows bottom-up, so two neighbouring
@@ -169,8 +175,9 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_rows(FwdArgs a) {
       const int fhe = FLIP ? a.FH - 1 - fh : fh;
 #pragma unroll
       for (int fw = 0; fw < FW; ++fw) {
-        const int fwe = FLIP ? FW - 1 - fw : fw;
-        wv[k][fw] = ld<DT>(ok ? wrs : zero, voff, ok ? (uint32_t)(fhe * FW + fwe) * Cb : 0u);
+        const bool okw = ok && (!PAD || fw < fwn);
+        const int fwe = FLIP ? fwn - 1 - fw : fw;
+        wv[k][fw] = ld<DT>(okw ? wrs : zero, voff, okw ? (uint32_t)(fhe * fwn + fwe) * Cb : 0u);
       }
     }
 #pragma unroll
@@ -185,9 +192,19 @@ __global__ __launch_bounds__(kBlockThreads) void fwd_rows(FwdArgs a) {
         const int k = m - r * S;
         if (k < 0 || k >= FHC || k < klo || k >= khi) continue;
 #pragma unroll
-        for (int fw = 0; fw < FW; ++fw)
+        for (int fw = 0; fw < FW; ++fw) {
+          if (fw < FWLO) {
 #pragma unroll
-          for (int q = 0; q < TMW; ++q) acc[r][q] = fmaf(xv[q * S + fw], wv[k][fw], acc[r][q]);
+            for (int q = 0; q < TMW; ++q) acc[r][q] = fmaf(xv[q * S + fw], wv[k][fw], acc[r][q]);
+          } else {
+            const bool real = fw < fwn;
+#pragma unroll
+            for (int q = 0; q < TMW; ++q) {
+              const float v = fmaf(xv[q * S + fw], wv[k][fw], acc[r][q]);
+              acc[r][q] = real ? v : acc[r][q];
+            }
+          }
+        }
       }
     }
   }
@@ -294,7 +311,7 @@ __global__ __launch_bounds__(kBlockThreads) void dgrad_phase(DgradPhaseArgs a) {
         if (k < 0 || k >= KC || k0 + k >= kh) continue;
 #pragma unroll
         for (int l = 0; l < KM; ++l) {
-          if (l >= kw) break;
+          if (l >= kw) continue;  // not break: a loop exit leaves acc in scratch memory
 #pragma unroll
           for (int q = 0; q < TMW; ++q)
             acc[r][q] = fmaf(yv[q - l + KM - 1], wv[k][l], acc[r][q]);
@@ -331,7 +348,9 @@ __global__ __launch_bounds__(kBlockThreads) void dgrad_phase(DgradPhaseArgs a) {
 // row) pair that reads it; along the width each input pixel meets every tap
 // whose window covers it (width-first reuse, §3.3).  The 4 waves add their
 // sums through LDS in a fixed order and one partial per slice is written;
-// reduce_partials adds the slices in slice order.  Deterministic.
+// reduce_partials adds the slices in slice order.  Deterministic.  A filter
+// a.FW < FW columns wide runs on the FW-wide body; its taps a.FW .. FW-1 are
+// summed but not written, and the partials have a.FW taps per filter row.
 // ---------------------------------------------------------------------------
 template <int DT, int FW, int S, int TJ>
 __global__ __launch_bounds__(kBlockThreads) void wgrad_rows(WgradArgs a) {
@@ -431,14 +450,15 @@ __global__ __launch_bounds__(kBlockThreads) void wgrad_rows(WgradArgs a) {
   }
   __syncthreads();
   if (wave == 0 && c < a.C) {
-    float* ws = a.ws + (size_t)z * a.FH * FW * a.C + c;
+    float* ws = a.ws + (size_t)z * a.FH * a.FW * a.C + c;
 #pragma unroll
     for (int k = 0; k < TFH; ++k) {
       const int fh = fh0 + k;
       if (fh >= a.FH) break;
 #pragma unroll
-      for (int fw = 0; fw < FW; ++fw)
-        ws[((size_t)fh * FW + fw) * a.C] = acc[k][fw] + red[0][k * FW + fw][lane];
+      for (int fw = 0; fw < FW; ++fw)  // (a guard, not a break: a loop exit
+                                       // would leave acc in scratch memory)
+        if (fw < a.FW) ws[((size_t)fh * a.FW + fw) * a.C] = acc[k][fw] + red[0][k * FW + fw][lane];
     }
   }
 }

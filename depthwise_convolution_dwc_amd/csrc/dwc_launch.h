@@ -12,7 +12,9 @@ namespace dwc {
 #define DWC_DT_LIST(X) X(0) X(1) X(2) X(3) X(4)
 
 // Per operand dtype D:
-//  * forward-type direct kernel (s: stride; flip: the stride-1 data gradient);
+//  * forward-type direct kernel (fw: the instantiated width; s: stride; flip:
+//    the stride-1 data gradient); the _pad_ form for a filter narrower than
+//    fw;
 //  * strided data gradient by output phase (km: padded sub-filter size, one
 //    of DWC_PHASE_KM_LIST);
 //  * filter-gradient direct kernel;
@@ -20,6 +22,8 @@ namespace dwc {
 #define DWC_DECL_DT(D)                                                                    \
   hipError_t launch_fwd_direct_dt##D(int fw, int s, int tmw, bool flip, const FwdArgs& a, \
                                      int blocks, hipStream_t st);                         \
+  hipError_t launch_fwd_direct_pad_dt##D(int fw, int s, int tmw, bool flip,               \
+                                         const FwdArgs& a, int blocks, hipStream_t st);   \
   hipError_t launch_dgrad_phase_dt##D(int km, const DgradPhaseArgs& a, int blocks,        \
                                       hipStream_t s);                                     \
   hipError_t launch_wgrad_direct_dt##D(int fw, int s, int tj, const WgradArgs& a,         \

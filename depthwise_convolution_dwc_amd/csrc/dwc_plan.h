@@ -21,6 +21,9 @@ struct Plan {
   int64_t oh = 0, ow = 0;
   bool empty = false;  // n == 0
 
+  // direct kernels: the instantiated filter width they run on (FW itself,
+  // else the next wider one, whose taps past FW are skipped)
+  int kfw = 0;
   // forward-type direct kernel (forward, stride-1 data gradient)
   int tmw = 0;
   bool flip = false;

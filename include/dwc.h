@@ -195,7 +195,7 @@ int dwc_fwd(const dwc_problem* p, const void* x, const void* w, void* y,
  *                  may be NULL when n == 0)
  *   act : a dwc_act
  * Runs the register-window vector kernels (the pages fuse on their CUDA-core
- * kernels, for small filters): odd filter widths up to 9, stride 1 or 2,
+ * kernels, for small filters): filter widths up to 9, stride 1 or 2,
  * any dtype; algo AUTO or DIRECT.  Otherwise DWC_ERR_UNSUPPORTED.  y must
  * not overlap x, w, scale or shift. */
 int dwc_fwd_fused(const dwc_problem* p, const void* x, const float* scale,

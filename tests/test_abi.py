@@ -2,6 +2,7 @@
 include/dwc.h declares, and rejects bad calls before touching the device."""
 
 import ctypes
+import json
 import os
 import re
 
@@ -85,10 +86,11 @@ def test_fp32_output_required():
 
 
 def test_direct_unavailable_is_unsupported():
-    # width 4 has no register-window kernel; forcing it is an error, auto falls back
-    p = dwc.problem(1, 8, 8, 4, 4, 4, 1, 1, algo="direct")
+    # width 33 is past every register-window kernel; forcing it is an error,
+    # auto falls back
+    p = dwc.problem(1, 40, 40, 4, 33, 33, 1, 1, algo="direct")
     assert dwc.check(p, 0) == 2
-    p = dwc.problem(1, 8, 8, 4, 4, 4, 1, 1, algo="auto")
+    p = dwc.problem(1, 40, 40, 4, 33, 33, 1, 1, algo="auto")
     assert dwc.check(p, 0) == 0
     assert "generic" in dwc.plan_describe(p, 0)
     # stride-2 data gradient runs the phase kernel, or the gather kernel
@@ -390,7 +392,7 @@ def test_fwd_fused_rejections_before_any_launch():
     for algo in ("mfma", "generic"):
         q = dwc.problem(2, 8, 8, 64, 3, 3, 1, 1, algo=algo)
         assert L.dwc_fwd_fused(P(q), X, SC, SH, 1, W, Y, None) == 2
-    for fh, fw, pad in ((11, 11, 5), (4, 4, 1), (3, 3, 1)):
+    for fh, fw, pad in ((11, 11, 5), (10, 10, 4), (3, 3, 1)):
         q = dwc.problem(2, 16, 16, 64, fh, fw, 3 if fw == 3 else 1, pad)
         assert L.dwc_fwd_fused(P(q), X, SC, SH, 1, W, Y, None) == 2, (fh, fw)
         assert "fused prologue" in dwc.last_error()
@@ -399,8 +401,11 @@ def test_fwd_fused_rejections_before_any_launch():
     assert L.dwc_fwd_fused(P(p), X, Y + 64, SH, 1, W, Y, None) == 5     # scale inside y
     empty = dwc.problem(0, 8, 8, 64, 3, 3, 1, 1)
     assert L.dwc_fwd_fused(P(empty), None, None, None, 3, None, None, None) == 0
-    # a 9-wide filter at stride 2 and a tall 31 x 9 filter are accepted
-    for q in (dwc.problem(1, 16, 16, 64, 9, 9, 2, 4), dwc.problem(1, 40, 16, 64, 31, 9, 1, 4)):
+    # a 9-wide filter at stride 2, a tall 31 x 9 filter and even or 1-wide
+    # filters (on the next wider body) are accepted
+    for q in (dwc.problem(1, 16, 16, 64, 9, 9, 2, 4), dwc.problem(1, 40, 16, 64, 31, 9, 1, 4),
+              dwc.problem(1, 16, 16, 64, 4, 4, 1, 1), dwc.problem(1, 16, 16, 64, 1, 1, 2, 0),
+              dwc.problem(1, 16, 16, 64, 8, 8, 1, 3)):
         assert L.dwc_fwd_fused(P(q), X, SC + 2, SH, 0, W, Y, None) == 3  # reaches the checks
 
 
@@ -627,3 +632,38 @@ def test_batch_kernel_one_round():
         d = dwc.plan_describe(dwc.problem(64, 28, 28, 256, f, f, 1, f // 2, dtype=dwc.BF16,
                                           algo="mfma"), 0)
         assert (" batch=1 " in d) == want, (f, d)
+
+
+def test_padded_direct_widths():
+    """Filter widths between the instantiated direct widths run on the next
+    wider body (its extra taps skipped): forward, stride-1 data gradient and
+    filter gradient take the direct plan with kfw the narrowest listed width
+    >= FW, for fp32 operands at stride 1 and 2 (no matrix-core kernel: C is
+    not a multiple of 16); widths past 31 stay on the generic kernels."""
+    listed = (3, 5, 7, 9, 13, 17, 21, 27, 31)
+    for fw in range(1, 32):
+        kfw = min(k for k in listed if k >= fw)
+        for s in (1, 2):
+            p = dwc.problem(2, 40, 40, 24, 6, fw, s, (2, fw // 2), algo="direct")
+            for op in ((0, 1, 2) if s == 1 else (0, 2)):
+                d = dwc.plan_describe(p, op)
+                g = dict(kv.split("=") for kv in d.split()[2:] if "=" in kv)
+                assert d.split()[1] == "direct" and g["fw"] == str(fw), d
+                assert g["kfw"] == str(kfw), d
+        a = dwc.problem(2, 40, 40, 24, 6, fw, 1, (2, fw // 2))
+        assert "generic" not in dwc.plan_describe(a, 2)
+    p = dwc.problem(2, 40, 40, 24, 5, 32, 1, (2, 16))
+    assert all(dwc.plan_describe(p, op).split()[1] == "generic" for op in (0, 2))
+
+
+def test_no_kernel_uses_scratch():
+    """Every kernel keeps its arrays in registers: the compiler's resource
+    remarks (recorded by the build) show no per-lane scratch memory, which
+    an array indexed past a loop exit or by a runtime value would need."""
+    path = os.path.join(os.path.dirname(dwc.__file__), "kernel_resources.json")
+    if not os.path.exists(path):
+        pytest.skip("library not built")
+    with open(path) as f:
+        res = json.load(f)
+    assert res and all("scratch" in v for v in res.values())
+    assert {k: v["scratch"] for k, v in res.items() if v["scratch"]} == {}

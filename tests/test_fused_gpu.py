@@ -29,6 +29,9 @@ FUSED_SHAPES = [
     (1, 12, 15, 64, 5, 3, 1, (2, 1)),  # row tiles, non-square filter
     (1, 30, 11, 64, 13, 9, 1, (6, 4)), # row tiles, filter rows in chunks
     (1, 9, 9, 8, 9, 9, 2, 0),          # no padding, C < 64
+    (2, 13, 14, 64, 4, 4, 1, (1, 2)),  # even width on the 5-wide body
+    (1, 14, 17, 40, 3, 8, 2, (1, 3)),  # 8 on the 9-wide body, stride 2
+    (1, 10, 12, 64, 1, 1, 1, 0),       # 1x1 on the 3-wide body
 ]
 
 

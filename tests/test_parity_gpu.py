@@ -47,6 +47,14 @@ SHAPES = [
     # negative (cropping) padding F-1-pad
     (1, 10, 10, 16, 3, 3, 1, 4),
     (2, 12, 12, 64, 13, 13, 1, 14),
+    # widths between the instantiated direct widths: the next wider body
+    # with its extra taps skipped (11 on 13, 2 on 3, 15 on 17, 29 on 31,
+    # 19 on 21), at stride 1 (all three operations) and 2
+    (2, 13, 15, 64, 11, 11, 1, 5),
+    (2, 9, 21, 24, 3, 2, 1, (1, 0)),
+    (1, 12, 18, 40, 6, 15, 2, (2, 7)),
+    (1, 10, 40, 70, 5, 29, 1, (2, 14)),
+    (1, 6, 30, 16, 1, 19, 1, (0, 9)),
 ]
 
 
@@ -394,6 +402,8 @@ NONFINITE_SHAPES = [
     (2, 12, 13, 40, 5, 3, 1, (2, 1)),  # register-window, non-square
     (2, 15, 15, 64, 7, 7, 2, 3),       # stride 2: phase data gradient
     (1, 11, 13, 40, 3, 3, 3, 1),       # stride 3: generic kernels
+    (2, 14, 16, 40, 5, 11, 1, (2, 5)), # width 11 on the 13-wide body
+    (2, 15, 15, 64, 4, 6, 2, (1, 2)),  # width 6 on the 7-wide body, stride 2
 ]
 
 
