@@ -15,6 +15,9 @@ constexpr int kWaveChannels = 64;
 // AUTO: 16-bit and fp8 operands stay on the sweep kernels up to this
 // square filter size (stride 1); the packed matrix-core kernels from above
 constexpr int kSweepAutoMaxF = 7;
+// ... and on the vector kernels for any filter of at most this many rows
+// and columns (stride 1)
+constexpr int kVecAutoMaxF = 5;
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlockThreads = 64 * kWavesPerBlock;
 
@@ -285,6 +288,8 @@ constexpr int kF32mCb = 16;         // channels per wave (the 16 blocks)
 constexpr int kF32mRows = 4;        // output rows per wave (the matrix rows)
 constexpr int kF32mMaxWaves = 8;    // waves per workgroup
 constexpr int kF32mMinFh = 13;      // AUTO: from this many filter rows and columns
+constexpr int kF32mMinFPad = 10;    // ... and at any output width for filters from
+                                    // this size whose columns stop short of 13
 constexpr int kF32mMinOw = 24;      // ... on outputs at least this wide
 constexpr int kF32mFillWaves = 2048;  // 8 waves per CU of the MI355X
 constexpr int kF32mStageBatch = 8;  // 16-byte band loads in flight per thread
@@ -340,7 +345,7 @@ struct MfmaF32Args {
 constexpr int kWf32Cb = 16;          // channels per workgroup (the 16 blocks)
 constexpr int kWf32MaxWaves = 8;     // FH <= 32
 constexpr int kWf32StageItems = 2;   // 16-byte X staging items per thread, at most
-constexpr int kWf32MinF = 12;        // AUTO: from this filter size (rows and columns)
+constexpr int kWf32MinF = 10;        // AUTO: from this filter size (rows and columns)
 struct WgradF32Args {
   const void* x;     // N x IH x IW x C fp32
   const void* dy;    // N x OH x OW x C fp32

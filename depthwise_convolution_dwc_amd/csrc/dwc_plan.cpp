@@ -425,9 +425,13 @@ static bool plan_mfma_f32(const FwdArgs& f, int dt, bool flip, bool forced, Plan
   //   4 rows, the whole width) has fewer than 8 waves per CU: 3-4x faster
   //   (N=8 14x14 C=512 31x31: 21 against 79 us; N=16 C=256 21x21: 17
   //   against 50 us).
+  // - filters of 10 to 12 columns (and at least 10 rows) at any width: the
+  //   vector kernels run them on their 13-wide body (11x11: 1.0-1.3x at
+  //   widths 56, 28, 14 and 7).
   const bool vec_few = f.OW <= 16 && (int64_t)f.N * ((f.C + 63) / 64) * rg < kF32mFillWaves;
-  const bool pick = f.FH >= kF32mMinFh && f.FW >= kF32mMinFh &&
-                    (f.OW >= kF32mMinOw || (f.OW <= 8 && f.FW >= 27) || img_auto || vec_few);
+  const bool pick = (f.FH >= kF32mMinFh && f.FW >= kF32mMinFh &&
+                     (f.OW >= kF32mMinOw || (f.OW <= 8 && f.FW >= 27) || img_auto || vec_few)) ||
+                    (f.FH >= kF32mMinFPad && f.FW >= kF32mMinFPad && f.FW < kF32mMinFh);
   const char* env = getenv("DWC_MFMA_F32");
   if (!forced && (env ? atoi(env) == 0 : !pick)) return false;
   // the images kernel addresses 4 images of X from one buffer resource
@@ -676,7 +680,8 @@ static bool plan_wgrad_mfma_f32(const dwc_problem* p, int64_t oh, int64_t ow, bo
   // outputs at most 8 wide only the largest filters (MI355X, N=64 stages:
   // 1.2-1.3x the vector kernels at 27x27 and 31x31 on 56, 28 and 14 wide
   // outputs, 0.7-0.9x at 17x17 and 21x21, whose tiles are 72-77% real taps;
-  // 1.00-1.06x at 13x13 (66%); at width 7, 1.10x at 31x31, 0.91x at 27x27).
+  // 1.00-1.06x at 13x13 (66%); at width 7, 1.10x at 31x31, 0.91x at 27x27;
+  // 11x11 (76%, on a 13-wide vector body): 1.2-1.6x at widths 56 to 7).
   const int64_t tiles = (int64_t)((p->fh + 3) / 4) * ((p->fw + 3) / 4);
   const int fill = p->fw <= 16 ? 64 : 85;
   const bool pick = p->fh >= kWf32MinF && p->fw >= kWf32MinF &&
@@ -890,6 +895,16 @@ int make_plan(const dwc_problem* p, int op, Plan* pl, std::string* err) {
   // C=1024 3x3 forward 12 against 47 us; from 9x9 on the matrix cores win)
   const bool sweep_auto = p->algo == DWC_ALGO_AUTO && sweep_ok && direct_fw(p->fw) &&
                           p->fw <= kSweepAutoMaxF && p->in_dtype != DT_F32;
+  // ... and the vector kernels for the other filters up to 5x5 (bf16, N=64:
+  // forward 1x1 26 against 35 us at 56x56 C=128, 3x5 11.0 against 18.5 us
+  // at 14x14 C=512; filter gradient 3x5 23.6 against 27.5 us at 28x28
+  // C=256; e4m3 forward 1x1 25 against 54 us at 56x56).  fp8 filter
+  // gradients only up to 5 taps: from 3x5 on its packed kernel is ahead.
+  const bool vec_auto =
+      p->algo == DWC_ALGO_AUTO && p->in_dtype != DT_F32 && can_direct && !sweep_ok &&
+      p->fh <= kVecAutoMaxF && p->fw <= kVecAutoMaxF &&
+      (op != DWC_OP_BWD_FILTER || elem_bytes(p->in_dtype) == 2 || p->fh * p->fw <= 5);
+  const bool vector_auto = sweep_auto || vec_auto;
   const bool hybrid = p->algo == DWC_ALGO_HYBRID;
   if (hybrid && (op != DWC_OP_BWD_FILTER || dt != DT_F16 || !sweep_ok))
     return fail(err, DWC_ERR_UNSUPPORTED,
@@ -915,7 +930,7 @@ int make_plan(const dwc_problem* p, int op, Plan* pl, std::string* err) {
     f.PW = bwd ? p->fw - 1 - p->pad_w : p->pad_w;
     // Packed MFMA for half-precision operands (the stride-1 data gradient
     // too: stride 1 is part of the kernel's conditions).
-    if ((p->algo == DWC_ALGO_AUTO && !sweep_auto) || p->algo == DWC_ALGO_MFMA) {
+    if ((p->algo == DWC_ALGO_AUTO && !vector_auto) || p->algo == DWC_ALGO_MFMA) {
       if (plan_mfma_h4(f, dt, bwd, &q) || plan_mfma_batch(f, dt, bwd, &q) || plan_mfma(f, dt, bwd, &q) ||
           plan_mfma8(f, dt, bwd, &q) ||
           plan_mfma_f32(f, dt, bwd, p->algo == DWC_ALGO_MFMA, &q)) {
@@ -1009,7 +1024,7 @@ int make_plan(const dwc_problem* p, int op, Plan* pl, std::string* err) {
   } else {
     if (p->wgrad_split > 0 && p->n * oh > 0 && p->wgrad_split > p->n * oh)
       return fail(err, DWC_ERR_BAD_PARAM, "wgrad_split larger than N*OH");
-    if ((p->algo == DWC_ALGO_AUTO && !sweep_auto) || p->algo == DWC_ALGO_MFMA) {
+    if ((p->algo == DWC_ALGO_AUTO && !vector_auto) || p->algo == DWC_ALGO_MFMA) {
       if (plan_wgrad_mfma(p, oh, ow, &q) || plan_wgrad_mfma8(p, oh, ow, &q) ||
           plan_wgrad_mfma_f32(p, oh, ow, p->algo == DWC_ALGO_MFMA, &q)) {
         const int64_t m = (int64_t)p->fh * p->fw * p->c;

@@ -93,8 +93,10 @@ typedef enum {
                              per instruction; output rows or images by
                              output columns, filter columns by rows).  AUTO takes them for the
                              problems where they beat the vector kernels
-                             (filters from 9x9 on, or outside the sweeps'
-                             square 3x3-9x9 stride-1 set).  Operands must be finite:
+                             (16-bit and fp8: filters from 9x9 on, and
+                             those outside the sweeps' square 3x3-7x7 set
+                             with more than 5 rows or columns; fp32: from
+                             10x10 on, by output width and batch).  Operands must be finite:
                              the packing multiplies staged elements by
                              structural zeros as well, so an inf or NaN
                              operand turns outputs that share an

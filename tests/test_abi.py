@@ -667,3 +667,29 @@ def test_no_kernel_uses_scratch():
         res = json.load(f)
     assert res and all("scratch" in v for v in res.values())
     assert {k: v["scratch"] for k, v in res.items() if v["scratch"]} == {}
+
+
+def test_small_and_mid_filter_auto_rules():
+    """AUTO (measured on MI355X): 16-bit and fp8 filters up to 5x5 stay on
+    the vector kernels (fp8 filter gradients only up to 5 taps); wider ones
+    take the packed matrix-core kernels; fp32 filters from 10x10 whose
+    columns stop short of 13 take the fp32 matrix-core kernels at any width
+    (the vector kernels would run them on their 13-wide body), 9x9 stays on
+    the sweeps."""
+    def fam(dt, fh, fw, op, n=64, h=28, c=256):
+        p = dwc.problem(n, h, h, c, fh, fw, 1, (fh // 2, fw // 2), dtype=dt)
+        return dwc.plan_describe(p, op).split()[1]
+    for dt in (dwc.BF16, dwc.F16, dwc.FP8_E4M3):
+        for fh, fw in ((1, 1), (3, 5), (5, 1), (2, 2), (4, 4)):
+            for op in (0, 1):
+                assert fam(dt, fh, fw, op) == "direct", (dt, fh, fw, op)
+        for fh, fw in ((1, 7), (7, 3), (6, 6)):
+            assert fam(dt, fh, fw, 0) == "mfma", (dt, fh, fw)
+    for fh, fw in ((1, 1), (3, 5), (4, 4)):
+        assert fam(dwc.BF16, fh, fw, 2) == "direct"
+    assert fam(dwc.FP8_E4M3, 1, 5, 2) == "direct"
+    assert fam(dwc.FP8_E4M3, 3, 5, 2) == "mfma"
+    for h, c in ((56, 128), (28, 256), (14, 512), (7, 1024)):
+        for op in (0, 1, 2):
+            assert fam(dwc.F32, 11, 11, op, h=h, c=c) == "mfma", (h, op)
+            assert fam(dwc.F32, 9, 9, op, h=h, c=c) == "sweep", (h, op)
