@@ -342,7 +342,7 @@ def kernels_of(dwc, s, op, dtype="f32", algo="auto"):
         if kv.get("h4") == "1":  # 16-bit 4x4x4 kernel
             k = f"fwd_mfma_h4n<{dt}, {kv['fwi']}, {kv['t']}, {flip}>"
         elif kv.get("f32") == "1":  # fp32 matrix-core kernels
-            k = (f"wgrad_mfma_f32<{kv['tw']}, {kv['nb']}>" if op == "bwd_filter" else
+            k = (f"wgrad_mfma_f32<{dt}, {kv['tw']}, {kv['nb']}>" if op == "bwd_filter" else
                  f"fwd_mfma_f32{'n' if kv.get('img') == '1' else ''}<{kv['fwi']}, {kv['t']}, "
                  f"{flip}>")
         elif op == "bwd_filter":

@@ -147,7 +147,7 @@ int run_bwd_filter(const dwc_problem* p, const Plan& pl, const void* x, const vo
     w.x = x;
     w.dy = dy;
     w.ws = (float*)workspace;
-    e = launch_wgrad_mfma_f32(pl.wf32_tw, pl.wf32_nb, w, s);
+    e = launch_wgrad_mfma_f32(pl.dt, pl.wf32_tw, pl.wf32_nb, w, s);
     if (e != hipSuccess) return hip_fail(e, "dwc_bwd_filter launch");
     e = launch_reduce(
         ReduceArgs{(const float*)workspace, (float*)dw, m, pl.z, kWf32Cb, w.C, w.FH * w.FW}, s);

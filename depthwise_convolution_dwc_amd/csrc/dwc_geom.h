@@ -347,8 +347,8 @@ constexpr int kWf32MaxWaves = 8;     // FH <= 32
 constexpr int kWf32StageItems = 2;   // 16-byte X staging items per thread, at most
 constexpr int kWf32MinF = 10;        // AUTO: from this filter size (rows and columns)
 struct WgradF32Args {
-  const void* x;     // N x IH x IW x C fp32
-  const void* dy;    // N x OH x OW x C fp32
+  const void* x;     // N x IH x IW x C fp32, bf16 or fp16
+  const void* dy;    // N x OH x OW x C, the same type
   float* ws;         // (Z * cg) x cblk x (FH * FW) x 16 partial sums
   int N, IH, IW, C, OH, OW;
   int FH, FW, PH, PW;

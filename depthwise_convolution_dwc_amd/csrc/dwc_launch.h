@@ -63,7 +63,7 @@ hipError_t launch_fwd_mfma_f32(int fwi, int t, bool img, bool flip, const MfmaF3
 // 32, C % 16 == 0): tw = ceil(FW / 4) column tiles, nb 4-column output
 // groups per wave (DWC_WF32_NB_LIST).  Writes channel-blocked slice
 // partials (reduce with cb = kWf32Cb).
-hipError_t launch_wgrad_mfma_f32(int tw, int nb, const WgradF32Args& a, hipStream_t s);
+hipError_t launch_wgrad_mfma_f32(int dt, int tw, int nb, const WgradF32Args& a, hipStream_t s);
 
 // Packed fp8 MFMA forward-type kernel (e4m3 / e5m2 operands, stride 1,
 // 16x16x128 MFMAs over four filter rows each): nf 16-tap fragments per

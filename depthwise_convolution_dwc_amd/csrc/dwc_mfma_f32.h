@@ -417,9 +417,30 @@ __global__ __launch_bounds__(64 * kF32mMaxWaves) void fwd_mfma_f32n(MfmaF32Args 
   }
 }
 
-// ---- filter gradient (layout and mapping: WgradF32Args)
-template <int TW, int NB>
+// Four consecutive 16-bit operand elements (bf16 or fp16, two per dword) as
+// fp32: exact.
+template <int DT>
+__device__ __forceinline__ f32m_x4 wf32_widen4(uint32_t lo, uint32_t hi) {
+  if constexpr (DT == DT_BF16) {
+    return f32m_x4{__uint_as_float(lo << 16), __uint_as_float(lo & 0xffff0000u),
+                   __uint_as_float(hi << 16), __uint_as_float(hi & 0xffff0000u)};
+  } else {
+    return f32m_x4{(float)__builtin_bit_cast(_Float16, (unsigned short)(lo & 0xffffu)),
+                   (float)__builtin_bit_cast(_Float16, (unsigned short)(lo >> 16)),
+                   (float)__builtin_bit_cast(_Float16, (unsigned short)(hi & 0xffffu)),
+                   (float)__builtin_bit_cast(_Float16, (unsigned short)(hi >> 16))};
+  }
+}
+
+// ---- filter gradient (layout and mapping: WgradF32Args).  DT: the operand
+// type of x and dY; 16-bit operands are widened to fp32 as they are loaded
+// (X on its way to the LDS, dY into the register window), so the matrix
+// cores see the same fp32 values the oracle multiplies.
+template <int DT, int TW, int NB>
 __global__ __launch_bounds__(64 * kWf32MaxWaves, 4) void wgrad_mfma_f32(WgradF32Args a) {
+  constexpr int EB = DT == DT_F32 ? 4 : 2;  // operand bytes
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  using XRaw = std::conditional_t<DT == DT_F32, f32m_x4, u32x2>;
   extern __shared__ __align__(16) unsigned char lds[];
   constexpr int OWW = 4 * NB;             // output columns per wave
   constexpr int NU = OWW + 4 * TW - 3;    // 4-column X windows u
@@ -443,29 +464,37 @@ __global__ __launch_bounds__(64 * kWf32MaxWaves, 4) void wgrad_mfma_f32(WgradF32
   const int npairs = a.N * IH;
   const int p0 = z * a.rps;
   const int p1 = min(p0 + a.rps, npairs);
-  const uint32_t xrow = (uint32_t)IW * (uint32_t)C * 4u;
+  const uint32_t xrow = (uint32_t)IW * (uint32_t)C * EB;
 
   // ---- X staging: item e = (pixel e / 4, channels 4 (e % 4) .. + 3) of the
   // row; pixel p is input column ow0 - PW + p
   const int items = XP * (kWf32Cb / 4);
-  f32m_x4 xv[kWf32StageItems];
+  XRaw xv[kWf32StageItems];
   auto x_fetch = [&](int n, int r) {
-    const auto rs = make_rsrc(reinterpret_cast<const float*>(a.x) + ((size_t)n * IH + r) * IW * C,
+    const auto rs = make_rsrc(reinterpret_cast<const char*>(a.x) +
+                                  ((size_t)n * IH + r) * IW * C * EB,
                               xrow);
 #pragma unroll
     for (int k = 0; k < kWf32StageItems; ++k) {
       const int e = tid + k * nthr;
       const int col = ow0 - PW + (e >> 2);
-      const uint32_t off = e < items ? (uint32_t)((col * C + c0 + (e & 3) * 4) * 4) : kOOB;
-      xv[k] = __builtin_bit_cast(f32m_x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0));
+      const uint32_t off = e < items ? (uint32_t)((col * C + c0 + (e & 3) * 4) * EB) : kOOB;
+      if constexpr (DT == DT_F32)
+        xv[k] = __builtin_bit_cast(f32m_x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0));
+      else
+        xv[k] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, (int)off, 0, 0));
     }
   };
   auto x_commit = [&](int buf) {
 #pragma unroll
     for (int k = 0; k < kWf32StageItems; ++k) {
       const int e = tid + k * nthr;
-      if (e < items)
-        *reinterpret_cast<f32m_x4*>(xb + (buf * XP + (e >> 2)) * kWf32Cb + (e & 3) * 4) = xv[k];
+      if (e < items) {
+        f32m_x4 v;
+        if constexpr (DT == DT_F32) v = xv[k];
+        else v = wf32_widen4<DT>(xv[k].x, xv[k].y);
+        *reinterpret_cast<f32m_x4*>(xb + (buf * XP + (e >> 2)) * kWf32Cb + (e & 3) * 4) = v;
+      }
     }
   };
 
@@ -476,18 +505,24 @@ __global__ __launch_bounds__(64 * kWf32MaxWaves, 4) void wgrad_mfma_f32(WgradF32
   // Each load below has its own buffer resource (scalar registers) starting
   // at its column, so that all of them share one lane offset register; the
   // resource's range still ends at the row's (image's) end.
-  const float* dyc = reinterpret_cast<const float*>(a.dy) + (size_t)ow0 * C;  // column ow0
+  const char* dyc = reinterpret_cast<const char*>(a.dy) + (size_t)ow0 * C * EB;  // column ow0
   const int wcols = OW - ow0;  // columns of the row from ow0 on
-  const uint32_t qoff = (uint32_t)((q * C + c0 + b) * 4);
+  const uint32_t qoff = (uint32_t)((q * C + c0 + b) * EB);
   auto dy_fetch = [&](int n, int row) {  // row `row` of image n, 4 columns per load
     const bool ok = row >= 0 && row < OH;
-    const float* rp = dyc + ((size_t)n * OH + (ok ? row : 0)) * OW * C;
+    const char* rp = dyc + ((size_t)n * OH + (ok ? row : 0)) * OW * C * EB;
 #pragma unroll
     for (int s2 = 0; s2 < NB; ++s2) {
       const int left = wcols - 4 * s2;  // columns of the row from this load's first on
-      const auto rs = make_rsrc(rp + (size_t)(4 * s2) * C,
-                                ok && left > 0 ? (uint32_t)(left * C) * 4u : 0u);
-      nv[s2] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)qoff, 0, 0));
+      const auto rs = make_rsrc(rp + (size_t)(4 * s2) * C * EB,
+                                ok && left > 0 ? (uint32_t)(left * C) * EB : 0u);
+      if constexpr (DT == DT_F32) {
+        nv[s2] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)qoff, 0, 0));
+      } else {
+        const uint32_t h = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)qoff, 0, 0);
+        nv[s2] = DT == DT_BF16 ? __uint_as_float(h << 16)
+                               : (float)__builtin_bit_cast(_Float16, (unsigned short)h);
+      }
     }
   };
   auto dy_shift = [&]() {  // the fetched row into lane 0, the others one lane on

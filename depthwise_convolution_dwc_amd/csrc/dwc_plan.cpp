@@ -671,8 +671,12 @@ bool plan_wgrad_mfma(const dwc_problem* p, int64_t oh, int64_t ow, Plan* q) {
 // so that the workgroups fill the GPU once (or the requested split).
 static bool plan_wgrad_mfma_f32(const dwc_problem* p, int64_t oh, int64_t ow, bool forced,
                                 Plan* q) {
-  if (p->in_dtype != DT_F32 || p->stride_h != 1 || p->stride_w != 1 || p->fw > 32 ||
-      p->fh > 32 || p->c % kWf32Cb != 0)
+  // 16-bit operands (widened as they are loaded) come here only where the
+  // packed 16-bit filter gradient does not apply (inputs wider than 64, or
+  // staged rows past its LDS budget)
+  const int dt = p->in_dtype;
+  if ((dt != DT_F32 && dt != DT_BF16 && dt != DT_F16) || p->stride_h != 1 ||
+      p->stride_w != 1 || p->fw > 32 || p->fh > 32 || p->c % kWf32Cb != 0)
     return false;
   // AUTO: where the 4x4 tiles cover the filter with little waste (at least
   // 85% of the computed taps are real ones; 64% for filters at most 16

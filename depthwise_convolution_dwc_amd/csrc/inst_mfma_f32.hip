@@ -45,29 +45,38 @@ hipError_t by_fw(int fwi, int t, bool img, const MfmaF32Args& a, hipStream_t s) 
   return hipErrorInvalidValue;
 }
 
-template <int TW, int NB>
+template <int DT, int TW, int NB>
 hipError_t go_w(const WgradF32Args& a, hipStream_t s) {
-  auto kernel = wgrad_mfma_f32<TW, NB>;
+  auto kernel = wgrad_mfma_f32<DT, TW, NB>;
   hipLaunchKernelGGL(kernel, dim3(a.num_blocks), dim3(64 * a.nw), a.lds_bytes, s, a);
   return hipGetLastError();
 }
 
-template <int TW>
+template <int DT, int TW>
 hipError_t by_nb(int nb, const WgradF32Args& a, hipStream_t s) {
 #define DWC_CASE(B) \
-  if (nb == B) return go_w<TW, B>(a, s);
+  if (nb == B) return go_w<DT, TW, B>(a, s);
   DWC_WF32_NB_LIST(DWC_CASE)
+#undef DWC_CASE
+  return hipErrorInvalidValue;
+}
+
+template <int DT>
+hipError_t by_tw(int tw, int nb, const WgradF32Args& a, hipStream_t s) {
+#define DWC_CASE(W) \
+  if (tw == W) return by_nb<DT, W>(nb, a, s);
+  DWC_WF32_TW_LIST(DWC_CASE)
 #undef DWC_CASE
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_wgrad_mfma_f32(int tw, int nb, const WgradF32Args& a, hipStream_t s) {
-#define DWC_CASE(W) \
-  if (tw == W) return by_nb<W>(nb, a, s);
-  DWC_WF32_TW_LIST(DWC_CASE)
-#undef DWC_CASE
+// dt: the operand type of x and dY (fp32, bf16 or fp16)
+hipError_t launch_wgrad_mfma_f32(int dt, int tw, int nb, const WgradF32Args& a, hipStream_t s) {
+  if (dt == DT_F32) return by_tw<DT_F32>(tw, nb, a, s);
+  if (dt == DT_BF16) return by_tw<DT_BF16>(tw, nb, a, s);
+  if (dt == DT_F16) return by_tw<DT_F16>(tw, nb, a, s);
   return hipErrorInvalidValue;
 }
 

@@ -297,13 +297,14 @@ def test_mfma_plans_and_rejections(monkeypatch):
     assert dwc.plan_describe(p, 2).startswith("bwd_filter direct")
     # conditions of the packed kernels: half-precision operands (fp32: the
     # forward and data gradient, C a multiple of 16), stride 1, C a multiple
-    # of 8, FW <= 32, output width <= 64 (forward), input width <= 64 and FH
-    # <= 32 (filter gradient)
+    # of 8, FW <= 32, output width <= 64 (forward), FH <= 32 (filter
+    # gradient); a 16-bit filter gradient on inputs wider than 64 runs the
+    # fp32 matrix-core kernel, its operands widened as they are loaded
     base = dict(n=2, h=20, w=20, c=16, fh=5, fw=5, stride=1, pad=2, dtype=dwc.BF16)
     for kw, ops in ((dict(dtype=dwc.F32, c=24), (0, 1, 2)),
                     (dict(stride=2), (0, 1, 2)),
                     (dict(c=12), (0, 1, 2)), (dict(fw=33, pad=16), (0, 1, 2)),
-                    (dict(w=80), (0, 2)), (dict(fh=33, pad=16), (2,))):
+                    (dict(w=80), (0,)), (dict(fh=33, pad=16), (2,))):
         a = dict(base, **kw)
         q = dwc.problem(a["n"], a["h"], a["w"], a["c"], a["fh"], a["fw"], a["stride"],
                         a["pad"], dtype=a["dtype"], algo="mfma")
@@ -312,6 +313,14 @@ def test_mfma_plans_and_rejections(monkeypatch):
             assert "packed-MFMA" in dwc.last_error()
     q = dwc.problem(2, 20, 20, 16, 5, 5, 1, 2, dtype=dwc.BF16, algo="mfma")
     assert dwc.check(q, 0) == 0 and dwc.check(q, 1) == 0 and dwc.check(q, 2) == 0
+    for dt, name in ((dwc.BF16, "bf16"), (dwc.F16, "f16")):
+        q = dwc.problem(2, 20, 80, 16, 5, 5, 1, 2, dtype=dt, algo="mfma")
+        d = dwc.plan_describe(q, 2)
+        assert d.startswith(f"bwd_filter mfma dt={name}") and " f32=1 " in d, d
+    # AUTO: the bf16 filter gradient of 56-wide images with 13x13 filters
+    # (past the packed kernel's LDS budget) takes it too
+    q = dwc.problem(64, 56, 56, 128, 13, 13, 1, 6, dtype=dwc.BF16)
+    assert " f32=1 " in dwc.plan_describe(q, 2)
     # an empty batch plans (it only zero-fills dW) and needs no workspace
     q = dwc.problem(0, 20, 20, 16, 5, 5, 1, 2, dtype=dwc.BF16, algo="mfma")
     assert dwc.check(q, 2) == 0 and dwc.workspace_size(q) == 0

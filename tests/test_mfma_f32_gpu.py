@@ -144,6 +144,37 @@ def test_mfma_f32_wgrad_parity(shape, split):
     check_parity(got, want, mag, "bwd_filter", s, "f32", what=f"split={split}")
 
 
+# 16-bit operands on the same filter-gradient kernel, widened to fp32 as
+# they are loaded: inputs wider than 64 (past the packed 16-bit kernel) and
+# 56-wide ones with 13x13 filters (past its LDS budget); column tiles from
+# 1 to 8, two column groups, cropping padding
+F32W16_SHAPES = [
+    (2, 10, 70, 16, 21, 21, 1, 10),
+    (3, 9, 66, 32, 13, 13, 1, 6),
+    (2, 12, 80, 16, 5, 11, 1, (2, 3)),
+    (1, 8, 72, 48, 1, 31, 1, (0, 15)),
+    (2, 56, 56, 16, 13, 13, 1, 6),
+    (1, 40, 65, 16, 32, 32, 1, (16, 16)),
+    (2, 30, 100, 16, 17, 9, 1, (8, 4)),
+]
+
+
+@pytest.mark.parametrize("split", [0, 7])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", F32W16_SHAPES, ids=_ids)
+def test_mfma_f32_wgrad_16bit_parity(shape, dtype, split):
+    s = _shape(shape)
+    p = dwc.problem(s.n, s.h, s.w, s.c, s.fh, s.fw, 1, (s.pad_h, s.pad_w), dtype=DT[dtype],
+                    algo="mfma", wgrad_split=split)
+    d = dwc.plan_describe(p, OPS["bwd_filter"])
+    assert d.startswith(f"bwd_filter mfma dt={dtype}") and " f32=1 " in d, d
+    inp = make_inputs(s, dtype, seed=90 + sum(shape[:6]))
+    want, mag = _want_mag("bwd_filter", s, inp)
+    log(f"case mfma f32 wgrad {dtype} {shape} split={split}: {d}")
+    got = _run("bwd_filter", s, inp, "mfma", wgrad_split=split)
+    check_parity(got, want, mag, "bwd_filter", s, dtype, what=f"split={split}")
+
+
 def test_mfma_f32_wgrad_deterministic():
     s = _shape((3, 30, 30, 16, 27, 27, 1, 13))
     inp = make_inputs(s, "f32", seed=81)
