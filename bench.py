@@ -343,8 +343,8 @@ def kernels_of(dwc, s, op, dtype="f32", algo="auto"):
             k = f"fwd_mfma_h4n<{dt}, {kv['fwi']}, {kv['t']}, {flip}>"
         elif kv.get("f32") == "1":  # fp32 matrix-core kernels
             k = (f"wgrad_mfma_f32<{dt}, {kv['tw']}, {kv['nb']}>" if op == "bwd_filter" else
-                 f"fwd_mfma_f32{'n' if kv.get('img') == '1' else ''}<{kv['fwi']}, {kv['t']}, "
-                 f"{flip}>")
+                 f"fwd_mfma_f32n<{kv['fwi']}, {kv['t']}, {flip}>" if kv.get('img') == '1' else
+                 f"fwd_mfma_f32<{dt}, {kv['fwi']}, {kv['t']}, {flip}>")
         elif op == "bwd_filter":
             k = f"wgrad_mfma{'8' if dt >= 3 else ''}<{dt}, {kv['nfm']}, {kv['nfn']}, {kv['nk']}, " \
                 f"{kv['pf']}>"
@@ -854,10 +854,12 @@ launches (each traced dispatch matched in order to the launch bench.py
 issued, kernel name and workgroup count checked).  Fraction: of the literal roofline min(8 TB/s x eta_D / operand
 bytes, peak), peak 157.3 TFLOP/s (fp32 operands), 2.5 PFLOP/s (bf16/fp16
 operands), 5.0 PFLOP/s (fp8 operands).  Template arguments: the operand
-dtype first (0 fp32, 1 bf16, 2 fp16, 3 e4m3), except for the fp32
-matrix-core kernels: `fwd_mfma_f32<band width, 4-column tiles per wave,
-FLIP>` (`fwd_mfma_f32n`: 4 images as the matrix rows), `wgrad_mfma_f32<4-column
-filter tiles, 4-column output groups per wave>`.
+dtype first (0 fp32, 1 bf16, 2 fp16, 3 e4m3), also for the fp32
+matrix-core kernels (`fwd_mfma_f32<dtype, band width, 4-column tiles per
+wave, FLIP>`, `wgrad_mfma_f32<dtype, 4-column filter tiles, 4-column output
+groups per wave>`, 16-bit operands widened to fp32 on load), except
+`fwd_mfma_f32n<band width, tiles, FLIP>` (fp32 only, 4 images as the
+matrix rows).
 
 {chr(10).join(clines)}
 """
@@ -1081,9 +1083,11 @@ Every kernel the benchmark's per-configuration entries launch (the five
 configurations of the target, the strided backward and fp8 rows), except
 the default step's, which are in `{PROFILE_NAME}.sq_counters.md`.  Kernel
 names carry their template arguments (operand dtype first: 0 fp32, 1 bf16,
-2 fp16, 3 e4m3, 4 e5m2; the fp32 matrix-core kernels, fp32 only, take
-`fwd_mfma_f32<band width, 4-column tiles per wave, FLIP>`, its images
-variant `fwd_mfma_f32n` and `wgrad_mfma_f32<4-column filter tiles, 4-column output groups per wave>`)
+2 fp16, 3 e4m3, 4 e5m2; the fp32 matrix-core kernels take
+`fwd_mfma_f32<dtype, band width, 4-column tiles per wave, FLIP>` and
+`wgrad_mfma_f32<dtype, 4-column filter tiles, 4-column output groups per
+wave>`, their fp32-only images variant `fwd_mfma_f32n<band width, tiles,
+FLIP>`)
 and the workgroup count, which tells the launch sizes of one kernel apart;
 `configs.kernel_trace.md` maps them to the configurations.
 

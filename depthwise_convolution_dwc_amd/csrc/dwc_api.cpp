@@ -46,7 +46,7 @@ hipError_t launch_fwd_type(const Plan& pl, const void* in, const void* filt, flo
     m.in = in;
     m.filt = filt;
     m.out = out;
-    return launch_fwd_mfma_f32(pl.f32m_fwi, pl.f32m_t, pl.f32m_img, pl.flip, m, s);
+    return launch_fwd_mfma_f32(pl.dt, pl.f32m_fwi, pl.f32m_t, pl.f32m_img, pl.flip, m, s);
   }
   if (pl.kind == PLAN_MFMA && pl.batch) {
     MfmaBatchArgs m = pl.mb;

@@ -56,8 +56,8 @@ hipError_t launch_fwd_mfma_batch16(int dt, int ng, bool flip, const MfmaBatchArg
 // the matrix rows (fwd_mfma_h4n).
 hipError_t launch_fwd_mfma_h4(int dt, int fwi, int t, bool flip, const MfmaF32Args& a,
                               hipStream_t s);
-hipError_t launch_fwd_mfma_f32(int fwi, int t, bool img, bool flip, const MfmaF32Args& a,
-                               hipStream_t s);
+hipError_t launch_fwd_mfma_f32(int dt, int fwi, int t, bool img, bool flip,
+                               const MfmaF32Args& a, hipStream_t s);
 
 // fp32 matrix-core filter gradient (fp32 operands, stride 1, FH and FW <=
 // 32, C % 16 == 0): tw = ceil(FW / 4) column tiles, nb 4-column output

@@ -79,8 +79,51 @@ __device__ __forceinline__ float quad_shift_up_in(float a, float n, float keep, 
   return x;
 }
 
-template <int FWI, int T, bool FLIP>
+// Four consecutive 16-bit operand elements (bf16 or fp16, two per dword) as
+// fp32: exact.
+template <int DT>
+__device__ __forceinline__ f32m_x4 wf32_widen4(uint32_t lo, uint32_t hi) {
+  if constexpr (DT == DT_BF16) {
+    return f32m_x4{__uint_as_float(lo << 16), __uint_as_float(lo & 0xffff0000u),
+                   __uint_as_float(hi << 16), __uint_as_float(hi & 0xffff0000u)};
+  } else {
+    return f32m_x4{(float)__builtin_bit_cast(_Float16, (unsigned short)(lo & 0xffffu)),
+                   (float)__builtin_bit_cast(_Float16, (unsigned short)(lo >> 16)),
+                   (float)__builtin_bit_cast(_Float16, (unsigned short)(hi & 0xffffu)),
+                   (float)__builtin_bit_cast(_Float16, (unsigned short)(hi >> 16))};
+  }
+}
+
+// One operand element (fp32, bf16 or fp16) at a lane offset, as fp32:
+// exact.  Offsets past the resource read 0.
+template <int DT>
+__device__ __forceinline__ float f32m_ld1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (DT == DT_F32) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+  } else {
+    const uint32_t h = __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+    if constexpr (DT == DT_BF16) return __uint_as_float(h << 16);
+    else return (float)__builtin_bit_cast(_Float16, (unsigned short)h);
+  }
+}
+
+// Four consecutive operand elements (one 16- or 8-byte load) as fp32.
+template <int DT>
+__device__ __forceinline__ f32m_x4 f32m_ld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (DT == DT_F32) {
+    return __builtin_bit_cast(f32m_x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+  } else {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+    return wf32_widen4<DT>(v.x, v.y);
+  }
+}
+
+// DT: the operand type of the input and filter (fp32, or bf16 / fp16
+// widened to fp32 as they are loaded).
+template <int DT, int FWI, int T, bool FLIP>
 __global__ __launch_bounds__(64 * kF32mMaxWaves) void fwd_mfma_f32(MfmaF32Args a) {
+  constexpr int EB = DT == DT_F32 ? 4 : 2;  // operand bytes
   extern __shared__ __align__(16) unsigned char lds[];
   constexpr int NT = FWI + 3;            // K steps (taps t) of one 4-column tile
   constexpr int NA = 4 * T + FWI - 1;    // input columns a wave holds
@@ -107,7 +150,7 @@ __global__ __launch_bounds__(64 * kF32mMaxWaves) void fwd_mfma_f32(MfmaF32Args a
   {
     const int taps = FH * FW;
     const int items = taps * (kF32mCb / 4);
-    const auto frs = make_rsrc(a.filt, (uint32_t)taps * (uint32_t)C * 4u);
+    const auto frs = make_rsrc(a.filt, (uint32_t)taps * (uint32_t)C * EB);
     for (int e0 = 0; e0 < items; e0 += kF32mStageBatch * nthr) {
       f32m_x4 v[kF32mStageBatch];
 #pragma unroll
@@ -115,8 +158,8 @@ __global__ __launch_bounds__(64 * kF32mMaxWaves) void fwd_mfma_f32(MfmaF32Args a
         const int e = e0 + j * nthr + tid;
         const int tap = e >> 2, c4 = (e & 3) * 4;
         const int src = FLIP ? taps - 1 - tap : tap;
-        const uint32_t off = e < items ? ((uint32_t)src * (uint32_t)C + (uint32_t)(c0 + c4)) * 4u : kOOB;
-        v[j] = __builtin_bit_cast(f32m_x4, __builtin_amdgcn_raw_buffer_load_b128(frs, (int)off, 0, 0));
+        const uint32_t off = e < items ? ((uint32_t)src * (uint32_t)C + (uint32_t)(c0 + c4)) * EB : kOOB;
+        v[j] = f32m_ld4<DT>(frs, off);
       }
 #pragma unroll
       for (int j = 0; j < kF32mStageBatch; ++j) {
@@ -149,12 +192,13 @@ __global__ __launch_bounds__(64 * kF32mMaxWaves) void fwd_mfma_f32(MfmaF32Args a
   const int lane = tid & 63, b = lane >> 2, q = lane & 3;
   const int IH = a.IH, IW = a.IW, PH = a.PH, PW = a.PW;
 
-  const float* ximg = reinterpret_cast<const float*>(a.in) + (size_t)n * IH * IW * C;
-  const uint32_t rowb = (uint32_t)IW * (uint32_t)C * 4u;
+  const char* ximg = reinterpret_cast<const char*>(a.in) + (size_t)n * IH * IW * C * EB;
+  const uint32_t rowb = (uint32_t)IW * (uint32_t)C * EB;
   // Lane (b, q) of a 4-column load takes column ow0 - PW + 4s + q of a row;
   // negative columns wrap to offsets past any row's range.
-  const uint32_t loff = (uint32_t)(((ow0 - PW + q) * C + c0 + b) * 4);
-  const uint32_t sstep = (uint32_t)C * 16u;
+  const uint32_t loff = (uint32_t)(((ow0 - PW + q) * C + c0 + b) * EB);
+  const uint32_t istep = (uint32_t)C * 4u * EB;  // 4 input columns
+  const uint32_t sstep = (uint32_t)C * 16u;       // 4 output columns
 
   // Filter rows whose 4 input rows are not all padding.
   const int k_lo = max(0, PH - oh0 - (kF32mRows - 1));
@@ -174,14 +218,13 @@ __global__ __launch_bounds__(64 * kF32mMaxWaves) void fwd_mfma_f32(MfmaF32Args a
       const int r = oh0 + q + k_lo - PH;
       const bool ok = r >= 0 && r < IH;
       const auto irs = make_rsrc(ximg, (uint32_t)IH * rowb);
-      const uint32_t rbase = ok ? (uint32_t)r * rowb + (uint32_t)(c0 + b) * 4u : kOOB;
+      const uint32_t rbase = ok ? (uint32_t)r * rowb + (uint32_t)(c0 + b) * EB : kOOB;
 #pragma unroll
       for (int u = 0; u < NA; ++u) {
         const int col = ow0 - PW + u;
         A[u] = 0.f;
         if (u >= L && u < NA - R && col >= 0 && col < IW)
-          A[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                               irs, (int)(rbase + (uint32_t)col * (uint32_t)C * 4u), 0, 0));
+          A[u] = f32m_ld1<DT>(irs, rbase + (uint32_t)col * (uint32_t)C * EB);
       }
     }
     // every load above has landed before the loop (whose first instructions
@@ -198,11 +241,9 @@ __global__ __launch_bounds__(64 * kF32mMaxWaves) void fwd_mfma_f32(MfmaF32Args a
         // the row that enters next: oh0 + 4 + k - PH for lane 3
         const int r = oh0 + kF32mRows + k - PH;
         const bool ok = r >= 0 && r < IH;
-        const auto rs = make_rsrc(ximg + (size_t)(ok ? r : 0) * IW * C, ok ? rowb : 0u);
+        const auto rs = make_rsrc(ximg + (size_t)(ok ? r : 0) * IW * C * EB, ok ? rowb : 0u);
 #pragma unroll
-        for (int s2 = 0; s2 < NS; ++s2)
-          nv[s2] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                 rs, (int)(loff + (uint32_t)s2 * sstep), 0, 0));
+        for (int s2 = 0; s2 < NS; ++s2) nv[s2] = f32m_ld1<DT>(rs, loff + (uint32_t)s2 * istep);
       }
       const float* bk = bl + k * (ZP * kF32mCb);
       float bcur = bk[0];
@@ -417,21 +458,6 @@ __global__ __launch_bounds__(64 * kF32mMaxWaves) void fwd_mfma_f32n(MfmaF32Args 
   }
 }
 
-// Four consecutive 16-bit operand elements (bf16 or fp16, two per dword) as
-// fp32: exact.
-template <int DT>
-__device__ __forceinline__ f32m_x4 wf32_widen4(uint32_t lo, uint32_t hi) {
-  if constexpr (DT == DT_BF16) {
-    return f32m_x4{__uint_as_float(lo << 16), __uint_as_float(lo & 0xffff0000u),
-                   __uint_as_float(hi << 16), __uint_as_float(hi & 0xffff0000u)};
-  } else {
-    return f32m_x4{(float)__builtin_bit_cast(_Float16, (unsigned short)(lo & 0xffffu)),
-                   (float)__builtin_bit_cast(_Float16, (unsigned short)(lo >> 16)),
-                   (float)__builtin_bit_cast(_Float16, (unsigned short)(hi & 0xffffu)),
-                   (float)__builtin_bit_cast(_Float16, (unsigned short)(hi >> 16))};
-  }
-}
-
 // ---- filter gradient (layout and mapping: WgradF32Args).  DT: the operand
 // type of x and dY; 16-bit operands are widened to fp32 as they are loaded
 // (X on its way to the LDS, dY into the register window), so the matrix
@@ -516,13 +542,7 @@ __global__ __launch_bounds__(64 * kWf32MaxWaves, 4) void wgrad_mfma_f32(WgradF32
       const int left = wcols - 4 * s2;  // columns of the row from this load's first on
       const auto rs = make_rsrc(rp + (size_t)(4 * s2) * C * EB,
                                 ok && left > 0 ? (uint32_t)(left * C) * EB : 0u);
-      if constexpr (DT == DT_F32) {
-        nv[s2] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)qoff, 0, 0));
-      } else {
-        const uint32_t h = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)qoff, 0, 0);
-        nv[s2] = DT == DT_BF16 ? __uint_as_float(h << 16)
-                               : (float)__builtin_bit_cast(_Float16, (unsigned short)h);
-      }
+      nv[s2] = f32m_ld1<DT>(rs, qoff);
     }
   };
   auto dy_shift = [&]() {  // the fetched row into lane 0, the others one lane on

@@ -396,8 +396,11 @@ static bool plan_mfma_h4(const FwdArgs& f, int dt, bool flip, Plan* q) {
 // (within the batch for the images kernel).  DWC_MFMA_F32: 0 never, 1
 // wherever it applies.
 static bool plan_mfma_f32(const FwdArgs& f, int dt, bool flip, bool forced, Plan* q) {
-  if (dt != DT_F32 || f.SH != 1 || f.SW != 1 || f.C % kF32mCb != 0 || f.FW < 1 || f.FW > 31 ||
-      f.FH < 1 || f.FH > 64)
+  // 16-bit operands (widened as they are loaded, rows kernel only) come here
+  // only where no packed 16-bit kernel applies (outputs wider than 64, or
+  // bands past their LDS budget)
+  if ((dt != DT_F32 && dt != DT_BF16 && dt != DT_F16) || f.SH != 1 || f.SW != 1 ||
+      f.C % kF32mCb != 0 || f.FW < 1 || f.FW > 31 || f.FH < 1 || f.FH > 64)
     return false;
   if ((int64_t)f.IH * f.IW * f.C * 4 >= kI32Max || (int64_t)f.OH * f.OW * f.C * 4 >= kI32Max)
     return false;
@@ -432,10 +435,15 @@ static bool plan_mfma_f32(const FwdArgs& f, int dt, bool flip, bool forced, Plan
   const bool pick = (f.FH >= kF32mMinFh && f.FW >= kF32mMinFh &&
                      (f.OW >= kF32mMinOw || (f.OW <= 8 && f.FW >= 27) || img_auto || vec_few)) ||
                     (f.FH >= kF32mMinFPad && f.FW >= kF32mMinFPad && f.FW < kF32mMinFh);
+  // 16-bit operands: on request only.  The widened rows kernel needs 130
+  // registers (3 waves per SIMD) and loses to the 16-bit vector kernels as
+  // often as it wins (MI355X, bf16 N=32 112x112 C=64: 175 against 131 us
+  // at 13x13, 400 against 450 us at 27x27; N=64 56x56 C=128 31x31: 538
+  // against 578 us).
   const char* env = getenv("DWC_MFMA_F32");
-  if (!forced && (env ? atoi(env) == 0 : !pick)) return false;
+  if (!forced && (env ? atoi(env) == 0 : (!pick || dt != DT_F32))) return false;
   // the images kernel addresses 4 images of X from one buffer resource
-  const bool img_ok = f.N >= 4 && (int64_t)f.N * f.IH * f.IW * f.C * 4 < kI32Max;
+  const bool img_ok = dt == DT_F32 && f.N >= 4 && (int64_t)f.N * f.IH * f.IW * f.C * 4 < kI32Max;
   // DWC_MFMA_F32_IMG: 0 never, 1 for every batch of 4 or more
   const char* iv = getenv("DWC_MFMA_F32_IMG");
   const bool img = img_ok && (iv ? atoi(iv) != 0 : img_auto);

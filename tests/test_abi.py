@@ -298,13 +298,14 @@ def test_mfma_plans_and_rejections(monkeypatch):
     # conditions of the packed kernels: half-precision operands (fp32: the
     # forward and data gradient, C a multiple of 16), stride 1, C a multiple
     # of 8, FW <= 32, output width <= 64 (forward), FH <= 32 (filter
-    # gradient); a 16-bit filter gradient on inputs wider than 64 runs the
-    # fp32 matrix-core kernel, its operands widened as they are loaded
+    # gradient); 16-bit problems past them (outputs or inputs wider than 64)
+    # with C a multiple of 16 run the fp32 matrix-core kernels, operands
+    # widened as they are loaded
     base = dict(n=2, h=20, w=20, c=16, fh=5, fw=5, stride=1, pad=2, dtype=dwc.BF16)
     for kw, ops in ((dict(dtype=dwc.F32, c=24), (0, 1, 2)),
                     (dict(stride=2), (0, 1, 2)),
                     (dict(c=12), (0, 1, 2)), (dict(fw=33, pad=16), (0, 1, 2)),
-                    (dict(w=80), (0,)), (dict(fh=33, pad=16), (2,))):
+                    (dict(w=80, c=8), (0, 2)), (dict(fh=33, pad=16), (2,))):
         a = dict(base, **kw)
         q = dwc.problem(a["n"], a["h"], a["w"], a["c"], a["fh"], a["fw"], a["stride"],
                         a["pad"], dtype=a["dtype"], algo="mfma")
@@ -315,11 +316,16 @@ def test_mfma_plans_and_rejections(monkeypatch):
     assert dwc.check(q, 0) == 0 and dwc.check(q, 1) == 0 and dwc.check(q, 2) == 0
     for dt, name in ((dwc.BF16, "bf16"), (dwc.F16, "f16")):
         q = dwc.problem(2, 20, 80, 16, 5, 5, 1, 2, dtype=dt, algo="mfma")
-        d = dwc.plan_describe(q, 2)
-        assert d.startswith(f"bwd_filter mfma dt={name}") and " f32=1 " in d, d
+        for op, opn in ((0, "fwd"), (1, "bwd_data"), (2, "bwd_filter")):
+            d = dwc.plan_describe(q, op)
+            assert d.startswith(f"{opn} mfma dt={name}") and " f32=1 " in d, d
     # AUTO: the bf16 filter gradient of 56-wide images with 13x13 filters
-    # (past the packed kernel's LDS budget) takes it too
+    # (past the packed kernel's LDS budget) takes it too; the 16-bit forward
+    # only on request
     q = dwc.problem(64, 56, 56, 128, 13, 13, 1, 6, dtype=dwc.BF16)
+    assert " f32=1 " in dwc.plan_describe(q, 2)
+    q = dwc.problem(32, 112, 112, 64, 13, 13, 1, 6, dtype=dwc.BF16)
+    assert dwc.plan_describe(q, 0).startswith("fwd direct")
     assert " f32=1 " in dwc.plan_describe(q, 2)
     # an empty batch plans (it only zero-fills dW) and needs no workspace
     q = dwc.problem(0, 20, 20, 16, 5, 5, 1, 2, dtype=dwc.BF16, algo="mfma")

@@ -175,6 +175,37 @@ def test_mfma_f32_wgrad_16bit_parity(shape, dtype, split):
     check_parity(got, want, mag, "bwd_filter", s, dtype, what=f"split={split}")
 
 
+# 16-bit operands on the rows forward-type kernel (widened on load): outputs
+# wider than 64 (past the packed 16-bit kernels), each band width and tile
+# width, the flipped data gradient, ragged rows and columns
+F32M16_SHAPES = [
+    (2, 10, 70, 16, 13, 13, 1, 6),
+    (1, 12, 80, 32, 17, 17, 1, 8),
+    (2, 9, 66, 16, 21, 11, 1, (10, 5)),
+    (1, 20, 90, 16, 27, 27, 1, 13),
+    (1, 33, 67, 48, 31, 31, 1, 15),
+]
+
+
+@pytest.mark.parametrize("tile", ["auto", "2", "4", "7"])
+@pytest.mark.parametrize("op", ["fwd", "bwd_data"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", F32M16_SHAPES, ids=_ids)
+def test_mfma_f32_16bit_parity(shape, dtype, op, tile, monkeypatch):
+    if tile != "auto":
+        monkeypatch.setenv("DWC_MFMA_F32_T", tile)
+    s = _shape(shape)
+    p = dwc.problem(s.n, s.h, s.w, s.c, s.fh, s.fw, 1, (s.pad_h, s.pad_w), dtype=DT[dtype],
+                    algo="mfma")
+    d = dwc.plan_describe(p, OPS[op])
+    assert f" mfma dt={dtype} " in d and " f32=1 " in d and " img=0 " in d, d
+    inp = make_inputs(s, dtype, seed=95 + sum(shape[:6]))
+    want, mag = _want_mag(op, s, inp)
+    log(f"case mfma f32 {dtype} {op} {shape} tile={tile}: {d}")
+    got = _run(op, s, inp, "mfma")
+    check_parity(got, want, mag, op, s, dtype, what=f"tile={tile}")
+
+
 def test_mfma_f32_wgrad_deterministic():
     s = _shape((3, 30, 30, 16, 27, 27, 1, 13))
     inp = make_inputs(s, "f32", seed=81)
