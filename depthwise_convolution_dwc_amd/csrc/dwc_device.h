@@ -56,9 +56,11 @@ __device__ __forceinline__ int fast_div(int p, uint64_t m) {
 // An offset that is always outside any resource built above.
 constexpr uint32_t kOOB = 0x80000000u;
 
-// The hardware hands workgroup b to XCD (b mod 8).  Give each XCD one
-// contiguous range of logical tile ids so that tiles which read the same
-// input rows share that XCD's L2.
+// The hardware hands workgroup b to XCD (b mod 8) on the MI355X's 8 XCDs.
+// Give each XCD one contiguous range of logical tile ids so that tiles
+// which read the same input rows share that XCD's L2.  The map is a
+// permutation of [0, nblocks) whatever the device's XCD count, so another
+// count changes only which tiles share an L2, never a result.
 __device__ __forceinline__ int xcd_logical_block(int bid, int nblocks) {
   constexpr int kXcd = 8;
   const int x = bid % kXcd, k = bid / kXcd;
